@@ -1,0 +1,196 @@
+"""Pins for the oracle's block-16 FP4 pack.
+
+The pages fix only the container (two E2M1 codes per byte, an FP8-E4M3 scale per
+16 K-values, an fp32 global scale); the quantisation recipe is the oracle's
+reading and is pinned here by: the format tables checked against torch's
+float8_e4m3fn decoder and conversion, exact rational brute force of every
+rounding decision, a hand-worked golden block, round trips and error bounds.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_e2m1_table_from_format():
+    # 1 sign, 2 exponent bits (bias 1), 1 mantissa bit: the OCP E2M1 value set.
+    assert list(oracle.E2M1_VALUES) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(oracle.e2m1_decode(np.arange(8, 16))) == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def test_e4m3fn_decode_matches_torch_for_all_256_codes():
+    codes = torch.arange(256, dtype=torch.uint8)
+    want = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3fn_decode(np.arange(256))
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert oracle.e4m3fn_decode(0x7E) == 448.0
+
+
+def test_e4m3fn_encode_is_inverse_on_grid():
+    codes = np.arange(0x7F)                         # every finite non-negative code
+    vals = oracle.e4m3fn_decode(codes)
+    assert np.array_equal(oracle.e4m3fn_encode_rne_sat(vals), codes)
+
+
+def test_e4m3fn_encode_matches_torch_rne_in_range():
+    rng = np.random.default_rng(0)
+    v = np.concatenate([rng.uniform(0, 464, 20000), np.exp2(rng.uniform(-12, 8.8, 20000))])
+    v = v[v < 464].astype(np.float32)               # torch does not saturate above 464
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    got = oracle.e4m3fn_encode_rne_sat(v.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_e4m3fn_saturates_and_ties_to_even():
+    assert oracle.e4m3fn_encode_rne_sat(np.array([1e6, 464.0, 500.0])).tolist() == [0x7E] * 3
+    # midpoint between 1.0 (0x38) and 1.125 (0x39) goes to the even mantissa 0x38;
+    # midpoint between 1.125 and 1.25 (0x3A) goes to 0x3A.
+    assert oracle.e4m3fn_encode_rne_sat(np.array([1.0625, 1.1875])).tolist() == [0x38, 0x3A]
+    # smallest subnormal 2^-9; half of it ties to zero, three halves ties to 2^-8
+    assert oracle.e4m3fn_encode_rne_sat(np.array([2.0 ** -10, 3 * 2.0 ** -10])).tolist() == [0, 2]
+
+
+# Exact rational brute force of each rounding decision --------------------------
+
+_E4M3_POS = [(c, Fraction(float(oracle.e4m3fn_decode(c)))) for c in range(0x7F)]
+_E2M1_POS = [(c, Fraction(float(v))) for c, v in enumerate(oracle.E2M1_VALUES)]
+
+
+def _nearest_even(q, table):
+    """Nearest table entry to the exact rational q; ties -> even code; beyond the
+    largest entry -> the largest entry."""
+    best = min(abs(q - v) for _, v in table)
+    cands = [c for c, v in table if abs(q - v) == best]
+    if len(cands) == 2:
+        return [c for c in cands if c % 2 == 0][0]
+    return cands[0]
+
+
+def _exact_pack(W):
+    N, K = W.shape
+    A = max(abs(Fraction(float(w))) for w in W.ravel())
+    g = oracle.global_scale(float(A))
+    packed = np.zeros((N, K // 2), np.int64)
+    scales = np.zeros((N, K // 16), np.int64)
+    for n in range(N):
+        codes = []
+        for b in range(K // 16):
+            blk = [Fraction(float(w)) for w in W[n, 16 * b:16 * b + 16]]
+            a = max(abs(w) for w in blk)
+            sf = _nearest_even(a / (6 * Fraction(g)), _E4M3_POS)
+            scales[n, b] = sf
+            D = Fraction(oracle.rn_f32_exact(Fraction(g) * Fraction(float(oracle.e4m3fn_decode(sf)))))
+            for w in blk:
+                if D == 0:
+                    codes.append(0)
+                    continue
+                m = _nearest_even(abs(w) / D, _E2M1_POS)
+                codes.append(m | (8 if (w < 0 and m != 0) else 0))
+        for i in range(K // 2):
+            packed[n, i] = codes[2 * i] | (codes[2 * i + 1] << 4)
+    return packed, scales, g
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pack_matches_exact_rational_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    N, K = 3, 64
+    scale = [1e-3, 1.0, 37.0, 2.0 ** -20, 5e3, 0.02][seed]
+    W = rng.standard_normal((N, K)) * scale
+    W[0, :16] *= 1e-3                               # a block far below the global max
+    if seed % 2:
+        W[1, 16:32] = 0.0                           # an all-zero block
+    W = torch.from_numpy(W.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    p, s, g = oracle.fp4_pack(W)
+    ep, es, eg = _exact_pack(W)
+    assert g == eg
+    assert np.array_equal(s, es)
+    assert np.array_equal(p, ep)
+
+
+def test_pack_ties_bruteforce():
+    """Elements placed exactly on E2M1 midpoints (times D = 1) follow ties-to-even."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    row = [10.5] + [0.0] * 15                       # A = 10.5 -> g = 2^-8 exactly
+    row += [6.0] + mids + [-m for m in mids] + [0.0]  # block max 6 -> scale 256, D = 1
+    W = np.array([row], dtype=np.float64)
+    p, s, g = oracle.fp4_pack(W)
+    ep, es, eg = _exact_pack(W)
+    assert g == 2.0 ** -8 and s.tolist() == [[0x7E, 0x78]]
+    assert np.array_equal(p, ep) and np.array_equal(s, es) and g == eg
+    codes = np.empty(32, np.int64)
+    codes[0::2] = p[0] & 0xF
+    codes[1::2] = p[0] >> 4
+    assert codes[17:24].tolist() == [0, 2, 2, 4, 4, 6, 6]        # even-code winners
+    assert codes[24:31].tolist() == [0, 10, 10, 12, 12, 14, 14]  # same, negative (no -0)
+
+
+def test_golden_hand_block():
+    with open(os.path.join(GOLDEN, "hand_fp4_block16.json")) as f:
+        gd = json.load(f)
+    W = np.array(gd["W"], dtype=np.float64)
+    p, s, g = oracle.fp4_pack(W)
+    assert g == gd["global_scale"]
+    assert s.tolist() == gd["scales"]
+    assert p.tolist() == gd["packed"]
+    codes = np.empty((1, 32), np.int64)
+    codes[:, 0::2] = p & 0xF
+    codes[:, 1::2] = p >> 4
+    assert codes.tolist() == gd["hand_codes"]
+
+
+def test_round_trip_of_grid_values_is_lossless():
+    rng = np.random.default_rng(21)
+    N, K = 4, 64
+    W = np.zeros((N, K))
+    for n in range(N):
+        for b in range(K // 16):
+            D = 2.0 ** int(rng.integers(-6, 3))          # block step, a power of two
+            vals = rng.choice(oracle.E2M1_VALUES, 16) * rng.choice([-1.0, 1.0], 16)
+            vals[0] = 6.0                                 # block max = 6 D
+            W[n, 16 * b:16 * b + 16] = vals * D
+    W[0, :16] = 0.0
+    W[0, 0] = 42.0                     # A = 21 * 2: g = 2^-6, so every D above is exact
+    p, s, g = oracle.fp4_pack(W)
+    assert g == 2.0 ** -6
+    back = oracle.fp4_unpack(p, s, g)
+    assert np.array_equal(back, W)
+
+
+def test_dequant_error_bound():
+    rng = np.random.default_rng(8)
+    W = rng.standard_normal((16, 256)) * np.exp2(rng.uniform(-4, 4, (16, 1)))
+    W = torch.from_numpy(W.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    p, s, g = oracle.fp4_pack(W)
+    back = oracle.fp4_unpack(p, s, g)
+    D = np.repeat(oracle.rne_f32(g * oracle.e4m3fn_decode(s.astype(np.int64))), 16, axis=1)
+    normal = np.repeat(s >= 8, 16, axis=1)                      # block scale not subnormal
+    assert normal.mean() > 0.99
+    err = np.abs(back - W)
+    assert np.all(err[normal] <= D[normal])                     # half the widest gap (2 D)
+    small = normal & (np.abs(W) <= 2 * D)
+    assert np.all(err[small] <= D[small] / 4)                   # gap 0.5 D below 2 D
+
+
+def test_all_zero_tensor():
+    p, s, g = oracle.fp4_pack(np.zeros((2, 32)))
+    assert g == 1.0 and not p.any() and not s.any()
+
+
+def test_global_scale_exact():
+    assert oracle.global_scale(10.5) == 2.0 ** -8
+    assert oracle.global_scale(0.0) == 1.0
+    # 1/448 is not a binary fraction: compare against exact rational rounding
+    g = oracle.global_scale(6.0)
+    assert g == oracle.rn_f32_exact(Fraction(6, 2688))
+    assert abs(g - 6 / 2688) <= 2.0 ** -24 * (6 / 2688)
