@@ -1,0 +1,417 @@
+"""Benchmark of the theta-bundle reconstructed linear on one MI355X.
+
+Default workload (one JSON line on stdout): the Gemma-3-1B-shaped decoder,
+26 layers, bf16, rank 16, decode batches M = 1, 4 and 16 tokens.  One step is a
+full pass of all 26 layers at each of the three batch sizes; a layer is four
+dispatches (fused Q/K/V, o, fused gate/up, down).  The weights of all 26 layers
+(1.4 GB of W0) stay resident in HBM, far beyond the 256 MB Infinity Cache, and
+are visited in model order, so every dispatch streams its weights from HBM.
+
+Other workloads (``--workload``): gemma_prefill (M = 512, 2048; rank 64),
+large_decoder (8 layers in 4 shared-W0 bands, rank 32, M = 1, 32, 512),
+materialize_fp4 (7 families x 26 layers, 13 bands, rank 64: W_eff then FP4).
+
+The step is timed as a captured HIP graph (launch cost excluded, as in serving)
+and, for comparison, eagerly.  The dominant kernel is also timed per launch with
+HIP events on the launch stream, queued behind a GPU sleep so that no CPU launch
+gap falls inside an event pair.  The CPU baseline is the fp64 oracle on a bounded
+sample of the same workload, on this host's cores.
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2516.6    # dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- workload
+
+class Call:
+    """One pre-marshalled C-ABI call (pointers, strides and stream fixed)."""
+
+    def __init__(self, fn, args, nbytes, flops, name, grid_key):
+        self.fn, self.args = fn, args
+        self.nbytes, self.flops, self.name, self.grid_key = nbytes, flops, name, grid_key
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            from rank_shared_block_amd import binding as B
+            raise RuntimeError(f"{self.name}: {B.status_string(st)}: {B.last_error()}")
+
+
+def _dispatch_bytes(M, K, bundles):
+    """Algorithmic bytes of one recon dispatch (bf16): every operand once."""
+    b = M * K * 2
+    for (N, r) in bundles:
+        b += (N * K + N + N * r + r * K) * 2 + M * N * 2
+    return b
+
+
+def _dispatch_flops(M, K, bundles):
+    f = 0
+    for (N, r) in bundles:
+        f += 2 * M * K * (N + r) + 2 * M * r * N
+    return f
+
+
+def make_recon_calls(torch, B, I, shapes, layer_dev, layer_np, M, x_tag, dtype="bf16"):
+    """Per layer, the four dispatches as pre-marshalled calls."""
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream().cuda_stream
+    calls = []
+    keep = []
+    lib = B.lib()
+    for l, fam_dev in enumerate(layer_dev):
+        for name, fams in I.LAYER_DISPATCHES:
+            K = shapes[fams[0]][0]
+            x = torch.from_numpy(I.activations("gemma_decode", x_tag + len(name), M, K, dtype)).to(dev).to(torch.bfloat16)
+            projs = [B.make_proj(*fam_dev[f]) for f in fams]
+            arr = (B.aq_proj * len(fams))(*projs)
+            ntot = sum(p.N for p in projs)
+            y = torch.empty((M, ntot), dtype=torch.bfloat16, device=dev)
+            need = lib.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, M, K, arr, len(fams))
+            ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+            fn = {"qkv": lib.aq_recon_qkv_fused, "gateup": lib.aq_recon_gateup_fused}.get(name, lib.aq_recon_linear)
+            args = (B.AQ_BF16, M, K, x.data_ptr(), K, arr, y.data_ptr(), ntot, ws.data_ptr(), ws.numel(), stream)
+            nr = [(shapes[f][1], layer_np[l][f]["U"].shape[1]) for f in fams]
+            calls.append(Call(fn, args, _dispatch_bytes(M, K, nr), _dispatch_flops(M, K, nr), f"L{l}.{name}.M{M}", name))
+            keep += [x, y, ws, arr]
+    return calls, keep
+
+
+def upload_layers(torch, I, layer_np):
+    dev = torch.device("cuda", 0)
+    shared = {}
+    out = []
+    for l in sorted(layer_np):
+        d = {}
+        for f, bd in layer_np[l].items():
+            key = id(bd["W0"])
+            if key not in shared:
+                shared[key] = torch.from_numpy(bd["W0"]).to(dev).to(torch.bfloat16)
+            d[f] = (shared[key],) + tuple(torch.from_numpy(bd[k]).to(dev).to(torch.bfloat16) for k in ("s", "U", "Vt"))
+        out.append(d)
+    return out
+
+
+# --------------------------------------------------------------------------- timing
+
+def time_graph(torch, calls, steps, warmup):
+    """Capture `calls` in one HIP graph; replay warmup + steps; return ms per replay."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in calls:             # eager warm-up on the capture stream
+            c()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        # the calls were marshalled with the ambient stream; re-marshal for the capture stream
+        cap = torch.cuda.current_stream().cuda_stream
+        for c in calls:
+            a = list(c.args)
+            a[-1] = cap
+            st = c.fn(*a)
+            assert st == 0, c.name
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, g
+
+
+def time_eager(torch, calls, steps, warmup):
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        for c in calls:
+            c()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_per_launch(torch, calls, reps):
+    """Average GPU duration of each launch, from event pairs around every launch,
+    all queued behind a GPU sleep so that the pairs see no CPU gaps."""
+    durs = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2e7))                  # ~10 ms of GPU spin while we enqueue
+        evs = []
+        for c in calls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            c()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        durs += [a.elapsed_time(b) for a, b in evs]
+    return float(np.mean(durs)), float(np.median(durs))
+
+
+# --------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(I, layer_np, shapes, Ms, x_tag, budget_s, layers_sample):
+    """The oracle on a bounded sample: `layers_sample` layers, every M, repeated
+    until `budget_s` of oracle time; returns GB/s of algorithmic bytes."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    ls = sorted(layer_np)[:layers_sample]
+    conv = {}
+    for l in ls:
+        for f, bd in layer_np[l].items():
+            conv[(l, f)] = tuple(bd[k].astype(np.float64) for k in ("W0", "s", "U", "Vt"))
+    xs = {}
+    for M in Ms:
+        for name, fams in I.LAYER_DISPATCHES:
+            K = shapes[fams[0]][0]
+            xs[(M, name)] = I.activations("gemma_decode", x_tag(M) + len(name), M, K, "bf16").astype(np.float64)
+    nbytes, t_used, passes = 0, 0.0, 0
+    while t_used < budget_s:
+        for M in Ms:
+            for l in ls:
+                for name, fams in I.LAYER_DISPATCHES:
+                    K = shapes[fams[0]][0]
+                    t0 = time.perf_counter()
+                    oracle.recon_fused(xs[(M, name)], [conv[(l, f)] for f in fams])
+                    t_used += time.perf_counter() - t0
+                    nbytes += _dispatch_bytes(M, K, [(shapes[f][1], conv[(l, f)][2].shape[1]) for f in fams])
+        passes += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(nbytes / t_used / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(ls)} of 26 layers x M in {list(Ms)} x 4 dispatches, {passes} passes, "
+                      f"{t_used:.1f} s of numpy float64 oracle time (bf16->fp64 conversion excluded)"}
+
+
+# --------------------------------------------------------------------------- workloads
+
+def run_gemma_decode(args, torch, B, I):
+    Ms = (1, 4, 16)
+    L = 26
+    t0 = time.time()
+    layer_np = I.layer_bundles("gemma_decode", I.GEMMA_1B, layers=L, r=16, dtype="bf16")
+    log(f"generated inputs in {time.time() - t0:.1f} s")
+    layer_dev = upload_layers(torch, I, layer_np)
+    torch.cuda.synchronize()
+    log(f"uploaded {L} layers")
+    xtag = lambda M: 10 * M
+    per_M = {}
+    all_calls = []
+    keep = []
+    for M in Ms:
+        calls, k = make_recon_calls(torch, B, I, I.GEMMA_1B, layer_dev, layer_np, M, xtag(M))
+        keep += k
+        per_M[M] = calls
+        all_calls += calls
+    step_bytes = sum(c.nbytes for c in all_calls)
+
+    # Headline: one graph for the whole step.
+    ms_step, g = time_graph(torch, all_calls, args.steps, args.warmup)
+    log(f"graph step: {ms_step:.4f} ms")
+    us_layer = {}
+    for M in Ms:
+        ms, _ = time_graph(torch, per_M[M], max(5, args.steps // 2), 2)
+        us_layer[f"M{M}"] = round(ms * 1e3 / L, 3)
+    ms_eager = time_eager(torch, all_calls, max(3, args.steps // 4), 1)
+
+    # Dominant kernel: the fused gate/up dispatch (59% of the bytes of a layer).
+    gu = [c for c in all_calls if c.grid_key == "gateup"]
+    avg_ms, med_ms = time_per_launch(torch, gu, args.roofline_reps)
+    gu_bytes = float(np.mean([c.nbytes for c in gu]))
+    achieved = gu_bytes / (avg_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_decode_bf16 (fused gate/up, K=1152, N=2x6912, r=16, M in {1,4,16})",
+            "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(avg_ms * 1e3, 3),
+            "median_launch_us": round(med_ms * 1e3, 3), "launches": len(gu) * args.roofline_reps}
+
+    line = {
+        "metric": "reconstructed-linear µs/layer + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)",
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1/in) W0, U(0.9,1.1) s, N(0,0.02) U/V, N(0,1) x)",
+        "config": {"workload": "gemma-3-1b-shaped decode: 26 layers x (fused QKV, o, fused gate/up, down), "
+                               "hidden 1152, rank 16, bf16, M in {1,4,16} tokens per step",
+                   "layers": L, "rank": 16, "tokens": list(Ms), "launch": "hip graph per step"},
+        "us_per_layer": us_layer,
+        "frac_of_hbm_peak_step": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "ms_per_step_eager": round(ms_eager, 4),
+        "bytes_per_step": int(step_bytes),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(I, layer_np, I.GEMMA_1B, Ms, xtag, args.cpu_budget, 4)
+    return line
+
+
+def run_gemma_prefill(args, torch, B, I):
+    Ms = (512, 2048)
+    L = args.layers or 26
+    layer_np = I.layer_bundles("gemma_prefill", I.GEMMA_1B, layers=L, r=64, dtype="bf16")
+    layer_dev = upload_layers(torch, I, layer_np)
+    res = {}
+    for M in Ms:
+        calls, keep = make_recon_calls(torch, B, I, I.GEMMA_1B, layer_dev, layer_np, M, 5 * M)
+        ms, _ = time_graph(torch, calls, args.steps, args.warmup)
+        fl = sum(c.flops for c in calls)
+        # dense baseline: torch.matmul (hipBLASLt) on W_eff of the identical stacked shapes
+        dense = []
+        dev = torch.device("cuda", 0)
+        for l in range(L):
+            for name, fams in I.LAYER_DISPATCHES:
+                K = I.GEMMA_1B[fams[0]][0]
+                N = sum(I.GEMMA_1B[f][1] for f in fams)
+                dense.append((torch.randn(M, K, device=dev, dtype=torch.bfloat16),
+                              torch.randn(N, K, device=dev, dtype=torch.bfloat16) * 0.03))
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        outs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for x, w in dense:
+                torch.matmul(x, w.t())
+        torch.cuda.current_stream().wait_stream(s)
+        with torch.cuda.graph(g):
+            for x, w in dense:
+                outs.append(torch.matmul(x, w.t()))
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_dense = e0.elapsed_time(e1) / args.steps
+        dfl = sum(2 * x.shape[0] * x.shape[1] * w.shape[0] for x, w in dense)
+        res[f"M{M}"] = {"us_per_layer": round(ms * 1e3 / L, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                        "frac_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+                        "dense_us_per_layer": round(ms_dense * 1e3 / L, 2),
+                        "dense_tflops": round(dfl / (ms_dense * 1e-3) / 1e12, 1),
+                        "recon_over_dense": round(ms / ms_dense, 3)}
+        del dense, outs, g
+    return {"workload": f"gemma-3-1b-shaped prefill, {L} layers, rank 64, bf16", "results": res}
+
+
+def run_large_decoder(args, torch, B, I):
+    Ms = (1, 32, 512)
+    L = 8
+    layer_np = I.layer_bundles("large_decoder", I.LARGE_DECODER, layers=L, r=32, dtype="bf16", num_bands=4)
+    layer_dev = upload_layers(torch, I, layer_np)
+    res = {}
+    for M in Ms:
+        calls, keep = make_recon_calls(torch, B, I, I.LARGE_DECODER, layer_dev, layer_np, M, 9 * M)
+        ms, _ = time_graph(torch, calls, args.steps, args.warmup)
+        nb = sum(c.nbytes for c in calls)
+        fl = sum(c.flops for c in calls)
+        res[f"M{M}"] = {"us_per_layer": round(ms * 1e3 / L, 2),
+                        "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                        "note": "bands of 2 layers share W0: the second layer may hit the Infinity Cache"}
+    return {"workload": "large-decoder-shaped, 8 layers in 4 W0 bands, rank 32, bf16", "results": res}
+
+
+def run_materialize_fp4(args, torch, B, I):
+    L, G = 26, 13
+    layer_np = I.layer_bundles("materialize_fp4", I.GEMMA_1B, layers=L, r=64, dtype="bf16", num_bands=G)
+    layer_dev = upload_layers(torch, I, layer_np)
+    dev = torch.device("cuda", 0)
+    lib = B.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    mats, packs, keep = [], [], []
+    mbytes = pbytes = 0
+    for l in range(L):
+        for f in I.FAMILIES:
+            K, N = I.GEMMA_1B[f]
+            bd = layer_dev[l][f]
+            w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+            p = B.make_proj(*bd)
+            pa = (B.aq_proj * 1)(p)
+            mats.append(Call(lib.aq_materialize_weff, (B.AQ_BF16, K, pa, w.data_ptr(), K, stream),
+                             (2 * N * K + N + N * 64 + 64 * K) * 2, 2 * N * K * 64, f"mat.L{l}.{f}", "mat"))
+            packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+            sc = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+            gs = torch.empty((1,), dtype=torch.float32, device=dev)
+            ws = torch.zeros(4096, dtype=torch.uint8, device=dev)
+            packs.append(Call(lib.aq_quant_fp4_block16, (N, K, w.data_ptr(), K, packed.data_ptr(), sc.data_ptr(),
+                                                         gs.data_ptr(), ws.data_ptr(), 4096, stream),
+                              2 * N * K * 2 + N * K // 2 + N * K // 16, 0, f"fp4.L{l}.{f}", "fp4"))
+            keep += [w, packed, sc, gs, ws, pa]
+            mbytes += mats[-1].nbytes
+            pbytes += packs[-1].nbytes
+    ms_m, _ = time_graph(torch, mats, args.steps, args.warmup)
+    ms_p, _ = time_graph(torch, packs, args.steps, args.warmup)
+    mat_avg, _ = time_per_launch(torch, mats, 2)
+    return {"workload": "materialise + FP4 pack, 7 families x 26 layers (Gemma-3-1B shapes), 13 W0 bands, rank 64",
+            "materialize": {"ms": round(ms_m, 4), "GBps": round(mbytes / (ms_m * 1e-3) / 1e9, 1),
+                            "frac_hbm_peak": round(mbytes / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "avg_launch_us": round(mat_avg * 1e3, 2), "bytes": mbytes},
+            "fp4_pack": {"ms": round(ms_p, 4), "GBps": round(pbytes / (ms_p * 1e-3) / 1e9, 1),
+                         "frac_hbm_peak": round(pbytes / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": pbytes}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gemma_decode",
+                    choices=["gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4"])
+    ap.add_argument("--layers", type=int, default=0)
+    ap.add_argument("--roofline-reps", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from rank_shared_block_amd import binding as B
+    from rank_shared_block_amd import inputs as I
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()
+    torch.cuda.set_device(0)
+    fn = {"gemma_decode": run_gemma_decode, "gemma_prefill": run_gemma_prefill,
+          "large_decoder": run_large_decoder, "materialize_fp4": run_materialize_fp4}[args.workload]
+    out = fn(args, torch, B, I)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

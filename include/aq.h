@@ -1,0 +1,164 @@
+/*
+ * aq.h -- C ABI of the MI355X (gfx950) theta-bundle reconstructed linear.
+ *
+ * A theta bundle replaces one projection's dense [out_dim, in_dim] weight by a
+ * shared block W0, a per-output-row scale s and a rank-r pair U, V
+ * ("How attnquant works", section "The theta bundle").  This library computes,
+ * on one GPU and with hand-written HIP kernels:
+ *
+ *   y     = s * (x W0^T) + (x Vt^T) U^T           (the reconstruction identity)
+ *   W_eff = diag(s) W0 + U Vt                     (the effective weight)
+ *   FP4   = block-16 E2M1 codes + E4M3 scales + fp32 global scale of W_eff
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Row vectors: x is [M, K] (M tokens, K = in_dim), y is [M, N] (N = out_dim).
+ * - All matrices are row-major with unit column stride.  W0 is [N, K] with row
+ *   stride K; s is [N]; U is [N, r] with row stride r; Vt = V^T is [r, K] with
+ *   row stride K (the pages' V is [K, r]; it is passed transposed so that W0 and
+ *   Vt are both K-contiguous).
+ * - Every pointer to tensor data is a DEVICE pointer owned by the caller; the
+ *   library never frees or retains it.  All tensors of one call share one dtype
+ *   (aq_dtype).  Outputs must not alias inputs.
+ * - Every call only enqueues work on `stream` (a hipStream_t; NULL = the null
+ *   stream) and returns without synchronising.  Argument errors are detected on
+ *   the host before anything is enqueued and return a status other than AQ_OK;
+ *   in that case nothing was launched.  A launch failure returns AQ_ERR_HIP.
+ *   Faults during execution surface at the caller's next synchronisation.
+ * - aq_last_error() returns a thread-local, human-readable detail of the last
+ *   failing call on this thread (which argument, which shape).
+ * - No C++ exception crosses this boundary.
+ */
+#ifndef AQ_H
+#define AQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum aq_status {
+  AQ_OK = 0,
+  AQ_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum             */
+  AQ_ERR_SHAPE = 2,       /* sizes or strides that do not fit together         */
+  AQ_ERR_ALIGNMENT = 3,   /* pointer / stride / K not aligned as required      */
+  AQ_ERR_UNSUPPORTED = 4, /* valid request outside the library's limits        */
+  AQ_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned        */
+  AQ_ERR_HIP = 6          /* the HIP runtime refused a launch                  */
+} aq_status;
+
+typedef enum aq_dtype { AQ_F32 = 0, AQ_BF16 = 1 } aq_dtype;
+
+typedef enum aq_op { AQ_OP_RECON = 0, AQ_OP_FP4 = 1 } aq_op;
+
+#define AQ_MAX_RANK 256
+
+/* One projection's bundle ("How attnquant works", section "The theta bundle").
+ * N = out_dim; r = rank (0 <= r <= AQ_MAX_RANK; for r == 0, U and Vt are
+ * ignored and may be NULL, and the projection is a pure scaled shared block as
+ * the end of "How the decomposition produces s, U, and V" describes).
+ * W0 [N, K], s [N], U [N, r], Vt [r, K], all device pointers, one dtype. */
+typedef struct aq_proj {
+  int64_t N;
+  int64_t r;
+  const void *W0;
+  const void *s;
+  const void *U;
+  const void *Vt;
+} aq_proj;
+
+/* y[M, ldy] (columns 0..N-1) = s * (x W0^T) + (x Vt^T) U^T.
+ * "How attnquant works", section "The reconstruction identity"; row-batch form of
+ * "Execution paths", section "The GEMM formulation".
+ *   dt     AQ_BF16: bf16 storage, fp32 accumulation, one rounding of y to bf16.
+ *          AQ_F32 : fp32 storage and arithmetic.
+ *   M      tokens (0 is a no-op returning AQ_OK; x and y may then be NULL).
+ *   K      in_dim >= 1; bf16 needs K % 8 == 0, f32 needs K % 4 == 0.
+ *   x      [M, ldx], ldx >= K, same divisibility as K; 16-byte aligned.
+ *   p      one projection; W0 and Vt 16-byte aligned; s, U naturally aligned.
+ *   y      [M, ldy], ldy >= N; naturally aligned.
+ *   ws     device workspace of at least aq_workspace_bytes(AQ_OP_RECON, ...)
+ *          bytes, 256-byte aligned (NULL allowed when that size is 0).  It must
+ *          be zero-filled before its first use; every call leaves it zero-filled
+ *          again (its counters reset themselves), so one zeroed allocation can be
+ *          reused by any number of calls that are ordered on one stream.  Calls
+ *          that share a workspace must not run concurrently.
+ * Limits: 1 <= N, K <= 2^24; M <= 2^20; r <= AQ_MAX_RANK (else
+ * AQ_ERR_UNSUPPORTED, a refusal rather than a silent fallback, as the pages' own
+ * custom op refuses ranks above its limit: "Execution paths", "The custom op"). */
+aq_status aq_recon_linear(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
+                          const aq_proj *p, void *y, int64_t ldy, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* Fused Q/K/V: p[0..2] = (q, k, v) read the same x; y = [y_q | y_k | y_v]
+ * concatenated along N (columns 0..Nq+Nk+Nv-1 of y), in one dispatch whose
+ * down-contraction runs over [W0_q; W0_k; W0_v; Vt_q; Vt_k; Vt_v] and whose
+ * up-projection is block-diagonal in U ("Execution paths", section "The GEMM
+ * formulation", the Q/K/V batching paragraph; section "Precompute-outside" for
+ * the concatenation along the output axis).  Arguments as aq_recon_linear;
+ * ldy >= Nq + Nk + Nv.  Each block may have its own N and r. */
+aq_status aq_recon_qkv_fused(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
+                             const aq_proj p[3], void *y, int64_t ldy, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* Fused gate/up: p[0..1] = (gate, up); y = [y_gate | y_up] along N.  Same
+ * batching as Q/K/V ("Execution paths", section "The GEMM formulation": the MLP
+ * fuses gate and up the same way).  No activation is applied (the pages name
+ * none).  Arguments as aq_recon_linear; ldy >= Ngate + Nup. */
+aq_status aq_recon_gateup_fused(aq_dtype dt, int64_t M, int64_t K, const void *x,
+                                int64_t ldx, const aq_proj p[2], void *y, int64_t ldy,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/* W_eff[N, ldw] (columns 0..K-1) = diag(s) W0 + U Vt, accumulated in fp32 and
+ * rounded once to dt.  "Execution paths", section "Precompute-outside" (the weight
+ * rebuilt once at load) and "How attnquant works", section "The reconstruction
+ * identity".  ldw >= K lets the caller write straight into a row range of a
+ * stacked Q/K/V or gate/up buffer.  bf16: K % 8 == 0, ldw % 8 == 0, W0, Vt and
+ * w_eff 16-byte aligned; f32: K % 4 == 0, ldw % 4 == 0.  No workspace.
+ * For r == 0 (and for s = 1, U = Vt = 0) the result is bit-exact: one rounding
+ * of the exact product s * W0. */
+aq_status aq_materialize_weff(aq_dtype dt, int64_t K, const aq_proj *p, void *w_eff,
+                              int64_t ldw, void *stream);
+
+/* Block-16 FP4 pack of a bf16 weight w[N, ldw] (columns 0..K-1).
+ * Container: "Internals and extension", section "Nvfp4Spec" -- two E2M1 codes per
+ * byte, one FP8-E4M3 scale per 16 K-values in the linear [N, K/16] layout, one
+ * fp32 global scale.  Recipe (the pages give only the container):
+ *   g  = RN_f32(max|w| / 2688) (1 when max|w| == 0), written to *global_scale;
+ *   scale[n, b] = E4M3FN round-to-nearest-even, saturating at 448, of
+ *                 max|w[n, 16b..16b+15]| / (6 g);
+ *   D  = RN_f32(g * scale); code = E2M1 round-to-nearest-even (ties to the even
+ *        code, saturating at 6) of |w| / D, sign bit only on non-zero codes,
+ *        all codes 0 when D == 0;
+ *   packed[n, i] = code[n, 2i] | code[n, 2i+1] << 4.
+ * Every decision is exact (no approximate division), so the output is one bit
+ * pattern.  N >= 1, K % 16 == 0, ldw >= K, ldw % 8 == 0, w 16-byte aligned,
+ * packed [N, K/2] 8-byte aligned (row stride K/2), scales [N, K/16] (row stride
+ * K/16), global_scale: one device float.  ws: aq_workspace_bytes(AQ_OP_FP4, ...)
+ * bytes, 256-byte aligned; no zero-fill needed.  Input must be finite. */
+aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t ldw,
+                               uint8_t *packed, uint8_t *scales, float *global_scale,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace size in bytes for one call.
+ *   AQ_OP_RECON: (dt, M, K, p[0..nproj-1]) exactly as passed to the recon call
+ *                (nproj = 1, 3 or 2).
+ *   AQ_OP_FP4  : M and dt ignored; p[0].N and K are the weight's shape.
+ * Returns 0 for invalid arguments (the call itself then reports why).
+ * Host-only: touches no GPU state. */
+size_t aq_workspace_bytes(aq_op op, aq_dtype dt, int64_t M, int64_t K, const aq_proj *p,
+                          int nproj);
+
+const char *aq_status_string(aq_status s);
+const char *aq_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int aq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AQ_H */

@@ -1,0 +1,239 @@
+// C-ABI front end: argument validation, kernel choice by batch size and dtype,
+// launch on the caller's stream.  Nothing here allocates device memory and
+// nothing synchronises; argument errors are reported before any HIP call.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "aq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+aq_status fail(aq_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMaxM = int64_t(1) << 19;
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+size_t esize(aq_dtype dt) { return dt == AQ_BF16 ? 2 : 4; }
+
+// Validates a recon request and fills `rq`.  `need_ptrs` is false for the
+// workspace-size query (no data pointers are inspected then).
+aq_status build_recon(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
+                      const aq_proj *p, int nproj, void *y, int64_t ldy, bool need_ptrs,
+                      aq::Recon *rq) {
+  if (dt != AQ_F32 && dt != AQ_BF16) return fail(AQ_ERR_INVALID_ARG, "dtype %d is not AQ_F32 or AQ_BF16", (int)dt);
+  if (!p) return fail(AQ_ERR_INVALID_ARG, "projection descriptor pointer is NULL");
+  if (M < 0) return fail(AQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+  if (K < 1) return fail(AQ_ERR_SHAPE, "K = %lld must be >= 1", (long long)K);
+  if (K > kMaxDim) return fail(AQ_ERR_UNSUPPORTED, "K = %lld exceeds 2^24", (long long)K);
+  if (M > kMaxM) return fail(AQ_ERR_UNSUPPORTED, "M = %lld exceeds 2^19", (long long)M);
+  const int64_t kdiv = dt == AQ_BF16 ? 8 : 4;
+  if (K % kdiv) return fail(AQ_ERR_ALIGNMENT, "K = %lld must be a multiple of %lld for this dtype", (long long)K, (long long)kdiv);
+  rq->dt = dt;
+  rq->M = M;
+  rq->K = K;
+  rq->nblk = nproj;
+  int64_t col = 0;
+  for (int b = 0; b < nproj; ++b) {
+    const aq_proj &P = p[b];
+    if (P.N < 1) return fail(AQ_ERR_SHAPE, "projection %d: N = %lld must be >= 1", b, (long long)P.N);
+    if (P.N > kMaxDim) return fail(AQ_ERR_UNSUPPORTED, "projection %d: N = %lld exceeds 2^24", b, (long long)P.N);
+    if (P.N * K > kMaxElems) return fail(AQ_ERR_UNSUPPORTED, "projection %d: N*K exceeds 2^31-1 elements", b);
+    if (P.r < 0) return fail(AQ_ERR_SHAPE, "projection %d: rank %lld is negative", b, (long long)P.r);
+    if (P.r > AQ_MAX_RANK) return fail(AQ_ERR_UNSUPPORTED, "projection %d: rank %lld exceeds the supported maximum %d", b, (long long)P.r, AQ_MAX_RANK);
+    if (need_ptrs) {
+      if (!P.W0 || !P.s) return fail(AQ_ERR_INVALID_ARG, "projection %d: W0 or s is NULL", b);
+      if (P.r > 0 && (!P.U || !P.Vt)) return fail(AQ_ERR_INVALID_ARG, "projection %d: rank %lld but U or Vt is NULL", b, (long long)P.r);
+      if (!aligned(P.W0, 16)) return fail(AQ_ERR_ALIGNMENT, "projection %d: W0 is not 16-byte aligned", b);
+      if (!aligned(P.s, esize(dt))) return fail(AQ_ERR_ALIGNMENT, "projection %d: s is not naturally aligned", b);
+      if (P.r > 0 && !aligned(P.Vt, 16)) return fail(AQ_ERR_ALIGNMENT, "projection %d: Vt is not 16-byte aligned", b);
+      if (P.r > 0 && !aligned(P.U, esize(dt))) return fail(AQ_ERR_ALIGNMENT, "projection %d: U is not naturally aligned", b);
+    }
+    rq->blk[b] = aq::Proj{P.N, P.r, P.W0, P.s, P.U, P.Vt, col};
+    col += P.N;
+  }
+  rq->Ntot = col;
+  if (M == 0) return AQ_OK;
+  if (ldx < K) return fail(AQ_ERR_SHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldx % kdiv) return fail(AQ_ERR_ALIGNMENT, "ldx = %lld must be a multiple of %lld", (long long)ldx, (long long)kdiv);
+  if (ldy < col) return fail(AQ_ERR_SHAPE, "ldy = %lld < total output columns %lld", (long long)ldy, (long long)col);
+  if (M * ldx > kMaxElems || M * ldy > kMaxElems) return fail(AQ_ERR_UNSUPPORTED, "x or y exceeds 2^31-1 elements");
+  if (need_ptrs) {
+    if (!x || !y) return fail(AQ_ERR_INVALID_ARG, "x or y is NULL");
+    if (!aligned(x, 16)) return fail(AQ_ERR_ALIGNMENT, "x is not 16-byte aligned");
+    if (!aligned(y, esize(dt))) return fail(AQ_ERR_ALIGNMENT, "y is not naturally aligned");
+  }
+  rq->x = x;
+  rq->ldx = ldx;
+  rq->y = y;
+  rq->ldy = ldy;
+  return AQ_OK;
+}
+
+// Path choice: fp32 -> generic fp32 kernel; bf16 with M <= 64 and a rank the
+// streaming kernel holds -> decode kernel; otherwise the tiled MFMA kernel.
+enum Path { P_F32, P_DECODE, P_PREFILL };
+
+struct Plan {
+  Path path;
+  aq::DecodePlan dec;
+  aq::PrefillPlan pf;
+  size_t ws;
+};
+
+void make_plan(const aq::Recon &rq, Plan *pl) {
+  pl->ws = 0;
+  if (rq.dt == AQ_F32) {
+    pl->path = P_F32;
+    return;
+  }
+  if (aq::plan_decode(rq, &pl->dec)) {
+    pl->path = P_DECODE;
+    pl->ws = pl->dec.ws_counters + pl->dec.ws_partials;
+    return;
+  }
+  pl->path = P_PREFILL;
+  aq::plan_prefill(rq, &pl->pf);
+  pl->ws = pl->pf.ws_t;
+}
+
+aq_status recon(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx, const aq_proj *p,
+                int nproj, void *y, int64_t ldy, void *ws, size_t ws_bytes, void *stream) {
+  aq::Recon rq;
+  aq_status s = build_recon(dt, M, K, x, ldx, p, nproj, y, ldy, true, &rq);
+  if (s != AQ_OK || M == 0) return s;
+  Plan pl;
+  make_plan(rq, &pl);
+  if (pl.ws > 0) {
+    if (!ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", pl.ws);
+    if (ws_bytes < pl.ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", pl.ws, ws_bytes);
+    if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  switch (pl.path) {
+    case P_F32: e = aq::launch_recon_f32(rq, st); break;
+    case P_DECODE: e = aq::launch_decode(rq, pl.dec, ws, st); break;
+    case P_PREFILL: e = aq::launch_prefill(rq, pl.pf, ws, st); break;
+  }
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return AQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+aq_status aq_recon_linear(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
+                          const aq_proj *p, void *y, int64_t ldy, void *ws, size_t ws_bytes,
+                          void *stream) {
+  return recon(dt, M, K, x, ldx, p, 1, y, ldy, ws, ws_bytes, stream);
+}
+
+aq_status aq_recon_qkv_fused(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
+                             const aq_proj p[3], void *y, int64_t ldy, void *ws,
+                             size_t ws_bytes, void *stream) {
+  return recon(dt, M, K, x, ldx, p, 3, y, ldy, ws, ws_bytes, stream);
+}
+
+aq_status aq_recon_gateup_fused(aq_dtype dt, int64_t M, int64_t K, const void *x,
+                                int64_t ldx, const aq_proj p[2], void *y, int64_t ldy,
+                                void *ws, size_t ws_bytes, void *stream) {
+  return recon(dt, M, K, x, ldx, p, 2, y, ldy, ws, ws_bytes, stream);
+}
+
+aq_status aq_materialize_weff(aq_dtype dt, int64_t K, const aq_proj *p, void *w_eff,
+                              int64_t ldw, void *stream) {
+  if (dt != AQ_F32 && dt != AQ_BF16) return fail(AQ_ERR_INVALID_ARG, "dtype %d is not AQ_F32 or AQ_BF16", (int)dt);
+  if (!p) return fail(AQ_ERR_INVALID_ARG, "projection descriptor pointer is NULL");
+  if (K < 1) return fail(AQ_ERR_SHAPE, "K = %lld must be >= 1", (long long)K);
+  if (K > kMaxDim) return fail(AQ_ERR_UNSUPPORTED, "K = %lld exceeds 2^24", (long long)K);
+  const int64_t kdiv = dt == AQ_BF16 ? 8 : 4;
+  if (K % kdiv) return fail(AQ_ERR_ALIGNMENT, "K = %lld must be a multiple of %lld for this dtype", (long long)K, (long long)kdiv);
+  if (p->N < 1) return fail(AQ_ERR_SHAPE, "N = %lld must be >= 1", (long long)p->N);
+  if (p->N > kMaxDim) return fail(AQ_ERR_UNSUPPORTED, "N = %lld exceeds 2^24", (long long)p->N);
+  if (p->r < 0) return fail(AQ_ERR_SHAPE, "rank %lld is negative", (long long)p->r);
+  if (p->r > AQ_MAX_RANK) return fail(AQ_ERR_UNSUPPORTED, "rank %lld exceeds the supported maximum %d", (long long)p->r, AQ_MAX_RANK);
+  if (ldw < K) return fail(AQ_ERR_SHAPE, "ldw = %lld < K = %lld", (long long)ldw, (long long)K);
+  if (ldw % kdiv) return fail(AQ_ERR_ALIGNMENT, "ldw = %lld must be a multiple of %lld", (long long)ldw, (long long)kdiv);
+  if (p->N * ldw > kMaxElems) return fail(AQ_ERR_UNSUPPORTED, "W_eff exceeds 2^31-1 elements");
+  if (!p->W0 || !p->s || !w_eff) return fail(AQ_ERR_INVALID_ARG, "W0, s or w_eff is NULL");
+  if (p->r > 0 && (!p->U || !p->Vt)) return fail(AQ_ERR_INVALID_ARG, "rank %lld but U or Vt is NULL", (long long)p->r);
+  if (!aligned(p->W0, 16) || !aligned(w_eff, 16)) return fail(AQ_ERR_ALIGNMENT, "W0 and w_eff must be 16-byte aligned");
+  if (p->r > 0 && !aligned(p->Vt, 16)) return fail(AQ_ERR_ALIGNMENT, "Vt must be 16-byte aligned");
+  if (!aligned(p->s, esize(dt)) || (p->r > 0 && !aligned(p->U, esize(dt)))) return fail(AQ_ERR_ALIGNMENT, "s or U is not naturally aligned");
+  aq::Proj P{p->N, p->r, p->W0, p->s, p->U, p->Vt, 0};
+  hipError_t e = aq::launch_materialize(dt, K, P, w_eff, ldw, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return AQ_OK;
+}
+
+aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t ldw,
+                               uint8_t *packed, uint8_t *scales, float *global_scale,
+                               void *ws, size_t ws_bytes, void *stream) {
+  if (N < 1) return fail(AQ_ERR_SHAPE, "N = %lld must be >= 1", (long long)N);
+  if (K < 16) return fail(AQ_ERR_SHAPE, "K = %lld must be >= 16", (long long)K);
+  if (N > kMaxDim || K > kMaxDim) return fail(AQ_ERR_UNSUPPORTED, "N or K exceeds 2^24");
+  if (K % 16) return fail(AQ_ERR_ALIGNMENT, "K = %lld must be a multiple of 16", (long long)K);
+  if (ldw < K) return fail(AQ_ERR_SHAPE, "ldw = %lld < K = %lld", (long long)ldw, (long long)K);
+  if (ldw % 8) return fail(AQ_ERR_ALIGNMENT, "ldw = %lld must be a multiple of 8", (long long)ldw);
+  if (N * ldw > kMaxElems) return fail(AQ_ERR_UNSUPPORTED, "weight exceeds 2^31-1 elements");
+  if (!w_bf16 || !packed || !scales || !global_scale) return fail(AQ_ERR_INVALID_ARG, "a data pointer is NULL");
+  if (!aligned(w_bf16, 16)) return fail(AQ_ERR_ALIGNMENT, "w is not 16-byte aligned");
+  if (!aligned(packed, 8)) return fail(AQ_ERR_ALIGNMENT, "packed is not 8-byte aligned");
+  if (!aligned(global_scale, 4)) return fail(AQ_ERR_ALIGNMENT, "global_scale is not 4-byte aligned");
+  const size_t need = (size_t)aq::kFp4AmaxBlocks * 4;
+  if (!ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (ws_bytes < need) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
+  if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  hipError_t e = aq::launch_fp4(N, K, w_bf16, ldw, packed, scales, global_scale, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return AQ_OK;
+}
+
+size_t aq_workspace_bytes(aq_op op, aq_dtype dt, int64_t M, int64_t K, const aq_proj *p,
+                          int nproj) {
+  if (op == AQ_OP_FP4) return (size_t)aq::kFp4AmaxBlocks * 4;
+  if (op != AQ_OP_RECON || nproj < 1 || nproj > aq::kMaxBlocks || !p) return 0;
+  int64_t ntot = 0;
+  for (int b = 0; b < nproj; ++b) ntot += p[b].N > 0 ? p[b].N : 0;
+  aq::Recon rq;
+  if (build_recon(dt, M, K, nullptr, K, p, nproj, nullptr, ntot, false, &rq) != AQ_OK) return 0;
+  if (M == 0) return 0;
+  rq.ldx = K;
+  rq.ldy = rq.Ntot;
+  Plan pl;
+  make_plan(rq, &pl);
+  return pl.ws;
+}
+
+const char *aq_status_string(aq_status s) {
+  switch (s) {
+    case AQ_OK: return "AQ_OK";
+    case AQ_ERR_INVALID_ARG: return "AQ_ERR_INVALID_ARG";
+    case AQ_ERR_SHAPE: return "AQ_ERR_SHAPE";
+    case AQ_ERR_ALIGNMENT: return "AQ_ERR_ALIGNMENT";
+    case AQ_ERR_UNSUPPORTED: return "AQ_ERR_UNSUPPORTED";
+    case AQ_ERR_WORKSPACE: return "AQ_ERR_WORKSPACE";
+    case AQ_ERR_HIP: return "AQ_ERR_HIP";
+  }
+  return "AQ_ERR_UNKNOWN";
+}
+
+const char *aq_last_error(void) { return g_err; }
+
+int aq_version(void) { return 100; }
+
+}  // extern "C"

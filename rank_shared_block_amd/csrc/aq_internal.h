@@ -1,0 +1,69 @@
+// Internal interface between the C-ABI front end (aq_api.hip) and the kernels.
+// Host-side plan structures: everything here is validated before it is built.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/aq.h"
+
+namespace aq {
+
+constexpr int kMaxBlocks = 3;     // Q/K/V
+constexpr int kNumCU = 256;       // MI355X: 256 CUs in 8 XCDs of 32
+constexpr int kNumXCD = 8;
+constexpr int kDecodeMaxM = 64;   // largest batch served by the streaming kernel
+
+// One projection of a (possibly fused) dispatch, host view.
+struct Proj {
+  int64_t N, r;
+  const void *W0, *s, *U, *Vt;
+  int64_t col;   // first output column of this block inside y
+};
+
+// A validated reconstruction request.
+struct Recon {
+  aq_dtype dt;
+  int64_t M, K, ldx, ldy, Ntot;
+  const void *x;
+  void *y;
+  int nblk;
+  Proj blk[kMaxBlocks];
+};
+
+// ---- decode (streaming, M <= kDecodeMaxM, bf16) ---------------------------
+struct DecodePlan {
+  int MT;          // 16-token groups: 1, 2 or 4
+  int NG;          // 16-row groups per workgroup (Vt groups + W0 groups)
+  int S;           // K splits across workgroups
+  int kchunk;      // K elements per split (multiple of 128)
+  int ntiles;      // row tiles over all blocks
+  int tile0[kMaxBlocks], ntile[kMaxBlocks], vg[kMaxBlocks];
+  size_t ws_counters, ws_partials;   // bytes
+};
+bool plan_decode(const Recon &rq, DecodePlan *pl);
+hipError_t launch_decode(const Recon &rq, const DecodePlan &pl, void *ws, hipStream_t st);
+
+// ---- prefill (MFMA tiles, bf16) ---------------------------------------------
+struct PrefillPlan {
+  int ldt;                          // columns of the t buffer (sum of r rounded to 16)
+  int tcol[kMaxBlocks];
+  size_t ws_t;                      // bytes of the t buffer
+};
+void plan_prefill(const Recon &rq, PrefillPlan *pl);
+hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipStream_t st);
+
+// ---- fp32 (any M) -------------------------------------------------------------
+hipError_t launch_recon_f32(const Recon &rq, hipStream_t st);
+
+// ---- materialise ----------------------------------------------------------------
+hipError_t launch_materialize(aq_dtype dt, int64_t K, const Proj &p, void *w, int64_t ldw,
+                              hipStream_t st);
+
+// ---- FP4 pack -------------------------------------------------------------------
+constexpr int kFp4AmaxBlocks = 1024;
+hipError_t launch_fp4(int64_t N, int64_t K, const void *w, int64_t ldw, uint8_t *packed,
+                      uint8_t *scales, float *gscale, void *ws, hipStream_t st);
+
+}  // namespace aq

@@ -1,0 +1,151 @@
+// Block-16 FP4 pack of a bf16 effective weight.
+//
+// Container: "Internals and extension", section "Nvfp4Spec" (two E2M1 codes per
+// byte, one FP8-E4M3 scale per 16 K-values in the linear [N, K/16] layout, one
+// fp32 global scale); "Execution paths", section "Precompute-outside" quantises
+// each W_eff at load.  The recipe (the pages give only the container):
+//   g     = RN_f32(A / 2688), A = max|w| (g = 1 when A == 0)
+//   scale = E4M3FN(max|block| / (6 g)), round to nearest even, saturating at 448
+//   D     = RN_f32(g * scale)
+//   code  = E2M1 nearest to |w| / D, ties to the even code, saturating at 6;
+//           sign bit only on non-zero codes; all zero when D == 0
+//   byte  = code[2i] | code[2i+1] << 4
+//
+// Two passes over HBM:
+//   1. amax: max |w| per workgroup as an integer max over the 15 magnitude bits
+//      of the bf16 patterns (exact and order-independent); partials to ws.
+//   2. pack: every workgroup folds the partials to A (a few KB from L2), derives
+//      g, and packs one 16-value block per thread (2 x 16-byte loads, one 8-byte
+//      store of codes, one scale byte).
+//
+// Exactness without a per-element division: the block-scale quotient is formed
+// by a correctly rounded fp64 division (which cannot cross an E4M3 rounding
+// boundary: the quotient of an 8-bit by a <= 26-bit significand is either exactly
+// a midpoint or far from every midpoint relative to fp64's precision), and the
+// element codes come from comparing |w| with the seven E2M1 midpoints times D,
+// products that are exact in fp64.  Equality with a midpoint selects the even code.
+
+#include "aq_internal.h"
+#include "device_common.h"
+
+namespace aq {
+
+__global__ __launch_bounds__(256) void k_fp4_amax(const uint16_t *w, int N, int K, int ldw,
+                                                  unsigned *partial) {
+  const int k8 = K >> 3;
+  const long nchunks = (long)N * k8;
+  unsigned m = 0;
+  for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += (long)gridDim.x * 256) {
+    const long n = c / k8;
+    const int kk = (int)(c - n * k8) * 8;
+    const uint4 v = ld16(w + n * ldw + kk);
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m = max(m, q[i] & 0x7FFFu);
+      m = max(m, (q[i] >> 16) & 0x7FFFu);
+    }
+  }
+  __shared__ unsigned red[256];
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+// E4M3FN bits of a finite q >= 0: round to nearest even, saturate at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(double q) {
+  if (!(q > 0.0)) return 0u;
+  if (q >= 448.0) return 0x7Eu;
+  int e;
+  (void)frexp(q, &e);                           // q in [2^(e-1), 2^e)
+  const int qexp = e - 4 > -9 ? e - 4 : -9;     // 3 fraction bits; subnormal step 2^-9
+  const double n = rint(ldexp(q, -qexp));       // ties to even
+  const int ni = (int)n;
+  uint32_t bits = qexp == -9 ? (uint32_t)ni : (uint32_t)(((e + 6) << 3) + ni - 8);
+  return bits > 0x7Eu ? 0x7Eu : bits;
+}
+
+__device__ __forceinline__ double e4m3_value(uint32_t b) {
+  return b < 8 ? ldexp((double)b, -9) : ldexp((double)(8 + (b & 7)), (int)(b >> 3) - 10);
+}
+
+__global__ __launch_bounds__(256) void k_fp4_pack(const uint16_t *w, int N, int K, int ldw,
+                                                  const unsigned *partial, int npartial,
+                                                  uint8_t *packed, uint8_t *scales,
+                                                  float *gscale) {
+  __shared__ unsigned red[256];
+  unsigned m = 0;
+  for (int i = threadIdx.x; i < npartial; i += 256) m = max(m, partial[i]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  const float A = bf2f((uint16_t)red[0]);
+  const float g = A == 0.f ? 1.0f : (float)((double)A / 2688.0);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = g;
+
+  const int kb = K >> 4;
+  const long nblocks = (long)N * kb;
+  for (long blk = (long)blockIdx.x * 256 + threadIdx.x; blk < nblocks; blk += (long)gridDim.x * 256) {
+    const long n = blk / kb;
+    const int b = (int)(blk - n * kb);
+    const uint16_t *src = w + n * ldw + b * 16;
+    const uint4 v0 = ld16(src), v1 = ld16(src + 8);
+    const uint32_t q[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t amag = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      amag = max(amag, q[i] & 0x7FFFu);
+      amag = max(amag, (q[i] >> 16) & 0x7FFFu);
+    }
+    const double ab = (double)bf2f((uint16_t)amag);
+    const uint32_t sf = e4m3_rne_sat(ab / (6.0 * (double)g));
+    const float D = (float)((double)g * e4m3_value(sf));
+    uint32_t lo = 0, hi = 0;
+    if (D > 0.f) {
+      const double d = (double)D;
+      const double t0 = 0.25 * d, t1 = 0.75 * d, t2 = 1.25 * d, t3 = 1.75 * d, t4 = 2.5 * d,
+                   t5 = 3.5 * d, t6 = 5.0 * d;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t bits = (q[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+        const double x = (double)bf2f((uint16_t)(bits & 0x7FFFu));
+        // Code = number of midpoints below |w|; at an exact midpoint between codes
+        // c and c+1 the even one wins (odd c steps up, even c stays).
+        uint32_t c = (x > t0) + (x >= t1) + (x > t2) + (x >= t3) + (x > t4) + (x >= t5) + (x > t6);
+        if (c != 0 && (bits & 0x8000u)) c |= 8u;
+        if (i < 8)
+          lo |= c << (4 * i);
+        else
+          hi |= c << (4 * (i - 8));
+      }
+    }
+    *reinterpret_cast<uint2 *>(packed + n * (K >> 1) + b * 8) = make_uint2(lo, hi);
+    scales[n * kb + b] = (uint8_t)sf;
+  }
+}
+
+hipError_t launch_fp4(int64_t N, int64_t K, const void *w, int64_t ldw, uint8_t *packed,
+                      uint8_t *scales, float *gscale, void *ws, hipStream_t st) {
+  const long nchunks = (long)N * (K / 8);
+  int g1 = (int)((nchunks + 255) / 256);
+  g1 = g1 < kFp4AmaxBlocks ? g1 : kFp4AmaxBlocks;
+  hipLaunchKernelGGL(k_fp4_amax, dim3(g1), dim3(256), 0, st, (const uint16_t *)w, (int)N,
+                     (int)K, (int)ldw, (unsigned *)ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long nblocks = (long)N * (K / 16);
+  long g2 = (nblocks + 255) / 256;
+  g2 = g2 < 8L * kNumCU * 4 ? g2 : 8L * kNumCU * 4;
+  hipLaunchKernelGGL(k_fp4_pack, dim3((unsigned)g2), dim3(256), 0, st, (const uint16_t *)w,
+                     (int)N, (int)K, (int)ldw, (const unsigned *)ws, g1, packed, scales, gscale);
+  return hipGetLastError();
+}
+
+}  // namespace aq

@@ -1,0 +1,344 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU fp64 oracle on
+the same seeded inputs.  Small shapes span several tiles and ragged tails; the
+workload shapes are checked in full (decode) or on sampled tokens and output
+columns (prefill, large decoder)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rank_shared_block_amd import binding as B
+from rank_shared_block_amd import inputs as I
+from helpers import (assert_parity, bundle_np, bundle_up, dev, down, rel_err, sub_bundle, up)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    d = dev()
+    B.lib()
+    assert len(B.hip_runtimes_mapped()) == 1, B.hip_runtimes_mapped()
+    torch.cuda.synchronize(d)
+    yield
+
+
+def _single(M, K, N, r, dtype, variant="normal", layer=0, tag=0):
+    bd = I.bundle("test", layer, "q", K, N, r, dtype, variant=variant)
+    x = I.activations("test", tag, M, K, dtype)
+    return bd, x
+
+
+# ------------------------------------------------------------- fp32 (C1)
+
+@pytest.mark.parametrize("variant", ["normal", "r0", "passthrough", "s0"])
+def test_single_projection_f32(variant):
+    bd = I.bundle("single_f32", 0, "q", 256, 256, 4, "f32", variant=variant)
+    x = I.activations("single_f32", 0, 8, 256, "f32")
+    y = B.recon_linear(up(x, "f32"), bundle_up(bd, "f32"))
+    ref = oracle.recon_linear(x, *bundle_np(bd))
+    assert_parity(down(y), ref, "f32", variant)
+    w = B.materialize(bundle_up(bd, "f32"))
+    wref = oracle.materialize(*bundle_np(bd))
+    if variant in ("r0", "passthrough"):
+        assert np.array_equal(down(w), oracle.rne_f32(wref))      # one rounding: bit-exact
+    else:
+        assert_parity(down(w), wref, "f32", "materialize " + variant)
+
+
+@pytest.mark.parametrize("M", [1, 5, 17, 40])
+def test_f32_ragged(M):
+    bd, x = _single(M, 132, 70, 9, "f32")
+    y = B.recon_linear(up(x, "f32"), bundle_up(bd, "f32"))
+    assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "f32")
+
+
+# ------------------------------------------------------------- bf16 recon, small
+
+@pytest.mark.parametrize("M", [1, 3, 5, 16, 17, 33, 64, 65, 130, 300])
+@pytest.mark.parametrize("variant", ["normal", "s0"])
+def test_bf16_batch_sizes(M, variant):
+    """Every batch bucket (streaming 16/32/64-token kernels, tiled MFMA beyond)
+    with a ragged N (200), a K that is not a tile multiple (1048) and r = 24."""
+    bd, x = _single(M, 1048, 200, 24, "bf16", variant=variant, tag=M)
+    y = B.recon_linear(up(x, "bf16"), bundle_up(bd, "bf16"))
+    assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"M={M} {variant}")
+
+
+@pytest.mark.parametrize("r", [0, 5, 16, 40, 100, 256])
+@pytest.mark.parametrize("M", [4, 200])
+def test_bf16_ranks(r, M):
+    bd, x = _single(M, 512, 160, r, "bf16", variant="s0" if r else "normal", layer=r, tag=r)
+    y = B.recon_linear(up(x, "bf16"), bundle_up(bd, "bf16"))
+    assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"r={r} M={M}")
+
+
+def test_bf16_rank0_and_passthrough_agree():
+    """Passthrough (s = 1, U = Vt = 0) and r = 0 with s = 1 give the same bits, and
+    both are within tolerance of x W^T."""
+    M, K, N = 16, 1024, 300
+    bd = I.bundle("test", 7, "o", K, N, 16, "bf16", variant="passthrough")
+    x = up(I.activations("test", 7, M, K, "bf16"), "bf16")
+    W0, s, U, Vt = bundle_up(bd, "bf16")
+    y_pt = B.recon_linear(x, (W0, s, U, Vt))
+    y_r0 = B.recon_linear(x, (W0, s, None, None))
+    ref = down(x) @ bd["W0"].astype(np.float64).T
+    assert_parity(down(y_pt), ref, "bf16", "passthrough")
+    assert_parity(down(y_r0), ref, "bf16", "r0")
+
+
+@pytest.mark.parametrize("M", [1, 16, 40, 300])
+def test_fused_qkv_small(M):
+    K = 264
+    shapes = [(96, 8), (40, 16), (24, 0)]
+    bds = [I.bundle("test", 1, f, K, n, r, "bf16") for f, (n, r) in zip(("q", "k", "v"), shapes)]
+    x = I.activations("test", 100 + M, M, K, "bf16")
+    y = B.recon_qkv(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+    ref = oracle.recon_fused(x, [bundle_np(b) for b in bds])
+    assert y.shape == (M, 160)
+    assert_parity(down(y), ref, "bf16", f"qkv M={M}")
+    # block-diagonal: each block's columns equal the single-projection call
+    col = 0
+    for b in bds:
+        n = b["W0"].shape[0]
+        assert_parity(down(y)[:, col:col + n], oracle.recon_linear(x, *bundle_np(b)), "bf16")
+        col += n
+
+
+@pytest.mark.parametrize("M", [1, 16, 33, 130])
+def test_fused_gateup_small(M):
+    K = 384
+    bds = [I.bundle("test", 2, f, K, 272, 24, "bf16", variant="s0") for f in ("gate", "up")]
+    x = I.activations("test", 200 + M, M, K, "bf16")
+    y = B.recon_gateup(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+    assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in bds]), "bf16")
+
+
+@pytest.mark.parametrize("M", [3, 100])
+def test_strided_x_and_y(M):
+    """ldx > K and ldy > N: only the addressed columns are written."""
+    K, N = 256, 48
+    bd, x = _single(M, K, N, 8, "bf16", tag=300 + M)
+    xb = torch.zeros((M, K + 24), dtype=torch.bfloat16, device=dev())
+    xb[:, :K] = up(x, "bf16")
+    yb = torch.full((M, N + 40), 7.0, dtype=torch.bfloat16, device=dev())
+    B.recon_linear(xb[:, :K], bundle_up(bd, "bf16"), y=yb[:, 8:8 + N])
+    got = down(yb)
+    assert np.all(got[:, :8] == 7.0) and np.all(got[:, 8 + N:] == 7.0)
+    assert_parity(got[:, 8:8 + N], oracle.recon_linear(x, *bundle_np(bd)), "bf16")
+
+
+def test_empty_batch_is_noop():
+    bd, _ = _single(1, 128, 32, 4, "bf16")
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device=dev())
+    y = B.recon_linear(x, bundle_up(bd, "bf16"))
+    assert y.shape == (0, 32)
+
+
+def test_deterministic_and_workspace_reuse():
+    """Repeated calls give identical bits; calls of different shapes share one
+    workspace (its split-K counters reset themselves)."""
+    K = 6912
+    bd = I.bundle("test", 3, "down", K, 1152, 16, "bf16")
+    W = bundle_up(bd, "bf16")
+    outs = []
+    for M in (1, 16, 1, 16, 7):
+        x = up(I.activations("test", 400 + M, M, K, "bf16"), "bf16")
+        outs.append((M, B.recon_linear(x, W)))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][1], outs[2][1]) and torch.equal(outs[1][1], outs[3][1])
+    for M, y in outs:
+        x = I.activations("test", 400 + M, M, K, "bf16")
+        assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"M={M}")
+
+
+# ------------------------------------------------------------- workload shapes
+
+def _layer_dispatches(shapes, layer_bd):
+    for name, fams in I.LAYER_DISPATCHES:
+        K = shapes[fams[0]][0]
+        yield name, fams, K, [layer_bd[f] for f in fams]
+
+
+def _run_dispatch(name, x_dev, bds_dev):
+    if name == "qkv":
+        return B.recon_qkv(x_dev, bds_dev)
+    if name == "gateup":
+        return B.recon_gateup(x_dev, bds_dev)
+    return B.recon_linear(x_dev, bds_dev[0])
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_gemma_decode_layer_full(M):
+    lb = I.layer_bundles("gemma_decode", I.GEMMA_1B, layers=1, r=16, dtype="bf16")[0]
+    for name, fams, K, bds in _layer_dispatches(I.GEMMA_1B, lb):
+        x = I.activations("gemma_decode", 10 * M + len(name), M, K, "bf16")
+        y = _run_dispatch(name, up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+        ref = oracle.recon_fused(x, [bundle_np(b) for b in bds])
+        assert_parity(down(y), ref, "bf16", f"gemma decode {name} M={M}")
+
+
+@pytest.mark.parametrize("M", [512, 2048])
+def test_gemma_prefill_layer_sampled(M):
+    lb = I.layer_bundles("gemma_prefill", I.GEMMA_1B, layers=1, r=64, dtype="bf16")[0]
+    rng = np.random.default_rng(M)
+    rows = np.sort(rng.choice(M, 48, replace=False))
+    for name, fams, K, bds in _layer_dispatches(I.GEMMA_1B, lb):
+        x = I.activations("gemma_prefill", M + len(name), M, K, "bf16")
+        y = down(_run_dispatch(name, up(x, "bf16"), [bundle_up(b, "bf16") for b in bds]))
+        ref = oracle.recon_fused(x[rows], [bundle_np(b) for b in bds])
+        assert_parity(y[rows], ref, "bf16", f"gemma prefill {name} M={M}")
+        assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("M", [1, 32, 512])
+def test_large_decoder_banded_sampled(M):
+    """Two layers of one W0 band (per-layer s, U, Vt): sampled tokens x sampled
+    output columns of every dispatch."""
+    lbs = I.layer_bundles("large_decoder", I.LARGE_DECODER, layers=2, r=32, dtype="bf16",
+                          num_bands=1)
+    rng = np.random.default_rng(1000 + M)
+    rows = np.sort(rng.choice(M, min(M, 16), replace=False))
+    for layer in (0, 1):
+        for name, fams, K, bds in _layer_dispatches(I.LARGE_DECODER, lbs[layer]):
+            x = I.activations("large_decoder", 7 * M + 3 * layer + len(name), M, K, "bf16")
+            y = down(_run_dispatch(name, up(x, "bf16"), [bundle_up(b, "bf16") for b in bds]))
+            col0, cols_all, refs = 0, [], []
+            for b in bds:
+                n = b["W0"].shape[0]
+                cols = np.sort(rng.choice(n, 192, replace=False))
+                refs.append(oracle.recon_linear(x[rows], *sub_bundle(b, cols)))
+                cols_all.append(col0 + cols)
+                col0 += n
+            got = y[np.ix_(rows, np.concatenate(cols_all))]
+            assert_parity(got, np.concatenate(refs, axis=1), "bf16", f"large {name} L{layer} M={M}")
+            assert np.all(np.isfinite(y))
+        torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------- materialise
+
+@pytest.mark.parametrize("N,K,r", [(70, 136, 0), (70, 136, 7), (130, 1048, 16), (200, 520, 64),
+                                   (64, 256, 100), (33, 64, 256)])
+def test_materialize_bf16(N, K, r):
+    bd = I.bundle("test", 5, "up", K, N, r, "bf16")
+    w = B.materialize(bundle_up(bd, "bf16"))
+    ref = oracle.materialize(*bundle_np(bd))
+    if r == 0:
+        assert np.array_equal(down(w), oracle.rne_bf16(ref))
+    else:
+        assert_parity(down(w), ref, "bf16", f"materialize N={N} K={K} r={r}")
+
+
+def test_materialize_passthrough_bit_exact_and_strided():
+    N, K = 96, 264
+    bd = I.bundle("test", 6, "gate", K, N, 16, "bf16", variant="passthrough")
+    stacked = torch.full((N + 10, K + 40), -3.0, dtype=torch.bfloat16, device=dev())
+    B.materialize(bundle_up(bd, "bf16"), out=stacked[5:5 + N, :])
+    got = down(stacked)
+    assert np.array_equal(got[5:5 + N, :K], bd["W0"].astype(np.float64))
+    assert np.all(got[5:5 + N, K:] == -3.0) and np.all(got[:5] == -3.0) and np.all(got[5 + N:] == -3.0)
+
+
+@pytest.mark.parametrize("fam", ["q", "gate", "down"])
+def test_materialize_gemma_r64(fam):
+    K, N = I.GEMMA_1B[fam]
+    bd = I.bundle("materialize_fp4", 0, fam, K, N, 64, "bf16")
+    w = B.materialize(bundle_up(bd, "bf16"))
+    assert_parity(down(w), oracle.materialize(*bundle_np(bd)), "bf16", f"materialize {fam}")
+
+
+# ------------------------------------------------------------- FP4 pack
+
+def _fp4_check(w_dev):
+    p, s, g = B.quant_fp4_block16(w_dev)
+    ep, es, eg = oracle.fp4_pack(down(w_dev))
+    assert float(g.cpu()[0]) == eg
+    assert np.array_equal(s.cpu().numpy(), es)
+    assert np.array_equal(p.cpu().numpy(), ep)
+
+
+@pytest.mark.parametrize("N,K", [(1, 16), (37, 48), (130, 1056)])
+def test_fp4_small(N, K):
+    bd = I.bundle("test", 8, "v", K, N, 8, "bf16")
+    w = B.materialize(bundle_up(bd, "bf16"))
+    _fp4_check(w)
+
+
+def test_fp4_edge_blocks():
+    """All-zero rows and blocks, blocks far below the global max (subnormal and
+    zero E4M3 scales), exact E2M1 midpoints, negative zeros."""
+    rng = np.random.default_rng(9)
+    W = rng.standard_normal((8, 64)).astype(np.float32)
+    W[1] = 0.0
+    W[2, :16] *= 1e-6
+    W[3, 16:32] *= 1e-12
+    W[4, :16] = -0.0
+    W[5] = 0.0
+    W[5, 0] = 10.5                      # this row: exact grid, ties at D = 1.75
+    W[5, 1:8] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]) * 1.75
+    W[0, 0] = 40.0                      # global max
+    w = torch.from_numpy(W).to(torch.bfloat16).to(dev())
+    _fp4_check(w)
+    z = torch.zeros((4, 32), dtype=torch.bfloat16, device=dev())
+    p, s, g = B.quant_fp4_block16(z)
+    assert float(g.cpu()[0]) == 1.0 and not p.any() and not s.any()
+
+
+@pytest.mark.parametrize("fam", ["k", "down"])
+def test_fp4_gemma_full(fam):
+    K, N = I.GEMMA_1B[fam]
+    bd = I.bundle("materialize_fp4", 1, fam, K, N, 64, "bf16")
+    _fp4_check(B.materialize(bundle_up(bd, "bf16")))
+
+
+def test_fp4_strided_source():
+    N, K = 40, 96
+    bd = I.bundle("test", 9, "o", K, N, 4, "bf16")
+    big = torch.zeros((N, K + 32), dtype=torch.bfloat16, device=dev())
+    B.materialize(bundle_up(bd, "bf16"), out=big)
+    p, s, g = B.quant_fp4_block16(big[:, :K])
+    ep, es, eg = oracle.fp4_pack(down(big[:, :K]))
+    assert np.array_equal(p.cpu().numpy(), ep) and np.array_equal(s.cpu().numpy(), es)
+
+
+# ------------------------------------------------------------- HIP graph capture
+
+def test_graph_capture_replays_match_eager():
+    """Decode (split-K counters in the workspace) and prefill (t buffer) calls
+    captured in one graph: every replay, with eager work and synchronisations in
+    between, reproduces the eager result bit for bit."""
+    d = dev()
+    bd_dec = I.bundle("test", 11, "down", 6912, 1152, 16, "bf16")
+    bd_pf = I.bundle("test", 12, "q", 1152, 1024, 64, "bf16")
+    Wd, Wp = bundle_up(bd_dec, "bf16"), bundle_up(bd_pf, "bf16")
+    xd = up(I.activations("test", 500, 16, 6912, "bf16"), "bf16")
+    xp = up(I.activations("test", 501, 300, 1152, "bf16"), "bf16")
+    ws = B.Workspace()
+    yd = B.recon_linear(xd, Wd, workspace=ws)
+    yp = B.recon_linear(xp, Wp, workspace=ws)
+    torch.cuda.synchronize()
+    eager_d, eager_p = yd.clone(), yp.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.recon_linear(xd, Wd, y=yd, workspace=ws)
+        B.recon_linear(xp, Wp, y=yp, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.recon_linear(xd, Wd, y=yd, workspace=ws)
+        B.recon_linear(xp, Wp, y=yp, workspace=ws)
+    for rep in range(4):
+        yd.zero_()
+        yp.zero_()
+        B.recon_linear(xd[:3], Wd, workspace=ws)          # eager work on the same workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yd, eager_d), f"decode replay {rep}"
+        assert torch.equal(yp, eager_p), f"prefill replay {rep}"
+    assert_parity(down(eager_d), oracle.recon_linear(I.activations("test", 500, 16, 6912, "bf16"),
+                                                    *bundle_np(bd_dec)), "bf16")

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI: the library loads, exports every function that
+include/aq.h declares, and rejects bad arguments with the documented status
+before touching the GPU.  No kernel is launched here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_shared_block_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aq.h")
+
+FAKE = 0x10000          # a plausible, 256-byte aligned "device pointer" (never dereferenced)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(aq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    names = _declared()
+    assert {"aq_recon_linear", "aq_recon_qkv_fused", "aq_recon_gateup_fused",
+            "aq_materialize_weff", "aq_quant_fp4_block16", "aq_workspace_bytes",
+            "aq_status_string", "aq_last_error", "aq_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_single_hip_runtime_in_process():
+    B.lib()
+    maps = B.hip_runtimes_mapped()
+    assert len(maps) == 1, maps
+
+
+def test_status_strings_and_version():
+    assert B.status_string(B.AQ_ERR_SHAPE) == "AQ_ERR_SHAPE"
+    assert B.status_string(99) == "AQ_ERR_UNKNOWN"
+    assert B.version() >= 100
+
+
+def _proj(N=64, r=4, W0=FAKE, s=FAKE, U=FAKE, Vt=FAKE):
+    return B.aq_proj(N, r, W0, s, U, Vt)
+
+
+def _call(**kw):
+    a = dict(dt=B.AQ_BF16, M=4, K=128, x=FAKE, ldx=128, p=_proj(), y=FAKE, ldy=64,
+             ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return B.aq_recon_linear(a["dt"], a["M"], a["K"], a["x"], a["ldx"], a["p"], a["y"],
+                             a["ldy"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dt=7), B.AQ_ERR_INVALID_ARG, "dtype"),
+    (dict(M=-1), B.AQ_ERR_INVALID_ARG, "negative"),
+    (dict(K=0), B.AQ_ERR_SHAPE, "K = 0"),
+    (dict(K=100, ldx=100), B.AQ_ERR_ALIGNMENT, "multiple of 8"),
+    (dict(ldx=64), B.AQ_ERR_SHAPE, "ldx"),
+    (dict(ldx=132), B.AQ_ERR_ALIGNMENT, "ldx"),
+    (dict(ldy=63), B.AQ_ERR_SHAPE, "ldy"),
+    (dict(p=_proj(N=0)), B.AQ_ERR_SHAPE, "N = 0"),
+    (dict(p=_proj(r=-1)), B.AQ_ERR_SHAPE, "negative"),
+    (dict(p=_proj(r=257)), B.AQ_ERR_UNSUPPORTED, "rank 257"),
+    (dict(p=_proj(U=None)), B.AQ_ERR_INVALID_ARG, "U or Vt"),
+    (dict(p=_proj(W0=FAKE + 8)), B.AQ_ERR_ALIGNMENT, "W0"),
+    (dict(p=_proj(Vt=FAKE + 2)), B.AQ_ERR_ALIGNMENT, "Vt"),
+    (dict(x=FAKE + 4), B.AQ_ERR_ALIGNMENT, "x is not"),
+    (dict(x=None), B.AQ_ERR_INVALID_ARG, "x or y"),
+    (dict(K=1 << 25, ldx=1 << 25), B.AQ_ERR_UNSUPPORTED, "2^24"),
+    (dict(ws=None), B.AQ_ERR_WORKSPACE, "workspace"),
+    (dict(ws_bytes=16), B.AQ_ERR_WORKSPACE, "workspace"),
+    (dict(ws=FAKE + 64), B.AQ_ERR_WORKSPACE, "256-byte"),
+])
+def test_recon_argument_errors(kw, status, needle):
+    assert _call(**kw) == status
+    assert needle in B.last_error()
+
+
+def test_rank_zero_allows_null_factors_and_empty_batch_is_noop():
+    # M == 0 is a no-op: AQ_OK without touching x, y or the GPU
+    assert _call(M=0, x=None, y=None, p=_proj(r=0, U=None, Vt=None)) == B.AQ_OK
+    assert _call(M=0, x=None, y=None) == B.AQ_OK
+
+
+def test_fused_calls_validate_every_block():
+    ps = [_proj(N=64), _proj(N=16, r=300), _proj(N=16)]
+    st = B.aq_recon_qkv_fused(B.AQ_BF16, 4, 128, FAKE, 128, ps, FAKE, 96, FAKE, 1 << 20, None)
+    assert st == B.AQ_ERR_UNSUPPORTED and "projection 1" in B.last_error()
+    ps = [_proj(N=64), _proj(N=64)]
+    st = B.aq_recon_gateup_fused(B.AQ_BF16, 4, 128, FAKE, 128, ps, FAKE, 127, FAKE, 1 << 20, None)
+    assert st == B.AQ_ERR_SHAPE and "ldy" in B.last_error()
+
+
+def test_workspace_query_is_host_only():
+    p1 = [_proj(N=1024, r=16)]
+    ws_dec = B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 16, 1152, p1, 1)
+    assert ws_dec % 256 == 0 and ws_dec > 0
+    # prefill: a bf16 t buffer of M x (r rounded to 16)
+    ws_pf = B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 512, 1152, p1, 1)
+    assert ws_pf == 512 * 16 * 2
+    assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_F32, 8, 256, [_proj(N=256)], 1) == 0
+    assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 0, 1152, p1, 1) == 0
+    assert B.aq_workspace_bytes(B.AQ_OP_FP4, B.AQ_BF16, 0, 1152, p1, 1) == 4096
+    assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 4, 100, p1, 1) == 0   # invalid K
+
+
+def test_materialize_argument_errors():
+    def mat(**kw):
+        a = dict(dt=B.AQ_BF16, K=128, p=_proj(), w=FAKE, ldw=128)
+        a.update(kw)
+        return B.aq_materialize_weff(a["dt"], a["K"], a["p"], a["w"], a["ldw"], None)
+    assert mat(ldw=120) == B.AQ_ERR_SHAPE
+    assert mat(ldw=132) == B.AQ_ERR_ALIGNMENT
+    assert mat(K=12, ldw=16) == B.AQ_ERR_ALIGNMENT
+    assert mat(p=_proj(r=300)) == B.AQ_ERR_UNSUPPORTED
+    assert mat(w=None) == B.AQ_ERR_INVALID_ARG
+    assert mat(w=FAKE + 8) == B.AQ_ERR_ALIGNMENT
+
+
+def test_fp4_argument_errors():
+    def q(**kw):
+        a = dict(N=32, K=64, w=FAKE, ldw=64, packed=FAKE, scales=FAKE, g=FAKE, ws=FAKE, ws_bytes=4096)
+        a.update(kw)
+        return B.aq_quant_fp4_block16(a["N"], a["K"], a["w"], a["ldw"], a["packed"], a["scales"],
+                                      a["g"], a["ws"], a["ws_bytes"], None)
+    assert q(K=40, ldw=40) == B.AQ_ERR_ALIGNMENT
+    assert q(N=0) == B.AQ_ERR_SHAPE
+    assert q(ldw=60) == B.AQ_ERR_SHAPE
+    assert q(ws_bytes=100) == B.AQ_ERR_WORKSPACE
+    assert q(packed=FAKE + 4) == B.AQ_ERR_ALIGNMENT
+    assert q(scales=None) == B.AQ_ERR_INVALID_ARG
