@@ -365,9 +365,10 @@ def run_materialize_fp4(args, torch, B, I):
             packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
             sc = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
             gs = torch.empty((1,), dtype=torch.float32, device=dev)
-            ws = torch.zeros(4096, dtype=torch.uint8, device=dev)
+            wsb = 65536 + 4096
+            ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
             packs.append(Call(lib.aq_quant_fp4_block16, (N, K, w.data_ptr(), K, packed.data_ptr(), sc.data_ptr(),
-                                                         gs.data_ptr(), ws.data_ptr(), 4096, stream),
+                                                         gs.data_ptr(), ws.data_ptr(), wsb, stream),
                               2 * N * K * 2 + N * K // 2 + N * K // 16, 0, f"fp4.L{l}.{f}", "fp4"))
             keep += [w, packed, sc, gs, ws, pa]
             mbytes += mats[-1].nbytes

@@ -80,10 +80,11 @@ typedef struct aq_proj {
  *   p      one projection; W0 and Vt 16-byte aligned; s, U naturally aligned.
  *   y      [M, ldy], ldy >= N; naturally aligned.
  *   ws     device workspace of at least aq_workspace_bytes(AQ_OP_RECON, ...)
- *          bytes, 256-byte aligned (NULL allowed when that size is 0).  It must
- *          be zero-filled before its first use; every call leaves it zero-filled
- *          again (its counters reset themselves), so one zeroed allocation can be
- *          reused by any number of calls that are ordered on one stream.  Calls
+ *          bytes, 256-byte aligned (NULL allowed when that size is 0).  Its
+ *          first 64 KiB hold split-K arrival counters: they must be zero before
+ *          the first use, and every call leaves them zero again; the rest is
+ *          per-call scratch.  So one zeroed allocation can serve any number and
+ *          kind of calls (recon and FP4) that are ordered on one stream.  Calls
  *          that share a workspace must not run concurrently.
  * Limits: 1 <= N, K <= 2^24; M <= 2^20; r <= AQ_MAX_RANK (else
  * AQ_ERR_UNSUPPORTED, a refusal rather than a silent fallback, as the pages' own
@@ -137,7 +138,8 @@ aq_status aq_materialize_weff(aq_dtype dt, int64_t K, const aq_proj *p, void *w_
  * pattern.  N >= 1, K % 16 == 0, ldw >= K, ldw % 8 == 0, w 16-byte aligned,
  * packed [N, K/2] 8-byte aligned (row stride K/2), scales [N, K/16] (row stride
  * K/16), global_scale: one device float.  ws: aq_workspace_bytes(AQ_OP_FP4, ...)
- * bytes, 256-byte aligned; no zero-fill needed.  Input must be finite. */
+ * bytes, 256-byte aligned; its first 64 KiB (the recon counters) are not
+ * touched, the scratch after them needs no zero-fill.  Input must be finite. */
 aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t ldw,
                                uint8_t *packed, uint8_t *scales, float *global_scale,
                                void *ws, size_t ws_bytes, void *stream);

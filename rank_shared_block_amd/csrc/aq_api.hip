@@ -67,6 +67,7 @@ aq_status build_recon(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t 
   rq->Ntot = col;
   if (M == 0) return AQ_OK;
   if (ldx < K) return fail(AQ_ERR_SHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldx > kMaxDim) return fail(AQ_ERR_UNSUPPORTED, "ldx = %lld exceeds 2^24", (long long)ldx);
   if (ldx % kdiv) return fail(AQ_ERR_ALIGNMENT, "ldx = %lld must be a multiple of %lld", (long long)ldx, (long long)kdiv);
   if (ldy < col) return fail(AQ_ERR_SHAPE, "ldy = %lld < total output columns %lld", (long long)ldy, (long long)col);
   if (M * ldx > kMaxElems || M * ldy > kMaxElems) return fail(AQ_ERR_UNSUPPORTED, "x or y exceeds 2^31-1 elements");
@@ -101,12 +102,12 @@ void make_plan(const aq::Recon &rq, Plan *pl) {
   }
   if (aq::plan_decode(rq, &pl->dec)) {
     pl->path = P_DECODE;
-    pl->ws = pl->dec.ws_counters + pl->dec.ws_partials;
+    pl->ws = pl->dec.ws_bytes;
     return;
   }
   pl->path = P_PREFILL;
   aq::plan_prefill(rq, &pl->pf);
-  pl->ws = pl->pf.ws_t;
+  pl->ws = pl->pf.ws_bytes;
 }
 
 aq_status recon(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx, const aq_proj *p,
@@ -194,7 +195,7 @@ aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t
   if (!aligned(w_bf16, 16)) return fail(AQ_ERR_ALIGNMENT, "w is not 16-byte aligned");
   if (!aligned(packed, 8)) return fail(AQ_ERR_ALIGNMENT, "packed is not 8-byte aligned");
   if (!aligned(global_scale, 4)) return fail(AQ_ERR_ALIGNMENT, "global_scale is not 4-byte aligned");
-  const size_t need = (size_t)aq::kFp4AmaxBlocks * 4;
+  const size_t need = aq::kWsReserved + (size_t)aq::kFp4AmaxBlocks * 4;
   if (!ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
   if (ws_bytes < need) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
   if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
@@ -205,7 +206,7 @@ aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t
 
 size_t aq_workspace_bytes(aq_op op, aq_dtype dt, int64_t M, int64_t K, const aq_proj *p,
                           int nproj) {
-  if (op == AQ_OP_FP4) return (size_t)aq::kFp4AmaxBlocks * 4;
+  if (op == AQ_OP_FP4) return aq::kWsReserved + (size_t)aq::kFp4AmaxBlocks * 4;
   if (op != AQ_OP_RECON || nproj < 1 || nproj > aq::kMaxBlocks || !p) return 0;
   int64_t ntot = 0;
   for (int b = 0; b < nproj; ++b) ntot += p[b].N > 0 ? p[b].N : 0;

@@ -15,6 +15,13 @@ constexpr int kNumCU = 256;       // MI355X: 256 CUs in 8 XCDs of 32
 constexpr int kNumXCD = 8;
 constexpr int kDecodeMaxM = 64;   // largest batch served by the streaming kernel
 
+// Workspace layout shared by every call: the first kWsReserved bytes hold the
+// split-K arrival counters (zero between calls); per-call scratch (partials, the
+// rank-r activation buffer, FP4 partial maxima) starts after them, so calls of
+// different kinds can share one workspace.
+constexpr size_t kWsReserved = 65536;
+constexpr int kMaxCounterTiles = (int)(kWsReserved / 4);
+
 // One projection of a (possibly fused) dispatch, host view.
 struct Proj {
   int64_t N, r;
@@ -36,11 +43,12 @@ struct Recon {
 struct DecodePlan {
   int MT;          // 16-token groups: 1, 2 or 4
   int NG;          // 16-row groups per workgroup (Vt groups + W0 groups)
-  int S;           // K splits across workgroups
+  int S;           // K splits across workgroups (partials + a reduce kernel)
+  int WAVES;       // waves per workgroup: 4 or 8
   int kchunk;      // K elements per split (multiple of 128)
   int ntiles;      // row tiles over all blocks
   int tile0[kMaxBlocks], ntile[kMaxBlocks], vg[kMaxBlocks];
-  size_t ws_counters, ws_partials;   // bytes
+  size_t ws_bytes;                   // total workspace bytes (0 when S == 1)
 };
 bool plan_decode(const Recon &rq, DecodePlan *pl);
 hipError_t launch_decode(const Recon &rq, const DecodePlan &pl, void *ws, hipStream_t st);
@@ -49,7 +57,7 @@ hipError_t launch_decode(const Recon &rq, const DecodePlan &pl, void *ws, hipStr
 struct PrefillPlan {
   int ldt;                          // columns of the t buffer (sum of r rounded to 16)
   int tcol[kMaxBlocks];
-  size_t ws_t;                      // bytes of the t buffer
+  size_t ws_bytes;                  // total workspace bytes (reserved region + t buffer)
 };
 void plan_prefill(const Recon &rq, PrefillPlan *pl);
 hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipStream_t st);

@@ -32,6 +32,22 @@ __device__ __forceinline__ uint4 ld16_stream(const void *p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Buffer resource over [base, base + bytes): a raw buffer load whose offset lies
+// outside that range returns zeros without touching memory.  This gives
+// branch-free predicated loads (rows past N, K past the end of a range, tokens
+// past M) so that every load of a step can be in flight at once.  `bytes` must be
+// below 2^31 so that kOOB is always out of range.  0x00020000 is the gfx9-family
+// descriptor word for raw 32-bit-format access.
+constexpr int kOOB = (int)0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ bf16x8 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
 
 // Workgroup ids are handed to the 8 XCDs round-robin (id % 8).  Remap so that

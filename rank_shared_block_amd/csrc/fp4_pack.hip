@@ -132,7 +132,8 @@ __global__ __launch_bounds__(256) void k_fp4_pack(const uint16_t *w, int N, int 
 }
 
 hipError_t launch_fp4(int64_t N, int64_t K, const void *w, int64_t ldw, uint8_t *packed,
-                      uint8_t *scales, float *gscale, void *ws, hipStream_t st) {
+                      uint8_t *scales, float *gscale, void *ws_base, hipStream_t st) {
+  void *ws = (char *)ws_base + kWsReserved;     // leave the counter region untouched
   const long nchunks = (long)N * (K / 8);
   int g1 = (int)((nchunks + 255) / 256);
   g1 = g1 < kFp4AmaxBlocks ? g1 : kFp4AmaxBlocks;

@@ -190,8 +190,7 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
     c += (int)((rq.blk[b].r + 15) / 16 * 16);
   }
   pl->ldt = c;
-  pl->ws_t = (size_t)rq.M * c * 2;
-  pl->ws_t = (pl->ws_t + 255) / 256 * 256;
+  pl->ws_bytes = c > 0 ? kWsReserved + (size_t)rq.M * c * 2 : 0;
 }
 
 static hipError_t run(PfArgs &a, hipStream_t st) {
@@ -209,7 +208,7 @@ static hipError_t run(PfArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipStream_t st) {
-  uint16_t *tbuf = (uint16_t *)ws;
+  uint16_t *tbuf = pl.ldt > 0 ? (uint16_t *)((char *)ws + kWsReserved) : nullptr;
   PfArgs a = {};
   a.x = (const uint16_t *)rq.x;
   a.ldx = (int)rq.ldx;

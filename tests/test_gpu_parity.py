@@ -342,3 +342,19 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(yp, eager_p), f"prefill replay {rep}"
     assert_parity(down(eager_d), oracle.recon_linear(I.activations("test", 500, 16, 6912, "bf16"),
                                                     *bundle_np(bd_dec)), "bf16")
+
+
+def test_workspace_shared_across_call_kinds():
+    """Split-K decode, prefill (rank-r scratch) and FP4 pack (partial maxima) on one
+    workspace: the scratch of one never disturbs the counters of another."""
+    ws = B.Workspace()
+    bd = I.bundle("test", 13, "down", 6912, 1152, 16, "bf16")
+    W = bundle_up(bd, "bf16")
+    for M in (16, 300, 2, 129, 16):
+        x = I.activations("test", 600 + M, M, 6912, "bf16")
+        y = B.recon_linear(up(x, "bf16"), W, workspace=ws)
+        assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"M={M}")
+        w = B.materialize(W)
+        p, s, g = B.quant_fp4_block16(w, workspace=ws)
+        ep, es, eg = oracle.fp4_pack(down(w))
+        assert np.array_equal(p.cpu().numpy(), ep) and float(g.cpu()[0]) == eg

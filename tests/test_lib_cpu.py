@@ -73,9 +73,10 @@ def _call(**kw):
     (dict(x=FAKE + 4), B.AQ_ERR_ALIGNMENT, "x is not"),
     (dict(x=None), B.AQ_ERR_INVALID_ARG, "x or y"),
     (dict(K=1 << 25, ldx=1 << 25), B.AQ_ERR_UNSUPPORTED, "2^24"),
-    (dict(ws=None), B.AQ_ERR_WORKSPACE, "workspace"),
-    (dict(ws_bytes=16), B.AQ_ERR_WORKSPACE, "workspace"),
-    (dict(ws=FAKE + 64), B.AQ_ERR_WORKSPACE, "256-byte"),
+    # K = 6912 splits K across workgroups, which needs the workspace
+    (dict(K=6912, ldx=6912, ws=None), B.AQ_ERR_WORKSPACE, "workspace"),
+    (dict(K=6912, ldx=6912, ws_bytes=16), B.AQ_ERR_WORKSPACE, "workspace"),
+    (dict(K=6912, ldx=6912, ws=FAKE + 64), B.AQ_ERR_WORKSPACE, "256-byte"),
 ])
 def test_recon_argument_errors(kw, status, needle):
     assert _call(**kw) == status
@@ -100,13 +101,13 @@ def test_fused_calls_validate_every_block():
 def test_workspace_query_is_host_only():
     p1 = [_proj(N=1024, r=16)]
     ws_dec = B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 16, 1152, p1, 1)
-    assert ws_dec % 256 == 0 and ws_dec > 0
+    assert ws_dec % 256 == 0 and ws_dec > 65536          # counters + split-K partials
     # prefill: a bf16 t buffer of M x (r rounded to 16)
     ws_pf = B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 512, 1152, p1, 1)
-    assert ws_pf == 512 * 16 * 2
+    assert ws_pf == 65536 + 512 * 16 * 2
     assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_F32, 8, 256, [_proj(N=256)], 1) == 0
     assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 0, 1152, p1, 1) == 0
-    assert B.aq_workspace_bytes(B.AQ_OP_FP4, B.AQ_BF16, 0, 1152, p1, 1) == 4096
+    assert B.aq_workspace_bytes(B.AQ_OP_FP4, B.AQ_BF16, 0, 1152, p1, 1) == 65536 + 4096
     assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 4, 100, p1, 1) == 0   # invalid K
 
 
@@ -125,7 +126,7 @@ def test_materialize_argument_errors():
 
 def test_fp4_argument_errors():
     def q(**kw):
-        a = dict(N=32, K=64, w=FAKE, ldw=64, packed=FAKE, scales=FAKE, g=FAKE, ws=FAKE, ws_bytes=4096)
+        a = dict(N=32, K=64, w=FAKE, ldw=64, packed=FAKE, scales=FAKE, g=FAKE, ws=FAKE, ws_bytes=65536 + 4096)
         a.update(kw)
         return B.aq_quant_fp4_block16(a["N"], a["K"], a["w"], a["ldw"], a["packed"], a["scales"],
                                       a["g"], a["ws"], a["ws_bytes"], None)
