@@ -86,7 +86,8 @@ typedef struct aq_proj {
  *          per-call scratch.  So one zeroed allocation can serve any number and
  *          kind of calls (recon and FP4) that are ordered on one stream.  Calls
  *          that share a workspace must not run concurrently.
- * Limits: 1 <= N, K <= 2^24; M <= 2^20; r <= AQ_MAX_RANK (else
+ * Limits: 1 <= N <= 2^24; 1 <= K, ldx < 2^22; M <= 2^19; N * K and M * ldx, M * ldy
+ * below 2^31 elements; r <= AQ_MAX_RANK (else
  * AQ_ERR_UNSUPPORTED, a refusal rather than a silent fallback, as the pages' own
  * custom op refuses ranks above its limit: "Execution paths", "The custom op"). */
 aq_status aq_recon_linear(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,

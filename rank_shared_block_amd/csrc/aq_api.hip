@@ -21,6 +21,7 @@ aq_status fail(aq_status s, const char *fmt, ...) {
 }
 
 constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMaxK = (int64_t(1) << 22) - 1;    // 32-bit buffer offsets over 256-row tiles
 constexpr int64_t kMaxM = int64_t(1) << 19;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 
@@ -37,7 +38,7 @@ aq_status build_recon(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t 
   if (!p) return fail(AQ_ERR_INVALID_ARG, "projection descriptor pointer is NULL");
   if (M < 0) return fail(AQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
   if (K < 1) return fail(AQ_ERR_SHAPE, "K = %lld must be >= 1", (long long)K);
-  if (K > kMaxDim) return fail(AQ_ERR_UNSUPPORTED, "K = %lld exceeds 2^24", (long long)K);
+  if (K > kMaxK) return fail(AQ_ERR_UNSUPPORTED, "K = %lld exceeds 2^22 - 1", (long long)K);
   if (M > kMaxM) return fail(AQ_ERR_UNSUPPORTED, "M = %lld exceeds 2^19", (long long)M);
   const int64_t kdiv = dt == AQ_BF16 ? 8 : 4;
   if (K % kdiv) return fail(AQ_ERR_ALIGNMENT, "K = %lld must be a multiple of %lld for this dtype", (long long)K, (long long)kdiv);
@@ -67,7 +68,7 @@ aq_status build_recon(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t 
   rq->Ntot = col;
   if (M == 0) return AQ_OK;
   if (ldx < K) return fail(AQ_ERR_SHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
-  if (ldx > kMaxDim) return fail(AQ_ERR_UNSUPPORTED, "ldx = %lld exceeds 2^24", (long long)ldx);
+  if (ldx > kMaxK) return fail(AQ_ERR_UNSUPPORTED, "ldx = %lld exceeds 2^22 - 1", (long long)ldx);
   if (ldx % kdiv) return fail(AQ_ERR_ALIGNMENT, "ldx = %lld must be a multiple of %lld", (long long)ldx, (long long)kdiv);
   if (ldy < col) return fail(AQ_ERR_SHAPE, "ldy = %lld < total output columns %lld", (long long)ldy, (long long)col);
   if (M * ldx > kMaxElems || M * ldy > kMaxElems) return fail(AQ_ERR_UNSUPPORTED, "x or y exceeds 2^31-1 elements");

@@ -72,7 +72,7 @@ def _call(**kw):
     (dict(p=_proj(Vt=FAKE + 2)), B.AQ_ERR_ALIGNMENT, "Vt"),
     (dict(x=FAKE + 4), B.AQ_ERR_ALIGNMENT, "x is not"),
     (dict(x=None), B.AQ_ERR_INVALID_ARG, "x or y"),
-    (dict(K=1 << 25, ldx=1 << 25), B.AQ_ERR_UNSUPPORTED, "2^24"),
+    (dict(K=1 << 22, ldx=1 << 22), B.AQ_ERR_UNSUPPORTED, "2^22"),
     # K = 6912 splits K across workgroups, which needs the workspace
     (dict(K=6912, ldx=6912, ws=None), B.AQ_ERR_WORKSPACE, "workspace"),
     (dict(K=6912, ldx=6912, ws_bytes=16), B.AQ_ERR_WORKSPACE, "workspace"),
