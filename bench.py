@@ -157,22 +157,13 @@ def time_eager(torch, calls, steps, warmup):
 
 
 def time_per_launch(torch, calls, reps):
-    """Average GPU duration of each launch, from event pairs around every launch,
-    all queued behind a GPU sleep so that the pairs see no CPU gaps."""
-    durs = []
-    for _ in range(reps):
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(2e7))                  # ~10 ms of GPU spin while we enqueue
-        evs = []
-        for c in calls:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            c()
-            b.record()
-            evs.append((a, b))
-        torch.cuda.synchronize()
-        durs += [a.elapsed_time(b) for a, b in evs]
-    return float(np.mean(durs)), float(np.median(durs))
+    """Average duration of one launch of `calls`' kernel: HIP events around
+    replays of a graph that holds only these launches back to back, on the
+    stream the graph runs on.  Consecutive kernels of a graph abut on the GPU,
+    so this equals the average kernel duration that rocprofv3 reports for the
+    same replays (start to start)."""
+    ms, _ = time_graph(torch, calls, reps, 2)
+    return ms / len(calls)
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -210,6 +201,118 @@ def cpu_baseline(I, layer_np, shapes, Ms, x_tag, budget_s, layers_sample):
                       f"{t_used:.1f} s of numpy float64 oracle time (bf16->fp64 conversion excluded)"}
 
 
+# --------------------------------------------------------------------------- counters
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+SOURCES = {"decode_gateup": "rank_shared_block_amd/csrc/recon_decode.hip"}
+
+
+def source_digest(rel):
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(key):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_digest(SOURCES[key]):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def run_pmc_probe(args, torch, B, I):
+    """Workload for the counter runs: a plain copy of known size (calibration),
+    then the 78 fused gate/up launches of a bench step, eagerly."""
+    dev = torch.device("cuda", 0)
+    src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    layer_np = I.layer_bundles("gemma_decode", I.GEMMA_1B, layers=26, r=16, dtype="bf16",
+                               families=("gate", "up"))
+    layer_dev = upload_layers(torch, I, layer_np)
+    for M in (1, 4, 16):
+        lib = B.lib()
+        stream = torch.cuda.current_stream().cuda_stream
+        for l in range(26):
+            x = torch.from_numpy(I.activations("gemma_decode", 10 * M + 6, M, 1152, "bf16")).to(dev).to(torch.bfloat16)
+            arr = (B.aq_proj * 2)(*[B.make_proj(*layer_dev[l][f]) for f in ("gate", "up")])
+            y = torch.empty((M, 13824), dtype=torch.bfloat16, device=dev)
+            need = lib.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, M, 1152, arr, 2)
+            ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+            st = lib.aq_recon_gateup_fused(B.AQ_BF16, M, 1152, x.data_ptr(), 1152, arr, y.data_ptr(), 13824,
+                                           ws.data_ptr(), ws.numel(), stream)
+            assert st == 0
+    torch.cuda.synchronize()
+    return {"probe": "copy of %d bytes, then 78 fused gate/up decode launches" % CALIB_BYTES}
+
+
+CALIB_BYTES = 256 * 2 ** 20
+
+
+def summarize_profiles(args):
+    """Turn rocprofv3 CSV output (kernel trace, and optionally the two counter
+    runs) into the markdown summary committed under profiles/."""
+    import csv
+    import collections
+
+    def rows(path):
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    out = []
+    if args.trace:
+        tr = rows(args.trace)
+        agg = collections.defaultdict(list)
+        for r in tr:
+            wg = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1) // int(r["Workgroup_Size_X"])
+            agg[(r["Kernel_Name"], wg)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        out.append("| kernel | workgroups | launches | avg us | median us | total us |")
+        out.append("|---|---|---|---|---|---|")
+        for (name, wg), d in sorted(agg.items(), key=lambda kv: -sum(kv[1]))[:14]:
+            d.sort()
+            out.append(f"| `{name[:80]}` | {wg} | {len(d)} | {sum(d)/len(d):.3f} | {d[len(d)//2]:.3f} | {sum(d):.1f} |")
+    if args.fetch and args.write:
+        res = {}
+        for key, path in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
+            rs = rows(path)
+            val = lambda r: float(r.get("Counter_Value", r.get("value", 0)))
+            copy = [val(r) for r in rs if "copyBuffer" in r["Kernel_Name"]]
+            dec = [val(r) for r in rs if "k_decode_bf16" in r["Kernel_Name"]]
+            res[key] = (max(copy) if copy else None, float(np.mean(dec)) if dec else None, len(dec))
+        # scale: a copy of CALIB_BYTES reads and writes CALIB_BYTES each
+        fscale = CALIB_BYTES / (res["FETCH_SIZE"][0] * 1024)
+        wscale = CALIB_BYTES / (res["WRITE_SIZE"][0] * 1024)
+        fetch_b = res["FETCH_SIZE"][1] * 1024 * fscale
+        write_b = res["WRITE_SIZE"][1] * 1024 * wscale
+        out.append("")
+        out.append(f"FETCH_SIZE copy calibration: {res['FETCH_SIZE'][0]:.0f} KiB for {CALIB_BYTES} B read "
+                   f"(scale {fscale:.4f}); WRITE_SIZE: {res['WRITE_SIZE'][0]:.0f} KiB for {CALIB_BYTES} B written "
+                   f"(scale {wscale:.4f}).")
+        out.append(f"k_decode_bf16 (fused gate/up), mean over {res['FETCH_SIZE'][2]} launches: "
+                   f"fetch {fetch_b/1e6:.3f} MB, write {write_b/1e6:.3f} MB per launch "
+                   f"(scaled), total {(fetch_b + write_b)/1e6:.3f} MB.")
+        t = {}
+        try:
+            with open(TRAFFIC_FILE) as f:
+                t = json.load(f)
+        except (OSError, ValueError):
+            pass
+        t["decode_gateup"] = {"bytes_per_launch": int(fetch_b + write_b), "fetch_bytes": int(fetch_b),
+                              "write_bytes": int(write_b), "fetch_scale": fscale, "write_scale": wscale,
+                              "source_sha256_16": source_digest(SOURCES["decode_gateup"])}
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+    print("\n".join(out))
+
+
 # --------------------------------------------------------------------------- workloads
 
 def run_gemma_decode(args, torch, B, I):
@@ -243,14 +346,14 @@ def run_gemma_decode(args, torch, B, I):
 
     # Dominant kernel: the fused gate/up dispatch (59% of the bytes of a layer).
     gu = [c for c in all_calls if c.grid_key == "gateup"]
-    avg_ms, med_ms = time_per_launch(torch, gu, args.roofline_reps)
+    avg_ms = time_per_launch(torch, gu, max(5, args.roofline_reps))
     gu_bytes = float(np.mean([c.nbytes for c in gu]))
     achieved = gu_bytes / (avg_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "k_decode_bf16 (fused gate/up, K=1152, N=2x6912, r=16, M in {1,4,16})",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode_gateup"),
+            "kernel": "k_decode_bf16 (fused gate/up, K=1152, N=2x6912, r=16, M in {1,4,16}, 26 layers)",
             "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(avg_ms * 1e3, 3),
-            "median_launch_us": round(med_ms * 1e3, 3), "launches": len(gu) * args.roofline_reps}
+            "launches_per_replay": len(gu)}
 
     line = {
         "metric": "reconstructed-linear µs/layer + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)",
@@ -375,7 +478,7 @@ def run_materialize_fp4(args, torch, B, I):
             pbytes += packs[-1].nbytes
     ms_m, _ = time_graph(torch, mats, args.steps, args.warmup)
     ms_p, _ = time_graph(torch, packs, args.steps, args.warmup)
-    mat_avg, _ = time_per_launch(torch, mats, 2)
+    mat_avg = time_per_launch(torch, mats, 2)
     return {"workload": "materialise + FP4 pack, 7 families x 26 layers (Gemma-3-1B shapes), 13 W0 bands, rank 64",
             "materialize": {"ms": round(ms_m, 4), "GBps": round(mbytes / (ms_m * 1e-3) / 1e9, 1),
                             "frac_hbm_peak": round(mbytes / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -390,12 +493,20 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gemma_decode",
-                    choices=["gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4"])
+                    choices=["gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4", "pmc_probe"])
+    ap.add_argument("--summarize", action="store_true",
+                    help="summarise rocprofv3 CSVs (--trace, --fetch, --write) instead of running")
+    ap.add_argument("--trace")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--roofline-reps", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -409,7 +520,8 @@ def main():
     B.lib()
     torch.cuda.set_device(0)
     fn = {"gemma_decode": run_gemma_decode, "gemma_prefill": run_gemma_prefill,
-          "large_decoder": run_large_decoder, "materialize_fp4": run_materialize_fp4}[args.workload]
+          "large_decoder": run_large_decoder, "materialize_fp4": run_materialize_fp4,
+          "pmc_probe": run_pmc_probe}[args.workload]
     out = fn(args, torch, B, I)
     print(json.dumps(out), flush=True)
 

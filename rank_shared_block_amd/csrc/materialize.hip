@@ -8,12 +8,15 @@
 //   rank-r product costs 2 r flop per element, which at r = 64 would exceed the
 //   fp32 VALU roofline, so it runs on v_mfma_f32_32x32x16_bf16 with U as the A
 //   operand (row n, 8 contiguous rank values per lane) and Vt as the B operand.
-// * A wave owns a strip of 32 * SETS columns.  MFMA column c of "set" e stands for
-//   actual column c0 + SETS * c + e, so after SETS MFMAs a lane holds SETS
-//   consecutive columns of each of its 16 rows and reads W0 / writes W_eff with
-//   SETS * 2-byte accesses instead of 2-byte ones.  The Vt operand of the strip
-//   (strided in K) is gathered once into registers and reused for every row
-//   block the wave visits.
+// * A workgroup owns a block of 512 columns (a wave 32 * SETS of them, SETS = 4)
+//   and a range of rows.  MFMA column c of "set" e stands for actual column
+//   c0 + SETS * c + e, so after SETS MFMAs a lane holds SETS consecutive columns
+//   of each of its 16 rows and reads W0 / writes W_eff with 8-byte accesses.
+//   The Vt block (K-contiguous, but needed rank-contiguous as an MFMA operand)
+//   is staged once in LDS transposed, read back as one 16-byte fragment per
+//   rank chunk and reused for every row of the range.  The first row block's W0,
+//   s and U are requested before the staging so that the two round trips
+//   overlap.
 // * diag(s) W0 is added in fp32 with one fused multiply-add per element; with
 //   r = 0 (or U = Vt = 0) the accumulator is +0 and the result is one rounding of
 //   the exact product s * w, i.e. bit-exact.
@@ -33,55 +36,47 @@ struct MatArgs {
 };
 
 template <int SETS, int JC>
-__global__ __launch_bounds__(256) void k_materialize_bf16(const MatArgs a) {
+__global__ __launch_bounds__(256, 2) void k_materialize_bf16(const MatArgs a) {
+  constexpr int CW = 32 * SETS;             // columns per wave
+  constexpr int CB = 4 * CW;                // columns per workgroup
+  constexpr int RP = 16 * JC + 8;           // LDS row (one column of Vt), padded
+  // Vt[:, c0 : c0 + CB] stored transposed: vts[c][j], so that the 8 ranks of one
+  // MFMA operand are one 16-byte LDS read.
+  __shared__ __attribute__((aligned(16))) uint16_t vts[CB * RP];
   const uint16_t *W0 = (const uint16_t *)a.W0, *S = (const uint16_t *)a.s;
   const uint16_t *U = (const uint16_t *)a.U, *Vt = (const uint16_t *)a.Vt;
   uint16_t *out = (uint16_t *)a.out;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, hi = lane >> 5;
   const int K = a.K, r = a.r, N = a.N;
-  const int c0 = (blockIdx.x * 4 + wave) * (32 * SETS);
-  if (c0 >= K) return;                     // no barriers below: a wave may leave alone
-  const int kl = c0 + SETS * c32;          // this lane's SETS consecutive columns
-  const bool colok = kl < K;               // K % SETS == 0, so all SETS or none
+  const int cb0 = blockIdx.x * CB;
+  const int c0 = cb0 + wave * CW;
+  const int kl = c0 + SETS * c32;            // this lane's SETS consecutive columns
+  const bool colok = kl < K;                 // K % SETS == 0, so all SETS or none
+  const int kloc = wave * CW + SETS * c32;   // ... their position in the LDS tile
 
-  bf16x8 bv[SETS][JC];
+  // Operands of one 32-row block: W0 and s of this lane's 16 output rows, U of
+  // its A-operand row.  The first block's are requested before the Vt staging
+  // so that the two memory round trips overlap.
+  uint2 w[16];
+  float sv[16];
+  bf16x8 au[JC];
+  auto fetch_rows = [&](int n0, int ne) {
 #pragma unroll
-  for (int e = 0; e < SETS; ++e)
-#pragma unroll
-    for (int jc = 0; jc < JC; ++jc) {
-      uint16_t v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int j = jc * 16 + 8 * hi + q;
-        v[q] = (j < r && colok) ? Vt[(size_t)j * K + kl + e] : (uint16_t)0;
-      }
-      uint4 u;
-      u.x = v[0] | ((uint32_t)v[1] << 16);
-      u.y = v[2] | ((uint32_t)v[3] << 16);
-      u.z = v[4] | ((uint32_t)v[5] << 16);
-      u.w = v[6] | ((uint32_t)v[7] << 16);
-      bv[e][jc] = as_bf16x8(u);
+    for (int v = 0; v < 16; ++v) {
+      const int n = n0 + 8 * (v >> 2) + 4 * hi + (v & 3);
+      const bool ok = colok && n < ne;
+      w[v] = ok ? *reinterpret_cast<const uint2 *>(W0 + (size_t)n * K + kl) : make_uint2(0, 0);
+      sv[v] = ok ? bf2f(S[n]) : 0.f;
     }
-
-  for (int nb = blockIdx.y * a.rows_per_wg; nb < N; nb += gridDim.y * a.rows_per_wg) {
-  const int ne = min(N, nb + a.rows_per_wg);
-  for (int n0 = nb; n0 < ne; n0 += 32) {
-    f32x16 acc[SETS];
-#pragma unroll
-    for (int e = 0; e < SETS; ++e)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[e][v] = 0.f;
-    const int na = n0 + c32;               // row of this lane's A operand
+    const int na = n0 + c32;
 #pragma unroll
     for (int jc = 0; jc < JC; ++jc) {
-      if (jc * 16 >= r) break;
       const int j = jc * 16 + 8 * hi;
-      bf16x8 au;
       if (na >= N || j >= r) {
-        au = zero_bf16x8();
+        au[jc] = zero_bf16x8();
       } else if (a.ufast) {
-        au = as_bf16x8(ld16(U + (size_t)na * r + j));
+        au[jc] = as_bf16x8(ld16(U + (size_t)na * r + j));
       } else {
         uint16_t v[8];
 #pragma unroll
@@ -91,34 +86,65 @@ __global__ __launch_bounds__(256) void k_materialize_bf16(const MatArgs a) {
         u.y = v[2] | ((uint32_t)v[3] << 16);
         u.z = v[4] | ((uint32_t)v[5] << 16);
         u.w = v[6] | ((uint32_t)v[7] << 16);
-        au = as_bf16x8(u);
+        au[jc] = as_bf16x8(u);
       }
+    }
+  };
+  const int nb0 = blockIdx.y * a.rows_per_wg;
+  if (nb0 < N) fetch_rows(nb0, min(N, nb0 + a.rows_per_wg));
+
+  // Stage Vt transposed (zeros past r or K).  Consecutive threads take
+  // consecutive ranks of one 8-column chunk, so their 2-byte LDS writes fall in
+  // consecutive banks.
+  for (int i = tid; i < 16 * JC * (CB / 8); i += 256) {
+    const int j = i % (16 * JC), c = (i / (16 * JC)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (j < r && cb0 + c < K) v = ld16(Vt + (size_t)j * K + cb0 + c);
+    const uint32_t q4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) vts[(c + q) * RP + j] = (uint16_t)(q4[q >> 1] >> ((q & 1) * 16));
+  }
+  __syncthreads();
+
+  // B operands (Vt): set e, rank chunk jc -> ranks jc*16 + 8*hi .. +7 of column kl + e.
+  bf16x8 bv[SETS][JC];
+#pragma unroll
+  for (int e = 0; e < SETS; ++e)
+#pragma unroll
+    for (int jc = 0; jc < JC; ++jc)
+      bv[e][jc] = as_bf16x8(*reinterpret_cast<const uint4 *>(&vts[(kloc + e) * RP + jc * 16 + 8 * hi]));
+
+  // Every lane stays active through the MFMAs (they read all 64 lanes'
+  // operands); lanes past K only skip their loads and stores of W0 / W_eff.
+  for (int nb = nb0; nb < N; nb += gridDim.y * a.rows_per_wg) {
+    const int ne = min(N, nb + a.rows_per_wg);
+    for (int n0 = nb; n0 < ne; n0 += 32) {
+      if (n0 != nb0) fetch_rows(n0, ne);
+      f32x16 acc[SETS];
 #pragma unroll
       for (int e = 0; e < SETS; ++e)
-        acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(au, bv[e][jc], acc[e], 0, 0, 0);
-    }
-    if (!colok) continue;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int n = n0 + 8 * (v >> 2) + 4 * hi + (v & 3);
-      if (n >= ne) continue;
-      const float sn = bf2f(S[n]);
-      const uint16_t *wr = W0 + (size_t)n * K + kl;
-      uint16_t *orow = out + (size_t)n * a.ldw + kl;
-      if constexpr (SETS == 4) {
-        const uint2 w = *reinterpret_cast<const uint2 *>(wr);
+        for (int v = 0; v < 16; ++v) acc[e][v] = 0.f;
+#pragma unroll
+      for (int jc = 0; jc < JC; ++jc) {
+        if (jc * 16 >= r) break;
+#pragma unroll
+        for (int e = 0; e < SETS; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(au[jc], bv[e][jc], acc[e], 0, 0, 0);
+      }
+      if (!colok) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int n = n0 + 8 * (v >> 2) + 4 * hi + (v & 3);
+        if (n >= ne) continue;
         uint2 o;
-        o.x = f2bf(fmaf(sn, bf2f((uint16_t)w.x), acc[0][v])) |
-              ((uint32_t)f2bf(fmaf(sn, bf2f((uint16_t)(w.x >> 16)), acc[1][v])) << 16);
-        o.y = f2bf(fmaf(sn, bf2f((uint16_t)w.y), acc[2][v])) |
-              ((uint32_t)f2bf(fmaf(sn, bf2f((uint16_t)(w.y >> 16)), acc[3][v])) << 16);
-        *reinterpret_cast<uint2 *>(orow) = o;
-      } else {
-#pragma unroll
-        for (int e = 0; e < SETS; ++e) orow[e] = f2bf(fmaf(sn, bf2f(wr[e]), acc[e][v]));
+        o.x = f2bf(fmaf(sv[v], bf2f((uint16_t)w[v].x), acc[0][v])) |
+              ((uint32_t)f2bf(fmaf(sv[v], bf2f((uint16_t)(w[v].x >> 16)), acc[1][v])) << 16);
+        o.y = f2bf(fmaf(sv[v], bf2f((uint16_t)w[v].y), acc[2][v])) |
+              ((uint32_t)f2bf(fmaf(sv[v], bf2f((uint16_t)(w[v].y >> 16)), acc[3][v])) << 16);
+        *reinterpret_cast<uint2 *>(out + (size_t)n * a.ldw + kl) = o;
       }
     }
-  }
   }
 }
 
@@ -198,16 +224,19 @@ hipError_t launch_materialize(aq_dtype dt, int64_t K, const Proj &p, void *w, in
     hipLaunchKernelGGL(k_materialize_f32, grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  // Row blocks per workgroup: enough workgroups to cover 256 CUs a few times over.
+  // Column blocks of 512 (4 waves x 128); row blocks sized so that the grid has
+  // about two workgroups per CU, each amortising its staged Vt tile over as many
+  // rows as possible.
   constexpr int SETS = 4;
-  const int colblocks_lo = (int)((K + 4 * 32 * SETS - 1) / (4 * 32 * SETS));
-  int rows = 256;
-  while (rows > 32 && (long)colblocks_lo * ((p.N + rows - 1) / rows) < 4 * kNumCU) rows /= 2;
-  a.rows_per_wg = rows;
+  const int colblocks = (int)((K + 4 * 32 * SETS - 1) / (4 * 32 * SETS));
+  long rows = (p.N * colblocks + 2 * kNumCU - 1) / (2 * kNumCU);
+  rows = (rows + 31) / 32 * 32;
+  if (rows < 32) rows = 32;
+  a.rows_per_wg = (int)rows;
   const long nrb = (p.N + rows - 1) / rows;
   const unsigned gy = (unsigned)(nrb < 65535 ? nrb : 65535);
   if (p.r <= 64) {
-    dim3 grid((unsigned)colblocks_lo, gy);
+    dim3 grid((unsigned)colblocks, gy);
     if (p.r <= 16)
       hipLaunchKernelGGL((k_materialize_bf16<SETS, 1>), grid, dim3(256), 0, st, a);
     else if (p.r <= 32)

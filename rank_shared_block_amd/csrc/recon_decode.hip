@@ -259,7 +259,6 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
   if (rq.dt != AQ_BF16 || rq.M < 1 || rq.M > kDecodeMaxM) return false;
   const int M = (int)rq.M, K = (int)rq.K;
   pl->MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  const int kstep = 128 / pl->MT;
   int vgmax = 0;
   for (int b = 0; b < rq.nblk; ++b) {
     pl->vg[b] = (int)((rq.blk[b].r + 15) / 16);
@@ -279,21 +278,19 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
     return t;
   };
   const int ngmin = vgmax + 1 > 2 ? vgmax + 1 : 2;
-  const int ksteps = (K + kstep - 1) / kstep;
 
-  // Defaults: the largest row tile (least re-reading of Vt) that still gives
-  // >= 2 workgroups per CU; 8 waves when each wave still gets >= 2 steps; split K
-  // only when the tiles alone cannot cover the CUs.
+  // Defaults, from sweeps over the Gemma-3-1B and large-decoder decode shapes on
+  // MI355X: 4 waves per workgroup; the largest row tile (least re-reading of Vt)
+  // that still gives >= 384 work units once K is split; K split only into
+  // ranges of >= 2304 values (a split costs fp32 partials and a reduce launch).
+  constexpr int kUnits = 384;
+  const int smax = K / 2304 > 1 ? K / 2304 : 1;
   int NG = ngmax;
-  while (NG - 1 >= ngmin && tiles_for(NG) < 2 * kNumCU) NG -= 1;
+  while (NG - 1 >= ngmin && tiles_for(NG) * smax < kUnits) NG -= 1;
   int ntiles = tiles_for(NG);
-  int WAVES = (pl->MT == 1 && ksteps >= 16) ? 8 : 4;
-  int S = 1;
-  if (ntiles < kNumCU) {
-    S = (2 * kNumCU + ntiles - 1) / ntiles;
-    const int smax = ksteps / (2 * WAVES) > 1 ? ksteps / (2 * WAVES) : 1;
-    S = S > smax ? smax : S;
-  }
+  int WAVES = 4;
+  int S = (kUnits + ntiles - 1) / ntiles;
+  S = S < 1 ? 1 : (S > smax ? smax : S);
   // Tuning overrides (profiling sweeps): AQ_DECODE_NG, AQ_DECODE_S, AQ_DECODE_WAVES.
   const int ng_o = env_int("AQ_DECODE_NG", 0), s_o = env_int("AQ_DECODE_S", 0);
   const int w_o = env_int("AQ_DECODE_WAVES", 0);
