@@ -40,15 +40,28 @@ struct Recon {
 };
 
 // ---- decode (streaming, M <= kDecodeMaxM, bf16) ---------------------------
+constexpr int kMaxSegs = 2 * kMaxBlocks;   // split mode: W0 rows and Vt rows per block
+
+struct DecodeSeg {
+  int b;           // block
+  int isVt;        // split mode: 1 for the block's Vt rows
+  int tile0, ntile;
+};
+
 struct DecodePlan {
   int MT;          // 16-token groups: 1, 2 or 4
-  int NG;          // 16-row groups per workgroup (Vt groups + W0 groups)
-  int S;           // K splits across workgroups (partials + a reduce kernel)
+  int NG;          // 16-row groups per workgroup
+  int split;       // 0: fused (t per workgroup, one kernel); 1: partials + combine
+  int S;           // K splits across workgroups (split mode only; 1 when fused)
   int WAVES;       // waves per workgroup: 4 or 8
   int kchunk;      // K elements per split (multiple of 128)
-  int ntiles;      // row tiles over all blocks
-  int tile0[kMaxBlocks], ntile[kMaxBlocks], vg[kMaxBlocks];
-  size_t ws_bytes;                   // total workspace bytes (0 when S == 1)
+  int ntiles;      // row tiles over all segments
+  int nseg;
+  DecodeSeg seg[kMaxSegs];
+  int vg[kMaxBlocks];                // fused: Vt groups per tile of each block
+  int tcol[kMaxBlocks];              // split: column of block b's t in a partial row
+  int Wp;                            // split: partial row width (sum N + sum r)
+  size_t ws_bytes;                   // total workspace bytes (0 when fused)
 };
 bool plan_decode(const Recon &rq, DecodePlan *pl);
 hipError_t launch_decode(const Recon &rq, const DecodePlan &pl, void *ws, hipStream_t st);

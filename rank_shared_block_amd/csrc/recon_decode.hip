@@ -11,30 +11,33 @@
 // * At decode the arithmetic intensity is ~1-16 flop/byte, so the kernel is
 //   bound by HBM: every byte of W0 is read exactly once, with 16-byte loads.
 // * The weights are the MFMA B operand and the tokens the A operand of
-//   v_mfma_f32_16x16x32_bf16: one 16-row group of W0 x 32 K-values per
+//   v_mfma_f32_16x16x32_bf16: one 16-row group of weights x 32 K-values per
 //   instruction, tokens padded to 16 (rows of x beyond M are zero registers, not
 //   loads).  A lane loads 16 contiguous bytes of one row; four lanes cover 64
 //   contiguous bytes.  No cross-lane reduction is needed and no bf16 -> fp32
 //   conversion runs on the VALU.
-// * The concatenated down-contraction of the pages ("one x @ [W0^T, V]") is
-//   realised by treating the block's Vt rows as extra 16-row groups that the
-//   workgroup streams alongside its W0 rows: the workgroup obtains the partial
-//   t = x Vt^T over its own K range and applies U in its epilogue, so t never
-//   leaves the chip.  Vt is small and is served from L2 to the workgroups that
-//   share it.
-// * Loads go through buffer resources: rows past N, K past the end of the range
-//   and tokens past M fall outside the resource and read as zero, so the loop is
-//   branch-free and every fragment of a step is requested at once; two steps are
-//   in flight per wave (two register sets used in turn).
-// * Each workgroup (WAVES = 4 or 8 waves) owns NG row groups (vg of Vt, NG - vg
-//   of W0) and one K range; its waves interleave over that range and their
-//   partial sums are added in LDS in a fixed wave order.  When a row tile is
-//   split over S workgroups along K (short, wide layers need it to fill 256 CUs),
-//   each split writes its fp32 partial y to the workspace and a second small
-//   kernel adds the S partials in split order.  The kernel boundary publishes the
-//   partials; a device-scope fence per workgroup would write back and invalidate
-//   the whole L2 each time, which costs far more than the extra launch.  The
-//   result is deterministic.
+// * The pages' concatenated down-contraction ("one x @ [W0^T, V]") is a stack of
+//   16-row groups: the W0 rows of every block and the r rows of its Vt.  A
+//   workgroup streams NG groups over one K range; its waves interleave over that
+//   range and their partial sums are added in LDS in a fixed wave order.
+// * Loads go through buffer resources: rows past the end, K past the end of the
+//   range and tokens past M fall outside the resource and read as zero, so the
+//   loop is branch-free and every fragment of a step is requested at once; two
+//   steps are in flight per wave (two register sets used in turn).
+//
+// Two ways to meet the rank-r term, chosen per dispatch by the host:
+// * fused (one kernel): each workgroup's tile holds vg groups of Vt next to its
+//   W0 groups, so the workgroup gets t = x Vt^T itself and applies s and U in its
+//   epilogue; t never leaves the chip.  The price is that every workgroup streams
+//   the whole Vt (served from L2): cheap while the tiles outnumber r heavily,
+//   ruinous for long K and large r, where it can double the load traffic.
+// * split (two kernels): Vt rows form tiles of their own, read exactly once, and
+//   K may be split over S workgroups to fill 256 CUs.  Every tile writes its fp32
+//   partial (z for W0 rows, t for Vt rows) to the workspace; a combine kernel then
+//   forms y = s * sum_p z_p + U (sum_p t_p) in split order.  The kernel boundary
+//   publishes the partials; a device-scope fence per workgroup would write back
+//   and invalidate the whole L2 each time, which costs far more than the launch.
+// Both are deterministic.
 
 #include <stdlib.h>
 
@@ -43,7 +46,10 @@
 
 namespace aq {
 
-struct DecBlk {
+// One segment of stacked rows.  Fused mode: a block (W0 rows plus vg groups of
+// its Vt per tile, s and U for the epilogue).  Split mode: either the W0 rows or
+// the Vt rows of a block (vg = 0), written as partials at column `col`.
+struct DecSeg {
   const uint16_t *W0, *s, *U, *Vt;
   int N, r, col, tile0, vg, ufast;
 };
@@ -51,23 +57,25 @@ struct DecBlk {
 struct DecArgs {
   const uint16_t *x;
   uint16_t *y;
-  float *part;          // [S][M][Ntot] fp32 partials (S > 1)
-  int ldx, ldy, M, K, Ntot;
-  int nblk, ntiles, S, kchunk;
-  DecBlk b[kMaxBlocks];
+  float *part;          // split mode: [S][M][Wp] fp32 partials
+  int ldx, ldy, M, K, Wp;
+  int nseg, ntiles, S, kchunk;
+  DecSeg g[kMaxSegs];
 };
 
 // MT: 16-token groups; NG: 16-row groups per workgroup; WAVES: waves per
-// workgroup.  A step covers KS = 4 / MT chunks of 32 K-values, so that the
-// fragments of two steps fit the register budget of two waves per SIMD.
-template <int MT, int NG, int WAVES>
+// workgroup; PART: split mode (partials out) instead of the fused epilogue.
+// A step covers KS = 4 / MT chunks of 32 K-values, so that the fragments of two
+// steps fit the register budget of two waves per SIMD.
+template <int MT, int NG, int WAVES, bool PART>
 __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(const DecArgs a) {
   constexpr int KS = 4 / MT;
   constexpr int KSTEP = 32 * KS;
   constexpr int NT = 64 * WAVES;
   constexpr int SLOT = NG * MT * 256;             // floats per wave's partial sums
+  constexpr int TSUM = PART ? 1 : 16 * MT * 16 * (NG - 1);
   __shared__ float red[WAVES * SLOT];
-  __shared__ float tsum[16 * MT * 16 * (NG - 1)];  // reduced t: [token][rank]
+  __shared__ float tsum[TSUM];                    // fused: reduced t, [token][rank]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j16 = lane & 15, g = lane >> 4;
@@ -77,11 +85,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(
   const int tile = unit / a.S, p = unit - tile * a.S;
 
   int bi = 0;
-  if (a.nblk > 1 && tile >= a.b[1].tile0) bi = 1;
-  if (a.nblk > 2 && tile >= a.b[2].tile0) bi = 2;
-  const DecBlk B = bi == 0 ? a.b[0] : (bi == 1 ? a.b[1] : a.b[2]);
+#pragma unroll
+  for (int i = 1; i < kMaxSegs; ++i)
+    if (i < a.nseg && tile >= a.g[i].tile0) bi = i;
+  const DecSeg B = a.g[bi];
 
-  const int vg = B.vg, wg = NG - vg;
+  const int vg = PART ? 0 : B.vg, wg = NG - vg;
   const int row0 = (tile - B.tile0) * 16 * wg;
   const int K = a.K;
   const int kbeg = p * a.kchunk;
@@ -92,7 +101,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(
   // and so do K chunks past this range (offset kOOB).
   const int Rv = min(16 * wg, B.N - row0);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(B.W0 + (size_t)row0 * K, (uint32_t)Rv * K * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(B.Vt, (uint32_t)B.r * K * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(B.Vt, PART ? 0u : (uint32_t)B.r * K * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((a.M - 1) * a.ldx + K) * 2);
   int roff[NG];
 #pragma unroll
@@ -105,13 +114,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(
     xoff[mt] = m < a.M ? m * a.ldx * 2 : kOOB;
   }
 
-  // Epilogue mapping: thread tid owns output row nl = tid % Rv and tokens
+  // Fused epilogue mapping: thread tid owns output row nl = tid % Rv and tokens
   // m = tid / Rv, tid / Rv + tpr, ...  Its s value and (for r <= 16) its U row are
   // requested now, so that their latency hides under the main loop.
-  const int r = B.r;
+  const int r = PART ? 0 : B.r;
   const int tpr = NT / Rv;                       // threads per output row (>= 1)
   const int nl_e = tid % Rv, m_e0 = tid / Rv;
-  const bool epi = m_e0 < tpr && m_e0 < a.M;
+  const bool epi = !PART && m_e0 < tpr && m_e0 < a.M;
   const int n_e = row0 + nl_e;
   const float s_e = epi ? bf2f(B.s[n_e]) : 0.f;
   uint4 u_pre0 = make_uint4(0, 0, 0, 0), u_pre1 = make_uint4(0, 0, 0, 0);
@@ -193,14 +202,25 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(
     for (int w = 0; w < WAVES; ++w) v += red[w * SLOT + idx];
     return v;
   };
-  // t[m][j] for this K range, once per workgroup.
+
+  if constexpr (PART) {
+    // Split mode: this tile's rows over this K range, as fp32 partials.
+    float *dst = a.part + (size_t)p * a.M * a.Wp + B.col + row0;
+    for (int e = tid; e < a.M * Rv; e += NT) {
+      const int m = e / Rv, nl = e - m * Rv;
+      dst[(size_t)m * a.Wp + nl] = red_at(nl >> 4, m, nl & 15);
+    }
+    return;
+  }
+
+  // t[m][j] over the whole K, once per workgroup.
   for (int e = tid; e < a.M * r; e += NT) {
     const int m = e / r, j = e - m * r;
     tsum[m * 16 * (NG - 1) + j] = red_at(j >> 4, m, j & 15);
   }
   __syncthreads();
 
-  // Epilogue: y_p = s * z_p + U t_p over this K range.
+  // Fused epilogue: y = s * z + U t.
   if (epi) {
     const uint16_t *u = B.U + (size_t)n_e * r;
     for (int m = m_e0; m < a.M; m += tpr) {
@@ -222,24 +242,67 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(
       } else {
         for (int j = 0; j < r; ++j) lr += bf2f(u[j]) * tm[j];
       }
-      const float yv = s_e * z + lr;
-      if (a.S == 1)
-        a.y[(size_t)m * a.ldy + B.col + n_e] = f2bf(yv);
-      else
-        a.part[((size_t)p * a.M + m) * a.Ntot + B.col + n_e] = yv;
+      a.y[(size_t)m * a.ldy + B.col + n_e] = f2bf(s_e * z + lr);
     }
   }
 }
 
-// y = bf16(sum over the S splits, in split order) for the split-K case.
-__global__ __launch_bounds__(256) void k_decode_reduce(const float *part, int S, int M, int Ntot,
-                                                       uint16_t *y, int ldy) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  const int m = blockIdx.y;
-  if (n >= Ntot) return;
-  float sum = 0.f;
-  for (int q = 0; q < S; ++q) sum += part[((size_t)q * M + m) * Ntot + n];
-  y[(size_t)m * ldy + n] = f2bf(sum);
+// Split mode, second kernel: y[m, col + n] = bf16(s[n] * Z[m, n] + U[n] . T[m])
+// with Z = sum_p z_p and T = sum_p t_p added in split order.  Workgroup
+// (chunk, m) owns 256 output columns of one block for one token m, so every
+// token runs in parallel; T[m] of its block is folded into LDS first.
+struct CombBlk {
+  const uint16_t *s, *U;
+  int N, r, col, tcol, chunk0, ufast;
+};
+
+struct CombArgs {
+  const float *part;
+  uint16_t *y;
+  int S, M, Wp, ldy, nblk;
+  CombBlk b[kMaxBlocks];
+};
+
+__global__ __launch_bounds__(256) void k_decode_combine(const CombArgs a) {
+  __shared__ float T[AQ_MAX_RANK];
+  const int chunk = blockIdx.x, m = blockIdx.y, tid = threadIdx.x;
+  int bi = 0;
+  if (a.nblk > 1 && chunk >= a.b[1].chunk0) bi = 1;
+  if (a.nblk > 2 && chunk >= a.b[2].chunk0) bi = 2;
+  const CombBlk B = bi == 0 ? a.b[0] : (bi == 1 ? a.b[1] : a.b[2]);
+  const int r = B.r;
+  const size_t pstride = (size_t)a.M * a.Wp;
+  const float *row = a.part + (size_t)m * a.Wp;
+
+  for (int j = tid; j < r; j += 256) {
+    float v = 0.f;
+    for (int q = 0; q < a.S; ++q) v += row[q * pstride + B.tcol + j];
+    T[j] = v;
+  }
+
+  const int n = (chunk - B.chunk0) * 256 + tid;
+  const bool live = n < B.N;
+  float z = 0.f, sn = 0.f;
+  if (live) {
+    sn = bf2f(B.s[n]);
+    for (int q = 0; q < a.S; ++q) z += row[q * pstride + B.col + n];
+  }
+  __syncthreads();
+  if (!live) return;
+
+  const uint16_t *u = B.U + (size_t)n * r;
+  float lr = 0.f;
+  if (B.ufast) {
+    for (int j0 = 0; j0 < r; j0 += 8) {
+      const uint4 uv = ld16(u + j0);
+      const uint32_t w4[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) lr += bf2f((uint16_t)(w4[q >> 1] >> ((q & 1) * 16))) * T[j0 + q];
+    }
+  } else {
+    for (int j = 0; j < r; ++j) lr += bf2f(u[j]) * T[j];
+  }
+  a.y[(size_t)m * a.ldy + B.col + n] = f2bf(sn * z + lr);
 }
 
 // ---------------------------------------------------------------- host side
@@ -265,11 +328,8 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
     vgmax = vgmax > pl->vg[b] ? vgmax : pl->vg[b];
   }
   const int ngmax = max_ng(pl->MT);
-  if (vgmax + 1 > ngmax) return false;          // rank too large for this kernel
-  // 32-bit buffer offsets: the row tile and Vt must stay below 2^31 bytes.
-  if ((int64_t)16 * ngmax * K * 2 >= (int64_t(1) << 31)) return false;
 
-  auto tiles_for = [&](int ng) {
+  auto fused_tiles = [&](int ng) {
     int t = 0;
     for (int b = 0; b < rq.nblk; ++b) {
       const int rows = 16 * (ng - pl->vg[b]);
@@ -277,121 +337,223 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
     }
     return t;
   };
-  const int ngmin = vgmax + 1 > 2 ? vgmax + 1 : 2;
+  auto split_tiles = [&](int ng) {
+    int t = 0;
+    for (int b = 0; b < rq.nblk; ++b)
+      t += (int)((rq.blk[b].N + 16 * ng - 1) / (16 * ng)) + (int)((rq.blk[b].r + 16 * ng - 1) / (16 * ng));
+    return t;
+  };
 
-  // Defaults, from sweeps over the Gemma-3-1B and large-decoder decode shapes on
-  // MI355X: 4 waves per workgroup; the largest row tile (least re-reading of Vt)
-  // that still gives >= 384 work units once K is split; K split only into
-  // ranges of >= 2304 values (a split costs fp32 partials and a reduce launch).
-  constexpr int kUnits = 384;
-  const int smax = K / 2304 > 1 ? K / 2304 : 1;
+  // Fused or split, from sweeps over the Gemma-3-1B and large-decoder decode
+  // shapes on MI355X.  Fused (the largest row tile that still gives >= 384
+  // workgroups) is kept while it fills the chip without a K split and its
+  // re-reads of Vt (every workgroup streams all of it) stay below ~24 MB, the
+  // traffic that the combine launch of split mode is worth.
+  constexpr int kUnitsFused = 384;
+  constexpr double kVtRereadLimit = 24e6;
+  const int ngmin = vgmax + 1 > 2 ? vgmax + 1 : 2;
+  bool split = true;
   int NG = ngmax;
-  while (NG - 1 >= ngmin && tiles_for(NG) * smax < kUnits) NG -= 1;
-  int ntiles = tiles_for(NG);
+  if (ngmin <= ngmax) {
+    while (NG - 1 >= ngmin && fused_tiles(NG) < kUnitsFused) NG -= 1;
+    double vt_bytes = 0;
+    for (int b = 0; b < rq.nblk; ++b) {
+      const int rows = 16 * (NG - pl->vg[b]);
+      vt_bytes += (double)((rq.blk[b].N + rows - 1) / rows) * 16.0 * pl->vg[b] * K * 2.0;
+    }
+    const bool fills = fused_tiles(NG) >= kUnitsFused || K < 2 * 2304;
+    split = !(fills && vt_bytes <= kVtRereadLimit);
+  }
+  // Tuning overrides (profiling sweeps): AQ_DECODE_SPLIT (0/1), AQ_DECODE_NG,
+  // AQ_DECODE_S, AQ_DECODE_WAVES.
+  const int sp_o = env_int("AQ_DECODE_SPLIT", -1);
+  if (sp_o == 1 || (sp_o == 0 && ngmin <= ngmax)) split = sp_o == 1;
+  int S = 1;
+  if (split) {
+    // Split mode: every work unit (a tile over one K range) moves the same
+    // bytes, and one workgroup per CU already keeps enough loads in flight, so
+    // the time follows the most loaded CU.  Score each tile height by
+    // units / (256 * ceil(units / 256)) and take the best, preferring tall
+    // tiles (less per-unit overhead).  Fewer than 256 tiles: split K until they
+    // cover the CUs, keeping ranges of >= 2048 values; 256 tiles or more: the
+    // split (up to 4) that evens the load best.
+    const int smax = K / 512 > 1 ? K / 512 : 1;
+    double best = -1e9;
+    for (int ng = ngmax; ng >= 1; --ng) {
+      const int t = split_tiles(ng);
+      int s_ng = 1;
+      if (t >= kNumCU) {
+        double eb = -1;
+        for (int sc = 1; sc <= 4 && sc <= smax; ++sc) {
+          const int u = t * sc;
+          const double e = (double)u / (kNumCU * ((u + kNumCU - 1) / kNumCU));
+          if (e > eb + 1e-3) { eb = e; s_ng = sc; }
+        }
+      } else {
+        s_ng = kNumCU / t;
+        if (s_ng > K / 2048) s_ng = K / 2048;
+        if (s_ng < 1) s_ng = 1;
+      }
+      const int u = t * s_ng;
+      const double score = (double)u / (kNumCU * ((u + kNumCU - 1) / kNumCU)) - 0.06 * (ngmax - ng);
+      if (score > best + 1e-9) { best = score; NG = ng; S = s_ng; }
+    }
+  }
+  const int ng_o = env_int("AQ_DECODE_NG", 0);
+  if (ng_o >= (split ? 1 : ngmin) && ng_o <= ngmax) NG = ng_o;
+  if (split) {
+    const int s_o = env_int("AQ_DECODE_S", 0);
+    if (s_o >= 1) S = s_o;
+  }
   int WAVES = 4;
-  int S = (kUnits + ntiles - 1) / ntiles;
-  S = S < 1 ? 1 : (S > smax ? smax : S);
-  // Tuning overrides (profiling sweeps): AQ_DECODE_NG, AQ_DECODE_S, AQ_DECODE_WAVES.
-  const int ng_o = env_int("AQ_DECODE_NG", 0), s_o = env_int("AQ_DECODE_S", 0);
   const int w_o = env_int("AQ_DECODE_WAVES", 0);
-  if (ng_o >= ngmin && ng_o <= ngmax) NG = ng_o;
-  if (s_o >= 1) S = s_o;
   if (w_o == 4 || (pl->MT == 1 && w_o == 8)) WAVES = w_o;
-  ntiles = tiles_for(NG);
 
   int kchunk = (K + S - 1) / S;
   kchunk = (kchunk + 127) / 128 * 128;
   S = (K + kchunk - 1) / kchunk;
+  // 32-bit buffer offsets: one tile's rows must stay below 2^31 bytes.
+  if ((int64_t)16 * NG * K * 2 >= (int64_t(1) << 31)) return false;
 
+  pl->split = split;
   pl->NG = NG;
   pl->S = S;
   pl->WAVES = WAVES;
   pl->kchunk = kchunk;
-  pl->ntiles = ntiles;
-  int t0 = 0;
+  int t0 = 0, nseg = 0, tcol = (int)rq.Ntot;
   for (int b = 0; b < rq.nblk; ++b) {
-    const int rows = 16 * (NG - pl->vg[b]);
-    pl->tile0[b] = t0;
-    pl->ntile[b] = (int)((rq.blk[b].N + rows - 1) / rows);
-    t0 += pl->ntile[b];
+    const Proj &P = rq.blk[b];
+    if (!split) {
+      const int rows = 16 * (NG - pl->vg[b]);
+      pl->seg[nseg++] = DecodeSeg{b, 0, t0, (int)((P.N + rows - 1) / rows)};
+      t0 += pl->seg[nseg - 1].ntile;
+      continue;
+    }
+    pl->seg[nseg++] = DecodeSeg{b, 0, t0, (int)((P.N + 16 * NG - 1) / (16 * NG))};
+    t0 += pl->seg[nseg - 1].ntile;
+    pl->tcol[b] = tcol;
+    if (P.r > 0) {
+      pl->seg[nseg++] = DecodeSeg{b, 1, t0, (int)((P.r + 16 * NG - 1) / (16 * NG))};
+      t0 += pl->seg[nseg - 1].ntile;
+      tcol += (int)P.r;
+    }
   }
-  pl->ws_bytes = S > 1 ? kWsReserved + (size_t)S * M * rq.Ntot * 4 : 0;
+  pl->nseg = nseg;
+  pl->ntiles = t0;
+  pl->Wp = tcol;
+  pl->ws_bytes = split ? kWsReserved + (size_t)S * M * tcol * 4 : 0;
   return true;
 }
 
-template <int MT, int NG, int WAVES>
+template <int MT, int NG, int WAVES, bool PART>
 static void launch_one(const DecArgs &a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_decode_bf16<MT, NG, WAVES>), dim3(grid), dim3(64 * WAVES), 0, st, a);
+  hipLaunchKernelGGL((k_decode_bf16<MT, NG, WAVES, PART>), dim3(grid), dim3(64 * WAVES), 0, st, a);
 }
 
-template <int MT, int WAVES>
+template <int MT, int WAVES, bool PART>
 static bool launch_ng(const DecArgs &a, int NG, int grid, hipStream_t st) {
   switch (NG) {
-    case 2: launch_one<MT, 2, WAVES>(a, grid, st); return true;
-    case 3: launch_one<MT, 3, WAVES>(a, grid, st); return true;
+    case 1:
+      if constexpr (PART) { launch_one<MT, 1, WAVES, PART>(a, grid, st); return true; }
+      return false;
+    case 2: launch_one<MT, 2, WAVES, PART>(a, grid, st); return true;
+    case 3: launch_one<MT, 3, WAVES, PART>(a, grid, st); return true;
     case 4:
-      if constexpr (MT < 4) { launch_one<MT, 4, WAVES>(a, grid, st); return true; }
+      if constexpr (MT < 4) { launch_one<MT, 4, WAVES, PART>(a, grid, st); return true; }
       return false;
     case 5:
-      if constexpr (MT == 2) { launch_one<MT, 5, WAVES>(a, grid, st); return true; }
+      if constexpr (MT == 2) { launch_one<MT, 5, WAVES, PART>(a, grid, st); return true; }
       return false;
     case 6:
-      if constexpr (MT == 2) { launch_one<MT, 6, WAVES>(a, grid, st); return true; }
+      if constexpr (MT == 2) { launch_one<MT, 6, WAVES, PART>(a, grid, st); return true; }
       return false;
   }
   return false;
 }
 
-template <int MT>
+template <int MT, bool PART>
 static bool launch_w(const DecArgs &a, int NG, int WAVES, int grid, hipStream_t st) {
   if constexpr (MT == 1) {
-    if (WAVES == 8) return launch_ng<1, 8>(a, NG, grid, st);
+    if (WAVES == 8) return launch_ng<1, 8, PART>(a, NG, grid, st);
   }
-  return WAVES == 4 ? launch_ng<MT, 4>(a, NG, grid, st) : false;
+  return WAVES == 4 ? launch_ng<MT, 4, PART>(a, NG, grid, st) : false;
+}
+
+template <bool PART>
+static bool launch_mt(const DecArgs &a, const DecodePlan &pl, int grid, hipStream_t st) {
+  switch (pl.MT) {
+    case 1: return launch_w<1, PART>(a, pl.NG, pl.WAVES, grid, st);
+    case 2: return launch_w<2, PART>(a, pl.NG, pl.WAVES, grid, st);
+    case 4: return launch_w<4, PART>(a, pl.NG, pl.WAVES, grid, st);
+  }
+  return false;
 }
 
 hipError_t launch_decode(const Recon &rq, const DecodePlan &pl, void *ws, hipStream_t st) {
   DecArgs a = {};
   a.x = (const uint16_t *)rq.x;
   a.y = (uint16_t *)rq.y;
-  a.part = pl.S > 1 ? (float *)((char *)ws + kWsReserved) : nullptr;
+  a.part = pl.split ? (float *)((char *)ws + kWsReserved) : nullptr;
   a.ldx = (int)rq.ldx;
   a.ldy = (int)rq.ldy;
   a.M = (int)rq.M;
   a.K = (int)rq.K;
-  a.Ntot = (int)rq.Ntot;
-  a.nblk = rq.nblk;
+  a.Wp = pl.Wp;
+  a.nseg = pl.nseg;
   a.ntiles = pl.ntiles;
   a.S = pl.S;
   a.kchunk = pl.kchunk;
-  for (int b = 0; b < rq.nblk; ++b) {
-    const Proj &P = rq.blk[b];
-    DecBlk &d = a.b[b];
-    d.W0 = (const uint16_t *)P.W0;
-    d.s = (const uint16_t *)P.s;
-    d.U = (const uint16_t *)P.U;
-    d.Vt = (const uint16_t *)P.Vt;
-    d.N = (int)P.N;
-    d.r = (int)P.r;
-    d.col = (int)P.col;
-    d.tile0 = pl.tile0[b];
-    d.vg = pl.vg[b];
-    d.ufast = (P.r % 8 == 0) && (((uintptr_t)P.U & 15) == 0);
+  for (int i = 0; i < pl.nseg; ++i) {
+    const DecodeSeg &sg = pl.seg[i];
+    const Proj &P = rq.blk[sg.b];
+    DecSeg &d = a.g[i];
+    d.tile0 = sg.tile0;
+    if (!pl.split) {
+      d.W0 = (const uint16_t *)P.W0;
+      d.s = (const uint16_t *)P.s;
+      d.U = (const uint16_t *)P.U;
+      d.Vt = (const uint16_t *)P.Vt;
+      d.N = (int)P.N;
+      d.r = (int)P.r;
+      d.col = (int)P.col;
+      d.vg = pl.vg[sg.b];
+      d.ufast = (P.r % 8 == 0) && (((uintptr_t)P.U & 15) == 0);
+    } else {
+      d.W0 = (const uint16_t *)(sg.isVt ? P.Vt : P.W0);
+      d.N = (int)(sg.isVt ? P.r : P.N);
+      d.col = sg.isVt ? pl.tcol[sg.b] : (int)P.col;
+    }
   }
   const int units = pl.ntiles * pl.S;
   const int grid = 8 * ((units + 7) / 8);
-  bool ok = false;
-  switch (pl.MT) {
-    case 1: ok = launch_w<1>(a, pl.NG, pl.WAVES, grid, st); break;
-    case 2: ok = launch_w<2>(a, pl.NG, pl.WAVES, grid, st); break;
-    case 4: ok = launch_w<4>(a, pl.NG, pl.WAVES, grid, st); break;
-  }
+  const bool ok = pl.split ? launch_mt<true>(a, pl, grid, st) : launch_mt<false>(a, pl, grid, st);
   if (!ok) return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.S == 1) return e;
-  dim3 rg((unsigned)((rq.Ntot + 255) / 256), (unsigned)rq.M);
-  hipLaunchKernelGGL(k_decode_reduce, rg, dim3(256), 0, st, (const float *)a.part, pl.S, a.M,
-                     a.Ntot, a.y, a.ldy);
+  if (e != hipSuccess || !pl.split) return e;
+
+  CombArgs c = {};
+  c.part = a.part;
+  c.y = a.y;
+  c.S = pl.S;
+  c.M = a.M;
+  c.Wp = pl.Wp;
+  c.ldy = a.ldy;
+  c.nblk = rq.nblk;
+  int chunks = 0;
+  for (int b = 0; b < rq.nblk; ++b) {
+    const Proj &P = rq.blk[b];
+    CombBlk &d = c.b[b];
+    d.s = (const uint16_t *)P.s;
+    d.U = (const uint16_t *)P.U;
+    d.N = (int)P.N;
+    d.r = (int)P.r;
+    d.col = (int)P.col;
+    d.tcol = pl.tcol[b];
+    d.chunk0 = chunks;
+    d.ufast = (P.r % 8 == 0) && (((uintptr_t)P.U & 15) == 0);
+    chunks += (int)((P.N + 255) / 256);
+  }
+  hipLaunchKernelGGL(k_decode_combine, dim3(chunks, c.M), dim3(256), 0, st, c);
   return hipGetLastError();
 }
 

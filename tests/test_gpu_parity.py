@@ -106,6 +106,40 @@ def test_fused_qkv_small(M):
         col += n
 
 
+# The streaming kernel meets the rank-r term either inside each workgroup (fused)
+# or with Vt rows as tiles of their own plus a combine kernel (split, with K
+# split over S workgroups).  The host picks one per dispatch; both are forced
+# here, over tile heights (NG 16-row groups) and split counts.
+_DECODE_MODES = [("0", None, None), ("1", None, None), ("1", 1, 1), ("1", 2, 3), ("1", 3, 7),
+                 ("1", 4, 2), ("1", 6, 5)]
+
+
+@pytest.mark.parametrize("M", [1, 7, 20, 40, 64])
+@pytest.mark.parametrize("split,ng,S", _DECODE_MODES)
+def test_decode_modes_qkv(M, split, ng, S, monkeypatch):
+    monkeypatch.setenv("AQ_DECODE_SPLIT", split)
+    if ng is not None:
+        monkeypatch.setenv("AQ_DECODE_NG", str(ng))
+        monkeypatch.setenv("AQ_DECODE_S", str(S))
+    K = 1048
+    shapes = [(200, 8), (40, 16), (24, 0)]
+    bds = [I.bundle("test", 3, f, K, n, r, "bf16", variant="s0" if f == "q" else "normal")
+           for f, (n, r) in zip(("q", "k", "v"), shapes)]
+    x = I.activations("test", 400 + M, M, K, "bf16")
+    y = B.recon_qkv(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+    assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in bds]), "bf16",
+                  f"M={M} split={split} NG={ng} S={S}")
+
+
+@pytest.mark.parametrize("M", [1, 16, 33, 64])
+@pytest.mark.parametrize("r", [49, 100, 256])
+def test_decode_high_rank_split(M, r):
+    """Ranks that no fused tile holds go to split mode (Vt rows as their own tiles)."""
+    bd, x = _single(M, 2048, 136, r, "bf16", variant="s0", layer=r, tag=500 + M)
+    y = B.recon_linear(up(x, "bf16"), bundle_up(bd, "bf16"))
+    assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"r={r} M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 16, 33, 130])
 def test_fused_gateup_small(M):
     K = 384
