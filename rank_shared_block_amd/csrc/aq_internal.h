@@ -70,7 +70,7 @@ hipError_t launch_decode(const Recon &rq, const DecodePlan &pl, void *ws, hipStr
 struct PrefillPlan {
   int ldt;                          // columns of the t buffer (sum of r rounded to 16)
   int tcol[kMaxBlocks];
-  int BM, BN, S;                    // output tile and K splits of the main pass
+  int BM, BN, BK, NST, S;           // output tile, K slice, LDS stages, K splits (main pass)
   int tBM, tBN, tS;                 // output tile and K splits of the rank-r (t) pass
   size_t tpart_off;                 // byte offset of the t-pass partials in the scratch
   size_t part_off;                  // byte offset of the main-pass partials in the scratch

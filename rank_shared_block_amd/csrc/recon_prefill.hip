@@ -7,33 +7,41 @@
 //     y[:, col_b + n]   = s_b[n] * (x W0_b^T)[:, n] + (t U_b^T)[:, n]
 // The pages run this as stock GEMMs (one over [W0^T, V], one block-diagonal
 // up-projection) plus an elementwise combine.  Here:
-// * pass 1: t = x [Vt_q; Vt_k; ...]^T for every block of the dispatch with the
-//   same GEMM kernel, into a bf16 [M, sum r] buffer of the caller's workspace.
-//   The contraction is long and the output narrow, so it is split along K into
-//   fp32 partials over enough workgroups to cover the CUs, and a small kernel
-//   folds them (in split order) into t;
-// * pass 2: the W0 contraction on v_mfma_f32_32x32x16_bf16 and an in-register
-//   epilogue: acc *= s[n], then acc += t U^T as r/16 further MFMA k-steps (t is
-//   the A operand, U the B operand, both read from L2), then one rounding to
-//   bf16.  t is an MFMA operand and therefore held in bf16; everything else is
-//   fp32 until the final store.
+// * pass 1 (rank-r pass): t = x [Vt_q; Vt_k; ...]^T for every block of the
+//   dispatch with the same GEMM kernel on small tiles.  The output is narrow and
+//   the contraction long, so K is split over enough workgroups to cover the CUs;
+//   the splits write fp32 partials and a small kernel folds them, in split order,
+//   into a bf16 [M, sum r] buffer of the caller's workspace;
+// * pass 2: the W0 contraction, and an in-register epilogue: acc *= s[n], then
+//   acc += t U^T as r/16 further MFMA k-steps (t the A operand, U the B operand,
+//   both read from L2), then one rounding to bf16.  t is an MFMA operand and so
+//   held in bf16; everything else is fp32 until the final store.
 //
-// GEMM design (gfx950):
-// * BM x BN output tile per workgroup of 4 waves (2 x 2), each wave a
-//   (BM/2) x (BN/2) block of 32x32 MFMA tiles; K in slices of 64.
+// GEMM design (gfx950, measured: v_mfma_f32_32x32x16_bf16 sustains ~2.2 PFLOP/s
+// over the chip, LDS reads > 180 B/clk/CU):
+// * BM x BN output tile per workgroup of 4 waves in a 2 x 2 grid, one wave per
+//   SIMD; each wave owns a (BM/2) x (BN/2) block of 32x32 MFMA tiles.  At
+//   256 x 256 a wave holds 16 accumulator tiles (256 registers, in AGPRs) and
+//   reads 8 fragments per 16 MFMAs, a quarter of the LDS bandwidth.
+// * K in slices of 32 (64 bytes per row) through a ring of 4 LDS stages, three
+//   slices in flight while one is multiplied: a slice of a 256 x 256 tile is
+//   ~1000 MFMA cycles, so three slices in flight cover a ~1.2 us load latency.
+//   Each stage is its own LDS object and the ring is unrolled, so the compiler
+//   can see that the loads landing in one stage never alias the fragment reads
+//   of another and does not wait for them.
 // * Operands go global -> LDS directly (buffer_load ... lds, 16 bytes per lane):
-//   no staging registers, and rows or K past the end fall outside the buffer
-//   resource and land in LDS as zeros.  Two LDS stages: the loads of slice s+1
-//   are in flight while slice s is multiplied.
-// * LDS rows are 128 bytes (64 bf16); the 16-byte chunk c of row r is stored at
-//   chunk position c ^ (r mod 8), so the 32 rows read by one MFMA fragment load
-//   hit different banks.
-// * The output tile is staged through LDS and written with 16-byte row-contiguous
-//   stores.  Tiles are handed to XCDs in contiguous ranges (m fastest), so the
-//   workgroups of one XCD share the W0 rows of a column tile in L2.
-// * When the tiles alone cannot cover the 256 CUs (short, wide layers), K is
-//   split over S workgroups that write fp32 partials (split 0 adds t U^T; all
-//   apply s), and a small kernel adds them in split order.  Deterministic.
+//   no staging registers; rows or K past the end fall outside the buffer
+//   resource and land in LDS as zeros.
+// * LDS rows are 64 bytes (4 chunks of 16 bytes); chunk c of row R sits at
+//   position c ^ ((R / 4) mod 4), so the 16 rows read by 16 lanes of one
+//   fragment load cover all 64 banks once.
+// * The output tile is staged through the (free) LDS stages 32 rows per wave
+//   row at a time and written with 16-byte row-contiguous stores.  Tiles are
+//   handed to XCDs in contiguous ranges (m fastest), so the workgroups of one
+//   XCD share the W0 rows of a column tile in L2.
+// * When the tiles cannot cover the 256 CUs (short, wide layers), K is split over
+//   S workgroups that write fp32 partials (split 0 adds t U^T; all apply s), and
+//   a small kernel adds them in split order.  Deterministic.
 
 #include <stdlib.h>
 
@@ -43,8 +51,7 @@
 namespace aq {
 
 namespace {
-constexpr int BK = 64;
-enum { EPI_PLAIN = 0, EPI_RECON = 1, EPI_PARTIAL = 2 };
+enum { MODE_RECON = 0, MODE_PART = 1, MODE_RAW = 2 };
 }  // namespace
 
 struct PfBlk {
@@ -57,10 +64,9 @@ struct PfBlk {
 struct PfArgs {
   const uint16_t *x;
   uint16_t *y;
-  float *part;             // [S][M][ldp] fp32 partials (EPI_PARTIAL)
-  const uint16_t *t;
+  float *part;             // [S][M][ldp] fp32 partials (MODE_PART, MODE_RAW)
+  const uint16_t *t;       // bf16 [M][ldt] (MODE_RECON, MODE_PART)
   int ldx, ldy, ldt, ldp, M, K, nblk, ntm, ntiles, S, kchunk, vec_store;
-  int raw;                 // EPI_PARTIAL without s and t U^T (the rank-r pass)
   PfBlk b[kMaxBlocks];
 };
 
@@ -84,18 +90,46 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint16_t *l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
 }
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16(const PfArgs a) {
+// s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 7, lgkmcnt 15).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence: the stage ring orders LDS itself
+// (explicit vmcnt waits for the direct loads; fragment reads are consumed by the
+// MFMAs before the barrier).  The memory clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Workgroups per CU a tile shape is built for: two when its LDS ring fits in
+// half of the 160 KiB (registers are then capped at 256 per lane).
+template <int BM, int BN, int BK, int NST>
+constexpr int gemm_occupancy() { return (BM + BN) * BK * 2 * NST <= 80 * 1024 ? 2 : 1; }
+
+template <int BM, int BN, int BK, int NST, int MODE>
+__global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_gemm_bf16(const PfArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2;          // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;        // 32x32 MFMA tiles per wave
-  constexpr int STAGE = (BM + BN) * BK;            // elements per LDS stage
-  // Two stages as two distinct LDS objects: the compiler can then tell that the
-  // direct loads in flight into one stage never alias the fragment reads of the
-  // other, and does not wait for them before reading.
-  __shared__ __attribute__((aligned(1024))) uint16_t lds0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds1[STAGE];
+  constexpr int STAGE = (BM + BN) * BK;            // bf16 elements per LDS stage
+  constexpr int CPR = BK / 8;                      // 16-byte chunks per LDS row
+  constexpr int RPL = 64 / CPR;                    // rows per 1 KiB load
+  constexpr int LA = BM / (4 * RPL), LB = BN / (4 * RPL);   // loads per wave per stage
+  constexpr int LPS = LA + LB;
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must be a multiple of 64");
+  static_assert(BK == 32 || BK == 64, "K slice of 32 or 64");
+  static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
+  // Each stage is its own LDS object; unused ones are a token size.
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[NST > 2 ? STAGE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[NST > 3 ? STAGE : 8];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave is read back from lane 0 so that the compiler knows it is uniform: the
+  // LDS address of a direct load (M0) is per wave.
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, lhi = lane >> 5;
   const int unit = xcd_contiguous_tile(blockIdx.x, a.ntiles * a.S);
   if (unit < 0) return;
@@ -118,27 +152,68 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const PfArgs a) {
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (size_t)m0 * a.ldx, (uint32_t)(((mrows - 1) * a.ldx + K) * 2));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(B.W + (size_t)n0 * K, nrows > 0 ? (uint32_t)nrows * K * 2 : 0u);
 
-  // Loader: instruction j of this wave fills 8 rows (1 KiB) of a stage; lane l
-  // takes row 8 q + l / 8 and chunk position l % 8, which holds global chunk
-  // (l % 8) ^ (row mod 8).
-  const int lrow = lane >> 3, lslot = lane & 7;
-  auto issue = [&](int slice, uint16_t *stage) {
-    const int k0 = kbeg + slice * BK;
-    uint16_t *As = stage, *Bs = stage + BM * BK;
+  // Swizzle: chunk c of LDS row R sits at position c ^ sw(R), with
+  // sw(R) = (R / 4) mod 4 for 4-chunk rows and (R / 2) mod 8 for 8-chunk rows,
+  // so the 16 rows that 16 lanes of a fragment load read cover all 64 banks
+  // once.  Loader: load j of this wave fills RPL rows (1 KiB) of a stage; lane
+  // l writes row RPL q + l / CPR at position l % CPR.
+  auto sw = [](int R) { return CPR == 4 ? (R >> 2) & 3 : (R >> 1) & 7; };
+  const int lrow = lane / CPR, lpos = lane % CPR;
+  int aoff[LA], boff[LB], achk[LA], bchk[LB];
 #pragma unroll
-    for (int j = 0; j < BM / 32; ++j) {
-      const int q = wave * (BM / 32) + j, row = 8 * q + lrow;
-      const int kk = k0 + 8 * (lslot ^ (row & 7));
-      const int off = (slice < nk && kk < kend) ? (row * a.ldx + kk) * 2 : kOOB;
-      lds_load16(rx, As + q * 512, off);
-    }
+  for (int j = 0; j < LA; ++j) {
+    const int row = (wave * LA + j) * RPL + lrow;
+    aoff[j] = row * a.ldx * 2;
+    achk[j] = lpos ^ sw(row);
+  }
 #pragma unroll
-    for (int j = 0; j < BN / 32; ++j) {
-      const int q = wave * (BN / 32) + j, row = 8 * q + lrow;
-      const int kk = k0 + 8 * (lslot ^ (row & 7));
-      const int off = (slice < nk && kk < kend) ? (row * K + kk) * 2 : kOOB;
-      lds_load16(rw, Bs + q * 512, off);
+  for (int j = 0; j < LB; ++j) {
+    const int row = (wave * LB + j) * RPL + lrow;
+    boff[j] = row * K * 2;
+    bchk[j] = lpos ^ sw(BM + row);
+  }
+  // The epilogue's rank-r term (see below) needs the tile's rows of t and U.
+  // They ride on the slices issued past the end of the ring (nkp .. nkp +
+  // NST - 2, never multiplied): rank chunk c (ranks BK c .. BK c + BK - 1) as
+  // slice nkp + c, t rows where x rows go and U rows where W rows go, so that
+  // their latency hides under the last steps.  Ranks past r16 (t) or r (U) and
+  // rows past M or N read as zero; U takes this path only with 16-byte aligned
+  // rows (ufast).
+  const bool addu = MODE != MODE_RAW && (MODE == MODE_RECON || p == 0) && B.r > 0;
+  const int r16 = (B.r + 15) & ~15;
+  const __amdgpu_buffer_rsrc_t rt =
+      make_rsrc(a.t + (size_t)m0 * a.ldt, addu ? (uint32_t)(mrows * a.ldt * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t ru =
+      make_rsrc(B.U + (size_t)n0 * B.r, addu && nrows > 0 && B.ufast ? (uint32_t)(nrows * B.r * 2) : 0u);
+  auto eoff_a = [&](int d, int c) __attribute__((always_inline)) {
+    const int row = (wave * LA + d) * RPL + lrow, col = BK * c + 8 * achk[d];
+    return col < r16 ? (row * a.ldt + B.tcol + col) * 2 : kOOB;
+  };
+  auto eoff_b = [&](int d, int c) __attribute__((always_inline)) {
+    const int row = (wave * LB + d) * RPL + lrow, col = BK * c + 8 * bchk[d];
+    return col < B.r ? (row * B.r + col) * 2 : kOOB;
+  };
+
+  // Every load is issued (an out-of-range offset for K past the range or a
+  // slice past the last), selected without branches, so that the number of
+  // loads per stage is fixed and the compiler's wait counting stays exact.
+  // Load d of a stage: d < LA an x (A) block, else a W (B) block; with
+  // ech >= 0 the blocks of rank chunk ech instead.
+  auto dma = [&](int d, int k0, int klim, int ech, uint16_t *stage) __attribute__((always_inline)) {
+    if (d < LA) {
+      const int kk = k0 + 8 * achk[d];
+      const int off = kk < klim ? aoff[d] + kk * 2 : kOOB;
+      lds_load16(ech >= 0 ? rt : rx, stage + (wave * LA + d) * 512, ech >= 0 ? eoff_a(d, ech) : off);
+    } else {
+      const int kk = k0 + 8 * bchk[d - LA];
+      const int off = kk < klim ? boff[d - LA] + kk * 2 : kOOB;
+      lds_load16(ech >= 0 ? ru : rw, stage + BM * BK + (wave * LB + d - LA) * 512, ech >= 0 ? eoff_b(d - LA, ech) : off);
     }
+  };
+  auto issue = [&](int slice, uint16_t *stage) __attribute__((always_inline)) {
+    const int k0 = kbeg + slice * BK, klim = slice < nk ? kend : -1;
+#pragma unroll
+    for (int d = 0; d < LPS; ++d) dma(d, k0, klim, -1, stage);
   };
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -150,121 +225,211 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const PfArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  auto compute = [&](const uint16_t *stage) {
-    const uint16_t *As = stage, *Bs = stage + BM * BK;
+  // Fragment reads: lane (l32, lhi) reads row R = base + l32 at chunk
+  // 2 kk + lhi; every base is a multiple of 32, so sw(R) = sw(l32).
+  const int swz = sw(l32);
+  const int arow = (wm * WM + l32) * BK, brow = (BM + wn * WN + l32) * BK;
+  auto frags = [&](const uint16_t *stage, int kk, bf16x8 (&af)[TM], bf16x8 (&bf)[TN]) __attribute__((always_inline)) {
+    const int c = 8 * ((2 * kk + lhi) ^ swz);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = 2 * kk + lhi;          // 16-byte chunk of the 64-wide row
-      bf16x8 af[TM], bf[TN];
+    for (int i = 0; i < TM; ++i) af[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(stage + arow + i * 32 * BK + c));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(stage + brow + j * 32 * BK + c));
+  };
+
+  // One step of the ring: multiply the stage `cur` while the loads of slice
+  // `nslice` into `next` go out.  The loads are spread over the MFMA stream (a
+  // group of TN MFMAs per slot, KK * TM slots) instead of being issued in one
+  // burst: the texture unit takes 16 cycles per 1 KiB load, and a wave whose
+  // load cannot issue stalls its MFMAs too.  The fragments of k-step kk + 1 are
+  // read while k-step kk is multiplied.
+  constexpr int KK = BK / 16, SLOTS = KK * TM;
+  const int nkp = (nk + NST - 1) / NST * NST;    // slices past nk are zeros
+  const int nchunk = (r16 + BK - 1) / BK;          // rank chunks of the epilogue
+  // ... riding on the tail slices (all but the last, or all but the last two
+  // when the output block needs two stages for staging)
+  constexpr int ESLOTS = 64 * (BN + 8) <= STAGE ? NST - 1 : NST - 2;
+  const int nech = addu ? min(nchunk, ESLOTS) : 0;
+  auto step = [&](int nslice, uint16_t *next, const uint16_t *cur) __attribute__((always_inline)) {
+    const int k0 = kbeg + nslice * BK, klim = nslice < nk ? kend : -1;
+    const int ech = nslice >= nkp && nslice - nkp < nech ? nslice - nkp : -1;
+    bf16x8 fa[2][TM], fb[2][TN];
+    frags(cur, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + i * 32 + l32;
-        af[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + row * BK + 8 * (c ^ (row & 7))));
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = wn * WN + j * 32 + l32;
-        bf[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(Bs + row * BK + 8 * (c ^ (row & 7))));
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
+        // W rows are the A operand and x rows the B operand, so that the
+        // result comes out transposed: a lane holds 4 consecutive output
+        // columns of one output row per group of 4 values.
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j], 0, 0, 0);
+        const int t = kk * TM + i;
+#pragma unroll
+        for (int d = t * LPS / SLOTS; d < (t + 1) * LPS / SLOTS; ++d) dma(d, k0, klim, ech, next);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
-  // Slice s lives in stage s % 2.  The loads of slice s + 1 are in flight while
-  // slice s is multiplied; past the last slice the loads are out of range (no
-  // memory traffic, zeros into an unused stage).
-  issue(0, lds0);
-  for (int s = 0; s < nk; s += 2) {
-    __builtin_amdgcn_s_waitcnt(0);       // this wave's loads of slice s have landed
-    __syncthreads();                     // ... and everyone's; slice s - 1 consumed
-    issue(s + 1, lds1);
-    compute(lds0);
-    if (s + 1 >= nk) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    issue(s + 2, lds0);
-    compute(lds1);
+  // Slice s lives in stage s % NST.  At step s: wait until this wave's loads of
+  // slice s have landed (the NST - 2 younger slices may still be in flight),
+  // then a barrier (everyone's have landed, and everyone is done with slice
+  // s - 1), then slice s is multiplied while the loads of slice s + NST - 1 go
+  // into the stage of slice s - 1.  Past the last slice the loads are out of
+  // range (zeros, no memory traffic), which keeps the wait counts uniform.
+  // The ring is written out per stage count with the stage objects named, so
+  // that the compiler keeps their distinct alias scopes and adds no waits.
+#define AQ_STEP(slice, next, cur)            \
+  wait_vmcnt<(NST - 2) * LPS>();             \
+  ring_barrier();                            \
+  step((slice) + NST - 1, next, cur);
+  issue(0, st0);                         // slices 0 .. NST - 2 ahead of the loop
+  if constexpr (NST > 2) issue(1, st1);
+  if constexpr (NST > 3) issue(2, st2);
+  for (int s = 0; s < nkp; s += NST) {
+    if constexpr (NST == 2) {
+      AQ_STEP(s, st1, st0)
+      AQ_STEP(s + 1, st0, st1)
+    } else if constexpr (NST == 3) {
+      AQ_STEP(s, st2, st0)
+      AQ_STEP(s + 1, st0, st1)
+      AQ_STEP(s + 2, st1, st2)
+    } else {
+      AQ_STEP(s, st3, st0)
+      AQ_STEP(s + 1, st0, st1)
+      AQ_STEP(s + 2, st1, st2)
+      AQ_STEP(s + 3, st2, st3)
+    }
   }
+#undef AQ_STEP
   __builtin_amdgcn_s_waitcnt(0);         // drain the (out-of-range) tail loads
 
-  // ---- epilogue.  MFMA 32x32 output layout: lane holds column (lane % 32) and
-  // rows 8 (v / 4) + 4 (lane / 32) + (v % 4), v = 0..15.
-  if (EPI != EPI_PLAIN && !a.raw) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * WN + j * 32 + l32;
-      const float sv = n < B.N ? bf2f(B.s[n]) : 0.f;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][j] *= sv;
-    }
-    if (EPI == EPI_RECON || p == 0) {
-      for (int jc = 0; jc < B.r; jc += 16) {
-        const int jj = jc + 8 * lhi;
-        bf16x8 ta[TM], ub[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int m = m0 + wm * WM + i * 32 + l32;
-          ta[i] = m < M ? as_bf16x8(ld16(a.t + (size_t)m * a.ldt + B.tcol + jj)) : zero_bf16x8();
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int n = n0 + wn * WN + j * 32 + l32;
-          ub[j] = n < B.N ? load_u8(B, n, jj) : zero_bf16x8();
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[i], ub[j], acc[i][j], 0, 0, 0);
-      }
-    }
-  }
-
-  if (EPI == EPI_PARTIAL) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 32 + l32;
-        if (n >= B.Nst) continue;            // padding columns carry zeros
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
-          if (m < M) a.part[((size_t)p * M + m) * a.ldp + B.col + n] = acc[i][j][v];
-        }
-      }
-    return;
-  }
-
-  // Stage the bf16 tile through LDS, half a tile (one wave row) at a time, then
-  // write rows with 16-byte stores.
+  // ---- epilogue, one 32-row block of each wave row per round.  MFMA 32x32
+  // output layout with W as the A operand: lane holds output row
+  // m = mbase + lane % 32 and output columns n = nbase + 8 (v / 4) +
+  // 4 (lane / 32) + (v % 4), v = 0..15.
+  // The rank-r term w = t U^T is one more contraction, over r instead of K.
+  // Rank chunk c < NST - 1 sits in stage c, laid out like a K slice (it came
+  // with the tail of the ring); chunks past those (r > BK (NST - 1)) are read
+  // straight from global memory.  Per round i and column block j, w goes into
+  // 16 fresh accumulators, then y = s * acc + w is written: fp32 partials
+  // directly, bf16 through stage NST - 1 (8 bytes per lane and column group).
+  // The rank-r pass (MODE_RAW) writes acc itself (no s, no w).
+  constexpr int OP = BN + 8;                     // staging row pitch (bank spread, 16-byte rows)
+  // Output staging: wave row 0's 32 rows in ost0, wave row 1's in ost1 (the
+  // last stage holds both when it can, else the last two stages).
+  static_assert(32 * OP <= STAGE && ESLOTS >= 1, "staging and one rank chunk must fit");
+  uint16_t *const slast = NST == 2 ? st1 : (NST == 3 ? st2 : st3);
+  uint16_t *const sprev = NST == 2 ? st0 : (NST == 3 ? st1 : st2);
+  uint16_t *const ost0 = ESLOTS == NST - 1 ? slast : sprev;
+  uint16_t *const ost1 = ESLOTS == NST - 1 ? slast + 32 * OP : slast;
+  __shared__ float s_lds[BN];
+  const bool fp32_out = MODE == MODE_PART || (MODE == MODE_RAW && a.part);
   const int nst = min(BN, B.Nst - n0);
-#pragma unroll 1
-  for (int h = 0; h < 2; ++h) {
-    __syncthreads();                     // previous users of lds0 are done
-    if (wm == h) {
+  if (MODE != MODE_RAW)
+    for (int c = tid; c < BN; c += 256) s_lds[c] = n0 + c < B.N ? bf2f(B.s[n0 + c]) : 0.f;
+  __syncthreads();                       // s_lds, and every wave's last loads, are in
+
+  // Rank-r fragments (this lane's 8 ranks of rank step kk): chunks c < nech
+  // from stage c, the rest from global memory.
+  auto tfrag_lds = [&](const uint16_t *stc, int i, int kk) __attribute__((always_inline)) {
+    return as_bf16x8(*reinterpret_cast<const uint4 *>(stc + arow + i * 32 * BK + 8 * ((2 * kk + lhi) ^ swz)));
+  };
+  auto ufrag_lds = [&](const uint16_t *stc, int j, int kk) __attribute__((always_inline)) {
+    return as_bf16x8(*reinterpret_cast<const uint4 *>(stc + brow + j * 32 * BK + 8 * ((2 * kk + lhi) ^ swz)));
+  };
+  auto tfrag_glb = [&](int i, int col) __attribute__((always_inline)) {
+    const int m = m0 + wm * WM + i * 32 + l32;
+    return m < M && col < r16 ? as_bf16x8(ld16(a.t + (size_t)m * a.ldt + B.tcol + col)) : zero_bf16x8();
+  };
+  auto ufrag_glb = [&](int j, int col) __attribute__((always_inline)) {
+    const int n = n0 + wn * WN + j * 32 + l32;
+    return n < B.N ? load_u8(B, n, col) : zero_bf16x8();
+  };
+  const int nch = (r16 + BK - 1) / BK;
+
+  // Column blocks per rank-r pass: every block's MFMA chain at once where the
+  // registers allow, else two at a time.
+  constexpr int JH = (gemm_occupancy<BM, BN, BK, NST>() == 1 && TM * TN <= 8) ? TN : (TN >= 2 ? 2 : 1);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * WM + i * 32 + l32;
+    uint16_t *const ost = wm ? ost1 : ost0;
+    if (!fp32_out) __syncthreads();      // the previous round's reads of the staging are done
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+    for (int j0 = 0; j0 < TN; j0 += JH) {
+      f32x16 w[JH];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int ml = i * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
-            const int nl = wn * WN + j * 32 + l32;
-            lds0[ml * BN + nl] = f2bf(acc[i][j][v]);
+      for (int q = 0; q < JH; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) w[q][v] = 0.f;
+      if (addu) {
+#pragma unroll
+        for (int c = 0; c < ESLOTS; ++c) {
+          if (c >= nech) break;
+          const uint16_t *stc = c == 0 ? st0 : (c == 1 ? st1 : st2);
+          const int kmax = min(BK / 16, (r16 - BK * c) / 16);
+          for (int kk = 0; kk < kmax; ++kk) {
+            const bf16x8 tb = tfrag_lds(stc, i, kk);
+#pragma unroll
+            for (int q = 0; q < JH; ++q) {
+              const bf16x8 ua = B.ufast ? ufrag_lds(stc, j0 + q, kk) : ufrag_glb(j0 + q, BK * c + 16 * kk + 8 * lhi);
+              w[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua, tb, w[q], 0, 0, 0);
+            }
           }
+        }
+        for (int c = nech; c < nch; ++c) {
+          const int kmax = min(BK / 16, (r16 - BK * c) / 16);
+          for (int kk = 0; kk < kmax; ++kk) {
+            const int col = BK * c + 16 * kk + 8 * lhi;
+            const bf16x8 tb = tfrag_glb(i, col);
+#pragma unroll
+            for (int q = 0; q < JH; ++q)
+              w[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ufrag_glb(j0 + q, col), tb, w[q], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < JH; ++q) {
+        const int j = j0 + q;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nl = wn * WN + j * 32 + 8 * g + 4 * lhi;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e];
+          if (MODE != MODE_RAW) {
+            const float4 sc = *reinterpret_cast<const float4 *>(s_lds + nl);
+            o[0] = sc.x * o[0] + w[q][4 * g + 0];
+            o[1] = sc.y * o[1] + w[q][4 * g + 1];
+            o[2] = sc.z * o[2] + w[q][4 * g + 2];
+            o[3] = sc.w * o[3] + w[q][4 * g + 3];
+          }
+          if (fp32_out) {
+            if (m < M) {
+              float *dst = a.part + ((size_t)p * M + m) * a.ldp + B.col + n0 + nl;
+              for (int e = 0; e < 4 && nl + e < nst; ++e) dst[e] = o[e];
+            }
+          } else {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            const bf16x4 h = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+            *reinterpret_cast<uint2 *>(ost + l32 * OP + nl) = __builtin_bit_cast(uint2, h);
+          }
+        }
+      }
     }
+    if (fp32_out) continue;
     __syncthreads();
-    for (int c = tid; c < WM * (BN / 8); c += 256) {
-      const int ml = c / (BN / 8), nc = (c - ml * (BN / 8)) * 8;
-      const int m = m0 + h * WM + ml;
-      if (m >= M || nc >= nst) continue;
-      uint16_t *dst = a.y + (size_t)m * a.ldy + B.col + n0 + nc;
-      const uint16_t *src = lds0 + ml * BN + nc;
+    for (int c = tid; c < 64 * (BN / 8); c += 256) {
+      const int rl = c / (BN / 8), nc = (c - rl * (BN / 8)) * 8;
+      const int h = rl >> 5;
+      const int mr = m0 + h * WM + i * 32 + (rl & 31);
+      if (mr >= M || nc >= nst) continue;
+      uint16_t *dst = a.y + (size_t)mr * a.ldy + B.col + n0 + nc;
+      const uint16_t *src = (h ? ost1 : ost0) + (rl & 31) * OP + nc;
       if (a.vec_store && nc + 8 <= nst) {
         *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
       } else {
@@ -291,7 +456,7 @@ __global__ __launch_bounds__(256) void k_prefill_reduce(const float *part, int S
 namespace {
 
 struct TileCfg {
-  int BM, BN, S;
+  int BM, BN, BK, NST, S;
 };
 
 static int env_int(const char *name, int dflt) {
@@ -310,25 +475,51 @@ int count_tiles(const Recon &rq, int BM, int BN, bool tpass) {
   return t;
 }
 
-// Output tile and K split of the main pass.  Measured on MI355X over the
-// Gemma-3-1B and large-decoder prefill shapes, 128 x 128 tiles were fastest in
-// every case (two workgroups per CU); K is split when the tiles cover fewer than
-// two workgroups per CU, as long as each split keeps >= 1024 K values.
+// Compiled main-pass tile shapes: BM x BN output, BK-wide K slices through NST
+// LDS stages; workgroups resident per CU follow from the LDS ring.
+struct Cand {
+  int BM, BN, BK, NST;
+};
+static const Cand kCands[] = {{128, 128, 64, 4}, {256, 128, 32, 3}, {256, 128, 64, 3}, {256, 256, 32, 4},
+                               {256, 256, 64, 2}, {128, 256, 64, 3}, {128, 128, 64, 2}, {256, 128, 32, 3},
+                               {128, 256, 32, 3}, {128, 128, 32, 4}};
+
+// Main-pass tile and K split, from sweeps over the Gemma-3-1B and
+// large-decoder prefill shapes on MI355X (per-tile times there: 128 x 128 with
+// four stages ~15 us at K = 1152, one workgroup per CU; 256 x 128 with three
+// 32-wide stages ~21 us per tile with two workgroups per CU overlapping each
+// other's epilogues):
+// * up to 256 tiles of 128 x 128 (one round on the CUs): 128 x 128, four
+//   stages, K split only for long K (>= 4096) when the tiles cover at most half
+//   of the CUs (ranges of >= 2048);
+// * more: 256 x 128, two per CU, unless its last round would be mostly empty
+//   (under 1.5 rounds of 512), then 256 x 128 one per CU with 64-wide slices.
 TileCfg choose(const Recon &rq) {
-  TileCfg best = {128, 128, 1};
-  const int tiles = count_tiles(rq, 128, 128, false);
-  if (tiles > 0 && tiles < 2 * kNumCU) {
-    const int S = (2 * kNumCU + tiles - 1) / tiles;
-    const int smax = rq.K / 1024 > 1 ? (int)(rq.K / 1024) : 1;
-    best.S = S < smax ? S : smax;
+  const int t128 = count_tiles(rq, 128, 128, false);
+  TileCfg tc = {128, 128, 64, 4, 1};
+  if (t128 > kNumCU) {
+    const int t = count_tiles(rq, 256, 128, false);
+    const double rounds = (double)t / (2 * kNumCU);
+    if (rounds < 1.5 && rounds > 1.0)
+      tc = {256, 128, 64, 3, 1};
+    else
+      tc = {256, 128, 32, 3, 1};
+  } else if (rq.K >= 4096 && t128 > 0 && 2 * t128 <= kNumCU) {
+    const int S = kNumCU / t128, smax = (int)(rq.K / 2048);
+    tc.S = S < smax ? S : smax;
   }
-  // Tuning overrides (profiling sweeps).
+  // Tuning overrides (profiling sweeps): AQ_PREFILL_BM/BN/BK/NST pick a compiled
+  // shape, AQ_PREFILL_S the K split.
   const int bm = env_int("AQ_PREFILL_BM", 0), bn = env_int("AQ_PREFILL_BN", 0);
+  const int bk = env_int("AQ_PREFILL_BK", 0), ns = env_int("AQ_PREFILL_NST", 0);
+  for (const Cand &c : kCands)
+    if (c.BM == bm && c.BN == bn && (bk == 0 || c.BK == bk) && (ns == 0 || c.NST == ns)) {
+      tc.BM = c.BM, tc.BN = c.BN, tc.BK = c.BK, tc.NST = c.NST;
+      break;
+    }
   const int so = env_int("AQ_PREFILL_S", 0);
-  if ((bm == 128 || bm == 256) && (bn == 128 || bn == 256) && !(bm == 256 && bn == 256))
-    best.BM = bm, best.BN = bn;
-  if (so >= 1) best.S = so;
-  return best;
+  if (so >= 1) tc.S = so;
+  return tc;
 }
 
 }  // namespace
@@ -343,16 +534,20 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
   const TileCfg tc = choose(rq);
   pl->BM = tc.BM;
   pl->BN = tc.BN;
+  pl->BK = tc.BK;
+  pl->NST = tc.NST;
   pl->S = tc.S;
-  // Rank-r pass: 64 x 128 tiles over t's columns (a narrow output, so small
-  // tiles keep enough workgroups busy); K is split only when it is long, and
-  // then a small kernel folds the fp32 partials.
+  // Rank-r pass: 64 x 64 tiles over t's columns, K split so that the
+  // workgroups cover the CUs with ranges of >= 128 K values; the fp32 partials
+  // are folded into the bf16 t buffer by the reduce kernel.
   pl->tBM = 64;
-  pl->tBN = 128;
+  pl->tBN = 64;
   pl->tS = 1;
   if (c > 0) {
-    const int kslices = (int)((rq.K + BK - 1) / BK);
-    pl->tS = (kslices + 35) / 36;                            // <= 36 K slices per split
+    const int tiles = count_tiles(rq, 64, 64, true);
+    int S = (kNumCU + tiles - 1) / tiles;
+    const int smax = rq.K / 128 > 1 ? (int)(rq.K / 128) : 1;
+    pl->tS = S < smax ? S : smax;
     const int to = env_int("AQ_TPASS_S", 0);
     if (to >= 1) pl->tS = to;
   }
@@ -365,22 +560,31 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
   pl->ws_bytes = bytes > 0 ? kWsReserved + bytes : 0;
 }
 
-template <int EPI>
-static void launch_tile(int BM, int BN, const PfArgs &a, int grid, hipStream_t st) {
-  if (BM == 64) {
-    if constexpr (EPI != EPI_RECON)
-      hipLaunchKernelGGL((k_gemm_bf16<64, 128, EPI>), dim3(grid), dim3(256), 0, st, a);
-    return;
+template <int MODE>
+static bool launch_tile(int BM, int BN, int BK, int NST, const PfArgs &a, int grid, hipStream_t st) {
+#define AQ_TILE(bm, bn, bk, ns)                                                                       \
+  if (BM == bm && BN == bn && BK == bk && NST == ns) {                                               \
+    hipLaunchKernelGGL((k_gemm_bf16<bm, bn, bk, ns, MODE>), dim3(grid), dim3(256), 0, st, a);        \
+    return true;                                                                                      \
   }
-  if (BM == 256 && BN == 128)
-    hipLaunchKernelGGL((k_gemm_bf16<256, 128, EPI>), dim3(grid), dim3(256), 0, st, a);
-  else if (BM == 128 && BN == 256)
-    hipLaunchKernelGGL((k_gemm_bf16<128, 256, EPI>), dim3(grid), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_gemm_bf16<128, 128, EPI>), dim3(grid), dim3(256), 0, st, a);
+  if constexpr (MODE == MODE_RAW) {
+    AQ_TILE(64, 64, 64, 4)
+  } else {
+    AQ_TILE(256, 256, 32, 4)
+    AQ_TILE(256, 256, 64, 2)
+    AQ_TILE(256, 128, 64, 3)
+    AQ_TILE(128, 256, 64, 3)
+    AQ_TILE(128, 128, 64, 2)
+    AQ_TILE(128, 128, 64, 4)
+    AQ_TILE(256, 128, 32, 3)
+    AQ_TILE(128, 256, 32, 3)
+    AQ_TILE(128, 128, 32, 4)
+  }
+#undef AQ_TILE
+  return false;
 }
 
-static hipError_t run(PfArgs &a, int BM, int BN, int epi, hipStream_t st) {
+static hipError_t run(PfArgs &a, int BM, int BN, int BK, int NST, int mode, hipStream_t st) {
   a.ntm = (a.M + BM - 1) / BM;
   int t0 = 0;
   for (int b = 0; b < a.nblk; ++b) {
@@ -392,11 +596,13 @@ static hipError_t run(PfArgs &a, int BM, int BN, int epi, hipStream_t st) {
   if (t0 == 0) return hipSuccess;
   const int units = t0 * a.S;
   const int grid = 8 * ((units + 7) / 8);
-  switch (epi) {
-    case EPI_PLAIN: launch_tile<EPI_PLAIN>(BM, BN, a, grid, st); break;
-    case EPI_RECON: launch_tile<EPI_RECON>(BM, BN, a, grid, st); break;
-    default: launch_tile<EPI_PARTIAL>(BM, BN, a, grid, st); break;
+  bool ok = false;
+  switch (mode) {
+    case MODE_RECON: ok = launch_tile<MODE_RECON>(BM, BN, BK, NST, a, grid, st); break;
+    case MODE_PART: ok = launch_tile<MODE_PART>(BM, BN, BK, NST, a, grid, st); break;
+    default: ok = launch_tile<MODE_RAW>(BM, BN, BK, NST, a, grid, st); break;
   }
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -409,18 +615,15 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
   a.M = (int)rq.M;
   a.K = (int)rq.K;
 
-  // pass 1: t = x Vt^T for every block with r > 0 (columns padded to 16 with
-  // zeros), split along K into fp32 partials when that fills more CUs.
+  // pass 1: fp32 partials of t = x Vt^T for every block with r > 0 (columns
+  // padded to 16 with zeros), then folded into the bf16 t buffer.
   if (pl.ldt > 0) {
     PfArgs t = a;
-    t.y = tbuf;
-    t.ldy = pl.ldt;
     t.S = pl.tS;
     int tkc = (int)((rq.K + pl.tS - 1) / pl.tS);
-    t.kchunk = (tkc + BK - 1) / BK * BK;
-    t.vec_store = 1;
-    t.raw = 1;
-    t.part = pl.tS > 1 ? (float *)(scratch + pl.tpart_off) : nullptr;
+    t.kchunk = (tkc + 63) / 64 * 64;
+    t.S = (int)((rq.K + t.kchunk - 1) / t.kchunk);
+    t.part = (float *)(scratch + pl.tpart_off);
     t.ldp = pl.ldt;
     t.nblk = 0;
     for (int b = 0; b < rq.nblk; ++b) {
@@ -432,12 +635,18 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
       d.Nst = (int)((rq.blk[b].r + 15) / 16 * 16);
       d.col = pl.tcol[b];
     }
-    hipError_t e = run(t, pl.tBM, pl.tBN, pl.tS > 1 ? EPI_PARTIAL : EPI_PLAIN, st);
+    if (t.S == 1) {                  // no K split: bf16 t straight from the tile
+      t.part = nullptr;
+      t.y = tbuf;
+      t.ldy = pl.ldt;
+      t.vec_store = 1;
+    }
+    hipError_t e = run(t, pl.tBM, pl.tBN, 64, 4, MODE_RAW, st);
     if (e != hipSuccess) return e;
-    if (pl.tS > 1) {
+    if (t.S > 1) {
       const long n = (long)rq.M * pl.ldt;
       hipLaunchKernelGGL(k_prefill_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                         (const float *)t.part, pl.tS, (int)rq.M, pl.ldt, pl.ldt, tbuf, pl.ldt);
+                         (const float *)t.part, t.S, (int)rq.M, pl.ldt, pl.ldt, tbuf, pl.ldt);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -448,11 +657,11 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
   a.ldy = (int)rq.ldy;
   a.t = tbuf;
   a.ldt = pl.ldt;
-  a.S = pl.S;
   int kc = (int)((rq.K + pl.S - 1) / pl.S);
-  a.kchunk = (kc + BK - 1) / BK * BK;
+  a.kchunk = (kc + pl.BK - 1) / pl.BK * pl.BK;
+  a.S = (int)((rq.K + a.kchunk - 1) / a.kchunk);
   a.nblk = rq.nblk;
-  a.part = pl.S > 1 ? (float *)(scratch + pl.part_off) : nullptr;
+  a.part = a.S > 1 ? (float *)(scratch + pl.part_off) : nullptr;
   a.ldp = (int)rq.Ntot;
   a.vec_store = ((uintptr_t)rq.y % 16 == 0) && (rq.ldy % 8 == 0);
   for (int b = 0; b < rq.nblk; ++b) {
@@ -469,11 +678,11 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
     d.ufast = (P.r % 8 == 0) && (((uintptr_t)P.U & 15) == 0);
     if (P.col % 8) a.vec_store = 0;
   }
-  hipError_t e = run(a, pl.BM, pl.BN, pl.S > 1 ? EPI_PARTIAL : EPI_RECON, st);
-  if (e != hipSuccess || pl.S == 1) return e;
+  hipError_t e = run(a, pl.BM, pl.BN, pl.BK, pl.NST, a.S > 1 ? MODE_PART : MODE_RECON, st);
+  if (e != hipSuccess || a.S == 1) return e;
   const long n = (long)rq.M * rq.Ntot;
   hipLaunchKernelGGL(k_prefill_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     (const float *)a.part, pl.S, (int)rq.M, (int)rq.Ntot, (int)rq.Ntot, a.y,
+                     (const float *)a.part, a.S, (int)rq.M, (int)rq.Ntot, (int)rq.Ntot, a.y,
                      (int)rq.ldy);
   return hipGetLastError();
 }

@@ -140,6 +140,49 @@ def test_decode_high_rank_split(M, r):
     assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"r={r} M={M}")
 
 
+# The tiled kernel: every compiled tile shape (BM x BN output, BK-wide K slices
+# through NST LDS stages), forced K splits of the main pass and of the rank-r
+# pass, on ragged M, N and K (K = 1048 leaves a partial last K slice; N = 200,
+# 40, 24 leave partial column tiles; r = 8, 16, 0).
+_PREFILL_MODES = [None, (256, 256, 32, 4, 1, None), (256, 256, 64, 2, 1, None), (256, 128, 64, 3, 1, 1),
+                  (128, 256, 64, 3, 1, 3), (128, 128, 64, 2, 1, None), (128, 128, 64, 4, 2, 5),
+                  (256, 256, 32, 4, 3, 2), (256, 256, 64, 2, 3, 2), (256, 128, 64, 3, 2, None),
+                  (256, 128, 32, 3, 1, None), (128, 256, 32, 3, 2, 1), (128, 128, 32, 4, 1, None)]
+
+
+@pytest.mark.parametrize("M", [65, 300, 513])
+@pytest.mark.parametrize("mode", _PREFILL_MODES, ids=str)
+def test_prefill_modes_qkv(M, mode, monkeypatch):
+    if mode is not None:
+        bm, bn, bk, nst, S, tS = mode
+        for k, v in (("BM", bm), ("BN", bn), ("BK", bk), ("NST", nst), ("S", S)):
+            monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
+        if tS is not None:
+            monkeypatch.setenv("AQ_TPASS_S", str(tS))
+    K = 1048
+    shapes = [(200, 8), (40, 16), (24, 0)]
+    bds = [I.bundle("test", 4, f, K, n, r, "bf16", variant="s0" if f == "k" else "normal")
+           for f, (n, r) in zip(("q", "k", "v"), shapes)]
+    x = I.activations("test", 600 + M, M, K, "bf16")
+    y = B.recon_qkv(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+    assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in bds]), "bf16", f"M={M} mode={mode}")
+
+
+@pytest.mark.parametrize("M", [80, 600])
+@pytest.mark.parametrize("r", [36, 64, 100, 256])
+@pytest.mark.parametrize("tile", [(256, 256, 32, 4), (256, 256, 64, 2), (256, 128, 64, 3), (128, 256, 32, 3)],
+                         ids=str)
+def test_prefill_high_rank(M, r, tile, monkeypatch):
+    """Rank-r epilogues over one or several rank chunks (some riding on the tail
+    of the K ring, the rest read from global memory), with U rows that are
+    16-byte aligned (r % 8 == 0) or not (r = 36, 100)."""
+    for k, v in zip(("BM", "BN", "BK", "NST"), tile):
+        monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
+    bd, x = _single(M, 512, 520, r, "bf16", variant="s0", layer=r, tag=700 + M)
+    y = B.recon_linear(up(x, "bf16"), bundle_up(bd, "bf16"))
+    assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"r={r} M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 16, 33, 130])
 def test_fused_gateup_small(M):
     K = 384
