@@ -141,6 +141,42 @@ def time_graph(torch, calls, steps, warmup):
     return e0.elapsed_time(e1) / steps, g
 
 
+def time_graph_streams(torch, calls, nstreams, steps, warmup):
+    """Like time_graph, but the calls (independent of each other) are issued
+    round-robin on `nstreams` streams forked from and joined back to the capture
+    stream, as a loader issues independent projections."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    side = [torch.cuda.Stream() for _ in range(nstreams)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream()
+        for st in side:
+            st.wait_stream(cap)
+        for i, c in enumerate(calls):
+            st = side[i % nstreams]
+            a = list(c.args)
+            a[-1] = st.cuda_stream
+            assert c.fn(*a) == 0, c.name
+        for st in side:
+            cap.wait_stream(st)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def time_eager(torch, calls, steps, warmup):
     for _ in range(warmup):
         for c in calls:
@@ -478,13 +514,25 @@ def run_materialize_fp4(args, torch, B, I):
             pbytes += packs[-1].nbytes
     ms_m, _ = time_graph(torch, mats, args.steps, args.warmup)
     ms_p, _ = time_graph(torch, packs, args.steps, args.warmup)
+    ms_m4 = time_graph_streams(torch, mats, 4, args.steps, args.warmup)
+    ms_p4 = time_graph_streams(torch, packs, 4, args.steps, args.warmup)
     mat_avg = time_per_launch(torch, mats, 2)
+    # the largest projections alone (gate, up, down: 6912 x 1152 elements)
+    big = [c for c in mats if c.name.split(".")[-1] in ("gate", "up", "down")]
+    big_avg = time_per_launch(torch, big, 2)
+    big_bytes = big[0].nbytes
+
+    def leg(ms, nb):
+        return {"ms": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return {"workload": "materialise + FP4 pack, 7 families x 26 layers (Gemma-3-1B shapes), 13 W0 bands, rank 64",
-            "materialize": {"ms": round(ms_m, 4), "GBps": round(mbytes / (ms_m * 1e-3) / 1e9, 1),
-                            "frac_hbm_peak": round(mbytes / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                            "avg_launch_us": round(mat_avg * 1e3, 2), "bytes": mbytes},
-            "fp4_pack": {"ms": round(ms_p, 4), "GBps": round(pbytes / (ms_p * 1e-3) / 1e9, 1),
-                         "frac_hbm_peak": round(pbytes / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": pbytes}}
+            "note": "serial: the 182 calls of each kind back to back in one graph; 4 streams: the same "
+                    "independent calls round-robin on 4 streams inside one graph",
+            "materialize": dict(leg(ms_m, mbytes), bytes=mbytes, avg_launch_us=round(mat_avg * 1e3, 2),
+                                streams4=leg(ms_m4, mbytes),
+                                largest_projection={"bytes": big_bytes, "avg_launch_us": round(big_avg * 1e3, 2),
+                                                    "GBps": round(big_bytes / (big_avg * 1e-3) / 1e9, 1)}),
+            "fp4_pack": dict(leg(ms_p, pbytes), bytes=pbytes, streams4=leg(ms_p4, pbytes))}
 
 
 def main():

@@ -35,15 +35,25 @@ __global__ __launch_bounds__(256) void k_fp4_amax(const uint16_t *w, int N, int 
   const int k8 = K >> 3;
   const long nchunks = (long)N * k8;
   unsigned m = 0;
-  for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += (long)gridDim.x * 256) {
-    const long n = c / k8;
-    const int kk = (int)(c - n * k8) * 8;
-    const uint4 v = ld16(w + n * ldw + kk);
-    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+  // Four 16-byte chunks per thread per step, all requested before any is used.
+  const long stride = (long)gridDim.x * 256;
+  for (long c0 = (long)blockIdx.x * 256 + threadIdx.x; c0 < nchunks; c0 += 4 * stride) {
+    uint4 v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m = max(m, q[i] & 0x7FFFu);
-      m = max(m, (q[i] >> 16) & 0x7FFFu);
+    for (int u = 0; u < 4; ++u) {
+      const long c = c0 + u * stride;
+      const long n = c / k8;
+      const int kk = (int)(c - n * k8) * 8;
+      v[u] = c < nchunks ? ld16(w + n * ldw + kk) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t q[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m = max(m, q[i] & 0x7FFFu);
+        m = max(m, (q[i] >> 16) & 0x7FFFu);
+      }
     }
   }
   __shared__ unsigned red[256];
@@ -109,6 +119,9 @@ __global__ __launch_bounds__(256) void k_fp4_pack(const uint16_t *w, int N, int 
     const float D = (float)((double)g * e4m3_value(sf));
     uint32_t lo = 0, hi = 0;
     if (D > 0.f) {
+      // Code = number of E2M1 midpoints m_i D below |w| (ties to the even code:
+      // strictly above m_0, m_2, m_4, m_6; at or above m_1, m_3, m_5), found by a
+      // three-step binary search over the monotone midpoints.
       const double d = (double)D;
       const double t0 = 0.25 * d, t1 = 0.75 * d, t2 = 1.25 * d, t3 = 1.75 * d, t4 = 2.5 * d,
                    t5 = 3.5 * d, t6 = 5.0 * d;
@@ -116,9 +129,10 @@ __global__ __launch_bounds__(256) void k_fp4_pack(const uint16_t *w, int N, int 
       for (int i = 0; i < 16; ++i) {
         const uint32_t bits = (q[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
         const double x = (double)bf2f((uint16_t)(bits & 0x7FFFu));
-        // Code = number of midpoints below |w|; at an exact midpoint between codes
-        // c and c+1 the even one wins (odd c steps up, even c stays).
-        uint32_t c = (x > t0) + (x >= t1) + (x > t2) + (x >= t3) + (x > t4) + (x >= t5) + (x > t6);
+        const bool b4 = x >= t3;
+        const bool b2 = x >= (b4 ? t5 : t1);
+        const double tl = b4 ? (b2 ? t6 : t4) : (b2 ? t2 : t0);
+        uint32_t c = (b4 ? 4u : 0u) + (b2 ? 2u : 0u) + (x > tl ? 1u : 0u);
         if (c != 0 && (bits & 0x8000u)) c |= 8u;
         if (i < 8)
           lo |= c << (4 * i);

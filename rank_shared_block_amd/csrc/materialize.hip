@@ -6,17 +6,17 @@
 // bf16 kernel (gfx950):
 // * Streaming W0 in and W_eff out is the bound (2 + 2 bytes per element); the
 //   rank-r product costs 2 r flop per element, which at r = 64 would exceed the
-//   fp32 VALU roofline, so it runs on v_mfma_f32_32x32x16_bf16 with U as the A
-//   operand (row n, 8 contiguous rank values per lane) and Vt as the B operand.
-// * A workgroup owns a block of 512 columns (a wave 32 * SETS of them, SETS = 4)
-//   and a range of rows.  MFMA column c of "set" e stands for actual column
-//   c0 + SETS * c + e, so after SETS MFMAs a lane holds SETS consecutive columns
-//   of each of its 16 rows and reads W0 / writes W_eff with 8-byte accesses.
-//   The Vt block (K-contiguous, but needed rank-contiguous as an MFMA operand)
-//   is staged once in LDS transposed, read back as one 16-byte fragment per
-//   rank chunk and reused for every row of the range.  The first row block's W0,
-//   s and U are requested before the staging so that the two round trips
-//   overlap.
+//   fp32 VALU roofline, so it runs on v_mfma_f32_32x32x16_bf16.
+// * A workgroup owns a block of 64 columns and a range of rows; each wave takes
+//   32-row blocks of the range in turn.  The Vt block [r, 64] is staged once in
+//   LDS transposed (64 columns x r ranks, rank-contiguous) and is the A operand
+//   (8 consecutive ranks of one column per lane); U rows are the B operand
+//   (8 consecutive ranks of one row per lane, one 16-byte load).  The result
+//   comes out transposed: a lane holds one output row and, per group of four
+//   accumulator values, 4 consecutive output columns, so W0 is read and W_eff
+//   written with 8-byte accesses.
+// * Many small workgroups (four per CU) keep enough loads in flight to hide the
+//   memory latency without software pipelining.
 // * diag(s) W0 is added in fp32 with one fused multiply-add per element; with
 //   r = 0 (or U = Vt = 0) the accumulator is +0 and the result is one rounding of
 //   the exact product s * w, i.e. bit-exact.
@@ -35,69 +35,64 @@ struct MatArgs {
   int N, K, r, ldw, rows_per_wg, ufast;
 };
 
-template <int SETS, int JC>
-__global__ __launch_bounds__(256, 2) void k_materialize_bf16(const MatArgs a) {
-  constexpr int CW = 32 * SETS;             // columns per wave
-  constexpr int CB = 4 * CW;                // columns per workgroup
-  constexpr int RP = 16 * JC + 8;           // LDS row (one column of Vt), padded
-  // Vt[:, c0 : c0 + CB] stored transposed: vts[c][j], so that the 8 ranks of one
-  // MFMA operand are one 16-byte LDS read.
+// RJ: 16-rank steps (r <= 16 RJ).
+template <int RJ>
+__global__ __launch_bounds__(256, 4) void k_materialize_bf16(const MatArgs a) {
+  constexpr int CB = 64;                    // columns per workgroup
+  constexpr int RP = 16 * RJ + 8;           // LDS row (one column of Vt, rank-contiguous), padded
   __shared__ __attribute__((aligned(16))) uint16_t vts[CB * RP];
   const uint16_t *W0 = (const uint16_t *)a.W0, *S = (const uint16_t *)a.s;
   const uint16_t *U = (const uint16_t *)a.U, *Vt = (const uint16_t *)a.Vt;
   uint16_t *out = (uint16_t *)a.out;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c32 = lane & 31, hi = lane >> 5;
+  const int l32 = lane & 31, hi = lane >> 5;
   const int K = a.K, r = a.r, N = a.N;
   const int cb0 = blockIdx.x * CB;
-  const int c0 = cb0 + wave * CW;
-  const int kl = c0 + SETS * c32;            // this lane's SETS consecutive columns
-  const bool colok = kl < K;                 // K % SETS == 0, so all SETS or none
-  const int kloc = wave * CW + SETS * c32;   // ... their position in the LDS tile
+  const int nb = blockIdx.y * a.rows_per_wg, ne = min(N, nb + a.rows_per_wg);
 
-  // Operands of one 32-row block: W0 and s of this lane's 16 output rows, U of
-  // its A-operand row.  The first block's are requested before the Vt staging
-  // so that the two memory round trips overlap.
-  uint2 w[16];
-  float sv[16];
-  bf16x8 au[JC];
-  auto fetch_rows = [&](int n0, int ne) {
+  // Operands of one 32-row block: W0 of this lane's row (column tile t, group
+  // g -> columns cb0 + 32 t + 8 g + 4 hi .. + 3, all in range or none since
+  // K % 8 == 0), its s, and its U row as B operands.
+  uint2 w[2][4];
+  float sv;
+  bf16x8 bu[RJ];
+  auto fetch = [&](int n0) {
+    const int n = n0 + l32;
+    const bool rowok = n < ne;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int n = n0 + 8 * (v >> 2) + 4 * hi + (v & 3);
-      const bool ok = colok && n < ne;
-      w[v] = ok ? *reinterpret_cast<const uint2 *>(W0 + (size_t)n * K + kl) : make_uint2(0, 0);
-      sv[v] = ok ? bf2f(S[n]) : 0.f;
-    }
-    const int na = n0 + c32;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int jc = 0; jc < JC; ++jc) {
-      const int j = jc * 16 + 8 * hi;
-      if (na >= N || j >= r) {
-        au[jc] = zero_bf16x8();
+      for (int g = 0; g < 4; ++g) {
+        const int k = cb0 + 32 * t + 8 * g + 4 * hi;
+        w[t][g] = rowok && k < K ? *reinterpret_cast<const uint2 *>(W0 + (size_t)n * K + k) : make_uint2(0, 0);
+      }
+    sv = rowok ? bf2f(S[n]) : 0.f;
+#pragma unroll
+    for (int kk = 0; kk < RJ; ++kk) {
+      const int j = 16 * kk + 8 * hi;
+      if (!rowok || j >= r) {
+        bu[kk] = zero_bf16x8();
       } else if (a.ufast) {
-        au[jc] = as_bf16x8(ld16(U + (size_t)na * r + j));
+        bu[kk] = as_bf16x8(ld16(U + (size_t)n * r + j));
       } else {
         uint16_t v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = (j + q < r) ? U[(size_t)na * r + j + q] : (uint16_t)0;
+        for (int q = 0; q < 8; ++q) v[q] = (j + q < r) ? U[(size_t)n * r + j + q] : (uint16_t)0;
         uint4 u;
         u.x = v[0] | ((uint32_t)v[1] << 16);
         u.y = v[2] | ((uint32_t)v[3] << 16);
         u.z = v[4] | ((uint32_t)v[5] << 16);
         u.w = v[6] | ((uint32_t)v[7] << 16);
-        au[jc] = as_bf16x8(u);
+        bu[kk] = as_bf16x8(u);
       }
     }
   };
-  const int nb0 = blockIdx.y * a.rows_per_wg;
-  if (nb0 < N) fetch_rows(nb0, min(N, nb0 + a.rows_per_wg));
+  const int nfirst = nb + 32 * wave;
 
-  // Stage Vt transposed (zeros past r or K).  Consecutive threads take
-  // consecutive ranks of one 8-column chunk, so their 2-byte LDS writes fall in
-  // consecutive banks.
-  for (int i = tid; i < 16 * JC * (CB / 8); i += 256) {
-    const int j = i % (16 * JC), c = (i / (16 * JC)) * 8;
+  // Stage Vt[:, cb0 : cb0 + 64] transposed (zeros past r or K): thread i reads
+  // 8 columns of one rank row and writes them to 8 LDS rows.
+  for (int i = tid; i < 16 * RJ * (CB / 8); i += 256) {
+    const int j = i % (16 * RJ), c = (i / (16 * RJ)) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (j < r && cb0 + c < K) v = ld16(Vt + (size_t)j * K + cb0 + c);
     const uint32_t q4[4] = {v.x, v.y, v.z, v.w};
@@ -106,49 +101,50 @@ __global__ __launch_bounds__(256, 2) void k_materialize_bf16(const MatArgs a) {
   }
   __syncthreads();
 
-  // B operands (Vt): set e, rank chunk jc -> ranks jc*16 + 8*hi .. +7 of column kl + e.
-  bf16x8 bv[SETS][JC];
+  // A operands: column tile t (columns 32 t + lane % 32), rank step kk.
+  bf16x8 av[2][RJ];
 #pragma unroll
-  for (int e = 0; e < SETS; ++e)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int jc = 0; jc < JC; ++jc)
-      bv[e][jc] = as_bf16x8(*reinterpret_cast<const uint4 *>(&vts[(kloc + e) * RP + jc * 16 + 8 * hi]));
+    for (int kk = 0; kk < RJ; ++kk)
+      av[t][kk] = as_bf16x8(*reinterpret_cast<const uint4 *>(&vts[(32 * t + l32) * RP + 16 * kk + 8 * hi]));
 
-  // Every lane stays active through the MFMAs (they read all 64 lanes'
-  // operands); lanes past K only skip their loads and stores of W0 / W_eff.
-  for (int nb = nb0; nb < N; nb += gridDim.y * a.rows_per_wg) {
-    const int ne = min(N, nb + a.rows_per_wg);
-    for (int n0 = nb; n0 < ne; n0 += 32) {
-      if (n0 != nb0) fetch_rows(n0, ne);
-      f32x16 acc[SETS];
+  for (int n0 = nfirst; n0 < ne; n0 += 128) {
+    const int n = n0 + l32;                   // this lane's output row
+    const bool rowok = n < ne;
+    fetch(n0);
+    // acc[t]: column 32 t + 8 (v / 4) + 4 hi + (v % 4) of row n.  Every lane
+    // takes part in the MFMAs (they read all lanes' operands).
+    f32x16 acc[2];
 #pragma unroll
-      for (int e = 0; e < SETS; ++e)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[e][v] = 0.f;
+      for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+    if (r > 0) {
 #pragma unroll
-      for (int jc = 0; jc < JC; ++jc) {
-        if (jc * 16 >= r) break;
+      for (int kk = 0; kk < RJ; ++kk)
 #pragma unroll
-        for (int e = 0; e < SETS; ++e)
-          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(au[jc], bv[e][jc], acc[e], 0, 0, 0);
-      }
-      if (!colok) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int n = n0 + 8 * (v >> 2) + 4 * hi + (v & 3);
-        if (n >= ne) continue;
-        uint2 o;
-        o.x = f2bf(fmaf(sv[v], bf2f((uint16_t)w[v].x), acc[0][v])) |
-              ((uint32_t)f2bf(fmaf(sv[v], bf2f((uint16_t)(w[v].x >> 16)), acc[1][v])) << 16);
-        o.y = f2bf(fmaf(sv[v], bf2f((uint16_t)w[v].y), acc[2][v])) |
-              ((uint32_t)f2bf(fmaf(sv[v], bf2f((uint16_t)(w[v].y >> 16)), acc[3][v])) << 16);
-        *reinterpret_cast<uint2 *>(out + (size_t)n * a.ldw + kl) = o;
-      }
+        for (int t = 0; t < 2; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], bu[kk], acc[t], 0, 0, 0);
     }
+    if (!rowok) continue;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int k = cb0 + 32 * t + 8 * g + 4 * hi;
+        if (k >= K) continue;
+        uint2 o;
+        o.x = f2bf(fmaf(sv, bf2f((uint16_t)w[t][g].x), acc[t][4 * g + 0])) |
+              ((uint32_t)f2bf(fmaf(sv, bf2f((uint16_t)(w[t][g].x >> 16)), acc[t][4 * g + 1])) << 16);
+        o.y = f2bf(fmaf(sv, bf2f((uint16_t)w[t][g].y), acc[t][4 * g + 2])) |
+              ((uint32_t)f2bf(fmaf(sv, bf2f((uint16_t)(w[t][g].y >> 16)), acc[t][4 * g + 3])) << 16);
+        *reinterpret_cast<uint2 *>(out + (size_t)n * a.ldw + k) = o;
+      }
   }
 }
 
-// Ranks above 16 * JC_MAX: same arithmetic, Vt operand gathered per row block.
+// Ranks above 64: same arithmetic, Vt operand gathered per row block.
 __global__ __launch_bounds__(256) void k_materialize_bf16_highrank(const MatArgs a) {
   const uint16_t *W0 = (const uint16_t *)a.W0, *S = (const uint16_t *)a.s;
   const uint16_t *U = (const uint16_t *)a.U, *Vt = (const uint16_t *)a.Vt;
@@ -224,27 +220,32 @@ hipError_t launch_materialize(aq_dtype dt, int64_t K, const Proj &p, void *w, in
     hipLaunchKernelGGL(k_materialize_f32, grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  // Column blocks of 512 (4 waves x 128); row blocks sized so that the grid has
-  // about two workgroups per CU, each amortising its staged Vt tile over as many
-  // rows as possible.
-  constexpr int SETS = 4;
-  const int colblocks = (int)((K + 4 * 32 * SETS - 1) / (4 * 32 * SETS));
-  long rows = (p.N * colblocks + 2 * kNumCU - 1) / (2 * kNumCU);
-  rows = (rows + 31) / 32 * 32;
-  if (rows < 32) rows = 32;
-  a.rows_per_wg = (int)rows;
-  const long nrb = (p.N + rows - 1) / rows;
-  const unsigned gy = (unsigned)(nrb < 65535 ? nrb : 65535);
   if (p.r <= 64) {
-    dim3 grid((unsigned)colblocks, gy);
+    // 64-column blocks; row ranges sized for about four workgroups per CU,
+    // at least one 32-row block per wave.
+    const int colblocks = (int)((K + 63) / 64);
+    long rows = (p.N * colblocks + 4 * kNumCU - 1) / (4 * kNumCU);
+    rows = (rows + 127) / 128 * 128;
+    if (rows < 128) rows = 128;
+    a.rows_per_wg = (int)rows;
+    const long nrb = (p.N + rows - 1) / rows;
+    dim3 grid((unsigned)colblocks, (unsigned)nrb);
     if (p.r <= 16)
-      hipLaunchKernelGGL((k_materialize_bf16<SETS, 1>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_materialize_bf16<1>), grid, dim3(256), 0, st, a);
     else if (p.r <= 32)
-      hipLaunchKernelGGL((k_materialize_bf16<SETS, 2>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_materialize_bf16<2>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((k_materialize_bf16<SETS, 4>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_materialize_bf16<4>), grid, dim3(256), 0, st, a);
   } else {
-    dim3 grid((unsigned)((K + 127) / 128), gy);
+    // Row blocks sized for about two workgroups per CU.
+    const int colblocks = (int)((K + 127) / 128);
+    long rows = (p.N * colblocks + 2 * kNumCU - 1) / (2 * kNumCU);
+    rows = (rows + 31) / 32 * 32;
+    if (rows < 32) rows = 32;
+    a.rows_per_wg = (int)rows;
+    const long nrb = (p.N + rows - 1) / rows;
+    const unsigned gy = (unsigned)(nrb < 65535 ? nrb : 65535);
+    dim3 grid((unsigned)colblocks, gy);
     hipLaunchKernelGGL(k_materialize_bf16_highrank, grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
