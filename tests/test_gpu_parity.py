@@ -168,6 +168,17 @@ def test_prefill_modes_qkv(M, mode, monkeypatch):
     assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in bds]), "bf16", f"M={M} mode={mode}")
 
 
+@pytest.mark.parametrize("M", [65, 1000])
+@pytest.mark.parametrize("K", [40, 1048, 6912])
+def test_rank_pass_shapes(M, K):
+    """The rank-r pass over short and long K, ranks of 1, 2 and 4 chunks of 64."""
+    shapes = [(64, 130), (48, 64), (40, 250)]
+    bds = [I.bundle("test", 9, f, K, n, r, "bf16", variant="s0") for f, (n, r) in zip(("q", "k", "v"), shapes)]
+    x = I.activations("test", 800 + M + K, M, K, "bf16")
+    y = B.recon_qkv(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+    assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in bds]), "bf16", f"M={M} K={K}")
+
+
 @pytest.mark.parametrize("M", [80, 600])
 @pytest.mark.parametrize("r", [36, 64, 100, 256])
 @pytest.mark.parametrize("tile", [(256, 256, 32, 4), (256, 256, 64, 2), (256, 128, 64, 3), (128, 256, 32, 3)],
