@@ -39,6 +39,7 @@
 //   and invalidate the whole L2 each time, which costs far more than the launch.
 // Both are deterministic.
 
+#include <limits.h>
 #include <stdlib.h>
 
 #include "aq_internal.h"
@@ -49,19 +50,27 @@ namespace aq {
 // One segment of stacked rows.  Fused mode: a block (W0 rows plus vg groups of
 // its Vt per tile, s and U for the epilogue).  Split mode: either the W0 rows or
 // the Vt rows of a block (vg = 0), written as partials at column `col`.
-struct DecSeg {
+struct alignas(64) DecSeg {
   const uint16_t *W0, *s, *U, *Vt;
-  int N, r, col, tile0, vg, ufast;
+  int N, r, col, vg, ufast, pad[3];
 };
+static_assert(sizeof(DecSeg) == 64, "one scalar load per segment");
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
+// The first 88 bytes hold everything a workgroup needs before it can pick its
+// segment (two scalar cache lines, loaded in one batch); the segment table
+// follows and is read once, with one dynamic offset.
 struct DecArgs {
+  int ntiles, S, K, kchunk;
+  int M, ldx, ldy, Wp;
+  int tile0[kMaxSegs];  // first tile of each segment; unused entries INT_MAX
+  int pad0, pad1;
   const uint16_t *x;
   uint16_t *y;
   float *part;          // split mode: [S][M][Wp] fp32 partials
-  int ldx, ldy, M, K, Wp;
-  int nseg, ntiles, S, kchunk;
   DecSeg g[kMaxSegs];
 };
+static_assert(sizeof(int) * (8 + kMaxSegs + 2) == 64, "header layout");
 
 // MT: 16-token groups; NG: 16-row groups per workgroup; WAVES: waves per
 // workgroup; PART: split mode (partials out) instead of the fused epilogue.
@@ -75,26 +84,49 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(
   constexpr int SLOT = NG * MT * 256;             // floats per wave's partial sums
   constexpr int TSUM = PART ? 1 : 16 * MT * 16 * (NG - 1);
   __shared__ float red[WAVES * SLOT];
-  __shared__ float tsum[TSUM];                    // fused: reduced t, [token][rank]
+  __shared__ __attribute__((aligned(16))) float tsum[TSUM];   // fused: reduced t, [token][rank]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const int j16 = lane & 15, g = lane >> 4;
 
-  const int unit = xcd_contiguous_tile(blockIdx.x, a.ntiles * a.S);
+  // Kernel arguments live in memory: request the header in one batch, then the
+  // segment, so that a workgroup waits for two scalar round trips, not one per
+  // field (the compiler would otherwise load each field at its first use).
+  const int ntiles = a.ntiles, nsplit = a.S, K = a.K, kchunk = a.kchunk;
+  int t0s[kMaxSegs];
+#pragma unroll
+  for (int i = 0; i < kMaxSegs; ++i) t0s[i] = a.tile0[i];
+  const uint16_t *const xptr = a.x;
+  const int Mtok = a.M, ldx = a.ldx;
+  asm volatile("" ::"s"(ntiles), "s"(nsplit), "s"(K), "s"(kchunk), "s"(Mtok), "s"(ldx), "s"(t0s[1]),
+               "s"(t0s[2]), "s"(t0s[3]), "s"(t0s[4]), "s"(t0s[5]), "s"(xptr));
+
+  const int unit = xcd_contiguous_tile(blockIdx.x, ntiles * nsplit);
   if (unit < 0) return;
-  const int tile = unit / a.S, p = unit - tile * a.S;
+  const int tile = unit / nsplit, p = unit - tile * nsplit;
 
   int bi = 0;
 #pragma unroll
-  for (int i = 1; i < kMaxSegs; ++i)
-    if (i < a.nseg && tile >= a.g[i].tile0) bi = i;
-  const DecSeg B = a.g[bi];
+  for (int i = 1; i < kMaxSegs; ++i) bi += tile >= t0s[i] ? 1 : 0;
+  // The whole 64-byte segment entry as one scalar load.
+  const i32x16 sraw = *reinterpret_cast<const i32x16 *>(&a.g[bi]);
+  auto ptr_at = [&](int i) {   // global-memory pointers: loads through them stay global loads
+    const uint64_t v = ((uint64_t)(uint32_t)sraw[2 * i + 1] << 32) | (uint32_t)sraw[2 * i];
+    return (const uint16_t *)(const __attribute__((address_space(1))) uint16_t *)v;
+  };
+  struct {
+    const uint16_t *W0, *s, *U, *Vt;
+    int N, r, col, vg, ufast;
+  } const B = {ptr_at(0), ptr_at(1), ptr_at(2), ptr_at(3), sraw[8], sraw[9], sraw[10], sraw[11], sraw[12]};
+  int tile0 = t0s[0];
+#pragma unroll
+  for (int i = 1; i < kMaxSegs; ++i) tile0 = bi == i ? t0s[i] : tile0;
 
   const int vg = PART ? 0 : B.vg, wg = NG - vg;
-  const int row0 = (tile - B.tile0) * 16 * wg;
-  const int K = a.K;
-  const int kbeg = p * a.kchunk;
-  const int kend = min(K, kbeg + a.kchunk);
+  const int row0 = (tile - tile0) * 16 * wg;
+  const int kbeg = p * kchunk;
+  const int kend = min(K, kbeg + kchunk);
   const int nsteps = (kend - kbeg + KSTEP - 1) / KSTEP;
 
   // One buffer resource per operand: rows past the valid range fall outside it,
@@ -102,7 +134,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(
   const int Rv = min(16 * wg, B.N - row0);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(B.W0 + (size_t)row0 * K, (uint32_t)Rv * K * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(B.Vt, PART ? 0u : (uint32_t)B.r * K * 2);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((a.M - 1) * a.ldx + K) * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xptr, (uint32_t)((Mtok - 1) * ldx + K) * 2);
   int roff[NG];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi)
@@ -116,16 +148,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(
 
   // Fused epilogue mapping: thread tid owns output row nl = tid % Rv and tokens
   // m = tid / Rv, tid / Rv + tpr, ...  Its s value and (for r <= 16) its U row are
-  // requested now, so that their latency hides under the main loop.
+  // requested now, by every thread (row n_e < N always) and with no branch, so
+  // that nothing waits for them before the main loop: their latency hides under
+  // it.  s stays raw bf16 until the epilogue.
   const int r = PART ? 0 : B.r;
   const int tpr = NT / Rv;                       // threads per output row (>= 1)
   const int nl_e = tid % Rv, m_e0 = tid / Rv;
   const bool epi = !PART && m_e0 < tpr && m_e0 < a.M;
   const int n_e = row0 + nl_e;
-  const float s_e = epi ? bf2f(B.s[n_e]) : 0.f;
+  uint16_t s_raw = 0;
+  if constexpr (!PART) s_raw = B.s[n_e];
   uint4 u_pre0 = make_uint4(0, 0, 0, 0), u_pre1 = make_uint4(0, 0, 0, 0);
   const bool upre = B.ufast && r <= 16;
-  if (epi && upre && r > 0) {
+  if (upre && r > 0) {
     u_pre0 = ld16(B.U + (size_t)n_e * r);
     if (r > 8) u_pre1 = ld16(B.U + (size_t)n_e * r + 8);
   }
@@ -164,21 +199,32 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(
 
   // Software pipeline with two register sets used in turn (no register copies,
   // so no wait on loads still in flight).  The scheduling barriers keep the
-  // compiler from sinking the next step's loads down to their uses.  Past the
-  // last step the offsets are out of range: the extra loads return zeros
-  // without touching memory.
+  // compiler from sinking the next step's loads down to their uses.  A wave
+  // fetches exactly its own steps: a load past the last one would return zeros
+  // without touching memory, but it still queues behind every load the CU has
+  // in flight, and the epilogue would wait for it.  The branches are uniform.
+  const int nmine = wave < nsteps ? (nsteps - 1 - wave) / WAVES + 1 : 0;
   bf16x8 xa[MT][KS], wa[NG][KS], xb[MT][KS], wb[NG][KS];
-  fetch(wave, xa, wa);
-  for (int st = wave; st < nsteps; st += 2 * WAVES) {
-    fetch(st + WAVES, xb, wb);
+  if (nmine > 0) fetch(wave, xa, wa);
+  int i = 0;
+  for (; i + 2 < nmine; i += 2) {
+    fetch(wave + (i + 1) * WAVES, xb, wb);
     __builtin_amdgcn_sched_barrier(0);
     compute(xa, wa);
     __builtin_amdgcn_sched_barrier(0);
-    if (st + WAVES >= nsteps) break;
-    fetch(st + 2 * WAVES, xa, wa);
+    fetch(wave + (i + 2) * WAVES, xa, wa);
     __builtin_amdgcn_sched_barrier(0);
     compute(xb, wb);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if (i + 1 < nmine) {
+    fetch(wave + (i + 1) * WAVES, xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(xb, wb);
+  } else if (i < nmine) {
+    compute(xa, wa);
   }
 
   // Every wave stores its partial sums in its own LDS slot; after one barrier
@@ -222,16 +268,26 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(
 
   // Fused epilogue: y = s * z + U t.
   if (epi) {
+    const float s_e = bf2f(s_raw);
     const uint16_t *u = B.U + (size_t)n_e * r;
     for (int m = m_e0; m < a.M; m += tpr) {
       const float z = red_at(vg + (nl_e >> 4), m, nl_e & 15);
       const float *tm = tsum + m * 16 * (NG - 1);
       float lr = 0.f;
       if (upre) {
+        // All 16 t values in four 16-byte LDS reads, requested together; terms
+        // past r are dropped by a select (their LDS words were never written).
+        // Per-term conditional reads would serialise 16 LDS round trips.
         const uint32_t w8[8] = {u_pre0.x, u_pre0.y, u_pre0.z, u_pre0.w, u_pre1.x, u_pre1.y, u_pre1.z, u_pre1.w};
+        const float4 *t4 = reinterpret_cast<const float4 *>(tm);
+        const float4 q0 = t4[0], q1 = t4[1], q2 = t4[2], q3 = t4[3];
+        const float tv[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                              q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (j < r) lr += bf2f((uint16_t)(w8[j >> 1] >> ((j & 1) * 16))) * tm[j];
+        for (int j = 0; j < 16; ++j) {
+          const float term = bf2f((uint16_t)(w8[j >> 1] >> ((j & 1) * 16))) * tv[j];
+          lr += j < r ? term : 0.f;
+        }
       } else if (B.ufast) {
         for (int j0 = 0; j0 < r; j0 += 8) {
           const uint4 uv = ld16(u + j0);
@@ -264,7 +320,7 @@ struct CombArgs {
 };
 
 __global__ __launch_bounds__(256) void k_decode_combine(const CombArgs a) {
-  __shared__ float T[AQ_MAX_RANK];
+  __shared__ __attribute__((aligned(16))) float T[AQ_MAX_RANK];
   const int chunk = blockIdx.x, m = blockIdx.y, tid = threadIdx.x;
   int bi = 0;
   if (a.nblk > 1 && chunk >= a.b[1].chunk0) bi = 1;
@@ -274,25 +330,44 @@ __global__ __launch_bounds__(256) void k_decode_combine(const CombArgs a) {
   const size_t pstride = (size_t)a.M * a.Wp;
   const float *row = a.part + (size_t)m * a.Wp;
 
+  // This thread's s and (for r <= 16) U row are requested together with the
+  // partials, before the barrier, so that the kernel waits for memory once.
+  const int n = (chunk - B.chunk0) * 256 + tid;
+  const bool live = n < B.N;
+  const int nc = live ? n : B.N - 1;
+  const uint16_t s_raw = B.s[nc];
+  const uint16_t *u = B.U + (size_t)nc * r;
+  const bool upre = B.ufast && r <= 16;
+  uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
+  if (upre && r > 0) {
+    u0 = ld16(u);
+    if (r > 8) u1 = ld16(u + 8);
+  }
+  float z = 0.f;
+  if (live)
+    for (int q = 0; q < a.S; ++q) z += row[q * pstride + B.col + n];
   for (int j = tid; j < r; j += 256) {
     float v = 0.f;
     for (int q = 0; q < a.S; ++q) v += row[q * pstride + B.tcol + j];
     T[j] = v;
   }
-
-  const int n = (chunk - B.chunk0) * 256 + tid;
-  const bool live = n < B.N;
-  float z = 0.f, sn = 0.f;
-  if (live) {
-    sn = bf2f(B.s[n]);
-    for (int q = 0; q < a.S; ++q) z += row[q * pstride + B.col + n];
-  }
   __syncthreads();
   if (!live) return;
 
-  const uint16_t *u = B.U + (size_t)n * r;
+  const float sn = bf2f(s_raw);
   float lr = 0.f;
-  if (B.ufast) {
+  if (upre) {
+    const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    const float4 *t4 = reinterpret_cast<const float4 *>(T);
+    const float4 q0 = t4[0], q1 = t4[1], q2 = t4[2], q3 = t4[3];
+    const float tv[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                          q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float term = bf2f((uint16_t)(w8[j >> 1] >> ((j & 1) * 16))) * tv[j];
+      lr += j < r ? term : 0.f;
+    }
+  } else if (B.ufast) {
     for (int j0 = 0; j0 < r; j0 += 8) {
       const uint4 uv = ld16(u + j0);
       const uint32_t w4[4] = {uv.x, uv.y, uv.z, uv.w};
@@ -499,15 +574,14 @@ hipError_t launch_decode(const Recon &rq, const DecodePlan &pl, void *ws, hipStr
   a.M = (int)rq.M;
   a.K = (int)rq.K;
   a.Wp = pl.Wp;
-  a.nseg = pl.nseg;
   a.ntiles = pl.ntiles;
   a.S = pl.S;
   a.kchunk = pl.kchunk;
+  for (int i = 0; i < kMaxSegs; ++i) a.tile0[i] = i < pl.nseg ? pl.seg[i].tile0 : INT_MAX;
   for (int i = 0; i < pl.nseg; ++i) {
     const DecodeSeg &sg = pl.seg[i];
     const Proj &P = rq.blk[sg.b];
     DecSeg &d = a.g[i];
-    d.tile0 = sg.tile0;
     if (!pl.split) {
       d.W0 = (const uint16_t *)P.W0;
       d.s = (const uint16_t *)P.s;
