@@ -46,6 +46,7 @@ struct DecodeSeg {
   int b;           // block
   int isVt;        // split mode: 1 for the block's Vt rows
   int tile0, ntile;
+  int rows;        // rows per tile (W0 rows in fused mode; at most 16 x the tile's W0 groups)
 };
 
 struct DecodePlan {

@@ -52,7 +52,7 @@ namespace aq {
 // the Vt rows of a block (vg = 0), written as partials at column `col`.
 struct alignas(64) DecSeg {
   const uint16_t *W0, *s, *U, *Vt;
-  int N, r, col, vg, ufast, pad[3];
+  int N, r, col, vg, ufast, rows, pad[2];
 };
 static_assert(sizeof(DecSeg) == 64, "one scalar load per segment");
 typedef int i32x16 __attribute__((ext_vector_type(16)));
@@ -77,7 +77,8 @@ static_assert(sizeof(int) * (8 + kMaxSegs + 2) == 64, "header layout");
 // A step covers KS = 4 / MT chunks of 32 K-values, so that the fragments of two
 // steps fit the register budget of two waves per SIMD.
 template <int MT, int NG, int WAVES, bool PART>
-__global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(const DecArgs a) {
+__global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || (MT == 1 && NG >= 5)) ? 1 : 2) void k_decode_bf16(
+    const DecArgs a) {
   constexpr int KS = 4 / MT;
   constexpr int KSTEP = 32 * KS;
   constexpr int NT = 64 * WAVES;
@@ -117,21 +118,23 @@ __global__ __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) void k_decode_bf16(
   };
   struct {
     const uint16_t *W0, *s, *U, *Vt;
-    int N, r, col, vg, ufast;
-  } const B = {ptr_at(0), ptr_at(1), ptr_at(2), ptr_at(3), sraw[8], sraw[9], sraw[10], sraw[11], sraw[12]};
+    int N, r, col, vg, ufast, rows;
+  } const B = {ptr_at(0), ptr_at(1), ptr_at(2), ptr_at(3), sraw[8], sraw[9], sraw[10], sraw[11], sraw[12], sraw[13]};
   int tile0 = t0s[0];
 #pragma unroll
   for (int i = 1; i < kMaxSegs; ++i) tile0 = bi == i ? t0s[i] : tile0;
 
-  const int vg = PART ? 0 : B.vg, wg = NG - vg;
-  const int row0 = (tile - tile0) * 16 * wg;
+  // A tile holds B.rows rows (any count up to 16 x its W0 groups): row groups
+  // past them lie outside the W0 resource and cost no memory traffic.
+  const int vg = PART ? 0 : B.vg;
+  const int row0 = (tile - tile0) * B.rows;
   const int kbeg = p * kchunk;
   const int kend = min(K, kbeg + kchunk);
   const int nsteps = (kend - kbeg + KSTEP - 1) / KSTEP;
 
   // One buffer resource per operand: rows past the valid range fall outside it,
   // and so do K chunks past this range (offset kOOB).
-  const int Rv = min(16 * wg, B.N - row0);
+  const int Rv = min(B.rows, B.N - row0);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(B.W0 + (size_t)row0 * K, (uint32_t)Rv * K * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(B.Vt, PART ? 0u : (uint32_t)B.r * K * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(xptr, (uint32_t)((Mtok - 1) * ldx + K) * 2);
@@ -404,12 +407,11 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
   }
   const int ngmax = max_ng(pl->MT);
 
-  auto fused_tiles = [&](int ng) {
+  // Fused tiles of R W0 rows (the same R for every block); a block's last tile
+  // may be shorter.
+  auto fused_tiles_r = [&](int R) {
     int t = 0;
-    for (int b = 0; b < rq.nblk; ++b) {
-      const int rows = 16 * (ng - pl->vg[b]);
-      t += (int)((rq.blk[b].N + rows - 1) / rows);
-    }
+    for (int b = 0; b < rq.nblk; ++b) t += (int)((rq.blk[b].N + R - 1) / R);
     return t;
   };
   auto split_tiles = [&](int ng) {
@@ -419,30 +421,42 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
     return t;
   };
 
-  // Fused or split, from sweeps over the Gemma-3-1B and large-decoder decode
-  // shapes on MI355X.  Fused (the largest row tile that still gives >= 384
-  // workgroups) is kept while it fills the chip without a K split and its
-  // re-reads of Vt (every workgroup streams all of it) stay below ~24 MB, the
-  // traffic that the combine launch of split mode is worth.
-  constexpr int kUnitsFused = 384;
-  constexpr double kVtRereadLimit = 24e6;
+  // Fused tile height.  The time of a fused dispatch follows its most loaded
+  // CU: ceil(tiles / 256) workgroups, each streaming R rows of W0 from HBM plus
+  // the block's Vt rows (served by L2, counted at 0.7 of a W0 row, a fit to
+  // sweeps on MI355X).  R is any row count from 16 up to what the largest
+  // compiled tile holds, so that e.g. 2 x 6912 rows become 256 tiles of 54,
+  // one per CU, rather than 432 tiles of 32 (two on most CUs).
+  const int ngmax_f = pl->MT == 1 ? 5 : ngmax;
   const int ngmin = vgmax + 1 > 2 ? vgmax + 1 : 2;
+  int Rf = 0;
+  double best_f = 1e30;
+  for (int R = 16; R <= 16 * (ngmax_f - vgmax); ++R) {
+    const int t = fused_tiles_r(R);
+    const double cost = (double)((t + kNumCU - 1) / kNumCU) * (R + 0.7 * 16 * vgmax);
+    if (cost < best_f - 1e-9) { best_f = cost; Rf = R; }
+  }
+  const int r_o = env_int("AQ_DECODE_ROWS", 0);
+  if (r_o >= 1 && r_o <= 16 * (ngmax_f - vgmax)) Rf = r_o;
+
+  // Fused or split, from sweeps over the Gemma-3-1B and large-decoder decode
+  // shapes on MI355X.  Fused is kept while its tiles fill the chip (or K is
+  // short) and its re-reads of Vt (every workgroup streams all of it) stay
+  // below ~24 MB, the traffic that the combine launch of split mode is worth.
+  constexpr int kUnitsFused = 230;
+  constexpr double kVtRereadLimit = 24e6;
   bool split = true;
   int NG = ngmax;
-  if (ngmin <= ngmax) {
-    while (NG - 1 >= ngmin && fused_tiles(NG) < kUnitsFused) NG -= 1;
-    double vt_bytes = 0;
-    for (int b = 0; b < rq.nblk; ++b) {
-      const int rows = 16 * (NG - pl->vg[b]);
-      vt_bytes += (double)((rq.blk[b].N + rows - 1) / rows) * 16.0 * pl->vg[b] * K * 2.0;
-    }
-    const bool fills = fused_tiles(NG) >= kUnitsFused || K < 2 * 2304;
+  if (Rf > 0) {
+    const double vt_bytes = (double)fused_tiles_r(Rf) * 16.0 * vgmax * K * 2.0;
+    const bool fills = fused_tiles_r(Rf) >= kUnitsFused || K < 2 * 2304;
     split = !(fills && vt_bytes <= kVtRereadLimit);
   }
   // Tuning overrides (profiling sweeps): AQ_DECODE_SPLIT (0/1), AQ_DECODE_NG,
   // AQ_DECODE_S, AQ_DECODE_WAVES.
   const int sp_o = env_int("AQ_DECODE_SPLIT", -1);
-  if (sp_o == 1 || (sp_o == 0 && ngmin <= ngmax)) split = sp_o == 1;
+  if (sp_o == 1 || (sp_o == 0 && Rf > 0)) split = sp_o == 1;
+  if (!split) NG = ngmin > vgmax + (Rf + 15) / 16 ? ngmin : vgmax + (Rf + 15) / 16;
   int S = 1;
   if (split) {
     // Split mode: every work unit (a tile over one K range) moves the same
@@ -475,7 +489,10 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
     }
   }
   const int ng_o = env_int("AQ_DECODE_NG", 0);
-  if (ng_o >= (split ? 1 : ngmin) && ng_o <= ngmax) NG = ng_o;
+  if (ng_o >= (split ? 1 : ngmin) && ng_o <= (split ? ngmax : ngmax_f)) {
+    NG = ng_o;
+    if (!split) Rf = 16 * (NG - vgmax);
+  }
   if (split) {
     const int s_o = env_int("AQ_DECODE_S", 0);
     if (s_o >= 1) S = s_o;
@@ -489,6 +506,7 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
   S = (K + kchunk - 1) / kchunk;
   // 32-bit buffer offsets: one tile's rows must stay below 2^31 bytes.
   if ((int64_t)16 * NG * K * 2 >= (int64_t(1) << 31)) return false;
+  if (!split && (Rf < 1 || vgmax + (Rf + 15) / 16 > NG)) return false;
 
   pl->split = split;
   pl->NG = NG;
@@ -499,16 +517,15 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
   for (int b = 0; b < rq.nblk; ++b) {
     const Proj &P = rq.blk[b];
     if (!split) {
-      const int rows = 16 * (NG - pl->vg[b]);
-      pl->seg[nseg++] = DecodeSeg{b, 0, t0, (int)((P.N + rows - 1) / rows)};
+      pl->seg[nseg++] = DecodeSeg{b, 0, t0, (int)((P.N + Rf - 1) / Rf), Rf};
       t0 += pl->seg[nseg - 1].ntile;
       continue;
     }
-    pl->seg[nseg++] = DecodeSeg{b, 0, t0, (int)((P.N + 16 * NG - 1) / (16 * NG))};
+    pl->seg[nseg++] = DecodeSeg{b, 0, t0, (int)((P.N + 16 * NG - 1) / (16 * NG)), 16 * NG};
     t0 += pl->seg[nseg - 1].ntile;
     pl->tcol[b] = tcol;
     if (P.r > 0) {
-      pl->seg[nseg++] = DecodeSeg{b, 1, t0, (int)((P.r + 16 * NG - 1) / (16 * NG))};
+      pl->seg[nseg++] = DecodeSeg{b, 1, t0, (int)((P.r + 16 * NG - 1) / (16 * NG)), 16 * NG};
       t0 += pl->seg[nseg - 1].ntile;
       tcol += (int)P.r;
     }
@@ -537,7 +554,7 @@ static bool launch_ng(const DecArgs &a, int NG, int grid, hipStream_t st) {
       if constexpr (MT < 4) { launch_one<MT, 4, WAVES, PART>(a, grid, st); return true; }
       return false;
     case 5:
-      if constexpr (MT == 2) { launch_one<MT, 5, WAVES, PART>(a, grid, st); return true; }
+      if constexpr (MT == 2 || (MT == 1 && !PART && WAVES == 4)) { launch_one<MT, 5, WAVES, PART>(a, grid, st); return true; }
       return false;
     case 6:
       if constexpr (MT == 2) { launch_one<MT, 6, WAVES, PART>(a, grid, st); return true; }
@@ -582,6 +599,7 @@ hipError_t launch_decode(const Recon &rq, const DecodePlan &pl, void *ws, hipStr
     const DecodeSeg &sg = pl.seg[i];
     const Proj &P = rq.blk[sg.b];
     DecSeg &d = a.g[i];
+    d.rows = sg.rows;
     if (!pl.split) {
       d.W0 = (const uint16_t *)P.W0;
       d.s = (const uint16_t *)P.s;

@@ -131,6 +131,22 @@ def test_decode_modes_qkv(M, split, ng, S, monkeypatch):
                   f"M={M} split={split} NG={ng} S={S}")
 
 
+@pytest.mark.parametrize("M", [1, 16, 20, 64])
+@pytest.mark.parametrize("rows", [5, 17, 27, 54, 64, 80])
+def test_decode_fused_rows(M, rows, monkeypatch):
+    """Fused tiles of any row count (not a multiple of 16; the last tile of each
+    block shorter still), over a fused gate/up pair with ragged N and K.  Row
+    counts that no compiled tile of the batch bucket holds fall back to the plan."""
+    monkeypatch.setenv("AQ_DECODE_SPLIT", "0")
+    monkeypatch.setenv("AQ_DECODE_ROWS", str(rows))
+    K = 1048
+    bds = [I.bundle("test", 4, f, K, 333, 16, "bf16", variant="s0" if f == "gate" else "normal")
+           for f in ("gate", "up")]
+    x = I.activations("test", 600 + M, M, K, "bf16")
+    y = B.recon_gateup(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+    assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in bds]), "bf16", f"M={M} rows={rows}")
+
+
 @pytest.mark.parametrize("M", [1, 16, 33, 64])
 @pytest.mark.parametrize("r", [49, 100, 256])
 def test_decode_high_rank_split(M, r):
