@@ -424,14 +424,15 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
   // Fused tile height.  The time of a fused dispatch follows its most loaded
   // CU: ceil(tiles / 256) workgroups, each streaming R rows of W0 from HBM plus
   // the block's Vt rows (served by L2, counted at 0.7 of a W0 row, a fit to
-  // sweeps on MI355X).  R is any row count from 16 up to what the largest
+  // sweeps on MI355X).  R is any row count from 4 up to what the largest
   // compiled tile holds, so that e.g. 2 x 6912 rows become 256 tiles of 54,
-  // one per CU, rather than 432 tiles of 32 (two on most CUs).
+  // one per CU, rather than 432 tiles of 32 (two on most CUs), and the 1536
+  // rows of a Gemma-3-1B QKV become 221 tiles of 7 rather than 96 of 16.
   const int ngmax_f = pl->MT == 1 ? 5 : ngmax;
   const int ngmin = vgmax + 1 > 2 ? vgmax + 1 : 2;
   int Rf = 0;
   double best_f = 1e30;
-  for (int R = 16; R <= 16 * (ngmax_f - vgmax); ++R) {
+  for (int R = 4; R <= 16 * (ngmax_f - vgmax); ++R) {
     const int t = fused_tiles_r(R);
     const double cost = (double)((t + kNumCU - 1) / kNumCU) * (R + 0.7 * 16 * vgmax);
     if (cost < best_f - 1e-9) { best_f = cost; Rf = R; }
