@@ -406,98 +406,67 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
     vgmax = vgmax > pl->vg[b] ? vgmax : pl->vg[b];
   }
   const int ngmax = max_ng(pl->MT);
-
-  // Fused tiles of R W0 rows (the same R for every block); a block's last tile
-  // may be shorter.
-  auto fused_tiles_r = [&](int R) {
-    int t = 0;
-    for (int b = 0; b < rq.nblk; ++b) t += (int)((rq.blk[b].N + R - 1) / R);
-    return t;
-  };
-  auto split_tiles = [&](int ng) {
-    int t = 0;
-    for (int b = 0; b < rq.nblk; ++b)
-      t += (int)((rq.blk[b].N + 16 * ng - 1) / (16 * ng)) + (int)((rq.blk[b].r + 16 * ng - 1) / (16 * ng));
-    return t;
-  };
-
-  // Fused tile height.  The time of a fused dispatch follows its most loaded
-  // CU: ceil(tiles / 256) workgroups, each streaming R rows of W0 from HBM plus
-  // the block's Vt rows (served by L2, counted at 0.7 of a W0 row, a fit to
-  // sweeps on MI355X).  R is any row count from 4 up to what the largest
-  // compiled tile holds, so that e.g. 2 x 6912 rows become 256 tiles of 54,
-  // one per CU, rather than 432 tiles of 32 (two on most CUs), and the 1536
-  // rows of a Gemma-3-1B QKV become 221 tiles of 7 rather than 96 of 16.
-  const int ngmax_f = pl->MT == 1 ? 5 : ngmax;
+  const int ngmax_f = pl->MT == 1 ? 5 : ngmax;    // fused tiles: one more group at 16 tokens
   const int ngmin = vgmax + 1 > 2 ? vgmax + 1 : 2;
+
+  // Cost model (microseconds), fitted to sweeps over the Gemma-3-1B and
+  // large-decoder decode shapes on MI355X.  A dispatch lasts as long as its
+  // most loaded CU: ceil(units / 256) work units in turn, each paying a fixed
+  // ~0.8 us (argument loads, first-load latency, epilogue) plus its bytes at
+  // the ~21.5 GB/s that one CU sustains when all 256 stream at once.  Vt rows
+  // re-read by every fused tile come from L2 and count 0.7 of a W0 row.  Split
+  // mode adds the combine launch (~3.7 us with its graph node).  Tiles hold any
+  // number of rows up to what the compiled tile holds, so that 2 x 6912 rows
+  // become 256 tiles of 54 (one per CU) and a 1536-row QKV 221 tiles of 7.
+  constexpr double kUnit = 0.8, kRate = 21500.0, kVtW = 0.7, kComb = 3.7;
+  auto rounds = [](long units) { return (double)((units + kNumCU - 1) / kNumCU); };
+  auto tiles_of = [&](int R, bool with_vt) {
+    long t = 0;
+    for (int b = 0; b < rq.nblk; ++b) {
+      t += (rq.blk[b].N + R - 1) / R;
+      if (with_vt && rq.blk[b].r > 0) t += (rq.blk[b].r + R - 1) / R;
+    }
+    return t;
+  };
   int Rf = 0;
   double best_f = 1e30;
   for (int R = 4; R <= 16 * (ngmax_f - vgmax); ++R) {
-    const int t = fused_tiles_r(R);
-    const double cost = (double)((t + kNumCU - 1) / kNumCU) * (R + 0.7 * 16 * vgmax);
-    if (cost < best_f - 1e-9) { best_f = cost; Rf = R; }
+    const double c = rounds(tiles_of(R, false)) * (kUnit + (R + kVtW * 16 * vgmax) * K * 2.0 / kRate);
+    if (c < best_f - 1e-9) { best_f = c; Rf = R; }
   }
-  const int r_o = env_int("AQ_DECODE_ROWS", 0);
-  if (r_o >= 1 && r_o <= 16 * (ngmax_f - vgmax)) Rf = r_o;
-
-  // Fused or split, from sweeps over the Gemma-3-1B and large-decoder decode
-  // shapes on MI355X.  Fused is kept while its tiles fill the chip (or K is
-  // short) and its re-reads of Vt (every workgroup streams all of it) stay
-  // below ~24 MB, the traffic that the combine launch of split mode is worth.
-  constexpr int kUnitsFused = 230;
-  constexpr double kVtRereadLimit = 24e6;
-  bool split = true;
-  int NG = ngmax;
-  if (Rf > 0) {
-    const double vt_bytes = (double)fused_tiles_r(Rf) * 16.0 * vgmax * K * 2.0;
-    const bool fills = fused_tiles_r(Rf) >= kUnitsFused || K < 2 * 2304;
-    split = !(fills && vt_bytes <= kVtRereadLimit);
-  }
-  // Tuning overrides (profiling sweeps): AQ_DECODE_SPLIT (0/1), AQ_DECODE_NG,
-  // AQ_DECODE_S, AQ_DECODE_WAVES.
-  const int sp_o = env_int("AQ_DECODE_SPLIT", -1);
-  if (sp_o == 1 || (sp_o == 0 && Rf > 0)) split = sp_o == 1;
-  if (!split) NG = ngmin > vgmax + (Rf + 15) / 16 ? ngmin : vgmax + (Rf + 15) / 16;
-  int S = 1;
-  if (split) {
-    // Split mode: every work unit (a tile over one K range) moves the same
-    // bytes, and one workgroup per CU already keeps enough loads in flight, so
-    // the time follows the most loaded CU.  Score each tile height by
-    // units / (256 * ceil(units / 256)) and take the best, preferring tall
-    // tiles (less per-unit overhead).  Fewer than 256 tiles: split K until they
-    // cover the CUs, keeping ranges of >= 2048 values; 256 tiles or more: the
-    // split (up to 4) that evens the load best.
-    const int smax = K / 512 > 1 ? K / 512 : 1;
-    double best = -1e9;
-    for (int ng = ngmax; ng >= 1; --ng) {
-      const int t = split_tiles(ng);
-      int s_ng = 1;
-      if (t >= kNumCU) {
-        double eb = -1;
-        for (int sc = 1; sc <= 4 && sc <= smax; ++sc) {
-          const int u = t * sc;
-          const double e = (double)u / (kNumCU * ((u + kNumCU - 1) / kNumCU));
-          if (e > eb + 1e-3) { eb = e; s_ng = sc; }
-        }
-      } else {
-        s_ng = kNumCU / t;
-        if (s_ng > K / 2048) s_ng = K / 2048;
-        if (s_ng < 1) s_ng = 1;
-      }
-      const int u = t * s_ng;
-      const double score = (double)u / (kNumCU * ((u + kNumCU - 1) / kNumCU)) - 0.06 * (ngmax - ng);
-      if (score > best + 1e-9) { best = score; NG = ng; S = s_ng; }
+  int Rs = 16, Ss = 1;
+  double best_s = 1e30;
+  const int smax = K / 256 > 1 ? (K / 256 < 16 ? K / 256 : 16) : 1;
+  for (int R = 8; R <= 16 * ngmax; ++R) {
+    const long t = tiles_of(R, true);
+    for (int sc = 1; sc <= smax; ++sc) {
+      const int kc = ((K + sc - 1) / sc + 127) / 128 * 128;
+      const int sr = (K + kc - 1) / kc;
+      if (sr != sc) continue;
+      const double c = rounds(t * sr) * (kUnit + (double)R * kc * 2.0 / kRate) + kComb;
+      if (c < best_s - 1e-9) { best_s = c; Rs = R; Ss = sr; }
     }
   }
+  bool split = best_s < best_f;
+
+  // Tuning overrides (profiling sweeps): AQ_DECODE_SPLIT (0/1), AQ_DECODE_ROWS,
+  // AQ_DECODE_NG (rows = 16 x the W0 groups), AQ_DECODE_S, AQ_DECODE_WAVES.
+  const int sp_o = env_int("AQ_DECODE_SPLIT", -1);
+  if (sp_o == 1 || (sp_o == 0 && Rf > 0)) split = sp_o == 1;
+  int R = split ? Rs : Rf, S = split ? Ss : 1;
+  const int rmax = split ? 16 * ngmax : 16 * (ngmax_f - vgmax);
   const int ng_o = env_int("AQ_DECODE_NG", 0);
-  if (ng_o >= (split ? 1 : ngmin) && ng_o <= (split ? ngmax : ngmax_f)) {
-    NG = ng_o;
-    if (!split) Rf = 16 * (NG - vgmax);
-  }
+  if (ng_o >= (split ? 1 : ngmin) && ng_o <= (split ? ngmax : ngmax_f)) R = 16 * (ng_o - (split ? 0 : vgmax));
+  const int r_o = env_int("AQ_DECODE_ROWS", 0);
+  if (r_o >= 1 && r_o <= rmax) R = r_o;
   if (split) {
     const int s_o = env_int("AQ_DECODE_S", 0);
     if (s_o >= 1) S = s_o;
   }
+  if (R < 1) return false;
+  int NG = split ? (R + 15) / 16 : vgmax + (R + 15) / 16;
+  if (!split && NG < ngmin) NG = ngmin;
+  if (NG > (split ? ngmax : ngmax_f)) return false;
   int WAVES = 4;
   const int w_o = env_int("AQ_DECODE_WAVES", 0);
   if (w_o == 4 || (pl->MT == 1 && w_o == 8)) WAVES = w_o;
@@ -507,7 +476,6 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
   S = (K + kchunk - 1) / kchunk;
   // 32-bit buffer offsets: one tile's rows must stay below 2^31 bytes.
   if ((int64_t)16 * NG * K * 2 >= (int64_t(1) << 31)) return false;
-  if (!split && (Rf < 1 || vgmax + (Rf + 15) / 16 > NG)) return false;
 
   pl->split = split;
   pl->NG = NG;
@@ -517,16 +485,12 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
   int t0 = 0, nseg = 0, tcol = (int)rq.Ntot;
   for (int b = 0; b < rq.nblk; ++b) {
     const Proj &P = rq.blk[b];
-    if (!split) {
-      pl->seg[nseg++] = DecodeSeg{b, 0, t0, (int)((P.N + Rf - 1) / Rf), Rf};
-      t0 += pl->seg[nseg - 1].ntile;
-      continue;
-    }
-    pl->seg[nseg++] = DecodeSeg{b, 0, t0, (int)((P.N + 16 * NG - 1) / (16 * NG)), 16 * NG};
+    pl->seg[nseg++] = DecodeSeg{b, 0, t0, (int)((P.N + R - 1) / R), R};
     t0 += pl->seg[nseg - 1].ntile;
+    if (!split) continue;
     pl->tcol[b] = tcol;
     if (P.r > 0) {
-      pl->seg[nseg++] = DecodeSeg{b, 1, t0, (int)((P.r + 16 * NG - 1) / (16 * NG)), 16 * NG};
+      pl->seg[nseg++] = DecodeSeg{b, 1, t0, (int)((P.r + R - 1) / R), R};
       t0 += pl->seg[nseg - 1].ntile;
       tcol += (int)P.r;
     }
