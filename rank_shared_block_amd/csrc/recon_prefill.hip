@@ -446,8 +446,17 @@ __global__ __launch_bounds__(256) void k_prefill_reduce(const float *part, int S
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long)M * ncols) return;
   const int m = (int)(i / ncols), n = (int)(i - (long)m * ncols);
+  // Eight partials requested at once, then added in split order: one memory
+  // round trip per eight splits instead of one per split.
   float sum = 0.f;
-  for (int q = 0; q < S; ++q) sum += part[((size_t)q * M + m) * ldp + n];
+  for (int q0 = 0; q0 < S; q0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = q0 + u < S ? part[((size_t)(q0 + u) * M + m) * ldp + n] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (q0 + u < S) sum += v[u];
+  }
   y[(size_t)m * ldy + n] = f2bf(sum);
 }
 
