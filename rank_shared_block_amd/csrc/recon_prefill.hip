@@ -491,13 +491,15 @@ struct Cand {
 };
 static const Cand kCands[] = {{128, 128, 64, 4}, {256, 128, 32, 3}, {256, 128, 64, 3}, {256, 256, 32, 4},
                                {256, 256, 64, 2}, {128, 256, 64, 3}, {128, 128, 64, 2}, {256, 128, 32, 3},
-                               {128, 256, 32, 3}, {128, 128, 32, 4}};
+                               {128, 256, 32, 3}, {128, 128, 32, 4}, {64, 64, 64, 4},   {64, 128, 64, 4},
+                               {128, 64, 64, 4}};
 
 // Main-pass tile and K split, from sweeps over the Gemma-3-1B and
 // large-decoder prefill shapes on MI355X (per-tile times there: 128 x 128 with
 // four stages ~15 us at K = 1152, one workgroup per CU; 256 x 128 with three
 // 32-wide stages ~21 us per tile with two workgroups per CU overlapping each
 // other's epilogues):
+// * up to 64 tiles of 128 x 128: 64 x 64 tiles, four stages, no K split;
 // * up to 256 tiles of 128 x 128 (one round on the CUs): 128 x 128, four
 //   stages, K split only for long K (>= 4096) when the tiles cover at most half
 //   of the CUs (ranges of >= 2048);
@@ -513,7 +515,11 @@ TileCfg choose(const Recon &rq) {
       tc = {256, 128, 64, 3, 1};
     else
       tc = {256, 128, 32, 3, 1};
-  } else if (rq.K >= 4096 && t128 > 0 && 2 * t128 <= kNumCU) {
+  } else if (t128 <= 64) {
+    // Few 128 x 128 tiles (short prompts through narrow projections): 64 x 64
+    // tiles cover four times as many CUs, with no K split to fold.
+    tc = {64, 64, 64, 4, 1};
+  } else if (rq.K >= 4096 && 2 * t128 <= kNumCU) {
     const int S = kNumCU / t128, smax = (int)(rq.K / 2048);
     tc.S = S < smax ? S : smax;
   }
@@ -588,6 +594,9 @@ static bool launch_tile(int BM, int BN, int BK, int NST, const PfArgs &a, int gr
     AQ_TILE(256, 128, 32, 3)
     AQ_TILE(128, 256, 32, 3)
     AQ_TILE(128, 128, 32, 4)
+    AQ_TILE(64, 64, 64, 4)
+    AQ_TILE(64, 128, 64, 4)
+    AQ_TILE(128, 64, 64, 4)
   }
 #undef AQ_TILE
   return false;

@@ -163,7 +163,8 @@ def test_decode_high_rank_split(M, r):
 _PREFILL_MODES = [None, (256, 256, 32, 4, 1, None), (256, 256, 64, 2, 1, None), (256, 128, 64, 3, 1, 1),
                   (128, 256, 64, 3, 1, 3), (128, 128, 64, 2, 1, None), (128, 128, 64, 4, 2, 5),
                   (256, 256, 32, 4, 3, 2), (256, 256, 64, 2, 3, 2), (256, 128, 64, 3, 2, None),
-                  (256, 128, 32, 3, 1, None), (128, 256, 32, 3, 2, 1), (128, 128, 32, 4, 1, None)]
+                  (256, 128, 32, 3, 1, None), (128, 256, 32, 3, 2, 1), (128, 128, 32, 4, 1, None),
+                  (64, 64, 64, 4, 1, None), (64, 128, 64, 4, 2, None), (128, 64, 64, 4, 1, 3)]
 
 
 @pytest.mark.parametrize("M", [65, 300, 513])
