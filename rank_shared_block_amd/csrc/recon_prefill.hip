@@ -552,16 +552,18 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
   pl->BK = tc.BK;
   pl->NST = tc.NST;
   pl->S = tc.S;
-  // Rank-r pass: 64 x 64 tiles over t's columns, K split so that the
-  // workgroups cover the CUs with ranges of >= 128 K values; the fp32 partials
-  // are folded into the bf16 t buffer by the reduce kernel.
+  // Rank-r pass: 64 x 64 tiles over t's columns.  For long K (> 2048) K is
+  // split so that the workgroups cover the CUs with ranges of >= 768 values and
+  // the fp32 partials are folded into the bf16 t buffer by the reduce kernel;
+  // for shorter K the fold costs more than the split saves (sweeps over the
+  // Gemma-3-1B prefill shapes on MI355X).
   pl->tBM = 64;
   pl->tBN = 64;
   pl->tS = 1;
-  if (c > 0) {
+  if (c > 0 && rq.K > 2048) {
     const int tiles = count_tiles(rq, 64, 64, true);
     int S = (kNumCU + tiles - 1) / tiles;
-    const int smax = rq.K / 128 > 1 ? (int)(rq.K / 128) : 1;
+    const int smax = rq.K / 768 > 1 ? (int)(rq.K / 768) : 1;
     pl->tS = S < smax ? S : smax;
     const int to = env_int("AQ_TPASS_S", 0);
     if (to >= 1) pl->tS = to;
