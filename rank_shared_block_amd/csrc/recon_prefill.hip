@@ -286,6 +286,13 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
   wait_vmcnt<(NST - 2) * LPS>();             \
   ring_barrier();                            \
   step((slice) + NST - 1, next, cur);
+  // The epilogue's s values (BN <= 256: one per thread) are requested now and
+  // kept raw in a register, so that their latency hides under the main loop;
+  // nothing waits for them before the epilogue.
+  // Every thread loads (clamped index, no branch: a load under a branch would
+  // be waited for where the branch joins).
+  uint16_t s_raw = 0;
+  if constexpr (MODE != MODE_RAW) s_raw = B.s[min(n0 + min(tid, BN - 1), B.N - 1)];
   issue(0, st0);                         // slices 0 .. NST - 2 ahead of the loop
   if constexpr (NST > 2) issue(1, st1);
   if constexpr (NST > 3) issue(2, st2);
@@ -330,7 +337,7 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
   const bool fp32_out = MODE == MODE_PART || (MODE == MODE_RAW && a.part);
   const int nst = min(BN, B.Nst - n0);
   if (MODE != MODE_RAW)
-    for (int c = tid; c < BN; c += 256) s_lds[c] = n0 + c < B.N ? bf2f(B.s[n0 + c]) : 0.f;
+    if (tid < BN) s_lds[tid] = n0 + tid < B.N ? bf2f(s_raw) : 0.f;
   __syncthreads();                       // s_lds, and every wave's last loads, are in
 
   // Rank-r fragments (this lane's 8 ranks of rank step kk): chunks c < nech
