@@ -346,10 +346,30 @@ __global__ __launch_bounds__(256) void k_decode_combine(const CombArgs a) {
     u0 = ld16(u);
     if (r > 8) u1 = ld16(u + 8);
   }
-  float z = 0.f;
-  if (live)
-    for (int q = 0; q < a.S; ++q) z += row[q * pstride + B.col + n];
-  for (int j = tid; j < r; j += 256) {
+  // The partials of this thread's column (z) and, for threads below r, of one
+  // rank (t) are requested eight splits at a time, both before either is
+  // added up (in split order): one memory round trip per eight splits, not one
+  // per split and partial.
+  float z = 0.f, tj = 0.f;
+  const bool has_t = tid < r;
+  const float *zp = row + B.col + nc, *tp = row + B.tcol + (has_t ? tid : 0);
+  for (int q0 = 0; q0 < a.S; q0 += 8) {
+    float zv[8], tv8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool in = q0 + e < a.S;
+      zv[e] = in ? zp[(size_t)(q0 + e) * pstride] : 0.f;
+      tv8[e] = in && has_t ? tp[(size_t)(q0 + e) * pstride] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (q0 + e < a.S) {
+        z += zv[e];
+        tj += tv8[e];
+      }
+  }
+  if (has_t) T[tid] = tj;
+  for (int j = tid + 256; j < r; j += 256) {   // ranks past 256 threads (not reached for r <= 256)
     float v = 0.f;
     for (int q = 0; q < a.S; ++q) v += row[q * pstride + B.tcol + j];
     T[j] = v;
