@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256, 4) void k_materialize_bf16(const MatArgs a) {
   // g -> columns cb0 + 32 t + 8 g + 4 hi .. + 3, all in range or none since
   // K % 8 == 0), its s, and its U row as B operands.
   uint2 w[2][4];
-  float sv;
+  uint16_t s_raw;
   bf16x8 bu[RJ];
   auto fetch = [&](int n0) {
     const int n = n0 + l32;
@@ -66,7 +66,9 @@ __global__ __launch_bounds__(256, 4) void k_materialize_bf16(const MatArgs a) {
         const int k = cb0 + 32 * t + 8 * g + 4 * hi;
         w[t][g] = rowok && k < K ? *reinterpret_cast<const uint2 *>(W0 + (size_t)n * K + k) : make_uint2(0, 0);
       }
-    sv = rowok ? bf2f(S[n]) : 0.f;
+    // s stays raw until it is used and its load is not under a branch, so
+    // that nothing waits for it before the U loads go out.
+    s_raw = S[rowok ? n : nb];
 #pragma unroll
     for (int kk = 0; kk < RJ; ++kk) {
       const int j = 16 * kk + 8 * hi;
@@ -128,6 +130,7 @@ __global__ __launch_bounds__(256, 4) void k_materialize_bf16(const MatArgs a) {
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], bu[kk], acc[t], 0, 0, 0);
     }
     if (!rowok) continue;
+    const float sv = bf2f(s_raw);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
