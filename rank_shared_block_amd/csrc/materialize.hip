@@ -7,14 +7,15 @@
 // * Streaming W0 in and W_eff out is the bound (2 + 2 bytes per element); the
 //   rank-r product costs 2 r flop per element, which at r = 64 would exceed the
 //   fp32 VALU roofline, so it runs on v_mfma_f32_32x32x16_bf16.
-// * A workgroup owns a block of 64 columns and a range of rows; each wave takes
-//   32-row blocks of the range in turn.  The Vt block [r, 64] is staged once in
-//   LDS transposed (64 columns x r ranks, rank-contiguous) and is the A operand
+// * A workgroup owns a block of 64 columns and a range of rows, taken 128 rows
+//   (32 per wave) at a time.  The Vt block [r, 64] is staged once in LDS
+//   transposed (64 columns x r ranks, rank-contiguous) and is the A operand
 //   (8 consecutive ranks of one column per lane); U rows are the B operand
 //   (8 consecutive ranks of one row per lane, one 16-byte load).  The result
 //   comes out transposed: a lane holds one output row and, per group of four
-//   accumulator values, 4 consecutive output columns, so W0 is read and W_eff
-//   written with 8-byte accesses.
+//   accumulator values, 4 consecutive output columns.  W0 comes in and W_eff
+//   goes out as whole 128-byte row pieces (16 bytes per lane) through an LDS
+//   tile, where the product meets W0 in the accumulator layout.
 // * Many small workgroups (four per CU) keep enough loads in flight to hide the
 //   memory latency without software pipelining.
 // * diag(s) W0 is added in fp32 with one fused multiply-add per element; with
@@ -39,8 +40,11 @@ struct MatArgs {
 template <int RJ>
 __global__ __launch_bounds__(256, 4) void k_materialize_bf16(const MatArgs a) {
   constexpr int CB = 64;                    // columns per workgroup
+  constexpr int RB = 128;                   // rows per step (32 per wave)
   constexpr int RP = 16 * RJ + 8;           // LDS row (one column of Vt, rank-contiguous), padded
+  constexpr int WP = CB + 8;                // LDS row of the W0 / W_eff tile, padded
   __shared__ __attribute__((aligned(16))) uint16_t vts[CB * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t wt[RB * WP];
   const uint16_t *W0 = (const uint16_t *)a.W0, *S = (const uint16_t *)a.s;
   const uint16_t *U = (const uint16_t *)a.U, *Vt = (const uint16_t *)a.Vt;
   uint16_t *out = (uint16_t *)a.out;
@@ -48,27 +52,45 @@ __global__ __launch_bounds__(256, 4) void k_materialize_bf16(const MatArgs a) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int K = a.K, r = a.r, N = a.N;
   const int cb0 = blockIdx.x * CB;
+  const int ncol = min(CB, K - cb0);        // a multiple of 8 (K % 8 == 0)
   const int nb = blockIdx.y * a.rows_per_wg, ne = min(N, nb + a.rows_per_wg);
 
-  // Operands of one 32-row block: W0 of this lane's row (column tile t, group
-  // g -> columns cb0 + 32 t + 8 g + 4 hi .. + 3, all in range or none since
-  // K % 8 == 0), its s, and its U row as B operands.
-  uint2 w[2][4];
-  uint16_t s_raw;
-  bf16x8 bu[RJ];
-  auto fetch = [&](int n0) {
-    const int n = n0 + l32;
-    const bool rowok = n < ne;
+  // Stage Vt[:, cb0 : cb0 + 64] transposed (zeros past r or K): thread i reads
+  // 8 columns of one rank row and writes them to 8 LDS rows.
+  for (int i = tid; i < 16 * RJ * (CB / 8); i += 256) {
+    const int j = i % (16 * RJ), c = (i / (16 * RJ)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (j < r && c < ncol) v = ld16(Vt + (size_t)j * K + cb0 + c);
+    const uint32_t q4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int q = 0; q < 8; ++q) vts[(c + q) * RP + j] = (uint16_t)(q4[q >> 1] >> ((q & 1) * 16));
+  }
+  __syncthreads();
+
+  // A operands: column tile t (columns 32 t + lane % 32), rank step kk.
+  bf16x8 av[2][RJ];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int k = cb0 + 32 * t + 8 * g + 4 * hi;
-        w[t][g] = rowok && k < K ? *reinterpret_cast<const uint2 *>(W0 + (size_t)n * K + k) : make_uint2(0, 0);
-      }
-    // s stays raw until it is used and its load is not under a branch, so
-    // that nothing waits for it before the U loads go out.
-    s_raw = S[rowok ? n : nb];
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int kk = 0; kk < RJ; ++kk)
+      av[t][kk] = as_bf16x8(*reinterpret_cast<const uint4 *>(&vts[(32 * t + l32) * RP + 16 * kk + 8 * hi]));
+
+  // W0 in and W_eff out move as whole 128-byte row pieces: thread i handles the
+  // 16-byte chunks i, i + 256, ... of the 128 x 64 step tile (8 per row),
+  // through the LDS tile wt; the MFMA result meets W0 there, in its own layout.
+  for (int n0 = nb; n0 < ne; n0 += RB) {
+    const int nrow = min(RB, ne - n0);
+    uint4 wv[RB * CB / 8 / 256];
+#pragma unroll
+    for (int q = 0; q < RB * CB / 8 / 256; ++q) {
+      const int c = tid + 256 * q, row = c >> 3, col = (c & 7) * 8;
+      wv[q] = row < nrow && col < ncol ? ld16(W0 + (size_t)(n0 + row) * K + cb0 + col) : make_uint4(0, 0, 0, 0);
+    }
+    // This lane's output row (its s, and its U row as the B operand).
+    const int rl = 32 * wave + l32, n = n0 + rl;
+    const bool rowok = rl < nrow;
+    const uint16_t s_raw = S[rowok ? n : n0];   // branch-free: converted at its use
+    bf16x8 bu[RJ];
 #pragma unroll
     for (int kk = 0; kk < RJ; ++kk) {
       const int j = 16 * kk + 8 * hi;
@@ -88,33 +110,11 @@ __global__ __launch_bounds__(256, 4) void k_materialize_bf16(const MatArgs a) {
         bu[kk] = as_bf16x8(u);
       }
     }
-  };
-  const int nfirst = nb + 32 * wave;
-
-  // Stage Vt[:, cb0 : cb0 + 64] transposed (zeros past r or K): thread i reads
-  // 8 columns of one rank row and writes them to 8 LDS rows.
-  for (int i = tid; i < 16 * RJ * (CB / 8); i += 256) {
-    const int j = i % (16 * RJ), c = (i / (16 * RJ)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (j < r && cb0 + c < K) v = ld16(Vt + (size_t)j * K + cb0 + c);
-    const uint32_t q4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) vts[(c + q) * RP + j] = (uint16_t)(q4[q >> 1] >> ((q & 1) * 16));
-  }
-  __syncthreads();
-
-  // A operands: column tile t (columns 32 t + lane % 32), rank step kk.
-  bf16x8 av[2][RJ];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int kk = 0; kk < RJ; ++kk)
-      av[t][kk] = as_bf16x8(*reinterpret_cast<const uint4 *>(&vts[(32 * t + l32) * RP + 16 * kk + 8 * hi]));
-
-  for (int n0 = nfirst; n0 < ne; n0 += 128) {
-    const int n = n0 + l32;                   // this lane's output row
-    const bool rowok = n < ne;
-    fetch(n0);
+    for (int q = 0; q < RB * CB / 8 / 256; ++q) {
+      const int c = tid + 256 * q, row = c >> 3, col = (c & 7) * 8;
+      *reinterpret_cast<uint4 *>(&wt[row * WP + col]) = wv[q];
+    }
     // acc[t]: column 32 t + 8 (v / 4) + 4 hi + (v % 4) of row n.  Every lane
     // takes part in the MFMAs (they read all lanes' operands).
     f32x16 acc[2];
@@ -129,21 +129,32 @@ __global__ __launch_bounds__(256, 4) void k_materialize_bf16(const MatArgs a) {
         for (int t = 0; t < 2; ++t)
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][kk], bu[kk], acc[t], 0, 0, 0);
     }
-    if (!rowok) continue;
+    __syncthreads();                        // the W0 tile is in LDS
+    // w_eff = s * w + acc, in place: every lane reads and writes only its own
+    // 4-column groups of its own row.
     const float sv = bf2f(s_raw);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int k = cb0 + 32 * t + 8 * g + 4 * hi;
-        if (k >= K) continue;
+        uint2 *p = reinterpret_cast<uint2 *>(&wt[rl * WP + 32 * t + 8 * g + 4 * hi]);
+        const uint2 w = *p;
         uint2 o;
-        o.x = f2bf(fmaf(sv, bf2f((uint16_t)w[t][g].x), acc[t][4 * g + 0])) |
-              ((uint32_t)f2bf(fmaf(sv, bf2f((uint16_t)(w[t][g].x >> 16)), acc[t][4 * g + 1])) << 16);
-        o.y = f2bf(fmaf(sv, bf2f((uint16_t)w[t][g].y), acc[t][4 * g + 2])) |
-              ((uint32_t)f2bf(fmaf(sv, bf2f((uint16_t)(w[t][g].y >> 16)), acc[t][4 * g + 3])) << 16);
-        *reinterpret_cast<uint2 *>(out + (size_t)n * a.ldw + k) = o;
+        o.x = f2bf(fmaf(sv, bf2f((uint16_t)w.x), acc[t][4 * g + 0])) |
+              ((uint32_t)f2bf(fmaf(sv, bf2f((uint16_t)(w.x >> 16)), acc[t][4 * g + 1])) << 16);
+        o.y = f2bf(fmaf(sv, bf2f((uint16_t)w.y), acc[t][4 * g + 2])) |
+              ((uint32_t)f2bf(fmaf(sv, bf2f((uint16_t)(w.y >> 16)), acc[t][4 * g + 3])) << 16);
+        *p = o;
       }
+    __syncthreads();                        // W_eff tile complete
+#pragma unroll
+    for (int q = 0; q < RB * CB / 8 / 256; ++q) {
+      const int c = tid + 256 * q, row = c >> 3, col = (c & 7) * 8;
+      if (row < nrow && col < ncol)
+        *reinterpret_cast<uint4 *>(out + (size_t)(n0 + row) * a.ldw + cb0 + col) =
+            *reinterpret_cast<const uint4 *>(&wt[row * WP + col]);
+    }
+    __syncthreads();                        // wt is reused by the next step
   }
 }
 
