@@ -365,7 +365,6 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
   for (int i = 0; i < TM; ++i) {
     const int m = m0 + wm * WM + i * 32 + l32;
     uint16_t *const ost = wm ? ost1 : ost0;
-    if (!fp32_out) __syncthreads();      // the previous round's reads of the staging are done
 #pragma unroll
     for (int j0 = 0; j0 < TN; j0 += JH) {
       f32x16 w[JH];
@@ -429,20 +428,24 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
       }
     }
     if (fp32_out) continue;
-    __syncthreads();
-    for (int c = tid; c < 64 * (BN / 8); c += 256) {
-      const int rl = c / (BN / 8), nc = (c - rl * (BN / 8)) * 8;
-      const int h = rl >> 5;
-      const int mr = m0 + h * WM + i * 32 + (rl & 31);
+    // Each wave stores the 32 x WN block it staged itself (rows of WN * 2
+    // bytes, 16 bytes per lane), so no workgroup barrier is needed: its own LDS
+    // writes complete before its reads (lgkmcnt), and its next round's writes
+    // come after these reads.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (int c = lane; c < 32 * (WN / 8); c += 64) {
+      const int rl = c / (WN / 8), nc = wn * WN + (c - rl * (WN / 8)) * 8;
+      const int mr = m0 + wm * WM + i * 32 + rl;
       if (mr >= M || nc >= nst) continue;
       uint16_t *dst = a.y + (size_t)mr * a.ldy + B.col + n0 + nc;
-      const uint16_t *src = (h ? ost1 : ost0) + (rl & 31) * OP + nc;
+      const uint16_t *src = ost + rl * OP + nc;
       if (a.vec_store && nc + 8 <= nst) {
         *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
       } else {
         for (int e = 0; e < 8 && nc + e < nst; ++e) dst[e] = src[e];
       }
     }
+    asm volatile("" ::: "memory");
   }
 }
 
