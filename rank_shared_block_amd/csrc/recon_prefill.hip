@@ -378,12 +378,27 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
           if (c >= nech) break;
           const uint16_t *stc = c == 0 ? st0 : (c == 1 ? st1 : st2);
           const int kmax = min(BK / 16, (r16 - BK * c) / 16);
-          for (int kk = 0; kk < kmax; ++kk) {
-            const bf16x8 tb = tfrag_lds(stc, i, kk);
+          if (B.ufast) {
+            // All of the chunk's fragments first, then the MFMA chain: one LDS
+            // round trip per chunk instead of one per k-step.  k-steps past
+            // kmax multiply zeros.
+            bf16x8 tf[BK / 16], uf[BK / 16][JH];
 #pragma unroll
-            for (int q = 0; q < JH; ++q) {
-              const bf16x8 ua = B.ufast ? ufrag_lds(stc, j0 + q, kk) : ufrag_glb(j0 + q, BK * c + 16 * kk + 8 * lhi);
-              w[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua, tb, w[q], 0, 0, 0);
+            for (int kk = 0; kk < BK / 16; ++kk) {
+              tf[kk] = kk < kmax ? tfrag_lds(stc, i, kk) : zero_bf16x8();
+#pragma unroll
+              for (int q = 0; q < JH; ++q) uf[kk][q] = kk < kmax ? ufrag_lds(stc, j0 + q, kk) : zero_bf16x8();
+            }
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+              for (int q = 0; q < JH; ++q) w[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf[kk][q], tf[kk], w[q], 0, 0, 0);
+          } else {
+            for (int kk = 0; kk < kmax; ++kk) {
+              const bf16x8 tb = tfrag_lds(stc, i, kk);
+#pragma unroll
+              for (int q = 0; q < JH; ++q)
+                w[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ufrag_glb(j0 + q, BK * c + 16 * kk + 8 * lhi), tb, w[q], 0, 0, 0);
             }
           }
         }
