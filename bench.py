@@ -315,6 +315,29 @@ def summarize_profiles(args):
         for (name, wg), d in sorted(agg.items(), key=lambda kv: -sum(kv[1]))[:14]:
             d.sort()
             out.append(f"| `{name[:80]}` | {wg} | {len(d)} | {sum(d)/len(d):.3f} | {d[len(d)//2]:.3f} | {sum(d):.1f} |")
+        if args.calls:
+            # A prefill call is its kernels in launch order up to the main GEMM
+            # (MODE 0), or up to the fold that follows a K-split main GEMM (MODE 1).
+            seq = []
+            for r in sorted(tr, key=lambda r: int(r["Start_Timestamp"])):
+                if "aq::" not in r["Kernel_Name"]:
+                    continue
+                name = r["Kernel_Name"].split("(")[0].replace("void aq::", "").replace("aq::", "")
+                wg = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1) // int(r["Workgroup_Size_X"])
+                seq.append((name, wg, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+            calls, cur = collections.defaultdict(list), []
+            for k in seq:
+                cur.append(k)
+                if k[0].endswith(", 0>") or (k[0] == "k_prefill_reduce" and any(c[0].endswith(", 1>") for c in cur)):
+                    calls[tuple((c[0], c[1]) for c in cur)].append([c[2] for c in cur])
+                    cur = []
+            out.append("")
+            out.append("| calls | kernels (grid) in order: mean us | total us |")
+            out.append("|---|---|---|")
+            for key, runs in sorted(calls.items(), key=lambda kv: -sum(map(sum, kv[1])) / len(kv[1]) * len(kv[1])):
+                means = [sum(r[i] for r in runs) / len(runs) for i in range(len(key))]
+                parts = " + ".join(f"`{key[i][0]}` [{key[i][1]}] {means[i]:.2f}" for i in range(len(key)))
+                out.append(f"| {len(runs)} | {parts} | {sum(means):.2f} |")
     if args.fetch and args.write:
         res = {}
         for key, path in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
@@ -545,6 +568,8 @@ def main():
     ap.add_argument("--summarize", action="store_true",
                     help="summarise rocprofv3 CSVs (--trace, --fetch, --write) instead of running")
     ap.add_argument("--trace")
+    ap.add_argument("--calls", action="store_true",
+                    help="with --trace: also group the library's prefill kernels into calls")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--layers", type=int, default=0)
