@@ -45,6 +45,8 @@
 
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "aq_internal.h"
 #include "device_common.h"
 
@@ -250,9 +252,11 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
   // when the output block needs two stages for staging)
   constexpr int ESLOTS = 64 * (BN + 8) <= STAGE ? NST - 1 : NST - 2;
   const int nech = addu ? min(nchunk, ESLOTS) : 0;
-  auto step = [&](int nslice, uint16_t *next, const uint16_t *cur) __attribute__((always_inline)) {
+  // TAIL: the step may issue a slice past nkp (a rank chunk); only the last
+  // NST steps can, so the others are compiled without that selection.
+  auto step = [&](auto tail, int nslice, uint16_t *next, const uint16_t *cur) __attribute__((always_inline)) {
     const int k0 = kbeg + nslice * BK, klim = nslice < nk ? kend : -1;
-    const int ech = nslice >= nkp && nslice - nkp < nech ? nslice - nkp : -1;
+    const int ech = decltype(tail)::value && nslice >= nkp && nslice - nkp < nech ? nslice - nkp : -1;
     bf16x8 fa[2][TM], fb[2][TN];
     frags(cur, 0, fa[0], fb[0]);
 #pragma unroll
@@ -282,10 +286,24 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
   // range (zeros, no memory traffic), which keeps the wait counts uniform.
   // The ring is written out per stage count with the stage objects named, so
   // that the compiler keeps their distinct alias scopes and adds no waits.
-#define AQ_STEP(slice, next, cur)            \
+#define AQ_STEP(tail, slice, next, cur)      \
   wait_vmcnt<(NST - 2) * LPS>();             \
   ring_barrier();                            \
-  step((slice) + NST - 1, next, cur);
+  step(tail, (slice) + NST - 1, next, cur);
+#define AQ_GROUP(tail, s)                       \
+  if constexpr (NST == 2) {                     \
+    AQ_STEP(tail, s, st1, st0)                  \
+    AQ_STEP(tail, s + 1, st0, st1)              \
+  } else if constexpr (NST == 3) {              \
+    AQ_STEP(tail, s, st2, st0)                  \
+    AQ_STEP(tail, s + 1, st0, st1)              \
+    AQ_STEP(tail, s + 2, st1, st2)              \
+  } else {                                      \
+    AQ_STEP(tail, s, st3, st0)                  \
+    AQ_STEP(tail, s + 1, st0, st1)              \
+    AQ_STEP(tail, s + 2, st1, st2)              \
+    AQ_STEP(tail, s + 3, st2, st3)              \
+  }
   // The epilogue's s values (BN <= 256: one per thread) are requested now and
   // kept raw in a register, so that their latency hides under the main loop;
   // nothing waits for them before the epilogue.
@@ -296,35 +314,30 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
   issue(0, st0);                         // slices 0 .. NST - 2 ahead of the loop
   if constexpr (NST > 2) issue(1, st1);
   if constexpr (NST > 3) issue(2, st2);
-  for (int s = 0; s < nkp; s += NST) {
-    if constexpr (NST == 2) {
-      AQ_STEP(s, st1, st0)
-      AQ_STEP(s + 1, st0, st1)
-    } else if constexpr (NST == 3) {
-      AQ_STEP(s, st2, st0)
-      AQ_STEP(s + 1, st0, st1)
-      AQ_STEP(s + 2, st1, st2)
-    } else {
-      AQ_STEP(s, st3, st0)
-      AQ_STEP(s + 1, st0, st1)
-      AQ_STEP(s + 2, st1, st2)
-      AQ_STEP(s + 3, st2, st3)
-    }
+  for (int s = 0; s < nkp - NST; s += NST) {
+    AQ_GROUP(std::false_type{}, s)
   }
+  // Every K range holds at least one slice (K >= 1), so nkp >= NST.  The last
+  // group runs unconditionally: a branch around it would put a join between
+  // the last MFMAs and the epilogue's first reads of their results.
+  AQ_GROUP(std::true_type{}, nkp - NST)
+#undef AQ_GROUP
 #undef AQ_STEP
   __builtin_amdgcn_s_waitcnt(0);         // drain the (out-of-range) tail loads
 
-  // ---- epilogue, one 32-row block of each wave row per round.  MFMA 32x32
-  // output layout with W as the A operand: lane holds output row
-  // m = mbase + lane % 32 and output columns n = nbase + 8 (v / 4) +
-  // 4 (lane / 32) + (v % 4), v = 0..15.
-  // The rank-r term w = t U^T is one more contraction, over r instead of K.
-  // Rank chunk c < NST - 1 sits in stage c, laid out like a K slice (it came
-  // with the tail of the ring); chunks past those (r > BK (NST - 1)) are read
-  // straight from global memory.  Per round i and column block j, w goes into
-  // 16 fresh accumulators, then y = s * acc + w is written: fp32 partials
-  // directly, bf16 through stage NST - 1 (8 bytes per lane and column group).
-  // The rank-r pass (MODE_RAW) writes acc itself (no s, no w).
+  // ---- epilogue.  MFMA 32x32 output layout with W as the A operand: lane
+  // holds output row m = mbase + lane % 32 and output columns n = nbase +
+  // 8 (v / 4) + 4 (lane / 32) + (v % 4), v = 0..15.
+  // First acc *= s, once per accumulator.  The rank-r term w = t U^T is one
+  // more contraction, over r instead of K, that adds straight into acc: rank
+  // chunk c < NST - 1 sits in stage c laid out like a K slice (it came with the
+  // tail of the ring), so it is multiplied like one more K slice, with the
+  // same fragment reads and MFMAs.  Chunks that did not fit in the ring, and U
+  // rows that are not 16-byte aligned, are read from global memory per 32-row
+  // round into 16 fresh accumulators that are added at the end.  Then, one
+  // 32-row block of each wave row per round, y is written: fp32 partials
+  // directly, bf16 through LDS (8 bytes per lane and column group).  The
+  // rank-r pass (MODE_RAW) writes acc itself (no s, no w).
   constexpr int OP = BN + 8;                     // staging row pitch (bank spread, 16-byte rows)
   // Output staging: wave row 0's 32 rows in ost0, wave row 1's in ost1 (the
   // last stage holds both when it can, else the last two stages).
@@ -335,18 +348,60 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
   uint16_t *const ost1 = ESLOTS == NST - 1 ? slast + 32 * OP : slast;
   __shared__ float s_lds[BN];
   const bool fp32_out = MODE == MODE_PART || (MODE == MODE_RAW && a.part);
+  // fp32 rows of 4 columns as one 16-byte store where every row and block
+  // start is 16-byte aligned
+  const bool part_vec = ((a.ldp | B.col) & 3) == 0;
   const int nst = min(BN, B.Nst - n0);
   if (MODE != MODE_RAW)
     if (tid < BN) s_lds[tid] = n0 + tid < B.N ? bf2f(s_raw) : 0.f;
   __syncthreads();                       // s_lds, and every wave's last loads, are in
 
-  // Rank-r fragments (this lane's 8 ranks of rank step kk): chunks c < nech
-  // from stage c, the rest from global memory.
+  if constexpr (MODE != MODE_RAW) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 sc = *reinterpret_cast<const float4 *>(s_lds + wn * WN + j * 32 + 8 * g + 4 * lhi);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          acc[i][j][4 * g + 0] *= sc.x;
+          acc[i][j][4 * g + 1] *= sc.y;
+          acc[i][j][4 * g + 2] *= sc.z;
+          acc[i][j][4 * g + 3] *= sc.w;
+        }
+      }
+  }
+  // Rank chunks in the ring (16-byte aligned U rows): k-steps past r16 hold
+  // zeros and are skipped.
+  const bool ring_rank = addu && B.ufast;
+  if (ring_rank) {
+#pragma unroll
+    for (int c = 0; c < ESLOTS; ++c) {
+      if (c >= nech) break;
+      const uint16_t *stc = c == 0 ? st0 : (c == 1 ? st1 : st2);
+      const int kmax = min(KK, (r16 - BK * c) / 16);
+      bf16x8 fa[2][TM], fb[2][TN];
+      frags(stc, 0, fa[0], fb[0]);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk >= kmax) break;
+        if (kk + 1 < KK) frags(stc, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+  // Rank chunks left for the per-round path.
+  const int cfirst = ring_rank ? nech : 0;
+  const bool wround = addu && cfirst < nchunk;
+
+  // Per-round rank-r fragments (this lane's 8 ranks at column col): t from
+  // stage c for chunks c < nech, else from global memory; U from global memory.
   auto tfrag_lds = [&](const uint16_t *stc, int i, int kk) __attribute__((always_inline)) {
     return as_bf16x8(*reinterpret_cast<const uint4 *>(stc + arow + i * 32 * BK + 8 * ((2 * kk + lhi) ^ swz)));
-  };
-  auto ufrag_lds = [&](const uint16_t *stc, int j, int kk) __attribute__((always_inline)) {
-    return as_bf16x8(*reinterpret_cast<const uint4 *>(stc + brow + j * 32 * BK + 8 * ((2 * kk + lhi) ^ swz)));
   };
   auto tfrag_glb = [&](int i, int col) __attribute__((always_inline)) {
     const int m = m0 + wm * WM + i * 32 + l32;
@@ -356,15 +411,48 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
     const int n = n0 + wn * WN + j * 32 + l32;
     return n < B.N ? load_u8(B, n, col) : zero_bf16x8();
   };
-  const int nch = (r16 + BK - 1) / BK;
 
-  // Column blocks per rank-r pass: every block's MFMA chain at once where the
-  // registers allow, else two at a time.
+  // Column blocks per round of the per-round rank-r path: every block's MFMA
+  // chain at once where the registers allow, else two at a time.
   constexpr int JH = (gemm_occupancy<BM, BN, BK, NST>() == 1 && TM * TN <= 8) ? TN : (TN >= 2 ? 2 : 1);
+  // bf16 output: each wave stages its 32 x WN block of a round in LDS and
+  // stores it itself as 16-byte row pieces, one round late: the staged block
+  // of round i - 1 is read back before round i is computed (LDS operations of
+  // one wave complete in order, so round i's writes land after those reads),
+  // and stored after round i's writes, so no wait sits between an LDS access
+  // and its use, and no workgroup barrier is needed.
+  constexpr int NSC = WN / 16;                     // 16-byte pieces per lane and round
+  uint16_t *const ost = wm ? ost1 : ost0;
+  uint4 pend[NSC];
+  auto stage_read = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NSC; ++q) {
+      const int c = lane + 64 * q, rl = c / (WN / 8), nc = wn * WN + (c - rl * (WN / 8)) * 8;
+      pend[q] = *reinterpret_cast<const uint4 *>(ost + rl * OP + nc);
+    }
+  };
+  auto stage_store = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NSC; ++q) {
+      const int c = lane + 64 * q, rl = c / (WN / 8), nc = wn * WN + (c - rl * (WN / 8)) * 8;
+      const int mr = m0 + wm * WM + i * 32 + rl;
+      if (mr >= M || nc >= nst) continue;
+      uint16_t *dst = a.y + (size_t)mr * a.ldy + B.col + n0 + nc;
+      if (a.vec_store && nc + 8 <= nst) {
+        *reinterpret_cast<uint4 *>(dst) = pend[q];
+      } else {
+        const uint32_t wv[4] = {pend[q].x, pend[q].y, pend[q].z, pend[q].w};
+        for (int e = 0; e < 8 && nc + e < nst; ++e) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  };
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m = m0 + wm * WM + i * 32 + l32;
-    uint16_t *const ost = wm ? ost1 : ost0;
+    if (!fp32_out && i > 0) {
+      stage_read();
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int j0 = 0; j0 < TN; j0 += JH) {
       f32x16 w[JH];
@@ -372,41 +460,13 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
       for (int q = 0; q < JH; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) w[q][v] = 0.f;
-      if (addu) {
-#pragma unroll
-        for (int c = 0; c < ESLOTS; ++c) {
-          if (c >= nech) break;
+      if (wround) {
+        for (int c = cfirst; c < nchunk; ++c) {
+          const int kmax = min(KK, (r16 - BK * c) / 16);
           const uint16_t *stc = c == 0 ? st0 : (c == 1 ? st1 : st2);
-          const int kmax = min(BK / 16, (r16 - BK * c) / 16);
-          if (B.ufast) {
-            // All of the chunk's fragments first, then the MFMA chain: one LDS
-            // round trip per chunk instead of one per k-step.  k-steps past
-            // kmax multiply zeros.
-            bf16x8 tf[BK / 16], uf[BK / 16][JH];
-#pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-              tf[kk] = kk < kmax ? tfrag_lds(stc, i, kk) : zero_bf16x8();
-#pragma unroll
-              for (int q = 0; q < JH; ++q) uf[kk][q] = kk < kmax ? ufrag_lds(stc, j0 + q, kk) : zero_bf16x8();
-            }
-#pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk)
-#pragma unroll
-              for (int q = 0; q < JH; ++q) w[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf[kk][q], tf[kk], w[q], 0, 0, 0);
-          } else {
-            for (int kk = 0; kk < kmax; ++kk) {
-              const bf16x8 tb = tfrag_lds(stc, i, kk);
-#pragma unroll
-              for (int q = 0; q < JH; ++q)
-                w[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ufrag_glb(j0 + q, BK * c + 16 * kk + 8 * lhi), tb, w[q], 0, 0, 0);
-            }
-          }
-        }
-        for (int c = nech; c < nch; ++c) {
-          const int kmax = min(BK / 16, (r16 - BK * c) / 16);
           for (int kk = 0; kk < kmax; ++kk) {
             const int col = BK * c + 16 * kk + 8 * lhi;
-            const bf16x8 tb = tfrag_glb(i, col);
+            const bf16x8 tb = c < nech ? tfrag_lds(stc, i, kk) : tfrag_glb(i, col);
 #pragma unroll
             for (int q = 0; q < JH; ++q)
               w[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ufrag_glb(j0 + q, col), tb, w[q], 0, 0, 0);
@@ -421,18 +481,15 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
           const int nl = wn * WN + j * 32 + 8 * g + 4 * lhi;
           float o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e];
-          if (MODE != MODE_RAW) {
-            const float4 sc = *reinterpret_cast<const float4 *>(s_lds + nl);
-            o[0] = sc.x * o[0] + w[q][4 * g + 0];
-            o[1] = sc.y * o[1] + w[q][4 * g + 1];
-            o[2] = sc.z * o[2] + w[q][4 * g + 2];
-            o[3] = sc.w * o[3] + w[q][4 * g + 3];
-          }
+          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e] + w[q][4 * g + e];
           if (fp32_out) {
             if (m < M) {
               float *dst = a.part + ((size_t)p * M + m) * a.ldp + B.col + n0 + nl;
-              for (int e = 0; e < 4 && nl + e < nst; ++e) dst[e] = o[e];
+              if (part_vec && nl + 4 <= nst) {
+                *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+              } else {
+                for (int e = 0; e < 4 && nl + e < nst; ++e) dst[e] = o[e];
+              }
             }
           } else {
             typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -442,25 +499,11 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
         }
       }
     }
-    if (fp32_out) continue;
-    // Each wave stores the 32 x WN block it staged itself (rows of WN * 2
-    // bytes, 16 bytes per lane), so no workgroup barrier is needed: its own LDS
-    // writes complete before its reads (lgkmcnt), and its next round's writes
-    // come after these reads.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    for (int c = lane; c < 32 * (WN / 8); c += 64) {
-      const int rl = c / (WN / 8), nc = wn * WN + (c - rl * (WN / 8)) * 8;
-      const int mr = m0 + wm * WM + i * 32 + rl;
-      if (mr >= M || nc >= nst) continue;
-      uint16_t *dst = a.y + (size_t)mr * a.ldy + B.col + n0 + nc;
-      const uint16_t *src = ost + rl * OP + nc;
-      if (a.vec_store && nc + 8 <= nst) {
-        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
-      } else {
-        for (int e = 0; e < 8 && nc + e < nst; ++e) dst[e] = src[e];
-      }
-    }
-    asm volatile("" ::: "memory");
+    if (!fp32_out && i > 0) stage_store(i - 1);
+  }
+  if (!fp32_out) {
+    stage_read();
+    stage_store(TM - 1);
   }
 }
 
