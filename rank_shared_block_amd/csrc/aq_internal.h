@@ -72,6 +72,7 @@ struct PrefillPlan {
   int ldt;                          // columns of the t buffer (sum of r rounded to 16)
   int tcol[kMaxBlocks];
   int BM, BN, BK, NST, S;           // output tile, K slice, LDS stages, K splits (main pass)
+  int NW;                           // waves per workgroup (main pass)
   int tBM, tBN, tS;                 // output tile and K splits of the rank-r (t) pass
   size_t tpart_off;                 // byte offset of the t-pass partials in the scratch
   size_t part_off;                  // byte offset of the main-pass partials in the scratch

@@ -111,16 +111,23 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "m
 template <int BM, int BN, int BK, int NST>
 constexpr int gemm_occupancy() { return (BM + BN) * BK * 2 * NST <= 80 * 1024 ? 2 : 1; }
 
-template <int BM, int BN, int BK, int NST, int MODE>
-__global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_gemm_bf16(const PfArgs a) {
-  constexpr int WM = BM / 2, WN = BN / 2;          // wave tile
+// NW waves per workgroup in a 2 x (NW / 2) grid: four (one or two workgroups
+// per CU) or eight (one workgroup per CU, two waves per SIMD, for 256 x 256
+// tiles: the same 128 x 64 wave tile as 256 x 128 with four waves, with a
+// third fewer bytes loaded per flop).
+template <int BM, int BN, int BK, int NST, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void k_gemm_bf16(const PfArgs a) {
+  constexpr int WGN = NW / 2;                      // waves along N
+  constexpr int WM = BM / 2, WN = BN / WGN;        // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;        // 32x32 MFMA tiles per wave
   constexpr int STAGE = (BM + BN) * BK;            // bf16 elements per LDS stage
   constexpr int CPR = BK / 8;                      // 16-byte chunks per LDS row
   constexpr int RPL = 64 / CPR;                    // rows per 1 KiB load
-  constexpr int LA = BM / (4 * RPL), LB = BN / (4 * RPL);   // loads per wave per stage
+  constexpr int LA = BM / (NW * RPL), LB = BN / (NW * RPL);   // loads per wave per stage
   constexpr int LPS = LA + LB;
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must be a multiple of 64");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(WN % 32 == 0 && LA * NW * RPL == BM && LB * NW * RPL == BN, "wave tiles and loads must divide the tile");
   static_assert(BK == 32 || BK == 64, "K slice of 32 or 64");
   static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
   // Each stage is its own LDS object; unused ones are a token size.
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(256, (gemm_occupancy<BM, BN, BK, NST>())) void k_ge
     for (int d = 0; d < LPS; ++d) dma(d, k0, klim, -1, stage);
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -533,7 +540,7 @@ __global__ __launch_bounds__(256) void k_prefill_reduce(const float *part, int S
 namespace {
 
 struct TileCfg {
-  int BM, BN, BK, NST, S;
+  int BM, BN, BK, NST, S, NW;
 };
 
 static int env_int(const char *name, int dflt) {
@@ -555,49 +562,60 @@ int count_tiles(const Recon &rq, int BM, int BN, bool tpass) {
 // Compiled main-pass tile shapes: BM x BN output, BK-wide K slices through NST
 // LDS stages; workgroups resident per CU follow from the LDS ring.
 struct Cand {
-  int BM, BN, BK, NST;
+  int BM, BN, BK, NST, NW;
 };
-static const Cand kCands[] = {{128, 128, 64, 4}, {256, 128, 32, 3}, {256, 128, 64, 3}, {256, 256, 32, 4},
-                               {256, 256, 64, 2}, {128, 256, 64, 3}, {128, 128, 64, 2}, {256, 128, 32, 3},
-                               {128, 256, 32, 3}, {128, 128, 32, 4}, {64, 64, 64, 4},   {64, 128, 64, 4},
-                               {128, 64, 64, 4}};
+static const Cand kCands[] = {{128, 128, 64, 4, 4}, {256, 128, 32, 3, 4}, {256, 128, 64, 3, 4}, {256, 256, 32, 4, 4},
+                               {256, 256, 64, 2, 4}, {256, 256, 32, 4, 8}, {256, 256, 64, 2, 8}, {128, 256, 64, 3, 4},
+                               {128, 128, 64, 2, 4}, {128, 256, 32, 3, 4}, {128, 128, 32, 4, 4}, {64, 64, 64, 4, 4},
+                               {64, 128, 64, 4, 4},  {128, 64, 64, 4, 4}};
 
-// Main-pass tile and K split, from sweeps over the Gemma-3-1B and
-// large-decoder prefill shapes on MI355X (per-tile times there: 128 x 128 with
-// four stages ~15 us at K = 1152, one workgroup per CU; 256 x 128 with three
-// 32-wide stages ~21 us per tile with two workgroups per CU overlapping each
-// other's epilogues):
-// * up to 64 tiles of 128 x 128: 64 x 64 tiles, four stages, no K split;
-// * up to 256 tiles of 128 x 128 (one round on the CUs): 128 x 128, four
-//   stages, K split only for long K (>= 4096) when the tiles cover at most half
-//   of the CUs (ranges of >= 2048);
-// * more: 256 x 128, two per CU, unless its last round would be mostly empty
-//   (under 1.5 rounds of 512), then 256 x 128 one per CU with 64-wide slices.
+// Main-pass tile and K split.  The tile comes from a cost model fitted to
+// sweeps over the Gemma-3-1B and large-decoder prefill shapes on MI355X: a
+// dispatch takes ceil(tiles / slots) rounds on the CUs, and a tile takes
+// (K / 32) x (time per 32-wide K slice) + (prologue and epilogue).  Measured
+// per-slice times (us): 256 x 256 with eight waves 0.85 (one per CU); 256 x 128
+// with 32-wide slices 0.89 when two share a CU, 0.71 alone; 256 x 128 with
+// 64-wide slices 0.52 (one per CU); 128 x 128 0.35 (one per CU).
+// * up to 64 tiles of 128 x 128: 64 x 64 tiles, four stages, no K split (they
+//   cover four times as many CUs);
+// * else the cheapest of the four by the model; 128 x 128 splits long K
+//   (>= 4096) when its tiles cover at most half of the CUs (ranges >= 2048).
+struct Est {
+  TileCfg tc;
+  int slots;
+  double step_us, step_alone_us, epi_us;
+};
+static const Est kEst[] = {{{256, 256, 32, 4, 1, 8}, kNumCU, 0.85, 0.85, 5.0},
+                           {{256, 128, 32, 3, 1, 4}, 2 * kNumCU, 0.89, 0.71, 5.0},
+                           {{256, 128, 64, 3, 1, 4}, kNumCU, 0.52, 0.52, 5.0},
+                           {{128, 128, 64, 4, 1, 4}, kNumCU, 0.35, 0.35, 3.0}};
+
 TileCfg choose(const Recon &rq) {
   const int t128 = count_tiles(rq, 128, 128, false);
-  TileCfg tc = {128, 128, 64, 4, 1};
-  if (t128 > kNumCU) {
-    const int t = count_tiles(rq, 256, 128, false);
-    const double rounds = (double)t / (2 * kNumCU);
-    if (rounds < 1.5 && rounds > 1.0)
-      tc = {256, 128, 64, 3, 1};
-    else
-      tc = {256, 128, 32, 3, 1};
-  } else if (t128 <= 64) {
-    // Few 128 x 128 tiles (short prompts through narrow projections): 64 x 64
-    // tiles cover four times as many CUs, with no K split to fold.
-    tc = {64, 64, 64, 4, 1};
-  } else if (rq.K >= 4096 && 2 * t128 <= kNumCU) {
-    const int S = kNumCU / t128, smax = (int)(rq.K / 2048);
-    tc.S = S < smax ? S : smax;
+  TileCfg tc = {128, 128, 64, 4, 1, 4};
+  if (t128 <= 64) {
+    tc = {64, 64, 64, 4, 1, 4};
+  } else {
+    double best = 1e30;
+    for (const Est &e : kEst) {
+      const int t = count_tiles(rq, e.tc.BM, e.tc.BN, false);
+      const double step = t <= kNumCU ? e.step_alone_us : e.step_us;
+      const double cost = (double)((t + e.slots - 1) / e.slots) * ((double)rq.K / 32.0 * step + e.epi_us);
+      if (cost < best) best = cost, tc = e.tc;
+    }
+    if (tc.BM == 128 && rq.K >= 4096 && 2 * t128 <= kNumCU) {
+      const int S = kNumCU / t128, smax = (int)(rq.K / 2048);
+      tc.S = S < smax ? S : smax;
+    }
   }
   // Tuning overrides (profiling sweeps): AQ_PREFILL_BM/BN/BK/NST pick a compiled
   // shape, AQ_PREFILL_S the K split.
   const int bm = env_int("AQ_PREFILL_BM", 0), bn = env_int("AQ_PREFILL_BN", 0);
   const int bk = env_int("AQ_PREFILL_BK", 0), ns = env_int("AQ_PREFILL_NST", 0);
+  const int nw = env_int("AQ_PREFILL_W", 4);
   for (const Cand &c : kCands)
-    if (c.BM == bm && c.BN == bn && (bk == 0 || c.BK == bk) && (ns == 0 || c.NST == ns)) {
-      tc.BM = c.BM, tc.BN = c.BN, tc.BK = c.BK, tc.NST = c.NST;
+    if (c.BM == bm && c.BN == bn && (bk == 0 || c.BK == bk) && (ns == 0 || c.NST == ns) && c.NW == nw) {
+      tc.BM = c.BM, tc.BN = c.BN, tc.BK = c.BK, tc.NST = c.NST, tc.NW = c.NW;
       break;
     }
   const int so = env_int("AQ_PREFILL_S", 0);
@@ -620,6 +638,7 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
   pl->BK = tc.BK;
   pl->NST = tc.NST;
   pl->S = tc.S;
+  pl->NW = tc.NW;
   // Rank-r pass: 64 x 64 tiles over t's columns.  For long K (> 2048) K is
   // split so that the workgroups cover the CUs with ranges of >= 768 values and
   // the fp32 partials are folded into the bf16 t buffer by the reduce kernel;
@@ -646,33 +665,35 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
 }
 
 template <int MODE>
-static bool launch_tile(int BM, int BN, int BK, int NST, const PfArgs &a, int grid, hipStream_t st) {
-#define AQ_TILE(bm, bn, bk, ns)                                                                       \
-  if (BM == bm && BN == bn && BK == bk && NST == ns) {                                               \
-    hipLaunchKernelGGL((k_gemm_bf16<bm, bn, bk, ns, MODE>), dim3(grid), dim3(256), 0, st, a);        \
+static bool launch_tile(int BM, int BN, int BK, int NST, int NW, const PfArgs &a, int grid, hipStream_t st) {
+#define AQ_TILE(bm, bn, bk, ns, nw)                                                                   \
+  if (BM == bm && BN == bn && BK == bk && NST == ns && NW == nw) {                                   \
+    hipLaunchKernelGGL((k_gemm_bf16<bm, bn, bk, ns, MODE, nw>), dim3(grid), dim3(64 * nw), 0, st, a); \
     return true;                                                                                      \
   }
   if constexpr (MODE == MODE_RAW) {
-    AQ_TILE(64, 64, 64, 4)
+    AQ_TILE(64, 64, 64, 4, 4)
   } else {
-    AQ_TILE(256, 256, 32, 4)
-    AQ_TILE(256, 256, 64, 2)
-    AQ_TILE(256, 128, 64, 3)
-    AQ_TILE(128, 256, 64, 3)
-    AQ_TILE(128, 128, 64, 2)
-    AQ_TILE(128, 128, 64, 4)
-    AQ_TILE(256, 128, 32, 3)
-    AQ_TILE(128, 256, 32, 3)
-    AQ_TILE(128, 128, 32, 4)
-    AQ_TILE(64, 64, 64, 4)
-    AQ_TILE(64, 128, 64, 4)
-    AQ_TILE(128, 64, 64, 4)
+    AQ_TILE(256, 256, 32, 4, 4)
+    AQ_TILE(256, 256, 64, 2, 4)
+    AQ_TILE(256, 256, 32, 4, 8)
+    AQ_TILE(256, 256, 64, 2, 8)
+    AQ_TILE(256, 128, 64, 3, 4)
+    AQ_TILE(128, 256, 64, 3, 4)
+    AQ_TILE(128, 128, 64, 2, 4)
+    AQ_TILE(128, 128, 64, 4, 4)
+    AQ_TILE(256, 128, 32, 3, 4)
+    AQ_TILE(128, 256, 32, 3, 4)
+    AQ_TILE(128, 128, 32, 4, 4)
+    AQ_TILE(64, 64, 64, 4, 4)
+    AQ_TILE(64, 128, 64, 4, 4)
+    AQ_TILE(128, 64, 64, 4, 4)
   }
 #undef AQ_TILE
   return false;
 }
 
-static hipError_t run(PfArgs &a, int BM, int BN, int BK, int NST, int mode, hipStream_t st) {
+static hipError_t run(PfArgs &a, int BM, int BN, int BK, int NST, int NW, int mode, hipStream_t st) {
   a.ntm = (a.M + BM - 1) / BM;
   int t0 = 0;
   for (int b = 0; b < a.nblk; ++b) {
@@ -686,9 +707,9 @@ static hipError_t run(PfArgs &a, int BM, int BN, int BK, int NST, int mode, hipS
   const int grid = 8 * ((units + 7) / 8);
   bool ok = false;
   switch (mode) {
-    case MODE_RECON: ok = launch_tile<MODE_RECON>(BM, BN, BK, NST, a, grid, st); break;
-    case MODE_PART: ok = launch_tile<MODE_PART>(BM, BN, BK, NST, a, grid, st); break;
-    default: ok = launch_tile<MODE_RAW>(BM, BN, BK, NST, a, grid, st); break;
+    case MODE_RECON: ok = launch_tile<MODE_RECON>(BM, BN, BK, NST, NW, a, grid, st); break;
+    case MODE_PART: ok = launch_tile<MODE_PART>(BM, BN, BK, NST, NW, a, grid, st); break;
+    default: ok = launch_tile<MODE_RAW>(BM, BN, BK, NST, NW, a, grid, st); break;
   }
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
@@ -729,7 +750,7 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
       t.ldy = pl.ldt;
       t.vec_store = 1;
     }
-    hipError_t e = run(t, pl.tBM, pl.tBN, 64, 4, MODE_RAW, st);
+    hipError_t e = run(t, pl.tBM, pl.tBN, 64, 4, 4, MODE_RAW, st);
     if (e != hipSuccess) return e;
     if (t.S > 1) {
       const long n = (long)rq.M * pl.ldt;
@@ -766,7 +787,7 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
     d.ufast = (P.r % 8 == 0) && (((uintptr_t)P.U & 15) == 0);
     if (P.col % 8) a.vec_store = 0;
   }
-  hipError_t e = run(a, pl.BM, pl.BN, pl.BK, pl.NST, a.S > 1 ? MODE_PART : MODE_RECON, st);
+  hipError_t e = run(a, pl.BM, pl.BN, pl.BK, pl.NST, pl.NW, a.S > 1 ? MODE_PART : MODE_RECON, st);
   if (e != hipSuccess || a.S == 1) return e;
   const long n = (long)rq.M * rq.Ntot;
   hipLaunchKernelGGL(k_prefill_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,

@@ -164,15 +164,17 @@ _PREFILL_MODES = [None, (256, 256, 32, 4, 1, None), (256, 256, 64, 2, 1, None), 
                   (128, 256, 64, 3, 1, 3), (128, 128, 64, 2, 1, None), (128, 128, 64, 4, 2, 5),
                   (256, 256, 32, 4, 3, 2), (256, 256, 64, 2, 3, 2), (256, 128, 64, 3, 2, None),
                   (256, 128, 32, 3, 1, None), (128, 256, 32, 3, 2, 1), (128, 128, 32, 4, 1, None),
-                  (64, 64, 64, 4, 1, None), (64, 128, 64, 4, 2, None), (128, 64, 64, 4, 1, 3)]
+                  (64, 64, 64, 4, 1, None), (64, 128, 64, 4, 2, None), (128, 64, 64, 4, 1, 3),
+                  (256, 256, 32, 4, 1, None, 8), (256, 256, 64, 2, 1, None, 8), (256, 256, 32, 4, 2, 2, 8)]
 
 
 @pytest.mark.parametrize("M", [65, 300, 513])
 @pytest.mark.parametrize("mode", _PREFILL_MODES, ids=str)
 def test_prefill_modes_qkv(M, mode, monkeypatch):
     if mode is not None:
-        bm, bn, bk, nst, S, tS = mode
-        for k, v in (("BM", bm), ("BN", bn), ("BK", bk), ("NST", nst), ("S", S)):
+        bm, bn, bk, nst, S, tS = mode[:6]
+        nw = mode[6] if len(mode) > 6 else 4
+        for k, v in (("BM", bm), ("BN", bn), ("BK", bk), ("NST", nst), ("S", S), ("W", nw)):
             monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
         if tS is not None:
             monkeypatch.setenv("AQ_TPASS_S", str(tS))
@@ -198,13 +200,14 @@ def test_rank_pass_shapes(M, K):
 
 @pytest.mark.parametrize("M", [80, 600])
 @pytest.mark.parametrize("r", [36, 64, 100, 256])
-@pytest.mark.parametrize("tile", [(256, 256, 32, 4), (256, 256, 64, 2), (256, 128, 64, 3), (128, 256, 32, 3)],
-                         ids=str)
+@pytest.mark.parametrize("tile", [(256, 256, 32, 4), (256, 256, 64, 2), (256, 128, 64, 3), (128, 256, 32, 3),
+                                  (256, 256, 32, 4, 8), (256, 256, 64, 2, 8)], ids=str)
 def test_prefill_high_rank(M, r, tile, monkeypatch):
     """Rank-r epilogues over one or several rank chunks (some riding on the tail
     of the K ring, the rest read from global memory), with U rows that are
-    16-byte aligned (r % 8 == 0) or not (r = 36, 100)."""
-    for k, v in zip(("BM", "BN", "BK", "NST"), tile):
+    16-byte aligned (r % 8 == 0) or not (r = 36, 100); four- and eight-wave
+    workgroups."""
+    for k, v in zip(("BM", "BN", "BK", "NST", "W"), tuple(tile) + ((4,) if len(tile) == 4 else ())):
         monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
     bd, x = _single(M, 512, 520, r, "bf16", variant="s0", layer=r, tag=700 + M)
     y = B.recon_linear(up(x, "bf16"), bundle_up(bd, "bf16"))
