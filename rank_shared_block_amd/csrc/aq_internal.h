@@ -74,6 +74,7 @@ struct PrefillPlan {
   int BM, BN, BK, NST, S;           // output tile, K slice, LDS stages, K splits (main pass)
   int NW;                           // waves per workgroup (main pass)
   int tBM, tBN, tS;                 // output tile and K splits of the rank-r (t) pass
+  int fuse;                         // rank-r pass inside the main-pass launch
   size_t tpart_off;                 // byte offset of the t-pass partials in the scratch
   size_t part_off;                  // byte offset of the main-pass partials in the scratch
   size_t ws_bytes;                  // total workspace bytes (reserved region + t buffer)

@@ -69,6 +69,12 @@ struct PfArgs {
   float *part;             // [S][M][ldp] fp32 partials (MODE_PART, MODE_RAW)
   const uint16_t *t;       // bf16 [M][ldt] (MODE_RECON, MODE_PART)
   int ldx, ldy, ldt, ldp, M, K, nblk, ntm, ntiles, S, kchunk, vec_store;
+  // Rank-r pass run by the first tgrid workgroups of the main-pass launch
+  // (0: none): they publish t with device-coherent stores (coherent = 1 in
+  // their arguments) and count themselves in sync[0]; the nwait main units
+  // that need t wait for the count, and the last of them zeroes sync[0..1].
+  int tgrid, nwait, coherent;
+  unsigned *sync;
   PfBlk b[kMaxBlocks];
 };
 
@@ -116,7 +122,9 @@ constexpr int gemm_occupancy() { return (BM + BN) * BK * 2 * NST <= 80 * 1024 ? 
 // tiles: the same 128 x 64 wave tile as 256 x 128 with four waves, with a
 // third fewer bytes loaded per flop).
 template <int BM, int BN, int BK, int NST, int MODE, int NW>
-__global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void k_gemm_bf16(const PfArgs a) {
+__device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a, const int unit, uint16_t *const st0,
+                                                               uint16_t *const st1, uint16_t *const st2,
+                                                               uint16_t *const st3, float *const s_lds) {
   constexpr int WGN = NW / 2;                      // waves along N
   constexpr int WM = BM / 2, WN = BN / WGN;        // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;        // 32x32 MFMA tiles per wave
@@ -130,18 +138,11 @@ __global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void 
   static_assert(WN % 32 == 0 && LA * NW * RPL == BM && LB * NW * RPL == BN, "wave tiles and loads must divide the tile");
   static_assert(BK == 32 || BK == 64, "K slice of 32 or 64");
   static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
-  // Each stage is its own LDS object; unused ones are a token size.
-  __shared__ __attribute__((aligned(1024))) uint16_t st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st2[NST > 2 ? STAGE : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t st3[NST > 3 ? STAGE : 8];
 
   // wave is read back from lane 0 so that the compiler knows it is uniform: the
   // LDS address of a direct load (M0) is per wave.
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, lhi = lane >> 5;
-  const int unit = xcd_contiguous_tile(blockIdx.x, a.ntiles * a.S);
-  if (unit < 0) return;
   const int tile = unit / a.S, p = unit - tile * a.S;
   int bi = 0;
   if (a.nblk > 1 && tile >= a.b[1].tile0) bi = 1;
@@ -324,6 +325,24 @@ __global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void 
   for (int s = 0; s < nkp - NST; s += NST) {
     AQ_GROUP(std::false_type{}, s)
   }
+  // t is read from the last group on (rank chunks riding on the ring, then the
+  // epilogue): with the rank-r pass in this launch, wait for its workgroups.
+  if (MODE != MODE_RAW && addu && a.tgrid > 0) {
+    if (tid == 0) {
+      // Bounded: the rank-r workgroups were dispatched before every main one
+      // and need no other workgroup to finish, so the count arrives; a spin
+      // past the bound goes on rather than hang.
+      for (int it = 0; it < (1 << 22); ++it) {
+        if (__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)a.tgrid) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (__hip_atomic_fetch_add(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == (unsigned)a.nwait) {
+        __hip_atomic_store(a.sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    ring_barrier();
+  }
   // Every K range holds at least one slice (K >= 1), so nkp >= NST.  The last
   // group runs unconditionally: a branch around it would put a join between
   // the last MFMAs and the epilogue's first reads of their results.
@@ -353,7 +372,6 @@ __global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void 
   uint16_t *const sprev = NST == 2 ? st0 : (NST == 3 ? st1 : st2);
   uint16_t *const ost0 = ESLOTS == NST - 1 ? slast : sprev;
   uint16_t *const ost1 = ESLOTS == NST - 1 ? slast + 32 * OP : slast;
-  __shared__ float s_lds[BN];
   const bool fp32_out = MODE == MODE_PART || (MODE == MODE_RAW && a.part);
   // fp32 rows of 4 columns as one 16-byte store where every row and block
   // start is 16-byte aligned
@@ -445,7 +463,14 @@ __global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void 
       const int mr = m0 + wm * WM + i * 32 + rl;
       if (mr >= M || nc >= nst) continue;
       uint16_t *dst = a.y + (size_t)mr * a.ldy + B.col + n0 + nc;
-      if (a.vec_store && nc + 8 <= nst) {
+      if (a.coherent) {
+        // device-coherent 4-byte stores (the reader may sit on another XCD)
+        unsigned *d4 = reinterpret_cast<unsigned *>(dst);
+        __hip_atomic_store(d4 + 0, pend[q].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(d4 + 1, pend[q].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(d4 + 2, pend[q].z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(d4 + 3, pend[q].w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (a.vec_store && nc + 8 <= nst) {
         *reinterpret_cast<uint4 *>(dst) = pend[q];
       } else {
         const uint32_t wv[4] = {pend[q].x, pend[q].y, pend[q].z, pend[q].w};
@@ -512,6 +537,50 @@ __global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void 
     stage_read();
     stage_store(TM - 1);
   }
+}
+
+// Rank-r pass tile shape run inside a main-pass launch: 64 x 64 (128 x 128
+// with eight waves) over 64-wide K slices, in as many stages as the main
+// shape has (its stages fit in the main shape's); ok is false where the main
+// shape has none.  (Tiles as tall as the main tile were tried: they take
+// nearly as long as a main tile, which then waits for t.)
+template <int BM, int BN, int BK, int NST, int NW>
+struct TPass {
+  static constexpr bool ok = (NW == 8 && BM == 256 && BN == 256 && BK == 32 && NST == 4) ||
+                             (NW == 4 && ((BM == 256 && BN == 128) || (BM == 128 && BN == 128 && BK == 64) ||
+                                          (BM == 64 && BN == 64 && BK == 64)));
+  static constexpr int tBM = NW == 8 ? 128 : 64, tBN = tBM, tBK = 64, tNST = NST;
+};
+
+// The main pass (MODE_RECON / MODE_PART) or the rank-r pass (MODE_RAW), one
+// tile per workgroup.  With tgrid > 0 (MODE_RECON only) the first tgrid
+// workgroups run the rank-r pass tiles described by tp instead.
+template <int BM, int BN, int BK, int NST, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void k_gemm_bf16(const PfArgs a,
+                                                                                           const PfArgs tp) {
+  constexpr int STAGE = (BM + BN) * BK;
+  // Each stage is its own LDS object; unused ones are a token size.
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[NST > 2 ? STAGE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[NST > 3 ? STAGE : 8];
+  __shared__ float s_lds[BN];
+  using T = TPass<BM, BN, BK, NST, NW>;
+  if constexpr (MODE == MODE_RECON && T::ok) {
+    static_assert((T::tBM + T::tBN) * T::tBK <= STAGE && T::tNST <= NST, "rank-r stages must fit");
+    if ((int)blockIdx.x < a.tgrid) {
+      const int u = xcd_contiguous_tile(blockIdx.x, tp.ntiles);
+      if (u >= 0) gemm_tile<T::tBM, T::tBN, T::tBK, T::tNST, MODE_RAW, NW>(tp, u, st0, st1, st2, st3, s_lds);
+      // every wave's coherent t stores are complete, then one arrival
+      __builtin_amdgcn_s_waitcnt(0);
+      ring_barrier();
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+  }
+  const int unit = xcd_contiguous_tile((int)blockIdx.x - a.tgrid, a.ntiles * a.S);
+  if (unit < 0) return;
+  gemm_tile<BM, BN, BK, NST, MODE, NW>(a, unit, st0, st1, st2, st3, s_lds);
 }
 
 // y = bf16(sum of the S fp32 partials, in split order); also folds the split
@@ -655,6 +724,28 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
     const int to = env_int("AQ_TPASS_S", 0);
     if (to >= 1) pl->tS = to;
   }
+  // The rank-r pass runs inside the main-pass launch (its tiles first, see
+  // k_gemm_bf16) when neither pass splits K, the main tile shape has a rank-r
+  // tile shape that fits its LDS stages (the shapes TPass lists), a main tile
+  // is at least four rank-r tiles (so that t is ready before the main tiles
+  // reach their epilogue), and the rank-r tiles fit in the slots that the main
+  // pass's last round leaves free (else they would push main tiles into
+  // another round): one launch and its ramp less.
+  const bool fusable =
+      (tc.NW == 8 && tc.BM == 256 && tc.BN == 256 && tc.BK == 32 && tc.NST == 4) ||
+      (tc.NW == 4 && ((tc.BM == 256 && tc.BN == 128) || (tc.BM == 128 && tc.BN == 128 && tc.BK == 64) ||
+                      (tc.BM == 64 && tc.BN == 64 && tc.BK == 64)));
+  pl->fuse = 0;
+  if (c > 0 && pl->tS == 1 && tc.S == 1 && fusable && env_int("AQ_PREFILL_FUSE", 1) != 0) {
+    const int tb = tc.NW == 8 ? 128 : 64;              // the shape TPass gives
+    const int slots = kNumCU * ((tc.BM + tc.BN) * tc.BK * 2 * tc.NST <= 80 * 1024 ? 2 : 1);
+    const int rem = count_tiles(rq, tc.BM, tc.BN, false) % slots;
+    const int tt = count_tiles(rq, tb, tb, true);
+    if (tc.BM * tc.BN >= 4 * tb * tb && rem > 0 && rem + tt <= slots) {
+      pl->fuse = 1;
+      pl->tBM = pl->tBN = tb;
+    }
+  }
   size_t bytes = (size_t)rq.M * c * 2;
   bytes = (bytes + 255) / 256 * 256;
   pl->tpart_off = bytes;
@@ -665,10 +756,11 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
 }
 
 template <int MODE>
-static bool launch_tile(int BM, int BN, int BK, int NST, int NW, const PfArgs &a, int grid, hipStream_t st) {
+static bool launch_tile(int BM, int BN, int BK, int NST, int NW, const PfArgs &a, const PfArgs &tp, int grid,
+                        hipStream_t st) {
 #define AQ_TILE(bm, bn, bk, ns, nw)                                                                   \
   if (BM == bm && BN == bn && BK == bk && NST == ns && NW == nw) {                                   \
-    hipLaunchKernelGGL((k_gemm_bf16<bm, bn, bk, ns, MODE, nw>), dim3(grid), dim3(64 * nw), 0, st, a); \
+    hipLaunchKernelGGL((k_gemm_bf16<bm, bn, bk, ns, MODE, nw>), dim3(grid), dim3(64 * nw), 0, st, a, tp); \
     return true;                                                                                      \
   }
   if constexpr (MODE == MODE_RAW) {
@@ -693,7 +785,7 @@ static bool launch_tile(int BM, int BN, int BK, int NST, int NW, const PfArgs &a
   return false;
 }
 
-static hipError_t run(PfArgs &a, int BM, int BN, int BK, int NST, int NW, int mode, hipStream_t st) {
+static void tile_prep(PfArgs &a, int BM, int BN) {
   a.ntm = (a.M + BM - 1) / BM;
   int t0 = 0;
   for (int b = 0; b < a.nblk; ++b) {
@@ -702,14 +794,18 @@ static hipError_t run(PfArgs &a, int BM, int BN, int BK, int NST, int NW, int mo
     t0 += a.b[b].ntn * a.ntm;
   }
   a.ntiles = t0;
-  if (t0 == 0) return hipSuccess;
-  const int units = t0 * a.S;
-  const int grid = 8 * ((units + 7) / 8);
+}
+
+static hipError_t run(PfArgs &a, const PfArgs &tp, int BM, int BN, int BK, int NST, int NW, int mode, hipStream_t st) {
+  tile_prep(a, BM, BN);
+  if (a.ntiles == 0) return hipSuccess;
+  const int units = a.ntiles * a.S;
+  const int grid = a.tgrid + 8 * ((units + 7) / 8);
   bool ok = false;
   switch (mode) {
-    case MODE_RECON: ok = launch_tile<MODE_RECON>(BM, BN, BK, NST, NW, a, grid, st); break;
-    case MODE_PART: ok = launch_tile<MODE_PART>(BM, BN, BK, NST, NW, a, grid, st); break;
-    default: ok = launch_tile<MODE_RAW>(BM, BN, BK, NST, NW, a, grid, st); break;
+    case MODE_RECON: ok = launch_tile<MODE_RECON>(BM, BN, BK, NST, NW, a, tp, grid, st); break;
+    case MODE_PART: ok = launch_tile<MODE_PART>(BM, BN, BK, NST, NW, a, tp, grid, st); break;
+    default: ok = launch_tile<MODE_RAW>(BM, BN, BK, NST, NW, a, tp, grid, st); break;
   }
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
@@ -726,8 +822,8 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
 
   // pass 1: fp32 partials of t = x Vt^T for every block with r > 0 (columns
   // padded to 16 with zeros), then folded into the bf16 t buffer.
+  PfArgs t = a;
   if (pl.ldt > 0) {
-    PfArgs t = a;
     t.S = pl.tS;
     int tkc = (int)((rq.K + pl.tS - 1) / pl.tS);
     t.kchunk = (tkc + 63) / 64 * 64;
@@ -750,7 +846,12 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
       t.ldy = pl.ldt;
       t.vec_store = 1;
     }
-    hipError_t e = run(t, pl.tBM, pl.tBN, 64, 4, 4, MODE_RAW, st);
+    if (pl.fuse) {
+      // run by the first workgroups of the main-pass launch (below)
+      t.coherent = 1;
+      tile_prep(t, pl.tBM, pl.tBN);
+    }
+    hipError_t e = pl.fuse ? hipSuccess : run(t, t, pl.tBM, pl.tBN, 64, 4, 4, MODE_RAW, st);
     if (e != hipSuccess) return e;
     if (t.S > 1) {
       const long n = (long)rq.M * pl.ldt;
@@ -787,7 +888,16 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
     d.ufast = (P.r % 8 == 0) && (((uintptr_t)P.U & 15) == 0);
     if (P.col % 8) a.vec_store = 0;
   }
-  hipError_t e = run(a, pl.BM, pl.BN, pl.BK, pl.NST, pl.NW, a.S > 1 ? MODE_PART : MODE_RECON, st);
+  if (pl.fuse && t.ntiles > 0) {
+    tile_prep(a, pl.BM, pl.BN);
+    a.tgrid = 8 * ((t.ntiles + 7) / 8);
+    a.sync = (unsigned *)ws;
+    a.nwait = 0;
+    for (int b = 0; b < rq.nblk; ++b)
+      if (a.b[b].r > 0) a.nwait += a.b[b].ntn * a.ntm;
+    if (a.nwait == 0) a.tgrid = 0;
+  }
+  hipError_t e = run(a, t, pl.BM, pl.BN, pl.BK, pl.NST, pl.NW, a.S > 1 ? MODE_PART : MODE_RECON, st);
   if (e != hipSuccess || a.S == 1) return e;
   const long n = (long)rq.M * rq.Ntot;
   hipLaunchKernelGGL(k_prefill_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
