@@ -708,35 +708,24 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
   pl->NST = tc.NST;
   pl->S = tc.S;
   pl->NW = tc.NW;
-  // Rank-r pass: 64 x 64 tiles over t's columns.  For long K (> 2048) K is
-  // split so that the workgroups cover the CUs with ranges of >= 768 values and
-  // the fp32 partials are folded into the bf16 t buffer by the reduce kernel;
-  // for shorter K the fold costs more than the split saves (sweeps over the
-  // Gemma-3-1B prefill shapes on MI355X).
   pl->tBM = 64;
   pl->tBN = 64;
   pl->tS = 1;
-  if (c > 0 && rq.K > 2048) {
-    const int tiles = count_tiles(rq, 64, 64, true);
-    int S = (kNumCU + tiles - 1) / tiles;
-    const int smax = rq.K / 768 > 1 ? (int)(rq.K / 768) : 1;
-    pl->tS = S < smax ? S : smax;
-    const int to = env_int("AQ_TPASS_S", 0);
-    if (to >= 1) pl->tS = to;
-  }
   // The rank-r pass runs inside the main-pass launch (its tiles first, see
-  // k_gemm_bf16) when neither pass splits K, the main tile shape has a rank-r
-  // tile shape that fits its LDS stages (the shapes TPass lists), a main tile
-  // is at least four rank-r tiles (so that t is ready before the main tiles
-  // reach their epilogue), and the rank-r tiles fit in the slots that the main
-  // pass's last round leaves free (else they would push main tiles into
-  // another round): one launch and its ramp less.
+  // k_gemm_bf16) when the main pass has no K split, its tile shape has a
+  // rank-r tile shape that fits its LDS stages (the shapes TPass lists), a
+  // main tile is at least four rank-r tiles (so that t is ready before the
+  // main tiles reach their epilogue, also with the rank-r pass's K unsplit),
+  // and the rank-r tiles fit in the slots that the main pass's last round
+  // leaves free (else they would push main tiles into another round): one
+  // launch, its ramp and the fold of a K split less.
   const bool fusable =
       (tc.NW == 8 && tc.BM == 256 && tc.BN == 256 && tc.BK == 32 && tc.NST == 4) ||
       (tc.NW == 4 && ((tc.BM == 256 && tc.BN == 128) || (tc.BM == 128 && tc.BN == 128 && tc.BK == 64) ||
                       (tc.BM == 64 && tc.BN == 64 && tc.BK == 64)));
+  const int to = env_int("AQ_TPASS_S", 0);
   pl->fuse = 0;
-  if (c > 0 && pl->tS == 1 && tc.S == 1 && fusable && env_int("AQ_PREFILL_FUSE", 1) != 0) {
+  if (c > 0 && tc.S == 1 && fusable && to <= 1 && env_int("AQ_PREFILL_FUSE", 1) != 0) {
     const int tb = tc.NW == 8 ? 128 : 64;              // the shape TPass gives
     const int slots = kNumCU * ((tc.BM + tc.BN) * tc.BK * 2 * tc.NST <= 80 * 1024 ? 2 : 1);
     const int rem = count_tiles(rq, tc.BM, tc.BN, false) % slots;
@@ -746,6 +735,18 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
       pl->tBM = pl->tBN = tb;
     }
   }
+  // Else a rank-r pass of its own: 64 x 64 tiles over t's columns.  For long K
+  // (> 2048) K is split so that the workgroups cover the CUs with ranges of
+  // >= 768 values and the fp32 partials are folded into the bf16 t buffer by
+  // the reduce kernel; for shorter K the fold costs more than the split saves
+  // (sweeps over the Gemma-3-1B prefill shapes on MI355X).
+  if (!pl->fuse && c > 0 && rq.K > 2048) {
+    const int tiles = count_tiles(rq, 64, 64, true);
+    int S = (kNumCU + tiles - 1) / tiles;
+    const int smax = rq.K / 768 > 1 ? (int)(rq.K / 768) : 1;
+    pl->tS = S < smax ? S : smax;
+  }
+  if (to >= 1) pl->tS = to;
   size_t bytes = (size_t)rq.M * c * 2;
   bytes = (bytes + 255) / 256 * 256;
   pl->tpart_off = bytes;

@@ -214,6 +214,29 @@ def test_prefill_high_rank(M, r, tile, monkeypatch):
     assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"r={r} M={M}")
 
 
+@pytest.mark.parametrize("M", [300, 700])
+@pytest.mark.parametrize("K", [1048, 3000])
+@pytest.mark.parametrize("tile", [(128, 128, 64, 4, 4), (256, 128, 32, 3, 4), (256, 256, 32, 4, 8)], ids=str)
+def test_prefill_rank_pass_in_main_launch(M, K, tile, monkeypatch):
+    """The rank-r pass run by the first workgroups of the main-pass launch
+    (these shapes leave free slots in the last round), with K short and long
+    (unsplit), U rows 16-byte aligned (r = 16) and not (r = 36, read per
+    round from global memory), a block without rank; the arrival counters are
+    back at zero after every call."""
+    for k, v in zip(("BM", "BN", "BK", "NST", "W"), tile):
+        monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
+    shapes = [(300, 16), (200, 36), (72, 0)]
+    bds = [I.bundle("test", 6, f, K, n, r, "bf16", variant="normal") for f, (n, r) in zip(("q", "k", "v"), shapes)]
+    x = I.activations("test", 950 + M + K, M, K, "bf16")
+    ref = oracle.recon_fused(x, [bundle_np(b) for b in bds])
+    for rep in range(2):
+        y = B.recon_qkv(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+        assert_parity(down(y), ref, "bf16", f"M={M} K={K} tile={tile} rep={rep}")
+        torch.cuda.synchronize()
+        counters = B.default_workspace()._buf[torch.device(dev()).index][:8].cpu()
+        assert int(counters.sum()) == 0, counters
+
+
 @pytest.mark.parametrize("M", [1, 16, 33, 130])
 def test_fused_gateup_small(M):
     K = 384
