@@ -23,7 +23,10 @@
 // boundary: the quotient of an 8-bit by a <= 26-bit significand is either exactly
 // a midpoint or far from every midpoint relative to fp64's precision), and the
 // element codes come from comparing |w| with the seven E2M1 midpoints times D,
-// products that are exact in fp64.  Equality with a midpoint selects the even code.
+// exactly: per block, each product is rounded to fp32 and its rounding error
+// (an fma) decides whether the fp32 threshold is the product or the next float
+// above it (products exact in fp64 where D is too small for that).  Equality
+// with a midpoint selects the even code.
 
 #include "aq_internal.h"
 #include "device_common.h"
@@ -118,10 +121,38 @@ __global__ __launch_bounds__(256) void k_fp4_pack(const uint16_t *w, int N, int 
     const uint32_t sf = e4m3_rne_sat(ab / (6.0 * (double)g));
     const float D = (float)((double)g * e4m3_value(sf));
     uint32_t lo = 0, hi = 0;
-    if (D > 0.f) {
+    if (D >= 0x1p-90f) {
       // Code = number of E2M1 midpoints m_i D below |w| (ties to the even code:
       // strictly above m_0, m_2, m_4, m_6; at or above m_1, m_3, m_5), found by a
-      // three-step binary search over the monotone midpoints.
+      // three-step binary search over the monotone midpoints, in fp32: with
+      // p = RN(m_i D) and its exact residual e = m_i D - p (an fma; no underflow
+      // for D >= 2^-90), a float x is >= m_i D iff x >= p (e <= 0) or x >= the
+      // next float above p (e > 0), and > m_i D iff x >= p (e < 0) or x >= the
+      // next float above p (e >= 0).  So every test is one exact fp32 x >= T_i.
+      float T[7];
+      const float mid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+#pragma unroll
+      for (int i = 0; i < 7; ++i) {
+        const float pr = mid[i] * D, e = __builtin_fmaf(mid[i], D, -pr);
+        const bool up = (i & 1) ? e > 0.f : e >= 0.f;
+        T[i] = up ? __uint_as_float(__float_as_uint(pr) + 1u) : pr;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t bits = (q[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+        const float x = __uint_as_float((bits & 0x7FFFu) << 16);
+        const bool b4 = x >= T[3];
+        const bool b2 = x >= (b4 ? T[5] : T[1]);
+        const float tl = b4 ? (b2 ? T[6] : T[4]) : (b2 ? T[2] : T[0]);
+        uint32_t c = (b4 ? 4u : 0u) + (b2 ? 2u : 0u) + (x >= tl ? 1u : 0u);
+        if (c != 0 && (bits & 0x8000u)) c |= 8u;
+        if (i < 8)
+          lo |= c << (4 * i);
+        else
+          hi |= c << (4 * (i - 8));
+      }
+    } else if (D > 0.f) {
+      // Tiny D: the same search on thresholds exact in fp64.
       const double d = (double)D;
       const double t0 = 0.25 * d, t1 = 0.75 * d, t2 = 1.25 * d, t3 = 1.75 * d, t4 = 2.5 * d,
                    t5 = 3.5 * d, t6 = 5.0 * d;

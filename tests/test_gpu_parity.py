@@ -417,6 +417,31 @@ def test_fp4_edge_blocks():
     assert float(g.cpu()[0]) == 1.0 and not p.any() and not s.any()
 
 
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_fp4_near_midpoints(seed):
+    """Values at and next to the E2M1 decision points m_i * D of their block,
+    with D of full fp32 precision (g = A / 2688 for an A of many bits), so that
+    m_i * D is not a float and the float-side tie decisions are exercised."""
+    rng = np.random.default_rng(100 + seed)
+    N, K = 48, 256
+    A = float(torch.tensor(97.3 + seed, dtype=torch.bfloat16))
+    g = oracle.fp4.global_scale(A)
+    W = np.zeros((N, K))
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for n in range(N):
+        for b in range(K // 16):
+            bmax = float(torch.tensor(rng.uniform(0.05, A), dtype=torch.bfloat16))
+            sf = oracle.fp4.e4m3fn_encode_rne_sat(np.array([bmax / (6.0 * g)]))
+            D = float(np.float32(g * oracle.fp4.e4m3fn_decode(sf)[0]))
+            v = mids[rng.integers(0, 7, 15)] * D * (1.0 + rng.choice([-1, 0, 1], 15) * 2.0 ** -9)
+            v = np.minimum(v, bmax)
+            blk = np.concatenate([[bmax], v * rng.choice([-1.0, 1.0], 15)])
+            W[n, 16 * b:16 * b + 16] = rng.permutation(blk)
+    W[0, 0] = A
+    w = torch.from_numpy(W).to(torch.bfloat16).to(dev())
+    _fp4_check(w)
+
+
 @pytest.mark.parametrize("fam", ["k", "down"])
 def test_fp4_gemma_full(fam):
     K, N = I.GEMMA_1B[fam]
