@@ -547,7 +547,7 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
 template <int BM, int BN, int BK, int NST, int NW>
 struct TPass {
   static constexpr bool ok = (NW == 8 && BM == 256 && BN == 256 && BK == 32 && NST == 4) ||
-                             (NW == 4 && ((BM == 256 && BN == 128) || (BM == 128 && BN == 128 && BK == 64) ||
+                             (NW == 4 && ((BM == 256 && BN == 128) || (BM == 128 && BN == 128 && NST == 4) ||
                                           (BM == 64 && BN == 64 && BK == 64)));
   static constexpr int tBM = NW == 8 ? 128 : 64, tBN = tBM, tBK = 64, tNST = NST;
 };
@@ -645,8 +645,11 @@ static const Cand kCands[] = {{128, 128, 64, 4, 4}, {256, 128, 32, 3, 4}, {256, 
 // per-slice times (us): 256 x 256 with eight waves 0.85 (one per CU); 256 x 128
 // with 32-wide slices 0.89 when two share a CU, 0.71 alone; 256 x 128 with
 // 64-wide slices 0.52 (one per CU); 128 x 128 0.35 (one per CU).
-// * up to 64 tiles of 128 x 128: 64 x 64 tiles, four stages, no K split (they
+// * up to 16 tiles of 128 x 128: 64 x 64 tiles, four stages, no K split (they
 //   cover four times as many CUs);
+// * K <= 2048 and at most one round of 128 x 128 tiles (the Gemma-3-1B QKV
+//   and o projections): 128 x 128 with 32-wide slices, two workgroups per CU,
+//   so that the rank-r pass tiles fit beside them in the same launch;
 // * else the cheapest of the four by the model; 128 x 128 splits long K
 //   (>= 4096) when its tiles cover at most half of the CUs (ranges >= 2048).
 struct Est {
@@ -662,8 +665,10 @@ static const Est kEst[] = {{{256, 256, 32, 4, 1, 8}, kNumCU, 0.85, 0.85, 5.0},
 TileCfg choose(const Recon &rq) {
   const int t128 = count_tiles(rq, 128, 128, false);
   TileCfg tc = {128, 128, 64, 4, 1, 4};
-  if (t128 <= 64) {
+  if (t128 <= 16) {
     tc = {64, 64, 64, 4, 1, 4};
+  } else if (rq.K <= 2048 && t128 <= kNumCU) {
+    tc = {128, 128, 32, 4, 1, 4};
   } else {
     double best = 1e30;
     for (const Est &e : kEst) {
@@ -721,7 +726,7 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
   // launch, its ramp and the fold of a K split less.
   const bool fusable =
       (tc.NW == 8 && tc.BM == 256 && tc.BN == 256 && tc.BK == 32 && tc.NST == 4) ||
-      (tc.NW == 4 && ((tc.BM == 256 && tc.BN == 128) || (tc.BM == 128 && tc.BN == 128 && tc.BK == 64) ||
+      (tc.NW == 4 && ((tc.BM == 256 && tc.BN == 128) || (tc.BM == 128 && tc.BN == 128 && tc.NST == 4) ||
                       (tc.BM == 64 && tc.BN == 64 && tc.BK == 64)));
   const int to = env_int("AQ_TPASS_S", 0);
   pl->fuse = 0;
