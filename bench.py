@@ -317,7 +317,9 @@ def summarize_profiles(args):
             out.append(f"| `{name[:80]}` | {wg} | {len(d)} | {sum(d)/len(d):.3f} | {d[len(d)//2]:.3f} | {sum(d):.1f} |")
         if args.calls:
             # A prefill call is its kernels in launch order up to the main GEMM
-            # (MODE 0), or up to the fold that follows a K-split main GEMM (MODE 1).
+            # (MODE 0, which may also run the rank-r pass in its first
+            # workgroups), or up to the fold that follows a K-split main GEMM
+            # (MODE 1).
             seq = []
             for r in sorted(tr, key=lambda r: int(r["Start_Timestamp"])):
                 if "aq::" not in r["Kernel_Name"]:
@@ -325,10 +327,12 @@ def summarize_profiles(args):
                 name = r["Kernel_Name"].split("(")[0].replace("void aq::", "").replace("aq::", "")
                 wg = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1) // int(r["Workgroup_Size_X"])
                 seq.append((name, wg, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+            def mode(n):             # k_gemm_bf16<BM, BN, BK, NST, MODE, NW>
+                return int(n[n.index("<") + 1:-1].split(", ")[4]) if n.startswith("k_gemm_bf16<") else -1
             calls, cur = collections.defaultdict(list), []
             for k in seq:
                 cur.append(k)
-                if k[0].endswith(", 0>") or (k[0] == "k_prefill_reduce" and any(c[0].endswith(", 1>") for c in cur)):
+                if mode(k[0]) == 0 or (k[0] == "k_prefill_reduce" and any(mode(c[0]) == 1 for c in cur)):
                     calls[tuple((c[0], c[1]) for c in cur)].append([c[2] for c in cur])
                     cur = []
             out.append("")
