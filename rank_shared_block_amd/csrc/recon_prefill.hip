@@ -74,6 +74,12 @@ struct PfArgs {
   // their arguments) and count themselves in sync[0]; the nwait main units
   // that need t wait for the count, and the last of them zeroes sync[0..1].
   int tgrid, nwait, coherent;
+  // tsplit: t is kept per K range (t_p = x_p Vt_p^T, bf16, at t + p * tstride)
+  // and every K-split unit p adds t_p U^T to its partial (the rank term is
+  // linear in K, so the fold of the partials sums it); the rank-r tiles write
+  // t_p the same way (y + p * tstride).
+  int tsplit;
+  long tstride;
   unsigned *sync;
   PfBlk b[kMaxBlocks];
 };
@@ -189,10 +195,11 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   // their latency hides under the last steps.  Ranks past r16 (t) or r (U) and
   // rows past M or N read as zero; U takes this path only with 16-byte aligned
   // rows (ufast).
-  const bool addu = MODE != MODE_RAW && (MODE == MODE_RECON || p == 0) && B.r > 0;
+  const bool addu = MODE != MODE_RAW && (MODE == MODE_RECON || p == 0 || a.tsplit) && B.r > 0;
+  const uint16_t *const tbase = a.t + (a.tsplit ? (size_t)p * a.tstride : 0);
   const int r16 = (B.r + 15) & ~15;
   const __amdgpu_buffer_rsrc_t rt =
-      make_rsrc(a.t + (size_t)m0 * a.ldt, addu ? (uint32_t)(mrows * a.ldt * 2) : 0u);
+      make_rsrc(tbase + (size_t)m0 * a.ldt, addu ? (uint32_t)(mrows * a.ldt * 2) : 0u);
   const __amdgpu_buffer_rsrc_t ru =
       make_rsrc(B.U + (size_t)n0 * B.r, addu && nrows > 0 && B.ufast ? (uint32_t)(nrows * B.r * 2) : 0u);
   auto eoff_a = [&](int d, int c) __attribute__((always_inline)) {
@@ -430,7 +437,7 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   };
   auto tfrag_glb = [&](int i, int col) __attribute__((always_inline)) {
     const int m = m0 + wm * WM + i * 32 + l32;
-    return m < M && col < r16 ? as_bf16x8(ld16(a.t + (size_t)m * a.ldt + B.tcol + col)) : zero_bf16x8();
+    return m < M && col < r16 ? as_bf16x8(ld16(tbase + (size_t)m * a.ldt + B.tcol + col)) : zero_bf16x8();
   };
   auto ufrag_glb = [&](int j, int col) __attribute__((always_inline)) {
     const int n = n0 + wn * WN + j * 32 + l32;
@@ -462,7 +469,7 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
       const int c = lane + 64 * q, rl = c / (WN / 8), nc = wn * WN + (c - rl * (WN / 8)) * 8;
       const int mr = m0 + wm * WM + i * 32 + rl;
       if (mr >= M || nc >= nst) continue;
-      uint16_t *dst = a.y + (size_t)mr * a.ldy + B.col + n0 + nc;
+      uint16_t *dst = a.y + (MODE == MODE_RAW && a.tsplit ? (size_t)p * a.tstride : 0) + (size_t)mr * a.ldy + B.col + n0 + nc;
       if (a.coherent) {
         // device-coherent 4-byte stores (the reader may sit on another XCD)
         unsigned *d4 = reinterpret_cast<unsigned *>(dst);
@@ -553,8 +560,9 @@ struct TPass {
 };
 
 // The main pass (MODE_RECON / MODE_PART) or the rank-r pass (MODE_RAW), one
-// tile per workgroup.  With tgrid > 0 (MODE_RECON only) the first tgrid
-// workgroups run the rank-r pass tiles described by tp instead.
+// tile (and K range) per workgroup.  With tgrid > 0 the first tgrid workgroups
+// run the rank-r pass tiles described by tp instead (over the same K ranges as
+// the main pass under a K split).
 template <int BM, int BN, int BK, int NST, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void k_gemm_bf16(const PfArgs a,
                                                                                            const PfArgs tp) {
@@ -566,10 +574,10 @@ __global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void 
   __shared__ __attribute__((aligned(1024))) uint16_t st3[NST > 3 ? STAGE : 8];
   __shared__ float s_lds[BN];
   using T = TPass<BM, BN, BK, NST, NW>;
-  if constexpr (MODE == MODE_RECON && T::ok) {
+  if constexpr (MODE != MODE_RAW && T::ok) {
     static_assert((T::tBM + T::tBN) * T::tBK <= STAGE && T::tNST <= NST, "rank-r stages must fit");
     if ((int)blockIdx.x < a.tgrid) {
-      const int u = xcd_contiguous_tile(blockIdx.x, tp.ntiles);
+      const int u = xcd_contiguous_tile(blockIdx.x, tp.ntiles * tp.S);
       if (u >= 0) gemm_tile<T::tBM, T::tBN, T::tBK, T::tNST, MODE_RAW, NW>(tp, u, st0, st1, st2, st3, s_lds);
       // every wave's coherent t stores are complete, then one arrival
       __builtin_amdgcn_s_waitcnt(0);
@@ -728,13 +736,15 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
       (tc.NW == 8 && tc.BM == 256 && tc.BN == 256 && tc.BK == 32 && tc.NST == 4) ||
       (tc.NW == 4 && ((tc.BM == 256 && tc.BN == 128) || (tc.BM == 128 && tc.BN == 128 && tc.NST == 4) ||
                       (tc.BM == 64 && tc.BN == 64 && tc.BK == 64)));
+  // Under a main-pass K split the rank-r tiles run over the same K ranges and
+  // keep one t per range (each main unit adds its own range's rank term).
   const int to = env_int("AQ_TPASS_S", 0);
   pl->fuse = 0;
-  if (c > 0 && tc.S == 1 && fusable && to <= 1 && env_int("AQ_PREFILL_FUSE", 1) != 0) {
+  if (c > 0 && fusable && to <= 1 && env_int("AQ_PREFILL_FUSE", 1) != 0) {
     const int tb = tc.NW == 8 ? 128 : 64;              // the shape TPass gives
     const int slots = kNumCU * ((tc.BM + tc.BN) * tc.BK * 2 * tc.NST <= 80 * 1024 ? 2 : 1);
-    const int rem = count_tiles(rq, tc.BM, tc.BN, false) % slots;
-    const int tt = count_tiles(rq, tb, tb, true);
+    const int rem = count_tiles(rq, tc.BM, tc.BN, false) * tc.S % slots;
+    const int tt = count_tiles(rq, tb, tb, true) * tc.S;
     if (tc.BM * tc.BN >= 4 * tb * tb && rem > 0 && rem + tt <= slots) {
       pl->fuse = 1;
       pl->tBM = pl->tBN = tb;
@@ -752,7 +762,7 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
     pl->tS = S < smax ? S : smax;
   }
   if (to >= 1) pl->tS = to;
-  size_t bytes = (size_t)rq.M * c * 2;
+  size_t bytes = (size_t)rq.M * c * 2 * (pl->fuse ? pl->S : 1);
   bytes = (bytes + 255) / 256 * 256;
   pl->tpart_off = bytes;
   if (pl->tS > 1) bytes += ((size_t)pl->tS * rq.M * c * 4 + 255) / 256 * 256;
@@ -853,13 +863,23 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
       t.vec_store = 1;
     }
     if (pl.fuse) {
-      // run by the first workgroups of the main-pass launch (below)
+      // run by the first workgroups of the main-pass launch (below), over the
+      // main pass's K ranges, one bf16 t per range
+      const int kc = (int)((rq.K + pl.S - 1) / pl.S);
+      t.kchunk = (kc + pl.BK - 1) / pl.BK * pl.BK;
+      t.S = (int)((rq.K + t.kchunk - 1) / t.kchunk);
+      t.part = nullptr;
+      t.y = tbuf;
+      t.ldy = pl.ldt;
+      t.vec_store = 1;
+      t.tsplit = t.S > 1;
+      t.tstride = (long)rq.M * pl.ldt;
       t.coherent = 1;
       tile_prep(t, pl.tBM, pl.tBN);
     }
     hipError_t e = pl.fuse ? hipSuccess : run(t, t, pl.tBM, pl.tBN, 64, 4, 4, MODE_RAW, st);
     if (e != hipSuccess) return e;
-    if (t.S > 1) {
+    if (!pl.fuse && t.S > 1) {
       const long n = (long)rq.M * pl.ldt;
       hipLaunchKernelGGL(k_prefill_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                          (const float *)t.part, t.S, (int)rq.M, pl.ldt, pl.ldt, tbuf, pl.ldt);
@@ -896,11 +916,13 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
   }
   if (pl.fuse && t.ntiles > 0) {
     tile_prep(a, pl.BM, pl.BN);
-    a.tgrid = 8 * ((t.ntiles + 7) / 8);
+    a.tgrid = 8 * ((t.ntiles * t.S + 7) / 8);
     a.sync = (unsigned *)ws;
+    a.tsplit = a.S > 1;
+    a.tstride = (long)rq.M * pl.ldt;
     a.nwait = 0;
     for (int b = 0; b < rq.nblk; ++b)
-      if (a.b[b].r > 0) a.nwait += a.b[b].ntn * a.ntm;
+      if (a.b[b].r > 0) a.nwait += a.b[b].ntn * a.ntm * (a.tsplit ? a.S : 1);
     if (a.nwait == 0) a.tgrid = 0;
   }
   hipError_t e = run(a, t, pl.BM, pl.BN, pl.BK, pl.NST, pl.NW, a.S > 1 ? MODE_PART : MODE_RECON, st);

@@ -216,14 +216,16 @@ def test_prefill_high_rank(M, r, tile, monkeypatch):
 
 @pytest.mark.parametrize("M", [300, 700])
 @pytest.mark.parametrize("K", [1048, 3000])
+@pytest.mark.parametrize("S", [1, 3])
 @pytest.mark.parametrize("tile", [(128, 128, 64, 4, 4), (256, 128, 32, 3, 4), (256, 256, 32, 4, 8)], ids=str)
-def test_prefill_rank_pass_in_main_launch(M, K, tile, monkeypatch):
+def test_prefill_rank_pass_in_main_launch(M, K, S, tile, monkeypatch):
     """The rank-r pass run by the first workgroups of the main-pass launch
     (these shapes leave free slots in the last round), with K short and long
-    (unsplit), U rows 16-byte aligned (r = 16) and not (r = 36, read per
-    round from global memory), a block without rank; the arrival counters are
-    back at zero after every call."""
-    for k, v in zip(("BM", "BN", "BK", "NST", "W"), tile):
+    (unsplit), or the main pass K-split in three with one t per K range; U rows
+    16-byte aligned (r = 16) and not (r = 36, read per round from global
+    memory), a block without rank; the arrival counters are back at zero after
+    every call."""
+    for k, v in zip(("BM", "BN", "BK", "NST", "W", "S"), tuple(tile) + (S,)):
         monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
     shapes = [(300, 16), (200, 36), (72, 0)]
     bds = [I.bundle("test", 6, f, K, n, r, "bf16", variant="normal") for f, (n, r) in zip(("q", "k", "v"), shapes)]
