@@ -292,6 +292,54 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
       }
     }
   };
+  // The same step with the next slice's barrier inside it (NST >= 3): before
+  // the last k-step, wait for this wave's loads of the next slice and for its
+  // own reads of `cur`, pass the barrier (everyone's loads of the next slice
+  // have landed and everyone is done reading `cur`), then read the next
+  // slice's first fragments (`nxt`, into f0) while the last k-step's MFMAs
+  // run.  So neither the barrier nor the first fragment reads after it leave
+  // the MFMA pipes idle.  The loads issued in this step go into the stage of
+  // slice s - 1, which everyone finished reading before the previous step's
+  // barrier.
+  constexpr int PA = ((KK - 1) * TM * LPS) / SLOTS;  // loads issued before the barrier
+  // Used with eight waves (two per SIMD of one workgroup, whose barrier waits
+  // took ~20% of the loop); four-wave shapes measured no better with it.
+  constexpr bool kSplitBar = NST >= 3 && NW == 8;
+  auto step2 = [&](auto tail, int nslice, uint16_t *next, const uint16_t *cur, const uint16_t *nxt,
+                   bf16x8(&f0a)[TM], bf16x8(&f0b)[TN]) __attribute__((always_inline)) {
+    const int k0 = kbeg + nslice * BK, klim = nslice < nk ? kend : -1;
+    const int ech = decltype(tail)::value && nslice >= nkp && nslice - nkp < nech ? nslice - nkp : -1;
+    // The carried fragments were requested a k-step ago: wait for them before
+    // requesting more, so that the first MFMAs do not wait for the new reads
+    // (across the loop's back edge the compiler would wait for all of them).
+    // As a builtin, so that the compiler's own wait counting sees it.
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0) only
+    bf16x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = f0a[i];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = f0b[j];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      if (kk == KK - 1) {
+        wait_vmcnt<(NST - 3) * LPS + PA>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        ring_barrier();
+        frags(nxt, 0, f0a, f0b);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j], 0, 0, 0);
+        const int t = kk * TM + i;
+#pragma unroll
+        for (int d = t * LPS / SLOTS; d < (t + 1) * LPS / SLOTS; ++d) dma(d, k0, klim, ech, next);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
 
   // Slice s lives in stage s % NST.  At step s: wait until this wave's loads of
   // slice s have landed (the NST - 2 younger slices may still be in flight),
@@ -305,19 +353,29 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   wait_vmcnt<(NST - 2) * LPS>();             \
   ring_barrier();                            \
   step(tail, (slice) + NST - 1, next, cur);
+#define AQ_STEP2(tail, slice, next, cur, nxt) step2(tail, (slice) + NST - 1, next, cur, nxt, f0a, f0b);
 #define AQ_GROUP(tail, s)                       \
   if constexpr (NST == 2) {                     \
     AQ_STEP(tail, s, st1, st0)                  \
     AQ_STEP(tail, s + 1, st0, st1)              \
-  } else if constexpr (NST == 3) {              \
+  } else if constexpr (NST == 3 && !kSplitBar) { \
     AQ_STEP(tail, s, st2, st0)                  \
     AQ_STEP(tail, s + 1, st0, st1)              \
     AQ_STEP(tail, s + 2, st1, st2)              \
-  } else {                                      \
+  } else if constexpr (NST == 3) {              \
+    AQ_STEP2(tail, s, st2, st0, st1)            \
+    AQ_STEP2(tail, s + 1, st0, st1, st2)        \
+    AQ_STEP2(tail, s + 2, st1, st2, st0)        \
+  } else if constexpr (!kSplitBar) {            \
     AQ_STEP(tail, s, st3, st0)                  \
     AQ_STEP(tail, s + 1, st0, st1)              \
     AQ_STEP(tail, s + 2, st1, st2)              \
     AQ_STEP(tail, s + 3, st2, st3)              \
+  } else {                                      \
+    AQ_STEP2(tail, s, st3, st0, st1)            \
+    AQ_STEP2(tail, s + 1, st0, st1, st2)        \
+    AQ_STEP2(tail, s + 2, st1, st2, st3)        \
+    AQ_STEP2(tail, s + 3, st2, st3, st0)        \
   }
   // The epilogue's s values (BN <= 256: one per thread) are requested now and
   // kept raw in a register, so that their latency hides under the main loop;
@@ -329,6 +387,12 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   issue(0, st0);                         // slices 0 .. NST - 2 ahead of the loop
   if constexpr (NST > 2) issue(1, st1);
   if constexpr (NST > 3) issue(2, st2);
+  bf16x8 f0a[TM], f0b[TN];               // first fragments of the next slice (split barrier)
+  if constexpr (kSplitBar) {
+    wait_vmcnt<(NST - 2) * LPS>();
+    ring_barrier();
+    frags(st0, 0, f0a, f0b);
+  }
   for (int s = 0; s < nkp - NST; s += NST) {
     AQ_GROUP(std::false_type{}, s)
   }
@@ -355,6 +419,7 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   // the last MFMAs and the epilogue's first reads of their results.
   AQ_GROUP(std::true_type{}, nkp - NST)
 #undef AQ_GROUP
+#undef AQ_STEP2
 #undef AQ_STEP
   __builtin_amdgcn_s_waitcnt(0);         // drain the (out-of-range) tail loads
 
