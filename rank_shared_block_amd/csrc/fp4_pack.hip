@@ -14,8 +14,8 @@
 // Two passes over HBM:
 //   1. amax: max |w| per workgroup as an integer max over the 15 magnitude bits
 //      of the bf16 patterns (exact and order-independent); partials to ws.
-//   2. pack: every workgroup folds the partials to A (a few KB from L2), derives
-//      g, and packs one 16-value block per thread (2 x 16-byte loads, one 8-byte
+//   2. pack: every wave folds the partials to A (1 KB from L2), derives g,
+//      and packs one 16-value block per thread (2 x 16-byte loads, one 8-byte
 //      store of codes, one scale byte).
 //
 // Exactness without a per-element division: the block-scale quotient is formed
@@ -90,16 +90,20 @@ __global__ __launch_bounds__(256) void k_fp4_pack(const uint16_t *w, int N, int 
                                                   const unsigned *partial, int npartial,
                                                   uint8_t *packed, uint8_t *scales,
                                                   float *gscale) {
-  __shared__ unsigned red[256];
-  unsigned m = 0;
-  for (int i = threadIdx.x; i < npartial; i += 256) m = max(m, partial[i]);
-  red[threadIdx.x] = m;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + s]);
-    __syncthreads();
+  // Every wave folds the (at most 256) partial maxima itself: four loads per
+  // lane requested together, then a butterfly over the wave; no LDS and no
+  // workgroup barrier before the packing starts.
+  const int lane = threadIdx.x & 63;
+  unsigned pm[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = lane + 64 * q;
+    pm[q] = partial[i < npartial ? i : 0];
   }
-  const float A = bf2f((uint16_t)red[0]);
+  unsigned m = max(max(pm[0], pm[1]), max(pm[2], pm[3]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, o));
+  const float A = bf2f((uint16_t)m);
   const float g = A == 0.f ? 1.0f : (float)((double)A / 2688.0);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = g;
 
@@ -181,7 +185,7 @@ hipError_t launch_fp4(int64_t N, int64_t K, const void *w, int64_t ldw, uint8_t 
   void *ws = (char *)ws_base + kWsReserved;     // leave the counter region untouched
   const long nchunks = (long)N * (K / 8);
   int g1 = (int)((nchunks + 255) / 256);
-  g1 = g1 < kFp4AmaxBlocks ? g1 : kFp4AmaxBlocks;
+  g1 = g1 < kNumCU ? g1 : kNumCU;               // <= 256 partials (the pack folds them per wave)
   hipLaunchKernelGGL(k_fp4_amax, dim3(g1), dim3(256), 0, st, (const uint16_t *)w, (int)N,
                      (int)K, (int)ldw, (unsigned *)ws);
   hipError_t e = hipGetLastError();
