@@ -81,8 +81,10 @@ typedef struct aq_proj {
  *   y      [M, ldy], ldy >= N; naturally aligned.
  *   ws     device workspace of at least aq_workspace_bytes(AQ_OP_RECON, ...)
  *          bytes, 256-byte aligned (NULL allowed when that size is 0).  Its
- *          first 64 KiB hold split-K arrival counters: they must be zero before
- *          the first use, and every call leaves them zero again; the rest is
+ *          first 64 KiB hold arrival counters (the hand-off of t from the
+ *          rank-r pass to the main pass when both run in one prefill launch):
+ *          they must be zero before the first use, and every call leaves them
+ *          zero again; the rest is
  *          per-call scratch.  So one zeroed allocation can serve any number and
  *          kind of calls (recon and FP4) that are ordered on one stream.  Calls
  *          that share a workspace must not run concurrently.

@@ -16,7 +16,8 @@ constexpr int kNumXCD = 8;
 constexpr int kDecodeMaxM = 64;   // largest batch served by the streaming kernel
 
 // Workspace layout shared by every call: the first kWsReserved bytes hold the
-// split-K arrival counters (zero between calls); per-call scratch (partials, the
+// arrival counters (zero between calls; the prefill launch that also runs the
+// rank-r pass uses the first two); per-call scratch (partials, the
 // rank-r activation buffer, FP4 partial maxima) starts after them, so calls of
 // different kinds can share one workspace.
 constexpr size_t kWsReserved = 65536;
