@@ -7,41 +7,49 @@
 //     y[:, col_b + n]   = s_b[n] * (x W0_b^T)[:, n] + (t U_b^T)[:, n]
 // The pages run this as stock GEMMs (one over [W0^T, V], one block-diagonal
 // up-projection) plus an elementwise combine.  Here:
-// * pass 1 (rank-r pass): t = x [Vt_q; Vt_k; ...]^T for every block of the
-//   dispatch with the same GEMM kernel on small tiles.  The output is narrow and
-//   the contraction long, so K is split over enough workgroups to cover the CUs;
-//   the splits write fp32 partials and a small kernel folds them, in split order,
-//   into a bf16 [M, sum r] buffer of the caller's workspace;
-// * pass 2: the W0 contraction, and an in-register epilogue: acc *= s[n], then
-//   acc += t U^T as r/16 further MFMA k-steps (t the A operand, U the B operand,
-//   both read from L2), then one rounding to bf16.  t is an MFMA operand and so
-//   held in bf16; everything else is fp32 until the final store.
+// * the rank-r pass, t = x [Vt_q; Vt_k; ...]^T for every block of the dispatch,
+//   is the same GEMM on small tiles.  Where its tiles fit in the CU slots the
+//   main pass leaves free, it runs in the first workgroups of the main pass's
+//   own launch: they publish t (bf16) with device-coherent stores and count
+//   themselves in the workspace; the main tiles wait for the count only before
+//   they first read t, near the end of their K loop.  Otherwise it is a launch
+//   of its own, K-split over enough workgroups for long K, with a small kernel
+//   folding the fp32 partials (in split order) into the bf16 t buffer;
+// * the main pass: the W0 contraction, then an in-register epilogue: acc *= s[n]
+//   once, then acc += t U^T as further MFMA k-steps over rank chunks that were
+//   loaded into the LDS ring like K slices (t where x goes, U where W0 goes),
+//   then one rounding to bf16.  t is an MFMA operand and so held in bf16;
+//   everything else is fp32 until the final store.
 //
 // GEMM design (gfx950, measured: v_mfma_f32_32x32x16_bf16 sustains ~2.2 PFLOP/s
 // over the chip, LDS reads > 180 B/clk/CU):
-// * BM x BN output tile per workgroup of 4 waves in a 2 x 2 grid, one wave per
-//   SIMD; each wave owns a (BM/2) x (BN/2) block of 32x32 MFMA tiles.  At
-//   256 x 256 a wave holds 16 accumulator tiles (256 registers, in AGPRs) and
-//   reads 8 fragments per 16 MFMAs, a quarter of the LDS bandwidth.
-// * K in slices of 32 (64 bytes per row) through a ring of 4 LDS stages, three
-//   slices in flight while one is multiplied: a slice of a 256 x 256 tile is
-//   ~1000 MFMA cycles, so three slices in flight cover a ~1.2 us load latency.
-//   Each stage is its own LDS object and the ring is unrolled, so the compiler
-//   can see that the loads landing in one stage never alias the fragment reads
-//   of another and does not wait for them.
+// * BM x BN output tile per workgroup of NW = 4 or 8 waves in a 2 x (NW / 2)
+//   grid of wave tiles of 32x32 MFMA tiles (128 x 64 per wave in the large
+//   shapes).  The main loop of those is bound by issuing the global -> LDS
+//   loads, so the largest dispatches use 256 x 256 with eight waves: one
+//   workgroup per CU, two waves per SIMD, a third fewer bytes per flop than
+//   256 x 128.
+// * K in slices of 32 or 64 through a ring of NST LDS stages, NST - 1 slices in
+//   flight while one is multiplied; the loads of a slice are spread over the
+//   MFMAs of the step.  Each stage is its own LDS object and the ring is
+//   unrolled, so the compiler can see that the loads landing in one stage never
+//   alias the fragment reads of another and does not wait for them.  With eight
+//   waves each step's barrier sits before its last k-step and the next slice's
+//   first fragments are read under that k-step's MFMAs.
 // * Operands go global -> LDS directly (buffer_load ... lds, 16 bytes per lane):
 //   no staging registers; rows or K past the end fall outside the buffer
 //   resource and land in LDS as zeros.
-// * LDS rows are 64 bytes (4 chunks of 16 bytes); chunk c of row R sits at
-//   position c ^ ((R / 4) mod 4), so the 16 rows read by 16 lanes of one
-//   fragment load cover all 64 banks once.
-// * The output tile is staged through the (free) LDS stages 32 rows per wave
-//   row at a time and written with 16-byte row-contiguous stores.  Tiles are
-//   handed to XCDs in contiguous ranges (m fastest), so the workgroups of one
-//   XCD share the W0 rows of a column tile in L2.
-// * When the tiles cannot cover the 256 CUs (short, wide layers), K is split over
-//   S workgroups that write fp32 partials (split 0 adds t U^T; all apply s), and
-//   a small kernel adds them in split order.  Deterministic.
+// * 16-byte chunks of an LDS row are XOR-swizzled by row, so the 16 rows read
+//   by 16 lanes of one fragment load cover all 64 banks once.
+// * Each wave stages its output block through a free LDS stage, 32 rows at a
+//   time, and writes it with 16-byte row-contiguous stores one round late.
+//   Tiles are handed to XCDs in contiguous ranges (m fastest), so the
+//   workgroups of one XCD share the W0 rows of a column tile in L2.
+// * When the tiles cannot cover the 256 CUs (long K, few tiles), K is split
+//   over S workgroups that write fp32 partials (all apply s; split 0 adds t U^T,
+//   or with the rank-r pass in the same launch every split adds the rank term
+//   of its own K range), and a small kernel adds them in split order.
+//   Deterministic.
 
 #include <stdlib.h>
 
