@@ -76,6 +76,8 @@ struct PrefillPlan {
   int NW;                           // waves per workgroup (main pass)
   int tBM, tBN, tS;                 // output tile and K splits of the rank-r (t) pass
   int fuse;                         // rank-r pass inside the main-pass launch
+  int tparts;                       // fused, main pass unsplit: t kept in this many K-range parts
+  int self;                         // main tiles compute their own rows of t (no rank-r pass)
   size_t tpart_off;                 // byte offset of the t-pass partials in the scratch
   size_t part_off;                  // byte offset of the main-pass partials in the scratch
   size_t ws_bytes;                  // total workspace bytes (reserved region + t buffer)

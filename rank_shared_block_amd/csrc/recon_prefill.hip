@@ -61,11 +61,13 @@
 namespace aq {
 
 namespace {
-enum { MODE_RECON = 0, MODE_PART = 1, MODE_RAW = 2 };
+// MODE_SELF: MODE_RECON for tiles that also compute their own rows of t
+// (their Vt rows ride in every LDS stage next to the W0 rows).
+enum { MODE_RECON = 0, MODE_PART = 1, MODE_RAW = 2, MODE_SELF = 3 };
 }  // namespace
 
 struct PfBlk {
-  const uint16_t *W, *s, *U;
+  const uint16_t *W, *s, *U, *Vt;   // Vt: MODE_SELF only
   int N;       // valid rows of W (output columns computed)
   int Nst;     // output columns stored (>= N: padding columns are stored as 0)
   int r, col, tcol, ntn, tile0, ufast;
@@ -87,6 +89,11 @@ struct PfArgs {
   // linear in K, so the fold of the partials sums it); the rank-r tiles write
   // t_p the same way (y + p * tstride).
   int tsplit;
+  // tparts: with the main pass unsplit, t may still be kept as tparts per-K-range
+  // parts (the rank-r tiles split K so that they finish well before the main
+  // tiles); every main unit then adds (sum_p t_p) U^T, each part as more rank
+  // chunks.  1 otherwise.
+  int tparts;
   long tstride;
   unsigned *sync;
   PfBlk b[kMaxBlocks];
@@ -128,8 +135,8 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "m
 
 // Workgroups per CU a tile shape is built for: two when its LDS ring fits in
 // half of the 160 KiB (registers are then capped at 256 per lane).
-template <int BM, int BN, int BK, int NST>
-constexpr int gemm_occupancy() { return (BM + BN) * BK * 2 * NST <= 80 * 1024 ? 2 : 1; }
+template <int BM, int BN, int BK, int NST, int RT = 0>
+constexpr int gemm_occupancy() { return (BM + BN + RT) * BK * 2 * NST + BN * 4 <= 80 * 1024 ? 2 : 1; }
 
 // NW waves per workgroup in a 2 x (NW / 2) grid: four (one or two workgroups
 // per CU) or eight (one workgroup per CU, two waves per SIMD, for 256 x 256
@@ -142,11 +149,18 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   constexpr int WGN = NW / 2;                      // waves along N
   constexpr int WM = BM / 2, WN = BN / WGN;        // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;        // 32x32 MFMA tiles per wave
-  constexpr int STAGE = (BM + BN) * BK;            // bf16 elements per LDS stage
+  constexpr bool SELF = MODE == MODE_SELF;
+  constexpr int RT = SELF ? 64 : 0;                // Vt rows per stage (the tile's own t, r <= 64)
+  constexpr int TNT = SELF ? RT / WGN / 32 : 0;    // 32x32 t tiles per wave
+  constexpr int STAGE = (BM + BN + RT) * BK;       // bf16 elements per LDS stage
   constexpr int CPR = BK / 8;                      // 16-byte chunks per LDS row
   constexpr int RPL = 64 / CPR;                    // rows per 1 KiB load
   constexpr int LA = BM / (NW * RPL), LB = BN / (NW * RPL);   // loads per wave per stage
-  constexpr int LPS = LA + LB;
+  constexpr int LT = RT / (NW * RPL);
+  constexpr int LPS = LA + LB + LT;
+  static_assert(!SELF || (NW == 4 && TNT == 1 && LT * NW * RPL == RT), "own-t tiles: four waves, 64 Vt rows");
+  static_assert(!SELF || 64 / BK <= (64 * (BN + 8) <= (BM + BN + RT) * BK ? NST - 1 : NST - 2),
+                "own-t tiles: every rank chunk of t rides the ring");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must be a multiple of 64");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(WN % 32 == 0 && LA * NW * RPL == BM && LB * NW * RPL == BN, "wave tiles and loads must divide the tile");
@@ -196,6 +210,13 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
     boff[j] = row * K * 2;
     bchk[j] = lpos ^ sw(BM + row);
   }
+  int voff[LT > 0 ? LT : 1], vchk[LT > 0 ? LT : 1];
+#pragma unroll
+  for (int j = 0; j < LT; ++j) {
+    const int row = (wave * LT + j) * RPL + lrow;
+    voff[j] = row * K * 2;
+    vchk[j] = lpos ^ sw(BM + BN + row);
+  }
   // The epilogue's rank-r term (see below) needs the tile's rows of t and U.
   // They ride on the slices issued past the end of the ring (nkp .. nkp +
   // NST - 2, never multiplied): rank chunk c (ranks BK c .. BK c + BK - 1) as
@@ -203,19 +224,30 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   // their latency hides under the last steps.  Ranks past r16 (t) or r (U) and
   // rows past M or N read as zero; U takes this path only with 16-byte aligned
   // rows (ufast).
-  const bool addu = MODE != MODE_RAW && (MODE == MODE_RECON || p == 0 || a.tsplit) && B.r > 0;
+  // With t in parts (tparts > 1), rank chunk c is chunk c % nchunk1 of part
+  // c / nchunk1: the parts are summed by the same MFMAs.
+  // MODE_SELF: no t in memory (its rank chunk's t rows are written from
+  // registers after the K loop).
+  const bool addu = MODE != MODE_RAW && (MODE == MODE_RECON || SELF || p == 0 || a.tsplit) && B.r > 0;
   const uint16_t *const tbase = a.t + (a.tsplit ? (size_t)p * a.tstride : 0);
   const int r16 = (B.r + 15) & ~15;
-  const __amdgpu_buffer_rsrc_t rt =
-      make_rsrc(tbase + (size_t)m0 * a.ldt, addu ? (uint32_t)(mrows * a.ldt * 2) : 0u);
+  const int tparts = MODE == MODE_RAW || SELF ? 1 : a.tparts;
+  const int nchunk1 = (r16 + BK - 1) / BK;         // rank chunks per part of t
+  const __amdgpu_buffer_rsrc_t rt = make_rsrc(
+      tbase + (size_t)m0 * a.ldt,
+      addu && !SELF ? (uint32_t)(((size_t)(tparts - 1) * a.tstride + (size_t)mrows * a.ldt) * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(SELF ? B.Vt : a.x, SELF && B.r > 0 ? (uint32_t)(B.r * K * 2) : 0u);
   const __amdgpu_buffer_rsrc_t ru =
       make_rsrc(B.U + (size_t)n0 * B.r, addu && nrows > 0 && B.ufast ? (uint32_t)(nrows * B.r * 2) : 0u);
+  auto part_of = [&](int c) __attribute__((always_inline)) { return tparts == 1 ? 0 : c / nchunk1; };
   auto eoff_a = [&](int d, int c) __attribute__((always_inline)) {
-    const int row = (wave * LA + d) * RPL + lrow, col = BK * c + 8 * achk[d];
-    return col < r16 ? (row * a.ldt + B.tcol + col) * 2 : kOOB;
+    const int pe = part_of(c);
+    const int row = (wave * LA + d) * RPL + lrow, col = BK * (c - pe * nchunk1) + 8 * achk[d];
+    // rows past M stay out of range also where another part follows
+    return col < r16 && row < mrows ? (int)(pe * a.tstride + row * a.ldt + B.tcol + col) * 2 : kOOB;
   };
   auto eoff_b = [&](int d, int c) __attribute__((always_inline)) {
-    const int row = (wave * LB + d) * RPL + lrow, col = BK * c + 8 * bchk[d];
+    const int row = (wave * LB + d) * RPL + lrow, col = BK * (c - part_of(c) * nchunk1) + 8 * bchk[d];
     return col < B.r ? (row * B.r + col) * 2 : kOOB;
   };
 
@@ -229,6 +261,10 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
       const int kk = k0 + 8 * achk[d];
       const int off = kk < klim ? aoff[d] + kk * 2 : kOOB;
       lds_load16(ech >= 0 ? rt : rx, stage + (wave * LA + d) * 512, ech >= 0 ? eoff_a(d, ech) : off);
+    } else if (d >= LA + LB) {          // Vt rows (MODE_SELF); none in a rank chunk
+      const int kk = k0 + 8 * vchk[d - LA - LB];
+      const int off = kk < klim && ech < 0 ? voff[d - LA - LB] + kk * 2 : kOOB;
+      lds_load16(rv, stage + (BM + BN) * BK + (wave * LT + d - LA - LB) * 512, off);
     } else {
       const int kk = k0 + 8 * bchk[d - LA];
       const int off = kk < klim ? boff[d - LA] + kk * 2 : kOOB;
@@ -249,6 +285,15 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  // MODE_SELF: this wave's block of t = x Vt^T (rows as acc, ranks wn * 32 ..)
+  constexpr int TNT1 = TNT > 0 ? TNT : 1;
+  f32x16 acct[TM][TNT1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TNT1; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acct[i][j][v] = 0.f;
 
   // Fragment reads: lane (l32, lhi) reads row R = base + l32 at chunk
   // 2 kk + lhi; every base is a multiple of 32, so sw(R) = sw(l32).
@@ -261,6 +306,12 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
 #pragma unroll
     for (int j = 0; j < TN; ++j) bf[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(stage + brow + j * 32 * BK + c));
   };
+  const int vrow = (BM + BN + wn * (RT / WGN) + l32) * BK;
+  auto tfrags = [&](const uint16_t *stage, int kk, bf16x8 (&tf)[TNT1]) __attribute__((always_inline)) {
+    const int c = 8 * ((2 * kk + lhi) ^ swz);
+#pragma unroll
+    for (int j = 0; j < TNT; ++j) tf[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(stage + vrow + j * 32 * BK + c));
+  };
 
   // One step of the ring: multiply the stage `cur` while the loads of slice
   // `nslice` into `next` go out.  The loads are spread over the MFMA stream (a
@@ -270,7 +321,8 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   // read while k-step kk is multiplied.
   constexpr int KK = BK / 16, SLOTS = KK * TM;
   const int nkp = (nk + NST - 1) / NST * NST;    // slices past nk are zeros
-  const int nchunk = (r16 + BK - 1) / BK;          // rank chunks of the epilogue
+  // rank chunks of the epilogue (MODE_SELF: the one it computes, r <= 64)
+  const int nchunk = SELF ? (nchunk1 < 64 / BK ? nchunk1 : 64 / BK) : nchunk1 * tparts;
   // ... riding on the tail slices (all but the last, or all but the last two
   // when the output block needs two stages for staging)
   constexpr int ESLOTS = 64 * (BN + 8) <= STAGE ? NST - 1 : NST - 2;
@@ -280,11 +332,15 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   auto step = [&](auto tail, int nslice, uint16_t *next, const uint16_t *cur) __attribute__((always_inline)) {
     const int k0 = kbeg + nslice * BK, klim = nslice < nk ? kend : -1;
     const int ech = decltype(tail)::value && nslice >= nkp && nslice - nkp < nech ? nslice - nkp : -1;
-    bf16x8 fa[2][TM], fb[2][TN];
+    bf16x8 fa[2][TM], fb[2][TN], ft[2][TNT1];
     frags(cur, 0, fa[0], fb[0]);
+    if constexpr (SELF) tfrags(cur, 0, ft[0]);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      if (kk + 1 < KK) {
+        frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        if constexpr (SELF) tfrags(cur, kk + 1, ft[(kk + 1) & 1]);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         // W rows are the A operand and x rows the B operand, so that the
@@ -293,6 +349,9 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < TNT; ++j)
+          acct[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ft[kk & 1][j], fa[kk & 1][i], acct[i][j], 0, 0, 0);
         const int t = kk * TM + i;
 #pragma unroll
         for (int d = t * LPS / SLOTS; d < (t + 1) * LPS / SLOTS; ++d) dma(d, k0, klim, ech, next);
@@ -460,6 +519,30 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   if (MODE != MODE_RAW)
     if (tid < BN) s_lds[tid] = n0 + tid < B.N ? bf2f(s_raw) : 0.f;
   __syncthreads();                       // s_lds, and every wave's last loads, are in
+  if constexpr (SELF) {
+    // This wave's block of t, rounded to bf16, goes where the rank chunks'
+    // t rows sit (chunk c = ranks BK c .. in stage c, x rows, same swizzle);
+    // U came with the ring.  Lane: row wm * WM + 32 i + l32, ranks
+    // wn * 32 + 8 g + 4 lhi + (0..3).
+    if (addu) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j0 = wn * 32 + 8 * g, c = j0 / BK;
+        if (c >= nchunk) continue;
+        uint16_t *const stc = c == 0 ? st0 : st1;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int R = wm * WM + i * 32 + l32;
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const bf16x4 h = {(__bf16)acct[i][0][4 * g + 0], (__bf16)acct[i][0][4 * g + 1], (__bf16)acct[i][0][4 * g + 2],
+                            (__bf16)acct[i][0][4 * g + 3]};
+          *reinterpret_cast<uint2 *>(stc + R * BK + 8 * (((j0 % BK) / 8) ^ sw(R)) + 4 * lhi) =
+              __builtin_bit_cast(uint2, h);
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   if constexpr (MODE != MODE_RAW) {
 #pragma unroll
@@ -484,7 +567,7 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
     for (int c = 0; c < ESLOTS; ++c) {
       if (c >= nech) break;
       const uint16_t *stc = c == 0 ? st0 : (c == 1 ? st1 : st2);
-      const int kmax = min(KK, (r16 - BK * c) / 16);
+      const int kmax = min(KK, (r16 - BK * (c - part_of(c) * nchunk1)) / 16);
       bf16x8 fa[2][TM], fb[2][TN];
       frags(stc, 0, fa[0], fb[0]);
 #pragma unroll
@@ -508,9 +591,10 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   auto tfrag_lds = [&](const uint16_t *stc, int i, int kk) __attribute__((always_inline)) {
     return as_bf16x8(*reinterpret_cast<const uint4 *>(stc + arow + i * 32 * BK + 8 * ((2 * kk + lhi) ^ swz)));
   };
-  auto tfrag_glb = [&](int i, int col) __attribute__((always_inline)) {
+  auto tfrag_glb = [&](int i, int pe, int col) __attribute__((always_inline)) {
     const int m = m0 + wm * WM + i * 32 + l32;
-    return m < M && col < r16 ? as_bf16x8(ld16(tbase + (size_t)m * a.ldt + B.tcol + col)) : zero_bf16x8();
+    return m < M && col < r16 ? as_bf16x8(ld16(tbase + pe * a.tstride + (size_t)m * a.ldt + B.tcol + col))
+                              : zero_bf16x8();
   };
   auto ufrag_glb = [&](int j, int col) __attribute__((always_inline)) {
     const int n = n0 + wn * WN + j * 32 + l32;
@@ -519,7 +603,7 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
 
   // Column blocks per round of the per-round rank-r path: every block's MFMA
   // chain at once where the registers allow, else two at a time.
-  constexpr int JH = (gemm_occupancy<BM, BN, BK, NST>() == 1 && TM * TN <= 8) ? TN : (TN >= 2 ? 2 : 1);
+  constexpr int JH = (gemm_occupancy<BM, BN, BK, NST, RT>() == 1 && TM * TN <= 8) ? TN : (TN >= 2 ? 2 : 1);
   // bf16 output: each wave stages its 32 x WN block of a round in LDS and
   // stores it itself as 16-byte row pieces, one round late: the staged block
   // of round i - 1 is read back before round i is computed (LDS operations of
@@ -574,11 +658,12 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
         for (int v = 0; v < 16; ++v) w[q][v] = 0.f;
       if (wround) {
         for (int c = cfirst; c < nchunk; ++c) {
-          const int kmax = min(KK, (r16 - BK * c) / 16);
+          const int pe = part_of(c), cc = c - pe * nchunk1;
+          const int kmax = min(KK, (r16 - BK * cc) / 16);
           const uint16_t *stc = c == 0 ? st0 : (c == 1 ? st1 : st2);
           for (int kk = 0; kk < kmax; ++kk) {
-            const int col = BK * c + 16 * kk + 8 * lhi;
-            const bf16x8 tb = c < nech ? tfrag_lds(stc, i, kk) : tfrag_glb(i, col);
+            const int col = BK * cc + 16 * kk + 8 * lhi;
+            const bf16x8 tb = c < nech ? tfrag_lds(stc, i, kk) : tfrag_glb(i, pe, col);
 #pragma unroll
             for (int q = 0; q < JH; ++q)
               w[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ufrag_glb(j0 + q, col), tb, w[q], 0, 0, 0);
@@ -637,9 +722,9 @@ struct TPass {
 // run the rank-r pass tiles described by tp instead (over the same K ranges as
 // the main pass under a K split).
 template <int BM, int BN, int BK, int NST, int MODE, int NW>
-__global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void k_gemm_bf16(const PfArgs a,
-                                                                                           const PfArgs tp) {
-  constexpr int STAGE = (BM + BN) * BK;
+__global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST, MODE == MODE_SELF ? 64 : 0>())) void k_gemm_bf16(
+    const PfArgs a, const PfArgs tp) {
+  constexpr int STAGE = (BM + BN + (MODE == MODE_SELF ? 64 : 0)) * BK;
   // Each stage is its own LDS object; unused ones are a token size.
   __shared__ __attribute__((aligned(1024))) uint16_t st0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[STAGE];
@@ -647,7 +732,7 @@ __global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST>())) void 
   __shared__ __attribute__((aligned(1024))) uint16_t st3[NST > 3 ? STAGE : 8];
   __shared__ float s_lds[BN];
   using T = TPass<BM, BN, BK, NST, NW>;
-  if constexpr (MODE != MODE_RAW && T::ok) {
+  if constexpr (MODE != MODE_RAW && MODE != MODE_SELF && T::ok) {
     static_assert((T::tBM + T::tBN) * T::tBK <= STAGE && T::tNST <= NST, "rank-r stages must fit");
     if ((int)blockIdx.x < a.tgrid) {
       const int u = xcd_contiguous_tile(blockIdx.x, tp.ntiles * tp.S);
@@ -717,7 +802,7 @@ struct Cand {
 static const Cand kCands[] = {{128, 128, 64, 4, 4}, {256, 128, 32, 3, 4}, {256, 128, 64, 3, 4}, {256, 256, 32, 4, 4},
                                {256, 256, 64, 2, 4}, {256, 256, 32, 4, 8}, {256, 256, 64, 2, 8}, {128, 256, 64, 3, 4},
                                {128, 128, 64, 2, 4}, {128, 256, 32, 3, 4}, {128, 128, 32, 4, 4}, {64, 64, 64, 4, 4},
-                               {64, 128, 64, 4, 4},  {128, 64, 64, 4, 4}};
+                               {64, 128, 64, 4, 4},  {128, 64, 64, 4, 4},  {128, 128, 64, 3, 4}};
 
 // Main-pass tile and K split.  The tile comes from a cost model fitted to
 // sweeps over the Gemma-3-1B and large-decoder prefill shapes on MI355X: a
@@ -726,11 +811,15 @@ static const Cand kCands[] = {{128, 128, 64, 4, 4}, {256, 128, 32, 3, 4}, {256, 
 // per-slice times (us): 256 x 256 with eight waves 0.85 (one per CU); 256 x 128
 // with 32-wide slices 0.89 when two share a CU, 0.71 alone; 256 x 128 with
 // 64-wide slices 0.52 (one per CU); 128 x 128 0.35 (one per CU).
-// * up to 16 tiles of 128 x 128: 64 x 64 tiles, four stages, no K split (they
-//   cover four times as many CUs);
+// * up to 16 tiles of 128 x 128, or K <= 2048 and at most one round of 64 x 64
+//   tiles (the Gemma-3-1B QKV and o projections at M = 512): 64 x 64 tiles,
+//   four stages, no K split (they cover four times as many CUs, and a tile's
+//   K loop, bound by load latency there, runs a quarter of the bytes);
 // * K <= 2048 and at most one round of 128 x 128 tiles (the Gemma-3-1B QKV
-//   and o projections): 128 x 128 with 32-wide slices, two workgroups per CU,
-//   so that the rank-r pass tiles fit beside them in the same launch;
+//   and o projections at M = 2048): 128 x 128 with 64-wide slices in three
+//   stages that compute their own rows of t (r <= 64), else with 32-wide
+//   slices, two workgroups per CU, so that the rank-r pass tiles fit beside
+//   them in the same launch;
 // * else the cheapest of the four by the model; 128 x 128 splits long K
 //   (>= 4096) when its tiles cover at most half of the CUs (ranges >= 2048).
 struct Est {
@@ -745,11 +834,14 @@ static const Est kEst[] = {{{256, 256, 32, 4, 1, 8}, kNumCU, 0.85, 0.85, 5.0},
 
 TileCfg choose(const Recon &rq) {
   const int t128 = count_tiles(rq, 128, 128, false);
+  int rmax = 0;
+  for (int b = 0; b < rq.nblk; ++b) rmax = rq.blk[b].r > rmax ? (int)rq.blk[b].r : rmax;
+  const bool own_t = rmax <= 64 && env_int("AQ_PREFILL_SELF", 1) != 0;
   TileCfg tc = {128, 128, 64, 4, 1, 4};
-  if (t128 <= 16) {
+  if (t128 <= 16 || (rq.K <= 2048 && count_tiles(rq, 64, 64, false) <= kNumCU)) {
     tc = {64, 64, 64, 4, 1, 4};
   } else if (rq.K <= 2048 && t128 <= kNumCU) {
-    tc = {128, 128, 32, 4, 1, 4};
+    tc = own_t ? TileCfg{128, 128, 64, 3, 1, 4} : TileCfg{128, 128, 32, 4, 1, 4};
   } else {
     double best = 1e30;
     for (const Est &e : kEst) {
@@ -811,15 +903,43 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
                       (tc.BM == 64 && tc.BN == 64 && tc.BK == 64)));
   // Under a main-pass K split the rank-r tiles run over the same K ranges and
   // keep one t per range (each main unit adds its own range's rank term).
+  // A main tile smaller than four rank-r tiles (64 x 64) takes about as long
+  // as one: there the rank-r tiles split K into parts (kept apart, summed by
+  // the main tiles' epilogue MFMAs) so that each runs at most half as many K
+  // slices as a main tile and t is ready before the main tiles need it.
   const int to = env_int("AQ_TPASS_S", 0);
   pl->fuse = 0;
-  if (c > 0 && fusable && to <= 1 && env_int("AQ_PREFILL_FUSE", 1) != 0) {
+  pl->tparts = 1;
+  // 64 x 64 tiles (few, latency-bound tiles) compute their own rows of t: the
+  // Vt rows of their block (r <= 64) ride in every LDS stage as 64 more B rows,
+  // so t never goes through memory and no tile waits for another; the extra
+  // MFMAs cost little where each K slice waits for its loads anyway.
+  int rmax = 0;
+  for (int b = 0; b < rq.nblk; ++b) rmax = rq.blk[b].r > rmax ? (int)rq.blk[b].r : rmax;
+  const bool self_tile = tc.NW == 4 && ((tc.BM == 64 && tc.BN == 64 && tc.BK == 64 && tc.NST == 4) ||
+                                         (tc.BM == 128 && tc.BN == 128 && tc.BK == 32 && tc.NST == 4) ||
+                                         (tc.BM == 128 && tc.BN == 128 && tc.BK == 64 && tc.NST == 3));
+  pl->self = c > 0 && self_tile && tc.S == 1 && rmax <= 64 && to <= 1 && env_int("AQ_PREFILL_SELF", 1) != 0;
+  if (c > 0 && !pl->self && fusable && to <= 1 && env_int("AQ_PREFILL_FUSE", 1) != 0) {
     const int tb = tc.NW == 8 ? 128 : 64;              // the shape TPass gives
     const int slots = kNumCU * ((tc.BM + tc.BN) * tc.BK * 2 * tc.NST <= 80 * 1024 ? 2 : 1);
     const int rem = count_tiles(rq, tc.BM, tc.BN, false) * tc.S % slots;
-    const int tt = count_tiles(rq, tb, tb, true) * tc.S;
-    if (tc.BM * tc.BN >= 4 * tb * tb && rem > 0 && rem + tt <= slots) {
+    const bool big = tc.BM * tc.BN >= 4 * tb * tb;
+    int parts = 1;
+    if (!big && tc.S == 1) {
+      parts = 2 * 64 / tc.BK;
+      const int po = env_int("AQ_TPASS_PARTS", 0);
+      if (po >= 1) parts = po;
+      const int pmax = (int)((rq.K + 127) / 128);        // parts of >= 128 K values
+      parts = parts < pmax ? parts : pmax;
+      parts = parts < 8 ? parts : 8;
+      // the parts' offsets stay 32-bit
+      if ((double)parts * (double)rq.M * c * 2 >= 2147483648.0) parts = 1;
+    }
+    const int tt = count_tiles(rq, tb, tb, true) * (tc.S > 1 ? tc.S : parts);
+    if ((big || parts > 1) && rem > 0 && rem + tt <= slots) {
       pl->fuse = 1;
+      pl->tparts = tc.S > 1 ? 1 : parts;
       pl->tBM = pl->tBN = tb;
     }
   }
@@ -828,14 +948,14 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
   // >= 768 values and the fp32 partials are folded into the bf16 t buffer by
   // the reduce kernel; for shorter K the fold costs more than the split saves
   // (sweeps over the Gemma-3-1B prefill shapes on MI355X).
-  if (!pl->fuse && c > 0 && rq.K > 2048) {
+  if (!pl->fuse && !pl->self && c > 0 && rq.K > 2048) {
     const int tiles = count_tiles(rq, 64, 64, true);
     int S = (kNumCU + tiles - 1) / tiles;
     const int smax = rq.K / 768 > 1 ? (int)(rq.K / 768) : 1;
     pl->tS = S < smax ? S : smax;
   }
   if (to >= 1) pl->tS = to;
-  size_t bytes = (size_t)rq.M * c * 2 * (pl->fuse ? pl->S : 1);
+  size_t bytes = pl->self ? 0 : (size_t)rq.M * c * 2 * (pl->fuse ? (pl->S > pl->tparts ? pl->S : pl->tparts) : 1);
   bytes = (bytes + 255) / 256 * 256;
   pl->tpart_off = bytes;
   if (pl->tS > 1) bytes += ((size_t)pl->tS * rq.M * c * 4 + 255) / 256 * 256;
@@ -854,6 +974,10 @@ static bool launch_tile(int BM, int BN, int BK, int NST, int NW, const PfArgs &a
   }
   if constexpr (MODE == MODE_RAW) {
     AQ_TILE(64, 64, 64, 4, 4)
+  } else if constexpr (MODE == MODE_SELF) {
+    AQ_TILE(64, 64, 64, 4, 4)
+    AQ_TILE(128, 128, 32, 4, 4)
+    AQ_TILE(128, 128, 64, 3, 4)
   } else {
     AQ_TILE(256, 256, 32, 4, 4)
     AQ_TILE(256, 256, 64, 2, 4)
@@ -862,6 +986,7 @@ static bool launch_tile(int BM, int BN, int BK, int NST, int NW, const PfArgs &a
     AQ_TILE(256, 128, 64, 3, 4)
     AQ_TILE(128, 256, 64, 3, 4)
     AQ_TILE(128, 128, 64, 2, 4)
+    AQ_TILE(128, 128, 64, 3, 4)
     AQ_TILE(128, 128, 64, 4, 4)
     AQ_TILE(256, 128, 32, 3, 4)
     AQ_TILE(128, 256, 32, 3, 4)
@@ -894,6 +1019,7 @@ static hipError_t run(PfArgs &a, const PfArgs &tp, int BM, int BN, int BK, int N
   switch (mode) {
     case MODE_RECON: ok = launch_tile<MODE_RECON>(BM, BN, BK, NST, NW, a, tp, grid, st); break;
     case MODE_PART: ok = launch_tile<MODE_PART>(BM, BN, BK, NST, NW, a, tp, grid, st); break;
+    case MODE_SELF: ok = launch_tile<MODE_SELF>(BM, BN, BK, NST, NW, a, tp, grid, st); break;
     default: ok = launch_tile<MODE_RAW>(BM, BN, BK, NST, NW, a, tp, grid, st); break;
   }
   if (!ok) return hipErrorInvalidValue;
@@ -904,6 +1030,7 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
   char *scratch = ws ? (char *)ws + kWsReserved : nullptr;
   uint16_t *tbuf = pl.ldt > 0 ? (uint16_t *)scratch : nullptr;
   PfArgs a = {};
+  a.tparts = 1;
   a.x = (const uint16_t *)rq.x;
   a.ldx = (int)rq.ldx;
   a.M = (int)rq.M;
@@ -912,7 +1039,7 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
   // pass 1: fp32 partials of t = x Vt^T for every block with r > 0 (columns
   // padded to 16 with zeros), then folded into the bf16 t buffer.
   PfArgs t = a;
-  if (pl.ldt > 0) {
+  if (pl.ldt > 0 && !pl.self) {
     t.S = pl.tS;
     int tkc = (int)((rq.K + pl.tS - 1) / pl.tS);
     t.kchunk = (tkc + 63) / 64 * 64;
@@ -937,9 +1064,11 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
     }
     if (pl.fuse) {
       // run by the first workgroups of the main-pass launch (below), over the
-      // main pass's K ranges, one bf16 t per range
-      const int kc = (int)((rq.K + pl.S - 1) / pl.S);
-      t.kchunk = (kc + pl.BK - 1) / pl.BK * pl.BK;
+      // main pass's K ranges (or in tparts K ranges of its own), one bf16 t
+      // per range
+      const int nr = pl.S > 1 ? pl.S : pl.tparts, kq = pl.S > 1 ? pl.BK : 64;
+      const int kc = (int)((rq.K + nr - 1) / nr);
+      t.kchunk = (kc + kq - 1) / kq * kq;
       t.S = (int)((rq.K + t.kchunk - 1) / t.kchunk);
       t.part = nullptr;
       t.y = tbuf;
@@ -979,6 +1108,7 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
     d.W = (const uint16_t *)P.W0;
     d.s = (const uint16_t *)P.s;
     d.U = (const uint16_t *)P.U;
+    d.Vt = (const uint16_t *)P.Vt;
     d.N = (int)P.N;
     d.Nst = (int)P.N;
     d.r = (int)P.r;
@@ -992,13 +1122,15 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
     a.tgrid = 8 * ((t.ntiles * t.S + 7) / 8);
     a.sync = (unsigned *)ws;
     a.tsplit = a.S > 1;
+    a.tparts = a.S > 1 ? 1 : t.S;
     a.tstride = (long)rq.M * pl.ldt;
     a.nwait = 0;
     for (int b = 0; b < rq.nblk; ++b)
       if (a.b[b].r > 0) a.nwait += a.b[b].ntn * a.ntm * (a.tsplit ? a.S : 1);
     if (a.nwait == 0) a.tgrid = 0;
   }
-  hipError_t e = run(a, t, pl.BM, pl.BN, pl.BK, pl.NST, pl.NW, a.S > 1 ? MODE_PART : MODE_RECON, st);
+  const int mode = pl.self ? MODE_SELF : (a.S > 1 ? MODE_PART : MODE_RECON);
+  hipError_t e = run(a, t, pl.BM, pl.BN, pl.BK, pl.NST, pl.NW, mode, st);
   if (e != hipSuccess || a.S == 1) return e;
   const long n = (long)rq.M * rq.Ntot;
   hipLaunchKernelGGL(k_prefill_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,

@@ -239,6 +239,59 @@ def test_prefill_rank_pass_in_main_launch(M, K, S, tile, monkeypatch):
         assert int(counters.sum()) == 0, counters
 
 
+@pytest.mark.parametrize("M", [130, 300])
+@pytest.mark.parametrize("K", [200, 1048])
+@pytest.mark.parametrize("parts", [2, 3, 4])
+def test_prefill_rank_pass_in_parts(M, K, parts, monkeypatch):
+    """Main tiles of 64 x 64 with the rank-r pass in the same launch, its K split
+    into parts that are kept apart and summed by the main tiles' epilogue: two
+    or three parts ride the LDS ring, a fourth goes the per-round path; U rows
+    aligned (r = 16) and not (r = 36); K = 200 allows two parts of >= 128 K
+    values only.  The workspace size shows that the plan keeps the parts."""
+    for k, v in zip(("BM", "BN", "BK", "NST", "W"), (64, 64, 64, 4, 4)):
+        monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
+    monkeypatch.setenv("AQ_TPASS_PARTS", str(parts))
+    monkeypatch.setenv("AQ_PREFILL_SELF", "0")
+    shapes = [(300, 16), (200, 36), (72, 0)]
+    bds = [I.bundle("test", 7, f, K, n, r, "bf16", variant="normal") for f, (n, r) in zip(("q", "k", "v"), shapes)]
+    nparts = min(parts, (K + 127) // 128)
+    ldt = 16 + 48
+    fake = [B.aq_proj(n, r, 256, 256, 256, 256) for n, r in shapes]
+    want = 65536 + (M * ldt * 2 * nparts + 255) // 256 * 256
+    assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, M, K, fake, 3) == want
+    x = I.activations("test", 970 + M + K, M, K, "bf16")
+    ref = oracle.recon_fused(x, [bundle_np(b) for b in bds])
+    for rep in range(2):
+        y = B.recon_qkv(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+        assert_parity(down(y), ref, "bf16", f"M={M} K={K} parts={parts} rep={rep}")
+        torch.cuda.synchronize()
+        counters = B.default_workspace()._buf[torch.device(dev()).index][:8].cpu()
+        assert int(counters.sum()) == 0, counters
+
+
+@pytest.mark.parametrize("M", [65, 130, 300])
+@pytest.mark.parametrize("K", [200, 1048, 3000])
+@pytest.mark.parametrize("tile", [(64, 64, 64, 4), (128, 128, 32, 4), (128, 128, 64, 3)])
+def test_prefill_own_t(M, K, tile, monkeypatch):
+    """Main tiles that compute their own rows of t (Vt rows as more B rows of
+    every stage, t rounded to bf16 in LDS, one or two rank chunks): r = 64,
+    r = 16, r = 36 (U rows not 16-byte aligned: the per-round path with t from
+    LDS), a block without rank; nothing in the workspace."""
+    for k, v in zip(("BM", "BN", "BK", "NST", "W"), tuple(tile) + (4,)):
+        monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
+    shapes = [(300, 64), (200, 16), (136, 36), (72, 0)]
+    bds = [I.bundle("test", 8, f, K, n, r, "bf16", variant="normal") for f, (n, r) in zip(("q", "k", "v", "o"), shapes)]
+    fake = [B.aq_proj(n, r, 256, 256, 256, 256) for n, r in shapes[:3]]
+    assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, M, K, fake, 3) == 0
+    x = I.activations("test", 990 + M + K, M, K, "bf16")
+    for sel in ((0, 1, 2), (1, 2, 3)):
+        sub = [bds[i] for i in sel]
+        y = B.recon_qkv(up(x, "bf16"), [bundle_up(b, "bf16") for b in sub])
+        assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in sub]), "bf16", f"M={M} K={K} {sel}")
+    y = B.recon_linear(up(x, "bf16"), bundle_up(bds[0], "bf16"))
+    assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bds[0])), "bf16", f"single M={M} K={K}")
+
+
 @pytest.mark.parametrize("M", [1, 16, 33, 130])
 def test_fused_gateup_small(M):
     K = 384

@@ -105,9 +105,14 @@ def test_workspace_query_is_host_only():
     assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 16, 1152, p1, 1) == 0
     ws_dec = B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 16, 6912, [_proj(N=1152, r=16)], 1)
     assert ws_dec % 256 == 0 and ws_dec > 65536
-    # prefill: at least a bf16 t buffer of M x (r rounded to 16)
-    ws_pf = B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 512, 1152, p1, 1)
-    assert ws_pf >= 65536 + 512 * 16 * 2
+    # prefill: at least a bf16 t buffer of M x (r rounded to 16), except where
+    # one round of 64 x 64 or 128 x 128 tiles covers the output (they compute
+    # their own t for r <= 64)
+    ws_pf = B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 2048, 1152, [_proj(N=6912, r=16)], 1)
+    assert ws_pf >= 65536 + 2048 * 16 * 2
+    assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 2048, 1152, [_proj(N=1024, r=72)], 1) >= 65536 + 2048 * 80 * 2
+    assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 512, 1152, p1, 1) == 0
+    assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 2048, 1152, p1, 1) == 0
     assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_F32, 8, 256, [_proj(N=256)], 1) == 0
     assert B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, 0, 1152, p1, 1) == 0
     assert B.aq_workspace_bytes(B.AQ_OP_FP4, B.AQ_BF16, 0, 1152, p1, 1) == 65536 + 4096
