@@ -332,7 +332,9 @@ def summarize_profiles(args):
             calls, cur = collections.defaultdict(list), []
             for k in seq:
                 cur.append(k)
-                if mode(k[0]) == 0 or (k[0] == "k_prefill_reduce" and any(mode(c[0]) == 1 for c in cur)):
+                # a call ends with its main pass (MODE 0, or 3: tiles with their
+                # own t), or with the fold after a K-split main pass (MODE 1)
+                if mode(k[0]) in (0, 3) or (k[0] == "k_prefill_reduce" and any(mode(c[0]) == 1 for c in cur)):
                     calls[tuple((c[0], c[1]) for c in cur)].append([c[2] for c in cur])
                     cur = []
             out.append("")

@@ -7,14 +7,19 @@
 //     y[:, col_b + n]   = s_b[n] * (x W0_b^T)[:, n] + (t U_b^T)[:, n]
 // The pages run this as stock GEMMs (one over [W0^T, V], one block-diagonal
 // up-projection) plus an elementwise combine.  Here:
-// * the rank-r pass, t = x [Vt_q; Vt_k; ...]^T for every block of the dispatch,
-//   is the same GEMM on small tiles.  Where its tiles fit in the CU slots the
-//   main pass leaves free, it runs in the first workgroups of the main pass's
-//   own launch: they publish t (bf16) with device-coherent stores and count
-//   themselves in the workspace; the main tiles wait for the count only before
-//   they first read t, near the end of their K loop.  Otherwise it is a launch
-//   of its own, K-split over enough workgroups for long K, with a small kernel
-//   folding the fp32 partials (in split order) into the bf16 t buffer;
+// * where one round of tiles covers the output (few, latency-bound tiles) and
+//   r <= 64, each tile computes its own rows of t: its block's Vt rows ride in
+//   every LDS stage next to its W0 rows (the concatenated [W0^T, V] GEMM per
+//   tile), and t goes from the accumulators to LDS, never to memory;
+// * else the rank-r pass, t = x [Vt_q; Vt_k; ...]^T for every block of the
+//   dispatch, is the same GEMM on small tiles.  Where its tiles fit in the CU
+//   slots the main pass leaves free, it runs in the first workgroups of the
+//   main pass's own launch: they publish t (bf16) with device-coherent stores
+//   and count themselves in the workspace; the main tiles wait for the count
+//   only before they first read t, near the end of their K loop.  Otherwise it
+//   is a launch of its own, K-split over enough workgroups for long K, with a
+//   small kernel folding the fp32 partials (in split order) into the bf16 t
+//   buffer;
 // * the main pass: the W0 contraction, then an in-register epilogue: acc *= s[n]
 //   once, then acc += t U^T as further MFMA k-steps over rank chunks that were
 //   loaded into the LDS ring like K slices (t where x goes, U where W0 goes),
