@@ -151,8 +151,11 @@ template <int BM, int BN, int BK, int NST, int MODE, int NW>
 __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a, const int unit, uint16_t *const st0,
                                                                uint16_t *const st1, uint16_t *const st2,
                                                                uint16_t *const st3, float *const s_lds) {
-  constexpr int WGN = NW / 2;                      // waves along N
-  constexpr int WM = BM / 2, WN = BN / WGN;        // wave tile
+  // Waves in a 2 x (NW / 2) grid, or NW x 1 where BN does not split into
+  // 32-multiples over NW / 2 wave columns (BN = 96).
+  constexpr int WGM = (BN / (NW / 2)) % 32 == 0 ? 2 : NW;
+  constexpr int WGN = NW / WGM;                    // waves along N
+  constexpr int WM = BM / WGM, WN = BN / WGN;      // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;        // 32x32 MFMA tiles per wave
   constexpr bool SELF = MODE == MODE_SELF;
   constexpr int RT = SELF ? 64 : 0;                // Vt rows per stage (the tile's own t, r <= 64)
@@ -163,10 +166,10 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   constexpr int LA = BM / (NW * RPL), LB = BN / (NW * RPL);   // loads per wave per stage
   constexpr int LT = RT / (NW * RPL);
   constexpr int LPS = LA + LB + LT;
-  static_assert(!SELF || (NW == 4 && TNT == 1 && LT * NW * RPL == RT), "own-t tiles: four waves, 64 Vt rows");
+  static_assert(!SELF || (NW == 4 && TNT >= 1 && LT * NW * RPL == RT), "own-t tiles: four waves, 64 Vt rows");
   static_assert(!SELF || 64 / BK <= (64 * (BN + 8) <= (BM + BN + RT) * BK ? NST - 1 : NST - 2),
                 "own-t tiles: every rank chunk of t rides the ring");
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must be a multiple of 64");
+  static_assert(BM % 64 == 0 && BN % 32 == 0 && WM % 32 == 0, "tile must be a multiple of 64 x 32");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(WN % 32 == 0 && LA * NW * RPL == BM && LB * NW * RPL == BN, "wave tiles and loads must divide the tile");
   static_assert(BK == 32 || BK == 64, "K slice of 32 or 64");
@@ -330,7 +333,7 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   const int nchunk = SELF ? (nchunk1 < 64 / BK ? nchunk1 : 64 / BK) : nchunk1 * tparts;
   // ... riding on the tail slices (all but the last, or all but the last two
   // when the output block needs two stages for staging)
-  constexpr int ESLOTS = 64 * (BN + 8) <= STAGE ? NST - 1 : NST - 2;
+  constexpr int ESLOTS = WGM * 32 * (BN + 8) <= STAGE ? NST - 1 : NST - 2;
   const int nech = addu ? min(nchunk, ESLOTS) : 0;
   // TAIL: the step may issue a slice past nkp (a rank chunk); only the last
   // NST steps can, so the others are compiled without that selection.
@@ -510,8 +513,10 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   // rank-r pass (MODE_RAW) writes acc itself (no s, no w).
   constexpr int OP = BN + 8;                     // staging row pitch (bank spread, 16-byte rows)
   // Output staging: wave row 0's 32 rows in ost0, wave row 1's in ost1 (the
-  // last stage holds both when it can, else the last two stages).
+  // last stage holds both when it can, else the last two stages); with NW wave
+  // rows, row w's in the last stage at 32 w rows.
   static_assert(32 * OP <= STAGE && ESLOTS >= 1, "staging and one rank chunk must fit");
+  static_assert(WGM == 2 || WGM * 32 * OP <= STAGE, "four wave rows stage in one LDS stage");
   uint16_t *const slast = NST == 2 ? st1 : (NST == 3 ? st2 : st3);
   uint16_t *const sprev = NST == 2 ? st0 : (NST == 3 ? st1 : st2);
   uint16_t *const ost0 = ESLOTS == NST - 1 ? slast : sprev;
@@ -528,23 +533,25 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
     // This wave's block of t, rounded to bf16, goes where the rank chunks'
     // t rows sit (chunk c = ranks BK c .. in stage c, x rows, same swizzle);
     // U came with the ring.  Lane: row wm * WM + 32 i + l32, ranks
-    // wn * 32 + 8 g + 4 lhi + (0..3).
+    // wn * RT / WGN + 32 jt + 8 g + 4 lhi + (0..3).
     if (addu) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j0 = wn * 32 + 8 * g, c = j0 / BK;
-        if (c >= nchunk) continue;
-        uint16_t *const stc = c == 0 ? st0 : st1;
+      for (int jt = 0; jt < TNT; ++jt)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int R = wm * WM + i * 32 + l32;
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          const bf16x4 h = {(__bf16)acct[i][0][4 * g + 0], (__bf16)acct[i][0][4 * g + 1], (__bf16)acct[i][0][4 * g + 2],
-                            (__bf16)acct[i][0][4 * g + 3]};
-          *reinterpret_cast<uint2 *>(stc + R * BK + 8 * (((j0 % BK) / 8) ^ sw(R)) + 4 * lhi) =
-              __builtin_bit_cast(uint2, h);
+        for (int g = 0; g < 4; ++g) {
+          const int j0 = wn * (RT / WGN) + jt * 32 + 8 * g, c = j0 / BK;
+          if (c >= nchunk) continue;
+          uint16_t *const stc = c == 0 ? st0 : st1;
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const int R = wm * WM + i * 32 + l32;
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            const bf16x4 h = {(__bf16)acct[i][jt][4 * g + 0], (__bf16)acct[i][jt][4 * g + 1],
+                              (__bf16)acct[i][jt][4 * g + 2], (__bf16)acct[i][jt][4 * g + 3]};
+            *reinterpret_cast<uint2 *>(stc + R * BK + 8 * (((j0 % BK) / 8) ^ sw(R)) + 4 * lhi) =
+                __builtin_bit_cast(uint2, h);
+          }
         }
-      }
     }
     __syncthreads();
   }
@@ -616,7 +623,7 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   // and stored after round i's writes, so no wait sits between an LDS access
   // and its use, and no workgroup barrier is needed.
   constexpr int NSC = WN / 16;                     // 16-byte pieces per lane and round
-  uint16_t *const ost = wm ? ost1 : ost0;
+  uint16_t *const ost = WGM == 2 ? (wm ? ost1 : ost0) : slast + wm * 32 * OP;
   uint4 pend[NSC];
   auto stage_read = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -717,7 +724,7 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
 template <int BM, int BN, int BK, int NST, int NW>
 struct TPass {
   static constexpr bool ok = (NW == 8 && BM == 256 && BN == 256 && BK == 32 && NST == 4) ||
-                             (NW == 4 && ((BM == 256 && BN == 128) || (BM == 128 && BN == 128 && NST == 4) ||
+                             (NW == 4 && ((BM == 256 && BN == 128) || (BM == 128 && (BN == 128 || BN == 96) && NST == 4) ||
                                           (BM == 64 && BN == 64 && BK == 64)));
   static constexpr int tBM = NW == 8 ? 128 : 64, tBN = tBM, tBK = 64, tNST = NST;
 };
@@ -807,7 +814,8 @@ struct Cand {
 static const Cand kCands[] = {{128, 128, 64, 4, 4}, {256, 128, 32, 3, 4}, {256, 128, 64, 3, 4}, {256, 256, 32, 4, 4},
                                {256, 256, 64, 2, 4}, {256, 256, 32, 4, 8}, {256, 256, 64, 2, 8}, {128, 256, 64, 3, 4},
                                {128, 128, 64, 2, 4}, {128, 256, 32, 3, 4}, {128, 128, 32, 4, 4}, {64, 64, 64, 4, 4},
-                               {64, 128, 64, 4, 4},  {128, 64, 64, 4, 4},  {128, 128, 64, 3, 4}};
+                               {64, 128, 64, 4, 4},  {128, 64, 64, 4, 4},  {128, 128, 64, 3, 4},  {128, 96, 64, 4, 4},
+                               {128, 96, 64, 3, 4}};
 
 // Main-pass tile and K split.  The tile comes from a cost model fitted to
 // sweeps over the Gemma-3-1B and large-decoder prefill shapes on MI355X: a
@@ -820,13 +828,18 @@ static const Cand kCands[] = {{128, 128, 64, 4, 4}, {256, 128, 32, 3, 4}, {256, 
 //   tiles (the Gemma-3-1B QKV and o projections at M = 512): 64 x 64 tiles,
 //   four stages, no K split (they cover four times as many CUs, and a tile's
 //   K loop, bound by load latency there, runs a quarter of the bytes);
-// * K <= 2048 and at most one round of 128 x 128 tiles (the Gemma-3-1B QKV
-//   and o projections at M = 2048): 128 x 128 with 64-wide slices in three
-//   stages that compute their own rows of t (r <= 64), else with 32-wide
-//   slices, two workgroups per CU, so that the rank-r pass tiles fit beside
-//   them in the same launch;
+// * K <= 2048 and at most one round of 128 x 128 tiles: where they cover
+//   more than half of the CUs and r <= 64 (the Gemma-3-1B QKV and o
+//   projections at M = 2048), tiles with 64-wide slices that compute their own
+//   rows of t, 128 x 96 where those still fit in one round (o), else 128 x 128
+//   in three stages (QKV); otherwise 128 x 128 with 32-wide slices, two
+//   workgroups per CU, so that the rank-r pass tiles fit beside them in the
+//   same launch (fewer tiles: M = 1024 measured faster so);
 // * else the cheapest of the four by the model; 128 x 128 splits long K
-//   (>= 4096) when its tiles cover at most half of the CUs (ranges >= 2048).
+//   (>= 4096) when its tiles cover at most half of the CUs (ranges >= 2048),
+//   else becomes 128 x 96 (four waves in a column) where those still fit in
+//   one round and cover more CUs (Gemma-3-1B down at M = 2048: 192 tiles
+//   instead of 144, 61 us instead of 70).
 struct Est {
   TileCfg tc;
   int slots;
@@ -846,7 +859,10 @@ TileCfg choose(const Recon &rq) {
   if (t128 <= 16 || (rq.K <= 2048 && count_tiles(rq, 64, 64, false) <= kNumCU)) {
     tc = {64, 64, 64, 4, 1, 4};
   } else if (rq.K <= 2048 && t128 <= kNumCU) {
-    tc = own_t ? TileCfg{128, 128, 64, 3, 1, 4} : TileCfg{128, 128, 32, 4, 1, 4};
+    if (own_t && 2 * t128 > kNumCU)
+      tc = count_tiles(rq, 128, 96, false) <= kNumCU ? TileCfg{128, 96, 64, 4, 1, 4} : TileCfg{128, 128, 64, 3, 1, 4};
+    else
+      tc = {128, 128, 32, 4, 1, 4};
   } else {
     double best = 1e30;
     for (const Est &e : kEst) {
@@ -858,6 +874,8 @@ TileCfg choose(const Recon &rq) {
     if (tc.BM == 128 && rq.K >= 4096 && 2 * t128 <= kNumCU) {
       const int S = kNumCU / t128, smax = (int)(rq.K / 2048);
       tc.S = S < smax ? S : smax;
+    } else if (tc.BM == 128 && tc.BN == 128 && t128 < kNumCU && count_tiles(rq, 128, 96, false) <= kNumCU) {
+      tc = {128, 96, 64, 4, 1, 4};
     }
   }
   // Tuning overrides (profiling sweeps): AQ_PREFILL_BM/BN/BK/NST pick a compiled
@@ -904,7 +922,7 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
   // launch, its ramp and the fold of a K split less.
   const bool fusable =
       (tc.NW == 8 && tc.BM == 256 && tc.BN == 256 && tc.BK == 32 && tc.NST == 4) ||
-      (tc.NW == 4 && ((tc.BM == 256 && tc.BN == 128) || (tc.BM == 128 && tc.BN == 128 && tc.NST == 4) ||
+      (tc.NW == 4 && ((tc.BM == 256 && tc.BN == 128) || (tc.BM == 128 && (tc.BN == 128 || tc.BN == 96) && tc.NST == 4) ||
                       (tc.BM == 64 && tc.BN == 64 && tc.BK == 64)));
   // Under a main-pass K split the rank-r tiles run over the same K ranges and
   // keep one t per range (each main unit adds its own range's rank term).
@@ -915,16 +933,20 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
   const int to = env_int("AQ_TPASS_S", 0);
   pl->fuse = 0;
   pl->tparts = 1;
-  // 64 x 64 tiles (few, latency-bound tiles) compute their own rows of t: the
-  // Vt rows of their block (r <= 64) ride in every LDS stage as 64 more B rows,
-  // so t never goes through memory and no tile waits for another; the extra
-  // MFMAs cost little where each K slice waits for its loads anyway.
+  // The tile shapes chosen for one round of few, latency-bound tiles with
+  // K <= 2048 compute their own rows of t: the Vt rows of their block (r <= 64)
+  // ride in every LDS stage as 64 more B rows, so t never goes through memory
+  // and no tile waits for another; the extra MFMAs cost little where each K
+  // slice waits for its loads anyway (with long K they do not: down at
+  // M = 2048 took 79 us so against 61 with the rank-r pass).
   int rmax = 0;
   for (int b = 0; b < rq.nblk; ++b) rmax = rq.blk[b].r > rmax ? (int)rq.blk[b].r : rmax;
   const bool self_tile = tc.NW == 4 && ((tc.BM == 64 && tc.BN == 64 && tc.BK == 64 && tc.NST == 4) ||
                                          (tc.BM == 128 && tc.BN == 128 && tc.BK == 32 && tc.NST == 4) ||
-                                         (tc.BM == 128 && tc.BN == 128 && tc.BK == 64 && tc.NST == 3));
-  pl->self = c > 0 && self_tile && tc.S == 1 && rmax <= 64 && to <= 1 && env_int("AQ_PREFILL_SELF", 1) != 0;
+                                         (tc.BM == 128 && tc.BN == 128 && tc.BK == 64 && tc.NST == 3) ||
+                                         (tc.BM == 128 && tc.BN == 96 && tc.BK == 64 && tc.NST >= 3));
+  pl->self = c > 0 && self_tile && tc.S == 1 && rq.K <= 2048 && rmax <= 64 && to <= 1 &&
+             env_int("AQ_PREFILL_SELF", 1) != 0;
   if (c > 0 && !pl->self && fusable && to <= 1 && env_int("AQ_PREFILL_FUSE", 1) != 0) {
     const int tb = tc.NW == 8 ? 128 : 64;              // the shape TPass gives
     const int slots = kNumCU * ((tc.BM + tc.BN) * tc.BK * 2 * tc.NST <= 80 * 1024 ? 2 : 1);
@@ -983,6 +1005,8 @@ static bool launch_tile(int BM, int BN, int BK, int NST, int NW, const PfArgs &a
     AQ_TILE(64, 64, 64, 4, 4)
     AQ_TILE(128, 128, 32, 4, 4)
     AQ_TILE(128, 128, 64, 3, 4)
+    AQ_TILE(128, 96, 64, 4, 4)
+    AQ_TILE(128, 96, 64, 3, 4)
   } else {
     AQ_TILE(256, 256, 32, 4, 4)
     AQ_TILE(256, 256, 64, 2, 4)
@@ -992,6 +1016,8 @@ static bool launch_tile(int BM, int BN, int BK, int NST, int NW, const PfArgs &a
     AQ_TILE(128, 256, 64, 3, 4)
     AQ_TILE(128, 128, 64, 2, 4)
     AQ_TILE(128, 128, 64, 3, 4)
+    AQ_TILE(128, 96, 64, 4, 4)
+    AQ_TILE(128, 96, 64, 3, 4)
     AQ_TILE(128, 128, 64, 4, 4)
     AQ_TILE(256, 128, 32, 3, 4)
     AQ_TILE(128, 256, 32, 3, 4)

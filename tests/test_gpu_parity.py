@@ -165,7 +165,8 @@ _PREFILL_MODES = [None, (256, 256, 32, 4, 1, None), (256, 256, 64, 2, 1, None), 
                   (256, 256, 32, 4, 3, 2), (256, 256, 64, 2, 3, 2), (256, 128, 64, 3, 2, None),
                   (256, 128, 32, 3, 1, None), (128, 256, 32, 3, 2, 1), (128, 128, 32, 4, 1, None),
                   (64, 64, 64, 4, 1, None), (64, 128, 64, 4, 2, None), (128, 64, 64, 4, 1, 3),
-                  (256, 256, 32, 4, 1, None, 8), (256, 256, 64, 2, 1, None, 8), (256, 256, 32, 4, 2, 2, 8)]
+                  (256, 256, 32, 4, 1, None, 8), (256, 256, 64, 2, 1, None, 8), (256, 256, 32, 4, 2, 2, 8),
+                  (128, 96, 64, 4, 1, None), (128, 96, 64, 4, 3, None), (128, 96, 64, 4, 1, 2)]
 
 
 @pytest.mark.parametrize("M", [65, 300, 513])
@@ -217,7 +218,7 @@ def test_prefill_high_rank(M, r, tile, monkeypatch):
 @pytest.mark.parametrize("M", [300, 700])
 @pytest.mark.parametrize("K", [1048, 3000])
 @pytest.mark.parametrize("S", [1, 3])
-@pytest.mark.parametrize("tile", [(128, 128, 64, 4, 4), (256, 128, 32, 3, 4), (256, 256, 32, 4, 8)], ids=str)
+@pytest.mark.parametrize("tile", [(128, 128, 64, 4, 4), (128, 96, 64, 4, 4), (256, 128, 32, 3, 4), (256, 256, 32, 4, 8)], ids=str)
 def test_prefill_rank_pass_in_main_launch(M, K, S, tile, monkeypatch):
     """The rank-r pass run by the first workgroups of the main-pass launch
     (these shapes leave free slots in the last round), with K short and long
@@ -270,13 +271,15 @@ def test_prefill_rank_pass_in_parts(M, K, parts, monkeypatch):
 
 
 @pytest.mark.parametrize("M", [65, 130, 300])
-@pytest.mark.parametrize("K", [200, 1048, 3000])
-@pytest.mark.parametrize("tile", [(64, 64, 64, 4), (128, 128, 32, 4), (128, 128, 64, 3)])
+@pytest.mark.parametrize("K", [200, 1048, 2000])
+@pytest.mark.parametrize("tile", [(64, 64, 64, 4), (128, 128, 32, 4), (128, 128, 64, 3), (128, 96, 64, 4),
+                                  (128, 96, 64, 3)])
 def test_prefill_own_t(M, K, tile, monkeypatch):
     """Main tiles that compute their own rows of t (Vt rows as more B rows of
-    every stage, t rounded to bf16 in LDS, one or two rank chunks): r = 64,
-    r = 16, r = 36 (U rows not 16-byte aligned: the per-round path with t from
-    LDS), a block without rank; nothing in the workspace."""
+    every stage, t rounded to bf16 in LDS, one or two rank chunks; K <= 2048):
+    r = 64, r = 16, r = 36 (U rows not 16-byte aligned: the per-round path
+    with t from LDS), a block without rank; nothing in the workspace.  Two or
+    four wave rows (128 x 96: one wave column, two t blocks per wave)."""
     for k, v in zip(("BM", "BN", "BK", "NST", "W"), tuple(tile) + (4,)):
         monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
     shapes = [(300, 64), (200, 16), (136, 36), (72, 0)]
