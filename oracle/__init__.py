@@ -16,8 +16,9 @@ passage it follows:
 * ``rounding``  -- single round-to-nearest-even of an fp64 result onto the bf16 /
                    fp32 / E4M3 / E2M1 grids, written from the formats' definitions.
 * ``fp4``       -- the block-16 FP4 container
-                   ("Internals and extension" §Nvfp4Spec) and the quantisation
-                   recipe read into it.  PARITY UNPINNED BY THE PAGES for the
+                   ("Internals and extension" §Nvfp4Spec), the quantisation
+                   recipe read into it, and the product of activations with the
+                   dequantised weight (the FP4 decode GEMV).  PARITY UNPINNED BY THE PAGES for the
                    recipe's constants and tie rules: the pages give only the
                    container; the recipe is pinned by self-consistency, exact
                    brute force and the format tables.
@@ -29,13 +30,13 @@ passage it follows:
 from .recon import recon_linear, recon_fused, recon_blockdiag, materialize
 from .rounding import rne_bf16, rne_f32, rn_f32_exact
 from .fp4 import (E2M1_VALUES, e2m1_decode, e4m3fn_decode, e4m3fn_encode_rne_sat,
-                  e2m1_rne_sat, fp4_pack, fp4_unpack, global_scale, FP4_BLOCK)
+                  e2m1_rne_sat, fp4_pack, fp4_unpack, fp4_linear, global_scale, FP4_BLOCK)
 from .decompose import lsq_row_scale, decompose, band_of_layer, band_means
 
 __all__ = [
     "recon_linear", "recon_fused", "recon_blockdiag", "materialize",
     "rne_bf16", "rne_f32", "rn_f32_exact",
     "E2M1_VALUES", "e2m1_decode", "e4m3fn_decode", "e4m3fn_encode_rne_sat",
-    "e2m1_rne_sat", "fp4_pack", "fp4_unpack", "global_scale", "FP4_BLOCK",
+    "e2m1_rne_sat", "fp4_pack", "fp4_unpack", "fp4_linear", "global_scale", "FP4_BLOCK",
     "lsq_row_scale", "decompose", "band_of_layer", "band_means",
 ]

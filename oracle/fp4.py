@@ -165,3 +165,21 @@ def fp4_unpack(packed, scales, g):
     codes[:, 1::2] = packed >> 4
     D = rne_f32(float(g) * e4m3fn_decode(np.asarray(scales, dtype=np.int64)))
     return e2m1_decode(codes) * np.repeat(D, FP4_BLOCK, axis=1)
+
+
+def fp4_linear(x, packed, scales, g):
+    """y = x Wq^T, float64 [M, N], with Wq the dequantised block-16 FP4 weight.
+
+    The decode GEMV over a quantised effective weight: "Execution paths"
+    §Precompute-outside quantises each W_eff at load and the forward pass then
+    uses it in place of the dense weight; the container is "Internals and
+    extension" §Nvfp4Spec.  Each weight's value is its E2M1 code's value times
+    its block's step ``RN_f32(g * E4M3(scale))`` (``fp4_unpack``); the product with
+    ``x`` ([M, K], bf16 values as float64) is exact in float64 up to the
+    summation's rounding.  No rounding of the result.
+    """
+    Wq = fp4_unpack(packed, scales, g)
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim != 2 or x.shape[1] != Wq.shape[1]:
+        raise ValueError("x must be [M, K] with K = 2 * packed.shape[1]")
+    return x @ Wq.T

@@ -194,3 +194,67 @@ def test_global_scale_exact():
     g = oracle.global_scale(6.0)
     assert g == oracle.rn_f32_exact(Fraction(6, 2688))
     assert abs(g - 6 / 2688) <= 2.0 ** -24 * (6 / 2688)
+
+
+# ------------------------------------------------------------------ FP4 GEMV
+
+_E2M1_BY_FORMAT = {0: 0.0, 1: 0.5, 2: 1.0, 3: 1.5, 4: 2.0, 5: 3.0, 6: 4.0, 7: 6.0}
+
+
+def _fp4_linear_bruteforce(x, packed, scales, g):
+    """Element by element from the container's definition: nibble 2i of byte i
+    is the low one; the code value from the E2M1 table; the block step is the
+    fp32 product of g and the E4M3 scale (torch's float8_e4m3fn decoder)."""
+    N, K2 = packed.shape
+    K = 2 * K2
+    sv = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    y = np.zeros((x.shape[0], N))
+    for n in range(N):
+        for k in range(K):
+            byte = int(packed[n, k // 2])
+            code = (byte >> 4) if k % 2 else (byte & 0xF)
+            val = _E2M1_BY_FORMAT[code & 7] * (-1.0 if code & 8 else 1.0)
+            step = float(np.float32(g) * np.float32(sv[n, k // 16]))
+            for m in range(x.shape[0]):
+                y[m, n] += x[m, k] * (val * step)
+    return y
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_fp4_linear_matches_bruteforce(seed):
+    rng = np.random.default_rng(300 + seed)
+    N, K, M = 5, 48, 3
+    W = rng.standard_normal((N, K)) * np.exp2(rng.uniform(-3, 3, (N, 1)))
+    W = torch.from_numpy(W.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    p, s, g = oracle.fp4_pack(W)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    got = oracle.fp4_linear(x, p, s, g)
+    want = _fp4_linear_bruteforce(x, p, s, g)
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-13)
+
+
+def test_fp4_linear_one_hot_rows_and_error_bound():
+    """A one-hot activation reads one column of the dequantised weight exactly;
+    against the unquantised weight the error stays within sum_k |x_k| times the
+    elementwise dequantisation bound (the block step D)."""
+    rng = np.random.default_rng(44)
+    N, K = 24, 128
+    W = torch.from_numpy(rng.standard_normal((N, K)).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    p, s, g = oracle.fp4_pack(W)
+    Wq = oracle.fp4_unpack(p, s, g)
+    for k in (0, 17, 127):
+        e = np.zeros((1, K))
+        e[0, k] = 1.0
+        assert np.array_equal(oracle.fp4_linear(e, p, s, g)[0], Wq[:, k])
+    x = rng.standard_normal((4, K))
+    D = np.repeat(oracle.rne_f32(g * oracle.e4m3fn_decode(s.astype(np.int64))), 16, axis=1)
+    err = np.abs(oracle.fp4_linear(x, p, s, g) - x @ W.T)
+    assert np.all(err <= np.abs(x) @ D.T)
+
+
+def test_fp4_linear_zero_codes_give_zero():
+    p = np.zeros((3, 16), dtype=np.uint8)
+    s = np.full((3, 2), 0x38, dtype=np.uint8)        # scale 1.0
+    assert not oracle.fp4_linear(np.ones((2, 32)), p, s, 0.5).any()
+    # 0x88: both nibbles are code 8, the negative zero pattern: value 0 too
+    assert not oracle.fp4_linear(np.ones((2, 32)), np.full((3, 16), 0x88, dtype=np.uint8), s, 0.5).any()
