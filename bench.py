@@ -564,13 +564,77 @@ def run_materialize_fp4(args, torch, B, I):
             "fp4_pack": dict(leg(ms_p, pbytes), bytes=pbytes, streams4=leg(ms_p4, pbytes))}
 
 
+def run_fp4_decode(args, torch, B, I):
+    """Gemma-3-1B-shaped decode layer on FP4-packed W_eff: the four dispatches
+    (stacked QKV 1536 x 1152, o 1152 x 1024, stacked gate/up 13824 x 1152, down
+    1152 x 6912) per layer, 26 layers, M in {1, 4, 16}; each layer's weights are
+    its own W_eff (materialised from the materialise workload's rank-64
+    bundles in 13 W0 bands) packed on the GPU."""
+    L = 26
+    layer_np = I.layer_bundles("materialize_fp4", I.GEMMA_1B, layers=L, r=64, dtype="bf16", num_bands=13)
+    dev = torch.device("cuda", 0)
+    lib = B.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    groups = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")), ("down", ("down",))]
+    packed = []                        # per layer: [(name, N, K, packed, scales, g)]
+    layer_dev = upload_layers(torch, I, layer_np)
+    for l in range(L):
+        row = []
+        for name, fams in groups:
+            w = torch.cat([B.materialize(layer_dev[l][f]) for f in fams], 0)
+            p, s, g = B.quant_fp4_block16(w)
+            row.append((name, w.shape[0], w.shape[1], p, s, g))
+            del w
+        packed.append(row)
+    del layer_dev
+    torch.cuda.synchronize()
+    Ms = (1, 4, 16)
+    wsz = max(lib.aq_workspace_bytes(B.AQ_OP_FP4_LINEAR, B.AQ_BF16, M, K,
+                                     (B.aq_proj * 1)(B.aq_proj(N, 0, None, None, None, None)), 1)
+              for M in Ms for (_, N, K, _, _, _) in packed[0])
+    ws = torch.zeros(max(wsz, 256), dtype=torch.uint8, device=dev)
+    keep, per_m, gu = [], {}, []
+    for M in Ms:
+        calls = []
+        for l in range(L):
+            for (name, N, K, p, s, g) in packed[l]:
+                x = (torch.randn(M, K, device=dev) * 0.5).to(torch.bfloat16)
+                y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                keep += [x, y]
+                nb = N * K // 2 + N * K // 16 + 4 + M * K * 2 + M * N * 2
+                c = Call(lib.aq_fp4_linear, (M, N, K, x.data_ptr(), K, p.data_ptr(), s.data_ptr(), g.data_ptr(),
+                                             y.data_ptr(), N, ws.data_ptr(), ws.numel(), stream),
+                         nb, 2 * M * N * K, f"fp4lin.L{l}.{name}.M{M}", name)
+                calls.append(c)
+                if name == "gateup":
+                    gu.append(c)
+        per_m[M] = calls
+    res = {}
+    for M in Ms:
+        ms, _ = time_graph(torch, per_m[M], args.steps, args.warmup)
+        nb = sum(c.nbytes for c in per_m[M])
+        res[f"M{M}"] = {"us_per_layer": round(ms * 1e3 / L, 2), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    avg = time_per_launch(torch, gu, args.roofline_reps)
+    gb = gu[0].nbytes
+    return {"workload": "gemma-3-1b-shaped decode on FP4-packed W_eff, 26 layers, M in {1, 4, 16}",
+            "results": res,
+            "dominant": {"kernel": "k_fp4_gemv (stacked gate/up, 13824 x 1152)", "bytes_per_launch_M1": gb,
+                         "avg_launch_us": round(avg * 1e3, 3),
+                         "GBps_M1_bytes": round(gb / (avg * 1e-3) / 1e9, 1),
+                         "frac_hbm_peak": round(gb / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "note": "average over the M = 1, 4 and 16 launches; bytes are the M = 1 launch's "
+                                 "(codes, scales, x, y)"}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gemma_decode",
-                    choices=["gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4", "pmc_probe"])
+                    choices=["gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4", "fp4_decode",
+                             "pmc_probe"])
     ap.add_argument("--summarize", action="store_true",
                     help="summarise rocprofv3 CSVs (--trace, --fetch, --write) instead of running")
     ap.add_argument("--trace")
@@ -600,7 +664,7 @@ def main():
     torch.cuda.set_device(0)
     fn = {"gemma_decode": run_gemma_decode, "gemma_prefill": run_gemma_prefill,
           "large_decoder": run_large_decoder, "materialize_fp4": run_materialize_fp4,
-          "pmc_probe": run_pmc_probe}[args.workload]
+          "fp4_decode": run_fp4_decode, "pmc_probe": run_pmc_probe}[args.workload]
     out = fn(args, torch, B, I)
     print(json.dumps(out), flush=True)
 

@@ -51,7 +51,7 @@ typedef enum aq_status {
 
 typedef enum aq_dtype { AQ_F32 = 0, AQ_BF16 = 1 } aq_dtype;
 
-typedef enum aq_op { AQ_OP_RECON = 0, AQ_OP_FP4 = 1 } aq_op;
+typedef enum aq_op { AQ_OP_RECON = 0, AQ_OP_FP4 = 1, AQ_OP_FP4_LINEAR = 2 } aq_op;
 
 #define AQ_MAX_RANK 256
 
@@ -147,10 +147,31 @@ aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t
                                uint8_t *packed, uint8_t *scales, float *global_scale,
                                void *ws, size_t ws_bytes, void *stream);
 
+/* FP4 decode GEMV over a packed weight: y[m, n] = bf16(sum_k x[m, k] * Wq[n, k])
+ * for m < M <= 16 tokens, where Wq[n, k] = E2M1(code) * RN_f32(g * E4M3(scale))
+ * is the weight that aq_quant_fp4_block16's output stands for ("Execution
+ * paths", section "Precompute-outside": the quantised W_eff replaces the dense
+ * weight; "Internals and extension", section "Nvfp4Spec": the container).
+ *   x       bf16 [M, ldx], ldx >= K, ldx % 8 == 0, 16-byte aligned.
+ *   packed  [N, K/2] bytes (code 2i in the low nibble of byte i), 16-byte aligned;
+ *   scales  [N, K/16] E4M3FN bytes; global_scale: one device float (g).
+ *   y       bf16 [M, ldy], ldy >= N.
+ *   ws      aq_workspace_bytes(AQ_OP_FP4_LINEAR, -, M, K, p = {N, ...}, 1)
+ *           bytes (0 when K is not split; else fp32 partials after the
+ *           reserved region), 256-byte aligned.
+ * Each weight is rounded once to bf16 before the fp32-accumulated MFMA
+ * product (relative error <= 2^-9 per weight).  K % 32 == 0, K >= 32; M > 16
+ * is AQ_ERR_UNSUPPORTED; M == 0 is a no-op.  Asynchronous on `stream`. */
+aq_status aq_fp4_linear(int64_t M, int64_t N, int64_t K, const void *x, int64_t ldx,
+                        const uint8_t *packed, const uint8_t *scales, const float *global_scale,
+                        void *y, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace size in bytes for one call.
  *   AQ_OP_RECON: (dt, M, K, p[0..nproj-1]) exactly as passed to the recon call
  *                (nproj = 1, 3 or 2).
  *   AQ_OP_FP4  : M and dt ignored; p[0].N and K are the weight's shape.
+ *   AQ_OP_FP4_LINEAR: dt ignored; M tokens, p[0].N and K the packed weight's
+ *                shape (nproj = 1).
  * Returns 0 for invalid arguments (the call itself then reports why).
  * Host-only: touches no GPU state. */
 size_t aq_workspace_bytes(aq_op op, aq_dtype dt, int64_t M, int64_t K, const aq_proj *p,

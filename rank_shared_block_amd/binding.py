@@ -19,7 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaq.so")
 AQ_OK, AQ_ERR_INVALID_ARG, AQ_ERR_SHAPE, AQ_ERR_ALIGNMENT = 0, 1, 2, 3
 AQ_ERR_UNSUPPORTED, AQ_ERR_WORKSPACE, AQ_ERR_HIP = 4, 5, 6
 AQ_F32, AQ_BF16 = 0, 1
-AQ_OP_RECON, AQ_OP_FP4 = 0, 1
+AQ_OP_RECON, AQ_OP_FP4, AQ_OP_FP4_LINEAR = 0, 1, 2
 AQ_MAX_RANK = 256
 
 
@@ -56,6 +56,8 @@ def lib():
         L.aq_materialize_weff.restype = ctypes.c_int
         L.aq_quant_fp4_block16.argtypes = [i64, i64, vp, i64, vp, vp, vp, vp, sz, vp]
         L.aq_quant_fp4_block16.restype = ctypes.c_int
+        L.aq_fp4_linear.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, vp, i64, vp, sz, vp]
+        L.aq_fp4_linear.restype = ctypes.c_int
         L.aq_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, P, ctypes.c_int]
         L.aq_workspace_bytes.restype = sz
         L.aq_status_string.argtypes = [ctypes.c_int]
@@ -249,6 +251,33 @@ def quant_fp4_block16(w, workspace=None):
     check(lib().aq_quant_fp4_block16(N, K, _ptr(w), w.stride(0), _ptr(packed), _ptr(scales),
                                      _ptr(g), ws, ws_bytes, _stream()))
     return packed, scales, g
+
+
+def aq_fp4_linear(M, N, K, x, ldx, packed, scales, global_scale, y, ldy, ws, ws_bytes, stream):
+    return lib().aq_fp4_linear(M, N, K, x, ldx, packed, scales, global_scale, y, ldy, ws, ws_bytes, stream)
+
+
+def fp4_linear(x, packed, scales, global_scale, y=None, workspace=None):
+    """y = x Wq^T for a packed weight (quant_fp4_block16's outputs), x bf16
+    [M <= 16, K]; returns bf16 [M, N]."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bfloat16 tensor with unit column stride")
+    M, K = x.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 2 != K or scales.shape != (N, K // 16):
+        raise ValueError("packed must be [N, K/2] and scales [N, K/16]")
+    if not (packed.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("packed and scales must be contiguous")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be 2-D with unit column stride")
+    need = lib().aq_workspace_bytes(AQ_OP_FP4_LINEAR, AQ_BF16, M, K,
+                                    (aq_proj * 1)(aq_proj(N, 0, None, None, None, None)), 1)
+    ws, ws_bytes = (workspace or _WS).get(need, x.device)
+    check(lib().aq_fp4_linear(M, N, K, _ptr(x), x.stride(0), _ptr(packed), _ptr(scales), _ptr(global_scale),
+                              _ptr(y), y.stride(0), ws, ws_bytes, _stream()))
+    return y
 
 
 def hip_runtimes_mapped():

@@ -205,9 +205,54 @@ aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t
   return AQ_OK;
 }
 
+// Shape checks shared by the FP4 GEMV and its workspace query.
+static aq_status check_fp4_linear(int64_t M, int64_t N, int64_t K) {
+  if (M < 0) return fail(AQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+  if (M > 16) return fail(AQ_ERR_UNSUPPORTED, "M = %lld: the FP4 GEMV takes at most 16 tokens", (long long)M);
+  if (N < 1) return fail(AQ_ERR_SHAPE, "N = %lld must be >= 1", (long long)N);
+  if (K < 32) return fail(AQ_ERR_SHAPE, "K = %lld must be >= 32", (long long)K);
+  if (N > kMaxDim || K > kMaxK) return fail(AQ_ERR_UNSUPPORTED, "N or K too large");
+  if (K % 32) return fail(AQ_ERR_ALIGNMENT, "K = %lld must be a multiple of 32", (long long)K);
+  if (N * (K / 2) > kMaxElems) return fail(AQ_ERR_UNSUPPORTED, "packed weight exceeds 2^31-1 bytes");
+  return AQ_OK;
+}
+
+aq_status aq_fp4_linear(int64_t M, int64_t N, int64_t K, const void *x, int64_t ldx, const uint8_t *packed,
+                        const uint8_t *scales, const float *global_scale, void *y, int64_t ldy, void *ws,
+                        size_t ws_bytes, void *stream) {
+  aq_status st = check_fp4_linear(M, N, K);
+  if (st != AQ_OK) return st;
+  if (ldx < K) return fail(AQ_ERR_SHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldx % 8) return fail(AQ_ERR_ALIGNMENT, "ldx = %lld must be a multiple of 8", (long long)ldx);
+  if (ldy < N) return fail(AQ_ERR_SHAPE, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
+  if (M * ldx > kMaxElems || M * ldy > kMaxElems) return fail(AQ_ERR_UNSUPPORTED, "x or y exceeds 2^31-1 elements");
+  if (M == 0) return AQ_OK;
+  if (!x || !y || !packed || !scales || !global_scale) return fail(AQ_ERR_INVALID_ARG, "a data pointer is NULL");
+  if (!aligned(x, 16) || !aligned(packed, 16)) return fail(AQ_ERR_ALIGNMENT, "x and packed must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(y, 2) || !aligned(global_scale, 4))
+    return fail(AQ_ERR_ALIGNMENT, "scales, y or global_scale is not naturally aligned");
+  aq::Fp4LinPlan pl;
+  aq::plan_fp4_linear(M, N, K, &pl);
+  if (pl.ws_bytes > 0) {
+    if (!ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", pl.ws_bytes);
+    if (ws_bytes < pl.ws_bytes) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", pl.ws_bytes, ws_bytes);
+    if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  }
+  hipError_t e = aq::launch_fp4_linear(M, N, K, x, ldx, packed, scales, global_scale, y, ldy, pl, ws,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return AQ_OK;
+}
+
 size_t aq_workspace_bytes(aq_op op, aq_dtype dt, int64_t M, int64_t K, const aq_proj *p,
                           int nproj) {
   if (op == AQ_OP_FP4) return aq::kWsReserved + (size_t)aq::kFp4AmaxBlocks * 4;
+  if (op == AQ_OP_FP4_LINEAR) {
+    if (!p || nproj != 1 || M == 0 || check_fp4_linear(M, p[0].N, K) != AQ_OK) return 0;
+    aq::Fp4LinPlan pl;
+    aq::plan_fp4_linear(M, p[0].N, K, &pl);
+    return pl.ws_bytes;
+  }
   if (op != AQ_OP_RECON || nproj < 1 || nproj > aq::kMaxBlocks || !p) return 0;
   int64_t ntot = 0;
   for (int b = 0; b < nproj; ++b) ntot += p[b].N > 0 ? p[b].N : 0;

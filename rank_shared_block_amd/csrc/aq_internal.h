@@ -97,4 +97,14 @@ constexpr int kFp4AmaxBlocks = 1024;
 hipError_t launch_fp4(int64_t N, int64_t K, const void *w, int64_t ldw, uint8_t *packed,
                       uint8_t *scales, float *gscale, void *ws, hipStream_t st);
 
+// ---- FP4 decode GEMV --------------------------------------------------------------
+struct Fp4LinPlan {
+  int NG, rows, ntiles, S, kchunk;  // 16-row groups and rows per tile, tiles, K splits, K per split
+  size_t ws_bytes;                  // 0 without a K split, else reserved region + fp32 partials
+};
+void plan_fp4_linear(int64_t M, int64_t N, int64_t K, Fp4LinPlan *pl);
+hipError_t launch_fp4_linear(int64_t M, int64_t N, int64_t K, const void *x, int64_t ldx, const uint8_t *packed,
+                             const uint8_t *scales, const float *gscale, void *y, int64_t ldy,
+                             const Fp4LinPlan &pl, void *ws, hipStream_t st);
+
 }  // namespace aq

@@ -1,0 +1,285 @@
+// FP4 decode GEMV: y = bf16(x Wq^T) for up to 16 tokens, where Wq is a weight
+// packed by the block-16 FP4 pack (two E2M1 codes per byte, [N, K/2]; one
+// FP8-E4M3 scale per 16 K-values, [N, K/16]; one fp32 global scale g).
+//
+// What it computes ("Execution paths", section "Precompute-outside": each W_eff
+// is quantised to 4 bits at load and used in place of the dense weight;
+// container from "Internals and extension", section "Nvfp4Spec"): weight (n, k)
+// is E2M1(code) * D, with the block step D = RN_f32(g * E4M3(scale)) of its
+// 16-value block; y[m, n] = sum_k x[m, k] * weight(n, k).
+//
+// Design (MI355X / gfx950): at decode the kernel streams 0.5625 bytes per weight
+// (3.56x fewer than bf16), so it is bound by HBM and by the dequantisation on
+// the VALU, not by the MFMAs.
+// * One 16-byte load per lane brings 32 consecutive codes of one weight row
+//   (four lanes: 128 K-values of the row), plus the row's two block-scale bytes
+//   for them; the tokens' 64 matching bytes of x come in four 16-byte loads.
+// * The codes are dequantised in registers: the E2M1 values' fp32 bits come
+//   from byte-permute table lookups (four codes per v_perm_b32), are multiplied
+//   by the block step (computed exactly as the pack defines it) and rounded once
+//   to bf16, about five VALU operations per weight; the dot products run on
+//   v_mfma_f32_16x16x32_bf16 with the weights as 16-row groups and the tokens as
+//   the other operand (rows of x beyond M are zero registers, not loads).  A
+//   lane's eight codes of one k-step are K positions 32 q + 8 s .. + 7 of its
+//   128 (q = lane / 16, s = the k-step); x is loaded with the same permutation,
+//   so the contraction is unchanged.  Each weight is rounded to bf16 once, a
+//   relative error of at most 2^-9 per weight, inside the bf16 tolerance.
+// * Eight waves per workgroup (two per SIMD), so that one wave's dequantisation
+//   overlaps another's loads.  Buffer resources make rows past N, K past the
+//   range and tokens past M read as zero: the loop is branch-free with two
+//   steps in flight per wave.
+// * Few rows (long K) split K over S workgroups; fp32 partials are added in
+//   split order by a small fold kernel.  Deterministic.
+
+#include <limits.h>
+#include <stdlib.h>
+
+#include "aq_internal.h"
+#include "device_common.h"
+
+namespace aq {
+
+struct F4Args {
+  const uint8_t *packed, *scales;
+  const float *g;
+  const uint16_t *x;
+  uint16_t *y;
+  float *part;            // S > 1: [S][M][N] fp32 partials
+  int M, N, K, ldx, ldy, rows, ntiles, S, kchunk;
+};
+
+
+// E4M3FN byte (sign clear) as fp32: 1 + m/8 times 2^(e - 7), or m/8 * 2^-6.
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// Eight codes (one 32-bit word, code i in bits 4 i .. 4 i + 3) times the block
+// step D, rounded to bf16: one MFMA operand, element i = code i.
+// The E2M1 magnitudes (0, .5, 1, 1.5, 2, 3, 4, 6) are exact in the upper half of
+// an fp32; their two bytes come from byte-permute table lookups (v_perm_b32: a
+// selector byte 0..7 picks a byte of the 8-byte table {s1, s0}), four codes per
+// lookup: bf16 high bytes 00 3F 3F 3F 40 40 40 40, low bytes 00 00 80 C0 00 40
+// 80 C0.  Each value is assembled as fp32 bits, multiplied by D (fp32) and the
+// pair rounded to bf16 at once; the code's sign bit is then moved onto the
+// bf16 sign (a code of -0 gives -0).
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float D) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t mE = w & 0x07070707u, mO = (w >> 4) & 0x07070707u;    // byte j: code 2j, 2j + 1
+  const uint32_t hE = __builtin_amdgcn_perm(0x40404040u, 0x3F3F3F00u, mE);
+  const uint32_t lE = __builtin_amdgcn_perm(0xC0804000u, 0xC0800000u, mE);
+  const uint32_t hO = __builtin_amdgcn_perm(0x40404040u, 0x3F3F3F00u, mO);
+  const uint32_t lO = __builtin_amdgcn_perm(0xC0804000u, 0xC0800000u, mO);
+  const uint32_t sE = (w << 4) & 0x80808080u, sO = w & 0x80808080u;       // sign at bit 7 of byte j
+  uint32_t out[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // fp32 bits: byte 3 = high byte, byte 2 = low byte (selector 0x0C = zero)
+    const uint32_t sel = 0x0C0Cu | ((uint32_t)j << 16) | ((uint32_t)(4 + j) << 24);
+    const float v0 = __uint_as_float(__builtin_amdgcn_perm(hE, lE, sel)) * D;
+    const float v1 = __uint_as_float(__builtin_amdgcn_perm(hO, lO, sel)) * D;
+    const bf16x2 h = {(__bf16)v0, (__bf16)v1};
+    // signs of codes 2j (to bit 15) and 2j + 1 (to bit 31)
+    const uint32_t sg = __builtin_amdgcn_perm(sO, sE, 0x000C000Cu | ((uint32_t)j << 8) | ((uint32_t)(4 + j) << 24));
+    out[j] = __builtin_bit_cast(uint32_t, h) ^ sg;
+  }
+  return as_bf16x8(make_uint4(out[0], out[1], out[2], out[3]));
+}
+
+__device__ __forceinline__ uint32_t bload_u16(__amdgpu_buffer_rsrc_t r, int off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint4 bload_u128(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// NG: 16-row groups per workgroup; PART: fp32 partials of a K split.
+template <int NG, bool PART>
+__global__ __launch_bounds__(512) void k_fp4_gemv(const F4Args a) {
+  constexpr int WAVES = 8, KS = 4, KSTEP = 128, NT = 64 * WAVES;
+  constexpr int SLOT = NG * 256;
+  __shared__ float red[WAVES * SLOT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, q = lane >> 4;
+
+  const int unit = xcd_contiguous_tile(blockIdx.x, a.ntiles * a.S);
+  if (unit < 0) return;
+  const int tile = unit / a.S, p = unit - tile * a.S;
+  const int K = a.K, row0 = tile * a.rows;
+  const int Rv = min(a.rows, a.N - row0);
+  const int kbeg = p * a.kchunk, kend = min(K, kbeg + a.kchunk);
+  const int nsteps = (kend - kbeg + KSTEP - 1) / KSTEP;
+  const float g = *a.g;
+
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.packed + (size_t)row0 * (K / 2), (uint32_t)Rv * (K / 2));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + (size_t)row0 * (K / 16), (uint32_t)Rv * (K / 16));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((a.M - 1) * a.ldx + K) * 2);
+  const int xoff = j16 < a.M ? j16 * a.ldx * 2 : kOOB;
+
+  f32x4 acc[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) acc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One step: 128 K-values; this lane's 32 of them start at k = k0 + 32 q.
+  auto fetch = [&](int st, uint4 (&cd)[NG], uint32_t (&sc)[NG], uint4 (&xd)[KS]) {
+    const int k = kbeg + st * KSTEP + 32 * q;
+    const bool in = st < nsteps && k < kend;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const int r = gi * 16 + j16;
+      cd[gi] = bload_u128(rc, in ? r * (K / 2) + k / 2 : kOOB);
+      sc[gi] = bload_u16(rs, in ? r * (K / 16) + k / 16 : kOOB);
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) xd[s] = bload_u128(rx, in && xoff != kOOB ? xoff + (k + 8 * s) * 2 : kOOB);
+  };
+  auto compute = [&](const uint4 (&cd)[NG], const uint32_t (&sc)[NG], const uint4 (&xd)[KS]) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const float D0 = g * e4m3_value(sc[gi] & 0xFFu), D1 = g * e4m3_value(sc[gi] >> 8);
+      const uint32_t w[4] = {cd[gi].x, cd[gi].y, cd[gi].z, cd[gi].w};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xd[s]), dequant8(w[s], s < 2 ? D0 : D1), acc[gi],
+                                                          0, 0, 0);
+    }
+  };
+
+  // Two register sets in turn; a wave fetches exactly its own steps.
+  const int nmine = wave < nsteps ? (nsteps - 1 - wave) / WAVES + 1 : 0;
+  uint4 ca[NG], cb[NG], xa[KS], xb[KS];
+  uint32_t sa[NG], sb[NG];
+  if (nmine > 0) fetch(wave, ca, sa, xa);
+  int i = 0;
+  for (; i + 2 < nmine; i += 2) {
+    fetch(wave + (i + 1) * WAVES, cb, sb, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ca, sa, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(wave + (i + 2) * WAVES, ca, sa, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cb, sb, xb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (i + 1 < nmine) {
+    fetch(wave + (i + 1) * WAVES, cb, sb, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ca, sa, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cb, sb, xb);
+  } else if (i < nmine) {
+    compute(ca, sa, xa);
+  }
+
+  // Partial sums of the waves added in wave order.  Element v of lane l is
+  // token 4 (l / 16) + v, row l % 16 of its group.
+  {
+    float *slot = red + wave * SLOT;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) slot[(gi * 4 + v) * 64 + lane] = acc[gi][v];
+  }
+  __syncthreads();
+  for (int e = tid; e < a.M * Rv; e += NT) {
+    const int m = e / Rv, nl = e - m * Rv;
+    const int idx = ((nl >> 4) * 4 + (m & 3)) * 64 + ((m >> 2) << 4) + (nl & 15);
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) v += red[w * SLOT + idx];
+    if constexpr (PART)
+      a.part[((size_t)p * a.M + m) * a.N + row0 + nl] = v;
+    else
+      a.y[(size_t)m * a.ldy + row0 + nl] = f2bf(v);
+  }
+}
+
+// y = bf16(sum of the S partials, in split order).
+__global__ __launch_bounds__(256) void k_fp4_fold(const float *part, int S, int M, int N, uint16_t *y, int ldy) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)M * N) return;
+  const int m = (int)(i / N), n = (int)(i - (long)m * N);
+  float s = 0.f;
+  for (int p = 0; p < S; ++p) s += part[((size_t)p * M + m) * N + n];
+  y[(size_t)m * ldy + n] = f2bf(s);
+}
+
+void plan_fp4_linear(int64_t M, int64_t N, int64_t K, Fp4LinPlan *pl) {
+  // Measured on the Gemma-3-1B decode shapes (graph replays over 26 layers):
+  // two workgroups per CU of 32 rows where the rows allow (stacked gate/up
+  // 13824 x 1152: 6.0 us against 7.5 with one of 64 rows), else 16-row
+  // tiles; K is split only where it is long (down, K = 6912: three ranges,
+  // 6.7 us against 7.6 unsplit) -- for K <= 2048 the fold launch costs more than
+  // the split saves (QKV 3.4 us unsplit against 5.3, o 3.0 against 4.8).
+  int NG = 1;
+  for (int ng = 4; ng >= 1; --ng)
+    if ((N + 16 * ng - 1) / (16 * ng) >= 400) { NG = ng; break; }
+  const int ngo = getenv("AQ_FP4_NG") ? atoi(getenv("AQ_FP4_NG")) : 0;   // tuning overrides: AQ_FP4_NG, AQ_FP4_S
+  if (ngo >= 1 && ngo <= 4) NG = ngo;
+  const int tiles = (int)((N + 16 * NG - 1) / (16 * NG));
+  int S = 1;
+  if (K > 2048 && tiles < 200) {
+    S = kNumCU / tiles;
+    const int smax = (int)(K / 1024);
+    S = S < smax ? S : smax;
+    S = S < 16 ? S : 16;
+    S = S > 1 ? S : 1;
+  }
+  const int so = getenv("AQ_FP4_S") ? atoi(getenv("AQ_FP4_S")) : 0;
+  if (so >= 1) S = so;
+  int kchunk = (int)((K + S - 1) / S);
+  kchunk = (kchunk + 127) / 128 * 128;
+  S = (int)((K + kchunk - 1) / kchunk);
+  pl->NG = NG;
+  pl->rows = 16 * NG;
+  pl->ntiles = tiles;
+  pl->S = S;
+  pl->kchunk = kchunk;
+  pl->ws_bytes = S > 1 ? kWsReserved + (size_t)S * M * N * 4 : 0;
+}
+
+template <bool PART>
+static bool launch_ng(const F4Args &a, int NG, int grid, hipStream_t st) {
+  switch (NG) {
+    case 1: hipLaunchKernelGGL((k_fp4_gemv<1, PART>), dim3(grid), dim3(512), 0, st, a); return true;
+    case 2: hipLaunchKernelGGL((k_fp4_gemv<2, PART>), dim3(grid), dim3(512), 0, st, a); return true;
+    case 3: hipLaunchKernelGGL((k_fp4_gemv<3, PART>), dim3(grid), dim3(512), 0, st, a); return true;
+    case 4: hipLaunchKernelGGL((k_fp4_gemv<4, PART>), dim3(grid), dim3(512), 0, st, a); return true;
+  }
+  return false;
+}
+
+hipError_t launch_fp4_linear(int64_t M, int64_t N, int64_t K, const void *x, int64_t ldx, const uint8_t *packed,
+                             const uint8_t *scales, const float *gscale, void *y, int64_t ldy,
+                             const Fp4LinPlan &pl, void *ws, hipStream_t st) {
+  F4Args a = {};
+  a.packed = packed;
+  a.scales = scales;
+  a.g = gscale;
+  a.x = (const uint16_t *)x;
+  a.y = (uint16_t *)y;
+  a.part = pl.S > 1 ? (float *)((char *)ws + kWsReserved) : nullptr;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.ldx = (int)ldx;
+  a.ldy = (int)ldy;
+  a.rows = pl.rows;
+  a.ntiles = pl.ntiles;
+  a.S = pl.S;
+  a.kchunk = pl.kchunk;
+  const int units = pl.ntiles * pl.S;
+  const int grid = 8 * ((units + 7) / 8);
+  const bool ok = pl.S > 1 ? launch_ng<true>(a, pl.NG, grid, st) : launch_ng<false>(a, pl.NG, grid, st);
+  if (!ok) return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.S == 1) return e;
+  const long n = (long)M * N;
+  hipLaunchKernelGGL(k_fp4_fold, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const float *)a.part, pl.S,
+                     (int)M, (int)N, (uint16_t *)y, (int)ldy);
+  return hipGetLastError();
+}
+
+}  // namespace aq

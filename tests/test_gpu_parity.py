@@ -572,3 +572,91 @@ def test_workspace_shared_across_call_kinds():
         p, s, g = B.quant_fp4_block16(w, workspace=ws)
         ep, es, eg = oracle.fp4_pack(down(w))
         assert np.array_equal(p.cpu().numpy(), ep) and float(g.cpu()[0]) == eg
+
+
+# ------------------------------------------------------------- FP4 decode GEMV
+
+def _fp4_weight(N, K, seed):
+    """A seeded bf16 weight (rows of different scales, so block steps vary) and
+    its oracle pack."""
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((N, K)) * K ** -0.5 * np.exp2(rng.uniform(-2, 2, (N, 1)))
+    Wb = torch.from_numpy(W.astype(np.float32)).to(torch.bfloat16)
+    return Wb, oracle.fp4_pack(Wb.double().numpy())
+
+
+def _assert_fp4_parity(got, x, p, s, g, what):
+    """The spec bf16 tolerance, and elementwise the bound this arithmetic
+    allows: each dequantised weight rounded once to bf16 (relative 2^-9 after an
+    fp32 product, 2^-24), exact bf16 x bf16 products, fp32 sums of K terms (at
+    most K 2^-24 of the sum of magnitudes), one bf16 rounding of the output."""
+    ref = oracle.fp4_linear(x, p, s, g)
+    assert rel_err(got, ref) <= 1e-2, what
+    absref = np.abs(np.asarray(x, dtype=np.float64)) @ np.abs(oracle.fp4_unpack(p, s, g)).T
+    K = x.shape[1]
+    bound = 2.0 ** -9 * np.abs(ref) + (2.0 ** -9 + 2.0 ** -23 + K * 2.0 ** -24) * absref * 1.01
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs beyond the derived bound"
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("N,K", [(300, 1152), (72, 96), (1152, 6912), (200, 2016), (4100, 1024)])
+def test_fp4_linear(M, N, K):
+    """FP4 GEMV against the oracle's product with the dequantised weight, from
+    the oracle's pack: short K with a ragged tail step (96), long K split over
+    workgroups with the fold (6912, 2016), wide N with 64-row tiles (4100)."""
+    _, (p, s, g) = _fp4_weight(N, K, 700 + N + K)
+    x = I.activations("test", 710 + M + K, M, K, "bf16")
+    d = dev()
+    y = B.fp4_linear(up(x, "bf16"), torch.from_numpy(p).to(d), torch.from_numpy(s).to(d),
+                     torch.tensor([g], dtype=torch.float32, device=d))
+    _assert_fp4_parity(down(y), x, p, s, g, f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("ng,S", [(1, 1), (2, 1), (3, 1), (4, 1), (1, 5), (3, 2)])
+def test_fp4_linear_tilings(ng, S, monkeypatch):
+    """Every compiled row-group count (16 to 64 rows per workgroup) with and
+    without a K split, on a ragged N."""
+    monkeypatch.setenv("AQ_FP4_NG", str(ng))
+    monkeypatch.setenv("AQ_FP4_S", str(S))
+    N, K, M = 999, 1280, 7
+    _, (p, s, g) = _fp4_weight(N, K, 720 + ng)
+    x = I.activations("test", 721 + S, M, K, "bf16")
+    d = dev()
+    y = B.fp4_linear(up(x, "bf16"), torch.from_numpy(p).to(d), torch.from_numpy(s).to(d),
+                     torch.tensor([g], dtype=torch.float32, device=d))
+    _assert_fp4_parity(down(y), x, p, s, g, f"NG={ng} S={S}")
+
+
+def test_fp4_linear_after_gpu_pack_and_strided_io():
+    """Pack on the GPU, then the GEMV with x and y inside wider buffers (ldx > K,
+    ldy > N): only the addressed columns of y are written."""
+    N, K, M = 640, 1152, 5
+    Wb, (p, s, g) = _fp4_weight(N, K, 733)
+    d = dev()
+    pd, sd, gd = B.quant_fp4_block16(Wb.to(d))
+    assert np.array_equal(pd.cpu().numpy(), p) and float(gd.cpu()[0]) == g
+    x = I.activations("test", 734, M, K, "bf16")
+    xb = torch.zeros((M, K + 64), dtype=torch.bfloat16, device=d)
+    xb[:, :K] = up(x, "bf16")
+    yb = torch.full((M, N + 24), 3.0, dtype=torch.bfloat16, device=d)
+    B.fp4_linear(xb[:, :K], pd, sd, gd, y=yb[:, 8:8 + N])
+    got = down(yb)
+    assert np.all(got[:, :8] == 3.0) and np.all(got[:, 8 + N:] == 3.0)
+    _assert_fp4_parity(got[:, 8:8 + N], x, p, s, g, "strided")
+
+
+def test_fp4_linear_gemma_stacked_gateup_and_limits():
+    """The stacked Gemma-3-1B gate/up weight (13824 x 1152) at M = 16 on
+    sampled output columns; M = 0 is a no-op and M = 17 is refused."""
+    N, K = 13824, 1152
+    Wb, (p, s, g) = _fp4_weight(N, K, 777)
+    d = dev()
+    pd, sd, gd = torch.from_numpy(p).to(d), torch.from_numpy(s).to(d), torch.tensor([g], dtype=torch.float32, device=d)
+    x = I.activations("test", 778, 16, K, "bf16")
+    y = down(B.fp4_linear(up(x, "bf16"), pd, sd, gd))
+    cols = np.random.default_rng(779).choice(N, 512, replace=False)
+    _assert_fp4_parity(y[:, cols], x, p[cols], s[cols], g, "gate/up sampled")
+    assert B.fp4_linear(torch.empty((0, K), dtype=torch.bfloat16, device=d), pd, sd, gd).shape == (0, N)
+    with pytest.raises(B.AQError):
+        B.fp4_linear(up(I.activations("test", 780, 17, K, "bf16"), "bf16"), pd, sd, gd)

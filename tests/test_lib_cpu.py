@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = _declared()
     assert {"aq_recon_linear", "aq_recon_qkv_fused", "aq_recon_gateup_fused",
-            "aq_materialize_weff", "aq_quant_fp4_block16", "aq_workspace_bytes",
+            "aq_materialize_weff", "aq_quant_fp4_block16", "aq_fp4_linear", "aq_workspace_bytes",
             "aq_status_string", "aq_last_error", "aq_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -144,3 +144,25 @@ def test_fp4_argument_errors():
     assert q(ws_bytes=100) == B.AQ_ERR_WORKSPACE
     assert q(packed=FAKE + 4) == B.AQ_ERR_ALIGNMENT
     assert q(scales=None) == B.AQ_ERR_INVALID_ARG
+
+
+def test_fp4_linear_argument_errors_and_workspace():
+    def call(M=1, N=64, K=128, ldx=None, ldy=None, x=FAKE, ptr=FAKE):
+        return B.aq_fp4_linear(M, N, K, x, K if ldx is None else ldx, ptr, ptr, ptr, ptr,
+                               N if ldy is None else ldy, FAKE, 1 << 20, None)
+    assert call(M=17) == B.AQ_ERR_UNSUPPORTED and "16 tokens" in B.last_error()
+    assert call(M=-1) == B.AQ_ERR_INVALID_ARG
+    assert call(K=48) == B.AQ_ERR_ALIGNMENT
+    assert call(K=16) == B.AQ_ERR_SHAPE
+    assert call(N=0) == B.AQ_ERR_SHAPE
+    assert call(ldx=64) == B.AQ_ERR_SHAPE
+    assert call(ldx=132) == B.AQ_ERR_ALIGNMENT
+    assert call(ldy=63) == B.AQ_ERR_SHAPE
+    assert call(M=0, x=None, ptr=None) == B.AQ_OK                 # no-op, nothing inspected
+    assert call(x=None) == B.AQ_ERR_INVALID_ARG
+    assert call(x=FAKE + 8) == B.AQ_ERR_ALIGNMENT
+    ws = lambda M, N, K: B.aq_workspace_bytes(B.AQ_OP_FP4_LINEAR, B.AQ_BF16, M, K, [_proj(N=N)], 1)
+    assert ws(1, 13824, 1152) == 0                                # enough row tiles: no K split
+    big = ws(16, 1152, 6912)                                      # few rows, long K: fp32 partials
+    assert big > 65536 and (big - 65536) % (16 * 1152 * 4) == 0
+    assert ws(17, 64, 128) == 0 and ws(0, 64, 128) == 0
