@@ -627,6 +627,60 @@ def run_fp4_decode(args, torch, B, I):
                                  "(codes, scales, x, y)"}}
 
 
+def run_fold(args, torch, B, I):
+    """The in-graph fold against the factored form, per call: W_eff
+    materialised into scratch every call, then a plain GEMM on it through the
+    same library (s = 1, r = 0), against one factored dispatch; Gemma-3-1B
+    shapes (QKV, o, gate/up, down), rank 64, 26 layers in 13 W0 bands, over M.
+    The crossover M is where the fold starts to win."""
+    L = 26
+    layer_np = I.layer_bundles("materialize_fp4", I.GEMMA_1B, layers=L, r=64, dtype="bf16", num_bands=13)
+    layer_dev = upload_layers(torch, I, layer_np)
+    dev = torch.device("cuda", 0)
+    lib = B.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    groups = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")), ("down", ("down",))]
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    keep, res = [], {}
+    for M in (16, 64, 128, 256, 512, 1024, 2048):
+        fact, fold = [], []
+        for l in range(L):
+            for name, fams in groups:
+                K = I.GEMMA_1B[fams[0]][0]
+                Ns = [I.GEMMA_1B[f][1] for f in fams]
+                Nt = sum(Ns)
+                x = (torch.randn(M, K, device=dev) * 0.5).to(torch.bfloat16)
+                y = torch.empty((M, Nt), dtype=torch.bfloat16, device=dev)
+                ps = [B.make_proj(*layer_dev[l][f]) for f in fams]
+                pa = (B.aq_proj * len(ps))(*ps)
+                fn = {1: lib.aq_recon_linear, 2: lib.aq_recon_gateup_fused, 3: lib.aq_recon_qkv_fused}[len(ps)]
+                fact.append(Call(fn, (B.AQ_BF16, M, K, x.data_ptr(), K, pa, y.data_ptr(), Nt, ws.data_ptr(),
+                                      ws.numel(), stream), 0, 0, f"fact.{name}", name))
+                # fold: every block's W_eff into one stacked scratch weight, then s = 1, r = 0
+                weff = torch.empty((Nt, K), dtype=torch.bfloat16, device=dev)
+                ones = torch.ones(Nt, dtype=torch.bfloat16, device=dev)
+                r0 = 0
+                for p1, n in zip(ps, Ns):
+                    one = (B.aq_proj * 1)(p1)
+                    fold.append(Call(lib.aq_materialize_weff, (B.AQ_BF16, K, one, weff[r0:].data_ptr(), K, stream),
+                                     0, 0, f"fold.mat.{name}", name))
+                    keep.append(one)
+                    r0 += n
+                dp = (B.aq_proj * 1)(B.aq_proj(Nt, 0, weff.data_ptr(), ones.data_ptr(), None, None))
+                fold.append(Call(lib.aq_recon_linear, (B.AQ_BF16, M, K, x.data_ptr(), K, dp, y.data_ptr(), Nt,
+                                                       ws.data_ptr(), ws.numel(), stream), 0, 0, f"fold.gemm.{name}",
+                                 name))
+                keep += [x, y, weff, ones, pa, dp]
+        ms_f, _ = time_graph(torch, fact, args.steps, args.warmup)
+        ms_d, _ = time_graph(torch, fold, args.steps, args.warmup)
+        res[f"M{M}"] = {"factored_us_per_layer": round(ms_f * 1e3 / L, 2), "fold_us_per_layer": round(ms_d * 1e3 / L, 2),
+                        "fold_over_factored": round(ms_d / ms_f, 3)}
+        keep = keep[-8:]
+    cross = next((m for m in (16, 64, 128, 256, 512, 1024, 2048) if res[f"M{m}"]["fold_over_factored"] < 1.0), None)
+    return {"workload": "in-graph fold (materialise every call + GEMM) vs factored, Gemma-3-1B shapes, 26 layers, rank 64",
+            "results": res, "fold_wins_from_M": cross}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -634,7 +688,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gemma_decode",
                     choices=["gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4", "fp4_decode",
-                             "pmc_probe"])
+                             "fold", "pmc_probe"])
     ap.add_argument("--summarize", action="store_true",
                     help="summarise rocprofv3 CSVs (--trace, --fetch, --write) instead of running")
     ap.add_argument("--trace")
@@ -664,7 +718,7 @@ def main():
     torch.cuda.set_device(0)
     fn = {"gemma_decode": run_gemma_decode, "gemma_prefill": run_gemma_prefill,
           "large_decoder": run_large_decoder, "materialize_fp4": run_materialize_fp4,
-          "fp4_decode": run_fp4_decode, "pmc_probe": run_pmc_probe}[args.workload]
+          "fp4_decode": run_fp4_decode, "fold": run_fold, "pmc_probe": run_pmc_probe}[args.workload]
     out = fn(args, torch, B, I)
     print(json.dumps(out), flush=True)
 

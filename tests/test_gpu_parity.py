@@ -660,3 +660,22 @@ def test_fp4_linear_gemma_stacked_gateup_and_limits():
     assert B.fp4_linear(torch.empty((0, K), dtype=torch.bfloat16, device=d), pd, sd, gd).shape == (0, N)
     with pytest.raises(B.AQError):
         B.fp4_linear(up(I.activations("test", 780, 17, K, "bf16"), "bf16"), pd, sd, gd)
+
+
+# ------------------------------------------------------------- in-graph fold
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_fold_path_matches_factored(M):
+    """The in-graph fold composed from the library (W_eff materialised into a
+    stacked scratch weight, then the GEMM with s = 1 and r = 0) against the
+    oracle's factored form: the same y up to the one extra rounding of W_eff."""
+    K = 1152
+    shapes = [(1024, 64), (256, 64), (256, 64)]
+    bds = [I.bundle("test", 9, f, K, n, r, "bf16") for f, (n, r) in zip(("q", "k", "v"), shapes)]
+    d = dev()
+    weff = torch.cat([B.materialize(bundle_up(b, "bf16")) for b in bds], 0)
+    Nt = weff.shape[0]
+    ones = torch.ones(Nt, dtype=torch.bfloat16, device=d)
+    x = I.activations("test", 990 + M, M, K, "bf16")
+    y = B.recon_linear(up(x, "bf16"), (weff, ones, None, None))
+    assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in bds]), "bf16", f"fold M={M}")
