@@ -9,6 +9,7 @@
  *   y     = s * (x W0^T) + (x Vt^T) U^T           (the reconstruction identity)
  *   W_eff = diag(s) W0 + U Vt                     (the effective weight)
  *   FP4   = block-16 E2M1 codes + E4M3 scales + fp32 global scale of W_eff
+ *   y     = x Wq^T                                (decode over the FP4-packed W_eff)
  *
  * Conventions shared by every call
  * --------------------------------
