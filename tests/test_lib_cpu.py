@@ -166,3 +166,21 @@ def test_fp4_linear_argument_errors_and_workspace():
     big = ws(16, 1152, 6912)                                      # few rows, long K: fp32 partials
     assert big > 65536 and (big - 65536) % (16 * 1152 * 4) == 0
     assert ws(17, 64, 128) == 0 and ws(0, 64, 128) == 0
+
+
+def test_prefill_plans_for_the_gemma_shapes():
+    """The planner's choices on the Gemma-3-1B prefill shapes (rank 64), read
+    from the workspace each implies: QKV and o tiles compute their own t (no
+    workspace); gate/up runs the rank-r pass in its launch with one bf16 t
+    [M, 128]; down at M = 512 splits K in three (one t per K range plus fp32
+    partials), at M = 2048 keeps K whole with t in two K parts."""
+    def ws(M, K, ns):
+        arr = (B.aq_proj * len(ns))(*[B.aq_proj(n, r, FAKE, FAKE, FAKE, FAKE) for n, r in ns])
+        return B.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, M, K, arr, len(ns))
+    qkv, o = [(1024, 64), (256, 64), (256, 64)], [(1152, 64)]
+    gateup, down = [(6912, 64), (6912, 64)], [(1152, 64)]
+    for M in (512, 2048):
+        assert ws(M, 1152, qkv) == 0 and ws(M, 1024, o) == 0
+        assert ws(M, 1152, gateup) == 65536 + M * 128 * 2
+    assert ws(512, 6912, down) == 65536 + 512 * 64 * 2 * 3 + 3 * 512 * 1152 * 4
+    assert ws(2048, 6912, down) == 65536 + 2048 * 64 * 2 * 2
