@@ -240,7 +240,10 @@ def cpu_baseline(I, layer_np, shapes, Ms, x_tag, budget_s, layers_sample):
 # --------------------------------------------------------------------------- counters
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-SOURCES = {"decode_gateup": "rank_shared_block_amd/csrc/recon_decode.hip"}
+SOURCES = {"decode_gateup": "rank_shared_block_amd/csrc/recon_decode.hip",
+           "fp4_gemv_gateup": "rank_shared_block_amd/csrc/fp4_gemv.hip"}
+PMC_KERNELS = {"decode_gateup": ("k_decode_bf16", "k_decode_bf16 (fused gate/up)"),
+               "fp4_gemv_gateup": ("k_fp4_gemv<2, false>", "k_fp4_gemv (FP4 stacked gate/up)")}
 
 
 def source_digest(rel):
@@ -288,6 +291,30 @@ def run_pmc_probe(args, torch, B, I):
             assert st == 0
     torch.cuda.synchronize()
     return {"probe": "copy of %d bytes, then 78 fused gate/up decode launches" % CALIB_BYTES}
+
+
+def run_pmc_probe_fp4(args, torch, B, I):
+    """Counter-run workload for the FP4 GEMV: the copy calibration, then 78
+    stacked gate/up launches (13824 x 1152 packed; 26 layers, each its own
+    weight, x M in {1, 4, 16}), eagerly."""
+    dev = torch.device("cuda", 0)
+    src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    N, K = 13824, 1152
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    packs = [B.quant_fp4_block16((torch.randn(N, K, device=dev, generator=g) * K ** -0.5).to(torch.bfloat16))
+             for _ in range(26)]
+    for M in (1, 4, 16):
+        x = (torch.randn(M, K, device=dev, generator=g)).to(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        for l in range(26):
+            B.fp4_linear(x, *packs[l], y=y)
+    torch.cuda.synchronize()
+    return {"probe": "copy of %d bytes, then 78 FP4 stacked gate/up GEMV launches" % CALIB_BYTES}
 
 
 CALIB_BYTES = 256 * 2 ** 20
@@ -350,7 +377,7 @@ def summarize_profiles(args):
             rs = rows(path)
             val = lambda r: float(r.get("Counter_Value", r.get("value", 0)))
             copy = [val(r) for r in rs if "copyBuffer" in r["Kernel_Name"]]
-            dec = [val(r) for r in rs if "k_decode_bf16" in r["Kernel_Name"]]
+            dec = [val(r) for r in rs if PMC_KERNELS[args.traffic_key][0] in r["Kernel_Name"]]
             res[key] = (max(copy) if copy else None, float(np.mean(dec)) if dec else None, len(dec))
         # scale: a copy of CALIB_BYTES reads and writes CALIB_BYTES each
         fscale = CALIB_BYTES / (res["FETCH_SIZE"][0] * 1024)
@@ -361,7 +388,7 @@ def summarize_profiles(args):
         out.append(f"FETCH_SIZE copy calibration: {res['FETCH_SIZE'][0]:.0f} KiB for {CALIB_BYTES} B read "
                    f"(scale {fscale:.4f}); WRITE_SIZE: {res['WRITE_SIZE'][0]:.0f} KiB for {CALIB_BYTES} B written "
                    f"(scale {wscale:.4f}).")
-        out.append(f"k_decode_bf16 (fused gate/up), mean over {res['FETCH_SIZE'][2]} launches: "
+        out.append(f"{PMC_KERNELS[args.traffic_key][1]}, mean over {res['FETCH_SIZE'][2]} launches: "
                    f"fetch {fetch_b/1e6:.3f} MB, write {write_b/1e6:.3f} MB per launch "
                    f"(scaled), total {(fetch_b + write_b)/1e6:.3f} MB.")
         t = {}
@@ -370,9 +397,9 @@ def summarize_profiles(args):
                 t = json.load(f)
         except (OSError, ValueError):
             pass
-        t["decode_gateup"] = {"bytes_per_launch": int(fetch_b + write_b), "fetch_bytes": int(fetch_b),
-                              "write_bytes": int(write_b), "fetch_scale": fscale, "write_scale": wscale,
-                              "source_sha256_16": source_digest(SOURCES["decode_gateup"])}
+        t[args.traffic_key] = {"bytes_per_launch": int(fetch_b + write_b), "fetch_bytes": int(fetch_b),
+                               "write_bytes": int(write_b), "fetch_scale": fscale, "write_scale": wscale,
+                               "source_sha256_16": source_digest(SOURCES[args.traffic_key])}
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(t, f, indent=1)
     print("\n".join(out))
@@ -688,13 +715,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gemma_decode",
                     choices=["gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4", "fp4_decode",
-                             "fold", "pmc_probe"])
+                             "fold", "pmc_probe", "pmc_probe_fp4"])
     ap.add_argument("--summarize", action="store_true",
                     help="summarise rocprofv3 CSVs (--trace, --fetch, --write) instead of running")
     ap.add_argument("--trace")
     ap.add_argument("--calls", action="store_true",
                     help="with --trace: also group the library's prefill kernels into calls")
     ap.add_argument("--fetch")
+    ap.add_argument("--traffic-key", default="decode_gateup", choices=["decode_gateup", "fp4_gemv_gateup"],
+                    help="with --fetch/--write: which kernel's counters to summarise")
     ap.add_argument("--write")
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--roofline-reps", type=int, default=3)
@@ -718,7 +747,8 @@ def main():
     torch.cuda.set_device(0)
     fn = {"gemma_decode": run_gemma_decode, "gemma_prefill": run_gemma_prefill,
           "large_decoder": run_large_decoder, "materialize_fp4": run_materialize_fp4,
-          "fp4_decode": run_fp4_decode, "fold": run_fold, "pmc_probe": run_pmc_probe}[args.workload]
+          "fp4_decode": run_fp4_decode, "fold": run_fold, "pmc_probe": run_pmc_probe,
+          "pmc_probe_fp4": run_pmc_probe_fp4}[args.workload]
     out = fn(args, torch, B, I)
     print(json.dumps(out), flush=True)
 
