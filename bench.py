@@ -242,8 +242,8 @@ def cpu_baseline(I, layer_np, shapes, Ms, x_tag, budget_s, layers_sample):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 SOURCES = {"decode_gateup": "rank_shared_block_amd/csrc/recon_decode.hip",
            "fp4_gemv_gateup": "rank_shared_block_amd/csrc/fp4_gemv.hip"}
-PMC_KERNELS = {"decode_gateup": ("k_decode_bf16", "k_decode_bf16 (fused gate/up)"),
-               "fp4_gemv_gateup": ("k_fp4_gemv<2, false>", "k_fp4_gemv (FP4 stacked gate/up)")}
+PMC_KERNELS = {"decode_gateup": (("k_decode_bf16",), "k_decode_bf16 (fused gate/up)"),
+               "fp4_gemv_gateup": (("k_fp4_gemv", "<2, false>"), "k_fp4_gemv / k_fp4_gemv_m4 (FP4 stacked gate/up)")}
 
 
 def source_digest(rel):
@@ -377,7 +377,7 @@ def summarize_profiles(args):
             rs = rows(path)
             val = lambda r: float(r.get("Counter_Value", r.get("value", 0)))
             copy = [val(r) for r in rs if "copyBuffer" in r["Kernel_Name"]]
-            dec = [val(r) for r in rs if PMC_KERNELS[args.traffic_key][0] in r["Kernel_Name"]]
+            dec = [val(r) for r in rs if all(k in r["Kernel_Name"] for k in PMC_KERNELS[args.traffic_key][0])]
             res[key] = (max(copy) if copy else None, float(np.mean(dec)) if dec else None, len(dec))
         # scale: a copy of CALIB_BYTES reads and writes CALIB_BYTES each
         fscale = CALIB_BYTES / (res["FETCH_SIZE"][0] * 1024)

@@ -161,7 +161,9 @@ aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t
  *           bytes (0 when K is not split; else fp32 partials after the
  *           reserved region), 256-byte aligned.
  * Each weight is rounded once to bf16 before the fp32-accumulated MFMA
- * product (relative error <= 2^-9 per weight).  K % 32 == 0, K >= 32; M > 16
+ * product (relative error <= 2^-8 per weight), except for M <= 4 with K % 64
+ * == 0, where the block step is applied per block after an exact product of the
+ * E2M1 values.  K % 32 == 0, K >= 32; M > 16
  * is AQ_ERR_UNSUPPORTED; M == 0 is a no-op.  Asynchronous on `stream`. */
 aq_status aq_fp4_linear(int64_t M, int64_t N, int64_t K, const void *x, int64_t ldx,
                         const uint8_t *packed, const uint8_t *scales, const float *global_scale,

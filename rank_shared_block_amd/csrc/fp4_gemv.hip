@@ -23,7 +23,9 @@
 //   lane's eight codes of one k-step are K positions 32 q + 8 s .. + 7 of its
 //   128 (q = lane / 16, s = the k-step); x is loaded with the same permutation,
 //   so the contraction is unchanged.  Each weight is rounded to bf16 once, a
-//   relative error of at most 2^-9 per weight, inside the bf16 tolerance.
+//   relative error of at most 2^-8 per weight, inside the bf16 tolerance.
+//   Up to four tokens (K % 64 == 0) take k_fp4_gemv_m4 instead, which needs no
+//   per-weight rounding (below).
 // * Eight waves per workgroup (two per SIMD), so that one wave's dequantisation
 //   overlaps another's loads.  Buffer resources make rows past N, K past the
 //   range and tokens past M read as zero: the loop is branch-free with two
@@ -196,6 +198,139 @@ __global__ __launch_bounds__(512) void k_fp4_gemv(const F4Args a) {
   }
 }
 
+// Up to four tokens: exact per-block scaling.  The x operand is spread over
+// the MFMA's 16 rows so that row 4 t + q holds token t's values only on the K
+// positions of lane group q (zeros elsewhere; the zeros are out-of-range buffer
+// loads).  Each output row of a 16x16x32 MFMA is then the partial sum of one
+// token over one lane group's eight codes -- eight codes of ONE 16-value block
+// -- so the weights enter as their exact E2M1 values (bf16) and the block step
+// D is applied once per block and token by an fp32 FMA: no per-weight
+// multiply or rounding.  Lane (t, n) receives token t's four partials of row n
+// (blocks 2 q + s / 2 of the step, q = 0..3) and adds D[n, block] times each to
+// its one accumulator.  Codes become bf16 pairs through a 256-entry LDS table
+// (one byte, two codes, per lookup); E4M3 scale bytes through another.
+template <int NG, bool PART>
+__global__ __launch_bounds__(512) void k_fp4_gemv_m4(const F4Args a) {
+  constexpr int WAVES = 8, KS = 4, KSTEP = 128, NT = 64 * WAVES;
+  constexpr int SLOT = NG * 64;
+  __shared__ float red[WAVES * SLOT];
+  __shared__ uint32_t code_lut[256];     // byte -> bf16 pair (low nibble in the low half)
+  __shared__ float scale_lut[256];       // E4M3 byte -> g * value (RN_f32)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, q = lane >> 4;
+
+  const int unit = xcd_contiguous_tile(blockIdx.x, a.ntiles * a.S);
+  if (unit < 0) return;
+  const float g = *a.g;
+  if (tid < 256) {
+    auto half = [](uint32_t c) {          // E2M1 code -> bf16 bits (exact)
+      const uint32_t m = c & 7u;
+      const uint32_t mag = m >= 2 ? ((m + 252u) << 6) : (m == 1 ? 0x3F00u : 0u);
+      return mag | ((c & 8u) << 12);
+    };
+    code_lut[tid] = half(tid & 15u) | (half(tid >> 4) << 16);
+    scale_lut[tid] = g * e4m3_value(tid & 0x7Fu);
+  }
+  __syncthreads();
+  const int tile = unit / a.S, p = unit - tile * a.S;
+  const int K = a.K, row0 = tile * a.rows;
+  const int Rv = min(a.rows, a.N - row0);
+  const int kbeg = p * a.kchunk, kend = min(K, kbeg + a.kchunk);
+  const int nsteps = (kend - kbeg + KSTEP - 1) / KSTEP;
+
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.packed + (size_t)row0 * (K / 2), (uint32_t)Rv * (K / 2));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + (size_t)row0 * (K / 16), (uint32_t)Rv * (K / 16));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((a.M - 1) * a.ldx + K) * 2);
+  // x operand row j16 = 4 t + q' carries token t only in lane group q' == q.
+  const int tx = j16 >> 2;
+  const int xoff = ((j16 & 3) == q && tx < a.M) ? tx * a.ldx * 2 : kOOB;
+
+  float acc[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) acc[gi] = 0.f;
+
+  auto fetch = [&](int st, uint4 (&cd)[NG], uint2 (&sc)[NG], uint4 (&xd)[KS]) {
+    const int k0 = kbeg + st * KSTEP, k = k0 + 32 * q;
+    const bool in = st < nsteps && k < kend, in0 = st < nsteps;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const int r = gi * 16 + j16;
+      cd[gi] = bload_u128(rc, in ? r * (K / 2) + k / 2 : kOOB);
+      // the step's eight scale bytes of row r (blocks past K read as zero)
+      const __amdgpu_buffer_rsrc_t rr = rs;
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rr, in0 && k0 < kend ? r * (K / 16) + k0 / 16 : kOOB, 0, 0);
+      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(rr, in0 && k0 + 64 < kend ? r * (K / 16) + k0 / 16 + 4 : kOOB, 0, 0);
+      sc[gi] = make_uint2(lo, hi);
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) xd[s] = bload_u128(rx, in && xoff != kOOB ? xoff + (k + 8 * s) * 2 : kOOB);
+  };
+  auto compute = [&](const uint4 (&cd)[NG], const uint2 (&sc)[NG], const uint4 (&xd)[KS]) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const uint32_t w[4] = {cd[gi].x, cd[gi].y, cd[gi].z, cd[gi].w};
+      float D[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) D[b] = scale_lut[((b < 4 ? sc[gi].x : sc[gi].y) >> (8 * (b & 3))) & 0xFFu];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint32_t ws = w[s];
+        const uint4 wb = make_uint4(code_lut[ws & 0xFFu], code_lut[(ws >> 8) & 0xFFu], code_lut[(ws >> 16) & 0xFFu],
+                                    code_lut[ws >> 24]);
+        const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xd[s]), as_bf16x8(wb),
+                                                                f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[gi] = fmaf(D[2 * v + (s >> 1)], c[v], acc[gi]);
+      }
+    }
+  };
+
+  const int nmine = wave < nsteps ? (nsteps - 1 - wave) / WAVES + 1 : 0;
+  uint4 ca[NG], cb[NG], xa[KS], xb[KS];
+  uint2 sa[NG], sb[NG];
+  if (nmine > 0) fetch(wave, ca, sa, xa);
+  int i = 0;
+  for (; i + 2 < nmine; i += 2) {
+    fetch(wave + (i + 1) * WAVES, cb, sb, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ca, sa, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(wave + (i + 2) * WAVES, ca, sa, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cb, sb, xb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (i + 1 < nmine) {
+    fetch(wave + (i + 1) * WAVES, cb, sb, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ca, sa, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cb, sb, xb);
+  } else if (i < nmine) {
+    compute(ca, sa, xa);
+  }
+
+  // Lane (t, n) holds token t, row n of each group; waves added in order.
+  {
+    float *slot = red + wave * SLOT;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) slot[gi * 64 + lane] = acc[gi];
+  }
+  __syncthreads();
+  for (int e = tid; e < a.M * Rv; e += NT) {
+    const int m = e / Rv, nl = e - m * Rv;
+    const int idx = (nl >> 4) * 64 + m * 16 + (nl & 15);
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) v += red[w * SLOT + idx];
+    if constexpr (PART)
+      a.part[((size_t)p * a.M + m) * a.N + row0 + nl] = v;
+    else
+      a.y[(size_t)m * a.ldy + row0 + nl] = f2bf(v);
+  }
+}
+
 // y = bf16(sum of the S partials, in split order).
 __global__ __launch_bounds__(256) void k_fp4_fold(const float *part, int S, int M, int N, uint16_t *y, int ldy) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -204,6 +339,12 @@ __global__ __launch_bounds__(256) void k_fp4_fold(const float *part, int S, int 
   float s = 0.f;
   for (int p = 0; p < S; ++p) s += part[((size_t)p * M + m) * N + n];
   y[(size_t)m * ldy + n] = f2bf(s);
+}
+
+// The exact per-block kernel for M <= 4 (AQ_FP4_M4=0 selects the other one).
+static bool getenv_m4() {
+  const char *v = getenv("AQ_FP4_M4");
+  return !(v && *v == '0');
 }
 
 void plan_fp4_linear(int64_t M, int64_t N, int64_t K, Fp4LinPlan *pl) {
@@ -242,6 +383,15 @@ void plan_fp4_linear(int64_t M, int64_t N, int64_t K, Fp4LinPlan *pl) {
 
 template <bool PART>
 static bool launch_ng(const F4Args &a, int NG, int grid, hipStream_t st) {
+  if (a.M <= 4 && a.K % 64 == 0 && getenv_m4()) {   // K % 64: the 4-byte scale loads stay aligned
+    switch (NG) {
+      case 1: hipLaunchKernelGGL((k_fp4_gemv_m4<1, PART>), dim3(grid), dim3(512), 0, st, a); return true;
+      case 2: hipLaunchKernelGGL((k_fp4_gemv_m4<2, PART>), dim3(grid), dim3(512), 0, st, a); return true;
+      case 3: hipLaunchKernelGGL((k_fp4_gemv_m4<3, PART>), dim3(grid), dim3(512), 0, st, a); return true;
+      case 4: hipLaunchKernelGGL((k_fp4_gemv_m4<4, PART>), dim3(grid), dim3(512), 0, st, a); return true;
+    }
+    return false;
+  }
   switch (NG) {
     case 1: hipLaunchKernelGGL((k_fp4_gemv<1, PART>), dim3(grid), dim3(512), 0, st, a); return true;
     case 2: hipLaunchKernelGGL((k_fp4_gemv<2, PART>), dim3(grid), dim3(512), 0, st, a); return true;
