@@ -258,3 +258,54 @@ def test_fp4_linear_zero_codes_give_zero():
     assert not oracle.fp4_linear(np.ones((2, 32)), p, s, 0.5).any()
     # 0x88: both nibbles are code 8, the negative zero pattern: value 0 too
     assert not oracle.fp4_linear(np.ones((2, 32)), np.full((3, 16), 0x88, dtype=np.uint8), s, 0.5).any()
+
+
+def _fp4_linear_variants():
+    """Plausible mistakes in the FP4 GEMV, each as a whole function: nibble
+    order swapped, the sign bit ignored, the block step taken per 32 values,
+    the global scale dropped, the weight not transposed (x W instead of x W^T
+    on a square case is still wrong)."""
+    def unpack_with(packed, scales, g, swap=False, nosign=False, block=16, use_g=True):
+        packed = np.asarray(packed, dtype=np.int64)
+        N, K2 = packed.shape
+        codes = np.empty((N, 2 * K2), dtype=np.int64)
+        lo, hi = packed & 0xF, packed >> 4
+        codes[:, 0::2], codes[:, 1::2] = (hi, lo) if swap else (lo, hi)
+        if nosign:
+            codes &= 7
+        sv = oracle.e4m3fn_decode(np.asarray(scales, dtype=np.int64))
+        D = oracle.rne_f32((float(g) if use_g else 1.0) * sv)
+        Dfull = np.repeat(D, 16, axis=1) if block == 16 else np.repeat(D[:, ::2], 32, axis=1)[:, :2 * K2]
+        return oracle.e2m1_decode(codes) * Dfull
+    return {
+        "swapped nibbles": lambda x, p, s, g: x @ unpack_with(p, s, g, swap=True).T,
+        "no sign": lambda x, p, s, g: x @ unpack_with(p, s, g, nosign=True).T,
+        "32-value blocks": lambda x, p, s, g: x @ unpack_with(p, s, g, block=32).T,
+        "no global scale": lambda x, p, s, g: x @ unpack_with(p, s, g, use_g=False).T,
+        "not transposed": lambda x, p, s, g: x @ unpack_with(p, s, g),
+    }
+
+
+def _fp4_pins_hold(fn):
+    """The GEMV pins above, run against `fn`: brute force, one-hot columns."""
+    rng = np.random.default_rng(300)
+    N = K = 32
+    W = rng.standard_normal((N, K)) * np.exp2(rng.uniform(-3, 3, (N, 1)))
+    W = torch.from_numpy(W.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    p, s, g = oracle.fp4_pack(W)
+    x = torch.from_numpy(rng.standard_normal((3, K)).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    try:
+        if not np.allclose(fn(x, p, s, g), _fp4_linear_bruteforce(x, p, s, g), rtol=1e-13, atol=1e-13):
+            return False
+        Wq = oracle.fp4_unpack(p, s, g)
+        e = np.zeros((1, K))
+        e[0, 5] = 1.0
+        return np.array_equal(fn(e, p, s, g)[0], Wq[:, 5])
+    except ValueError:
+        return False
+
+
+def test_fp4_linear_pins_catch_planted_mistakes():
+    assert _fp4_pins_hold(oracle.fp4_linear)
+    for name, fn in _fp4_linear_variants().items():
+        assert not _fp4_pins_hold(fn), f"planted mistake passed the pins: {name}"
