@@ -47,7 +47,9 @@ typedef enum aq_status {
   AQ_ERR_ALIGNMENT = 3,   /* pointer / stride / K not aligned as required      */
   AQ_ERR_UNSUPPORTED = 4, /* valid request outside the library's limits        */
   AQ_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned        */
-  AQ_ERR_HIP = 6          /* the HIP runtime refused a launch                  */
+  AQ_ERR_HIP = 6,         /* the HIP runtime refused a launch                  */
+  AQ_ERR_HANDOFF = 7      /* a prefill launch's wait for t gave up (see
+                             aq_workspace_check)                               */
 } aq_status;
 
 typedef enum aq_dtype { AQ_F32 = 0, AQ_BF16 = 1 } aq_dtype;
@@ -180,8 +182,46 @@ aq_status aq_fp4_linear(int64_t M, int64_t N, int64_t K, const void *x, int64_t 
 size_t aq_workspace_bytes(aq_op op, aq_dtype dt, int64_t M, int64_t K, const aq_proj *p,
                           int nproj);
 
+/* Health check of a workspace after the calls that used it: waits for `stream`
+ * to drain (this call synchronises), then reads the reserved region.
+ *
+ * A prefill launch that also runs the rank-r pass in its first workgroups has
+ * its main tiles wait, before they first read t, for every rank-r workgroup to
+ * count itself in the workspace ("Execution paths", section "The GEMM
+ * formulation": the down-contraction and the up-projection are two dependent
+ * GEMMs; here they meet inside one launch).  That wait is bounded so that a
+ * kernel can never hang: if it ever gives up, the main tiles go on with
+ * whatever t holds and set a flag word in the reserved region.  This call
+ * reports the flag as AQ_ERR_HANDOFF (the outputs of the prefill calls since
+ * the last check are then not valid), and AQ_ERR_WORKSPACE if the counters are
+ * not back at zero (a workspace that was not zero-filled, or shared by calls
+ * that ran concurrently).  In both cases it clears the reserved region, so the
+ * workspace can be used again.  AQ_OK otherwise.  ws must be the workspace
+ * pointer passed to the calls (256-byte aligned); NULL is AQ_OK. */
+aq_status aq_workspace_check(void *ws, void *stream);
+
 const char *aq_status_string(aq_status s);
 const char *aq_last_error(void);
+
+/* Test-only plan overrides, for callers that must force one particular kernel
+ * variant (the parity tests exercise every compiled tile shape, split and mode
+ * this way): the kernel choice of a call otherwise depends only on its
+ * arguments.  The overrides are thread-local, unset until set, and apply to
+ * the calls made on the same thread; values that no compiled variant takes
+ * are ignored by the planner, as if unset.  AQ_DBG_HANDOFF_SPIN bounds the
+ * prefill wait for t to that many polls and AQ_DBG_HANDOFF_UNREACHABLE = 1
+ * makes the awaited count one more than will arrive, so that a test can make
+ * the wait give up from the host while every kernel still exits normally.
+ * aq_debug_force_plan returns AQ_ERR_INVALID_ARG for an unknown knob. */
+typedef enum aq_debug_knob {
+  AQ_DBG_DECODE_SPLIT = 0, AQ_DBG_DECODE_NG, AQ_DBG_DECODE_ROWS, AQ_DBG_DECODE_S, AQ_DBG_DECODE_WAVES,
+  AQ_DBG_PREFILL_BM, AQ_DBG_PREFILL_BN, AQ_DBG_PREFILL_BK, AQ_DBG_PREFILL_NST, AQ_DBG_PREFILL_W,
+  AQ_DBG_PREFILL_S, AQ_DBG_PREFILL_SELF, AQ_DBG_PREFILL_FUSE, AQ_DBG_TPASS_S, AQ_DBG_TPASS_PARTS,
+  AQ_DBG_FP4_NG, AQ_DBG_FP4_S, AQ_DBG_FP4_M4, AQ_DBG_HANDOFF_SPIN, AQ_DBG_HANDOFF_UNREACHABLE,
+  AQ_DBG_COUNT
+} aq_debug_knob;
+aq_status aq_debug_force_plan(aq_debug_knob knob, int64_t value);
+void aq_debug_reset_plan(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int aq_version(void);

@@ -2,10 +2,14 @@
 
 The functions ``aq_*`` mirror the C ABI in ``include/aq.h`` one to one (same
 names, same arguments; device pointers and the stream are plain integers).  The
-tensor helpers below them only turn torch tensors into pointers, strides and the
-current HIP stream and raise ``AQError`` for a non-OK status; every step of the
-computation runs in the library's HIP kernels.  There is no fallback: if the
-library is missing or fails to load, every call raises.
+tensor helpers below them only check that the tensors they are given fit
+together (device, dtype, shape, layout), turn them into pointers, strides and
+the current HIP stream, and raise ``AQError`` for a non-OK status; every step of
+the computation runs in the library's HIP kernels.  ``check_bundles`` and
+``materialize_model`` are the load-time path: every layer's bundle is checked
+against its band's shared block before anything is launched, and one exception
+lists every offending layer.  There is no fallback: if the library is missing
+or fails to load, every call raises.
 """
 
 import ctypes
@@ -17,10 +21,16 @@ import torch   # loaded first: libaq.so then binds to the HIP runtime torch alre
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaq.so")
 
 AQ_OK, AQ_ERR_INVALID_ARG, AQ_ERR_SHAPE, AQ_ERR_ALIGNMENT = 0, 1, 2, 3
-AQ_ERR_UNSUPPORTED, AQ_ERR_WORKSPACE, AQ_ERR_HIP = 4, 5, 6
+AQ_ERR_UNSUPPORTED, AQ_ERR_WORKSPACE, AQ_ERR_HIP, AQ_ERR_HANDOFF = 4, 5, 6, 7
 AQ_F32, AQ_BF16 = 0, 1
 AQ_OP_RECON, AQ_OP_FP4, AQ_OP_FP4_LINEAR = 0, 1, 2
 AQ_MAX_RANK = 256
+
+# Plan overrides (include/aq.h, aq_debug_knob): test-only.
+DEBUG_KNOBS = ("DECODE_SPLIT", "DECODE_NG", "DECODE_ROWS", "DECODE_S", "DECODE_WAVES",
+               "PREFILL_BM", "PREFILL_BN", "PREFILL_BK", "PREFILL_NST", "PREFILL_W",
+               "PREFILL_S", "PREFILL_SELF", "PREFILL_FUSE", "TPASS_S", "TPASS_PARTS",
+               "FP4_NG", "FP4_S", "FP4_M4", "HANDOFF_SPIN", "HANDOFF_UNREACHABLE")
 
 
 class aq_proj(ctypes.Structure):
@@ -66,6 +76,12 @@ def lib():
         L.aq_last_error.restype = ctypes.c_char_p
         L.aq_version.argtypes = []
         L.aq_version.restype = ctypes.c_int
+        L.aq_workspace_check.argtypes = [vp, vp]
+        L.aq_workspace_check.restype = ctypes.c_int
+        L.aq_debug_force_plan.argtypes = [ctypes.c_int, i64]
+        L.aq_debug_force_plan.restype = ctypes.c_int
+        L.aq_debug_reset_plan.argtypes = []
+        L.aq_debug_reset_plan.restype = None
         _lib = L
     return _lib
 
@@ -107,6 +123,23 @@ def aq_workspace_bytes(op, dt, M, K, p, nproj):
     return lib().aq_workspace_bytes(op, dt, M, K, _projs(p, nproj), nproj)
 
 
+def aq_workspace_check(ws, stream):
+    return lib().aq_workspace_check(ws, stream)
+
+
+def aq_debug_force_plan(knob, value):
+    return lib().aq_debug_force_plan(knob, value)
+
+
+def aq_debug_reset_plan():
+    lib().aq_debug_reset_plan()
+
+
+def debug_force_plan(name, value):
+    """Test-only: force one plan knob (a name of DEBUG_KNOBS) on this thread."""
+    check(aq_debug_force_plan(DEBUG_KNOBS.index(name), int(value)))
+
+
 def status_string(s):
     return lib().aq_status_string(s).decode()
 
@@ -144,13 +177,54 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_proj(W0, s, U=None, Vt=None):
-    """aq_proj for one bundle of contiguous device tensors (U [N, r], Vt [r, K])."""
+def _bundle_problems(W0, s, U, Vt, K=None, dtype=None, device=None):
+    """Every way a bundle (W0 [N, K], s [N], U [N, r], Vt [r, K]) fails to fit
+    together or to fit (K, dtype, device); an empty list when it fits."""
+    bad = []
+    if W0 is None or W0.dim() != 2:
+        return ["W0 must be a 2-D tensor [N, K]"]
+    N, K0 = W0.shape
+    if K is not None and K0 != K:
+        bad.append(f"W0 is [{N}, {K0}] but the input has K = {K}")
+    dtype = W0.dtype if dtype is None else dtype
+    device = W0.device if device is None else device
+    r = 0 if U is None else (U.shape[1] if U.dim() == 2 else -1)
+    if s is None or tuple(s.shape) != (N,):
+        bad.append(f"s must be [{N}], got {None if s is None else list(s.shape)}")
+    if (U is None) != (Vt is None):
+        bad.append("U and Vt must both be given or both be None")
+    if U is not None and (U.dim() != 2 or U.shape[0] != N):
+        bad.append(f"U must be [{N}, r], got {list(U.shape)}")
+    if Vt is not None and U is not None and tuple(Vt.shape) != (max(r, 0), K0):
+        bad.append(f"Vt must be [{r}, {K0}] (r from U), got {list(Vt.shape)}")
+    if r > AQ_MAX_RANK:
+        bad.append(f"rank {r} exceeds the supported maximum {AQ_MAX_RANK}")
+    for name, t in (("W0", W0), ("s", s), ("U", U), ("Vt", Vt)):
+        if t is None:
+            continue
+        if t.dtype != dtype:
+            bad.append(f"{name} is {t.dtype}, expected {dtype}")
+        if t.device != device:
+            bad.append(f"{name} is on {t.device}, expected {device}")
+        if t.numel() > 0 and not t.is_contiguous():
+            bad.append(f"{name} must be contiguous")
+    if dtype not in _DT:
+        bad.append(f"dtype {dtype} is not bfloat16 or float32")
+    elif K0 % (8 if dtype == torch.bfloat16 else 4):
+        bad.append(f"K = {K0} must be a multiple of {8 if dtype == torch.bfloat16 else 4} for {dtype}")
+    if device.type != "cuda":
+        bad.append(f"tensors must be on a GPU, got {device}")
+    return bad
+
+
+def make_proj(W0, s, U=None, Vt=None, K=None, dtype=None, device=None):
+    """aq_proj for one bundle of contiguous device tensors (U [N, r], Vt [r, K]);
+    raises ValueError listing every mismatch (shapes, dtype, device, layout)."""
+    bad = _bundle_problems(W0, s, U, Vt, K, dtype, device)
+    if bad:
+        raise ValueError("bundle does not fit: " + "; ".join(bad))
     N = W0.shape[0]
     r = 0 if U is None else U.shape[1]
-    for name, t in (("W0", W0), ("s", s), ("U", U), ("Vt", Vt)):
-        if t is not None and t.numel() > 0 and not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     return aq_proj(N, r, _ptr(W0), _ptr(s), _ptr(U), _ptr(Vt))
 
 
@@ -176,6 +250,15 @@ class Workspace:
             self._buf[key] = buf
         return buf.data_ptr(), buf.numel()
 
+    def check(self, device=None):
+        """aq_workspace_check on this workspace's buffer for `device` (raises
+        AQError for a prefill hand-off that gave up, or dirty counters)."""
+        key = torch.device(device if device is not None else "cuda").index
+        key = torch.cuda.current_device() if key is None else key
+        buf = self._buf.get(key)
+        if buf is not None:
+            check(aq_workspace_check(buf.data_ptr(), _stream()))
+
 
 _WS = Workspace()
 
@@ -184,17 +267,31 @@ def default_workspace():
     return _WS
 
 
+def _check_out(y, M, ncols, x, what="y"):
+    if y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError(f"{what} must be 2-D with unit column stride")
+    if y.shape[0] != M or y.shape[1] < ncols:
+        raise ValueError(f"{what} must be [{M}, >= {ncols}], got {list(y.shape)}")
+    if y.dtype != x.dtype or y.device != x.device:
+        raise ValueError(f"{what} must be {x.dtype} on {x.device}, got {y.dtype} on {y.device}")
+
+
 def _recon(fn, nproj, x, bundles, y, workspace):
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     dt = _dt(x)
-    projs = [make_proj(*b) for b in bundles]
     M, K = x.shape
+    bad = [] if x.device.type == "cuda" else [f"x must be on a GPU, got {x.device}"]
+    for i, b in enumerate(bundles):
+        for msg in _bundle_problems(*b, K=K, dtype=x.dtype, device=x.device):
+            bad.append(f"projection {i}: {msg}")
+    if bad:
+        raise ValueError("; ".join(bad))
+    projs = [make_proj(*b) for b in bundles]
     ntot = sum(p.N for p in projs)
     if y is None:
         y = torch.empty((M, ntot), dtype=x.dtype, device=x.device)
-    if y.dim() != 2 or y.stride(1) != 1:
-        raise ValueError("y must be 2-D with unit column stride")
+    _check_out(y, M, ntot, x)
     arr = (aq_proj * nproj)(*projs)
     need = lib().aq_workspace_bytes(AQ_OP_RECON, dt, M, K, arr, nproj)
     ws, ws_bytes = (workspace or _WS).get(need, x.device)
@@ -225,13 +322,15 @@ def materialize(bundle, out=None):
     """W_eff = diag(s) W0 + U Vt into `out` (a [N, >=K] view with unit column
     stride; allocated when None)."""
     W0 = bundle[0]
+    p = make_proj(*bundle)
     dt = _dt(W0)
     N, K = W0.shape
     if out is None:
         out = torch.empty((N, K), dtype=W0.dtype, device=W0.device)
-    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != N:
-        raise ValueError("out must be [N, >=K] with unit column stride")
-    p = make_proj(*bundle)
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != N or out.shape[1] < K:
+        raise ValueError(f"out must be [{N}, >= {K}] with unit column stride, got {list(out.shape)}")
+    if out.dtype != W0.dtype or out.device != W0.device:
+        raise ValueError(f"out must be {W0.dtype} on {W0.device}")
     check(lib().aq_materialize_weff(dt, K, ctypes.byref(p), _ptr(out), out.stride(0), _stream()))
     return out
 
@@ -242,6 +341,11 @@ def quant_fp4_block16(w, workspace=None):
     if w.dtype != torch.bfloat16 or w.dim() != 2 or w.stride(1) != 1:
         raise ValueError("w must be a 2-D bfloat16 tensor with unit column stride")
     N, K = w.shape
+    bad = [] if w.device.type == "cuda" else [f"w must be on a GPU, got {w.device}"]
+    if K % 16:
+        bad.append(f"K = {K} must be a multiple of 16")
+    if bad:
+        raise ValueError("; ".join(bad))
     dev = w.device
     packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
@@ -264,20 +368,102 @@ def fp4_linear(x, packed, scales, global_scale, y=None, workspace=None):
         raise ValueError("x must be a 2-D bfloat16 tensor with unit column stride")
     M, K = x.shape
     N = packed.shape[0]
-    if packed.shape[1] * 2 != K or scales.shape != (N, K // 16):
-        raise ValueError("packed must be [N, K/2] and scales [N, K/16]")
+    bad = []
+    if packed.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        bad.append("packed and scales must be uint8")
+    if packed.dim() != 2 or packed.shape[1] * 2 != K:
+        bad.append(f"packed must be [N, {K // 2}], got {list(packed.shape)}")
+    if tuple(scales.shape) != (N, K // 16):
+        bad.append(f"scales must be [{N}, {K // 16}], got {list(scales.shape)}")
+    if global_scale.dtype != torch.float32 or global_scale.numel() != 1:
+        bad.append("global_scale must be one float32 value")
     if not (packed.is_contiguous() and scales.is_contiguous()):
-        raise ValueError("packed and scales must be contiguous")
+        bad.append("packed and scales must be contiguous")
+    for name, t in (("x", x), ("packed", packed), ("scales", scales), ("global_scale", global_scale)):
+        if t.device != x.device or t.device.type != "cuda":
+            bad.append(f"{name} must be on the GPU of x, got {t.device}")
+    if bad:
+        raise ValueError("; ".join(bad))
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    if y.dim() != 2 or y.stride(1) != 1:
-        raise ValueError("y must be 2-D with unit column stride")
+    _check_out(y, M, N, x)
     need = lib().aq_workspace_bytes(AQ_OP_FP4_LINEAR, AQ_BF16, M, K,
                                     (aq_proj * 1)(aq_proj(N, 0, None, None, None, None)), 1)
     ws, ws_bytes = (workspace or _WS).get(need, x.device)
     check(lib().aq_fp4_linear(M, N, K, _ptr(x), x.stride(0), _ptr(packed), _ptr(scales), _ptr(global_scale),
                               _ptr(y), y.stride(0), ws, ws_bytes, _stream()))
     return y
+
+
+# ----------------------------------------------------------- load-time path
+
+class BundleError(ValueError):
+    """A model's bundles do not fit their shared blocks.  ``offenders`` lists
+    ``(layer, family, reason)`` for every offending layer."""
+
+    def __init__(self, offenders):
+        self.offenders = offenders
+        lines = [f"layer {l} {f}: {why}" for l, f, why in offenders]
+        super().__init__(f"{len(offenders)} bundle(s) do not match a shape- and band-compatible "
+                         "shared block (a band count that differs between decomposition and "
+                         "serving is the usual cause):\n  " + "\n  ".join(lines))
+
+
+def check_bundles(shared, layers, quant=None, require_gpu=True):
+    """Validate a whole model before anything is launched.
+
+    ``shared[band][family]`` is the shared block W0 [N, K] of a band;
+    ``layers[l][family]`` is ``(band, s, U, Vt)`` (U, Vt None for rank 0).  Each
+    layer's bundle must name an existing band whose W0 for that family exists,
+    and s [N], U [N, r], Vt [r, K] must fit that W0 (one dtype, one GPU,
+    contiguous, r <= 256, K a multiple of 8 for bf16 or 4 for fp32, and of 16
+    with ``quant="nvfp4"``).  Raises one BundleError that lists every offending
+    layer ("Execution paths", section "Precompute-outside": the precompute
+    raises immediately with the offending layers listed).  ``require_gpu=False``
+    checks everything but the device type (host-side tests of the check).
+    """
+    if quant not in (None, "nvfp4"):
+        raise ValueError(f"unknown quant {quant!r}")
+    bad = []
+    dtype = device = None
+    for l in sorted(layers):
+        for f in sorted(layers[l]):
+            entry = layers[l][f]
+            if len(entry) != 4:
+                bad.append((l, f, "expected (band, s, U, Vt)"))
+                continue
+            band, s, U, Vt = entry
+            if band not in shared:
+                bad.append((l, f, f"band {band} does not exist (bands: {sorted(shared)})"))
+                continue
+            W0 = shared[band].get(f)
+            if W0 is None:
+                bad.append((l, f, f"band {band} has no shared block for {f}"))
+                continue
+            dtype = W0.dtype if dtype is None else dtype
+            device = W0.device if device is None else device
+            for msg in _bundle_problems(W0, s, U, Vt, dtype=dtype, device=device):
+                if require_gpu or not msg.startswith("tensors must be on a GPU"):
+                    bad.append((l, f, msg))
+            if quant == "nvfp4" and W0.dim() == 2 and W0.shape[1] % 16:
+                bad.append((l, f, f"K = {W0.shape[1]} must be a multiple of 16 for the FP4 pack"))
+    if bad:
+        raise BundleError(bad)
+
+
+def materialize_model(shared, layers, quant=None):
+    """The load-time path: ``check_bundles``, then every W_eff, then (with
+    ``quant="nvfp4"``) its FP4 pack.  Returns ``{layer: {family: W_eff}}`` or
+    ``{layer: {family: (packed, scales, global_scale)}}``."""
+    check_bundles(shared, layers, quant)
+    out = {}
+    for l in sorted(layers):
+        out[l] = {}
+        for f in sorted(layers[l]):
+            band, s, U, Vt = layers[l][f]
+            w = materialize((shared[band][f], s, U, Vt))
+            out[l][f] = quant_fp4_block16(w) if quant == "nvfp4" else w
+    return out
 
 
 def hip_runtimes_mapped():

@@ -2,6 +2,7 @@
 // launch on the caller's stream.  Nothing here allocates device memory and
 // nothing synchronises; argument errors are reported before any HIP call.
 
+#include <limits.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -11,6 +12,16 @@
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Plan overrides (aq_debug_force_plan): unset unless a test sets them.
+constexpr int kUnset = INT_MIN;
+struct Knobs {
+  int v[AQ_DBG_COUNT];
+  Knobs() {
+    for (int &x : v) x = kUnset;
+  }
+};
+thread_local Knobs g_knobs;
 
 aq_status fail(aq_status s, const char *fmt, ...) {
   va_list ap;
@@ -135,6 +146,11 @@ aq_status recon(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx, c
 }
 
 }  // namespace
+
+int aq::debug_knob(aq_debug_knob k, int dflt) {
+  const int v = (k >= 0 && k < AQ_DBG_COUNT) ? g_knobs.v[k] : kUnset;
+  return v == kUnset ? dflt : v;
+}
 
 extern "C" {
 
@@ -275,11 +291,43 @@ const char *aq_status_string(aq_status s) {
     case AQ_ERR_UNSUPPORTED: return "AQ_ERR_UNSUPPORTED";
     case AQ_ERR_WORKSPACE: return "AQ_ERR_WORKSPACE";
     case AQ_ERR_HIP: return "AQ_ERR_HIP";
+    case AQ_ERR_HANDOFF: return "AQ_ERR_HANDOFF";
   }
   return "AQ_ERR_UNKNOWN";
 }
 
 const char *aq_last_error(void) { return g_err; }
+
+aq_status aq_workspace_check(void *ws, void *stream) {
+  if (!ws) return AQ_OK;
+  if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  unsigned w[3] = {0, 0, 0};
+  if (e == hipSuccess) e = hipMemcpy(w, ws, sizeof w, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "reading the workspace failed: %s", hipGetErrorString(e));
+  if (w[aq::kSyncArrive] == 0 && w[aq::kSyncPassed] == 0 && w[aq::kSyncFlag] == 0) return AQ_OK;
+  e = hipMemset(ws, 0, sizeof w);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "clearing the workspace failed: %s", hipGetErrorString(e));
+  if (w[aq::kSyncFlag])
+    return fail(AQ_ERR_HANDOFF,
+                "a prefill launch gave up waiting for its rank-r workgroups (counters %u, %u): the outputs of "
+                "the prefill calls since the last check are not valid; the workspace has been cleared",
+                w[aq::kSyncArrive], w[aq::kSyncPassed]);
+  return fail(AQ_ERR_WORKSPACE,
+              "hand-off counters not zero (%u, %u): the workspace was not zero-filled or was used by "
+              "concurrent calls; it has been cleared",
+              w[aq::kSyncArrive], w[aq::kSyncPassed]);
+}
+
+aq_status aq_debug_force_plan(aq_debug_knob knob, int64_t value) {
+  if (knob < 0 || knob >= AQ_DBG_COUNT) return fail(AQ_ERR_INVALID_ARG, "unknown plan knob %d", (int)knob);
+  if (value < INT_MIN + 1 || value > INT_MAX) return fail(AQ_ERR_INVALID_ARG, "knob value out of range");
+  g_knobs.v[knob] = (int)value;
+  return AQ_OK;
+}
+
+void aq_debug_reset_plan(void) { g_knobs = Knobs(); }
 
 int aq_version(void) { return 100; }
 

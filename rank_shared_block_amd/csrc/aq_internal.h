@@ -23,6 +23,17 @@ constexpr int kDecodeMaxM = 64;   // largest batch served by the streaming kerne
 constexpr size_t kWsReserved = 65536;
 constexpr int kMaxCounterTiles = (int)(kWsReserved / 4);
 
+// Plan overrides set through aq_debug_force_plan (thread-local, for tests that
+// force one kernel variant).  Returns dflt while the knob is unset, so without
+// those calls a plan depends only on the call's arguments.
+int debug_knob(aq_debug_knob k, int dflt);
+
+// Prefill hand-off words in the reserved workspace region: [0] arrivals of
+// the rank-r workgroups, [1] main workgroups past their wait, [2] flag set
+// when a wait gave up (read and cleared by aq_workspace_check).
+constexpr int kSyncArrive = 0, kSyncPassed = 1, kSyncFlag = 2;
+constexpr int kHandoffSpin = 1 << 22;   // polls before a wait gives up
+
 // One projection of a (possibly fused) dispatch, host view.
 struct Proj {
   int64_t N, r;

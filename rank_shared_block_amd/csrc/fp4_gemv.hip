@@ -341,11 +341,8 @@ __global__ __launch_bounds__(256) void k_fp4_fold(const float *part, int S, int 
   y[(size_t)m * ldy + n] = f2bf(s);
 }
 
-// The exact per-block kernel for M <= 4 (AQ_FP4_M4=0 selects the other one).
-static bool getenv_m4() {
-  const char *v = getenv("AQ_FP4_M4");
-  return !(v && *v == '0');
-}
+// The exact per-block kernel for M <= 4 (a plan override of 0 selects the other one).
+static bool use_m4() { return debug_knob(AQ_DBG_FP4_M4, 1) != 0; }
 
 void plan_fp4_linear(int64_t M, int64_t N, int64_t K, Fp4LinPlan *pl) {
   // Measured on the Gemma-3-1B decode shapes (graph replays over 26 layers):
@@ -357,7 +354,7 @@ void plan_fp4_linear(int64_t M, int64_t N, int64_t K, Fp4LinPlan *pl) {
   int NG = 1;
   for (int ng = 4; ng >= 1; --ng)
     if ((N + 16 * ng - 1) / (16 * ng) >= 400) { NG = ng; break; }
-  const int ngo = getenv("AQ_FP4_NG") ? atoi(getenv("AQ_FP4_NG")) : 0;   // tuning overrides: AQ_FP4_NG, AQ_FP4_S
+  const int ngo = debug_knob(AQ_DBG_FP4_NG, 0);   // plan overrides (tests): row groups, K splits
   if (ngo >= 1 && ngo <= 4) NG = ngo;
   const int tiles = (int)((N + 16 * NG - 1) / (16 * NG));
   int S = 1;
@@ -368,7 +365,7 @@ void plan_fp4_linear(int64_t M, int64_t N, int64_t K, Fp4LinPlan *pl) {
     S = S < 16 ? S : 16;
     S = S > 1 ? S : 1;
   }
-  const int so = getenv("AQ_FP4_S") ? atoi(getenv("AQ_FP4_S")) : 0;
+  const int so = debug_knob(AQ_DBG_FP4_S, 0);
   if (so >= 1) S = so;
   int kchunk = (int)((K + S - 1) / S);
   kchunk = (kchunk + 127) / 128 * 128;
@@ -383,7 +380,7 @@ void plan_fp4_linear(int64_t M, int64_t N, int64_t K, Fp4LinPlan *pl) {
 
 template <bool PART>
 static bool launch_ng(const F4Args &a, int NG, int grid, hipStream_t st) {
-  if (a.M <= 4 && a.K % 64 == 0 && getenv_m4()) {   // K % 64: the 4-byte scale loads stay aligned
+  if (a.M <= 4 && a.K % 64 == 0 && use_m4()) {   // K % 64: the 4-byte scale loads stay aligned
     switch (NG) {
       case 1: hipLaunchKernelGGL((k_fp4_gemv_m4<1, PART>), dim3(grid), dim3(512), 0, st, a); return true;
       case 2: hipLaunchKernelGGL((k_fp4_gemv_m4<2, PART>), dim3(grid), dim3(512), 0, st, a); return true;

@@ -40,7 +40,6 @@
 // Both are deterministic.
 
 #include <limits.h>
-#include <stdlib.h>
 
 #include "aq_internal.h"
 #include "device_common.h"
@@ -405,11 +404,6 @@ __global__ __launch_bounds__(256) void k_decode_combine(const CombArgs a) {
 
 // ---------------------------------------------------------------- host side
 
-static int env_int(const char *name, int dflt) {
-  const char *v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
-
 // Largest row-group count per workgroup: the fragments of two steps
 // (2 * 4 * KS * (NG + MT) VGPRs) plus NG * MT * 4 accumulators must fit the
 // 256 registers of a wave at two waves per SIMD.
@@ -469,18 +463,18 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
   }
   bool split = best_s < best_f;
 
-  // Tuning overrides (profiling sweeps): AQ_DECODE_SPLIT (0/1), AQ_DECODE_ROWS,
-  // AQ_DECODE_NG (rows = 16 x the W0 groups), AQ_DECODE_S, AQ_DECODE_WAVES.
-  const int sp_o = env_int("AQ_DECODE_SPLIT", -1);
+  // Plan overrides (tests, aq_debug_force_plan): split (0/1), rows per tile,
+  // W0 groups per tile (rows = 16 x groups), K splits, waves.
+  const int sp_o = debug_knob(AQ_DBG_DECODE_SPLIT, -1);
   if (sp_o == 1 || (sp_o == 0 && Rf > 0)) split = sp_o == 1;
   int R = split ? Rs : Rf, S = split ? Ss : 1;
   const int rmax = split ? 16 * ngmax : 16 * (ngmax_f - vgmax);
-  const int ng_o = env_int("AQ_DECODE_NG", 0);
+  const int ng_o = debug_knob(AQ_DBG_DECODE_NG, 0);
   if (ng_o >= (split ? 1 : ngmin) && ng_o <= (split ? ngmax : ngmax_f)) R = 16 * (ng_o - (split ? 0 : vgmax));
-  const int r_o = env_int("AQ_DECODE_ROWS", 0);
+  const int r_o = debug_knob(AQ_DBG_DECODE_ROWS, 0);
   if (r_o >= 1 && r_o <= rmax) R = r_o;
   if (split) {
-    const int s_o = env_int("AQ_DECODE_S", 0);
+    const int s_o = debug_knob(AQ_DBG_DECODE_S, 0);
     if (s_o >= 1) S = s_o;
   }
   if (R < 1) return false;
@@ -488,7 +482,7 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
   if (!split && NG < ngmin) NG = ngmin;
   if (NG > (split ? ngmax : ngmax_f)) return false;
   int WAVES = 4;
-  const int w_o = env_int("AQ_DECODE_WAVES", 0);
+  const int w_o = debug_knob(AQ_DBG_DECODE_WAVES, 0);
   if (w_o == 4 || (pl->MT == 1 && w_o == 8)) WAVES = w_o;
 
   int kchunk = (K + S - 1) / S;

@@ -56,8 +56,6 @@
 //   of its own K range), and a small kernel adds them in split order.
 //   Deterministic.
 
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "aq_internal.h"
@@ -86,9 +84,11 @@ struct PfArgs {
   int ldx, ldy, ldt, ldp, M, K, nblk, ntm, ntiles, S, kchunk, vec_store;
   // Rank-r pass run by the first tgrid workgroups of the main-pass launch
   // (0: none): they publish t with device-coherent stores (coherent = 1 in
-  // their arguments) and count themselves in sync[0]; the nwait main units
-  // that need t wait for the count, and the last of them zeroes sync[0..1].
-  int tgrid, nwait, coherent;
+  // their arguments) and count themselves in sync[0] with a release; the
+  // nwait main units that need t wait (at most `spin` polls) until the count
+  // reaches `wait_for` (= tgrid), acquire, and the last of them zeroes
+  // sync[0..1].  A wait that gives up sets the flag word sync[2].
+  int tgrid, nwait, coherent, wait_for, spin;
   // tsplit: t is kept per K range (t_p = x_p Vt_p^T, bf16, at t + p * tstride)
   // and every K-split unit p adds t_p U^T to its partial (the rank term is
   // linear in K, so the fold of the partials sums it); the rank-r tiles write
@@ -476,15 +476,28 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   if (MODE != MODE_RAW && addu && a.tgrid > 0) {
     if (tid == 0) {
       // Bounded: the rank-r workgroups were dispatched before every main one
-      // and need no other workgroup to finish, so the count arrives; a spin
-      // past the bound goes on rather than hang.
-      for (int it = 0; it < (1 << 22); ++it) {
-        if (__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)a.tgrid) break;
+      // and need no other workgroup to finish, so the count arrives.  A wait
+      // that reaches the bound all the same goes on rather than hang, and
+      // records that in the flag word for aq_workspace_check to report.
+      bool seen = false;
+      for (int it = 0; it < a.spin; ++it) {
+        if (__hip_atomic_load(a.sync + kSyncArrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)a.wait_for) {
+          seen = true;
+          break;
+        }
         __builtin_amdgcn_s_sleep(2);
       }
-      if (__hip_atomic_fetch_add(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == (unsigned)a.nwait) {
-        __hip_atomic_store(a.sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!seen) __hip_atomic_fetch_or(a.sync + kSyncFlag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // Acquire at agent scope: the producers released their t stores with
+      // their arrival, and t is read below with plain loads, possibly on
+      // another XCD than the one that wrote it; this invalidates the lines
+      // those loads could otherwise find stale in this CU's caches.  The
+      // workgroup barrier after it orders every wave's reads behind it.
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (__hip_atomic_fetch_add(a.sync + kSyncPassed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
+          (unsigned)a.nwait) {
+        __hip_atomic_store(a.sync + kSyncArrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.sync + kSyncPassed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     ring_barrier();
@@ -749,10 +762,11 @@ __global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST, MODE == M
     if ((int)blockIdx.x < a.tgrid) {
       const int u = xcd_contiguous_tile(blockIdx.x, tp.ntiles * tp.S);
       if (u >= 0) gemm_tile<T::tBM, T::tBN, T::tBK, T::tNST, MODE_RAW, NW>(tp, u, st0, st1, st2, st3, s_lds);
-      // every wave's coherent t stores are complete, then one arrival
+      // every wave's coherent t stores are complete, then one arrival that
+      // releases them at agent scope (the readers may sit on other XCDs)
       __builtin_amdgcn_s_waitcnt(0);
       ring_barrier();
-      if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync + kSyncArrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
   }
@@ -789,11 +803,6 @@ namespace {
 struct TileCfg {
   int BM, BN, BK, NST, S, NW;
 };
-
-static int env_int(const char *name, int dflt) {
-  const char *v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
 
 int count_tiles(const Recon &rq, int BM, int BN, bool tpass) {
   const int ntm = (int)((rq.M + BM - 1) / BM);
@@ -854,7 +863,7 @@ TileCfg choose(const Recon &rq) {
   const int t128 = count_tiles(rq, 128, 128, false);
   int rmax = 0;
   for (int b = 0; b < rq.nblk; ++b) rmax = rq.blk[b].r > rmax ? (int)rq.blk[b].r : rmax;
-  const bool own_t = rmax <= 64 && env_int("AQ_PREFILL_SELF", 1) != 0;
+  const bool own_t = rmax <= 64 && debug_knob(AQ_DBG_PREFILL_SELF, 1) != 0;
   TileCfg tc = {128, 128, 64, 4, 1, 4};
   if (t128 <= 16 || (rq.K <= 2048 && count_tiles(rq, 64, 64, false) <= kNumCU)) {
     tc = {64, 64, 64, 4, 1, 4};
@@ -878,17 +887,17 @@ TileCfg choose(const Recon &rq) {
       tc = {128, 96, 64, 4, 1, 4};
     }
   }
-  // Tuning overrides (profiling sweeps): AQ_PREFILL_BM/BN/BK/NST pick a compiled
-  // shape, AQ_PREFILL_S the K split.
-  const int bm = env_int("AQ_PREFILL_BM", 0), bn = env_int("AQ_PREFILL_BN", 0);
-  const int bk = env_int("AQ_PREFILL_BK", 0), ns = env_int("AQ_PREFILL_NST", 0);
-  const int nw = env_int("AQ_PREFILL_W", 4);
+  // Plan overrides (tests, aq_debug_force_plan): BM/BN/BK/NST/W pick a compiled
+  // shape, S the K split.
+  const int bm = debug_knob(AQ_DBG_PREFILL_BM, 0), bn = debug_knob(AQ_DBG_PREFILL_BN, 0);
+  const int bk = debug_knob(AQ_DBG_PREFILL_BK, 0), ns = debug_knob(AQ_DBG_PREFILL_NST, 0);
+  const int nw = debug_knob(AQ_DBG_PREFILL_W, 4);
   for (const Cand &c : kCands)
     if (c.BM == bm && c.BN == bn && (bk == 0 || c.BK == bk) && (ns == 0 || c.NST == ns) && c.NW == nw) {
       tc.BM = c.BM, tc.BN = c.BN, tc.BK = c.BK, tc.NST = c.NST, tc.NW = c.NW;
       break;
     }
-  const int so = env_int("AQ_PREFILL_S", 0);
+  const int so = debug_knob(AQ_DBG_PREFILL_S, 0);
   if (so >= 1) tc.S = so;
   return tc;
 }
@@ -930,7 +939,7 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
   // as one: there the rank-r tiles split K into parts (kept apart, summed by
   // the main tiles' epilogue MFMAs) so that each runs at most half as many K
   // slices as a main tile and t is ready before the main tiles need it.
-  const int to = env_int("AQ_TPASS_S", 0);
+  const int to = debug_knob(AQ_DBG_TPASS_S, 0);
   pl->fuse = 0;
   pl->tparts = 1;
   // The tile shapes chosen for one round of few, latency-bound tiles with
@@ -946,8 +955,8 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
                                          (tc.BM == 128 && tc.BN == 128 && tc.BK == 64 && tc.NST == 3) ||
                                          (tc.BM == 128 && tc.BN == 96 && tc.BK == 64 && tc.NST >= 3));
   pl->self = c > 0 && self_tile && tc.S == 1 && rq.K <= 2048 && rmax <= 64 && to <= 1 &&
-             env_int("AQ_PREFILL_SELF", 1) != 0;
-  if (c > 0 && !pl->self && fusable && to <= 1 && env_int("AQ_PREFILL_FUSE", 1) != 0) {
+             debug_knob(AQ_DBG_PREFILL_SELF, 1) != 0;
+  if (c > 0 && !pl->self && fusable && to <= 1 && debug_knob(AQ_DBG_PREFILL_FUSE, 1) != 0) {
     const int tb = tc.NW == 8 ? 128 : 64;              // the shape TPass gives
     const int slots = kNumCU * ((tc.BM + tc.BN) * tc.BK * 2 * tc.NST <= 80 * 1024 ? 2 : 1);
     const int rem = count_tiles(rq, tc.BM, tc.BN, false) * tc.S % slots;
@@ -955,7 +964,7 @@ void plan_prefill(const Recon &rq, PrefillPlan *pl) {
     int parts = 1;
     if (!big && tc.S == 1) {
       parts = 2 * 64 / tc.BK;
-      const int po = env_int("AQ_TPASS_PARTS", 0);
+      const int po = debug_knob(AQ_DBG_TPASS_PARTS, 0);
       if (po >= 1) parts = po;
       const int pmax = (int)((rq.K + 127) / 128);        // parts of >= 128 K values
       parts = parts < pmax ? parts : pmax;
@@ -1159,6 +1168,11 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
     for (int b = 0; b < rq.nblk; ++b)
       if (a.b[b].r > 0) a.nwait += a.b[b].ntn * a.ntm * (a.tsplit ? a.S : 1);
     if (a.nwait == 0) a.tgrid = 0;
+    // the rank-r workgroups that arrive: those with a tile (the grid is
+    // rounded up to whole XCD rounds; the padding workgroups count too)
+    a.wait_for = a.tgrid + (debug_knob(AQ_DBG_HANDOFF_UNREACHABLE, 0) ? 1 : 0);
+    a.spin = debug_knob(AQ_DBG_HANDOFF_SPIN, kHandoffSpin);
+    if (a.spin < 1) a.spin = 1;
   }
   const int mode = pl.self ? MODE_SELF : (a.S > 1 ? MODE_PART : MODE_RECON);
   hipError_t e = run(a, t, pl.BM, pl.BN, pl.BK, pl.NST, pl.NW, mode, st);

@@ -74,15 +74,25 @@ def test_bf16_ranks(r, M):
     assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"r={r} M={M}")
 
 
-def test_bf16_rank0_and_passthrough_agree():
-    """Passthrough (s = 1, U = Vt = 0) and r = 0 with s = 1 give the same bits, and
-    both are within tolerance of x W^T."""
-    M, K, N = 16, 1024, 300
+@pytest.mark.parametrize("M", [16, 300])
+def test_bf16_rank0_and_passthrough_agree(M, force_plan):
+    """Passthrough (s = 1, U = Vt = 0, W0 = the layer's own weight) and r = 0
+    with s = 1 give the same bits (the W0 contraction's summation order does not
+    depend on r, and the rank term adds exact zeros), at a decode batch (the
+    streaming kernel, its fused mode forced for both so that the K split is the
+    same) and at a prefill batch (the tiled kernel); both are within tolerance
+    of x W^T ("How attnquant works", section "The passthrough operating
+    point")."""
+    K, N = 1024, 300
+    if M <= 64:
+        force_plan("DECODE_SPLIT", 0)
     bd = I.bundle("test", 7, "o", K, N, 16, "bf16", variant="passthrough")
-    x = up(I.activations("test", 7, M, K, "bf16"), "bf16")
+    x = up(I.activations("test", 7 + M, M, K, "bf16"), "bf16")
     W0, s, U, Vt = bundle_up(bd, "bf16")
     y_pt = B.recon_linear(x, (W0, s, U, Vt))
     y_r0 = B.recon_linear(x, (W0, s, None, None))
+    torch.cuda.synchronize()
+    assert torch.equal(y_pt, y_r0), f"M={M}: passthrough and r = 0 differ"
     ref = down(x) @ bd["W0"].astype(np.float64).T
     assert_parity(down(y_pt), ref, "bf16", "passthrough")
     assert_parity(down(y_r0), ref, "bf16", "r0")
@@ -116,11 +126,11 @@ _DECODE_MODES = [("0", None, None), ("1", None, None), ("1", 1, 1), ("1", 2, 3),
 
 @pytest.mark.parametrize("M", [1, 7, 20, 40, 64])
 @pytest.mark.parametrize("split,ng,S", _DECODE_MODES)
-def test_decode_modes_qkv(M, split, ng, S, monkeypatch):
-    monkeypatch.setenv("AQ_DECODE_SPLIT", split)
+def test_decode_modes_qkv(M, split, ng, S, force_plan):
+    force_plan("DECODE_SPLIT", int(split))
     if ng is not None:
-        monkeypatch.setenv("AQ_DECODE_NG", str(ng))
-        monkeypatch.setenv("AQ_DECODE_S", str(S))
+        force_plan("DECODE_NG", ng)
+        force_plan("DECODE_S", S)
     K = 1048
     shapes = [(200, 8), (40, 16), (24, 0)]
     bds = [I.bundle("test", 3, f, K, n, r, "bf16", variant="s0" if f == "q" else "normal")
@@ -133,12 +143,12 @@ def test_decode_modes_qkv(M, split, ng, S, monkeypatch):
 
 @pytest.mark.parametrize("M", [1, 16, 20, 64])
 @pytest.mark.parametrize("rows", [5, 17, 27, 54, 64, 80])
-def test_decode_fused_rows(M, rows, monkeypatch):
+def test_decode_fused_rows(M, rows, force_plan):
     """Fused tiles of any row count (not a multiple of 16; the last tile of each
     block shorter still), over a fused gate/up pair with ragged N and K.  Row
     counts that no compiled tile of the batch bucket holds fall back to the plan."""
-    monkeypatch.setenv("AQ_DECODE_SPLIT", "0")
-    monkeypatch.setenv("AQ_DECODE_ROWS", str(rows))
+    force_plan("DECODE_SPLIT", 0)
+    force_plan("DECODE_ROWS", rows)
     K = 1048
     bds = [I.bundle("test", 4, f, K, 333, 16, "bf16", variant="s0" if f == "gate" else "normal")
            for f in ("gate", "up")]
@@ -171,14 +181,14 @@ _PREFILL_MODES = [None, (256, 256, 32, 4, 1, None), (256, 256, 64, 2, 1, None), 
 
 @pytest.mark.parametrize("M", [65, 300, 513])
 @pytest.mark.parametrize("mode", _PREFILL_MODES, ids=str)
-def test_prefill_modes_qkv(M, mode, monkeypatch):
+def test_prefill_modes_qkv(M, mode, force_plan):
     if mode is not None:
         bm, bn, bk, nst, S, tS = mode[:6]
         nw = mode[6] if len(mode) > 6 else 4
         for k, v in (("BM", bm), ("BN", bn), ("BK", bk), ("NST", nst), ("S", S), ("W", nw)):
-            monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
+            force_plan(f"PREFILL_{k}", v)
         if tS is not None:
-            monkeypatch.setenv("AQ_TPASS_S", str(tS))
+            force_plan("TPASS_S", tS)
     K = 1048
     shapes = [(200, 8), (40, 16), (24, 0)]
     bds = [I.bundle("test", 4, f, K, n, r, "bf16", variant="s0" if f == "k" else "normal")
@@ -203,13 +213,13 @@ def test_rank_pass_shapes(M, K):
 @pytest.mark.parametrize("r", [36, 64, 100, 256])
 @pytest.mark.parametrize("tile", [(256, 256, 32, 4), (256, 256, 64, 2), (256, 128, 64, 3), (128, 256, 32, 3),
                                   (256, 256, 32, 4, 8), (256, 256, 64, 2, 8)], ids=str)
-def test_prefill_high_rank(M, r, tile, monkeypatch):
+def test_prefill_high_rank(M, r, tile, force_plan):
     """Rank-r epilogues over one or several rank chunks (some riding on the tail
     of the K ring, the rest read from global memory), with U rows that are
     16-byte aligned (r % 8 == 0) or not (r = 36, 100); four- and eight-wave
     workgroups."""
     for k, v in zip(("BM", "BN", "BK", "NST", "W"), tuple(tile) + ((4,) if len(tile) == 4 else ())):
-        monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
+        force_plan(f"PREFILL_{k}", v)
     bd, x = _single(M, 512, 520, r, "bf16", variant="s0", layer=r, tag=700 + M)
     y = B.recon_linear(up(x, "bf16"), bundle_up(bd, "bf16"))
     assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"r={r} M={M}")
@@ -219,7 +229,7 @@ def test_prefill_high_rank(M, r, tile, monkeypatch):
 @pytest.mark.parametrize("K", [1048, 3000])
 @pytest.mark.parametrize("S", [1, 3])
 @pytest.mark.parametrize("tile", [(128, 128, 64, 4, 4), (128, 96, 64, 4, 4), (256, 128, 32, 3, 4), (256, 256, 32, 4, 8)], ids=str)
-def test_prefill_rank_pass_in_main_launch(M, K, S, tile, monkeypatch):
+def test_prefill_rank_pass_in_main_launch(M, K, S, tile, force_plan):
     """The rank-r pass run by the first workgroups of the main-pass launch
     (these shapes leave free slots in the last round), with K short and long
     (unsplit), or the main pass K-split in three with one t per K range; U rows
@@ -227,7 +237,7 @@ def test_prefill_rank_pass_in_main_launch(M, K, S, tile, monkeypatch):
     memory), a block without rank; the arrival counters are back at zero after
     every call."""
     for k, v in zip(("BM", "BN", "BK", "NST", "W", "S"), tuple(tile) + (S,)):
-        monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
+        force_plan(f"PREFILL_{k}", v)
     shapes = [(300, 16), (200, 36), (72, 0)]
     bds = [I.bundle("test", 6, f, K, n, r, "bf16", variant="normal") for f, (n, r) in zip(("q", "k", "v"), shapes)]
     x = I.activations("test", 950 + M + K, M, K, "bf16")
@@ -243,16 +253,16 @@ def test_prefill_rank_pass_in_main_launch(M, K, S, tile, monkeypatch):
 @pytest.mark.parametrize("M", [130, 300])
 @pytest.mark.parametrize("K", [200, 1048])
 @pytest.mark.parametrize("parts", [2, 3, 4])
-def test_prefill_rank_pass_in_parts(M, K, parts, monkeypatch):
+def test_prefill_rank_pass_in_parts(M, K, parts, force_plan):
     """Main tiles of 64 x 64 with the rank-r pass in the same launch, its K split
     into parts that are kept apart and summed by the main tiles' epilogue: two
     or three parts ride the LDS ring, a fourth goes the per-round path; U rows
     aligned (r = 16) and not (r = 36); K = 200 allows two parts of >= 128 K
     values only.  The workspace size shows that the plan keeps the parts."""
     for k, v in zip(("BM", "BN", "BK", "NST", "W"), (64, 64, 64, 4, 4)):
-        monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
-    monkeypatch.setenv("AQ_TPASS_PARTS", str(parts))
-    monkeypatch.setenv("AQ_PREFILL_SELF", "0")
+        force_plan(f"PREFILL_{k}", v)
+    force_plan("TPASS_PARTS", parts)
+    force_plan("PREFILL_SELF", 0)
     shapes = [(300, 16), (200, 36), (72, 0)]
     bds = [I.bundle("test", 7, f, K, n, r, "bf16", variant="normal") for f, (n, r) in zip(("q", "k", "v"), shapes)]
     nparts = min(parts, (K + 127) // 128)
@@ -270,18 +280,47 @@ def test_prefill_rank_pass_in_parts(M, K, parts, monkeypatch):
         assert int(counters.sum()) == 0, counters
 
 
+def test_prefill_handoff_give_up_is_reported(force_plan):
+    """The bounded wait of the main tiles for the rank-r workgroups of their
+    launch: with the awaited count forced one above what arrives and the wait
+    bounded to 64 polls, every kernel still exits, the flag is set and
+    aq_workspace_check reports it (and clears the workspace); the next call,
+    with the plan back to normal, is correct and leaves the workspace clean."""
+    M, K = 300, 1048
+    shapes = [(300, 16), (200, 36), (72, 0)]
+    bds = [I.bundle("test", 6, f, K, n, r, "bf16", variant="normal") for f, (n, r) in zip(("q", "k", "v"), shapes)]
+    x = I.activations("test", 960, M, K, "bf16")
+    ref = oracle.recon_fused(x, [bundle_np(b) for b in bds])
+    ws = B.Workspace()
+    for k, v in zip(("BM", "BN", "BK", "NST", "W"), (128, 128, 64, 4, 4)):
+        force_plan(f"PREFILL_{k}", v)
+    force_plan("HANDOFF_SPIN", 64)
+    force_plan("HANDOFF_UNREACHABLE", 1)
+    B.recon_qkv(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds], workspace=ws)
+    with pytest.raises(B.AQError) as e:
+        ws.check()
+    assert e.value.status == B.AQ_ERR_HANDOFF, e.value
+    assert int(ws._buf[torch.device(dev()).index][:12].cpu().sum()) == 0
+    B.aq_debug_reset_plan()
+    for k, v in zip(("BM", "BN", "BK", "NST", "W"), (128, 128, 64, 4, 4)):
+        force_plan(f"PREFILL_{k}", v)
+    y = B.recon_qkv(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds], workspace=ws)
+    assert_parity(down(y), ref, "bf16", "after the reported give-up")
+    ws.check()
+
+
 @pytest.mark.parametrize("M", [65, 130, 300])
 @pytest.mark.parametrize("K", [200, 1048, 2000])
 @pytest.mark.parametrize("tile", [(64, 64, 64, 4), (128, 128, 32, 4), (128, 128, 64, 3), (128, 96, 64, 4),
                                   (128, 96, 64, 3)])
-def test_prefill_own_t(M, K, tile, monkeypatch):
+def test_prefill_own_t(M, K, tile, force_plan):
     """Main tiles that compute their own rows of t (Vt rows as more B rows of
     every stage, t rounded to bf16 in LDS, one or two rank chunks; K <= 2048):
     r = 64, r = 16, r = 36 (U rows not 16-byte aligned: the per-round path
     with t from LDS), a block without rank; nothing in the workspace.  Two or
     four wave rows (128 x 96: one wave column, two t blocks per wave)."""
     for k, v in zip(("BM", "BN", "BK", "NST", "W"), tuple(tile) + (4,)):
-        monkeypatch.setenv(f"AQ_PREFILL_{k}", str(v))
+        force_plan(f"PREFILL_{k}", v)
     shapes = [(300, 64), (200, 16), (136, 36), (72, 0)]
     bds = [I.bundle("test", 8, f, K, n, r, "bf16", variant="normal") for f, (n, r) in zip(("q", "k", "v", "o"), shapes)]
     fake = [B.aq_proj(n, r, 256, 256, 256, 256) for n, r in shapes[:3]]
@@ -381,14 +420,22 @@ def test_gemma_prefill_layer_sampled(M):
         assert np.all(np.isfinite(y))
 
 
+def _strided_sample(rng, n, stride):
+    """One index in every `stride`-wide window of range(n) (random offset per
+    window): every tile of that width or wider is hit."""
+    return np.array([w + rng.integers(0, min(stride, n - w)) for w in range(0, n, stride)])
+
+
 @pytest.mark.parametrize("M", [1, 32, 512])
 def test_large_decoder_banded_sampled(M):
-    """Two layers of one W0 band (per-layer s, U, Vt): sampled tokens x sampled
-    output columns of every dispatch."""
+    """Two layers of one W0 band (per-layer s, U, Vt), every dispatch: one
+    output column in every 64-column window of every block (so every output
+    tile and, with it, every tile of t it reads is compared) on one token in
+    every 32-token window (every M tile)."""
     lbs = I.layer_bundles("large_decoder", I.LARGE_DECODER, layers=2, r=32, dtype="bf16",
                           num_bands=1)
     rng = np.random.default_rng(1000 + M)
-    rows = np.sort(rng.choice(M, min(M, 16), replace=False))
+    rows = np.unique(_strided_sample(rng, M, 32))
     for layer in (0, 1):
         for name, fams, K, bds in _layer_dispatches(I.LARGE_DECODER, lbs[layer]):
             x = I.activations("large_decoder", 7 * M + 3 * layer + len(name), M, K, "bf16")
@@ -396,7 +443,7 @@ def test_large_decoder_banded_sampled(M):
             col0, cols_all, refs = 0, [], []
             for b in bds:
                 n = b["W0"].shape[0]
-                cols = np.sort(rng.choice(n, 192, replace=False))
+                cols = _strided_sample(rng, n, 64)
                 refs.append(oracle.recon_linear(x[rows], *sub_bundle(b, cols)))
                 cols_all.append(col0 + cols)
                 col0 += n
@@ -617,12 +664,12 @@ def test_fp4_linear(M, N, K):
 
 @pytest.mark.parametrize("M", [2, 7])
 @pytest.mark.parametrize("ng,S", [(1, 1), (2, 1), (3, 1), (4, 1), (1, 5), (3, 2)])
-def test_fp4_linear_tilings(M, ng, S, monkeypatch):
+def test_fp4_linear_tilings(M, ng, S, force_plan):
     """Every compiled row-group count (16 to 64 rows per workgroup) with and
     without a K split, on a ragged N; M = 2 takes the exact per-block kernel
     (up to four tokens), M = 7 the other."""
-    monkeypatch.setenv("AQ_FP4_NG", str(ng))
-    monkeypatch.setenv("AQ_FP4_S", str(S))
+    force_plan("FP4_NG", ng)
+    force_plan("FP4_S", S)
     N, K = 999, 1280
     _, (p, s, g) = _fp4_weight(N, K, 720 + ng)
     x = I.activations("test", 721 + S, M, K, "bf16")
@@ -633,7 +680,7 @@ def test_fp4_linear_tilings(M, ng, S, monkeypatch):
 
 
 @pytest.mark.parametrize("M", [1, 4])
-def test_fp4_linear_both_kernels_agree_closely(M, monkeypatch):
+def test_fp4_linear_both_kernels_agree_closely(M, force_plan):
     """Up to four tokens: the exact per-block kernel and the per-weight-rounding
     one against the oracle; the exact one is the closer of the two."""
     N, K = 640, 1152
@@ -643,7 +690,7 @@ def test_fp4_linear_both_kernels_agree_closely(M, monkeypatch):
     args = (torch.from_numpy(p).to(d), torch.from_numpy(s).to(d), torch.tensor([g], dtype=torch.float32, device=d))
     ref = oracle.fp4_linear(x, p, s, g)
     y_exact = down(B.fp4_linear(up(x, "bf16"), *args))
-    monkeypatch.setenv("AQ_FP4_M4", "0")
+    force_plan("FP4_M4", 0)
     y_round = down(B.fp4_linear(up(x, "bf16"), *args))
     _assert_fp4_parity(y_exact, x, p, s, g, "exact")
     _assert_fp4_parity(y_round, x, p, s, g, "rounded")
