@@ -118,6 +118,27 @@ aq_status aq_recon_gateup_fused(aq_dtype dt, int64_t M, int64_t K, const void *x
                                 int64_t ldx, const aq_proj p[2], void *y, int64_t ldy,
                                 void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation as aq_recon_linear (nproj = 1), aq_recon_gateup_fused (nproj =
+ * 2, p = (gate, up)) or aq_recon_qkv_fused (nproj = 3, p = (q, k, v)), with the
+ * same kernels and results, but with no workspace argument: the scratch comes
+ * from an array of 16 MiB that the library holds on each GPU (allocated when
+ * the library is loaded, kept until the process ends), the one of the device
+ * that is current at the call (the stream must belong to it).  Nothing is
+ * allocated or freed.  A call whose plan needs more scratch than 16 MiB
+ * returns AQ_ERR_UNSUPPORTED (every decode and prefill dispatch of the
+ * Gemma-3-1B-shaped and larger-decoder-shaped layers needs at most 7 MiB).
+ * Every call on one GPU shares that GPU's array and overwrites what the
+ * previous call left there; calls that overlap in time on one GPU (on
+ * different streams, or from several threads) race and must not be issued.
+ * Before a prefill launch that hands t between its workgroups, the hand-off
+ * counters are zeroed by a small kernel (graph-capturable); a wait that gave
+ * up is reported by aq_workspace_check(NULL, stream).  Limits and errors as
+ * aq_recon_linear; nproj outside 1..3 is AQ_ERR_INVALID_ARG. */
+aq_status aq_recon_linear_noalloc(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
+                                  const aq_proj *p, int nproj, void *y, int64_t ldy, void *stream);
+
 /* W_eff[N, ldw] (columns 0..K-1) = diag(s) W0 + U Vt, accumulated in fp32 and
  * rounded once to dt.  "Execution paths", section "Precompute-outside" (the weight
  * rebuilt once at load) and "How attnquant works", section "The reconstruction
@@ -197,7 +218,8 @@ size_t aq_workspace_bytes(aq_op op, aq_dtype dt, int64_t M, int64_t K, const aq_
  * not back at zero (a workspace that was not zero-filled, or shared by calls
  * that ran concurrently).  In both cases it clears the reserved region, so the
  * workspace can be used again.  AQ_OK otherwise.  ws must be the workspace
- * pointer passed to the calls (256-byte aligned); NULL is AQ_OK. */
+ * pointer passed to the calls (256-byte aligned); NULL checks the scratch of
+ * aq_recon_linear_noalloc on the current device. */
 aq_status aq_workspace_check(void *ws, void *stream);
 
 const char *aq_status_string(aq_status s);

@@ -76,6 +76,8 @@ def lib():
         L.aq_last_error.restype = ctypes.c_char_p
         L.aq_version.argtypes = []
         L.aq_version.restype = ctypes.c_int
+        L.aq_recon_linear_noalloc.argtypes = [ctypes.c_int, i64, i64, vp, i64, P, ctypes.c_int, vp, i64, vp]
+        L.aq_recon_linear_noalloc.restype = ctypes.c_int
         L.aq_workspace_check.argtypes = [vp, vp]
         L.aq_workspace_check.restype = ctypes.c_int
         L.aq_debug_force_plan.argtypes = [ctypes.c_int, i64]
@@ -109,6 +111,10 @@ def aq_recon_qkv_fused(dt, M, K, x, ldx, p, y, ldy, ws, ws_bytes, stream):
 
 def aq_recon_gateup_fused(dt, M, K, x, ldx, p, y, ldy, ws, ws_bytes, stream):
     return lib().aq_recon_gateup_fused(dt, M, K, x, ldx, _projs(p, 2), y, ldy, ws, ws_bytes, stream)
+
+
+def aq_recon_linear_noalloc(dt, M, K, x, ldx, p, nproj, y, ldy, stream):
+    return lib().aq_recon_linear_noalloc(dt, M, K, x, ldx, _projs(p, nproj), nproj, y, ldy, stream)
 
 
 def aq_materialize_weff(dt, K, p, w_eff, ldw, stream):

@@ -7,7 +7,17 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "aq_internal.h"
+
+// Device memory of the allocation-free entry point (aq_recon_linear_noalloc):
+// one array per GPU, loaded with the code object and held until the process
+// ends.  On the host the name is only a stand-in, never a device address: host
+// code looks up each device's address (scratch_of_current_device) and passes
+// that to kernels.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -122,13 +132,34 @@ void make_plan(const aq::Recon &rq, Plan *pl) {
   pl->ws = pl->pf.ws_bytes;
 }
 
+// Zeroes n words (the hand-off counters of the library's own scratch before a
+// prefill launch that uses them): a kernel rather than a memset, so that a
+// caller may capture it in a HIP graph.
+__global__ void k_clear_words(unsigned *p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
+
+// `clear_counters`: the workspace is the library's own scratch, whose counters
+// are zeroed before each prefill launch that waits on them (its flag word is
+// kept for aq_workspace_check).
 aq_status recon(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx, const aq_proj *p,
-                int nproj, void *y, int64_t ldy, void *ws, size_t ws_bytes, void *stream) {
+                int nproj, void *y, int64_t ldy, void *ws, size_t ws_bytes, void *stream,
+                bool clear_counters = false) {
   aq::Recon rq;
   aq_status s = build_recon(dt, M, K, x, ldx, p, nproj, y, ldy, true, &rq);
   if (s != AQ_OK || M == 0) return s;
   Plan pl;
   make_plan(rq, &pl);
+  if (clear_counters && pl.ws > ws_bytes)
+    return fail(AQ_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of scratch; the allocation-free entry point holds at most %zu "
+                "(use aq_recon_* with a workspace)",
+                pl.ws, ws_bytes);
+  if (clear_counters && pl.path == P_PREFILL && pl.pf.fuse) {
+    hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(64), 0, (hipStream_t)stream, (unsigned *)ws, 2);
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e0));
+  }
   if (pl.ws > 0) {
     if (!ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", pl.ws);
     if (ws_bytes < pl.ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", pl.ws, ws_bytes);
@@ -142,6 +173,31 @@ aq_status recon(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx, c
     case P_PREFILL: e = aq::launch_prefill(rq, pl.pf, ws, st); break;
   }
   if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return AQ_OK;
+}
+
+// ---- the library's own scratch (aq_recon_linear_noalloc) -------------------
+// Each device's address of `scratch`, looked up once with that device current.
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use).
+aq_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(AQ_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(AQ_ERR_HIP, "looking up the scratch array on device %d failed: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return AQ_OK;
 }
 
@@ -170,6 +226,16 @@ aq_status aq_recon_gateup_fused(aq_dtype dt, int64_t M, int64_t K, const void *x
                                 int64_t ldx, const aq_proj p[2], void *y, int64_t ldy,
                                 void *ws, size_t ws_bytes, void *stream) {
   return recon(dt, M, K, x, ldx, p, 2, y, ldy, ws, ws_bytes, stream);
+}
+
+aq_status aq_recon_linear_noalloc(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
+                                  const aq_proj *p, int nproj, void *y, int64_t ldy, void *stream) {
+  if (nproj < 1 || nproj > aq::kMaxBlocks)
+    return fail(AQ_ERR_INVALID_ARG, "nproj = %d must be 1, 2 or 3", nproj);
+  void *ws = nullptr;
+  const aq_status s = scratch_of_current_device(&ws);
+  if (s != AQ_OK) return s;
+  return recon(dt, M, K, x, ldx, p, nproj, y, ldy, ws, kScratchBytes, stream, true);
 }
 
 aq_status aq_materialize_weff(aq_dtype dt, int64_t K, const aq_proj *p, void *w_eff,
@@ -299,7 +365,10 @@ const char *aq_status_string(aq_status s) {
 const char *aq_last_error(void) { return g_err; }
 
 aq_status aq_workspace_check(void *ws, void *stream) {
-  if (!ws) return AQ_OK;
+  if (!ws) {
+    const aq_status s = scratch_of_current_device(&ws);
+    if (s != AQ_OK) return s;
+  }
   if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);
   unsigned w[3] = {0, 0, 0};
