@@ -1,27 +1,43 @@
 """Benchmark of the theta-bundle reconstructed linear on one MI355X.
 
-Default workload (one JSON line on stdout): the Gemma-3-1B-shaped decoder,
-26 layers, bf16, rank 16, decode batches M = 1, 4 and 16 tokens.  One step is a
-full pass of all 26 layers at each of the three batch sizes; a layer is four
-dispatches (fused Q/K/V, o, fused gate/up, down).  The weights of all 26 layers
-(1.4 GB of W0) stay resident in HBM, far beyond the 256 MB Infinity Cache, and
-are visited in model order, so every dispatch streams its weights from HBM.
+Default run (one JSON line on stdout): the large-decoder-shaped model -- hidden
+5376; q 5376->4096, k/v 5376->2048, o 4096->5376, gate/up 5376->21504, down
+21504->5376 -- with 8 layers sharing W0 in 4 bands of 2 (per-layer s, U, Vt),
+rank 32, bf16.  One step is a full pass of the 8 layers at each of M = 1 and 32
+tokens (decode) and M = 512 tokens (prefill); a layer is four dispatches (fused
+Q/K/V, o, fused gate/up, down), every one captured in one HIP graph (launch cost
+excluded, as in serving).  All weights (3.3 GB of W0) stay resident in HBM.
 
-Other workloads (``--workload``): gemma_prefill (M = 512, 2048; rank 64),
-large_decoder (8 layers in 4 shared-W0 bands, rank 32, M = 1, 32, 512),
-materialize_fp4 (7 families x 26 layers, 13 bands, rank 64: W_eff then FP4).
+The line reports:
+* ``value``: microseconds per layer over the step (the sum of the three batch
+  sizes), from exactly ``--steps`` timed graph replays after ``--warmup``;
+* ``decode`` / ``prefill``: per batch size the median (p10, p90) of >= 50
+  replays, achieved HBM GB/s (decode) or MFMA TFLOP/s (prefill) as a fraction of
+  the MI355X peak, and the same stacked shapes as a dense ``torch.matmul``
+  (hipBLASLt) on a materialised-size weight in the same graph mode
+  (``recon_over_dense``);
+* ``roofline``: the kernel that takes the most time in the step (the prefill
+  gate/up dispatch), its algorithmic flops per launch over its average launch
+  duration (HIP events around graph replays that hold only those launches, on
+  the stream the graph runs on), against the bf16 dense MFMA peak;
+  ``roofline_decode``: the same for the decode gate/up dispatch at M = 1 against
+  the HBM peak; ``traffic`` from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+  (profiles/traffic.json), null when the kernel source has changed since;
+* ``cpu_baseline``: the fp64 oracle on a bounded sample of the same workload,
+  on this host's cores, in the same unit;
+* ``extra``: the Gemma-3-1B-shaped decode (26 layers, rank 16, M = 1, 4, 16),
+  prefill (rank 64, M = 512, 2048, against dense) and the load-time materialise
+  + FP4 pack of all 182 projections (13 bands, rank 64).
 
-The step is timed as a captured HIP graph (launch cost excluded, as in serving)
-and, for comparison, eagerly.  The dominant kernel is also timed per launch with
-HIP events on the launch stream, queued behind a GPU sleep so that no CPU launch
-gap falls inside an event pair.  The CPU baseline is the fp64 oracle on a bounded
-sample of the same workload, on this host's cores.
+Other workloads (``--workload``) print their own JSON: gemma_decode,
+gemma_prefill, large_decoder, materialize_fp4, fp4_decode, fold, rebuild, and
+the counter-run probes.
 """
 
 import argparse
-import ctypes
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -32,6 +48,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2516.6    # dense bf16 MFMA
+METRIC = "reconstructed-linear µs/layer + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
+DATA = "synthetic (seeded N(0,1/in) W0, U(0.9,1.1) s, N(0,0.02) U/V, N(0,1) x)"
 
 
 def log(*a):
@@ -47,11 +65,23 @@ class Call:
         self.fn, self.args = fn, args
         self.nbytes, self.flops, self.name, self.grid_key = nbytes, flops, name, grid_key
 
-    def __call__(self):
-        st = self.fn(*self.args)
+    def __call__(self, stream=None):
+        a = self.args if stream is None else self.args[:-1] + (stream,)
+        st = self.fn(*a)
         if st != 0:
             from rank_shared_block_amd import binding as B
             raise RuntimeError(f"{self.name}: {B.status_string(st)}: {B.last_error()}")
+
+
+class TorchCall:
+    """A dense baseline launch (torch.matmul into a preallocated output)."""
+
+    def __init__(self, torch, x, w, y, name, grid_key, flops):
+        self.torch, self.x, self.w, self.y = torch, x, w, y
+        self.name, self.grid_key, self.flops, self.nbytes = name, grid_key, flops, 0
+
+    def __call__(self, stream=None):
+        self.torch.matmul(self.x, self.w.t(), out=self.y)
 
 
 def _dispatch_bytes(M, K, bundles):
@@ -69,17 +99,16 @@ def _dispatch_flops(M, K, bundles):
     return f
 
 
-def make_recon_calls(torch, B, I, shapes, layer_dev, layer_np, M, x_tag, dtype="bf16"):
+def make_recon_calls(torch, B, I, workload, shapes, layer_dev, layer_np, M, x_tag):
     """Per layer, the four dispatches as pre-marshalled calls."""
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream().cuda_stream
-    calls = []
-    keep = []
+    calls, keep = [], []
     lib = B.lib()
     for l, fam_dev in enumerate(layer_dev):
         for name, fams in I.LAYER_DISPATCHES:
             K = shapes[fams[0]][0]
-            x = torch.from_numpy(I.activations("gemma_decode", x_tag + len(name), M, K, dtype)).to(dev).to(torch.bfloat16)
+            x = torch.from_numpy(I.activations(workload, x_tag + len(name), M, K, "bf16")).to(dev).to(torch.bfloat16)
             projs = [B.make_proj(*fam_dev[f]) for f in fams]
             arr = (B.aq_proj * len(fams))(*projs)
             ntot = sum(p.N for p in projs)
@@ -92,6 +121,24 @@ def make_recon_calls(torch, B, I, shapes, layer_dev, layer_np, M, x_tag, dtype="
             calls.append(Call(fn, args, _dispatch_bytes(M, K, nr), _dispatch_flops(M, K, nr), f"L{l}.{name}.M{M}", name))
             keep += [x, y, ws, arr]
     return calls, keep
+
+
+def make_dense_calls(torch, I, shapes, L, M):
+    """The same stacked shapes as plain dense GEMMs y = x W^T (torch.matmul,
+    hipBLASLt) on random bf16 weights of the materialised size, one per layer."""
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234 + M)
+    calls = []
+    for l in range(L):
+        for name, fams in I.LAYER_DISPATCHES:
+            K = shapes[fams[0]][0]
+            N = sum(shapes[f][1] for f in fams)
+            x = torch.randn(M, K, device=dev, dtype=torch.bfloat16, generator=g)
+            w = torch.randn(N, K, device=dev, dtype=torch.bfloat16, generator=g) * 0.03
+            y = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+            calls.append(TorchCall(torch, x, w, y, f"dense.L{l}.{name}.M{M}", name, 2 * M * K * N))
+    return calls
 
 
 def upload_layers(torch, I, layer_np):
@@ -111,60 +158,28 @@ def upload_layers(torch, I, layer_np):
 
 # --------------------------------------------------------------------------- timing
 
-def time_graph(torch, calls, steps, warmup):
-    """Capture `calls` in one HIP graph; replay warmup + steps; return ms per replay."""
+def capture(torch, calls):
+    """One HIP graph holding `calls` in order (eager warm-up first, on the
+    capture stream); the library calls are re-marshalled for that stream."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for c in calls:             # eager warm-up on the capture stream
-            c()
+        for c in calls:
+            c(torch.cuda.current_stream().cuda_stream)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        # the calls were marshalled with the ambient stream; re-marshal for the capture stream
         cap = torch.cuda.current_stream().cuda_stream
         for c in calls:
-            a = list(c.args)
-            a[-1] = cap
-            st = c.fn(*a)
-            assert st == 0, c.name
-    for _ in range(warmup):
-        g.replay()
+            c(cap)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, g
+    return g
 
 
-def time_graph_streams(torch, calls, nstreams, steps, warmup):
-    """Like time_graph, but the calls (independent of each other) are issued
-    round-robin on `nstreams` streams forked from and joined back to the capture
-    stream, as a loader issues independent projections."""
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for c in calls:
-            c()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    side = [torch.cuda.Stream() for _ in range(nstreams)]
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        cap = torch.cuda.current_stream()
-        for st in side:
-            st.wait_stream(cap)
-        for i, c in enumerate(calls):
-            st = side[i % nstreams]
-            a = list(c.args)
-            a[-1] = st.cuda_stream
-            assert c.fn(*a) == 0, c.name
-        for st in side:
-            cap.wait_stream(st)
+def time_steps(torch, g, steps, warmup):
+    """`warmup` untimed replays, then exactly `steps` replays between two
+    synchronisations; ms per replay."""
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -175,6 +190,63 @@ def time_graph_streams(torch, calls, nstreams, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def replay_stats(torch, g, reps, warmup=3):
+    """Median, p10 and p90 (ms) of `reps` replays, each between its own events."""
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)),
+            "p90": float(np.percentile(t, 90)), "n": int(reps)}
+
+
+def time_graph(torch, calls, steps, warmup):
+    g = capture(torch, calls)
+    return time_steps(torch, g, steps, warmup), g
+
+
+def time_per_launch(torch, calls, reps):
+    """Average duration of one launch of `calls`: HIP events around replays of
+    a graph that holds only these launches back to back, on the stream the
+    graph runs on.  Consecutive kernels of a graph abut on the GPU, so this is
+    the average kernel duration (start to start) that rocprofv3 reports for the
+    same launches."""
+    g = capture(torch, calls)
+    st = replay_stats(torch, g, reps, 2)
+    del g
+    return st["median"] / len(calls)
+
+
+def time_graph_streams(torch, calls, nstreams, steps, warmup):
+    """Like time_graph, but the calls (independent of each other) are issued
+    round-robin on `nstreams` streams forked from and joined back to the capture
+    stream, as a loader issues independent projections."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in calls:
+            c(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    side = [torch.cuda.Stream() for _ in range(nstreams)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream()
+        for st in side:
+            st.wait_stream(cap)
+        for i, c in enumerate(calls):
+            c(side[i % nstreams].cuda_stream)
+        for st in side:
+            cap.wait_stream(st)
+    return time_steps(torch, g, steps, warmup)
 
 
 def time_eager(torch, calls, steps, warmup):
@@ -192,57 +264,87 @@ def time_eager(torch, calls, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def time_per_launch(torch, calls, reps):
-    """Average duration of one launch of `calls`' kernel: HIP events around
-    replays of a graph that holds only these launches back to back, on the
-    stream the graph runs on.  Consecutive kernels of a graph abut on the GPU,
-    so this equals the average kernel duration that rocprofv3 reports for the
-    same replays (start to start)."""
-    ms, _ = time_graph(torch, calls, reps, 2)
-    return ms / len(calls)
+def _r(x, n=3):
+    return None if x is None else round(float(x), n)
+
+
+# --------------------------------------------------------------------------- host facts
+
+def blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    except Exception as e:          # noqa: BLE001 -- informational only
+        return {"error": str(e)}
+    if not info:
+        return {"vendor": None}
+    p = info[0]
+    return {"vendor": p.get("internal_api"), "version": p.get("version"), "threads": p.get("num_threads"),
+            "architecture": p.get("architecture")}
+
+
+def gpu_clocks():
+    """Current GPU clocks as amd-smi reports them (child process; best effort)."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(r.stdout)
+    except Exception as e:          # noqa: BLE001 -- informational only
+        return {"error": str(e)[:200]}
+    out = {}
+    try:
+        gpus = data.get("gpu_data", data) if isinstance(data, dict) else data
+        clk = gpus[0]["clock"]
+        gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_") and isinstance(v, dict)]
+        out["gfx_mhz_min_max"] = [min(gfx), max(gfx)] if gfx else None
+        for k in ("mem_0", "fclk_0", "socclk_0"):
+            if isinstance(clk.get(k), dict):
+                out[k.replace("_0", "_mhz")] = clk[k]["clk"]["value"]
+    except Exception as e:          # noqa: BLE001 -- informational only
+        out["error"] = str(e)[:200]
+    return out
 
 
 # --------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(I, layer_np, shapes, Ms, x_tag, budget_s, layers_sample):
-    """The oracle on a bounded sample: `layers_sample` layers, every M, repeated
-    until `budget_s` of oracle time; returns GB/s of algorithmic bytes."""
+def cpu_baseline_layers(I, workload, shapes, layer_np, Ms, x_tag, layers, reps, per_m_layers=None):
+    """The oracle (numpy float64, this host's BLAS threads) on a bounded sample:
+    the four dispatches of `layers` at every M, each timed `reps` times (median),
+    operands converted to float64 per projection outside the timed region.
+    Returns microseconds per layer per M and their sum."""
     import oracle
-    from threadpoolctl import threadpool_info
-    ls = sorted(layer_np)[:layers_sample]
-    conv = {}
-    for l in ls:
-        for f, bd in layer_np[l].items():
-            conv[(l, f)] = tuple(bd[k].astype(np.float64) for k in ("W0", "s", "U", "Vt"))
-    xs = {}
+    per_m = {}
+    conv_s = 0.0
     for M in Ms:
-        for name, fams in I.LAYER_DISPATCHES:
-            K = shapes[fams[0]][0]
-            xs[(M, name)] = I.activations("gemma_decode", x_tag(M) + len(name), M, K, "bf16").astype(np.float64)
-    nbytes, t_used, passes = 0, 0.0, 0
-    while t_used < budget_s:
-        for M in Ms:
-            for l in ls:
-                for name, fams in I.LAYER_DISPATCHES:
-                    K = shapes[fams[0]][0]
+        ls = layers if per_m_layers is None else per_m_layers.get(M, layers)
+        tot = 0.0
+        for l in ls:
+            for name, fams in I.LAYER_DISPATCHES:
+                K = shapes[fams[0]][0]
+                t0 = time.perf_counter()
+                bds = [tuple(layer_np[l][f][k].astype(np.float64) for k in ("W0", "s", "U", "Vt")) for f in fams]
+                x = I.activations(workload, x_tag(M) + len(name), M, K, "bf16").astype(np.float64)
+                conv_s += time.perf_counter() - t0
+                ts = []
+                for _ in range(reps):
                     t0 = time.perf_counter()
-                    oracle.recon_fused(xs[(M, name)], [conv[(l, f)] for f in fams])
-                    t_used += time.perf_counter() - t0
-                    nbytes += _dispatch_bytes(M, K, [(shapes[f][1], conv[(l, f)][2].shape[1]) for f in fams])
-        passes += 1
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": round(nbytes / t_used / 1e9, 3), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(ls)} of 26 layers x M in {list(Ms)} x 4 dispatches, {passes} passes, "
-                      f"{t_used:.1f} s of numpy float64 oracle time (bf16->fp64 conversion excluded)"}
+                    oracle.recon_fused(x, bds)
+                    ts.append(time.perf_counter() - t0)
+                tot += float(np.median(ts))
+                del bds
+        per_m[f"M{M}"] = round(tot / len(ls) * 1e6, 1)
+    return per_m, conv_s
 
 
 # --------------------------------------------------------------------------- counters
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 SOURCES = {"decode_gateup": "rank_shared_block_amd/csrc/recon_decode.hip",
+           "decode_gateup_large": "rank_shared_block_amd/csrc/recon_decode.hip",
+           "prefill_gateup_large": "rank_shared_block_amd/csrc/recon_prefill.hip",
            "fp4_gemv_gateup": "rank_shared_block_amd/csrc/fp4_gemv.hip"}
-PMC_KERNELS = {"decode_gateup": (("k_decode_bf16",), "k_decode_bf16 (fused gate/up)"),
+PMC_KERNELS = {"decode_gateup": (("k_decode_bf16",), "k_decode_bf16 (fused gate/up, Gemma-3-1B-shaped)"),
+               "decode_gateup_large": (("k_decode_bf16",), "k_decode_bf16 (gate/up, large-decoder-shaped, M = 1)"),
+               "prefill_gateup_large": (("k_gemm_bf16",), "k_gemm_bf16 (gate/up, large-decoder-shaped, M = 512)"),
                "fp4_gemv_gateup": (("k_fp4_gemv", "<2, false>"), "k_fp4_gemv / k_fp4_gemv_m4 (FP4 stacked gate/up)")}
 
 
@@ -265,44 +367,56 @@ def read_traffic(key):
     return t.get("bytes_per_launch")
 
 
-def run_pmc_probe(args, torch, B, I):
-    """Workload for the counter runs: a plain copy of known size (calibration),
-    then the 78 fused gate/up launches of a bench step, eagerly."""
+CALIB_BYTES = 256 * 2 ** 20
+
+
+def _calibration_copy(torch):
     dev = torch.device("cuda", 0)
     src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    layer_np = I.layer_bundles("gemma_decode", I.GEMMA_1B, layers=26, r=16, dtype="bf16",
-                               families=("gate", "up"))
+
+
+def run_pmc_probe(args, torch, B, I):
+    """Workload for the counter runs: a plain copy of known size (calibration),
+    then the dispatches named by --probe, eagerly:
+    decode_gateup (Gemma-3-1B fused gate/up, 26 layers x M in {1, 4, 16}),
+    decode_gateup_large (large-decoder gate/up at M = 1, 8 layers),
+    prefill_gateup_large (large-decoder gate/up at M = 512, 8 layers)."""
+    _calibration_copy(torch)
+    probe = args.probe
+    if probe == "decode_gateup":
+        wl, shapes, L, G, r, Ms = "gemma_decode", I.GEMMA_1B, 26, None, 16, (1, 4, 16)
+    else:
+        wl, shapes, L, G, r = "large_decoder", I.LARGE_DECODER, 8, 4, 32
+        Ms = (1,) if probe == "decode_gateup_large" else (512,)
+    layer_np = I.layer_bundles(wl, shapes, layers=L, r=r, dtype="bf16", num_bands=G, families=("gate", "up"))
     layer_dev = upload_layers(torch, I, layer_np)
-    for M in (1, 4, 16):
-        lib = B.lib()
-        stream = torch.cuda.current_stream().cuda_stream
-        for l in range(26):
-            x = torch.from_numpy(I.activations("gemma_decode", 10 * M + 6, M, 1152, "bf16")).to(dev).to(torch.bfloat16)
+    dev = torch.device("cuda", 0)
+    lib = B.lib()
+    K = shapes["gate"][0]
+    N = 2 * shapes["gate"][1]
+    for M in Ms:
+        x = torch.from_numpy(I.activations(wl, 10 * M + 6, M, K, "bf16")).to(dev).to(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        for l in range(L):
             arr = (B.aq_proj * 2)(*[B.make_proj(*layer_dev[l][f]) for f in ("gate", "up")])
-            y = torch.empty((M, 13824), dtype=torch.bfloat16, device=dev)
-            need = lib.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, M, 1152, arr, 2)
+            need = lib.aq_workspace_bytes(B.AQ_OP_RECON, B.AQ_BF16, M, K, arr, 2)
             ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
-            st = lib.aq_recon_gateup_fused(B.AQ_BF16, M, 1152, x.data_ptr(), 1152, arr, y.data_ptr(), 13824,
-                                           ws.data_ptr(), ws.numel(), stream)
-            assert st == 0
+            B.check(lib.aq_recon_gateup_fused(B.AQ_BF16, M, K, x.data_ptr(), K, arr, y.data_ptr(), N,
+                                              ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
-    return {"probe": "copy of %d bytes, then 78 fused gate/up decode launches" % CALIB_BYTES}
+    return {"probe": f"copy of {CALIB_BYTES} bytes, then {probe}: {L} layers x M in {list(Ms)}"}
 
 
 def run_pmc_probe_fp4(args, torch, B, I):
     """Counter-run workload for the FP4 GEMV: the copy calibration, then 78
     stacked gate/up launches (13824 x 1152 packed; 26 layers, each its own
     weight, x M in {1, 4, 16}), eagerly."""
+    _calibration_copy(torch)
     dev = torch.device("cuda", 0)
-    src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
     N, K = 13824, 1152
     g = torch.Generator(device=dev)
     g.manual_seed(5)
@@ -315,9 +429,6 @@ def run_pmc_probe_fp4(args, torch, B, I):
             B.fp4_linear(x, *packs[l], y=y)
     torch.cuda.synchronize()
     return {"probe": "copy of %d bytes, then 78 FP4 stacked gate/up GEMV launches" % CALIB_BYTES}
-
-
-CALIB_BYTES = 256 * 2 ** 20
 
 
 def summarize_profiles(args):
@@ -339,9 +450,9 @@ def summarize_profiles(args):
             agg[(r["Kernel_Name"], wg)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         out.append("| kernel | workgroups | launches | avg us | median us | total us |")
         out.append("|---|---|---|---|---|---|")
-        for (name, wg), d in sorted(agg.items(), key=lambda kv: -sum(kv[1]))[:14]:
+        for (name, wg), d in sorted(agg.items(), key=lambda kv: -sum(kv[1]))[:args.top]:
             d.sort()
-            out.append(f"| `{name[:80]}` | {wg} | {len(d)} | {sum(d)/len(d):.3f} | {d[len(d)//2]:.3f} | {sum(d):.1f} |")
+            out.append(f"| `{name[:90]}` | {wg} | {len(d)} | {sum(d)/len(d):.3f} | {d[len(d)//2]:.3f} | {sum(d):.1f} |")
         if args.calls:
             # A prefill call is its kernels in launch order up to the main GEMM
             # (MODE 0, which may also run the rank-r pass in its first
@@ -354,13 +465,12 @@ def summarize_profiles(args):
                 name = r["Kernel_Name"].split("(")[0].replace("void aq::", "").replace("aq::", "")
                 wg = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1) // int(r["Workgroup_Size_X"])
                 seq.append((name, wg, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+
             def mode(n):             # k_gemm_bf16<BM, BN, BK, NST, MODE, NW>
                 return int(n[n.index("<") + 1:-1].split(", ")[4]) if n.startswith("k_gemm_bf16<") else -1
             calls, cur = collections.defaultdict(list), []
             for k in seq:
                 cur.append(k)
-                # a call ends with its main pass (MODE 0, or 3: tiles with their
-                # own t), or with the fold after a K-split main pass (MODE 1)
                 if mode(k[0]) in (0, 3) or (k[0] == "k_prefill_reduce" and any(mode(c[0]) == 1 for c in cur)):
                     calls[tuple((c[0], c[1]) for c in cur)].append([c[2] for c in cur])
                     cur = []
@@ -373,11 +483,12 @@ def summarize_profiles(args):
                 out.append(f"| {len(runs)} | {parts} | {sum(means):.2f} |")
     if args.fetch and args.write:
         res = {}
+        match = tuple(args.kernel_match.split("|")) if args.kernel_match else PMC_KERNELS[args.traffic_key][0]
         for key, path in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
             rs = rows(path)
             val = lambda r: float(r.get("Counter_Value", r.get("value", 0)))
             copy = [val(r) for r in rs if "copyBuffer" in r["Kernel_Name"]]
-            dec = [val(r) for r in rs if all(k in r["Kernel_Name"] for k in PMC_KERNELS[args.traffic_key][0])]
+            dec = [val(r) for r in rs if all(k in r["Kernel_Name"] for k in match)]
             res[key] = (max(copy) if copy else None, float(np.mean(dec)) if dec else None, len(dec))
         # scale: a copy of CALIB_BYTES reads and writes CALIB_BYTES each
         fscale = CALIB_BYTES / (res["FETCH_SIZE"][0] * 1024)
@@ -388,9 +499,9 @@ def summarize_profiles(args):
         out.append(f"FETCH_SIZE copy calibration: {res['FETCH_SIZE'][0]:.0f} KiB for {CALIB_BYTES} B read "
                    f"(scale {fscale:.4f}); WRITE_SIZE: {res['WRITE_SIZE'][0]:.0f} KiB for {CALIB_BYTES} B written "
                    f"(scale {wscale:.4f}).")
-        out.append(f"{PMC_KERNELS[args.traffic_key][1]}, mean over {res['FETCH_SIZE'][2]} launches: "
-                   f"fetch {fetch_b/1e6:.3f} MB, write {write_b/1e6:.3f} MB per launch "
-                   f"(scaled), total {(fetch_b + write_b)/1e6:.3f} MB.")
+        out.append(f"{PMC_KERNELS[args.traffic_key][1]} (kernel name containing {list(match)}), mean over "
+                   f"{res['FETCH_SIZE'][2]} launches: fetch {fetch_b/1e6:.3f} MB, write {write_b/1e6:.3f} MB per "
+                   f"launch (scaled), total {(fetch_b + write_b)/1e6:.3f} MB.")
         t = {}
         try:
             with open(TRAFFIC_FILE) as f:
@@ -399,147 +510,233 @@ def summarize_profiles(args):
             pass
         t[args.traffic_key] = {"bytes_per_launch": int(fetch_b + write_b), "fetch_bytes": int(fetch_b),
                                "write_bytes": int(write_b), "fetch_scale": fscale, "write_scale": wscale,
+                               "launches": res["FETCH_SIZE"][2],
                                "source_sha256_16": source_digest(SOURCES[args.traffic_key])}
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(t, f, indent=1)
+    if args.pmc:
+        # any other counter run (e.g. MFMA busy): mean per kernel-name match
+        rs = rows(args.pmc)
+        match = tuple(args.kernel_match.split("|")) if args.kernel_match else ("aq::",)
+        agg = collections.defaultdict(list)
+        for r in rs:
+            if all(k in r["Kernel_Name"] for k in match):
+                agg[r.get("Counter_Name", "?")].append(float(r.get("Counter_Value", r.get("value", 0))))
+        out.append("")
+        out.append(f"Counters for kernels whose name contains {list(match)}:")
+        out.append("")
+        out.append("| counter | launches | mean per launch |")
+        out.append("|---|---|---|")
+        for name, v in sorted(agg.items()):
+            out.append(f"| {name} | {len(v)} | {np.mean(v):.1f} |")
     print("\n".join(out))
 
 
-# --------------------------------------------------------------------------- workloads
+# --------------------------------------------------------------------------- model workloads
 
-def run_gemma_decode(args, torch, B, I):
-    Ms = (1, 4, 16)
-    L = 26
-    t0 = time.time()
-    layer_np = I.layer_bundles("gemma_decode", I.GEMMA_1B, layers=L, r=16, dtype="bf16")
-    log(f"generated inputs in {time.time() - t0:.1f} s")
-    layer_dev = upload_layers(torch, I, layer_np)
-    torch.cuda.synchronize()
-    log(f"uploaded {L} layers")
-    xtag = lambda M: 10 * M
-    per_M = {}
-    all_calls = []
-    keep = []
-    for M in Ms:
-        calls, k = make_recon_calls(torch, B, I, I.GEMMA_1B, layer_dev, layer_np, M, xtag(M))
-        keep += k
-        per_M[M] = calls
-        all_calls += calls
-    step_bytes = sum(c.nbytes for c in all_calls)
+class Model:
+    """A decoder's bundles resident on the GPU, its recon calls and its dense
+    baseline calls per batch size."""
 
-    # Headline: one graph for the whole step.
-    ms_step, g = time_graph(torch, all_calls, args.steps, args.warmup)
-    log(f"graph step: {ms_step:.4f} ms")
-    us_layer = {}
-    for M in Ms:
-        ms, _ = time_graph(torch, per_M[M], max(5, args.steps // 2), 2)
-        us_layer[f"M{M}"] = round(ms * 1e3 / L, 3)
-    ms_eager = time_eager(torch, all_calls, max(3, args.steps // 4), 1)
+    def __init__(self, torch, B, I, workload, shapes, L, G, r, Ms, x_tag, dense=True):
+        t0 = time.time()
+        self.I, self.workload, self.shapes, self.L, self.r, self.Ms = I, workload, shapes, L, r, Ms
+        self.layer_np = I.layer_bundles(workload, shapes, layers=L, r=r, dtype="bf16", num_bands=G)
+        log(f"{workload}: generated inputs in {time.time() - t0:.1f} s")
+        self.layer_dev = upload_layers(torch, I, self.layer_np)
+        torch.cuda.synchronize()
+        self.x_tag = x_tag
+        self.calls, self.keep, self.dense = {}, [], {}
+        for M in Ms:
+            c, k = make_recon_calls(torch, B, I, workload, shapes, self.layer_dev, self.layer_np, M, x_tag(M))
+            self.calls[M] = c
+            self.keep += k
+            if dense:
+                self.dense[M] = make_dense_calls(torch, I, shapes, L, M)
+        log(f"{workload}: uploaded {L} layers")
 
-    # Dominant kernel: the fused gate/up dispatch (59% of the bytes of a layer).
-    gu = [c for c in all_calls if c.grid_key == "gateup"]
-    avg_ms = time_per_launch(torch, gu, max(5, args.roofline_reps))
-    gu_bytes = float(np.mean([c.nbytes for c in gu]))
-    achieved = gu_bytes / (avg_ms * 1e-3) / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode_gateup"),
-            "kernel": "k_decode_bf16 (fused gate/up, K=1152, N=2x6912, r=16, M in {1,4,16}, 26 layers)",
-            "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(avg_ms * 1e3, 3),
-            "launches_per_replay": len(gu)}
 
+def measure_model(torch, mdl, reps, prefill_Ms):
+    """Per batch size: recon graph median/p10/p90, bytes and flops, and the dense
+    baseline in the same graph mode."""
+    out = {}
+    for M in mdl.Ms:
+        calls = mdl.calls[M]
+        g = capture(torch, calls)
+        st = replay_stats(torch, g, reps)
+        del g
+        ms = st["median"]
+        nb = sum(c.nbytes for c in calls)
+        fl = sum(c.flops for c in calls)
+        res = {"us_per_layer": _r(ms * 1e3 / mdl.L, 2),
+               "us_per_layer_p10": _r(st["p10"] * 1e3 / mdl.L, 2), "us_per_layer_p90": _r(st["p90"] * 1e3 / mdl.L, 2)}
+        if M in prefill_Ms:
+            res.update({"tflops": _r(fl / (ms * 1e-3) / 1e12, 1),
+                        "frac_mfma_peak": _r(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)})
+        else:
+            res.update({"GBps": _r(nb / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm_peak": _r(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        if M in mdl.dense:
+            gd = capture(torch, mdl.dense[M])
+            sd = replay_stats(torch, gd, reps)
+            del gd
+            dfl = sum(c.flops for c in mdl.dense[M])
+            res.update({"dense_us_per_layer": _r(sd["median"] * 1e3 / mdl.L, 2),
+                        "dense_tflops": _r(dfl / (sd["median"] * 1e-3) / 1e12, 1),
+                        "recon_over_dense": _r(ms / sd["median"], 3)})
+        res["replays"] = st["n"]
+        out[f"M{M}"] = res
+    return out
+
+
+def dominant(torch, mdl, reps):
+    """Per-launch time of every dispatch kind at every M: {(M, kind): ms}."""
+    d = {}
+    for M in mdl.Ms:
+        for kind, _ in mdl.I.LAYER_DISPATCHES:
+            cs = [c for c in mdl.calls[M] if c.grid_key == kind]
+            d[(M, kind)] = (time_per_launch(torch, cs, reps), cs)
+    return d
+
+
+def roofline_of(M, kind, ms, cs, prefill_Ms, traffic_key, what):
+    fl = float(np.mean([c.flops for c in cs]))
+    nb = float(np.mean([c.nbytes for c in cs]))
+    if M in prefill_Ms:
+        ach = fl / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": _r(ach, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": _r(ach / MFMA_BF16_PEAK_TFS, 4), "flops_per_launch": int(fl)}
+    else:
+        ach = nb / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": _r(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": _r(ach / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": read_traffic(traffic_key) if traffic_key else None,
+                 "bytes_per_launch": int(nb), "avg_launch_us": _r(ms * 1e3, 3), "launches_per_replay": len(cs),
+                 "kernel": what})
+    return roof
+
+
+def run_headline(args, torch, B, I):
+    Ms, PF = (1, 32, 512), (512,)
+    L = 8
+    clocks0 = gpu_clocks()
+    mdl = Model(torch, B, I, "large_decoder", I.LARGE_DECODER, L, 4, 32, Ms, lambda M: 9 * M)
+    step_calls = [c for M in Ms for c in mdl.calls[M]]
+    g = capture(torch, step_calls)
+    ms_step = time_steps(torch, g, args.steps, args.warmup)
+    del g
+    log(f"large decoder step: {ms_step:.4f} ms")
+    reps = max(50, args.steps)
+    per_m = measure_model(torch, mdl, reps, PF)
+    dom = dominant(torch, mdl, max(10, args.roofline_reps))
+    tot = {k: v[0] * len(v[1]) for k, v in dom.items()}
+    (Mk, kind) = max(tot, key=tot.get)
+    roof = roofline_of(Mk, kind, dom[(Mk, kind)][0], dom[(Mk, kind)][1], PF,
+                       "prefill_gateup_large" if (Mk, kind) == (512, "gateup") else None,
+                       f"{kind} dispatch at M = {Mk} (large-decoder-shaped, rank 32, {L} layers): "
+                       + ("k_gemm_bf16 main pass with the rank-r tiles in the same launch" if Mk in PF else
+                          "k_decode_bf16"))
+    roof_dec = roofline_of(1, "gateup", dom[(1, "gateup")][0], dom[(1, "gateup")][1], PF, "decode_gateup_large",
+                           f"gate/up dispatch at M = 1 (K = 5376, N = 2 x 21504, rank 32, {L} layers): k_decode_bf16")
+    share = {f"M{M}.{k}": _r(v / sum(tot.values()), 3) for (M, k), v in sorted(tot.items(), key=lambda kv: -kv[1])}
+    step_bytes = sum(c.nbytes for M in Ms if M not in PF for c in mdl.calls[M])
+    step_flops = sum(c.flops for M in PF for c in mdl.calls[M])
     line = {
-        "metric": "reconstructed-linear µs/layer + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)",
-        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
-        "unit": "GB/s",
+        "metric": METRIC,
+        "value": _r(ms_step * 1e3 / L, 2),
+        "unit": "us/layer (M=1 + M=32 + M=512)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded N(0,1/in) W0, U(0.9,1.1) s, N(0,0.02) U/V, N(0,1) x)",
-        "config": {"workload": "gemma-3-1b-shaped decode: 26 layers x (fused QKV, o, fused gate/up, down), "
-                               "hidden 1152, rank 16, bf16, M in {1,4,16} tokens per step",
-                   "layers": L, "rank": 16, "tokens": list(Ms), "launch": "hip graph per step"},
-        "us_per_layer": us_layer,
-        "frac_of_hbm_peak_step": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "ms_per_step_eager": round(ms_eager, 4),
-        "bytes_per_step": int(step_bytes),
+        "ms_per_step": _r(ms_step, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": DATA,
+        "config": {"workload": "large-decoder-shaped: 8 layers, W0 shared in 4 bands of 2, x (fused QKV, o, "
+                               "fused gate/up, down), hidden 5376, rank 32, bf16, M in {1, 32, 512} tokens per step",
+                   "layers": L, "bands": 4, "rank": 32, "tokens": list(Ms), "launch": "hip graph per step",
+                   "note": "the second layer of a band reads the same W0 (826 MB per layer, > the 256 MB "
+                           "Infinity Cache): effective, MALL-assisted at most marginally"},
+        "decode": {k: v for k, v in per_m.items() if int(k[1:]) not in PF},
+        "prefill": {k: v for k, v in per_m.items() if int(k[1:]) in PF},
+        "decode_GBps_step": _r(step_bytes / (sum(per_m[f"M{M}"]["us_per_layer"] for M in Ms if M not in PF)
+                                              * L * 1e-6) / 1e9, 1),
+        "prefill_tflops_step": _r(step_flops / (sum(per_m[f"M{M}"]["us_per_layer"] for M in PF) * L * 1e-6) / 1e12, 1),
         "roofline": roof,
+        "roofline_decode": roof_dec,
+        "time_share_by_dispatch": share,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(I, layer_np, I.GEMMA_1B, Ms, xtag, args.cpu_budget, 4)
+        t0 = time.time()
+        per, conv = cpu_baseline_layers(I, "large_decoder", I.LARGE_DECODER, mdl.layer_np, Ms, mdl.x_tag,
+                                        layers=[0, 1], reps=3, per_m_layers={512: [0]})
+        bl = blas_info()
+        line["cpu_baseline"] = {
+            "value": _r(sum(per.values()), 1), "unit": "us/layer (M=1 + M=32 + M=512)",
+            "cores": int(bl.get("threads") or os.cpu_count() or 1), "kind": "oracle",
+            "sample": f"layers 0 and 1 (one W0 band) at M = 1 and 32, layer 0 at M = 512; all four dispatches; "
+                      f"median of 3 runs each; numpy float64 ({bl.get('vendor')} {bl.get('version')}, "
+                      f"{bl.get('threads')} threads); bf16->fp64 conversion ({conv:.1f} s) excluded",
+            "per_M_us_per_layer": per, "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "blas": bl, "wall_s": _r(time.time() - t0, 1)}
+    del mdl
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        line["extra"] = {}
+        for name, fn in (("gemma_decode", run_gemma_decode), ("gemma_prefill", run_gemma_prefill),
+                         ("materialize_fp4", run_materialize_fp4)):
+            t0 = time.time()
+            line["extra"][name] = fn(args, torch, B, I, nested=True)
+            torch.cuda.empty_cache()
+            log(f"extra {name}: {time.time() - t0:.1f} s")
+    line["clocks"] = {"before": clocks0, "after": gpu_clocks()}
     return line
 
 
-def run_gemma_prefill(args, torch, B, I):
+def run_gemma_decode(args, torch, B, I, nested=False):
+    Ms = (1, 4, 16)
+    L = 26
+    mdl = Model(torch, B, I, "gemma_decode", I.GEMMA_1B, L, None, 16, Ms, lambda M: 10 * M, dense=True)
+    step = [c for M in Ms for c in mdl.calls[M]]
+    g = capture(torch, step)
+    ms_step = time_steps(torch, g, args.steps, args.warmup)
+    del g
+    step_bytes = sum(c.nbytes for c in step)
+    per_m = measure_model(torch, mdl, max(50, args.steps), ())
+    gu = [c for c in step if c.grid_key == "gateup"]
+    ms = time_per_launch(torch, gu, max(10, args.roofline_reps))
+    roof = roofline_of(1, "gateup", ms, gu, (), "decode_gateup",
+                       "k_decode_bf16 (fused gate/up, K=1152, N=2x6912, r=16, M in {1,4,16}, 26 layers)")
+    res = {"workload": "gemma-3-1b-shaped decode: 26 layers x (fused QKV, o, fused gate/up, down), hidden 1152, "
+                       "rank 16, bf16, M in {1, 4, 16}",
+           "ms_per_step": _r(ms_step, 4), "GBps_step": _r(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+           "frac_hbm_peak_step": _r(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "results": per_m, "roofline": roof}
+    if not nested:
+        res = {"metric": METRIC, "value": res["GBps_step"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+               "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": DATA,
+               "config": {"workload": res["workload"]}, **res}
+        if not args.no_cpu_baseline:
+            per, conv = cpu_baseline_layers(I, "gemma_decode", I.GEMMA_1B, mdl.layer_np, Ms, mdl.x_tag,
+                                            layers=[0, 1, 2, 3], reps=5)
+            res["cpu_baseline"] = {"per_M_us_per_layer": per, "kind": "oracle", "blas": blas_info()}
+    return res
+
+
+def run_gemma_prefill(args, torch, B, I, nested=False):
     Ms = (512, 2048)
     L = args.layers or 26
-    layer_np = I.layer_bundles("gemma_prefill", I.GEMMA_1B, layers=L, r=64, dtype="bf16")
-    layer_dev = upload_layers(torch, I, layer_np)
-    res = {}
-    for M in Ms:
-        calls, keep = make_recon_calls(torch, B, I, I.GEMMA_1B, layer_dev, layer_np, M, 5 * M)
-        ms, _ = time_graph(torch, calls, args.steps, args.warmup)
-        fl = sum(c.flops for c in calls)
-        # dense baseline: torch.matmul (hipBLASLt) on W_eff of the identical stacked shapes
-        dense = []
-        dev = torch.device("cuda", 0)
-        for l in range(L):
-            for name, fams in I.LAYER_DISPATCHES:
-                K = I.GEMMA_1B[fams[0]][0]
-                N = sum(I.GEMMA_1B[f][1] for f in fams)
-                dense.append((torch.randn(M, K, device=dev, dtype=torch.bfloat16),
-                              torch.randn(N, K, device=dev, dtype=torch.bfloat16) * 0.03))
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        outs = []
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for x, w in dense:
-                torch.matmul(x, w.t())
-        torch.cuda.current_stream().wait_stream(s)
-        with torch.cuda.graph(g):
-            for x, w in dense:
-                outs.append(torch.matmul(x, w.t()))
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms_dense = e0.elapsed_time(e1) / args.steps
-        dfl = sum(2 * x.shape[0] * x.shape[1] * w.shape[0] for x, w in dense)
-        res[f"M{M}"] = {"us_per_layer": round(ms * 1e3 / L, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-                        "frac_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
-                        "dense_us_per_layer": round(ms_dense * 1e3 / L, 2),
-                        "dense_tflops": round(dfl / (ms_dense * 1e-3) / 1e12, 1),
-                        "recon_over_dense": round(ms / ms_dense, 3)}
-        del dense, outs, g
-    return {"workload": f"gemma-3-1b-shaped prefill, {L} layers, rank 64, bf16", "results": res}
+    mdl = Model(torch, B, I, "gemma_prefill", I.GEMMA_1B, L, None, 64, Ms, lambda M: 5 * M)
+    per_m = measure_model(torch, mdl, max(50, args.steps) if not nested else 50, Ms)
+    return {"workload": f"gemma-3-1b-shaped prefill, {L} layers, rank 64, bf16", "results": per_m}
 
 
-def run_large_decoder(args, torch, B, I):
+def run_large_decoder(args, torch, B, I, nested=False):
     Ms = (1, 32, 512)
-    L = 8
-    layer_np = I.layer_bundles("large_decoder", I.LARGE_DECODER, layers=L, r=32, dtype="bf16", num_bands=4)
-    layer_dev = upload_layers(torch, I, layer_np)
-    res = {}
-    for M in Ms:
-        calls, keep = make_recon_calls(torch, B, I, I.LARGE_DECODER, layer_dev, layer_np, M, 9 * M)
-        ms, _ = time_graph(torch, calls, args.steps, args.warmup)
-        nb = sum(c.nbytes for c in calls)
-        fl = sum(c.flops for c in calls)
-        res[f"M{M}"] = {"us_per_layer": round(ms * 1e3 / L, 2),
-                        "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
-                        "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
-                        "note": "bands of 2 layers share W0: the second layer may hit the Infinity Cache"}
-    return {"workload": "large-decoder-shaped, 8 layers in 4 W0 bands, rank 32, bf16", "results": res}
+    mdl = Model(torch, B, I, "large_decoder", I.LARGE_DECODER, 8, 4, 32, Ms, lambda M: 9 * M)
+    per_m = measure_model(torch, mdl, max(50, args.steps), (512,))
+    return {"workload": "large-decoder-shaped, 8 layers in 4 W0 bands, rank 32, bf16", "results": per_m}
 
 
-def run_materialize_fp4(args, torch, B, I):
+def run_materialize_fp4(args, torch, B, I, nested=False):
     L, G = 26, 13
     layer_np = I.layer_bundles("materialize_fp4", I.GEMMA_1B, layers=L, r=64, dtype="bf16", num_bands=G)
     layer_dev = upload_layers(torch, I, layer_np)
@@ -568,30 +765,30 @@ def run_materialize_fp4(args, torch, B, I):
             keep += [w, packed, sc, gs, ws, pa]
             mbytes += mats[-1].nbytes
             pbytes += packs[-1].nbytes
-    ms_m, _ = time_graph(torch, mats, args.steps, args.warmup)
-    ms_p, _ = time_graph(torch, packs, args.steps, args.warmup)
-    ms_m4 = time_graph_streams(torch, mats, 4, args.steps, args.warmup)
-    ms_p4 = time_graph_streams(torch, packs, 4, args.steps, args.warmup)
-    mat_avg = time_per_launch(torch, mats, 2)
-    # the largest projections alone (gate, up, down: 6912 x 1152 elements)
+    steps, warm = (10, 2) if nested else (args.steps, args.warmup)
+    ms_m, _ = time_graph(torch, mats, steps, warm)
+    ms_p, _ = time_graph(torch, packs, steps, warm)
+    ms_m4 = time_graph_streams(torch, mats, 4, steps, warm)
+    ms_p4 = time_graph_streams(torch, packs, 4, steps, warm)
+    mat_avg = time_per_launch(torch, mats, 3)
     big = [c for c in mats if c.name.split(".")[-1] in ("gate", "up", "down")]
-    big_avg = time_per_launch(torch, big, 2)
+    big_avg = time_per_launch(torch, big, 3)
     big_bytes = big[0].nbytes
 
     def leg(ms, nb):
-        return {"ms": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
-                "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        return {"ms": _r(ms, 4), "GBps": _r(nb / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm_peak": _r(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return {"workload": "materialise + FP4 pack, 7 families x 26 layers (Gemma-3-1B shapes), 13 W0 bands, rank 64",
             "note": "serial: the 182 calls of each kind back to back in one graph; 4 streams: the same "
                     "independent calls round-robin on 4 streams inside one graph",
-            "materialize": dict(leg(ms_m, mbytes), bytes=mbytes, avg_launch_us=round(mat_avg * 1e3, 2),
+            "materialize": dict(leg(ms_m, mbytes), bytes=mbytes, avg_launch_us=_r(mat_avg * 1e3, 2),
                                 streams4=leg(ms_m4, mbytes),
-                                largest_projection={"bytes": big_bytes, "avg_launch_us": round(big_avg * 1e3, 2),
-                                                    "GBps": round(big_bytes / (big_avg * 1e-3) / 1e9, 1)}),
+                                largest_projection={"bytes": big_bytes, "avg_launch_us": _r(big_avg * 1e3, 2),
+                                                    "GBps": _r(big_bytes / (big_avg * 1e-3) / 1e9, 1)}),
             "fp4_pack": dict(leg(ms_p, pbytes), bytes=pbytes, streams4=leg(ms_p4, pbytes))}
 
 
-def run_fp4_decode(args, torch, B, I):
+def run_fp4_decode(args, torch, B, I, nested=False):
     """Gemma-3-1B-shaped decode layer on FP4-packed W_eff: the four dispatches
     (stacked QKV 1536 x 1152, o 1152 x 1024, stacked gate/up 13824 x 1152, down
     1152 x 6912) per layer, 26 layers, M in {1, 4, 16}; each layer's weights are
@@ -603,7 +800,7 @@ def run_fp4_decode(args, torch, B, I):
     lib = B.lib()
     stream = torch.cuda.current_stream().cuda_stream
     groups = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")), ("down", ("down",))]
-    packed = []                        # per layer: [(name, N, K, packed, scales, g)]
+    packed = []
     layer_dev = upload_layers(torch, I, layer_np)
     for l in range(L):
         row = []
@@ -640,21 +837,22 @@ def run_fp4_decode(args, torch, B, I):
     for M in Ms:
         ms, _ = time_graph(torch, per_m[M], args.steps, args.warmup)
         nb = sum(c.nbytes for c in per_m[M])
-        res[f"M{M}"] = {"us_per_layer": round(ms * 1e3 / L, 2), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
-                        "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    avg = time_per_launch(torch, gu, args.roofline_reps)
+        res[f"M{M}"] = {"us_per_layer": _r(ms * 1e3 / L, 2), "GBps": _r(nb / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm_peak": _r(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    avg = time_per_launch(torch, gu, max(10, args.roofline_reps))
     gb = gu[0].nbytes
     return {"workload": "gemma-3-1b-shaped decode on FP4-packed W_eff, 26 layers, M in {1, 4, 16}",
             "results": res,
             "dominant": {"kernel": "k_fp4_gemv (stacked gate/up, 13824 x 1152)", "bytes_per_launch_M1": gb,
-                         "avg_launch_us": round(avg * 1e3, 3),
-                         "GBps_M1_bytes": round(gb / (avg * 1e-3) / 1e9, 1),
-                         "frac_hbm_peak": round(gb / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "avg_launch_us": _r(avg * 1e3, 3),
+                         "GBps_M1_bytes": _r(gb / (avg * 1e-3) / 1e9, 1),
+                         "frac_hbm_peak": _r(gb / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": read_traffic("fp4_gemv_gateup"),
                          "note": "average over the M = 1, 4 and 16 launches; bytes are the M = 1 launch's "
                                  "(codes, scales, x, y)"}}
 
 
-def run_fold(args, torch, B, I):
+def run_fold(args, torch, B, I, nested=False):
     """The in-graph fold against the factored form, per call: W_eff
     materialised into scratch every call, then a plain GEMM on it through the
     same library (s = 1, r = 0), against one factored dispatch; Gemma-3-1B
@@ -683,7 +881,6 @@ def run_fold(args, torch, B, I):
                 fn = {1: lib.aq_recon_linear, 2: lib.aq_recon_gateup_fused, 3: lib.aq_recon_qkv_fused}[len(ps)]
                 fact.append(Call(fn, (B.AQ_BF16, M, K, x.data_ptr(), K, pa, y.data_ptr(), Nt, ws.data_ptr(),
                                       ws.numel(), stream), 0, 0, f"fact.{name}", name))
-                # fold: every block's W_eff into one stacked scratch weight, then s = 1, r = 0
                 weff = torch.empty((Nt, K), dtype=torch.bfloat16, device=dev)
                 ones = torch.ones(Nt, dtype=torch.bfloat16, device=dev)
                 r0 = 0
@@ -700,35 +897,41 @@ def run_fold(args, torch, B, I):
                 keep += [x, y, weff, ones, pa, dp]
         ms_f, _ = time_graph(torch, fact, args.steps, args.warmup)
         ms_d, _ = time_graph(torch, fold, args.steps, args.warmup)
-        res[f"M{M}"] = {"factored_us_per_layer": round(ms_f * 1e3 / L, 2), "fold_us_per_layer": round(ms_d * 1e3 / L, 2),
-                        "fold_over_factored": round(ms_d / ms_f, 3)}
+        res[f"M{M}"] = {"factored_us_per_layer": _r(ms_f * 1e3 / L, 2), "fold_us_per_layer": _r(ms_d * 1e3 / L, 2),
+                        "fold_over_factored": _r(ms_d / ms_f, 3)}
         keep = keep[-8:]
     cross = next((m for m in (16, 64, 128, 256, 512, 1024, 2048) if res[f"M{m}"]["fold_over_factored"] < 1.0), None)
-    return {"workload": "in-graph fold (materialise every call + GEMM) vs factored, Gemma-3-1B shapes, 26 layers, rank 64",
-            "results": res, "fold_wins_from_M": cross}
+    return {"workload": "in-graph fold (materialise every call + GEMM) vs factored, Gemma-3-1B shapes, 26 layers, "
+                        "rank 64", "results": res, "fold_wins_from_M": cross}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gemma_decode",
-                    choices=["gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4", "fp4_decode",
-                             "fold", "pmc_probe", "pmc_probe_fp4"])
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline", "gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4",
+                             "fp4_decode", "fold", "pmc_probe", "pmc_probe_fp4"])
+    ap.add_argument("--probe", default="decode_gateup",
+                    choices=["decode_gateup", "decode_gateup_large", "prefill_gateup_large"],
+                    help="with --workload pmc_probe: which dispatches the counter run covers")
     ap.add_argument("--summarize", action="store_true",
-                    help="summarise rocprofv3 CSVs (--trace, --fetch, --write) instead of running")
+                    help="summarise rocprofv3 CSVs (--trace, --fetch/--write, --pmc) instead of running")
     ap.add_argument("--trace")
+    ap.add_argument("--top", type=int, default=16)
     ap.add_argument("--calls", action="store_true",
                     help="with --trace: also group the library's prefill kernels into calls")
     ap.add_argument("--fetch")
-    ap.add_argument("--traffic-key", default="decode_gateup", choices=["decode_gateup", "fp4_gemv_gateup"],
-                    help="with --fetch/--write: which kernel's counters to summarise")
     ap.add_argument("--write")
+    ap.add_argument("--pmc", help="with --summarize: a counter CSV to average per counter")
+    ap.add_argument("--kernel-match", default="", help="with --summarize: '|'-separated substrings of the kernel name")
+    ap.add_argument("--traffic-key", default="decode_gateup", choices=sorted(PMC_KERNELS),
+                    help="with --fetch/--write: which kernel's counters to summarise")
     ap.add_argument("--layers", type=int, default=0)
-    ap.add_argument("--roofline-reps", type=int, default=3)
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--roofline-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="headline only (no Gemma-3-1B / materialise keys)")
     args = ap.parse_args()
     if args.summarize:
         summarize_profiles(args)
@@ -736,7 +939,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "this build has no multi-GPU path.", file=sys.stderr)
+              "the reconstructed linear here runs on a single GPU and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -745,11 +948,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.lib()
     torch.cuda.set_device(0)
-    fn = {"gemma_decode": run_gemma_decode, "gemma_prefill": run_gemma_prefill,
+    fn = {"headline": run_headline, "gemma_decode": run_gemma_decode, "gemma_prefill": run_gemma_prefill,
           "large_decoder": run_large_decoder, "materialize_fp4": run_materialize_fp4,
           "fp4_decode": run_fp4_decode, "fold": run_fold, "pmc_probe": run_pmc_probe,
           "pmc_probe_fp4": run_pmc_probe_fp4}[args.workload]
+    t0 = time.time()
     out = fn(args, torch, B, I)
+    out["bench_wall_s"] = _r(time.time() - t0, 1)
     print(json.dumps(out), flush=True)
 
 

@@ -81,24 +81,27 @@ def uniform(key, shape, lo, hi, dtype, seed=0):
 
 
 def bundle(workload, layer, family, in_dim, out_dim, r, dtype, band=None,
-           variant="normal", seed=0):
+           variant="normal", seed=0, draw_w0=True):
     """One projection's theta bundle: dict with W0 [N,K], s [N], U [N,r], Vt [r,K].
 
     ``band`` selects the shared W0 (default: one band per layer).  Variants:
     ``normal``; ``r0`` (rank 0, empty U/Vt); ``passthrough`` (s = 1, U = Vt = 0,
     W0 = the drawn weight, i.e. the layer's own weight); ``s0`` (s = 0, only the
-    low-rank term remains; a stress case for the U/V path).
+    low-rank term remains; a stress case for the U/V path).  ``draw_w0=False``
+    leaves W0 as None (a caller that already holds the band's identical draw).
     """
     wid, fid = WORKLOAD_ID[workload], FAMILY_ID.get(family, family)
     K, N = in_dim, out_dim
     b = layer if band is None else band
-    W0 = normal((wid, 1000 + b, fid, TENSOR_ID["W0"]), (N, K), 1.0 / np.sqrt(K), dtype, seed)
+    W0 = normal((wid, 1000 + b, fid, TENSOR_ID["W0"]), (N, K), 1.0 / np.sqrt(K), dtype, seed) if draw_w0 else None
     if variant == "r0":
         r = 0
     s = uniform((wid, layer, fid, TENSOR_ID["s"]), (N,), 0.9, 1.1, dtype, seed)
     U = normal((wid, layer, fid, TENSOR_ID["U"]), (N, r), 0.02, dtype, seed)
     Vt = normal((wid, layer, fid, TENSOR_ID["Vt"]), (r, K), 0.02, dtype, seed)
     if variant == "passthrough":
+        if W0 is None:
+            raise ValueError("passthrough needs the drawn W0")
         s = np.ones((N,), np.float32)
         U = np.zeros((N, r), np.float32)
         Vt = np.zeros((r, K), np.float32)
@@ -127,22 +130,22 @@ def layer_bundles(workload, shapes, layers, r, dtype, num_bands=None, seed=0,
     G = L if num_bands is None else num_bands
     band = [(l * G) // L for l in range(L)]
     threads = threads or min(16, os.cpu_count() or 1)
+    first = {}                             # the first layer of each band draws its W0
+    for l in range(L):
+        first.setdefault(band[l], l)
     jobs = [(l, f) for l in range(L) for f in families]
 
     def one(job):
         l, f = job
         K, N = shapes[f]
-        return job, bundle(workload, l, f, K, N, r, dtype, band=band[l], seed=seed)
+        return job, bundle(workload, l, f, K, N, r, dtype, band=band[l], seed=seed,
+                           draw_w0=first[band[l]] == l)
 
     with ThreadPoolExecutor(threads) as ex:
         done = dict(ex.map(one, jobs))
     out = {l: {} for l in range(L)}
-    shared = {}
     for (l, f), bd in done.items():
-        key = (band[l], f)
-        if key in shared:                  # identical draw; keep one copy per band
-            bd["W0"] = shared[key]
-        else:
-            shared[key] = bd["W0"]
+        if bd["W0"] is None:               # the same draw as the band's first layer: share it
+            bd["W0"] = done[(first[band[l]], f)]["W0"]
         out[l][f] = bd
     return out
