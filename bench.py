@@ -297,8 +297,10 @@ def gpu_clocks():
         gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_") and isinstance(v, dict)]
         out["gfx_mhz_min_max"] = [min(gfx), max(gfx)] if gfx else None
         for k in ("mem_0", "fclk_0", "socclk_0"):
-            if isinstance(clk.get(k), dict):
+            try:
                 out[k.replace("_0", "_mhz")] = clk[k]["clk"]["value"]
+            except (KeyError, TypeError):
+                pass
     except Exception as e:          # noqa: BLE001 -- informational only
         out["error"] = str(e)[:200]
     return out

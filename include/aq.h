@@ -132,9 +132,9 @@ aq_status aq_recon_gateup_fused(aq_dtype dt, int64_t M, int64_t K, const void *x
  * Every call on one GPU shares that GPU's array and overwrites what the
  * previous call left there; calls that overlap in time on one GPU (on
  * different streams, or from several threads) race and must not be issued.
- * Before a prefill launch that hands t between its workgroups, the hand-off
- * counters are zeroed by a small kernel (graph-capturable); a wait that gave
- * up is reported by aq_workspace_check(NULL, stream).  Limits and errors as
+ * Before a launch that hands t between its workgroups, the hand-off counters
+ * are zeroed by a small kernel (graph-capturable); a wait that gave up is
+ * reported by aq_workspace_check(NULL, stream).  Limits and errors as
  * aq_recon_linear; nproj outside 1..3 is AQ_ERR_INVALID_ARG. */
 aq_status aq_recon_linear_noalloc(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
                                   const aq_proj *p, int nproj, void *y, int64_t ldy, void *stream);

@@ -133,15 +133,16 @@ void make_plan(const aq::Recon &rq, Plan *pl) {
 }
 
 // Zeroes n words (the hand-off counters of the library's own scratch before a
-// prefill launch that uses them): a kernel rather than a memset, so that a
+// launch that uses them): a kernel rather than a memset, so that a
 // caller may capture it in a HIP graph.
-__global__ void k_clear_words(unsigned *p, int n) {
-  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+__global__ void k_clear_words(unsigned *p, int n, int keep) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x)
+    if (i != keep) p[i] = 0u;
 }
 
 // `clear_counters`: the workspace is the library's own scratch, whose counters
-// are zeroed before each prefill launch that waits on them (its flag word is
-// kept for aq_workspace_check).
+// are zeroed before each launch that waits on them (a prefill launch with the
+// rank-r tiles inside); its flag word is kept for aq_workspace_check.
 aq_status recon(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx, const aq_proj *p,
                 int nproj, void *y, int64_t ldy, void *ws, size_t ws_bytes, void *stream,
                 bool clear_counters = false) {
@@ -156,7 +157,8 @@ aq_status recon(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx, c
                 "(use aq_recon_* with a workspace)",
                 pl.ws, ws_bytes);
   if (clear_counters && pl.path == P_PREFILL && pl.pf.fuse) {
-    hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(64), 0, (hipStream_t)stream, (unsigned *)ws, 2);
+    hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(64), 0, (hipStream_t)stream, (unsigned *)ws, aq::kSyncWords,
+                       aq::kSyncFlag);
     const hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e0));
   }
@@ -371,22 +373,25 @@ aq_status aq_workspace_check(void *ws, void *stream) {
   }
   if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);
-  unsigned w[3] = {0, 0, 0};
+  unsigned w[aq::kSyncWords] = {};
   if (e == hipSuccess) e = hipMemcpy(w, ws, sizeof w, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(AQ_ERR_HIP, "reading the workspace failed: %s", hipGetErrorString(e));
-  if (w[aq::kSyncArrive] == 0 && w[aq::kSyncPassed] == 0 && w[aq::kSyncFlag] == 0) return AQ_OK;
+  unsigned passed = 0, any = 0;
+  for (int g = 0; g < aq::kHandoffGroups; ++g) passed += w[aq::kSyncGroup0 + aq::kSyncGroupStride * g];
+  for (unsigned v : w) any |= v;
+  if (!any) return AQ_OK;
   e = hipMemset(ws, 0, sizeof w);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return fail(AQ_ERR_HIP, "clearing the workspace failed: %s", hipGetErrorString(e));
   if (w[aq::kSyncFlag])
     return fail(AQ_ERR_HANDOFF,
-                "a prefill launch gave up waiting for its rank-r workgroups (counters %u, %u): the outputs of "
-                "the prefill calls since the last check are not valid; the workspace has been cleared",
-                w[aq::kSyncArrive], w[aq::kSyncPassed]);
+                "a launch gave up waiting for the workgroups that compute t (arrivals %u, waiters passed %u): "
+                "the outputs of the calls since the last check are not valid; the workspace has been cleared",
+                w[aq::kSyncArrive], passed);
   return fail(AQ_ERR_WORKSPACE,
-              "hand-off counters not zero (%u, %u): the workspace was not zero-filled or was used by "
-              "concurrent calls; it has been cleared",
-              w[aq::kSyncArrive], w[aq::kSyncPassed]);
+              "hand-off counters not zero (arrivals %u, groups %u, waiters passed %u): the workspace was not "
+              "zero-filled or was used by concurrent calls; it has been cleared",
+              w[aq::kSyncArrive], w[aq::kSyncGroups], passed);
 }
 
 aq_status aq_debug_force_plan(aq_debug_knob knob, int64_t value) {

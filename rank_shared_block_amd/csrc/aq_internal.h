@@ -28,10 +28,14 @@ constexpr int kMaxCounterTiles = (int)(kWsReserved / 4);
 // those calls a plan depends only on the call's arguments.
 int debug_knob(aq_debug_knob k, int dflt);
 
-// Prefill hand-off words in the reserved workspace region: [0] arrivals of
-// the rank-r workgroups, [1] main workgroups past their wait, [2] flag set
-// when a wait gave up (read and cleared by aq_workspace_check).
-constexpr int kSyncArrive = 0, kSyncPassed = 1, kSyncFlag = 2;
+// Hand-off words in the reserved workspace region (handoff.h): [0] arrivals of
+// the workgroups that compute t, [1] groups of waiters that have all passed,
+// [2] flag set when a wait gave up (read and cleared by aq_workspace_check),
+// [16 + 16 g] waiters of group g that have passed (g = 0..7, one 64-byte line
+// each).  All zero between calls.
+constexpr int kSyncArrive = 0, kSyncGroups = 1, kSyncFlag = 2;
+constexpr int kSyncGroup0 = 16, kSyncGroupStride = 16, kHandoffGroups = 8;
+constexpr int kSyncWords = kSyncGroup0 + kSyncGroupStride * kHandoffGroups;
 constexpr int kHandoffSpin = 1 << 22;   // polls before a wait gives up
 
 // One projection of a (possibly fused) dispatch, host view.

@@ -60,6 +60,7 @@
 
 #include "aq_internal.h"
 #include "device_common.h"
+#include "handoff.h"
 
 namespace aq {
 
@@ -84,11 +85,10 @@ struct PfArgs {
   int ldx, ldy, ldt, ldp, M, K, nblk, ntm, ntiles, S, kchunk, vec_store;
   // Rank-r pass run by the first tgrid workgroups of the main-pass launch
   // (0: none): they publish t with device-coherent stores (coherent = 1 in
-  // their arguments) and count themselves in sync[0] with a release; the
-  // nwait main units that need t wait (at most `spin` polls) until the count
-  // reaches `wait_for` (= tgrid), acquire, and the last of them zeroes
-  // sync[0..1].  A wait that gives up sets the flag word sync[2].
-  int tgrid, nwait, coherent, wait_for, spin;
+  // their arguments) and count themselves in the workspace; the main units
+  // that need t wait for them before they first read t (handoff.h).
+  int tgrid, coherent;
+  HandoffWait hw;
   // tsplit: t is kept per K range (t_p = x_p Vt_p^T, bf16, at t + p * tstride)
   // and every K-split unit p adds t_p U^T to its partial (the rank term is
   // linear in K, so the fold of the partials sums it); the rank-r tiles write
@@ -474,32 +474,12 @@ __device__ __attribute__((always_inline)) inline void gemm_tile(const PfArgs &a,
   // t is read from the last group on (rank chunks riding on the ring, then the
   // epilogue): with the rank-r pass in this launch, wait for its workgroups.
   if (MODE != MODE_RAW && addu && a.tgrid > 0) {
-    if (tid == 0) {
-      // Bounded: the rank-r workgroups were dispatched before every main one
-      // and need no other workgroup to finish, so the count arrives.  A wait
-      // that reaches the bound all the same goes on rather than hang, and
-      // records that in the flag word for aq_workspace_check to report.
-      bool seen = false;
-      for (int it = 0; it < a.spin; ++it) {
-        if (__hip_atomic_load(a.sync + kSyncArrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)a.wait_for) {
-          seen = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      if (!seen) __hip_atomic_fetch_or(a.sync + kSyncFlag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // Acquire at agent scope: the producers released their t stores with
-      // their arrival, and t is read below with plain loads, possibly on
-      // another XCD than the one that wrote it; this invalidates the lines
-      // those loads could otherwise find stale in this CU's caches.  The
-      // workgroup barrier after it orders every wave's reads behind it.
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      if (__hip_atomic_fetch_add(a.sync + kSyncPassed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
-          (unsigned)a.nwait) {
-        __hip_atomic_store(a.sync + kSyncArrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.sync + kSyncPassed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    // Bounded: the rank-r workgroups were dispatched before every main one and
+    // need no other workgroup to finish, so the count arrives (a wait that
+    // reaches the bound all the same goes on and sets the flag word that
+    // aq_workspace_check reports).  The workgroup barrier after it orders
+    // every wave's reads of t behind the acquire.
+    if (tid == 0) handoff_wait(a.sync, a.hw, (int)blockIdx.x & 7, handoff_poll(a.sync));
     ring_barrier();
   }
   // Every K range holds at least one slice (K >= 1), so nkp >= NST.  The last
@@ -766,7 +746,7 @@ __global__ __launch_bounds__(64 * NW, (gemm_occupancy<BM, BN, BK, NST, MODE == M
       // releases them at agent scope (the readers may sit on other XCDs)
       __builtin_amdgcn_s_waitcnt(0);
       ring_barrier();
-      if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync + kSyncArrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) handoff_arrive(a.sync);
       return;
     }
   }
@@ -1164,15 +1144,23 @@ hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipS
     a.tsplit = a.S > 1;
     a.tparts = a.S > 1 ? 1 : t.S;
     a.tstride = (long)rq.M * pl.ldt;
-    a.nwait = 0;
-    for (int b = 0; b < rq.nblk; ++b)
-      if (a.b[b].r > 0) a.nwait += a.b[b].ntn * a.ntm * (a.tsplit ? a.S : 1);
-    if (a.nwait == 0) a.tgrid = 0;
-    // the rank-r workgroups that arrive: those with a tile (the grid is
-    // rounded up to whole XCD rounds; the padding workgroups count too)
-    a.wait_for = a.tgrid + (debug_knob(AQ_DBG_HANDOFF_UNREACHABLE, 0) ? 1 : 0);
-    a.spin = debug_knob(AQ_DBG_HANDOFF_SPIN, kHandoffSpin);
-    if (a.spin < 1) a.spin = 1;
+    // The main units that wait: those of blocks with a rank-r term, every K
+    // range with one t per range, else the first (it adds the rank term).
+    // Every rank-r workgroup arrives (the grid is rounded up to whole XCD
+    // rounds; the padding workgroups count themselves too).
+    const int S = a.S;
+    const bool tsplit = a.tsplit;
+    auto waits = [&](int u) {
+      const int tile = u / S, p = u - tile * S;
+      int bi = 0;
+      if (a.nblk > 1 && tile >= a.b[1].tile0) bi = 1;
+      if (a.nblk > 2 && tile >= a.b[2].tile0) bi = 2;
+      return a.b[bi].r > 0 && (S == 1 || tsplit || p == 0);
+    };
+    int nwait = 0;
+    for (int u = 0; u < a.ntiles * S; ++u) nwait += waits(u) ? 1 : 0;
+    if (nwait == 0) a.tgrid = 0;
+    else handoff_counts(a.ntiles * S, a.tgrid, waits, &a.hw);
   }
   const int mode = pl.self ? MODE_SELF : (a.S > 1 ? MODE_PART : MODE_RECON);
   hipError_t e = run(a, t, pl.BM, pl.BN, pl.BK, pl.NST, pl.NW, mode, st);

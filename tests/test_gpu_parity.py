@@ -130,6 +130,7 @@ def test_decode_modes_qkv(M, split, ng, S, force_plan):
     force_plan("DECODE_SPLIT", int(split))
     if ng is not None:
         force_plan("DECODE_NG", ng)
+    if S is not None:
         force_plan("DECODE_S", S)
     K = 1048
     shapes = [(200, 8), (40, 16), (24, 0)]
@@ -246,7 +247,7 @@ def test_prefill_rank_pass_in_main_launch(M, K, S, tile, force_plan):
         y = B.recon_qkv(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
         assert_parity(down(y), ref, "bf16", f"M={M} K={K} tile={tile} rep={rep}")
         torch.cuda.synchronize()
-        counters = B.default_workspace()._buf[torch.device(dev()).index][:8].cpu()
+        counters = B.default_workspace()._buf[torch.device(dev()).index][:576].cpu()
         assert int(counters.sum()) == 0, counters
 
 
@@ -276,7 +277,7 @@ def test_prefill_rank_pass_in_parts(M, K, parts, force_plan):
         y = B.recon_qkv(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
         assert_parity(down(y), ref, "bf16", f"M={M} K={K} parts={parts} rep={rep}")
         torch.cuda.synchronize()
-        counters = B.default_workspace()._buf[torch.device(dev()).index][:8].cpu()
+        counters = B.default_workspace()._buf[torch.device(dev()).index][:576].cpu()
         assert int(counters.sum()) == 0, counters
 
 
@@ -300,7 +301,7 @@ def test_prefill_handoff_give_up_is_reported(force_plan):
     with pytest.raises(B.AQError) as e:
         ws.check()
     assert e.value.status == B.AQ_ERR_HANDOFF, e.value
-    assert int(ws._buf[torch.device(dev()).index][:12].cpu().sum()) == 0
+    assert int(ws._buf[torch.device(dev()).index][:576].cpu().sum()) == 0
     B.aq_debug_reset_plan()
     for k, v in zip(("BM", "BN", "BK", "NST", "W"), (128, 128, 64, 4, 4)):
         force_plan(f"PREFILL_{k}", v)
