@@ -907,6 +907,59 @@ def run_fold(args, torch, B, I, nested=False):
                         "rank 64", "results": res, "fold_wins_from_M": cross}
 
 
+def make_rebuild_calls(torch, B, I, workload, shapes, layer_dev, layer_np, M, x_tag):
+    """Per layer, the four dispatches through the per-element rebuild entry point."""
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream().cuda_stream
+    calls, keep = [], []
+    lib = B.lib()
+    for l, fam_dev in enumerate(layer_dev):
+        for name, fams in I.LAYER_DISPATCHES:
+            K = shapes[fams[0]][0]
+            x = torch.from_numpy(I.activations(workload, x_tag + len(name), M, K, "bf16")).to(dev).to(torch.bfloat16)
+            projs = [B.make_proj(*fam_dev[f]) for f in fams]
+            arr = (B.aq_proj * len(fams))(*projs)
+            ntot = sum(p.N for p in projs)
+            y = torch.empty((M, ntot), dtype=torch.bfloat16, device=dev)
+            need = lib.aq_workspace_bytes(B.AQ_OP_REBUILD, B.AQ_BF16, M, K, arr, len(fams))
+            ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+            args = (B.AQ_BF16, M, K, x.data_ptr(), K, arr, len(fams), y.data_ptr(), ntot, ws.data_ptr(), ws.numel(),
+                    stream)
+            nr = [(shapes[f][1], layer_np[l][f]["U"].shape[1]) for f in fams]
+            calls.append(Call(lib.aq_rebuild_linear, args, _dispatch_bytes(M, K, nr), _dispatch_flops(M, K, nr),
+                              f"rb.L{l}.{name}.M{M}", name))
+            keep += [x, y, ws, arr]
+    return calls, keep
+
+
+def run_rebuild(args, torch, B, I, nested=False):
+    """The per-element rebuild (every weight rebuilt inside the kernel, no t)
+    against the factored form, per rank and batch size: Gemma-3-1B-shaped
+    layers (26, ranks 4, 16, 64) and large-decoder-shaped layers (8 in 4 W0
+    bands, rank 32); us per layer, both as HIP graphs."""
+    res = {}
+    cases = [("gemma_decode", I.GEMMA_1B, 26, None, r, (1, 4, 16)) for r in (4, 16, 64)]
+    cases.append(("large_decoder", I.LARGE_DECODER, 8, 4, 32, (1, 16)))
+    for wl, shapes, L, G, r, Ms in cases:
+        layer_np = I.layer_bundles(wl, shapes, layers=L, r=r, dtype="bf16", num_bands=G)
+        layer_dev = upload_layers(torch, I, layer_np)
+        for M in Ms:
+            fc, k1 = make_recon_calls(torch, B, I, wl, shapes, layer_dev, layer_np, M, 11 * M)
+            rc, k2 = make_rebuild_calls(torch, B, I, wl, shapes, layer_dev, layer_np, M, 11 * M)
+            gf, gr = capture(torch, fc), capture(torch, rc)
+            sf, sr = replay_stats(torch, gf, 30), replay_stats(torch, gr, 30)
+            del gf, gr, k1, k2
+            nb = sum(c.nbytes for c in fc)
+            res[f"{wl}.r{r}.M{M}"] = {"factored_us_per_layer": _r(sf["median"] * 1e3 / L, 2),
+                                      "rebuild_us_per_layer": _r(sr["median"] * 1e3 / L, 2),
+                                      "rebuild_over_factored": _r(sr["median"] / sf["median"], 3),
+                                      "rebuild_GBps": _r(nb / (sr["median"] * 1e-3) / 1e9, 1)}
+            log(f"rebuild {wl} r={r} M={M}: {res[f'{wl}.r{r}.M{M}']}")
+        del layer_dev
+        torch.cuda.empty_cache()
+    return {"workload": "per-element rebuild vs factored form, decode batch sizes", "results": res}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -914,7 +967,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4",
-                             "fp4_decode", "fold", "pmc_probe", "pmc_probe_fp4"])
+                             "fp4_decode", "fold", "rebuild", "pmc_probe", "pmc_probe_fp4"])
     ap.add_argument("--probe", default="decode_gateup",
                     choices=["decode_gateup", "decode_gateup_large", "prefill_gateup_large"],
                     help="with --workload pmc_probe: which dispatches the counter run covers")
@@ -952,7 +1005,7 @@ def main():
     torch.cuda.set_device(0)
     fn = {"headline": run_headline, "gemma_decode": run_gemma_decode, "gemma_prefill": run_gemma_prefill,
           "large_decoder": run_large_decoder, "materialize_fp4": run_materialize_fp4,
-          "fp4_decode": run_fp4_decode, "fold": run_fold, "pmc_probe": run_pmc_probe,
+          "fp4_decode": run_fp4_decode, "fold": run_fold, "rebuild": run_rebuild, "pmc_probe": run_pmc_probe,
           "pmc_probe_fp4": run_pmc_probe_fp4}[args.workload]
     t0 = time.time()
     out = fn(args, torch, B, I)

@@ -54,7 +54,7 @@ typedef enum aq_status {
 
 typedef enum aq_dtype { AQ_F32 = 0, AQ_BF16 = 1 } aq_dtype;
 
-typedef enum aq_op { AQ_OP_RECON = 0, AQ_OP_FP4 = 1, AQ_OP_FP4_LINEAR = 2 } aq_op;
+typedef enum aq_op { AQ_OP_RECON = 0, AQ_OP_FP4 = 1, AQ_OP_FP4_LINEAR = 2, AQ_OP_REBUILD = 3 } aq_op;
 
 #define AQ_MAX_RANK 256
 
@@ -139,6 +139,25 @@ aq_status aq_recon_gateup_fused(aq_dtype dt, int64_t M, int64_t K, const void *x
 aq_status aq_recon_linear_noalloc(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
                                   const aq_proj *p, int nproj, void *y, int64_t ldy, void *stream);
 
+/* Per-element reconstruction: y = x W_eff^T with every weight of W_eff = diag(s)
+ * W0 + U Vt rebuilt inside the kernel, rounded once to bf16, and the dense
+ * [N, K] matrix never formed ("Execution paths", section "The custom op": the
+ * weight rebuilt per element, one dispatch per projection).  p[0..nproj-1]
+ * (nproj = 1, 2 or 3) read the same x; y = [y_0 | y_1 | ...] along N as for the
+ * fused recon calls.  Limits as that section states for its custom op: r <= 64
+ * per block (larger ranks are refused with AQ_ERR_UNSUPPORTED, a refusal rather
+ * than a silent fallback; use aq_recon_* there), and it is a decode kernel:
+ * M <= 16 tokens (else AQ_ERR_UNSUPPORTED; M == 0 is a no-op).  bf16 only
+ * (AQ_F32 is AQ_ERR_UNSUPPORTED).  Arguments otherwise as aq_recon_linear;
+ * ws: aq_workspace_bytes(AQ_OP_REBUILD, ...) bytes (0 unless long K is split
+ * over workgroups: then fp32 partials after the reserved region), 256-byte
+ * aligned.  Precision: the rank-r products and s W0 + U Vt in fp32, one bf16
+ * rounding per rebuilt weight (relative <= 2^-8), exact products with x, fp32
+ * sums, one rounding of y. */
+aq_status aq_rebuild_linear(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
+                            const aq_proj *p, int nproj, void *y, int64_t ldy, void *ws,
+                            size_t ws_bytes, void *stream);
+
 /* W_eff[N, ldw] (columns 0..K-1) = diag(s) W0 + U Vt, accumulated in fp32 and
  * rounded once to dt.  "Execution paths", section "Precompute-outside" (the weight
  * rebuilt once at load) and "How attnquant works", section "The reconstruction
@@ -198,6 +217,7 @@ aq_status aq_fp4_linear(int64_t M, int64_t N, int64_t K, const void *x, int64_t 
  *   AQ_OP_FP4  : M and dt ignored; p[0].N and K are the weight's shape.
  *   AQ_OP_FP4_LINEAR: dt ignored; M tokens, p[0].N and K the packed weight's
  *                shape (nproj = 1).
+ *   AQ_OP_REBUILD: (dt, M, K, p[0..nproj-1]) as passed to aq_rebuild_linear.
  * Returns 0 for invalid arguments (the call itself then reports why).
  * Host-only: touches no GPU state. */
 size_t aq_workspace_bytes(aq_op op, aq_dtype dt, int64_t M, int64_t K, const aq_proj *p,
@@ -240,6 +260,7 @@ typedef enum aq_debug_knob {
   AQ_DBG_PREFILL_BM, AQ_DBG_PREFILL_BN, AQ_DBG_PREFILL_BK, AQ_DBG_PREFILL_NST, AQ_DBG_PREFILL_W,
   AQ_DBG_PREFILL_S, AQ_DBG_PREFILL_SELF, AQ_DBG_PREFILL_FUSE, AQ_DBG_TPASS_S, AQ_DBG_TPASS_PARTS,
   AQ_DBG_FP4_NG, AQ_DBG_FP4_S, AQ_DBG_FP4_M4, AQ_DBG_HANDOFF_SPIN, AQ_DBG_HANDOFF_UNREACHABLE,
+  AQ_DBG_REBUILD_NG, AQ_DBG_REBUILD_ROWS, AQ_DBG_REBUILD_S,
   AQ_DBG_COUNT
 } aq_debug_knob;
 aq_status aq_debug_force_plan(aq_debug_knob knob, int64_t value);

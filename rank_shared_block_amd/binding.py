@@ -23,14 +23,15 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaq.so")
 AQ_OK, AQ_ERR_INVALID_ARG, AQ_ERR_SHAPE, AQ_ERR_ALIGNMENT = 0, 1, 2, 3
 AQ_ERR_UNSUPPORTED, AQ_ERR_WORKSPACE, AQ_ERR_HIP, AQ_ERR_HANDOFF = 4, 5, 6, 7
 AQ_F32, AQ_BF16 = 0, 1
-AQ_OP_RECON, AQ_OP_FP4, AQ_OP_FP4_LINEAR = 0, 1, 2
+AQ_OP_RECON, AQ_OP_FP4, AQ_OP_FP4_LINEAR, AQ_OP_REBUILD = 0, 1, 2, 3
 AQ_MAX_RANK = 256
 
 # Plan overrides (include/aq.h, aq_debug_knob): test-only.
 DEBUG_KNOBS = ("DECODE_SPLIT", "DECODE_NG", "DECODE_ROWS", "DECODE_S", "DECODE_WAVES",
                "PREFILL_BM", "PREFILL_BN", "PREFILL_BK", "PREFILL_NST", "PREFILL_W",
                "PREFILL_S", "PREFILL_SELF", "PREFILL_FUSE", "TPASS_S", "TPASS_PARTS",
-               "FP4_NG", "FP4_S", "FP4_M4", "HANDOFF_SPIN", "HANDOFF_UNREACHABLE")
+               "FP4_NG", "FP4_S", "FP4_M4", "HANDOFF_SPIN", "HANDOFF_UNREACHABLE", "REBUILD_NG",
+               "REBUILD_ROWS", "REBUILD_S")
 
 
 class aq_proj(ctypes.Structure):
@@ -76,6 +77,8 @@ def lib():
         L.aq_last_error.restype = ctypes.c_char_p
         L.aq_version.argtypes = []
         L.aq_version.restype = ctypes.c_int
+        L.aq_rebuild_linear.argtypes = [ctypes.c_int, i64, i64, vp, i64, P, ctypes.c_int, vp, i64, vp, sz, vp]
+        L.aq_rebuild_linear.restype = ctypes.c_int
         L.aq_recon_linear_noalloc.argtypes = [ctypes.c_int, i64, i64, vp, i64, P, ctypes.c_int, vp, i64, vp]
         L.aq_recon_linear_noalloc.restype = ctypes.c_int
         L.aq_workspace_check.argtypes = [vp, vp]
@@ -111,6 +114,10 @@ def aq_recon_qkv_fused(dt, M, K, x, ldx, p, y, ldy, ws, ws_bytes, stream):
 
 def aq_recon_gateup_fused(dt, M, K, x, ldx, p, y, ldy, ws, ws_bytes, stream):
     return lib().aq_recon_gateup_fused(dt, M, K, x, ldx, _projs(p, 2), y, ldy, ws, ws_bytes, stream)
+
+
+def aq_rebuild_linear(dt, M, K, x, ldx, p, nproj, y, ldy, ws, ws_bytes, stream):
+    return lib().aq_rebuild_linear(dt, M, K, x, ldx, _projs(p, nproj), nproj, y, ldy, ws, ws_bytes, stream)
 
 
 def aq_recon_linear_noalloc(dt, M, K, x, ldx, p, nproj, y, ldy, stream):
@@ -322,6 +329,34 @@ def recon_gateup(x, bundles, y=None, workspace=None):
     if len(bundles) != 2:
         raise ValueError("need two bundles (gate, up)")
     return _recon(lib().aq_recon_gateup_fused, 2, x, bundles, y, workspace)
+
+
+def rebuild_linear(x, bundles, y=None, workspace=None):
+    """Per-element rebuild: y = x W_eff^T, every weight rebuilt in the kernel;
+    bundles = one to three (W0, s, U, Vt) read by the same x, outputs
+    concatenated along N (x bf16 [M <= 16, K], r <= 64)."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if not 1 <= len(bundles) <= 3:
+        raise ValueError("need one to three bundles")
+    M, K = x.shape
+    bad = [] if x.device.type == "cuda" else [f"x must be on a GPU, got {x.device}"]
+    for i, b in enumerate(bundles):
+        for msg in _bundle_problems(*b, K=K, dtype=x.dtype, device=x.device):
+            bad.append(f"projection {i}: {msg}")
+    if bad:
+        raise ValueError("; ".join(bad))
+    projs = [make_proj(*b) for b in bundles]
+    ntot = sum(p.N for p in projs)
+    if y is None:
+        y = torch.empty((M, ntot), dtype=x.dtype, device=x.device)
+    _check_out(y, M, ntot, x)
+    arr = (aq_proj * len(projs))(*projs)
+    need = lib().aq_workspace_bytes(AQ_OP_REBUILD, _dt(x), M, K, arr, len(projs))
+    ws, ws_bytes = (workspace or _WS).get(need, x.device)
+    check(lib().aq_rebuild_linear(_dt(x), M, K, _ptr(x), x.stride(0), arr, len(projs), _ptr(y), y.stride(0),
+                                  ws, ws_bytes, _stream()))
+    return y
 
 
 def materialize(bundle, out=None):

@@ -230,6 +230,40 @@ aq_status aq_recon_gateup_fused(aq_dtype dt, int64_t M, int64_t K, const void *x
   return recon(dt, M, K, x, ldx, p, 2, y, ldy, ws, ws_bytes, stream);
 }
 
+// Checks shared by the per-element rebuild and its workspace query.
+aq_status check_rebuild(aq_dtype dt, int64_t M, const aq_proj *p, int nproj) {
+  if (dt != AQ_BF16) return fail(AQ_ERR_UNSUPPORTED, "the per-element rebuild takes bf16 only");
+  for (int b = 0; b < nproj; ++b)
+    if (p[b].r > aq::kRebuildMaxRank)
+      return fail(AQ_ERR_UNSUPPORTED, "projection %d: rank %lld exceeds the per-element rebuild's limit %d", b,
+                  (long long)p[b].r, aq::kRebuildMaxRank);
+  if (M > aq::kRebuildMaxM)
+    return fail(AQ_ERR_UNSUPPORTED, "M = %lld: the per-element rebuild takes at most %d tokens", (long long)M,
+                aq::kRebuildMaxM);
+  return AQ_OK;
+}
+
+aq_status aq_rebuild_linear(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx, const aq_proj *p,
+                            int nproj, void *y, int64_t ldy, void *ws, size_t ws_bytes, void *stream) {
+  if (nproj < 1 || nproj > aq::kMaxBlocks)
+    return fail(AQ_ERR_INVALID_ARG, "nproj = %d must be 1, 2 or 3", nproj);
+  aq::Recon rq;
+  aq_status s = build_recon(dt, M, K, x, ldx, p, nproj, y, ldy, true, &rq);
+  if (s != AQ_OK) return s;
+  s = check_rebuild(dt, M, p, nproj);
+  if (s != AQ_OK || M == 0) return s;
+  aq::RebuildPlan pl;
+  aq::plan_rebuild(rq, &pl);
+  if (pl.ws_bytes > 0) {
+    if (!ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", pl.ws_bytes);
+    if (ws_bytes < pl.ws_bytes) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", pl.ws_bytes, ws_bytes);
+    if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  }
+  const hipError_t e = aq::launch_rebuild(rq, pl, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return AQ_OK;
+}
+
 aq_status aq_recon_linear_noalloc(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
                                   const aq_proj *p, int nproj, void *y, int64_t ldy, void *stream) {
   if (nproj < 1 || nproj > aq::kMaxBlocks)
@@ -335,6 +369,17 @@ size_t aq_workspace_bytes(aq_op op, aq_dtype dt, int64_t M, int64_t K, const aq_
     if (!p || nproj != 1 || M == 0 || check_fp4_linear(M, p[0].N, K) != AQ_OK) return 0;
     aq::Fp4LinPlan pl;
     aq::plan_fp4_linear(M, p[0].N, K, &pl);
+    return pl.ws_bytes;
+  }
+  if (op == AQ_OP_REBUILD) {
+    if (!p || nproj < 1 || nproj > aq::kMaxBlocks || M == 0) return 0;
+    int64_t ntot = 0;
+    for (int b = 0; b < nproj; ++b) ntot += p[b].N > 0 ? p[b].N : 0;
+    aq::Recon rq;
+    if (build_recon(dt, M, K, nullptr, K, p, nproj, nullptr, ntot, false, &rq) != AQ_OK) return 0;
+    if (check_rebuild(dt, M, p, nproj) != AQ_OK) return 0;
+    aq::RebuildPlan pl;
+    aq::plan_rebuild(rq, &pl);
     return pl.ws_bytes;
   }
   if (op != AQ_OP_RECON || nproj < 1 || nproj > aq::kMaxBlocks || !p) return 0;

@@ -100,6 +100,20 @@ struct PrefillPlan {
 void plan_prefill(const Recon &rq, PrefillPlan *pl);
 hipError_t launch_prefill(const Recon &rq, const PrefillPlan &pl, void *ws, hipStream_t st);
 
+// ---- per-element rebuild (M <= 16, r <= 64, bf16) -----------------------------
+constexpr int kRebuildMaxM = 16, kRebuildMaxRank = 64;
+struct RebuildPlan {
+  int rows;                    // rows per tile (at most 16 NG)
+  int NG;                      // 16-row groups per tile
+  int RC;                      // 32-wide rank chunks (0 for rank 0)
+  int S, kchunk;               // K ranges and their length (multiple of 32)
+  int ntiles;
+  int tile0[kMaxBlocks];
+  size_t ws_bytes;             // 0 without a K split, else reserved region + fp32 partials
+};
+void plan_rebuild(const Recon &rq, RebuildPlan *pl);
+hipError_t launch_rebuild(const Recon &rq, const RebuildPlan &pl, void *ws, hipStream_t st);
+
 // ---- fp32 (any M) -------------------------------------------------------------
 hipError_t launch_recon_f32(const Recon &rq, hipStream_t st);
 

@@ -753,3 +753,109 @@ def test_fold_path_matches_factored(M):
     x = I.activations("test", 990 + M, M, K, "bf16")
     y = B.recon_linear(up(x, "bf16"), (weff, ones, None, None))
     assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in bds]), "bf16", f"fold M={M}")
+
+
+# ------------------------------------------------------------- per-element rebuild
+
+def _assert_rebuild_parity(got, x, bds, what):
+    """The spec bf16 tolerance against the oracle's factored form, and
+    elementwise the bound this arithmetic allows: each rebuilt weight
+    s W0 + U Vt formed in fp32 (r + 2 roundings of 2^-24 relative to
+    |s W0| + |U| |Vt|) and rounded once to bf16 (2^-8 relative), exact products
+    with x, fp32 sums of K terms, one bf16 rounding of y."""
+    nb = [bundle_np(b) for b in bds]
+    ref = oracle.recon_fused(x, nb)
+    assert rel_err(got, ref) <= 1e-2, what
+    x64 = np.abs(np.asarray(x, dtype=np.float64))
+    A = np.concatenate([np.abs(s)[:, None] * np.abs(W0) + np.abs(U) @ np.abs(Vt) for (W0, s, U, Vt) in nb], 0)
+    K = x.shape[1]
+    r = max(b[2].shape[1] for b in nb)
+    bound = 2.0 ** -8 * np.abs(ref) + (2.0 ** -8 + (r + 2 + K) * 2.0 ** -24) * (x64 @ A.T) * 1.01
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs beyond the derived bound"
+
+
+@pytest.mark.parametrize("M", [1, 3, 16])
+@pytest.mark.parametrize("r", [0, 4, 16, 36, 64])
+@pytest.mark.parametrize("variant", ["normal", "s0"])
+def test_rebuild_ranks(M, r, variant):
+    """Every rank chunk count (r = 0: s W0 only; 4, 16 in one chunk of 32; 36
+    and 64 in two, 36 with U rows that are not 16-byte aligned), a ragged N
+    (200) and a K that leaves a partial last 32-wide step (1048)."""
+    if r == 0 and variant == "s0":
+        pytest.skip("s = 0 with r = 0 is the zero map")
+    bd, x = _single(M, 1048, 200, r, "bf16", variant=variant, layer=30 + r, tag=3000 + M + r)
+    y = B.rebuild_linear(up(x, "bf16"), [bundle_up(bd, "bf16")])
+    _assert_rebuild_parity(down(y), x, [bd], f"r={r} M={M} {variant}")
+
+
+@pytest.mark.parametrize("M", [1, 7, 16])
+def test_rebuild_fused_blocks(M):
+    """Q/K/V in one dispatch with a rank per block (8, 64, 0): block-diagonal
+    U, outputs concatenated along N."""
+    K = 264
+    shapes = [(200, 8), (40, 64), (24, 0)]
+    bds = [I.bundle("test", 31, f, K, n, r, "bf16") for f, (n, r) in zip(("q", "k", "v"), shapes)]
+    x = I.activations("test", 3100 + M, M, K, "bf16")
+    y = B.rebuild_linear(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+    assert y.shape == (M, 264)
+    _assert_rebuild_parity(down(y), x, bds, f"qkv M={M}")
+
+
+@pytest.mark.parametrize("rows,S", [(5, 1), (16, 1), (27, 1), (33, 2), (48, 3), (64, 1), (64, 5), (16, 16)])
+def test_rebuild_tilings(rows, S, force_plan):
+    """Tiles of any height up to 64 rows (1 to 4 16-row groups, the last tile of
+    each block shorter still), with K whole or split over S ranges (fp32
+    partials, then the fold), on a ragged gate/up pair."""
+    force_plan("REBUILD_ROWS", rows)
+    force_plan("REBUILD_S", S)
+    K = 1048
+    bds = [I.bundle("test", 32, f, K, 333, 16, "bf16") for f in ("gate", "up")]
+    x = I.activations("test", 3200 + rows + S, 5, K, "bf16")
+    y = B.rebuild_linear(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+    _assert_rebuild_parity(down(y), x, bds, f"rows={rows} S={S}")
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_rebuild_gemma_layer_full(M):
+    """The Gemma-3-1B-shaped decode layer (rank 16), all four dispatches, every
+    output compared."""
+    lb = I.layer_bundles("gemma_decode", I.GEMMA_1B, layers=1, r=16, dtype="bf16")[0]
+    for name, fams, K, bds in _layer_dispatches(I.GEMMA_1B, lb):
+        x = I.activations("gemma_decode", 10 * M + len(name), M, K, "bf16")
+        y = B.rebuild_linear(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+        _assert_rebuild_parity(down(y), x, bds, f"gemma {name} M={M}")
+
+
+def test_rebuild_large_decoder_sampled():
+    """Large-decoder gate/up and down (rank 32) at M = 4: one output column in
+    every 64-column window of every block."""
+    lb = I.layer_bundles("large_decoder", I.LARGE_DECODER, layers=1, r=32, dtype="bf16",
+                         families=("gate", "up", "down"))[0]
+    rng = np.random.default_rng(3300)
+    M = 4
+    for name, fams in (("gateup", ("gate", "up")), ("down", ("down",))):
+        K = I.LARGE_DECODER[fams[0]][0]
+        bds = [lb[f] for f in fams]
+        x = I.activations("large_decoder", 3300 + len(name), M, K, "bf16")
+        y = down(B.rebuild_linear(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds]))
+        col0 = 0
+        for b in bds:
+            n = b["W0"].shape[0]
+            cols = _strided_sample(rng, n, 64)
+            sb = sub_bundle(b, cols)
+            sub = {"W0": sb[0], "s": sb[1], "U": sb[2], "Vt": sb[3]}
+            _assert_rebuild_parity(y[:, col0 + cols], x, [sub], f"large {name}")
+            col0 += n
+        torch.cuda.empty_cache()
+
+
+def test_rebuild_matches_factored_closely():
+    """The rebuild and the factored kernels differ by the one bf16 rounding of
+    each rebuilt weight: both within the bound of their own arithmetic, and
+    within 2^-7 of max|y| of each other."""
+    bd, x = _single(16, 1152, 1024, 16, "bf16", layer=34, tag=3400)
+    xd, bdd = up(x, "bf16"), bundle_up(bd, "bf16")
+    y_rb = down(B.rebuild_linear(xd, [bdd]))
+    y_f = down(B.recon_linear(xd, bdd))
+    assert rel_err(y_rb, y_f) <= 2.0 ** -7

@@ -184,3 +184,20 @@ def test_prefill_plans_for_the_gemma_shapes():
         assert ws(M, 1152, gateup) == 65536 + M * 128 * 2
     assert ws(512, 6912, down) == 65536 + 512 * 64 * 2 * 3 + 3 * 512 * 1152 * 4
     assert ws(2048, 6912, down) == 65536 + 2048 * 64 * 2 * 2
+
+
+def test_rebuild_refusals_before_any_launch():
+    def call(dt=B.AQ_BF16, M=4, K=128, ps=None, nproj=1):
+        ps = ps or [_proj(N=64, r=16)]
+        return B.aq_rebuild_linear(dt, M, K, FAKE, K, ps, nproj, FAKE, 64 * nproj, FAKE, 1 << 20, None)
+    assert call(ps=[_proj(r=65)]) == B.AQ_ERR_UNSUPPORTED and "limit 64" in B.last_error()
+    assert call(M=17) == B.AQ_ERR_UNSUPPORTED and "16 tokens" in B.last_error()
+    assert call(dt=B.AQ_F32) == B.AQ_ERR_UNSUPPORTED and "bf16" in B.last_error()
+    assert call(nproj=4, ps=[_proj()] * 4) == B.AQ_ERR_INVALID_ARG
+    assert call(K=100) == B.AQ_ERR_ALIGNMENT
+    assert call(M=0) == B.AQ_OK
+    ws = lambda M, K, N, r: B.aq_workspace_bytes(B.AQ_OP_REBUILD, B.AQ_BF16, M, K, [_proj(N=N, r=r)], 1)
+    assert ws(1, 1152, 13824, 16) == 0                       # many rows: whole K per tile
+    big = ws(16, 6912, 1152, 16)                             # few rows, long K: fp32 partials
+    assert big > 65536 and (big - 65536) % (16 * 1152 * 4) == 0
+    assert ws(4, 128, 64, 65) == 0 and ws(17, 128, 64, 4) == 0
