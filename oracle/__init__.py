@@ -22,7 +22,8 @@ passage it follows:
                    recipe's constants and tie rules: the pages give only the
                    container; the recipe is pinned by self-consistency, exact
                    brute force and the format tables.
-* ``decompose`` -- the analytic decomposition used only to build test fixtures
+* ``decompose`` -- the analytic decomposition: least-squares scale, full and
+                   randomized truncated SVD, band mean
                    ("How attnquant works" §How the decomposition produces s, U, and V,
                    §The passthrough operating point).
 """
@@ -31,12 +32,14 @@ from .recon import recon_linear, recon_fused, recon_blockdiag, materialize
 from .rounding import rne_bf16, rne_f32, rn_f32_exact
 from .fp4 import (E2M1_VALUES, e2m1_decode, e4m3fn_decode, e4m3fn_encode_rne_sat,
                   e2m1_rne_sat, fp4_pack, fp4_unpack, fp4_linear, global_scale, FP4_BLOCK)
-from .decompose import lsq_row_scale, decompose, band_of_layer, band_means
+from .decompose import (lsq_row_scale, decompose, band_of_layer, band_means, randomized_svd,
+                        decompose_randomized, FULL_SVD_MAX_MIN_DIM)
 
 __all__ = [
     "recon_linear", "recon_fused", "recon_blockdiag", "materialize",
     "rne_bf16", "rne_f32", "rn_f32_exact",
     "E2M1_VALUES", "e2m1_decode", "e4m3fn_decode", "e4m3fn_encode_rne_sat",
     "e2m1_rne_sat", "fp4_pack", "fp4_unpack", "fp4_linear", "global_scale", "FP4_BLOCK",
-    "lsq_row_scale", "decompose", "band_of_layer", "band_means",
+    "lsq_row_scale", "decompose", "band_of_layer", "band_means", "randomized_svd",
+    "decompose_randomized", "FULL_SVD_MAX_MIN_DIM",
 ]

@@ -30,7 +30,7 @@ import numpy as np
 
 FAMILIES = ("q", "k", "v", "o", "gate", "up", "down")
 FAMILY_ID = {f: i for i, f in enumerate(FAMILIES)}
-TENSOR_ID = {"W0": 0, "s": 1, "U": 2, "Vt": 3, "x": 4}
+TENSOR_ID = {"W0": 0, "s": 1, "U": 2, "Vt": 3, "x": 4, "omega": 5, "W": 6}
 
 # (in_dim, out_dim) per family
 GEMMA_1B = {"q": (1152, 1024), "k": (1152, 256), "v": (1152, 256), "o": (1024, 1152),
@@ -40,7 +40,7 @@ LARGE_DECODER = {"q": (5376, 4096), "k": (5376, 2048), "v": (5376, 2048), "o": (
 
 # Workload ids used in the seed path (stable; never renumber).
 WORKLOAD_ID = {"single_f32": 1, "gemma_decode": 2, "gemma_prefill": 3,
-               "large_decoder": 4, "materialize_fp4": 5, "test": 9}
+               "large_decoder": 4, "materialize_fp4": 5, "decompose": 6, "test": 9}
 
 # One decoder layer = four dispatches: fused QKV, o, fused gate/up, down.
 LAYER_DISPATCHES = (("qkv", ("q", "k", "v")), ("o", ("o",)),
@@ -149,3 +149,37 @@ def layer_bundles(workload, shapes, layers, r, dtype, num_bands=None, seed=0,
             bd["W0"] = done[(first[band[l]], f)]["W0"]
         out[l][f] = bd
     return out
+
+
+def gaussian_probe(workload, tag, l, K, seed=0):
+    """The randomized SVD's Gaussian test matrix, [l, K] float64 ~ N(0, 1):
+    each row one probe (drawn here so that both sides use the same one)."""
+    return _rng(seed, (WORKLOAD_ID[workload], 70000 + int(tag), 0, TENSOR_ID["omega"])).standard_normal((l, K))
+
+
+def trained_weight(workload, layer, family, in_dim, out_dim, dtype, band=None, waves=4, seed=0):
+    """A synthetic stand-in for a trained projection weight [out_dim, in_dim]
+    (no checkpoint is used): the band's shared draw W0 ~ N(0, 1/in_dim) with a
+    row scale a ~ U(0.8, 1.2) drawn per layer, plus a smooth perturbation of
+    low rank -- ``waves`` cosine waves over the (row, column) index grid, each
+    of rank 2, amplitudes 0.2/sqrt(in_dim) down to 0.05/sqrt(in_dim),
+    frequencies and phases drawn per layer -- plus noise ~ N(0, (0.01/sqrt(in_dim))^2).
+    Rounded once to ``dtype``.  Layers of one band share the W0 draw, so the
+    band mean of their weights is close to it."""
+    wid, fid = WORKLOAD_ID[workload], FAMILY_ID.get(family, family)
+    K, N = in_dim, out_dim
+    b = layer if band is None else band
+    base = _rng(seed, (wid, 1000 + b, fid, TENSOR_ID["W0"])).standard_normal((N, K), dtype=np.float32)
+    g = _rng(seed, (wid, layer, fid, TENSOR_ID["W"]))
+    a = g.uniform(0.8, 1.2, size=(N, 1))
+    sd = 1.0 / np.sqrt(K)
+    w = base.astype(np.float64) * (a * sd)
+    n = np.arange(N, dtype=np.float64)[:, None] / N
+    k = np.arange(K, dtype=np.float64)[None, :] / K
+    for i in range(waves):
+        amp = sd * (0.2 - 0.15 * i / max(1, waves - 1))
+        fn, fk = g.uniform(0.5, 6.0, size=2)
+        ph = g.uniform(0.0, 2.0 * np.pi)
+        w += amp * np.cos(2.0 * np.pi * (fn * n + fk * k) + ph)
+    w += g.standard_normal((N, K)) * (0.01 * sd)
+    return _finish(w.astype(np.float32), dtype)

@@ -49,3 +49,18 @@ def test_variants_and_bands():
     assert lb[0]["q"]["W0"] is lb[1]["q"]["W0"]
     assert not np.array_equal(lb[1]["q"]["W0"], lb[2]["q"]["W0"])
     assert not np.array_equal(lb[0]["q"]["U"], lb[1]["q"]["U"])
+
+
+def test_decomposition_inputs_are_seeded_and_banded():
+    from rank_shared_block_amd import inputs as I
+    a = I.trained_weight("decompose", 0, "q", 256, 96, "bf16", band=0)
+    b = I.trained_weight("decompose", 0, "q", 256, 96, "bf16", band=0)
+    c = I.trained_weight("decompose", 1, "q", 256, 96, "bf16", band=0)
+    assert a.shape == (96, 256) and np.array_equal(a, b) and not np.array_equal(a, c)
+    assert np.array_equal(a, I.round_to_bf16(a))
+    # layers of one band share the W0 draw: strongly correlated rows
+    cor = np.corrcoef(a.ravel(), c.ravel())[0, 1]
+    assert cor > 0.8
+    om = I.gaussian_probe("decompose", 3, 12, 256)
+    assert om.shape == (12, 256) and om.dtype == np.float64
+    assert np.array_equal(om, I.gaussian_probe("decompose", 3, 12, 256))

@@ -9,6 +9,7 @@ band map and band mean by direct enumeration.
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 import oracle
 
@@ -84,3 +85,139 @@ def test_band_mean_and_passthrough():
         assert np.array_equal(own[l], Ws[l])
         s, U, Vt, _ = oracle.decompose(Ws[l], own[l], r=3)
         assert np.array_equal(oracle.recon_linear(x, own[l], s, U, Vt), x @ Ws[l].T)
+
+
+# ------------------------------------------------------------- randomized SVD
+
+def _gapped(N, K, r, seed, tail=1e-6, top=2.0):
+    """A [N, K] with singular values top .. 1 (geometric) for the first r and
+    `tail` times smaller after, from random orthonormal factors (numpy's QR)."""
+    rng = np.random.default_rng(seed)
+    m = min(N, K)
+    P, _ = np.linalg.qr(rng.standard_normal((N, m)))
+    R, _ = np.linalg.qr(rng.standard_normal((K, m)))
+    sig = np.concatenate([np.geomspace(top, 1.0, r), tail * np.linspace(1.0, 0.5, m - r)])
+    return (P * sig) @ R.T, sig
+
+
+def test_randomized_svd_exact_rank_is_exact():
+    """A matrix of rank <= l is captured exactly: U Vt = A (any q), and equals
+    the full SVD's truncation."""
+    rng = np.random.default_rng(1)
+    N, K, k = 300, 280, 6
+    A = rng.standard_normal((N, k)) @ rng.standard_normal((k, K))
+    om = rng.standard_normal((16, K))
+    for q in (0, 2):
+        U, Vt, S = oracle.randomized_svd(A, 6, om, q)
+        assert np.max(np.abs(U @ Vt - A)) <= 1e-10 * np.max(np.abs(A))
+    Uf, Sf, Vf = np.linalg.svd(A)
+    assert np.allclose(S[:6], Sf[:6], rtol=1e-12)
+
+
+def test_randomized_svd_matches_truncation_on_gapped_spectrum():
+    """With a clear gap after r, the randomized truncation is the truncated SVD
+    to within the tail (Halko et al.'s bound: error of the order of
+    sigma_{r+1})."""
+    N, K, r = 400, 350, 8
+    A, sig = _gapped(N, K, r, 2)
+    om = np.random.default_rng(3).standard_normal((r + 10, K))
+    U, Vt, S = oracle.randomized_svd(A, r, om, 2)
+    Uf, Sf, Vhf = np.linalg.svd(A, full_matrices=False)
+    Ar = (Uf[:, :r] * Sf[:r]) @ Vhf[:r]
+    assert np.linalg.norm(U @ Vt - Ar, 2) <= 10 * sig[r]
+    assert np.allclose(S[:r], sig[:r], rtol=1e-10)
+
+
+def test_randomized_svd_factor_structure_and_eckart_young():
+    """U = U_svd S (orthogonal columns of norms S), Vt orthonormal rows, the
+    error never below the Eckart-Young optimum, and subspace iteration brings it
+    to the optimum on a slowly decaying spectrum (q = 6 beats q = 0)."""
+    rng = np.random.default_rng(4)
+    N, K, r = 260, 300, 10
+    A = rng.standard_normal((N, K)) * np.exp(-np.arange(K) / 40.0)[None, :]
+    sig = np.linalg.svd(A, compute_uv=False)
+    om = rng.standard_normal((r + 10, K))
+    errs = []
+    for q in (0, 6):
+        U, Vt, S = oracle.randomized_svd(A, r, om, q)
+        assert np.allclose(Vt @ Vt.T, np.eye(r), atol=1e-12)
+        G = U.T @ U
+        assert np.allclose(np.diag(G), S[:r] ** 2, rtol=1e-10)
+        assert np.max(np.abs(G - np.diag(np.diag(G)))) <= 1e-10 * S[0] ** 2
+        e = np.linalg.norm(A - U @ Vt) ** 2
+        assert e >= np.sum(sig[r:] ** 2) * (1 - 1e-12)
+        errs.append(e)
+    assert errs[1] < errs[0]
+    assert errs[1] <= np.sum(sig[r:] ** 2) * (1 + 1e-3)
+
+
+def test_decompose_randomized_size_rule():
+    """min(out, in) <= 256, or a probe as wide as the matrix: the full SVD
+    (identical to oracle.decompose); beyond, the randomized SVD."""
+    rng = np.random.default_rng(5)
+    W0 = rng.standard_normal((200, 300))
+    W = 1.1 * W0 + rng.standard_normal((200, 300)) * 0.1
+    om = rng.standard_normal((14, 300))
+    s, U, Vt, S = oracle.decompose_randomized(W, W0, 4, om, 2)
+    s2, U2, Vt2, S2 = oracle.decompose(W, W0, 4)
+    assert np.array_equal(s, s2) and np.allclose(U @ Vt, U2 @ Vt2, rtol=0, atol=1e-13)
+    W0b = rng.standard_normal((300, 320))
+    Wb = 0.9 * W0b + rng.standard_normal((300, 320)) * 0.1
+    om2 = rng.standard_normal((300, 320))                          # probe covers min(N, K)
+    sb, Ub, Vtb, _ = oracle.decompose_randomized(Wb, W0b, 5, om2, 1)
+    sf, Uf, Vtf, _ = oracle.decompose(Wb, W0b, 5)
+    assert np.allclose(Ub @ Vtb, Uf @ Vtf, atol=1e-12)
+    om3 = rng.standard_normal((15, 320))                           # randomized branch
+    sr, Ur, Vtr, _ = oracle.decompose_randomized(Wb, W0b, 5, om3, 2)
+    resid = Wb - sr[:, None] * W0b
+    U4, Vt4, _ = oracle.randomized_svd(resid, 5, om3, 2)
+    assert np.array_equal(Ur @ Vtr, U4 @ Vt4)
+
+
+def test_randomized_pins_catch_planted_mistakes():
+    """Copies of the randomized SVD with plausible mistakes each fail a pin:
+    S not absorbed into U, V's columns instead of rows, no re-orthonormalisation
+    in the subspace iteration (the basis collapses onto the top direction),
+    the probe applied to A^T."""
+    N, K, r = 320, 300, 6
+    # a wide spread of the leading singular values (1e4 .. 1): without
+    # re-orthonormalisation, q = 8 subspace steps raise it to the 17th power
+    # and the basis collapses onto the top directions in float64
+    A, sig = _gapped(N, K, r, 6, tail=1e-3, top=1e4)
+    om = np.random.default_rng(8).standard_normal((r + 10, K))
+
+    def no_absorb(A, r, om, q):
+        U, Vt, S = oracle.randomized_svd(A, r, om, q)
+        return U / S[:r], Vt, S
+
+    def vh_columns(A, r, om, q):
+        U, Vt, S = oracle.randomized_svd(A, r, om, q)
+        Q, _ = np.linalg.qr(A @ om.T)
+        _, _, Vh = np.linalg.svd(Q.T @ A, full_matrices=False)
+        return U, Vh[:, :r].T if Vh.shape[1] >= r else Vt, S
+
+    def no_reorth(A, r, om, q):
+        Y = A @ om.T
+        for _ in range(q):
+            Y = A @ (A.T @ Y)
+        Q, _ = np.linalg.qr(Y)
+        Ub, S, Vh = np.linalg.svd(Q.T @ A, full_matrices=False)
+        return (Q @ Ub)[:, :r] * S[:r], Vh[:r], S
+
+    def pins_pass(fn):
+        try:
+            U, Vt, S = fn(A, r, om, 8)
+            Uf, Sf, Vhf = np.linalg.svd(A, full_matrices=False)
+            ok = np.linalg.norm(U @ Vt - (Uf[:, :r] * Sf[:r]) @ Vhf[:r], 2) <= 10 * Sf[r]
+            ok &= np.allclose(np.linalg.norm(U, axis=0), S[:r], rtol=1e-8)
+            ok &= np.allclose(Vt @ Vt.T, np.eye(r), atol=1e-10)
+            return bool(ok)
+        except (ValueError, np.linalg.LinAlgError):
+            return False
+
+    assert pins_pass(oracle.randomized_svd)
+    for bad in (no_absorb, vh_columns, no_reorth):
+        assert not pins_pass(bad), bad.__name__
+    # the probe on the wrong side of a non-square matrix breaks the shapes
+    with pytest.raises(ValueError):
+        oracle.randomized_svd(A, r, np.zeros((r + 10, N)), 1)
