@@ -960,6 +960,54 @@ def run_rebuild(args, torch, B, I, nested=False):
     return {"workload": "per-element rebuild vs factored form, decode batch sizes", "results": res}
 
 
+def run_decompose(args, torch, B, I, nested=False):
+    """The decomposition on the GPU (least-squares scale, randomized SVD of the
+    residual at rank 64 with 10 probes of oversampling and 2 subspace steps,
+    float64) for the seven Gemma-3-1B-shaped projections of one layer, against
+    the oracle's on this host's cores (one projection, q)."""
+    dev = torch.device("cuda", 0)
+    r, q = 64, 2
+    res, keep = {}, []
+    total_ms = 0.0
+    for fam in I.FAMILIES:
+        K, N = I.GEMMA_1B[fam]
+        W = torch.from_numpy(I.trained_weight("decompose", 0, fam, K, N, "bf16", waves=32)).to(dev).to(torch.bfloat16)
+        W0 = torch.from_numpy(I.bundle("decompose", 0, fam, K, N, 0, "bf16")["W0"]).to(dev).to(torch.bfloat16)
+        l = B.probe_width(N, K, r)
+        om = torch.from_numpy(I.gaussian_probe("decompose", 7, l, K)).to(dev)
+        ws = B.Workspace()
+        for _ in range(2):
+            B.decompose(W, W0, r, om, q=q, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            B.decompose(W, W0, r, om, q=q, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        total_ms += ms
+        passes = 1 + (2 * q + 2)                       # scale, then R-sized contractions
+        res[fam] = {"N": N, "K": K, "l": l, "ms": _r(ms, 3),
+                    "fp64_GFLOP": _r(passes * 2.0 * N * K * l / 1e9 if fam else 0, 2),
+                    "fp64_TFLOPs": _r(passes * 2.0 * N * K * l / (ms * 1e-3) / 1e12, 2)}
+        keep += [W, W0, om]
+    out = {"workload": "decomposition of the 7 Gemma-3-1B-shaped projections of one layer (rank 64, p = 10, "
+                       "q = 2, fp64)", "per_projection": res, "ms_per_layer": _r(total_ms, 3)}
+    if not args.no_cpu_baseline:
+        import oracle
+        K, N = I.GEMMA_1B["q"]
+        Wn = I.trained_weight("decompose", 0, "q", K, N, "bf16", waves=32).astype(np.float64)
+        W0n = I.bundle("decompose", 0, "q", K, N, 0, "bf16")["W0"].astype(np.float64)
+        omn = I.gaussian_probe("decompose", 7, B.probe_width(N, K, r), K)
+        t0 = time.perf_counter()
+        oracle.decompose_randomized(Wn, W0n, r, omn, q)
+        out["cpu_baseline_q_proj_ms"] = _r((time.perf_counter() - t0) * 1e3, 1)
+        out["cpu_baseline_blas"] = blas_info()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -967,7 +1015,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4",
-                             "fp4_decode", "fold", "rebuild", "pmc_probe", "pmc_probe_fp4"])
+                             "fp4_decode", "fold", "rebuild", "decompose", "pmc_probe", "pmc_probe_fp4"])
     ap.add_argument("--probe", default="decode_gateup",
                     choices=["decode_gateup", "decode_gateup_large", "prefill_gateup_large"],
                     help="with --workload pmc_probe: which dispatches the counter run covers")
@@ -1005,7 +1053,8 @@ def main():
     torch.cuda.set_device(0)
     fn = {"headline": run_headline, "gemma_decode": run_gemma_decode, "gemma_prefill": run_gemma_prefill,
           "large_decoder": run_large_decoder, "materialize_fp4": run_materialize_fp4,
-          "fp4_decode": run_fp4_decode, "fold": run_fold, "rebuild": run_rebuild, "pmc_probe": run_pmc_probe,
+          "fp4_decode": run_fp4_decode, "fold": run_fold, "rebuild": run_rebuild, "decompose": run_decompose,
+          "pmc_probe": run_pmc_probe,
           "pmc_probe_fp4": run_pmc_probe_fp4}[args.workload]
     t0 = time.time()
     out = fn(args, torch, B, I)

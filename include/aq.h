@@ -211,6 +211,43 @@ aq_status aq_fp4_linear(int64_t M, int64_t N, int64_t K, const void *x, int64_t 
                         const uint8_t *packed, const uint8_t *scales, const float *global_scale,
                         void *y, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 
+/* The decomposition that produces a bundle from trained weights, on the GPU
+ * ("How attnquant works", section "How the decomposition produces s, U, and V",
+ * and the band-mean sentence after it).  All results are float64.
+ *
+ * aq_band_mean: W0[N, K] = the mean of the L layer weights W[0..L-1] that share
+ * it, summed in float64 (exact for bf16 and fp32 inputs), divided by L and
+ * rounded once to dt; bit-exact against the exact mean rounded once.  W is a
+ * HOST array of L device pointers (1 <= L <= 64), every weight [N, K]
+ * row-major with unit stride, dt storage, naturally aligned.
+ *
+ * aq_decompose: for one weight W [N, K] and its shared block W0 [N, K] (dt
+ * storage, row-major, unit stride):
+ *   s[o]  = (W[o] . W0[o]) / (W0[o] . W0[o])   (1 where W0[o] is zero),
+ *   R     = W - diag(s) W0,
+ *   U, Vt = the rank-r truncated SVD of R with U absorbing the singular values,
+ * the SVD by the randomized method (Halko, Martinsson and Tropp, 2009) with
+ * the caller's Gaussian test matrix omega [l, K] (row j = probe j, l = r +
+ * oversampling) and q steps of re-orthonormalised subspace iteration:
+ * Y = R omega^T, Q = orth(Y); q times Q~ = orth(R^T Q), Q = orth(R Q~);
+ * B = Q^T R = U_b S V^T; U = Q U_b[:, :r] S[:r]; Vt = V^T[:r].  The pages take
+ * a full SVD when min(N, K) <= 256 or when the oversampled probe would cover
+ * the matrix: pass l = min(N, K) there, and the same steps give the exact
+ * truncated SVD.  Outputs: s [N], U [N, r] (row stride r), Vt [r, K] (row
+ * stride K), float64, 8-byte aligned; r == 0 computes s only (omega, U, Vt may
+ * be NULL).  Limits: r <= l <= min(N, K), l <= 256, q <= 64, N * K < 2^31.
+ * ws: aq_decompose_workspace_bytes(N, K, r, l) bytes, 256-byte aligned (the
+ * basis, the co-range, partial sums; no zero-fill needed).  Asynchronous on
+ * stream; many launches, all on that stream.  Singular vectors are unique only
+ * up to sign (and within repeated singular values): U Vt is the result. */
+aq_status aq_band_mean(aq_dtype dt, int L, const void *const *W, int64_t N, int64_t K, void *W0,
+                       void *stream);
+aq_status aq_decompose(aq_dtype dt, int64_t N, int64_t K, int64_t r, int64_t l, int q, const void *W,
+                       const void *W0, const double *omega, double *s, double *U, double *Vt, void *ws,
+                       size_t ws_bytes, void *stream);
+/* 0 for r == 0 or invalid arguments (the call itself then reports why). */
+size_t aq_decompose_workspace_bytes(int64_t N, int64_t K, int64_t r, int64_t l);
+
 /* Workspace size in bytes for one call.
  *   AQ_OP_RECON: (dt, M, K, p[0..nproj-1]) exactly as passed to the recon call
  *                (nproj = 1, 3 or 2).

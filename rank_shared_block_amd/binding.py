@@ -81,6 +81,12 @@ def lib():
         L.aq_rebuild_linear.restype = ctypes.c_int
         L.aq_recon_linear_noalloc.argtypes = [ctypes.c_int, i64, i64, vp, i64, P, ctypes.c_int, vp, i64, vp]
         L.aq_recon_linear_noalloc.restype = ctypes.c_int
+        L.aq_band_mean.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), i64, i64, vp, vp]
+        L.aq_band_mean.restype = ctypes.c_int
+        L.aq_decompose.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.aq_decompose.restype = ctypes.c_int
+        L.aq_decompose_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        L.aq_decompose_workspace_bytes.restype = sz
         L.aq_workspace_check.argtypes = [vp, vp]
         L.aq_workspace_check.restype = ctypes.c_int
         L.aq_debug_force_plan.argtypes = [ctypes.c_int, i64]
@@ -134,6 +140,19 @@ def aq_quant_fp4_block16(N, K, w, ldw, packed, scales, global_scale, ws, ws_byte
 
 def aq_workspace_bytes(op, dt, M, K, p, nproj):
     return lib().aq_workspace_bytes(op, dt, M, K, _projs(p, nproj), nproj)
+
+
+def aq_band_mean(dt, L, W_ptrs, N, K, W0, stream):
+    arr = (ctypes.c_void_p * max(L, 1))(*W_ptrs)
+    return lib().aq_band_mean(dt, L, arr, N, K, W0, stream)
+
+
+def aq_decompose(dt, N, K, r, l, q, W, W0, omega, s, U, Vt, ws, ws_bytes, stream):
+    return lib().aq_decompose(dt, N, K, r, l, q, W, W0, omega, s, U, Vt, ws, ws_bytes, stream)
+
+
+def aq_decompose_workspace_bytes(N, K, r, l):
+    return lib().aq_decompose_workspace_bytes(N, K, r, l)
 
 
 def aq_workspace_check(ws, stream):
@@ -434,6 +453,65 @@ def fp4_linear(x, packed, scales, global_scale, y=None, workspace=None):
     check(lib().aq_fp4_linear(M, N, K, _ptr(x), x.stride(0), _ptr(packed), _ptr(scales), _ptr(global_scale),
                               _ptr(y), y.stride(0), ws, ws_bytes, _stream()))
     return y
+
+
+# ----------------------------------------------------------- decomposition
+
+FULL_SVD_MAX_MIN_DIM = 256      # the pages take a full SVD at or below this min(out, in)
+
+
+def probe_width(N, K, r, oversample=10):
+    """Width l of the randomized SVD's probe for a rank-r truncation of an
+    [N, K] residual: r + oversample, or min(N, K) -- the whole matrix, which
+    makes the same steps an exact SVD -- where the pages take a full SVD
+    (min(N, K) <= 256, or r + oversample >= min(N, K))."""
+    m = min(N, K)
+    return m if (m <= FULL_SVD_MAX_MIN_DIM or r + oversample >= m) else r + oversample
+
+
+def band_mean(weights, out=None):
+    """W0 = the mean of a band's layer weights (same shape, bf16 or fp32, one
+    device), rounded once."""
+    W = list(weights)
+    if not W:
+        raise ValueError("need at least one layer weight")
+    w0 = W[0]
+    bad = [i for i, w in enumerate(W) if w.shape != w0.shape or w.dtype != w0.dtype or w.device != w0.device
+           or w.dim() != 2 or not w.is_contiguous()]
+    if bad:
+        raise ValueError(f"layer weights {bad} differ from layer 0 in shape, dtype, device or layout")
+    if w0.device.type != "cuda":
+        raise ValueError(f"weights must be on a GPU, got {w0.device}")
+    N, K = w0.shape
+    if out is None:
+        out = torch.empty_like(w0)
+    check(aq_band_mean(_dt(w0), len(W), [w.data_ptr() for w in W], N, K, out.data_ptr(), _stream()))
+    return out
+
+
+def decompose(W, W0, r, omega, q=2, workspace=None):
+    """(s, U, Vt) float64 for one weight and its shared block: least-squares
+    row scale, then the rank-r truncated SVD of the residual by the randomized
+    method with the Gaussian probe `omega` [l, K] (float64, on the GPU) and q
+    subspace steps; l = probe_width(...) reproduces the pages' size rule."""
+    if W.shape != W0.shape or W.dtype != W0.dtype or W.device != W0.device or W.dim() != 2:
+        raise ValueError("W and W0 must be 2-D tensors of one shape, dtype and device")
+    if not (W.is_contiguous() and W0.is_contiguous()) or W.device.type != "cuda":
+        raise ValueError("W and W0 must be contiguous GPU tensors")
+    N, K = W.shape
+    dev = W.device
+    l = 0 if r == 0 else omega.shape[0]
+    if r > 0 and (omega.dtype != torch.float64 or omega.dim() != 2 or omega.shape[1] != K
+                  or omega.device != dev or not omega.is_contiguous()):
+        raise ValueError(f"omega must be a contiguous float64 [l, {K}] tensor on {dev}")
+    s = torch.empty(N, dtype=torch.float64, device=dev)
+    U = torch.empty((N, r), dtype=torch.float64, device=dev)
+    Vt = torch.empty((r, K), dtype=torch.float64, device=dev)
+    need = aq_decompose_workspace_bytes(N, K, r, l) if r > 0 else 0
+    ws, ws_bytes = (workspace or _WS).get(need, dev) if need else (None, 0)
+    check(aq_decompose(_dt(W), N, K, r, l, q, W.data_ptr(), W0.data_ptr(), _ptr(omega) if r else None,
+                       s.data_ptr(), _ptr(U), _ptr(Vt), ws, ws_bytes, _stream()))
+    return s, U, Vt
 
 
 # ----------------------------------------------------------- load-time path

@@ -264,6 +264,69 @@ aq_status aq_rebuild_linear(aq_dtype dt, int64_t M, int64_t K, const void *x, in
   return AQ_OK;
 }
 
+aq_status aq_band_mean(aq_dtype dt, int L, const void *const *W, int64_t N, int64_t K, void *W0, void *stream) {
+  if (dt != AQ_F32 && dt != AQ_BF16) return fail(AQ_ERR_INVALID_ARG, "dtype %d is not AQ_F32 or AQ_BF16", (int)dt);
+  if (L < 1 || L > aq::kMaxBandLayers) return fail(AQ_ERR_UNSUPPORTED, "L = %d layers: 1 to %d per band", L, aq::kMaxBandLayers);
+  if (!W || !W0) return fail(AQ_ERR_INVALID_ARG, "W or W0 is NULL");
+  if (N < 1 || K < 1) return fail(AQ_ERR_SHAPE, "N = %lld and K = %lld must be >= 1", (long long)N, (long long)K);
+  if (N > kMaxDim || K > kMaxDim || N * K > kMaxElems) return fail(AQ_ERR_UNSUPPORTED, "weight exceeds 2^31-1 elements");
+  for (int l = 0; l < L; ++l) {
+    if (!W[l]) return fail(AQ_ERR_INVALID_ARG, "layer %d: W is NULL", l);
+    if (!aligned(W[l], esize(dt))) return fail(AQ_ERR_ALIGNMENT, "layer %d: W is not naturally aligned", l);
+  }
+  if (!aligned(W0, esize(dt))) return fail(AQ_ERR_ALIGNMENT, "W0 is not naturally aligned");
+  const hipError_t e = aq::launch_band_mean(dt, L, W, N * K, W0, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return AQ_OK;
+}
+
+// Shape checks shared by aq_decompose and its workspace query.
+static aq_status check_decompose(int64_t N, int64_t K, int64_t r, int64_t l, int q) {
+  if (N < 1 || K < 1) return fail(AQ_ERR_SHAPE, "N = %lld and K = %lld must be >= 1", (long long)N, (long long)K);
+  if (N > kMaxDim || K > kMaxDim || N * K > kMaxElems) return fail(AQ_ERR_UNSUPPORTED, "weight exceeds 2^31-1 elements");
+  if (r < 0 || q < 0) return fail(AQ_ERR_INVALID_ARG, "rank %lld and subspace steps %d must be >= 0", (long long)r, q);
+  if (r > AQ_MAX_RANK) return fail(AQ_ERR_UNSUPPORTED, "rank %lld exceeds the supported maximum %d", (long long)r, AQ_MAX_RANK);
+  if (r > 0 && (l < r || l > (N < K ? N : K)))
+    return fail(AQ_ERR_SHAPE, "probe width l = %lld must be in [r, min(N, K)] = [%lld, %lld]", (long long)l,
+                (long long)r, (long long)(N < K ? N : K));
+  if (l > aq::kDecompMaxL) return fail(AQ_ERR_UNSUPPORTED, "probe width l = %lld exceeds %d", (long long)l, aq::kDecompMaxL);
+  if (q > 64) return fail(AQ_ERR_UNSUPPORTED, "q = %d subspace steps: at most 64", q);
+  return AQ_OK;
+}
+
+aq_status aq_decompose(aq_dtype dt, int64_t N, int64_t K, int64_t r, int64_t l, int q, const void *W,
+                       const void *W0, const double *omega, double *s, double *U, double *Vt, void *ws,
+                       size_t ws_bytes, void *stream) {
+  if (dt != AQ_F32 && dt != AQ_BF16) return fail(AQ_ERR_INVALID_ARG, "dtype %d is not AQ_F32 or AQ_BF16", (int)dt);
+  aq_status st = check_decompose(N, K, r, l, q);
+  if (st != AQ_OK) return st;
+  if (!W || !W0 || !s) return fail(AQ_ERR_INVALID_ARG, "W, W0 or s is NULL");
+  if (r > 0 && (!omega || !U || !Vt)) return fail(AQ_ERR_INVALID_ARG, "rank %lld but omega, U or Vt is NULL", (long long)r);
+  if (!aligned(W, esize(dt)) || !aligned(W0, esize(dt))) return fail(AQ_ERR_ALIGNMENT, "W or W0 is not naturally aligned");
+  if (!aligned(s, 8) || (r > 0 && (!aligned(omega, 8) || !aligned(U, 8) || !aligned(Vt, 8))))
+    return fail(AQ_ERR_ALIGNMENT, "s, omega, U and Vt must be 8-byte aligned");
+  aq::DecompPlan pl;
+  const size_t need = r > 0 ? aq::decompose_ws_bytes(N, K, r, l, &pl) : 0;
+  if (need > 0) {
+    if (!ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+    if (ws_bytes < need) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
+    if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  } else {
+    pl = aq::DecompPlan{};
+    pl.lj = 32;
+  }
+  aq::DecompArgs d{dt, N, K, r, l, q, W, W0, omega, s, U, Vt};
+  const hipError_t e = aq::launch_decompose(d, pl, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return AQ_OK;
+}
+
+size_t aq_decompose_workspace_bytes(int64_t N, int64_t K, int64_t r, int64_t l) {
+  if (r == 0 || check_decompose(N, K, r, l, 0) != AQ_OK) return 0;
+  aq::DecompPlan pl;
+  return aq::decompose_ws_bytes(N, K, r, l, &pl);
+}
+
 aq_status aq_recon_linear_noalloc(aq_dtype dt, int64_t M, int64_t K, const void *x, int64_t ldx,
                                   const aq_proj *p, int nproj, void *y, int64_t ldy, void *stream) {
   if (nproj < 1 || nproj > aq::kMaxBlocks)

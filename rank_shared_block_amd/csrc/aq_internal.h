@@ -114,6 +114,27 @@ struct RebuildPlan {
 void plan_rebuild(const Recon &rq, RebuildPlan *pl);
 hipError_t launch_rebuild(const Recon &rq, const RebuildPlan &pl, void *ws, hipStream_t st);
 
+// ---- decomposition (band mean, least squares, randomized SVD; fp64) ----------
+constexpr int kMaxBandLayers = 64;
+constexpr int kDecompMaxL = 256;
+struct DecompArgs {
+  aq_dtype dt;
+  int64_t N, K, r, l;
+  int q;
+  const void *W, *W0;
+  const double *omega;
+  double *s, *U, *Vt;
+};
+struct DecompPlan {
+  int lj;                      // compiled width of the l side (32, 64, 128, 256)
+  int srt, sgram;              // N ranges of R^T Q; ranges of the Gram sums
+  long nchunk;                 // rows per N range
+  size_t o_y1, o_y2, o_z1, o_z2, o_zp, o_gp, o_g, o_rinv, o_scr, o_v, o_lam, o_wu, o_wv;   // byte offsets
+};
+size_t decompose_ws_bytes(int64_t N, int64_t K, int64_t r, int64_t l, DecompPlan *pl);
+hipError_t launch_decompose(const DecompArgs &d, const DecompPlan &pl, void *ws, hipStream_t st);
+hipError_t launch_band_mean(aq_dtype dt, int L, const void *const *W, int64_t n, void *out, hipStream_t st);
+
 // ---- fp32 (any M) -------------------------------------------------------------
 hipError_t launch_recon_f32(const Recon &rq, hipStream_t st);
 

@@ -1,0 +1,166 @@
+"""GPU parity of the decomposition (aq_band_mean, aq_decompose) against the
+oracle's: the band mean bit for bit, the least-squares scale and the rank-r
+product U Vt of the truncated SVD of the residual (the singular vectors
+themselves are unique only up to sign), with the same Gaussian probe on both
+sides.
+
+Tolerances: both sides compute in float64; they differ in the order of their
+sums and in the factorisations they use for the same mathematical steps (the
+GPU: Cholesky QR twice and a Jacobi eigendecomposition of B B^T; the oracle:
+Householder QR and LAPACK's SVD).  Rounding of ~1e-16, amplified by at most
+sigma_1^2 / (sigma_r^2 - sigma_{r+1}^2) in the truncated subspace (the fixtures
+have a clear gap after r), stays far below the 1e-9 (of max |U Vt|) checked
+here; the scale is a quotient of two K-term dot products, 1e-12 relative."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rank_shared_block_amd import binding as B
+from rank_shared_block_amd import inputs as I
+from helpers import dev, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL_UV = 1e-9
+TOL_S = 1e-12
+
+
+def _dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev()).to(dtype)
+
+
+def _weights(N, K, r, layer, dtype="bf16", band=0, family="q"):
+    """A trained-like weight with a low-rank perturbation of rank r (r / 2
+    cosine waves) and its band's shared block."""
+    W = I.trained_weight("decompose", layer, family, K, N, dtype, band=band, waves=max(1, r // 2))
+    W0 = I.bundle("decompose", layer, family, K, N, 0, dtype, band=band)["W0"]
+    return W, W0
+
+
+def _check(N, K, r, q, W, W0, dtype, what, oversample=10):
+    l = B.probe_width(N, K, r, oversample)
+    om = I.gaussian_probe("decompose", N + K + r, l, K) if r > 0 else np.zeros((0, K))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    s, U, Vt = B.decompose(_dev(W, tdt), _dev(W0, tdt), r, torch.from_numpy(om).to(dev()), q=q)
+    s, U, Vt = s.cpu().numpy(), U.cpu().numpy(), Vt.cpu().numpy()
+    so, Uo, Vto, So = oracle.decompose_randomized(W, W0, r, om, q)
+    assert np.max(np.abs(s - so)) <= TOL_S * np.max(np.abs(so)), f"{what}: s"
+    if r == 0:
+        return
+    P, Po = U @ Vt, Uo @ Vto
+    scale = np.max(np.abs(Po))
+    err = np.max(np.abs(P - Po)) / (scale if scale > 0 else 1.0)
+    assert err <= TOL_UV or (scale == 0 and np.max(np.abs(P)) == 0), f"{what}: U Vt rel err {err:.3e}"
+    # validity of the factors: U's columns orthogonal with the singular values
+    # as norms, Vt's rows orthonormal (rows of zero singular value are zero)
+    nz = So[:r] > 1e-12 * So[0] if So[0] > 0 else np.zeros(r, bool)
+    assert np.allclose(np.linalg.norm(U, axis=0)[nz], So[:r][nz], rtol=1e-9), what
+    G = Vt[nz] @ Vt[nz].T
+    assert np.allclose(G, np.eye(int(nz.sum())), atol=1e-9), what
+    return err
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("L", [1, 2, 3, 7])
+def test_band_mean_bit_exact(L, dtype):
+    """W0 = the mean of the band's layer weights, rounded once: the same bits
+    as the oracle's float64 mean rounded to the storage type."""
+    N, K = 130, 264
+    Ws = [I.trained_weight("decompose", l, "k", K, N, dtype, band=0) for l in range(L)]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    got = B.band_mean([_dev(w, tdt) for w in Ws]).float().cpu().numpy().astype(np.float64)
+    ref = oracle.band_means(Ws, 1)[0]
+    ref = oracle.rne_bf16(ref) if dtype == "bf16" else oracle.rne_f32(ref)
+    assert np.array_equal(got, ref)
+    if L == 1:
+        assert np.array_equal(got, Ws[0].astype(np.float64))      # one layer per band: its own weight
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_lsq_scale_and_zero_rows(dtype):
+    """r = 0: the scale only; rows of W0 that are zero get s = 1."""
+    N, K = 77, 200
+    W, W0 = _weights(N, K, 4, 1, dtype)
+    W0 = W0.copy()
+    W0[[3, 40]] = 0.0
+    _check(N, K, 0, 0, W, W0, dtype, "r=0")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    s, _, _ = B.decompose(_dev(W, tdt), _dev(W0, tdt), 0, None)
+    assert float(s[3]) == 1.0 and float(s[40]) == 1.0
+
+
+@pytest.mark.parametrize("N,K,r,q", [(300, 520, 8, 2), (520, 300, 8, 0), (600, 700, 16, 3), (333, 1048, 4, 1)])
+def test_decompose_randomized(N, K, r, q):
+    """min(N, K) > 256: the randomized branch, with and without subspace steps,
+    tall and wide."""
+    W, W0 = _weights(N, K, r, 2)
+    _check(N, K, r, q, W, W0, "bf16", f"{N}x{K} r={r} q={q}")
+
+
+@pytest.mark.parametrize("N,K,r", [(256, 256, 4), (200, 264, 6), (96, 1152, 8), (1024, 100, 10)])
+def test_decompose_full_svd_rule(N, K, r):
+    """min(N, K) <= 256: the pages' full SVD, here the same steps with a probe
+    covering the matrix (l = min(N, K); 256 takes the kernels' paths with the
+    l x l matrices in global memory)."""
+    W, W0 = _weights(N, K, r, 3, "f32")
+    _check(N, K, r, 1, W, W0, "f32", f"{N}x{K} r={r}")
+
+
+def test_decompose_passthrough_and_rank_deficient():
+    """W0 = W: s = 1 and a zero residual, so U Vt = 0; a residual of rank 3
+    below r = 8: the probe's basis loses the missing directions (dropped
+    columns) and U Vt is the residual itself."""
+    N, K = 300, 400
+    W, W0 = _weights(N, K, 4, 4, "f32")
+    _check(N, K, 6, 2, W, W, "f32", "passthrough")
+    rng = np.random.default_rng(5)
+    R3 = (rng.standard_normal((N, 3)) @ rng.standard_normal((3, K)) * 1e-3).astype(np.float32)
+    Wd = (W0.astype(np.float64) * 1.05 + R3).astype(np.float32)
+    _check(N, K, 8, 1, Wd, W0, "f32", "rank 3")
+
+
+@pytest.mark.parametrize("fam,r", [("q", 16), ("gate", 64), ("down", 64)])
+def test_decompose_gemma_shapes(fam, r):
+    """Gemma-3-1B-shaped projections (bf16): q 1152 -> 1024 at rank 16, gate
+    1152 -> 6912 and down 6912 -> 1152 at rank 64."""
+    K, N = I.GEMMA_1B[fam]
+    W, W0 = _weights(N, K, r, 5, "bf16", family=fam)
+    _check(N, K, r, 2, W, W0, "bf16", f"{fam} r={r}")
+
+
+def test_decompose_band_end_to_end():
+    """Two layers of one band: W0 = their band mean, then each layer's bundle;
+    GPU (band mean, decompose) against the oracle (band mean, decomposition) on
+    the scale and on the size of what the rank-r term leaves, which the
+    randomized SVD brings within 1e-6 of the Eckart-Young optimum here."""
+    N, K, r = 640, 576, 12
+    Ws = [I.trained_weight("decompose", l, "o", K, N, "bf16", band=1, waves=6) for l in (0, 1)]
+    W0d = B.band_mean([_dev(w, torch.bfloat16) for w in Ws])
+    W0o = oracle.rne_bf16(oracle.band_means(Ws, 1)[0])
+    l = B.probe_width(N, K, r)
+    om = I.gaussian_probe("decompose", 77, l, K)
+    for Wl in Ws:
+        s, U, Vt = B.decompose(_dev(Wl, torch.bfloat16), W0d, r, torch.from_numpy(om).to(dev()), q=3)
+        so, Uo, Vto, So = oracle.decompose_randomized(Wl, W0o, r, om, 3)
+        s, U, Vt = s.cpu().numpy(), U.cpu().numpy(), Vt.cpu().numpy()
+        assert rel_err(s, so) <= TOL_S
+        R = Wl.astype(np.float64) - so[:, None] * W0o
+        e_gpu = np.linalg.norm(R - U @ Vt)
+        e_ora = np.linalg.norm(R - Uo @ Vto)
+        opt = np.sqrt(np.sum(np.linalg.svd(R, compute_uv=False)[r:] ** 2))
+        assert abs(e_gpu - e_ora) <= 1e-6 * e_ora
+        assert e_gpu <= opt * (1 + 1e-6)
+
+
+def test_decompose_refusals():
+    d = dev()
+    W = torch.zeros((64, 128), dtype=torch.bfloat16, device=d)
+    om = torch.zeros((300, 128), dtype=torch.float64, device=d)
+    with pytest.raises(B.AQError) as e:                # l > min(N, K)
+        B.decompose(W, W, 4, om[:100])
+    assert e.value.status == B.AQ_ERR_SHAPE
+    with pytest.raises(B.AQError) as e:                # l < r
+        B.decompose(W, W, 8, om[:4])
+    assert e.value.status == B.AQ_ERR_SHAPE
