@@ -988,10 +988,11 @@ def run_decompose(args, torch, B, I, nested=False):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         total_ms += ms
-        passes = 1 + (2 * q + 2)                       # scale, then R-sized contractions
-        res[fam] = {"N": N, "K": K, "l": l, "ms": _r(ms, 3),
-                    "fp64_GFLOP": _r(passes * 2.0 * N * K * l / 1e9 if fam else 0, 2),
-                    "fp64_TFLOPs": _r(passes * 2.0 * N * K * l / (ms * 1e-3) / 1e12, 2)}
+        # contractions with R: R Omega^T, then per subspace step R^T Q and R Q',
+        # then B = Q^T R; each 2 N K l flops (the l x l work is second order)
+        flop = (2 * q + 2) * 2.0 * N * K * l
+        res[fam] = {"N": N, "K": K, "l": l, "ms": _r(ms, 3), "fp64_GFLOP": _r(flop / 1e9, 2),
+                    "fp64_TFLOPs": _r(flop / (ms * 1e-3) / 1e12, 2)}
         keep += [W, W0, om]
     out = {"workload": "decomposition of the 7 Gemma-3-1B-shaped projections of one layer (rank 64, p = 10, "
                        "q = 2, fp64)", "per_projection": res, "ms_per_layer": _r(total_ms, 3)}

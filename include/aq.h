@@ -237,7 +237,9 @@ aq_status aq_fp4_linear(int64_t M, int64_t N, int64_t K, const void *x, int64_t 
  * stride K), float64, 8-byte aligned; r == 0 computes s only (omega, U, Vt may
  * be NULL).  Limits: r <= l <= min(N, K), l <= 256, q <= 64, N * K < 2^31.
  * ws: aq_decompose_workspace_bytes(N, K, r, l) bytes, 256-byte aligned (the
- * basis, the co-range, partial sums; no zero-fill needed).  Asynchronous on
+ * basis, the co-range, partial sums; no zero-fill needed); its first 64 KiB
+ * (the recon calls' counter words) are not touched, so the same workspace
+ * serves both kinds of call.  Asynchronous on
  * stream; many launches, all on that stream.  Singular vectors are unique only
  * up to sign (and within repeated singular values): U Vt is the result. */
 aq_status aq_band_mean(aq_dtype dt, int L, const void *const *W, int64_t N, int64_t K, void *W0,

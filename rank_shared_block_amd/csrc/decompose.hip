@@ -471,7 +471,9 @@ size_t decompose_ws_bytes(int64_t N, int64_t K, int64_t r, int64_t l, DecompPlan
   long sg = (len + 511) / 512;
   sg = sg < 128 ? sg : 128;
   pl->sgram = (int)(sg > 1 ? sg : 1);
-  size_t off = 0;
+  // after the reserved region: its counter words belong to the recon calls
+  // that share the workspace and must stay zero
+  size_t off = kWsReserved;
   auto take = [&](size_t nd) {
     const size_t o = off;
     off += (nd * 8 + 255) / 256 * 256;

@@ -19,7 +19,7 @@ import torch
 import oracle
 from rank_shared_block_amd import binding as B
 from rank_shared_block_amd import inputs as I
-from helpers import dev, rel_err
+from helpers import bundle_np, bundle_up, dev, down, rel_err, up
 
 pytestmark = pytest.mark.gpu
 
@@ -152,6 +152,25 @@ def test_decompose_band_end_to_end():
         opt = np.sqrt(np.sum(np.linalg.svd(R, compute_uv=False)[r:] ** 2))
         assert abs(e_gpu - e_ora) <= 1e-6 * e_ora
         assert e_gpu <= opt * (1 + 1e-6)
+
+
+def test_decompose_leaves_recon_counters_zero():
+    """The decomposition shares the default workspace with the recon calls:
+    its scratch must not touch the reserved counter words that the prefill
+    hand-off depends on (a dirty word would let waiters read t before it is
+    written).  Decompose, then check the words and run a prefill with a
+    rank-r hand-off on the same workspace."""
+    N, K, r = 600, 700, 16
+    W, W0 = _weights(N, K, r, 6)
+    _check(N, K, r, 1, W, W0, "bf16", "before the recon call")
+    ws = B.default_workspace()
+    ws.check()
+    M, Kr, Nr, rr = 200, 512, 160, 100
+    bd = I.bundle("test", rr, "q", Kr, Nr, rr, "bf16", variant="s0")
+    x = I.activations("test", rr, M, Kr, "bf16")
+    y = B.recon_linear(up(x, "bf16"), bundle_up(bd, "bf16"))
+    ws.check()
+    assert rel_err(down(y), oracle.recon_linear(x, *bundle_np(bd))) <= 1e-2
 
 
 def test_decompose_refusals():
