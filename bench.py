@@ -342,18 +342,28 @@ def cpu_baseline_layers(I, workload, shapes, layer_np, Ms, x_tag, layers, reps, 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 SOURCES = {"decode_gateup": "rank_shared_block_amd/csrc/recon_decode.hip",
            "decode_gateup_large": "rank_shared_block_amd/csrc/recon_decode.hip",
-           "prefill_gateup_large": "rank_shared_block_amd/csrc/recon_prefill.hip",
-           "fp4_gemv_gateup": "rank_shared_block_amd/csrc/fp4_gemv.hip"}
+           "prefill_gateup_large": ("rank_shared_block_amd/csrc/recon_prefill.hip",
+                                    "rank_shared_block_amd/csrc/handoff.h"),
+           "fp4_gemv_gateup": "rank_shared_block_amd/csrc/fp4_gemv.hip",
+           "materialize_batch": "rank_shared_block_amd/csrc/materialize.hip",
+           "fp4_pack_batch": "rank_shared_block_amd/csrc/fp4_pack.hip"}
 PMC_KERNELS = {"decode_gateup": (("k_decode_bf16",), "k_decode_bf16 (fused gate/up, Gemma-3-1B-shaped)"),
                "decode_gateup_large": (("k_decode_bf16",), "k_decode_bf16 (gate/up, large-decoder-shaped, M = 1)"),
                "prefill_gateup_large": (("k_gemm_bf16",), "k_gemm_bf16 (gate/up, large-decoder-shaped, M = 512)"),
-               "fp4_gemv_gateup": (("k_fp4_gemv", "<2, false>"), "k_fp4_gemv / k_fp4_gemv_m4 (FP4 stacked gate/up)")}
+               "fp4_gemv_gateup": (("k_fp4_gemv", "<2, false>"), "k_fp4_gemv / k_fp4_gemv_m4 (FP4 stacked gate/up)"),
+               "materialize_batch": (("k_materialize_batch",), "k_materialize_batch (182 Gemma-3-1B-shaped W_eff, "
+                                                               "13 bands)"),
+               "fp4_pack_batch": (("k_fp4_pack_batch",), "k_fp4_pack_batch (the same 182 W_eff)")}
 
 
 def source_digest(rel):
+    """Digest of a kernel's source file (or files, in order)."""
     import hashlib
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for r in ((rel,) if isinstance(rel, str) else rel):
+        with open(os.path.join(ROOT, r), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(key):
@@ -389,6 +399,19 @@ def run_pmc_probe(args, torch, B, I):
     prefill_gateup_large (large-decoder gate/up at M = 512, 8 layers)."""
     _calibration_copy(torch)
     probe = args.probe
+    if probe == "load_batch":
+        # one aq_materialize_batch call over the 182 Gemma-3-1B-shaped
+        # projections (13 bands of 2 layers, rank 64), then one
+        # aq_quant_fp4_batch call with its maxima
+        L = 26
+        layer_np = I.layer_bundles("materialize_fp4", I.GEMMA_1B, layers=L, r=64, dtype="bf16", num_bands=13)
+        layer_dev = upload_layers(torch, I, layer_np)
+        bundles = [layer_dev[l][f] for f in I.FAMILIES for l in range(L)]
+        ws, amax = B.materialize_batch(bundles, want_amax=True)
+        B.quant_fp4_batch(ws, amax)
+        torch.cuda.synchronize()
+        return {"probe": f"copy of {CALIB_BYTES} bytes, then one batched materialisation and one batched pack "
+                         f"of {len(bundles)} projections"}
     if probe == "decode_gateup":
         wl, shapes, L, G, r, Ms = "gemma_decode", I.GEMMA_1B, 26, None, 16, (1, 4, 16)
     else:
@@ -491,7 +514,8 @@ def summarize_profiles(args):
             val = lambda r: float(r.get("Counter_Value", r.get("value", 0)))
             copy = [val(r) for r in rs if "copyBuffer" in r["Kernel_Name"]]
             dec = [val(r) for r in rs if all(k in r["Kernel_Name"] for k in match)]
-            res[key] = (max(copy) if copy else None, float(np.mean(dec)) if dec else None, len(dec))
+            res[key] = (max(copy) if copy else None, float(np.mean(dec)) if dec else None, len(dec),
+                        float(np.sum(dec)) if dec else None)
         # scale: a copy of CALIB_BYTES reads and writes CALIB_BYTES each
         fscale = CALIB_BYTES / (res["FETCH_SIZE"][0] * 1024)
         wscale = CALIB_BYTES / (res["WRITE_SIZE"][0] * 1024)
@@ -503,7 +527,9 @@ def summarize_profiles(args):
                    f"(scale {wscale:.4f}).")
         out.append(f"{PMC_KERNELS[args.traffic_key][1]} (kernel name containing {list(match)}), mean over "
                    f"{res['FETCH_SIZE'][2]} launches: fetch {fetch_b/1e6:.3f} MB, write {write_b/1e6:.3f} MB per "
-                   f"launch (scaled), total {(fetch_b + write_b)/1e6:.3f} MB.")
+                   f"launch (scaled), total {(fetch_b + write_b)/1e6:.3f} MB; summed over those launches: fetch "
+                   f"{res['FETCH_SIZE'][3] * 1024 * fscale / 1e6:.3f} MB, write "
+                   f"{res['WRITE_SIZE'][3] * 1024 * wscale / 1e6:.3f} MB.")
         t = {}
         try:
             with open(TRAFFIC_FILE) as f:
@@ -531,6 +557,11 @@ def summarize_profiles(args):
         out.append("|---|---|---|")
         for name, v in sorted(agg.items()):
             out.append(f"| {name} | {len(v)} | {np.mean(v):.1f} |")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in agg:
+            # one MOPS unit is 512 flops (the derived MfmaFlopsBF16 counter)
+            out.append("")
+            out.append(f"bf16 MFMA flops per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512): "
+                       f"{np.mean(agg['SQ_INSTS_VALU_MFMA_MOPS_BF16']) * 512 / 1e9:.2f} GFLOP")
     print("\n".join(out))
 
 
@@ -780,9 +811,65 @@ def run_materialize_fp4(args, torch, B, I, nested=False):
     def leg(ms, nb):
         return {"ms": _r(ms, 4), "GBps": _r(nb / (ms * 1e-3) / 1e9, 1),
                 "frac_hbm_peak": _r(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    # The batched load-time calls: the whole model in one aq_materialize_batch
+    # call (family by family, the two layers of each band next to each other,
+    # so each W0 tile is read once per band) that also reports each W_eff's
+    # largest magnitude, then one aq_quant_fp4_batch call that takes them and
+    # reads each W_eff once.
+    order = [(f, l) for f in I.FAMILIES for l in range(L)]
+    n = len(order)
+    mitems, fitems = (B.aq_mat_item * n)(), (B.aq_fp4_item * n)()
+    amax = torch.zeros(n, dtype=torch.int32, device=dev)
+    bmat = bpack = 0
+    seen = set()
+    for i, (f, l) in enumerate(order):
+        K, N = I.GEMMA_1B[f]
+        bd = layer_dev[l][f]
+        w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+        gs = torch.empty((1,), dtype=torch.float32, device=dev)
+        mitems[i] = B.aq_mat_item(K, B.make_proj(*bd), w.data_ptr(), K)
+        fitems[i] = B.aq_fp4_item(N, K, K, w.data_ptr(), packed.data_ptr(), sc.data_ptr(), gs.data_ptr())
+        keep += [w, packed, sc, gs]
+        if bd[0].data_ptr() not in seen:              # W0 read once per band
+            seen.add(bd[0].data_ptr())
+            bmat += N * K * 2
+        bmat += (N * K + N + N * 64 + 64 * K) * 2     # W_eff written; s, U, Vt read
+        bpack += N * K * 2 + N * K // 2 + N * K // 16
+    keep += [mitems, fitems]
+    matb = Call(lib.aq_materialize_batch, (B.AQ_BF16, n, mitems, amax.data_ptr(), stream), bmat,
+                2 * sum(I.GEMMA_1B[f][0] * I.GEMMA_1B[f][1] for f, _ in order) * 64, "mat.batch", "matb")
+    packb = Call(lib.aq_quant_fp4_batch, (n, fitems, amax.data_ptr(), None, 0, stream), bpack, 0, "fp4.batch",
+                 "fp4b")
+    ms_mb, _ = time_graph(torch, [matb], steps, warm)
+    ms_pb, _ = time_graph(torch, [packb], steps, warm)
+    ms_both, _ = time_graph(torch, [matb, packb], steps, warm)
+    # Ceilings for this traffic mix, in the same graph setting: a device copy
+    # (read + write) and a fill (write only) of 1 GiB.
+    class _Op:
+        def __init__(self, fn):
+            self.fn = fn
+
+        def __call__(self, stream=None):
+            self.fn()
+    big_a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
+    big_b = torch.empty_like(big_a)
+    ms_copy, _ = time_graph(torch, [_Op(lambda: big_b.copy_(big_a))], steps, warm)
+    ms_fill, _ = time_graph(torch, [_Op(lambda: big_b.fill_(1.0))], steps, warm)
+    calib = {"copy_1GiB": leg(ms_copy, 2 << 30), "fill_1GiB": leg(ms_fill, 1 << 30)}
+    del big_a, big_b
+    batched = {"materialize": dict(leg(ms_mb, bmat), bytes=bmat,
+                                   bytes_note="W0 once per band (13 x 7), W_eff written, s, U, V read"),
+               "fp4_pack": dict(leg(ms_pb, bpack), bytes=bpack, bytes_note="W_eff read once, codes and scales written"),
+               "both": dict(leg(ms_both, bmat + bpack), bytes=bmat + bpack)}
     return {"workload": "materialise + FP4 pack, 7 families x 26 layers (Gemma-3-1B shapes), 13 W0 bands, rank 64",
-            "note": "serial: the 182 calls of each kind back to back in one graph; 4 streams: the same "
-                    "independent calls round-robin on 4 streams inside one graph",
+            "batched": batched, "calibration": calib,
+            "note": "batched: one aq_materialize_batch call for all 182 projections, then one "
+                    "aq_quant_fp4_batch call with its maxima; serial: the 182 one-projection calls of each "
+                    "kind back to back in one graph; 4 streams: the same independent calls round-robin on 4 "
+                    "streams inside one graph",
             "materialize": dict(leg(ms_m, mbytes), bytes=mbytes, avg_launch_us=_r(mat_avg * 1e3, 2),
                                 streams4=leg(ms_m4, mbytes),
                                 largest_projection={"bytes": big_bytes, "avg_launch_us": _r(big_avg * 1e3, 2),
@@ -1018,7 +1105,7 @@ def main():
                     choices=["headline", "gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4",
                              "fp4_decode", "fold", "rebuild", "decompose", "pmc_probe", "pmc_probe_fp4"])
     ap.add_argument("--probe", default="decode_gateup",
-                    choices=["decode_gateup", "decode_gateup_large", "prefill_gateup_large"],
+                    choices=["decode_gateup", "decode_gateup_large", "prefill_gateup_large", "load_batch"],
                     help="with --workload pmc_probe: which dispatches the counter run covers")
     ap.add_argument("--summarize", action="store_true",
                     help="summarise rocprofv3 CSVs (--trace, --fetch/--write, --pmc) instead of running")

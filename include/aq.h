@@ -190,6 +190,49 @@ aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t
                                uint8_t *packed, uint8_t *scales, float *global_scale,
                                void *ws, size_t ws_bytes, void *stream);
 
+/* Load-time materialisation of many projections in a few launches (bf16):
+ * items[i] gets w_eff = diag(s) W0 + U Vt exactly as aq_materialize_weff
+ * computes it (same bits), for the whole model at once ("Execution paths",
+ * section "Precompute-outside": every layer's W_eff is rebuilt once at load;
+ * "How attnquant works", section "The theta bundle": the layers of a band share
+ * W0).  Consecutive items that name the same W0 (same pointer, N and K) form
+ * a run -- the layers of one band for one projection family -- and each W0
+ * tile is read once for the first two items of its run (a longer run is taken
+ * two items at a time).  amax: NULL, or n device words; amax[i] receives the
+ * largest magnitude of item i's W_eff as bf16 bits (bits 0..14 of the rounded
+ * values, an exact maximum), which aq_quant_fp4_batch takes to skip its own
+ * pass over the weights.  Per item as aq_materialize_weff (bf16), plus
+ * r <= 64 (AQ_ERR_UNSUPPORTED above: use aq_materialize_weff); errors name
+ * the item ("item 5: ...").  0 <= n <= 65536; no workspace; a few launches
+ * (up to 24 runs each) on stream. */
+typedef struct aq_mat_item {
+  int64_t K;        /* in_dim */
+  aq_proj p;        /* N, r, W0, s, U, Vt */
+  void *w_eff;      /* bf16 [N, ldw], columns 0..K-1 written */
+  int64_t ldw;
+} aq_mat_item;
+aq_status aq_materialize_batch(aq_dtype dt, int n, const aq_mat_item *items, uint32_t *amax, void *stream);
+
+/* Block-16 FP4 pack of many bf16 weights, each exactly as
+ * aq_quant_fp4_block16 packs it (same bytes and global scale), in a few
+ * launches ("Execution paths", section "Precompute-outside": each W_eff is
+ * quantised at load; "Internals and extension", section "Nvfp4Spec").  amax:
+ * the weights' largest magnitudes as bf16 bits (from aq_materialize_batch),
+ * then one pass reads each weight once; NULL: a first pass computes them into
+ * the workspace.  ws: aq_quant_fp4_batch_workspace_bytes(n, amax != NULL)
+ * bytes (0: may be NULL), 256-byte aligned, its first 64 KiB untouched.
+ * Per item as aq_quant_fp4_block16; errors name the item. */
+typedef struct aq_fp4_item {
+  int64_t N, K, ldw;
+  const void *w;          /* bf16 [N, ldw] */
+  uint8_t *packed;        /* [N, K/2] */
+  uint8_t *scales;        /* [N, K/16] */
+  float *global_scale;    /* one device float */
+} aq_fp4_item;
+aq_status aq_quant_fp4_batch(int n, const aq_fp4_item *items, const uint32_t *amax, void *ws, size_t ws_bytes,
+                             void *stream);
+size_t aq_quant_fp4_batch_workspace_bytes(int n, int have_amax);
+
 /* FP4 decode GEMV over a packed weight: y[m, n] = bf16(sum_k x[m, k] * Wq[n, k])
  * for m < M <= 16 tokens, where Wq[n, k] = E2M1(code) * RN_f32(g * E4M3(scale))
  * is the weight that aq_quant_fp4_block16's output stands for ("Execution
@@ -299,7 +342,7 @@ typedef enum aq_debug_knob {
   AQ_DBG_PREFILL_BM, AQ_DBG_PREFILL_BN, AQ_DBG_PREFILL_BK, AQ_DBG_PREFILL_NST, AQ_DBG_PREFILL_W,
   AQ_DBG_PREFILL_S, AQ_DBG_PREFILL_SELF, AQ_DBG_PREFILL_FUSE, AQ_DBG_TPASS_S, AQ_DBG_TPASS_PARTS,
   AQ_DBG_FP4_NG, AQ_DBG_FP4_S, AQ_DBG_FP4_M4, AQ_DBG_HANDOFF_SPIN, AQ_DBG_HANDOFF_UNREACHABLE,
-  AQ_DBG_REBUILD_NG, AQ_DBG_REBUILD_ROWS, AQ_DBG_REBUILD_S,
+  AQ_DBG_REBUILD_NG, AQ_DBG_REBUILD_ROWS, AQ_DBG_REBUILD_S, AQ_DBG_MAT_STEPS, AQ_DBG_FP4_UNIT,
   AQ_DBG_COUNT
 } aq_debug_knob;
 aq_status aq_debug_force_plan(aq_debug_knob knob, int64_t value);

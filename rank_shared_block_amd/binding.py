@@ -31,12 +31,21 @@ DEBUG_KNOBS = ("DECODE_SPLIT", "DECODE_NG", "DECODE_ROWS", "DECODE_S", "DECODE_W
                "PREFILL_BM", "PREFILL_BN", "PREFILL_BK", "PREFILL_NST", "PREFILL_W",
                "PREFILL_S", "PREFILL_SELF", "PREFILL_FUSE", "TPASS_S", "TPASS_PARTS",
                "FP4_NG", "FP4_S", "FP4_M4", "HANDOFF_SPIN", "HANDOFF_UNREACHABLE", "REBUILD_NG",
-               "REBUILD_ROWS", "REBUILD_S")
+               "REBUILD_ROWS", "REBUILD_S", "MAT_STEPS", "FP4_UNIT")
 
 
 class aq_proj(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int64), ("r", ctypes.c_int64), ("W0", ctypes.c_void_p),
                 ("s", ctypes.c_void_p), ("U", ctypes.c_void_p), ("Vt", ctypes.c_void_p)]
+
+
+class aq_mat_item(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int64), ("p", aq_proj), ("w_eff", ctypes.c_void_p), ("ldw", ctypes.c_int64)]
+
+
+class aq_fp4_item(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("K", ctypes.c_int64), ("ldw", ctypes.c_int64), ("w", ctypes.c_void_p),
+                ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_scale", ctypes.c_void_p)]
 
 
 class AQError(RuntimeError):
@@ -93,6 +102,12 @@ def lib():
         L.aq_debug_force_plan.restype = ctypes.c_int
         L.aq_debug_reset_plan.argtypes = []
         L.aq_debug_reset_plan.restype = None
+        L.aq_materialize_batch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(aq_mat_item), vp, vp]
+        L.aq_materialize_batch.restype = ctypes.c_int
+        L.aq_quant_fp4_batch.argtypes = [ctypes.c_int, ctypes.POINTER(aq_fp4_item), vp, vp, sz, vp]
+        L.aq_quant_fp4_batch.restype = ctypes.c_int
+        L.aq_quant_fp4_batch_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.aq_quant_fp4_batch_workspace_bytes.restype = sz
         _lib = L
     return _lib
 
@@ -136,6 +151,18 @@ def aq_materialize_weff(dt, K, p, w_eff, ldw, stream):
 
 def aq_quant_fp4_block16(N, K, w, ldw, packed, scales, global_scale, ws, ws_bytes, stream):
     return lib().aq_quant_fp4_block16(N, K, w, ldw, packed, scales, global_scale, ws, ws_bytes, stream)
+
+
+def aq_materialize_batch(dt, n, items, amax, stream):
+    return lib().aq_materialize_batch(dt, n, items, amax, stream)
+
+
+def aq_quant_fp4_batch(n, items, amax, ws, ws_bytes, stream):
+    return lib().aq_quant_fp4_batch(n, items, amax, ws, ws_bytes, stream)
+
+
+def aq_quant_fp4_batch_workspace_bytes(n, have_amax):
+    return lib().aq_quant_fp4_batch_workspace_bytes(n, have_amax)
 
 
 def aq_workspace_bytes(op, dt, M, K, p, nproj):
@@ -417,6 +444,61 @@ def quant_fp4_block16(w, workspace=None):
     return packed, scales, g
 
 
+def materialize_batch(bundles, outs=None, want_amax=False):
+    """W_eff for many bundles (W0, s, U, Vt) in a few launches (bf16, r <= 64);
+    bundles that name the same W0 tensor next to each other share its reads.
+    Returns the list of W_eff (and, with want_amax, the int32 tensor of their
+    largest magnitudes as bf16 bits, the input of quant_fp4_batch)."""
+    n = len(bundles)
+    if n == 0:
+        return ([], None) if want_amax else []
+    dev = bundles[0][0].device
+    outs = list(outs) if outs is not None else [None] * n
+    items = (aq_mat_item * n)()
+    for i, bd in enumerate(bundles):
+        W0 = bd[0]
+        N, K = W0.shape
+        if outs[i] is None:
+            outs[i] = torch.empty((N, K), dtype=W0.dtype, device=W0.device)
+        o = outs[i]
+        if o.dim() != 2 or o.stride(1) != 1 or o.shape[0] != N or o.shape[1] < K or o.dtype != W0.dtype \
+                or o.device != W0.device:
+            raise ValueError(f"bundle {i}: out must be {W0.dtype} [{N}, >= {K}] with unit column stride on {W0.device}")
+        items[i] = aq_mat_item(K, make_proj(*bd), _ptr(o), o.stride(0))
+    amax = torch.empty(n, dtype=torch.int32, device=dev) if want_amax else None
+    check(lib().aq_materialize_batch(_dt(bundles[0][0]), n, items, _ptr(amax) if want_amax else None, _stream()))
+    return (outs, amax) if want_amax else outs
+
+
+def quant_fp4_batch(weights, amax=None, workspace=None):
+    """FP4 pack of many bf16 [N, K] weights in a few launches; amax (from
+    materialize_batch) lets it read each weight once.  Returns a list of
+    (packed, scales, global_scale) as quant_fp4_block16."""
+    n = len(weights)
+    if n == 0:
+        return []
+    dev = weights[0].device
+    items = (aq_fp4_item * n)()
+    out = []
+    for i, w in enumerate(weights):
+        if w.dtype != torch.bfloat16 or w.dim() != 2 or w.stride(1) != 1 or w.device != dev:
+            raise ValueError(f"weight {i}: must be a 2-D bfloat16 tensor with unit column stride on {dev}")
+        N, K = w.shape
+        if K % 16:
+            raise ValueError(f"weight {i}: K = {K} must be a multiple of 16")
+        packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+        g = torch.empty((1,), dtype=torch.float32, device=dev)
+        items[i] = aq_fp4_item(N, K, w.stride(0), _ptr(w), _ptr(packed), _ptr(scales), _ptr(g))
+        out.append((packed, scales, g))
+    if amax is not None and (amax.dtype != torch.int32 or amax.numel() != n or amax.device != dev):
+        raise ValueError(f"amax must be an int32 tensor of {n} words on {dev}")
+    need = lib().aq_quant_fp4_batch_workspace_bytes(n, 1 if amax is not None else 0)
+    ws, ws_bytes = (workspace or _WS).get(need, dev)
+    check(lib().aq_quant_fp4_batch(n, items, _ptr(amax) if amax is not None else None, ws, ws_bytes, _stream()))
+    return out
+
+
 def aq_fp4_linear(M, N, K, x, ldx, packed, scales, global_scale, y, ldy, ws, ws_bytes, stream):
     return lib().aq_fp4_linear(M, N, K, x, ldx, packed, scales, global_scale, y, ldy, ws, ws_bytes, stream)
 
@@ -575,10 +657,20 @@ def materialize_model(shared, layers, quant=None):
     ``quant="nvfp4"``) its FP4 pack.  Returns ``{layer: {family: W_eff}}`` or
     ``{layer: {family: (packed, scales, global_scale)}}``."""
     check_bundles(shared, layers, quant)
-    out = {}
-    for l in sorted(layers):
-        out[l] = {}
-        for f in sorted(layers[l]):
+    # family by family, band by band: the layers of one band sit next to each
+    # other, so each of their shared blocks is read once per pair of layers
+    order = sorted(((f, layers[l][f][0], l) for l in layers for f in layers[l]), key=lambda k: (k[0], str(k[1]), k[2]))
+    batch = [(f, b, l) for f, b, l in order if shared[b][f].dtype == torch.bfloat16
+             and (layers[l][f][2] is None or layers[l][f][2].shape[1] <= 64)]
+    out = {l: {} for l in layers}
+    if batch:
+        bundles = [(shared[b][f],) + tuple(layers[l][f][1:]) for f, b, l in batch]
+        ws, amax = materialize_batch(bundles, want_amax=True)
+        packs = quant_fp4_batch(ws, amax) if quant == "nvfp4" else ws
+        for (f, b, l), v in zip(batch, packs):
+            out[l][f] = v
+    for f, b, l in order:                  # fp32 weights and ranks above 64
+        if f not in out[l]:
             band, s, U, Vt = layers[l][f]
             w = materialize((shared[band][f], s, U, Vt))
             out[l][f] = quant_fp4_block16(w) if quant == "nvfp4" else w

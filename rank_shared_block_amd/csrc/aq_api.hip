@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "aq_internal.h"
 
@@ -45,6 +46,7 @@ constexpr int64_t kMaxDim = int64_t(1) << 24;
 constexpr int64_t kMaxK = (int64_t(1) << 22) - 1;    // 32-bit buffer offsets over 256-row tiles
 constexpr int64_t kMaxM = int64_t(1) << 19;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+constexpr int kMaxBatchItems = 1 << 16;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -337,8 +339,8 @@ aq_status aq_recon_linear_noalloc(aq_dtype dt, int64_t M, int64_t K, const void 
   return recon(dt, M, K, x, ldx, p, nproj, y, ldy, ws, kScratchBytes, stream, true);
 }
 
-aq_status aq_materialize_weff(aq_dtype dt, int64_t K, const aq_proj *p, void *w_eff,
-                              int64_t ldw, void *stream) {
+// Argument checks of one materialisation (also each item of a batch).
+static aq_status check_materialize(aq_dtype dt, int64_t K, const aq_proj *p, const void *w_eff, int64_t ldw) {
   if (dt != AQ_F32 && dt != AQ_BF16) return fail(AQ_ERR_INVALID_ARG, "dtype %d is not AQ_F32 or AQ_BF16", (int)dt);
   if (!p) return fail(AQ_ERR_INVALID_ARG, "projection descriptor pointer is NULL");
   if (K < 1) return fail(AQ_ERR_SHAPE, "K = %lld must be >= 1", (long long)K);
@@ -357,15 +359,29 @@ aq_status aq_materialize_weff(aq_dtype dt, int64_t K, const aq_proj *p, void *w_
   if (!aligned(p->W0, 16) || !aligned(w_eff, 16)) return fail(AQ_ERR_ALIGNMENT, "W0 and w_eff must be 16-byte aligned");
   if (p->r > 0 && !aligned(p->Vt, 16)) return fail(AQ_ERR_ALIGNMENT, "Vt must be 16-byte aligned");
   if (!aligned(p->s, esize(dt)) || (p->r > 0 && !aligned(p->U, esize(dt)))) return fail(AQ_ERR_ALIGNMENT, "s or U is not naturally aligned");
+  return AQ_OK;
+}
+
+// Prefixes the detail string of the failure just recorded with the item index.
+static aq_status item_fail(aq_status st, int i) {
+  char tmp[sizeof g_err];
+  snprintf(tmp, sizeof tmp, "item %d: %s", i, g_err);
+  memcpy(g_err, tmp, sizeof g_err);
+  return st;
+}
+
+aq_status aq_materialize_weff(aq_dtype dt, int64_t K, const aq_proj *p, void *w_eff,
+                              int64_t ldw, void *stream) {
+  const aq_status cs = check_materialize(dt, K, p, w_eff, ldw);
+  if (cs != AQ_OK) return cs;
   aq::Proj P{p->N, p->r, p->W0, p->s, p->U, p->Vt, 0};
   hipError_t e = aq::launch_materialize(dt, K, P, w_eff, ldw, (hipStream_t)stream);
   if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return AQ_OK;
 }
 
-aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t ldw,
-                               uint8_t *packed, uint8_t *scales, float *global_scale,
-                               void *ws, size_t ws_bytes, void *stream) {
+static aq_status check_fp4_pack(int64_t N, int64_t K, const void *w_bf16, int64_t ldw, const uint8_t *packed,
+                                const uint8_t *scales, const float *global_scale) {
   if (N < 1) return fail(AQ_ERR_SHAPE, "N = %lld must be >= 1", (long long)N);
   if (K < 16) return fail(AQ_ERR_SHAPE, "K = %lld must be >= 16", (long long)K);
   if (N > kMaxDim || K > kMaxDim) return fail(AQ_ERR_UNSUPPORTED, "N or K exceeds 2^24");
@@ -377,11 +393,69 @@ aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t
   if (!aligned(w_bf16, 16)) return fail(AQ_ERR_ALIGNMENT, "w is not 16-byte aligned");
   if (!aligned(packed, 8)) return fail(AQ_ERR_ALIGNMENT, "packed is not 8-byte aligned");
   if (!aligned(global_scale, 4)) return fail(AQ_ERR_ALIGNMENT, "global_scale is not 4-byte aligned");
+  return AQ_OK;
+}
+
+aq_status aq_quant_fp4_block16(int64_t N, int64_t K, const void *w_bf16, int64_t ldw,
+                               uint8_t *packed, uint8_t *scales, float *global_scale,
+                               void *ws, size_t ws_bytes, void *stream) {
+  const aq_status cs = check_fp4_pack(N, K, w_bf16, ldw, packed, scales, global_scale);
+  if (cs != AQ_OK) return cs;
   const size_t need = aq::kWsReserved + (size_t)aq::kFp4AmaxBlocks * 4;
   if (!ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
   if (ws_bytes < need) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
   if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   hipError_t e = aq::launch_fp4(N, K, w_bf16, ldw, packed, scales, global_scale, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return AQ_OK;
+}
+
+aq_status aq_materialize_batch(aq_dtype dt, int n, const aq_mat_item *items, uint32_t *amax, void *stream) {
+  if (dt != AQ_BF16) return fail(AQ_ERR_UNSUPPORTED, "the batched materialisation is bf16 only (dtype %d)", (int)dt);
+  if (n < 0 || n > kMaxBatchItems) return fail(AQ_ERR_INVALID_ARG, "n = %d outside [0, %d]", n, kMaxBatchItems);
+  if (n == 0) return AQ_OK;
+  if (!items) return fail(AQ_ERR_INVALID_ARG, "items is NULL");
+  if (amax && !aligned(amax, 4)) return fail(AQ_ERR_ALIGNMENT, "amax is not 4-byte aligned");
+  std::vector<aq::MatItem> v((size_t)n);
+  for (int i = 0; i < n; ++i) {
+    const aq_mat_item &it = items[i];
+    const aq_status cs = check_materialize(dt, it.K, &it.p, it.w_eff, it.ldw);
+    if (cs != AQ_OK) return item_fail(cs, i);
+    if (it.p.r > aq::kMatBatchMaxRank)
+      return item_fail(fail(AQ_ERR_UNSUPPORTED, "rank %lld above %d (use aq_materialize_weff)", (long long)it.p.r,
+                            aq::kMatBatchMaxRank), i);
+    v[(size_t)i] = aq::MatItem{it.p.N, it.K, it.p.r, it.ldw, it.p.W0, it.p.s, it.p.U, it.p.Vt, it.w_eff};
+  }
+  hipError_t e = aq::launch_materialize_batch(n, v.data(), amax, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return AQ_OK;
+}
+
+size_t aq_quant_fp4_batch_workspace_bytes(int n, int have_amax) {
+  if (n < 1 || n > kMaxBatchItems) return 0;
+  return aq::fp4_batch_ws_bytes(n, have_amax != 0);
+}
+
+aq_status aq_quant_fp4_batch(int n, const aq_fp4_item *items, const uint32_t *amax, void *ws, size_t ws_bytes,
+                             void *stream) {
+  if (n < 0 || n > kMaxBatchItems) return fail(AQ_ERR_INVALID_ARG, "n = %d outside [0, %d]", n, kMaxBatchItems);
+  if (n == 0) return AQ_OK;
+  if (!items) return fail(AQ_ERR_INVALID_ARG, "items is NULL");
+  if (amax && !aligned(amax, 4)) return fail(AQ_ERR_ALIGNMENT, "amax is not 4-byte aligned");
+  std::vector<aq::Fp4Item> v((size_t)n);
+  for (int i = 0; i < n; ++i) {
+    const aq_fp4_item &it = items[i];
+    const aq_status cs = check_fp4_pack(it.N, it.K, it.w, it.ldw, it.packed, it.scales, it.global_scale);
+    if (cs != AQ_OK) return item_fail(cs, i);
+    v[(size_t)i] = aq::Fp4Item{it.N, it.K, it.ldw, it.w, it.packed, it.scales, it.global_scale};
+  }
+  const size_t need = aq::fp4_batch_ws_bytes(n, amax != nullptr);
+  if (need > 0) {
+    if (!ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+    if (ws_bytes < need) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
+    if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  }
+  hipError_t e = aq::launch_fp4_batch(n, v.data(), amax, ws, (hipStream_t)stream);
   if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return AQ_OK;
 }

@@ -142,10 +142,36 @@ hipError_t launch_recon_f32(const Recon &rq, hipStream_t st);
 hipError_t launch_materialize(aq_dtype dt, int64_t K, const Proj &p, void *w, int64_t ldw,
                               hipStream_t st);
 
+// Many projections per launch (bf16, r <= 64): consecutive items that name the
+// same W0 (and N, K) share each read of a W0 tile, up to kMatRunMax of them.
+constexpr int kMatRunMax = 2, kMatBatchRuns = 24, kMatBatchOuts = 48, kMatBatchMaxRank = 64;
+struct MatItem {
+  int64_t N, K, r, ldw;
+  const void *W0, *s, *U, *Vt;
+  void *w;
+};
+// amax: NULL, or n device words that receive each W_eff's largest magnitude as
+// bf16 bits (zeroed here first).
+hipError_t launch_materialize_batch(int n, const MatItem *items, unsigned *amax, hipStream_t st);
+
 // ---- FP4 pack -------------------------------------------------------------------
 constexpr int kFp4AmaxBlocks = 1024;
 hipError_t launch_fp4(int64_t N, int64_t K, const void *w, int64_t ldw, uint8_t *packed,
                       uint8_t *scales, float *gscale, void *ws, hipStream_t st);
+
+// Many weights per launch: the pack of each weight as above, its global scale
+// from amax (bf16 bits of its largest magnitude, e.g. from
+// launch_materialize_batch) or, when amax is NULL, from a batched max pass into
+// the workspace (fp4_batch_ws_bytes).
+constexpr int kFp4BatchItems = 64;
+struct Fp4Item {
+  int64_t N, K, ldw;
+  const void *w;
+  uint8_t *packed, *scales;
+  float *gscale;
+};
+size_t fp4_batch_ws_bytes(int n, bool have_amax);
+hipError_t launch_fp4_batch(int n, const Fp4Item *items, const unsigned *amax, void *ws, hipStream_t st);
 
 // ---- FP4 decode GEMV --------------------------------------------------------------
 struct Fp4LinPlan {

@@ -86,6 +86,73 @@ __device__ __forceinline__ double e4m3_value(uint32_t b) {
   return b < 8 ? ldexp((double)b, -9) : ldexp((double)(8 + (b & 7)), (int)(b >> 3) - 10);
 }
 
+// One 16-value block (its bf16 bits in q[0..7], element 2i in the low half of
+// q[i]) with global scale g: the E4M3 scale byte and the 16 codes.
+__device__ __forceinline__ void pack_block16(const uint32_t q[8], float g, uint32_t &lo, uint32_t &hi,
+                                             uint32_t &sf) {
+  uint32_t amag = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    amag = max(amag, q[i] & 0x7FFFu);
+    amag = max(amag, (q[i] >> 16) & 0x7FFFu);
+  }
+  const double ab = (double)bf2f((uint16_t)amag);
+  sf = e4m3_rne_sat(ab / (6.0 * (double)g));
+  const float D = (float)((double)g * e4m3_value(sf));
+  lo = 0;
+  hi = 0;
+  if (D >= 0x1p-90f) {
+    // Code = number of E2M1 midpoints m_i D below |w| (ties to the even code:
+    // strictly above m_0, m_2, m_4, m_6; at or above m_1, m_3, m_5), found by a
+    // three-step binary search over the monotone midpoints, in fp32: with
+    // p = RN(m_i D) and its exact residual e = m_i D - p (an fma; no underflow
+    // for D >= 2^-90), a float x is >= m_i D iff x >= p (e <= 0) or x >= the
+    // next float above p (e > 0), and > m_i D iff x >= p (e < 0) or x >= the
+    // next float above p (e >= 0).  So every test is one exact fp32 x >= T_i.
+    float T[7];
+    const float mid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      const float pr = mid[i] * D, e = __builtin_fmaf(mid[i], D, -pr);
+      const bool up = (i & 1) ? e > 0.f : e >= 0.f;
+      T[i] = up ? __uint_as_float(__float_as_uint(pr) + 1u) : pr;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t bits = (q[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+      const float x = __uint_as_float((bits & 0x7FFFu) << 16);
+      const bool b4 = x >= T[3];
+      const bool b2 = x >= (b4 ? T[5] : T[1]);
+      const float tl = b4 ? (b2 ? T[6] : T[4]) : (b2 ? T[2] : T[0]);
+      uint32_t c = (b4 ? 4u : 0u) + (b2 ? 2u : 0u) + (x >= tl ? 1u : 0u);
+      if (c != 0 && (bits & 0x8000u)) c |= 8u;
+      if (i < 8)
+        lo |= c << (4 * i);
+      else
+        hi |= c << (4 * (i - 8));
+    }
+  } else if (D > 0.f) {
+    // Tiny D: the same search on thresholds exact in fp64.
+    const double d = (double)D;
+    const double t0 = 0.25 * d, t1 = 0.75 * d, t2 = 1.25 * d, t3 = 1.75 * d, t4 = 2.5 * d,
+                 t5 = 3.5 * d, t6 = 5.0 * d;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t bits = (q[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+      const double x = (double)bf2f((uint16_t)(bits & 0x7FFFu));
+      const bool b4 = x >= t3;
+      const bool b2 = x >= (b4 ? t5 : t1);
+      const double tl = b4 ? (b2 ? t6 : t4) : (b2 ? t2 : t0);
+      uint32_t c = (b4 ? 4u : 0u) + (b2 ? 2u : 0u) + (x > tl ? 1u : 0u);
+      if (c != 0 && (bits & 0x8000u)) c |= 8u;
+      if (i < 8)
+        lo |= c << (4 * i);
+      else
+        hi |= c << (4 * (i - 8));
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_fp4_pack(const uint16_t *w, int N, int K, int ldw,
                                                   const unsigned *partial, int npartial,
                                                   uint8_t *packed, uint8_t *scales,
@@ -115,66 +182,8 @@ __global__ __launch_bounds__(256) void k_fp4_pack(const uint16_t *w, int N, int 
     const uint16_t *src = w + n * ldw + b * 16;
     const uint4 v0 = ld16(src), v1 = ld16(src + 8);
     const uint32_t q[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t amag = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      amag = max(amag, q[i] & 0x7FFFu);
-      amag = max(amag, (q[i] >> 16) & 0x7FFFu);
-    }
-    const double ab = (double)bf2f((uint16_t)amag);
-    const uint32_t sf = e4m3_rne_sat(ab / (6.0 * (double)g));
-    const float D = (float)((double)g * e4m3_value(sf));
-    uint32_t lo = 0, hi = 0;
-    if (D >= 0x1p-90f) {
-      // Code = number of E2M1 midpoints m_i D below |w| (ties to the even code:
-      // strictly above m_0, m_2, m_4, m_6; at or above m_1, m_3, m_5), found by a
-      // three-step binary search over the monotone midpoints, in fp32: with
-      // p = RN(m_i D) and its exact residual e = m_i D - p (an fma; no underflow
-      // for D >= 2^-90), a float x is >= m_i D iff x >= p (e <= 0) or x >= the
-      // next float above p (e > 0), and > m_i D iff x >= p (e < 0) or x >= the
-      // next float above p (e >= 0).  So every test is one exact fp32 x >= T_i.
-      float T[7];
-      const float mid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-#pragma unroll
-      for (int i = 0; i < 7; ++i) {
-        const float pr = mid[i] * D, e = __builtin_fmaf(mid[i], D, -pr);
-        const bool up = (i & 1) ? e > 0.f : e >= 0.f;
-        T[i] = up ? __uint_as_float(__float_as_uint(pr) + 1u) : pr;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t bits = (q[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-        const float x = __uint_as_float((bits & 0x7FFFu) << 16);
-        const bool b4 = x >= T[3];
-        const bool b2 = x >= (b4 ? T[5] : T[1]);
-        const float tl = b4 ? (b2 ? T[6] : T[4]) : (b2 ? T[2] : T[0]);
-        uint32_t c = (b4 ? 4u : 0u) + (b2 ? 2u : 0u) + (x >= tl ? 1u : 0u);
-        if (c != 0 && (bits & 0x8000u)) c |= 8u;
-        if (i < 8)
-          lo |= c << (4 * i);
-        else
-          hi |= c << (4 * (i - 8));
-      }
-    } else if (D > 0.f) {
-      // Tiny D: the same search on thresholds exact in fp64.
-      const double d = (double)D;
-      const double t0 = 0.25 * d, t1 = 0.75 * d, t2 = 1.25 * d, t3 = 1.75 * d, t4 = 2.5 * d,
-                   t5 = 3.5 * d, t6 = 5.0 * d;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t bits = (q[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-        const double x = (double)bf2f((uint16_t)(bits & 0x7FFFu));
-        const bool b4 = x >= t3;
-        const bool b2 = x >= (b4 ? t5 : t1);
-        const double tl = b4 ? (b2 ? t6 : t4) : (b2 ? t2 : t0);
-        uint32_t c = (b4 ? 4u : 0u) + (b2 ? 2u : 0u) + (x > tl ? 1u : 0u);
-        if (c != 0 && (bits & 0x8000u)) c |= 8u;
-        if (i < 8)
-          lo |= c << (4 * i);
-        else
-          hi |= c << (4 * (i - 8));
-      }
-    }
+    uint32_t lo, hi, sf;
+    pack_block16(q, g, lo, hi, sf);
     *reinterpret_cast<uint2 *>(packed + n * (K >> 1) + b * 8) = make_uint2(lo, hi);
     scales[n * kb + b] = (uint8_t)sf;
   }
@@ -196,6 +205,164 @@ hipError_t launch_fp4(int64_t N, int64_t K, const void *w, int64_t ldw, uint8_t 
   hipLaunchKernelGGL(k_fp4_pack, dim3((unsigned)g2), dim3(256), 0, st, (const uint16_t *)w,
                      (int)N, (int)K, (int)ldw, (const unsigned *)ws, g1, packed, scales, gscale);
   return hipGetLastError();
+}
+
+// ---- many weights per launch (load time) ----------------------------------------
+//
+// A work unit is 256 x BPT consecutive 16-value blocks of one weight (BPT per
+// thread, all 2 BPT 16-byte loads requested before any is used).  The
+// global scale of each weight comes from amax[] (its largest magnitude as bf16
+// bits): from the batched materialisation, which folds it in while writing
+// W_eff, or from k_fp4_amax_batch over the weights here.  The encoding is
+// pack_block16, as for one weight, so the bytes are identical.
+struct Fp4BItem {
+  const uint16_t *w;
+  uint8_t *packed, *scales;
+  float *gscale;
+  int N, K, ldw, unit0;
+};
+struct Fp4BatchArgs {
+  int nitem, nunits, amax0, pad;
+  unsigned *amax;
+  Fp4BItem item[kFp4BatchItems];
+};
+static_assert(sizeof(Fp4BatchArgs) <= 3584, "kernel arguments stay well inside 4 KiB");
+
+__device__ __forceinline__ int fp4b_item(const Fp4BatchArgs &a, int unit) {
+  int i = 0;
+  for (int j = 1; j < a.nitem; ++j)
+    if (unit >= a.item[j].unit0) i = j;
+  return i;
+}
+
+// Loads of the BPT blocks of this thread (zeros past the weight).
+template <int BPT>
+__device__ __forceinline__ void fp4b_load(const Fp4BItem &I, long b0, uint4 (&v)[2 * BPT], long (&blk)[BPT]) {
+  const int kb = I.K >> 4;
+  const long nblocks = (long)I.N * kb;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    blk[j] = b0 + 256 * j + threadIdx.x;
+    if (blk[j] < nblocks) {
+      const long n = blk[j] / kb;
+      const uint16_t *src = I.w + n * I.ldw + (blk[j] - n * kb) * 16;
+      v[2 * j] = ld16(src);
+      v[2 * j + 1] = ld16(src + 8);
+    } else {
+      v[2 * j] = v[2 * j + 1] = make_uint4(0, 0, 0, 0);
+      blk[j] = -1;
+    }
+  }
+}
+
+template <int BPT>
+__global__ __launch_bounds__(256) void k_fp4_amax_batch(const Fp4BatchArgs a) {
+  const int unit = (int)blockIdx.x;
+  const int ii = fp4b_item(a, unit);
+  const Fp4BItem &I = a.item[ii];
+  uint4 v[2 * BPT];
+  long blk[BPT];
+  fp4b_load<BPT>(I, (long)(unit - I.unit0) * 256 * BPT, v, blk);
+  unsigned m = 0;
+#pragma unroll
+  for (int j = 0; j < 2 * BPT; ++j) {
+    const uint32_t q[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max(q[i] & 0x7FFFu, (q[i] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, o));
+  __shared__ unsigned red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(a.amax + a.amax0 + ii, max(max(red[0], red[1]), max(red[2], red[3])));
+}
+
+template <int BPT>
+__global__ __launch_bounds__(256) void k_fp4_pack_batch(const Fp4BatchArgs a) {
+  const int unit = (int)blockIdx.x;
+  const int ii = fp4b_item(a, unit);
+  const Fp4BItem &I = a.item[ii];
+  uint4 v[2 * BPT];
+  long blk[BPT];
+  const long b0 = (long)(unit - I.unit0) * 256 * BPT;
+  fp4b_load<BPT>(I, b0, v, blk);
+  const float A = bf2f((uint16_t)a.amax[a.amax0 + ii]);
+  const float g = A == 0.f ? 1.0f : (float)((double)A / 2688.0);
+  if (b0 == 0 && threadIdx.x == 0) *I.gscale = g;
+  const int kb = I.K >> 4;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    if (blk[j] < 0) continue;
+    const uint32_t q[8] = {v[2 * j].x, v[2 * j].y, v[2 * j].z, v[2 * j].w,
+                           v[2 * j + 1].x, v[2 * j + 1].y, v[2 * j + 1].z, v[2 * j + 1].w};
+    uint32_t lo, hi, sf;
+    pack_block16(q, g, lo, hi, sf);
+    const long n = blk[j] / kb, b = blk[j] - n * kb;
+    *reinterpret_cast<uint2 *>(I.packed + n * (I.K >> 1) + b * 8) = make_uint2(lo, hi);
+    I.scales[n * kb + b] = (uint8_t)sf;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fp4_fill_u32(unsigned *p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+size_t fp4_batch_ws_bytes(int n, bool have_amax) {
+  return have_amax ? 0 : kWsReserved + ((size_t)n * 4 + 255) / 256 * 256;
+}
+
+hipError_t launch_fp4_batch(int n, const Fp4Item *it, const unsigned *amax_in, void *ws, hipStream_t st) {
+  unsigned *amax = const_cast<unsigned *>(amax_in);
+  const bool own = amax == nullptr;
+  if (own) {
+    amax = (unsigned *)((char *)ws + kWsReserved);
+    hipLaunchKernelGGL(k_fp4_fill_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, amax, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  int bpt = debug_knob(AQ_DBG_FP4_UNIT, 2);
+  if (bpt != 1 && bpt != 2 && bpt != 4 && bpt != 8) bpt = 2;
+  const int unit_blocks = 256 * bpt;
+  for (int pass = own ? 0 : 1; pass < 2; ++pass) {
+    for (int i0 = 0; i0 < n; i0 += kFp4BatchItems) {
+      Fp4BatchArgs a = {};
+      a.amax = amax;
+      a.amax0 = i0;
+      int units = 0;
+      for (int i = i0; i < n && a.nitem < kFp4BatchItems; ++i) {
+        Fp4BItem &I = a.item[a.nitem++];
+        I.w = (const uint16_t *)it[i].w;
+        I.packed = it[i].packed;
+        I.scales = it[i].scales;
+        I.gscale = it[i].gscale;
+        I.N = (int)it[i].N;
+        I.K = (int)it[i].K;
+        I.ldw = (int)it[i].ldw;
+        I.unit0 = units;
+        const long nblocks = it[i].N * (it[i].K / 16);
+        units += (int)((nblocks + unit_blocks - 1) / unit_blocks);
+      }
+      a.nunits = units;
+      const dim3 grid((unsigned)units);
+#define AQ_FP4B(B)                                                                     \
+  if (bpt == B) {                                                                      \
+    if (pass == 0)                                                                     \
+      hipLaunchKernelGGL(k_fp4_amax_batch<B>, grid, dim3(256), 0, st, a);              \
+    else                                                                               \
+      hipLaunchKernelGGL(k_fp4_pack_batch<B>, grid, dim3(256), 0, st, a);              \
+  }
+      AQ_FP4B(1)
+      AQ_FP4B(2)
+      AQ_FP4B(4)
+      AQ_FP4B(8)
+#undef AQ_FP4B
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace aq

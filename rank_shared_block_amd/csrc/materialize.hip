@@ -216,6 +216,272 @@ __global__ __launch_bounds__(256) void k_materialize_f32(const MatArgs a) {
   }
 }
 
+// ---- many projections per launch (load time) ----------------------------------
+//
+// The whole model's W_eff in a few launches instead of one per projection: a
+// work unit is one 128-row x 64-column tile of a shared block W0 together with
+// every output of its run (consecutive items that name the same W0, i.e. the
+// layers of one band, up to kMatRunMax of them): the W0 tile is read from HBM
+// once and each output's W_eff tile is formed from it with the same arithmetic
+// and summation order as k_materialize_bf16 (so the bits are identical).  Units
+// are numbered run by run, row block by row block, column blocks fastest, and
+// remapped so that each XCD takes a contiguous range: the units that share a U
+// row block or a run's Vt share one L2.  Optionally each output's largest
+// magnitude (bits 0..14 of the rounded bf16 values, an exact integer maximum)
+// is folded into amax[] with one atomic maximum per unit and output, which lets
+// the FP4 pack skip its own pass over W_eff.
+struct MatBOut {
+  const uint16_t *s, *U, *Vt;
+  uint16_t *w;
+  int r, ldw;
+};
+struct MatBRun {
+  const uint16_t *W0;
+  int N, K, colblocks, unit0, out0, nout;
+};
+struct MatBatchArgs {
+  int nrun, nunits, amax0, ufast_all, steps;
+  unsigned *amax;          // NULL: no maxima; else amax[amax0 + output index]
+  MatBRun run[kMatBatchRuns];
+  MatBOut out[kMatBatchOuts];
+};
+static_assert(sizeof(MatBatchArgs) <= 3584, "kernel arguments stay well inside 4 KiB");
+
+template <int RJ>
+__global__ __launch_bounds__(256, 3) void k_materialize_batch(const MatBatchArgs a) {
+  constexpr int CB = 64, RB = 128;
+  constexpr int RP = 16 * RJ + 8, WP = CB + 8;
+  constexpr int NQ = RB * CB / 8 / 256;     // 16-byte W0 chunks per thread and step
+  __shared__ __attribute__((aligned(16))) uint16_t vts[kMatRunMax][CB * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t wt[RB * WP];
+  __shared__ unsigned red[4][kMatRunMax];
+  const int unit = xcd_contiguous_tile((int)blockIdx.x, a.nunits);
+  if (unit < 0) return;
+  int ri = 0;
+  for (int i = 1; i < a.nrun; ++i)
+    if (unit >= a.run[i].unit0) ri = i;
+  const MatBRun &R = a.run[ri];
+  const int u = unit - R.unit0;
+  const int K = R.K, N = R.N, nout = R.nout;
+  // a unit: one 64-column block and a.steps row steps of 128 rows
+  const int cb0 = (u % R.colblocks) * CB, g0 = (u / R.colblocks) * RB * a.steps;
+  const int gend = min(N, g0 + RB * a.steps);
+  const int ncol = min(CB, K - cb0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // W0 tile of a step, as 16-byte chunks (zeros past N and K)
+  uint4 wv[NQ];
+  auto load_w0 = [&](int n0) __attribute__((always_inline)) {
+    const int nrow = min(RB, gend - n0);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int c = tid + 256 * q, row = c >> 3, col = (c & 7) * 8;
+      wv[q] = row < nrow && col < ncol ? ld16(R.W0 + (size_t)(n0 + row) * K + cb0 + col) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  load_w0(g0);
+  // Each output's Vt[:, cb0 : cb0 + 64], transposed (zeros past r or K), once
+  // per unit: every row step uses it.
+  for (int o = 0; o < nout; ++o) {
+    const MatBOut &O = a.out[R.out0 + o];
+    for (int i = tid; i < 16 * RJ * (CB / 8); i += 256) {
+      const int j = i % (16 * RJ), c = (i / (16 * RJ)) * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (j < O.r && c < ncol) v = ld16(O.Vt + (size_t)j * K + cb0 + c);
+      const uint32_t q4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) vts[o][(c + q) * RP + j] = (uint16_t)(q4[q >> 1] >> ((q & 1) * 16));
+    }
+  }
+
+  unsigned amx[kMatRunMax];
+#pragma unroll
+  for (int o = 0; o < kMatRunMax; ++o) amx[o] = 0u;
+  for (int n0 = g0; n0 < gend; n0 += RB) {
+    const int nrow = min(RB, gend - n0);
+    // This lane's output row: its s and U row (the B operand) per output.
+    const int rl = 32 * wave + l32, n = n0 + rl;
+    const bool rowok = rl < nrow;
+    uint16_t s_raw[kMatRunMax];
+    bf16x8 bu[kMatRunMax][RJ];
+#pragma unroll
+    for (int o = 0; o < kMatRunMax; ++o) {
+      const MatBOut &O = a.out[R.out0 + (o < nout ? o : 0)];
+      s_raw[o] = O.s[rowok ? n : n0];
+#pragma unroll
+      for (int kk = 0; kk < RJ; ++kk) {
+        const int j = 16 * kk + 8 * hi;
+        if (o >= nout || !rowok || j >= O.r) {
+          bu[o][kk] = zero_bf16x8();
+        } else if (a.ufast_all) {
+          bu[o][kk] = as_bf16x8(ld16(O.U + (size_t)n * O.r + j));
+        } else {
+          uint16_t v[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] = (j + q < O.r) ? O.U[(size_t)n * O.r + j + q] : (uint16_t)0;
+          uint4 w;
+          w.x = v[0] | ((uint32_t)v[1] << 16);
+          w.y = v[2] | ((uint32_t)v[3] << 16);
+          w.z = v[4] | ((uint32_t)v[5] << 16);
+          w.w = v[6] | ((uint32_t)v[7] << 16);
+          bu[o][kk] = as_bf16x8(w);
+        }
+      }
+    }
+    __syncthreads();                        // the previous step's stores have read wt (and Vt is staged)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int c = tid + 256 * q, row = c >> 3, col = (c & 7) * 8;
+      *reinterpret_cast<uint4 *>(&wt[row * WP + col]) = wv[q];
+    }
+    if (n0 + RB < gend) load_w0(n0 + RB);   // the next step's W0 tile, in flight during this step
+    __syncthreads();
+    // This lane's W0 values, in the accumulator layout (see below).
+    uint2 w0[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) w0[t][g] = *reinterpret_cast<const uint2 *>(&wt[rl * WP + 32 * t + 8 * g + 4 * hi]);
+
+#pragma unroll
+    for (int o = 0; o < kMatRunMax; ++o) {
+      if (o >= nout) break;
+      const MatBOut &O = a.out[R.out0 + o];
+      // acc[t]: column 32 t + 8 (v / 4) + 4 hi + (v % 4) of row n, as in
+      // k_materialize_bf16 (same operands, same order of the rank steps).
+      f32x16 acc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+      if (O.r > 0) {
+#pragma unroll
+        for (int kk = 0; kk < RJ; ++kk)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4 *>(&vts[o][(32 * t + l32) * RP + 16 * kk + 8 * hi]));
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bu[o][kk], acc[t], 0, 0, 0);
+          }
+      }
+      __syncthreads();                      // every lane is done reading wt
+      const float sv = bf2f(s_raw[o]);
+      unsigned m = amx[o];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint2 w = w0[t][g];
+          const uint32_t e0 = f2bf(fmaf(sv, bf2f((uint16_t)w.x), acc[t][4 * g + 0]));
+          const uint32_t e1 = f2bf(fmaf(sv, bf2f((uint16_t)(w.x >> 16)), acc[t][4 * g + 1]));
+          const uint32_t e2 = f2bf(fmaf(sv, bf2f((uint16_t)w.y), acc[t][4 * g + 2]));
+          const uint32_t e3 = f2bf(fmaf(sv, bf2f((uint16_t)(w.y >> 16)), acc[t][4 * g + 3]));
+          m = max(max(m, max(e0 & 0x7FFFu, e1 & 0x7FFFu)), max(e2 & 0x7FFFu, e3 & 0x7FFFu));
+          *reinterpret_cast<uint2 *>(&wt[rl * WP + 32 * t + 8 * g + 4 * hi]) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+        }
+      amx[o] = m;                           // rows and columns past the tile hold exact zeros
+      __syncthreads();                      // W_eff tile complete
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int c = tid + 256 * q, row = c >> 3, col = (c & 7) * 8;
+        if (row < nrow && col < ncol)
+          *reinterpret_cast<uint4 *>(O.w + (size_t)(n0 + row) * O.ldw + cb0 + col) =
+              *reinterpret_cast<const uint4 *>(&wt[row * WP + col]);
+      }
+    }
+  }
+  if (a.amax) {
+#pragma unroll
+    for (int o = 0; o < kMatRunMax; ++o) {
+      unsigned m = amx[o];
+#pragma unroll
+      for (int sh = 32; sh > 0; sh >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, sh));
+      if (lane == 0) red[wave][o] = m;
+    }
+    __syncthreads();
+    if (tid < nout) {
+      const unsigned m = max(max(red[0][tid], red[1][tid]), max(red[2][tid], red[3][tid]));
+      atomicMax(a.amax + a.amax0 + R.out0 + tid, m);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_u32(unsigned *p, int n, unsigned v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+int matb_rank_steps(int64_t r) { return r <= 16 ? 1 : (r <= 32 ? 2 : 4); }
+
+hipError_t launch_materialize_batch(int n, const MatItem *it, unsigned *amax, hipStream_t st) {
+  // Row steps per work unit: 128-row steps with the next W0 tile in flight;
+  // longer units keep the pipeline full, shorter ones fill the CUs' last round.
+  int steps = debug_knob(AQ_DBG_MAT_STEPS, 3);
+  if (steps < 1 || steps > 8) steps = 3;
+  if (amax) {
+    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, amax, n, 0u);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  int i = 0;
+  while (i < n) {
+    // One launch: whole runs (consecutive items on one W0, at most kMatRunMax
+    // per run) while they fit in the argument block; the rank steps of the
+    // largest rank of the launch.
+    MatBatchArgs a = {};
+    a.amax = amax;
+    a.amax0 = i;
+    a.ufast_all = 1;
+    a.steps = steps;
+    int nout = 0, units = 0, rj = 1;
+    while (i + nout < n && a.nrun < kMatBatchRuns) {
+      const MatItem &f = it[i + nout];
+      int len = 1;
+      while (len < kMatRunMax && i + nout + len < n) {
+        const MatItem &g = it[i + nout + len];
+        if (g.W0 != f.W0 || g.N != f.N || g.K != f.K) break;
+        ++len;
+      }
+      if (nout + len > kMatBatchOuts) break;
+      MatBRun &R = a.run[a.nrun++];
+      R.W0 = (const uint16_t *)f.W0;
+      R.N = (int)f.N;
+      R.K = (int)f.K;
+      R.colblocks = (int)((f.K + 63) / 64);
+      R.unit0 = units;
+      R.out0 = nout;
+      R.nout = len;
+      units += R.colblocks * (int)((f.N + 128 * steps - 1) / (128 * steps));
+      for (int o = 0; o < len; ++o) {
+        const MatItem &g = it[i + nout + o];
+        MatBOut &O = a.out[nout + o];
+        O.s = (const uint16_t *)g.s;
+        O.U = (const uint16_t *)g.U;
+        O.Vt = (const uint16_t *)g.Vt;
+        O.w = (uint16_t *)g.w;
+        O.r = (int)g.r;
+        O.ldw = (int)g.ldw;
+        if (!(g.r % 8 == 0 && ((uintptr_t)g.U & 15) == 0)) a.ufast_all = 0;
+        const int q = matb_rank_steps(g.r);
+        rj = q > rj ? q : rj;
+      }
+      nout += len;
+    }
+    a.nunits = units;
+    const dim3 grid((unsigned)(8 * ((units + 7) / 8)));
+    if (rj == 1)
+      hipLaunchKernelGGL((k_materialize_batch<1>), grid, dim3(256), 0, st, a);
+    else if (rj == 2)
+      hipLaunchKernelGGL((k_materialize_batch<2>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_materialize_batch<4>), grid, dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    i += nout;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_materialize(aq_dtype dt, int64_t K, const Proj &p, void *w, int64_t ldw,
                               hipStream_t st) {
   MatArgs a = {};

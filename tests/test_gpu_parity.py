@@ -488,6 +488,12 @@ def test_materialize_gemma_r64(fam):
 
 # ------------------------------------------------------------- FP4 pack
 
+def _weff_seeded(bd):
+    """A bundle's effective weight from the oracle, rounded once to bf16: a
+    W_eff-shaped pack input that does not come from the HIP path."""
+    return oracle.rne_bf16(oracle.materialize(*bundle_np(bd)))
+
+
 def _fp4_check(w_dev):
     p, s, g = B.quant_fp4_block16(w_dev)
     ep, es, eg = oracle.fp4_pack(down(w_dev))
@@ -499,8 +505,7 @@ def _fp4_check(w_dev):
 @pytest.mark.parametrize("N,K", [(1, 16), (37, 48), (130, 1056)])
 def test_fp4_small(N, K):
     bd = I.bundle("test", 8, "v", K, N, 8, "bf16")
-    w = B.materialize(bundle_up(bd, "bf16"))
-    _fp4_check(w)
+    _fp4_check(up(_weff_seeded(bd), "bf16"))
 
 
 def test_fp4_edge_blocks():
@@ -552,16 +557,17 @@ def test_fp4_near_midpoints(seed):
 def test_fp4_gemma_full(fam):
     K, N = I.GEMMA_1B[fam]
     bd = I.bundle("materialize_fp4", 1, fam, K, N, 64, "bf16")
-    _fp4_check(B.materialize(bundle_up(bd, "bf16")))
+    _fp4_check(up(_weff_seeded(bd), "bf16"))
 
 
 def test_fp4_strided_source():
     N, K = 40, 96
     bd = I.bundle("test", 9, "o", K, N, 4, "bf16")
     big = torch.zeros((N, K + 32), dtype=torch.bfloat16, device=dev())
-    B.materialize(bundle_up(bd, "bf16"), out=big)
+    wn = _weff_seeded(bd)
+    big[:, :K] = up(wn, "bf16")
     p, s, g = B.quant_fp4_block16(big[:, :K])
-    ep, es, eg = oracle.fp4_pack(down(big[:, :K]))
+    ep, es, eg = oracle.fp4_pack(wn)
     assert np.array_equal(p.cpu().numpy(), ep) and np.array_equal(s.cpu().numpy(), es)
 
 
@@ -616,9 +622,9 @@ def test_workspace_shared_across_call_kinds():
         x = I.activations("test", 600 + M, M, 6912, "bf16")
         y = B.recon_linear(up(x, "bf16"), W, workspace=ws)
         assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"M={M}")
-        w = B.materialize(W)
-        p, s, g = B.quant_fp4_block16(w, workspace=ws)
-        ep, es, eg = oracle.fp4_pack(down(w))
+        wn = _weff_seeded(bd)
+        p, s, g = B.quant_fp4_block16(up(wn, "bf16"), workspace=ws)
+        ep, es, eg = oracle.fp4_pack(wn)
         assert np.array_equal(p.cpu().numpy(), ep) and float(g.cpu()[0]) == eg
 
 

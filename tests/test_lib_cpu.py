@@ -146,6 +146,41 @@ def test_fp4_argument_errors():
     assert q(scales=None) == B.AQ_ERR_INVALID_ARG
 
 
+def test_batch_argument_errors_name_the_item():
+    """The load-time batch calls check every item before any launch and name
+    the first offending one."""
+    def mat_items(**bad):
+        items = (B.aq_mat_item * 3)()
+        for i in range(3):
+            items[i] = B.aq_mat_item(128, _proj(), FAKE, 128)
+        for k, v in bad.items():
+            setattr(items[2], k, v)
+        return items
+    assert B.aq_materialize_batch(B.AQ_BF16, 3, mat_items(ldw=120), None, None) == B.AQ_ERR_SHAPE
+    assert B.last_error().startswith("item 2: ")
+    assert B.aq_materialize_batch(B.AQ_BF16, 3, mat_items(p=_proj(r=65)), None, None) == B.AQ_ERR_UNSUPPORTED
+    assert "item 2" in B.last_error() and "aq_materialize_weff" in B.last_error()
+    assert B.aq_materialize_batch(B.AQ_F32, 3, mat_items(), None, None) == B.AQ_ERR_UNSUPPORTED
+    assert B.aq_materialize_batch(B.AQ_BF16, -1, mat_items(), None, None) == B.AQ_ERR_INVALID_ARG
+    assert B.aq_materialize_batch(B.AQ_BF16, 3, mat_items(), FAKE + 2, None) == B.AQ_ERR_ALIGNMENT
+    assert B.aq_materialize_batch(B.AQ_BF16, 0, None, None, None) == B.AQ_OK
+
+    def fp4_items(**bad):
+        items = (B.aq_fp4_item * 2)()
+        for i in range(2):
+            items[i] = B.aq_fp4_item(32, 64, 64, FAKE, FAKE, FAKE, FAKE)
+        for k, v in bad.items():
+            setattr(items[1], k, v)
+        return items
+    need = B.aq_quant_fp4_batch_workspace_bytes(2, 0)
+    assert need == 65536 + 256 and B.aq_quant_fp4_batch_workspace_bytes(2, 1) == 0
+    assert B.aq_quant_fp4_batch(2, fp4_items(K=40, ldw=40), None, FAKE, need, None) == B.AQ_ERR_ALIGNMENT
+    assert B.last_error().startswith("item 1: ")
+    assert B.aq_quant_fp4_batch(2, fp4_items(), None, FAKE, need - 1, None) == B.AQ_ERR_WORKSPACE
+    assert B.aq_quant_fp4_batch(2, fp4_items(), None, None, 0, None) == B.AQ_ERR_WORKSPACE
+    assert B.aq_quant_fp4_batch(2, fp4_items(packed=FAKE + 4), FAKE, None, 0, None) == B.AQ_ERR_ALIGNMENT
+
+
 def test_fp4_linear_argument_errors_and_workspace():
     def call(M=1, N=64, K=128, ldx=None, ldy=None, x=FAKE, ptr=FAKE):
         return B.aq_fp4_linear(M, N, K, x, K if ldx is None else ldx, ptr, ptr, ptr, ptr,
