@@ -877,20 +877,19 @@ def run_materialize_fp4(args, torch, B, I, nested=False):
             "fp4_pack": dict(leg(ms_p, pbytes), bytes=pbytes, streams4=leg(ms_p4, pbytes))}
 
 
-def run_fp4_decode(args, torch, B, I, nested=False):
-    """Gemma-3-1B-shaped decode layer on FP4-packed W_eff: the four dispatches
-    (stacked QKV 1536 x 1152, o 1152 x 1024, stacked gate/up 13824 x 1152, down
-    1152 x 6912) per layer, 26 layers, M in {1, 4, 16}; each layer's weights are
-    its own W_eff (materialised from the materialise workload's rank-64
-    bundles in 13 W0 bands) packed on the GPU."""
-    L = 26
-    layer_np = I.layer_bundles("materialize_fp4", I.GEMMA_1B, layers=L, r=64, dtype="bf16", num_bands=13)
+def _fp4_decode_model(args, torch, B, I, wl, shapes, L, G, r, Ms, label):
+    """One decoder on FP4-packed W_eff: per layer the four dispatches (stacked
+    QKV, o, stacked gate/up, down), each layer's weights its own W_eff
+    (materialised from its bundles) packed on the GPU; per M the layer time and
+    the stacked gate/up launch's average duration."""
+    layer_np = I.layer_bundles(wl, shapes, layers=L, r=r, dtype="bf16", num_bands=G)
     dev = torch.device("cuda", 0)
     lib = B.lib()
     stream = torch.cuda.current_stream().cuda_stream
     groups = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")), ("down", ("down",))]
     packed = []
     layer_dev = upload_layers(torch, I, layer_np)
+    del layer_np
     for l in range(L):
         row = []
         for name, fams in groups:
@@ -901,14 +900,14 @@ def run_fp4_decode(args, torch, B, I, nested=False):
         packed.append(row)
     del layer_dev
     torch.cuda.synchronize()
-    Ms = (1, 4, 16)
     wsz = max(lib.aq_workspace_bytes(B.AQ_OP_FP4_LINEAR, B.AQ_BF16, M, K,
                                      (B.aq_proj * 1)(B.aq_proj(N, 0, None, None, None, None)), 1)
               for M in Ms for (_, N, K, _, _, _) in packed[0])
     ws = torch.zeros(max(wsz, 256), dtype=torch.uint8, device=dev)
-    keep, per_m, gu = [], {}, []
+    keep, per_m, gu = [], {}, {}
     for M in Ms:
         calls = []
+        gu[M] = []
         for l in range(L):
             for (name, N, K, p, s, g) in packed[l]:
                 x = (torch.randn(M, K, device=dev) * 0.5).to(torch.bfloat16)
@@ -920,25 +919,42 @@ def run_fp4_decode(args, torch, B, I, nested=False):
                          nb, 2 * M * N * K, f"fp4lin.L{l}.{name}.M{M}", name)
                 calls.append(c)
                 if name == "gateup":
-                    gu.append(c)
+                    gu[M].append(c)
         per_m[M] = calls
     res = {}
     for M in Ms:
         ms, _ = time_graph(torch, per_m[M], args.steps, args.warmup)
         nb = sum(c.nbytes for c in per_m[M])
+        avg = time_per_launch(torch, gu[M], max(10, args.roofline_reps))
+        gb = gu[M][0].nbytes
         res[f"M{M}"] = {"us_per_layer": _r(ms * 1e3 / L, 2), "GBps": _r(nb / (ms * 1e-3) / 1e9, 1),
-                        "frac_hbm_peak": _r(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    avg = time_per_launch(torch, gu, max(10, args.roofline_reps))
-    gb = gu[0].nbytes
-    return {"workload": "gemma-3-1b-shaped decode on FP4-packed W_eff, 26 layers, M in {1, 4, 16}",
-            "results": res,
-            "dominant": {"kernel": "k_fp4_gemv (stacked gate/up, 13824 x 1152)", "bytes_per_launch_M1": gb,
-                         "avg_launch_us": _r(avg * 1e3, 3),
-                         "GBps_M1_bytes": _r(gb / (avg * 1e-3) / 1e9, 1),
-                         "frac_hbm_peak": _r(gb / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": read_traffic("fp4_gemv_gateup"),
-                         "note": "average over the M = 1, 4 and 16 launches; bytes are the M = 1 launch's "
-                                 "(codes, scales, x, y)"}}
+                        "frac_hbm_peak": _r(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "gateup_avg_launch_us": _r(avg * 1e3, 3),
+                        "gateup_GBps": _r(gb / (avg * 1e-3) / 1e9, 1),
+                        "gateup_frac_hbm_peak": _r(gb / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    N, K = packed[0][2][1], packed[0][2][2]
+    return {"workload": label, "results": res,
+            "gateup": f"k_fp4_gemv, stacked gate/up {N} x {K}: {N * K // 2 + N * K // 16} bytes of codes and "
+                      f"scales per launch"}
+
+
+def run_fp4_decode(args, torch, B, I, nested=False):
+    """Decode on FP4-packed W_eff: the Gemma-3-1B-shaped decoder (stacked QKV
+    1536 x 1152, o 1152 x 1024, stacked gate/up 13824 x 1152, down 1152 x 6912;
+    26 layers, rank-64 bundles in 13 W0 bands, M in {1, 4, 16}) and the
+    large-decoder-shaped one (8 layers, rank 32, 4 bands, M in {1, 16}; its
+    stacked gate/up streams 130 MB of codes and scales per launch)."""
+    gem = _fp4_decode_model(args, torch, B, I, "materialize_fp4", I.GEMMA_1B, 26, 13, 64, (1, 4, 16),
+                            "gemma-3-1b-shaped decode on FP4-packed W_eff, 26 layers, M in {1, 4, 16}")
+    torch.cuda.empty_cache()
+    large = _fp4_decode_model(args, torch, B, I, "large_decoder", I.LARGE_DECODER, 8, 4, 32, (1, 16),
+                              "large-decoder-shaped decode on FP4-packed W_eff, 8 layers, M in {1, 16}")
+    g1 = gem["results"]["M1"]
+    return {"workload": "decode on FP4-packed W_eff", "gemma": gem, "large_decoder": large,
+            "dominant": {"kernel": "k_fp4_gemv (Gemma-3-1B stacked gate/up, 13824 x 1152, M = 1)",
+                         "avg_launch_us": g1["gateup_avg_launch_us"], "GBps": g1["gateup_GBps"],
+                         "frac_hbm_peak": g1["gateup_frac_hbm_peak"],
+                         "traffic": read_traffic("fp4_gemv_gateup")}}
 
 
 def run_fold(args, torch, B, I, nested=False):

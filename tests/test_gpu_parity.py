@@ -726,6 +726,35 @@ def test_fp4_linear_after_gpu_pack_and_strided_io():
     _assert_fp4_parity(got[:, 8:8 + N], x, p, s, g, "strided")
 
 
+@pytest.mark.parametrize("fam,M", [("gateup", 1), ("gateup", 16), ("down", 4)])
+def test_fp4_linear_large_decoder_sampled(fam, M):
+    """The large-decoder-shaped weights (stacked gate/up 43008 x 5376; down
+    5376 x 21504, K split) on 384 sampled output rows: the GPU pack of the
+    whole seeded weight and the GEMV, against the oracle's pack of those rows
+    (the weight's largest magnitude is planted in row 0, which every sample
+    holds, so the rows' global scale is the whole weight's) and its GEMV."""
+    N, K = (43008, 5376) if fam == "gateup" else (5376, 21504)
+    rng = np.random.default_rng(4242 + M)
+    W = (rng.standard_normal((N, K), dtype=np.float32) * np.float32(K ** -0.5)).astype(np.float32)
+    W[0, 7] = 1.0                                        # larger than every other |w| (bf16-exact)
+    rows = np.concatenate([[0], np.sort(rng.choice(np.arange(1, N), 383, replace=False))])
+    d = dev()
+    Wb = torch.from_numpy(W).to(torch.bfloat16)        # rounded once, on the host
+    del W
+    Wr = Wb[torch.from_numpy(rows)].double().numpy()
+    Wd = Wb.to(d)
+    del Wb
+    pd, sd, gd = B.quant_fp4_block16(Wd)
+    del Wd
+    p, s, g = oracle.fp4_pack(Wr)
+    rt = torch.from_numpy(rows).to(d)
+    assert float(gd.cpu()[0]) == g
+    assert np.array_equal(sd[rt].cpu().numpy(), s) and np.array_equal(pd[rt].cpu().numpy(), p)
+    x = I.activations("test", 4300 + M, M, K, "bf16")
+    y = down(B.fp4_linear(up(x, "bf16"), pd, sd, gd))
+    _assert_fp4_parity(y[:, rows], x, p, s, g, f"{fam} M={M} sampled")
+
+
 def test_fp4_linear_gemma_stacked_gateup_and_limits():
     """The stacked Gemma-3-1B gate/up weight (13824 x 1152) at M = 16 on
     sampled output columns; M = 0 is a no-op and M = 17 is refused."""
