@@ -34,7 +34,7 @@
 //   dropped (zeroed) instead of divided by zero;
 // * k_chol_inv: Cholesky and the triangular inverse in one workgroup;
 // * k_jacobi: the symmetric eigendecomposition of B B^T (l x l) by cyclic
-//   Jacobi in one workgroup, rotations of disjoint pairs in parallel
+//   Jacobi in one workgroup of 1024 threads, rotations of disjoint pairs in parallel
 //   (round-robin ordering), sorted descending; S = sqrt of the eigenvalues.
 
 #include <math.h>
@@ -361,7 +361,8 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double *G, int l, double
 // sqrt(max(lambda, 0)) gives Wu[a][c] = V[a][c] sigma_c and Wv[a][c] = V[a][c] /
 // sigma_c (0 where sigma_c <= 1e-15 sigma_0).  One workgroup; G in LDS for
 // l <= 128, else in `gscr`; V in `vscr` (both l x l doubles).
-__global__ __launch_bounds__(512) void k_jacobi(const double *Gin, int l, int r, double *gscr, double *vscr,
+constexpr int kJacobiBatch = 8;
+__global__ __launch_bounds__(1024) void k_jacobi(const double *Gin, int l, int r, double *gscr, double *vscr,
                                                 double *lam_out, double *Wu, double *Wv) {
   __shared__ double Gs[128 * 128];
   __shared__ double cs[128], sn[128];
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(512) void k_jacobi(const double *Gin, int l, int r,
   __shared__ int rank_of[256];
   double *G = l <= 128 ? Gs : gscr;
   double *V = vscr;
-  const int tid = threadIdx.x, NT = 512;
+  const int tid = threadIdx.x, NT = 1024;
   for (int idx = tid; idx < l * l; idx += NT) {
     G[idx] = Gin[idx];
     V[idx] = (idx / l == idx % l) ? 1.0 : 0.0;
@@ -404,28 +405,54 @@ __global__ __launch_bounds__(512) void k_jacobi(const double *Gin, int l, int r,
         qq[tid] = q < l ? q : -1;
       }
       __syncthreads();
-      // rows p and q of every pair: G <- J^T G
-      for (int idx = tid; idx < np * l; idx += NT) {
-        const int m = idx / l, col = idx - m * l, q = qq[m];
-        if (q < 0) continue;
-        const int p = pp[m];
-        const double c = cs[m], s = sn[m], gp = G[p * l + col], gq = G[q * l + col];
-        G[p * l + col] = c * gp - s * gq;
-        G[q * l + col] = s * gp + c * gq;
+      // rows p and q of every pair: G <- J^T G.  Eight updates per thread at a
+      // time, all their loads before any store (the updates touch disjoint
+      // elements), so that G in global memory costs one round trip per eight.
+      for (int base = tid; base < np * l; base += NT * kJacobiBatch) {
+        double gp[kJacobiBatch], gq[kJacobiBatch];
+#pragma unroll
+        for (int u = 0; u < kJacobiBatch; ++u) {
+          const int idx = base + u * NT;
+          const int m = idx / l, col = idx - m * l;
+          const bool ok = idx < np * l && qq[m < np ? m : 0] >= 0;
+          gp[u] = ok ? G[pp[m] * l + col] : 0.0;
+          gq[u] = ok ? G[qq[m] * l + col] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kJacobiBatch; ++u) {
+          const int idx = base + u * NT;
+          const int m = idx / l, col = idx - m * l;
+          if (idx >= np * l || qq[m] < 0) continue;
+          const double c = cs[m], s = sn[m];
+          G[pp[m] * l + col] = c * gp[u] - s * gq[u];
+          G[qq[m] * l + col] = s * gp[u] + c * gq[u];
+        }
       }
       __syncthreads();
-      // columns p and q: G <- G J, V <- V J
-      for (int idx = tid; idx < np * l; idx += NT) {
-        const int m = idx / l, row = idx - m * l, q = qq[m];
-        if (q < 0) continue;
-        const int p = pp[m];
-        const double c = cs[m], s = sn[m];
-        const double gp = G[row * l + p], gq = G[row * l + q];
-        G[row * l + p] = c * gp - s * gq;
-        G[row * l + q] = s * gp + c * gq;
-        const double vp = V[row * l + p], vq = V[row * l + q];
-        V[row * l + p] = c * vp - s * vq;
-        V[row * l + q] = s * vp + c * vq;
+      // columns p and q: G <- G J, V <- V J (batched the same way)
+      for (int base = tid; base < np * l; base += NT * kJacobiBatch) {
+        double gp[kJacobiBatch], gq[kJacobiBatch], vp[kJacobiBatch], vq[kJacobiBatch];
+#pragma unroll
+        for (int u = 0; u < kJacobiBatch; ++u) {
+          const int idx = base + u * NT;
+          const int m = idx / l, row = idx - m * l;
+          const bool ok = idx < np * l && qq[m < np ? m : 0] >= 0;
+          gp[u] = ok ? G[row * l + pp[m]] : 0.0;
+          gq[u] = ok ? G[row * l + qq[m]] : 0.0;
+          vp[u] = ok ? V[row * l + pp[m]] : 0.0;
+          vq[u] = ok ? V[row * l + qq[m]] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kJacobiBatch; ++u) {
+          const int idx = base + u * NT;
+          const int m = idx / l, row = idx - m * l;
+          if (idx >= np * l || qq[m] < 0) continue;
+          const double c = cs[m], s = sn[m];
+          G[row * l + pp[m]] = c * gp[u] - s * gq[u];
+          G[row * l + qq[m]] = s * gp[u] + c * gq[u];
+          V[row * l + pp[m]] = c * vp[u] - s * vq[u];
+          V[row * l + qq[m]] = s * vp[u] + c * vq[u];
+        }
       }
       __syncthreads();
     }
@@ -550,7 +577,7 @@ static void run_decompose_t(const DecompArgs &d, const DecompPlan &pl, char *ws,
   }
   rtmul(Y1, Z1);                     // B^T = R^T Q, i.e. B = Q^T R as [l][K]
   gram(Z1, K);                       // B B^T
-  hipLaunchKernelGGL(k_jacobi, dim3(1), dim3(512), 0, st, (const double *)G, l, r, scr, V, lam, Wu, Wv);
+  hipLaunchKernelGGL(k_jacobi, dim3(1), dim3(1024), 0, st, (const double *)G, l, r, scr, V, lam, Wu, Wv);
   // U [N][r] = Q (V_r S_r);  Vt [r][K] = (V_r S_r^-1)^T B
   hipLaunchKernelGGL((k_small_right<LJ>), dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st, (const double *)Y1, N, l,
                      (const double *)Wu, r, d.U, 1);
