@@ -25,7 +25,9 @@
 //   so the contraction is unchanged.  Each weight is rounded to bf16 once, a
 //   relative error of at most 2^-8 per weight, inside the bf16 tolerance.
 //   Up to four tokens (K % 64 == 0) take k_fp4_gemv_m4 instead, which needs no
-//   per-weight rounding (below).
+//   per-weight rounding (below); one token on a large weight takes
+//   k_fp4_gemv_dot, which converts the codes with gfx950's FP4 -> bf16
+//   instruction and multiplies on the VALU's packed bf16 dot products (below).
 // * Eight waves per workgroup (two per SIMD), so that one wave's dequantisation
 //   overlaps another's loads.  Buffer resources make rows past N, K past the
 //   range and tokens past M read as zero: the loop is branch-free with two
@@ -94,6 +96,27 @@ __device__ __forceinline__ uint32_t bload_u16(__amdgpu_buffer_rsrc_t r, int off)
 }
 __device__ __forceinline__ uint4 bload_u128(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Eight codes (one word: code 2j in the low nibble of byte j, code 2j + 1 in
+// the high one) as four exact bf16 pairs, element 2j in the low half of pair
+// j: gfx950's FP4 -> bf16 conversion with a unit scale, one instruction per
+// byte (exact E2M1 values, low nibble into the low half: checked for all 256
+// bytes in each byte position).
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t w, int j) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  switch (j) {                     // the byte select is an immediate
+    case 0: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0); break;
+    case 1: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1); break;
+    case 2: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2); break;
+    default: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3); break;
+  }
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ void e2m1_pairs(uint32_t w, uint32_t (&pr)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pr[j] = e2m1_pair(w, j);
 }
 
 // NG: 16-row groups per workgroup; PART: fp32 partials of a K split.
@@ -207,14 +230,14 @@ __global__ __launch_bounds__(512) void k_fp4_gemv(const F4Args a) {
 // D is applied once per block and token by an fp32 FMA: no per-weight
 // multiply or rounding.  Lane (t, n) receives token t's four partials of row n
 // (blocks 2 q + s / 2 of the step, q = 0..3) and adds D[n, block] times each to
-// its one accumulator.  Codes become bf16 pairs through a 256-entry LDS table
-// (one byte, two codes, per lookup); E4M3 scale bytes through another.
+// its one accumulator.  Codes become bf16 pairs by gfx950's FP4 -> bf16
+// conversion (one byte, two codes, per instruction); E4M3 scale bytes through
+// a 256-entry LDS table.
 template <int NG, bool PART>
 __global__ __launch_bounds__(512) void k_fp4_gemv_m4(const F4Args a) {
   constexpr int WAVES = 8, KS = 4, KSTEP = 128, NT = 64 * WAVES;
   constexpr int SLOT = NG * 64;
   __shared__ float red[WAVES * SLOT];
-  __shared__ uint32_t code_lut[256];     // byte -> bf16 pair (low nibble in the low half)
   __shared__ float scale_lut[256];       // E4M3 byte -> g * value (RN_f32)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -223,15 +246,7 @@ __global__ __launch_bounds__(512) void k_fp4_gemv_m4(const F4Args a) {
   const int unit = xcd_contiguous_tile(blockIdx.x, a.ntiles * a.S);
   if (unit < 0) return;
   const float g = *a.g;
-  if (tid < 256) {
-    auto half = [](uint32_t c) {          // E2M1 code -> bf16 bits (exact)
-      const uint32_t m = c & 7u;
-      const uint32_t mag = m >= 2 ? ((m + 252u) << 6) : (m == 1 ? 0x3F00u : 0u);
-      return mag | ((c & 8u) << 12);
-    };
-    code_lut[tid] = half(tid & 15u) | (half(tid >> 4) << 16);
-    scale_lut[tid] = g * e4m3_value(tid & 0x7Fu);
-  }
+  if (tid < 256) scale_lut[tid] = g * e4m3_value(tid & 0x7Fu);
   __syncthreads();
   const int tile = unit / a.S, p = unit - tile * a.S;
   const int K = a.K, row0 = tile * a.rows;
@@ -276,8 +291,7 @@ __global__ __launch_bounds__(512) void k_fp4_gemv_m4(const F4Args a) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const uint32_t ws = w[s];
-        const uint4 wb = make_uint4(code_lut[ws & 0xFFu], code_lut[(ws >> 8) & 0xFFu], code_lut[(ws >> 16) & 0xFFu],
-                                    code_lut[ws >> 24]);
+        const uint4 wb = make_uint4(e2m1_pair(ws, 0), e2m1_pair(ws, 1), e2m1_pair(ws, 2), e2m1_pair(ws, 3));
         const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xd[s]), as_bf16x8(wb),
                                                                 f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
@@ -332,6 +346,127 @@ __global__ __launch_bounds__(512) void k_fp4_gemv_m4(const F4Args a) {
 }
 
 // y = bf16(sum of the S partials, in split order).
+// Up to MT tokens (M <= 4), packed dot products instead of MFMAs: a wave takes
+// NG groups of four rows; lane (row in group, chunk c) holds 32 codes of its row
+// per step (a step covers 512 K-values of four rows), converts them into exact
+// bf16 pairs (one instruction per byte), and multiplies them with the tokens' x pairs
+// (staged once per workgroup in LDS, read by the four row lanes of a chunk
+// together) by v_dot2c_f32_bf16 into one fp32 sum per 16-value block; the
+// block step D = RN_f32(g E4M3(scale)) then scales that sum into the row's
+// accumulator by one FMA.  Products are exact; only the sums and the output
+// are rounded.  The 16 chunk lanes of a row add their sums with a butterfly.
+constexpr int kFp4DotXCap = 8192;              // K-values of x per workgroup (LDS)
+template <int MT, int NG, bool PART>
+__global__ __launch_bounds__(256) void k_fp4_gemv_dot(const F4Args a) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [MT][kchunk] (launch-time size)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, rsub = lane >> 4;
+  const int unit = xcd_contiguous_tile(blockIdx.x, a.ntiles * a.S);
+  if (unit < 0) return;
+  const int tile = unit / a.S, p = unit - tile * a.S;
+  const int K = a.K, row0 = tile * a.rows;
+  const int Rv = min(a.rows, a.N - row0);
+  const int kbeg = p * a.kchunk, kend = min(K, kbeg + a.kchunk), kn = kend - kbeg;
+  const float g = *a.g;
+
+  // x[m][kbeg, kend) into LDS (zeros for tokens past M), 16 bytes per thread
+  for (int i = tid; i < MT * (kn / 8); i += 256) {
+    const int m = i / (kn / 8), k8 = (i - m * (kn / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (m < a.M) v = ld16(a.x + (size_t)m * a.ldx + kbeg + k8);
+    *reinterpret_cast<uint4 *>(&xs[m * a.kchunk + k8]) = v;
+  }
+  __syncthreads();
+
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.packed + (size_t)row0 * (K / 2), (uint32_t)Rv * (K / 2));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + (size_t)row0 * (K / 16), (uint32_t)Rv * (K / 16));
+  float acc[NG][MT];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[gi][m] = 0.f;
+
+  auto fetch = [&](int k0, uint4 (&cd)[NG], uint32_t (&sc)[NG]) {
+    const int k = k0 + 32 * c;
+    const bool in = k < kend;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const int r = (wave * NG + gi) * 4 + rsub;
+      cd[gi] = bload_u128(rc, in ? r * (K / 2) + k / 2 : kOOB);
+      sc[gi] = bload_u16(rs, in ? r * (K / 16) + k / 16 : kOOB);
+    }
+  };
+  auto compute = [&](int k0, const uint4 (&cd)[NG], const uint32_t (&sc)[NG]) {
+    const int kl = k0 + 32 * c - kbeg;          // this lane's 32 K-values in the LDS copy of x
+    if (kl >= kn) return;
+    uint32_t xp[MT][16];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(&xs[m * a.kchunk + kl + 8 * v]);
+        xp[m][4 * v] = q.x;
+        xp[m][4 * v + 1] = q.y;
+        xp[m][4 * v + 2] = q.z;
+        xp[m][4 * v + 3] = q.w;
+      }
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const uint32_t w[4] = {cd[gi].x, cd[gi].y, cd[gi].z, cd[gi].w};
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const float D = g * e4m3_value((sc[gi] >> (8 * b)) & 0x7Fu);
+        uint32_t pr[8];
+        e2m1_pairs(w[2 * b], *reinterpret_cast<uint32_t(*)[4]>(&pr[0]));
+        e2m1_pairs(w[2 * b + 1], *reinterpret_cast<uint32_t(*)[4]>(&pr[4]));
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float ps = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr[j]),
+                                                 __builtin_bit_cast(bf16x2, xp[m][8 * b + j]), ps, false);
+          acc[gi][m] = fmaf(D, ps, acc[gi][m]);
+        }
+      }
+    }
+  };
+
+  // two steps in flight: the next step's codes load while this one is computed
+  constexpr int KSTEP = 512;
+  uint4 ca[NG], cb[NG];
+  uint32_t sa[NG], sb[NG];
+  int k0 = kbeg;
+  fetch(k0, ca, sa);
+  for (; k0 + KSTEP < kend; k0 += 2 * KSTEP) {
+    fetch(k0 + KSTEP, cb, sb);
+    compute(k0, ca, sa);
+    if (k0 + 2 * KSTEP < kend) fetch(k0 + 2 * KSTEP, ca, sa);
+    compute(k0 + KSTEP, cb, sb);
+  }
+  if (k0 < kend) compute(k0, ca, sa);
+
+  // the row's 16 chunk lanes add their sums (butterfly within 16 lanes)
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int r = (wave * NG + gi) * 4 + rsub;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float v = acc[gi][m];
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 16);
+      if (c == 0 && m < a.M && r < Rv) {
+        if constexpr (PART)
+          a.part[((size_t)p * a.M + m) * a.N + row0 + r] = v;
+        else
+          a.y[(size_t)m * a.ldy + row0 + r] = f2bf(v);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_fp4_fold(const float *part, int S, int M, int N, uint16_t *y, int ldy) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long)M * N) return;
@@ -341,8 +476,18 @@ __global__ __launch_bounds__(256) void k_fp4_fold(const float *part, int S, int 
   y[(size_t)m * ldy + n] = f2bf(s);
 }
 
-// The exact per-block kernel for M <= 4 (a plan override of 0 selects the other one).
-static bool use_m4() { return debug_knob(AQ_DBG_FP4_M4, 1) != 0; }
+// The kernel for M <= 4: 1 the exact per-block MFMA kernel, 2 the packed-dot
+// kernel, 0 the per-weight rounding kernel (plan override).  One token on a
+// weight of 2^24 codes or more takes the packed-dot kernel (large-decoder
+// shapes at M = 1: stacked gate/up 30.1 us against 45.7, down 20.0 against
+// 31.8, o 7.1 against 10.5); smaller weights and more tokens the MFMA kernel
+// (the Gemma-3-1B shapes within 0.1-0.5 us of each other; at M = 4 the
+// packed-dot kernel's per-token dot products cost more).
+static int small_m_kernel(int64_t M, int64_t N, int64_t K) {
+  const int dflt = (M == 1 && N * K >= (int64_t(1) << 24)) ? 2 : 1;
+  const int k = debug_knob(AQ_DBG_FP4_M4, dflt);
+  return k >= 0 && k <= 2 ? k : dflt;
+}
 
 void plan_fp4_linear(int64_t M, int64_t N, int64_t K, Fp4LinPlan *pl) {
   // Measured on the Gemma-3-1B decode shapes (graph replays over 26 layers):
@@ -374,6 +519,10 @@ void plan_fp4_linear(int64_t M, int64_t N, int64_t K, Fp4LinPlan *pl) {
   }
   const int so = debug_knob(AQ_DBG_FP4_S, 0);
   if (so >= 1) S = so;
+  if (M <= 4 && small_m_kernel(M, N, K) == 2) {   // x of a K range must fit the LDS copy
+    const int sx = (int)((K + kFp4DotXCap - 1) / kFp4DotXCap);
+    S = S > sx ? S : sx;
+  }
   int kchunk = (int)((K + S - 1) / S);
   kchunk = (kchunk + 127) / 128 * 128;
   S = (int)((K + kchunk - 1) / kchunk);
@@ -385,9 +534,27 @@ void plan_fp4_linear(int64_t M, int64_t N, int64_t K, Fp4LinPlan *pl) {
   pl->ws_bytes = S > 1 ? kWsReserved + (size_t)S * M * N * 4 : 0;
 }
 
+template <int MT, bool PART>
+static bool launch_dot(const F4Args &a, int NG, int grid, hipStream_t st) {
+  const size_t lds = (size_t)MT * a.kchunk * 2;   // <= 64 KiB: kchunk <= kFp4DotXCap
+  switch (NG) {
+    case 1: hipLaunchKernelGGL((k_fp4_gemv_dot<MT, 1, PART>), dim3(grid), dim3(256), lds, st, a); return true;
+    case 2: hipLaunchKernelGGL((k_fp4_gemv_dot<MT, 2, PART>), dim3(grid), dim3(256), lds, st, a); return true;
+    case 3: hipLaunchKernelGGL((k_fp4_gemv_dot<MT, 3, PART>), dim3(grid), dim3(256), lds, st, a); return true;
+    case 4: hipLaunchKernelGGL((k_fp4_gemv_dot<MT, 4, PART>), dim3(grid), dim3(256), lds, st, a); return true;
+  }
+  return false;
+}
+
 template <bool PART>
 static bool launch_ng(const F4Args &a, int NG, int grid, hipStream_t st) {
-  if (a.M <= 4 && a.K % 64 == 0 && use_m4()) {   // K % 64: the 4-byte scale loads stay aligned
+  const int smk = small_m_kernel(a.M, a.N, a.K);
+  if (a.M <= 4 && smk == 2 && a.kchunk <= kFp4DotXCap) {
+    if (a.M == 1) return launch_dot<1, PART>(a, NG, grid, st);
+    if (a.M == 2) return launch_dot<2, PART>(a, NG, grid, st);
+    return launch_dot<4, PART>(a, NG, grid, st);
+  }
+  if (a.M <= 4 && a.K % 64 == 0 && smk >= 1) {   // K % 64: the 4-byte scale loads stay aligned
     switch (NG) {
       case 1: hipLaunchKernelGGL((k_fp4_gemv_m4<1, PART>), dim3(grid), dim3(512), 0, st, a); return true;
       case 2: hipLaunchKernelGGL((k_fp4_gemv_m4<2, PART>), dim3(grid), dim3(512), 0, st, a); return true;

@@ -669,6 +669,27 @@ def test_fp4_linear(M, N, K):
     _assert_fp4_parity(down(y), x, p, s, g, f"M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("N,K,ng,S", [(300, 1152, None, None), (72, 96, None, None), (1152, 6912, None, None),
+                                      (200, 2016, 3, 1), (4100, 1024, 4, 1), (50, 64, 1, 1), (130, 32, 2, 1),
+                                      (600, 4640, 2, 3), (64, 20000, 1, None)], ids=str)
+def test_fp4_linear_dot_kernel(M, N, K, ng, S, force_plan):
+    """The packed-dot kernel for up to four tokens (forced): ragged tail steps
+    (96, 32, 4640 = 9 x 512 + 32), K split with the fold, every row-group
+    count, K beyond the LDS copy of x (20000: split in at least three)."""
+    force_plan("FP4_M4", 2)
+    if ng is not None:
+        force_plan("FP4_NG", ng)
+    if S is not None:
+        force_plan("FP4_S", S)
+    _, (p, s, g) = _fp4_weight(N, K, 900 + N + K)
+    x = I.activations("test", 910 + M + K, M, K, "bf16")
+    d = dev()
+    y = B.fp4_linear(up(x, "bf16"), torch.from_numpy(p).to(d), torch.from_numpy(s).to(d),
+                     torch.tensor([g], dtype=torch.float32, device=d))
+    _assert_fp4_parity(down(y), x, p, s, g, f"dot M={M} N={N} K={K} ng={ng} S={S}")
+
+
 @pytest.mark.parametrize("M", [2, 7])
 @pytest.mark.parametrize("ng,S", [(1, 1), (2, 1), (3, 1), (4, 1), (1, 5), (3, 2)])
 def test_fp4_linear_tilings(M, ng, S, force_plan):
