@@ -345,12 +345,14 @@ SOURCES = {"decode_gateup": "rank_shared_block_amd/csrc/recon_decode.hip",
            "prefill_gateup_large": ("rank_shared_block_amd/csrc/recon_prefill.hip",
                                     "rank_shared_block_amd/csrc/handoff.h"),
            "fp4_gemv_gateup": "rank_shared_block_amd/csrc/fp4_gemv.hip",
+           "fp4_gemv_dot_large": "rank_shared_block_amd/csrc/fp4_gemv.hip",
            "materialize_batch": "rank_shared_block_amd/csrc/materialize.hip",
            "fp4_pack_batch": "rank_shared_block_amd/csrc/fp4_pack.hip"}
 PMC_KERNELS = {"decode_gateup": (("k_decode_bf16",), "k_decode_bf16 (fused gate/up, Gemma-3-1B-shaped)"),
                "decode_gateup_large": (("k_decode_bf16",), "k_decode_bf16 (gate/up, large-decoder-shaped, M = 1)"),
                "prefill_gateup_large": (("k_gemm_bf16",), "k_gemm_bf16 (gate/up, large-decoder-shaped, M = 512)"),
                "fp4_gemv_gateup": (("k_fp4_gemv", "<2, false>"), "k_fp4_gemv / k_fp4_gemv_m4 (FP4 stacked gate/up)"),
+               "fp4_gemv_dot_large": (("k_fp4_gemv_dot",), "k_fp4_gemv_dot (FP4 large stacked gate/up, M = 1)"),
                "materialize_batch": (("k_materialize_batch",), "k_materialize_batch (182 Gemma-3-1B-shaped W_eff, "
                                                                "13 bands)"),
                "fp4_pack_batch": (("k_fp4_pack_batch",), "k_fp4_pack_batch (the same 182 W_eff)")}
@@ -442,9 +444,21 @@ def run_pmc_probe_fp4(args, torch, B, I):
     weight, x M in {1, 4, 16}), eagerly."""
     _calibration_copy(torch)
     dev = torch.device("cuda", 0)
-    N, K = 13824, 1152
     g = torch.Generator(device=dev)
     g.manual_seed(5)
+    if args.probe == "fp4_large":
+        # the large decoder's stacked gate/up (43008 x 5376 packed), 8 weights,
+        # one token: the packed-dot kernel
+        N, K = 43008, 5376
+        packs = [B.quant_fp4_block16((torch.randn(N, K, device=dev, generator=g) * K ** -0.5).to(torch.bfloat16))
+                 for _ in range(8)]
+        x = (torch.randn(1, K, device=dev, generator=g)).to(torch.bfloat16)
+        y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+        for l in range(8):
+            B.fp4_linear(x, *packs[l], y=y)
+        torch.cuda.synchronize()
+        return {"probe": "copy of %d bytes, then 8 FP4 large stacked gate/up GEMV launches at M = 1" % CALIB_BYTES}
+    N, K = 13824, 1152
     packs = [B.quant_fp4_block16((torch.randn(N, K, device=dev, generator=g) * K ** -0.5).to(torch.bfloat16))
              for _ in range(26)]
     for M in (1, 4, 16):
@@ -949,12 +963,16 @@ def run_fp4_decode(args, torch, B, I, nested=False):
     torch.cuda.empty_cache()
     large = _fp4_decode_model(args, torch, B, I, "large_decoder", I.LARGE_DECODER, 8, 4, 32, (1, 16),
                               "large-decoder-shaped decode on FP4-packed W_eff, 8 layers, M in {1, 16}")
-    g1 = gem["results"]["M1"]
+    g1, l1 = gem["results"]["M1"], large["results"]["M1"]
     return {"workload": "decode on FP4-packed W_eff", "gemma": gem, "large_decoder": large,
-            "dominant": {"kernel": "k_fp4_gemv (Gemma-3-1B stacked gate/up, 13824 x 1152, M = 1)",
+            "dominant": {"kernel": "k_fp4_gemv_m4 (Gemma-3-1B stacked gate/up, 13824 x 1152, M = 1)",
                          "avg_launch_us": g1["gateup_avg_launch_us"], "GBps": g1["gateup_GBps"],
                          "frac_hbm_peak": g1["gateup_frac_hbm_peak"],
-                         "traffic": read_traffic("fp4_gemv_gateup")}}
+                         "traffic": read_traffic("fp4_gemv_gateup")},
+            "dominant_large": {"kernel": "k_fp4_gemv_dot (large-decoder stacked gate/up, 43008 x 5376, M = 1)",
+                               "avg_launch_us": l1["gateup_avg_launch_us"], "GBps": l1["gateup_GBps"],
+                               "frac_hbm_peak": l1["gateup_frac_hbm_peak"],
+                               "traffic": read_traffic("fp4_gemv_dot_large")}}
 
 
 def run_fold(args, torch, B, I, nested=False):
@@ -1121,7 +1139,8 @@ def main():
                     choices=["headline", "gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4",
                              "fp4_decode", "fold", "rebuild", "decompose", "pmc_probe", "pmc_probe_fp4"])
     ap.add_argument("--probe", default="decode_gateup",
-                    choices=["decode_gateup", "decode_gateup_large", "prefill_gateup_large", "load_batch"],
+                    choices=["decode_gateup", "decode_gateup_large", "prefill_gateup_large", "load_batch",
+                             "fp4_large"],
                     help="with --workload pmc_probe: which dispatches the counter run covers")
     ap.add_argument("--summarize", action="store_true",
                     help="summarise rocprofv3 CSVs (--trace, --fetch/--write, --pmc) instead of running")
