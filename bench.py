@@ -1109,9 +1109,11 @@ def run_decompose(args, torch, B, I, nested=False):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         total_ms += ms
-        # contractions with R: R Omega^T, then per subspace step R^T Q and R Q',
-        # then B = Q^T R; each 2 N K l flops (the l x l work is second order)
-        flop = (2 * q + 2) * 2.0 * N * K * l
+        # contractions with R, each 2 N K l flops (the l x l work is second
+        # order): R Omega^T, then per subspace step R^T Q and R Q', then
+        # B = Q^T R; where l = N, B = R (one pass); where l = K, no steps
+        passes = 1 if l == N else (2 if l == K else 2 * q + 2)
+        flop = passes * 2.0 * N * K * l
         res[fam] = {"N": N, "K": K, "l": l, "ms": _r(ms, 3), "fp64_GFLOP": _r(flop / 1e9, 2),
                     "fp64_TFLOPs": _r(flop / (ms * 1e-3) / 1e12, 2)}
         keep += [W, W0, om]

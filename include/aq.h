@@ -282,7 +282,11 @@ aq_status aq_fp4_linear(int64_t M, int64_t N, int64_t K, const void *x, int64_t 
  * ws: aq_decompose_workspace_bytes(N, K, r, l) bytes, 256-byte aligned (the
  * basis, the co-range, partial sums; no zero-fill needed); its first 64 KiB
  * (the recon calls' counter words) are not touched, so the same workspace
- * serves both kinds of call.  Asynchronous on
+ * serves both kinds of call -- except the flag word that aq_workspace_check
+ * reads: for l > 96 the eigensolver runs on many workgroups with bounded
+ * grid barriers, and one that gives up sets that flag and makes U and Vt NaN
+ * (never seen in practice; the call's stream must not run another call on the
+ * same workspace at the same time).  Asynchronous on
  * stream; many launches, all on that stream.  Singular vectors are unique only
  * up to sign (and within repeated singular values): U Vt is the result. */
 aq_status aq_band_mean(aq_dtype dt, int L, const void *const *W, int64_t N, int64_t K, void *W0,
@@ -333,9 +337,13 @@ const char *aq_last_error(void);
  * arguments.  The overrides are thread-local, unset until set, and apply to
  * the calls made on the same thread; values that no compiled variant takes
  * are ignored by the planner, as if unset.  AQ_DBG_HANDOFF_SPIN bounds the
- * prefill wait for t to that many polls and AQ_DBG_HANDOFF_UNREACHABLE = 1
+ * prefill wait for t, and each grid barrier of the decomposition's many-
+ * workgroup eigensolver, to that many polls; AQ_DBG_HANDOFF_UNREACHABLE = 1
  * makes the awaited count one more than will arrive, so that a test can make
  * the wait give up from the host while every kernel still exits normally.
+ * AQ_DBG_JACOBI picks the eigensolver (1: one workgroup with both matrices in
+ * LDS, taken only where l <= 96; 2: the many-workgroup one) and
+ * AQ_DBG_JACOBI_WGS the latter's workgroups (1 to 64).
  * aq_debug_force_plan returns AQ_ERR_INVALID_ARG for an unknown knob. */
 typedef enum aq_debug_knob {
   AQ_DBG_DECODE_SPLIT = 0, AQ_DBG_DECODE_NG, AQ_DBG_DECODE_ROWS, AQ_DBG_DECODE_S, AQ_DBG_DECODE_WAVES,
@@ -343,6 +351,7 @@ typedef enum aq_debug_knob {
   AQ_DBG_PREFILL_S, AQ_DBG_PREFILL_SELF, AQ_DBG_PREFILL_FUSE, AQ_DBG_TPASS_S, AQ_DBG_TPASS_PARTS,
   AQ_DBG_FP4_NG, AQ_DBG_FP4_S, AQ_DBG_FP4_M4, AQ_DBG_HANDOFF_SPIN, AQ_DBG_HANDOFF_UNREACHABLE,
   AQ_DBG_REBUILD_NG, AQ_DBG_REBUILD_ROWS, AQ_DBG_REBUILD_S, AQ_DBG_MAT_STEPS, AQ_DBG_FP4_UNIT,
+  AQ_DBG_JACOBI, AQ_DBG_JACOBI_WGS,
   AQ_DBG_COUNT
 } aq_debug_knob;
 aq_status aq_debug_force_plan(aq_debug_knob knob, int64_t value);

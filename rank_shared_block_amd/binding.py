@@ -31,7 +31,7 @@ DEBUG_KNOBS = ("DECODE_SPLIT", "DECODE_NG", "DECODE_ROWS", "DECODE_S", "DECODE_W
                "PREFILL_BM", "PREFILL_BN", "PREFILL_BK", "PREFILL_NST", "PREFILL_W",
                "PREFILL_S", "PREFILL_SELF", "PREFILL_FUSE", "TPASS_S", "TPASS_PARTS",
                "FP4_NG", "FP4_S", "FP4_M4", "HANDOFF_SPIN", "HANDOFF_UNREACHABLE", "REBUILD_NG",
-               "REBUILD_ROWS", "REBUILD_S", "MAT_STEPS", "FP4_UNIT")
+               "REBUILD_ROWS", "REBUILD_S", "MAT_STEPS", "FP4_UNIT", "JACOBI", "JACOBI_WGS")
 
 
 class aq_proj(ctypes.Structure):

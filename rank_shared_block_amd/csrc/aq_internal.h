@@ -126,10 +126,13 @@ struct DecompArgs {
   double *s, *U, *Vt;
 };
 struct DecompPlan {
-  int lj;                      // compiled width of the l side (32, 64, 128, 256)
+  int lj;                      // compiled width of the l side (32, 64, 80, 128, 256)
+  int srm, kchunk;             // K ranges of R X; columns per range
   int srt, sgram;              // N ranges of R^T Q; ranges of the Gram sums
   long nchunk;                 // rows per N range
-  size_t o_y1, o_y2, o_z1, o_z2, o_zp, o_gp, o_g, o_rinv, o_scr, o_v, o_lam, o_wu, o_wv;   // byte offsets
+  int jac_wgs;                 // workgroups of the grid Jacobi (0: the one-workgroup LDS kernel)
+  int jac_spin, jac_extra;     // its barrier's poll bound; arrivals awaited beyond the grid's
+  size_t o_y1, o_y2, o_z1, o_z2, o_zp, o_yp, o_gp, o_g, o_rinv, o_scr, o_jac, o_ctr, o_lam, o_wu, o_wv;   // byte offsets
 };
 size_t decompose_ws_bytes(int64_t N, int64_t K, int64_t r, int64_t l, DecompPlan *pl);
 hipError_t launch_decompose(const DecompArgs &d, const DecompPlan &pl, void *ws, hipStream_t st);

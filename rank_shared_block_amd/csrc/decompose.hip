@@ -32,10 +32,16 @@
 //   M <- M L^{-T}; twice, so that the basis is orthonormal to working
 //   precision.  A column whose remaining norm vanishes (rank deficiency) is
 //   dropped (zeroed) instead of divided by zero;
-// * k_chol_inv: Cholesky and the triangular inverse in one workgroup;
-// * k_jacobi: the symmetric eigendecomposition of B B^T (l x l) by cyclic
-//   Jacobi in one workgroup of 1024 threads, rotations of disjoint pairs in parallel
+// * k_chol_inv: Cholesky and the triangular inverse in one workgroup, both
+//   triangles packed in LDS (k_chol_inv_global above l = 128);
+// * k_jacobi_lds / k_jacobi_grid: the symmetric eigendecomposition of B B^T
+//   (l x l) by cyclic Jacobi, rotations of disjoint pairs in parallel
 //   (round-robin ordering), sorted descending; S = sqrt of the eigenvalues.
+//   One workgroup with G and V in LDS up to l = 96; above, many workgroups
+//   over global memory with one grid barrier per round.
+// Where l = N (the full SVD of a matrix with at most as many rows as
+// columns), Q = I and B = R; where l = K the subspace steps are skipped (the
+// first basis already spans R's range).
 
 #include <math.h>
 
@@ -247,14 +253,17 @@ struct FillColsA {            // As[t][i] = Mt[i0 + i][t0 + t] (row-major [i][t]
   }
 };
 
-// Y^T[j][n] = sum_k R[n][k] X^T[j][k]   (R X, X given as X^T [l][K])
+// partial p of Y^T[j][n] = sum_{k in range p} R[n][k] X^T[j][k]   (R X, X
+// given as X^T [l][K]; one range: Y^T itself)
 template <int LJ, typename T>
 __global__ __launch_bounds__(256) void k_rmul(const T *W, const T *W0, const double *s, long N, int K,
-                                              const double *Xt, int l, double *Yt) {
-  const int i0 = blockIdx.x * 64;
-  contract<LJ>(i0, 0, K, FillR_tk<T>{W, W0, s, N, K}, FillColsB<LJ>{Xt, K, l},
+                                              const double *Xt, int l, int kchunk, double *Yp) {
+  const int i0 = blockIdx.x * 64, p = blockIdx.y;
+  const int kb = p * kchunk, ke = kb + kchunk < K ? kb + kchunk : K;
+  double *Y = Yp + (size_t)p * l * N;
+  contract<LJ>(i0, kb, ke, FillR_tk<T>{W, W0, s, N, K}, FillColsB<LJ>{Xt, K, l},
                [&](int i, int j, double v) {
-                 if (i < N && j < l) Yt[(size_t)j * N + i] = v;
+                 if (i < N && j < l) Y[(size_t)j * N + i] = v;
                });
 }
 
@@ -311,14 +320,105 @@ __global__ __launch_bounds__(256) void k_fold_parts(const double *part, int S, l
 
 // ---------------------------------------------------------------- small factorizations
 
+// LDS of the one-workgroup Jacobi (doubles): G and V, n x n each, up to n = 96.
+constexpr int kSmallLds = 18432;
+__device__ __host__ __forceinline__ bool two_fit(int n) { return 2 * n * n <= kSmallLds; }
+// Packed lower triangles in LDS (row i, column k <= i at i (i + 1) / 2 + k).
+constexpr int kTriLmax = 128, kTriMax = kTriLmax * (kTriLmax + 1) / 2;
+__device__ __forceinline__ int tri(int i) { return i * (i + 1) / 2; }
+constexpr int kCholThreads = 1024, kCholTpr = kCholThreads / kTriLmax;   // threads per row
+constexpr int kCholBatch = 4;   // updates of one thread with all their loads before any store
+
 // G = L L^T (Cholesky, lower L), then Rinv = L^{-T} (upper): Q = M Rinv.  A
 // pivot at or below 1e-24 of its column's original square norm (a column that
 // adds no direction, or a zero column) gives a zero column of L and of Rinv.
-// One workgroup; L in LDS for l <= 128, else in `scratch` (l x l doubles).
-__global__ __launch_bounds__(256) void k_chol_inv(const double *G, int l, double *Rinv, double *scratch) {
-  __shared__ double Ls[128 * 128];
+//
+// One workgroup, l <= 128: both triangles packed in LDS, right-looking.  Once
+// column j of L is final, every entry below and to its right takes its update
+// from it at once (kCholTpr threads per row, alternate columns).  Entry (i, k)
+// still receives its updates in the order j = 0, 1, ..., k - 1, one fma each,
+// as in the column-by-column form; the inverse likewise (row k of L^{-1} is
+// final once its update from row k - 1 is in, then rows below take theirs).
+// A thread's updates of one step touch other entries than the ones they read
+// (column j, row k), so kCholBatch of them load before any stores.
+__global__ __launch_bounds__(kCholThreads) void k_chol_inv(const double *G, int l, double *Rinv) {
+  __shared__ double A[kTriMax];     // G's lower triangle, then L (diagonal in Ld)
+  __shared__ double X[kTriMax];     // the identity, then L^{-1} (lower)
+  __shared__ double g0[kTriLmax], Ld[kTriLmax];
+  const int tid = threadIdx.x, row = tid / kCholTpr, h = tid % kCholTpr;
+  const bool mine = row < l;
+  const int trow = tri(row);
+  if (mine) {
+    for (int k = h; k <= row; k += kCholTpr) {
+      A[trow + k] = G[(size_t)row * l + k];
+      X[trow + k] = row == k ? 1.0 : 0.0;
+    }
+    if (h == 0) g0[row] = G[(size_t)row * l + row];
+  }
+  __syncthreads();
+  for (int j = 0; j < l; ++j) {
+    const double dj = A[tri(j) + j];
+    const bool ok = dj > 1e-24 * g0[j] && dj > 0.0;
+    const double rj = ok ? sqrt(dj) : 0.0;
+    if (mine && h == 0 && row >= j) {
+      if (row == j) Ld[j] = rj;
+      else A[trow + j] = ok ? A[trow + j] / rj : 0.0;
+    }
+    __syncthreads();
+    if (mine && row > j) {
+      const double lij = A[trow + j];
+      for (int k0 = j + 1 + h; k0 <= row; k0 += kCholBatch * kCholTpr) {
+        double lk[kCholBatch], ak[kCholBatch];
+#pragma unroll
+        for (int u = 0; u < kCholBatch; ++u) {
+          const int k = k0 + u * kCholTpr;
+          lk[u] = k <= row ? A[tri(k) + j] : 0.0;
+          ak[u] = k <= row ? A[trow + k] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kCholBatch; ++u) {
+          const int k = k0 + u * kCholTpr;
+          if (k <= row) A[trow + k] = fma(-lij, lk[u], ak[u]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int k = 0; k < l; ++k) {
+    const double lkk = Ld[k];
+    const int tk = tri(k);
+    for (int c = tid; c <= k; c += kCholThreads) X[tk + c] = lkk != 0.0 ? X[tk + c] / lkk : 0.0;
+    __syncthreads();
+    if (mine && row > k) {
+      const double lik = A[trow + k];
+      for (int c0 = h; c0 <= k; c0 += kCholBatch * kCholTpr) {
+        double xk[kCholBatch], xr[kCholBatch];
+#pragma unroll
+        for (int u = 0; u < kCholBatch; ++u) {
+          const int c = c0 + u * kCholTpr;
+          xk[u] = c <= k ? X[tk + c] : 0.0;
+          xr[u] = c <= k ? X[trow + c] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kCholBatch; ++u) {
+          const int c = c0 + u * kCholTpr;
+          if (c <= k) X[trow + c] = fma(-lik, xk[u], xr[u]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < l * l; idx += kCholThreads) {
+    const int c = idx / l, i = idx - c * l;
+    Rinv[idx] = i >= c ? X[tri(i) + c] : 0.0;
+  }
+}
+
+// The same for l > 128, with L in `scratch` and the inverse built in Rinv
+// (global memory, l x l doubles each): column-by-column Cholesky, then forward
+// substitution, one column of the inverse per thread.
+__global__ __launch_bounds__(256) void k_chol_inv_global(const double *G, int l, double *Rinv, double *L) {
   __shared__ double tmp[256];
-  double *L = l <= 128 ? Ls : scratch;
   const int tid = threadIdx.x;
   for (int idx = tid; idx < l * l; idx += 256) L[idx] = 0.0;
   __syncthreads();
@@ -335,8 +435,7 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double *G, int l, double
     if (tid >= j && tid < l) L[tid * l + j] = ok ? (tid == j ? rj : tmp[tid] / rj) : 0.0;
     __syncthreads();
   }
-  // X = L^{-1} by forward substitution, one column c per thread; written as
-  // Rinv[c][i] = X[i][c] (so Rinv = X^T) and read back by the same thread.
+  // Rinv[c][i] = L^{-1}[i][c], read back by the thread that wrote it
   if (tid < l) {
     const int c = tid;
     for (int i = 0; i < l; ++i) {
@@ -352,33 +451,108 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double *G, int l, double
   }
 }
 
-// Symmetric eigendecomposition of G (l x l) by cyclic Jacobi: per round, the
-// disjoint pairs of a round-robin schedule are rotated in parallel (rotation
-// angles from the round's G, then all row rotations, then all column
-// rotations and the eigenvector updates); sweeps until no pair has an
+// Symmetric eigendecomposition of G (l x l) by cyclic Jacobi.  A sweep is
+// n - 1 rounds (n = l rounded up to even, with a zero row and column for a
+// dummy index when l is odd); in a round the indices form n / 2 disjoint pairs
+// (the round-robin schedule: one index fixed, the others moving one place per
+// round, so that every pair meets once per sweep), each pair's rotation is
+// taken from the round's G, and G <- J^T G J, V <- V J for all of them at
+// once -- each 2 x 2 block of G (rows of pair i, columns of pair j) is rotated
+// on both sides by one thread.  Sweeps repeat until no pair had an
 // off-diagonal entry above 1e-15 of sqrt(|G_pp G_qq|), at most 40.  Then the
-// eigenvalues are sorted descending and, for the r leading ones, sigma =
-// sqrt(max(lambda, 0)) gives Wu[a][c] = V[a][c] sigma_c and Wv[a][c] = V[a][c] /
-// sigma_c (0 where sigma_c <= 1e-15 sigma_0).  One workgroup; G in LDS for
-// l <= 128, else in `gscr`; V in `vscr` (both l x l doubles).
-constexpr int kJacobiBatch = 8;
-__global__ __launch_bounds__(1024) void k_jacobi(const double *Gin, int l, int r, double *gscr, double *vscr,
-                                                double *lam_out, double *Wu, double *Wv) {
-  __shared__ double Gs[128 * 128];
-  __shared__ double cs[128], sn[128];
-  __shared__ int pp[128], qq[128];
-  __shared__ int changed;
-  __shared__ double lam[256];
-  __shared__ int rank_of[256];
-  double *G = l <= 128 ? Gs : gscr;
-  double *V = vscr;
-  const int tid = threadIdx.x, NT = 1024;
-  for (int idx = tid; idx < l * l; idx += NT) {
-    G[idx] = Gin[idx];
-    V[idx] = (idx / l == idx % l) ? 1.0 : 0.0;
+// eigenvalues are sorted descending (ties by position) and, for the r leading
+// ones, sigma = sqrt(max(lambda, 0)) gives Wu[a][c] = V[a][c] sigma_c and
+// Wv[a][c] = V[a][c] / sigma_c (0 where sigma_c <= 1e-15 sigma_0).
+
+// The rotation that zeroes G_pq: tau = (G_qq - G_pp) / (2 G_pq),
+// t = sign(tau) / (|tau| + sqrt(1 + tau^2)), c = 1 / sqrt(1 + t^2), s = t c;
+// the identity where G_pq = 0.  `big`: G_pq is above the convergence bound.
+__device__ __forceinline__ void jacobi_angle(double gpp, double gqq, double gpq, double &c, double &s, bool &big) {
+  c = 1.0;
+  s = 0.0;
+  big = false;
+  if (gpq != 0.0) {
+    big = fabs(gpq) > 1e-15 * sqrt(fabs(gpp * gqq));
+    const double tau = (gqq - gpp) / (2.0 * gpq);
+    const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+    c = 1.0 / sqrt(1.0 + t * t);
+    s = t * c;
   }
-  const int n = l + (l & 1);   // even, with a dummy index l when l is odd
-  const int np = n / 2;
+}
+
+// One 2 x 2 block of J^T G J: rows (p_i, q_i) by (ci, si) -- new row p =
+// c row p - s row q, new row q = s row p + c row q -- then columns (p_j, q_j)
+// by (cj, sj) the same way.
+__device__ __forceinline__ void rot_block(double &a00, double &a01, double &a10, double &a11, double ci, double si,
+                                          double cj, double sj) {
+  const double r00 = ci * a00 - si * a10, r01 = ci * a01 - si * a11;
+  const double r10 = si * a00 + ci * a10, r11 = si * a01 + ci * a11;
+  a00 = cj * r00 - sj * r01;
+  a01 = sj * r00 + cj * r01;
+  a10 = cj * r10 - sj * r11;
+  a11 = sj * r10 + cj * r11;
+}
+
+// Eigenvalues lam[0..n) (the dummy at -inf), eigenvectors V(a, i) = vec(a, i):
+// the sorted outputs.  One workgroup of NT threads; rank_of has room for n.
+template <int NT, class VecAt>
+__device__ __forceinline__ void jacobi_outputs(int l, int n, int r, double *lam, int *rank_of, VecAt vec,
+                                               double *lam_out, double *Wu, double *Wv) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < n; i += NT) {
+    int rk = 0;
+    for (int j = 0; j < n; ++j) rk += (lam[j] > lam[i] || (lam[j] == lam[i] && j < i)) ? 1 : 0;
+    rank_of[i] = rk;
+    if (rk < l) lam_out[rk] = lam[i];
+  }
+  __syncthreads();
+  double lmax = 0.0;
+  for (int j = 0; j < n; ++j) lmax = lam[j] > lmax ? lam[j] : lmax;
+  const double smax = sqrt(lmax);
+  for (int idx = tid; idx < l * n; idx += NT) {
+    const int a = idx / n, i = idx - a * n, c = rank_of[i];
+    if (c >= r) continue;
+    const double sg = sqrt(lam[i] > 0.0 ? lam[i] : 0.0);
+    const double v = vec(a, i);
+    Wu[(size_t)a * r + c] = v * sg;
+    Wv[(size_t)a * r + c] = sg > 1e-15 * smax && sg > 0.0 ? v / sg : 0.0;
+  }
+}
+
+// One workgroup of 1024 threads, G and V in LDS (n <= 96).  Each thread owns
+// up to three blocks of G and five (pair, coordinate) entries of V for the
+// whole run; pairs are looked up per round.
+constexpr int kJacLdsMaxN = 96, kJacLdsB = 3, kJacLdsV = 5;
+static_assert((kJacLdsMaxN / 2) * (kJacLdsMaxN / 2) <= kJacLdsB * 1024, "G blocks per thread");
+static_assert((kJacLdsMaxN / 2) * kJacLdsMaxN <= kJacLdsV * 1024, "V entries per thread");
+__global__ __launch_bounds__(1024) void k_jacobi_lds(const double *Gin, int l, int r, double *lam_out, double *Wu,
+                                                    double *Wv) {
+  __shared__ double S[kSmallLds];
+  __shared__ double cs[kJacLdsMaxN / 2], sn[kJacLdsMaxN / 2];
+  __shared__ int pp[kJacLdsMaxN / 2], qq[kJacLdsMaxN / 2];
+  __shared__ int changed;
+  __shared__ double lam[kJacLdsMaxN];
+  __shared__ int rank_of[kJacLdsMaxN];
+  const int n = l + (l & 1), np = n / 2, tid = threadIdx.x;
+  double *G = S, *V = S + n * n;   // G[a][b]; V[a][i] = coordinate a of eigenvector i
+  for (int idx = tid; idx < n * n; idx += 1024) {
+    const int a = idx / n, b = idx - a * n;
+    G[idx] = a < l && b < l ? Gin[(size_t)a * l + b] : 0.0;
+    V[idx] = a == b ? 1.0 : 0.0;
+  }
+  int bi[kJacLdsB], bj[kJacLdsB], vi[kJacLdsV], va[kJacLdsV];
+#pragma unroll
+  for (int u = 0; u < kJacLdsB; ++u) {
+    const int b = tid + u * 1024;
+    bi[u] = b < np * np ? b / np : -1;
+    bj[u] = b - (b / np) * np;
+  }
+#pragma unroll
+  for (int u = 0; u < kJacLdsV; ++u) {
+    const int e = tid + u * 1024;
+    vi[u] = e < np * l ? e / l : -1;
+    va[u] = e - (e / l) * l;
+  }
   __syncthreads();
   for (int sweep = 0; sweep < 40; ++sweep) {
     if (tid == 0) changed = 0;
@@ -387,105 +561,233 @@ __global__ __launch_bounds__(1024) void k_jacobi(const double *Gin, int l, int r
       if (tid < np) {
         auto player = [&](int x) { return x == 0 ? 0 : ((x - 1 + round) % (n - 1)) + 1; };
         int p = player(tid), q = player(n - 1 - tid);
-        if (p > q) { const int t = p; p = q; q = t; }
-        double c = 1.0, s = 0.0;
-        if (q < l) {
-          const double gpq = G[p * l + q], gpp = G[p * l + p], gqq = G[q * l + q];
-          if (gpq != 0.0) {
-            if (fabs(gpq) > 1e-15 * sqrt(fabs(gpp * gqq))) changed = 1;
-            const double tau = (gqq - gpp) / (2.0 * gpq);
-            const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
-            c = 1.0 / sqrt(1.0 + t * t);
-            s = t * c;
-          }
+        if (p > q) {
+          const int t = p;
+          p = q;
+          q = t;
         }
+        double c, s;
+        bool big;
+        jacobi_angle(G[p * n + p], G[q * n + q], G[p * n + q], c, s, big);
+        if (big) changed = 1;
         cs[tid] = c;
         sn[tid] = s;
         pp[tid] = p;
-        qq[tid] = q < l ? q : -1;
+        qq[tid] = q;
       }
       __syncthreads();
-      // rows p and q of every pair: G <- J^T G.  Eight updates per thread at a
-      // time, all their loads before any store (the updates touch disjoint
-      // elements), so that G in global memory costs one round trip per eight.
-      for (int base = tid; base < np * l; base += NT * kJacobiBatch) {
-        double gp[kJacobiBatch], gq[kJacobiBatch];
 #pragma unroll
-        for (int u = 0; u < kJacobiBatch; ++u) {
-          const int idx = base + u * NT;
-          const int m = idx / l, col = idx - m * l;
-          const bool ok = idx < np * l && qq[m < np ? m : 0] >= 0;
-          gp[u] = ok ? G[pp[m] * l + col] : 0.0;
-          gq[u] = ok ? G[qq[m] * l + col] : 0.0;
-        }
-#pragma unroll
-        for (int u = 0; u < kJacobiBatch; ++u) {
-          const int idx = base + u * NT;
-          const int m = idx / l, col = idx - m * l;
-          if (idx >= np * l || qq[m] < 0) continue;
-          const double c = cs[m], s = sn[m];
-          G[pp[m] * l + col] = c * gp[u] - s * gq[u];
-          G[qq[m] * l + col] = s * gp[u] + c * gq[u];
-        }
+      for (int u = 0; u < kJacLdsB; ++u) {
+        if (bi[u] < 0) continue;
+        const int i = bi[u], j = bj[u];
+        const int pi = pp[i], qi = qq[i], pj = pp[j], qj = qq[j];
+        double a00 = G[pi * n + pj], a01 = G[pi * n + qj], a10 = G[qi * n + pj], a11 = G[qi * n + qj];
+        rot_block(a00, a01, a10, a11, cs[i], sn[i], cs[j], sn[j]);
+        G[pi * n + pj] = a00;
+        G[pi * n + qj] = a01;
+        G[qi * n + pj] = a10;
+        G[qi * n + qj] = a11;
       }
-      __syncthreads();
-      // columns p and q: G <- G J, V <- V J (batched the same way)
-      for (int base = tid; base < np * l; base += NT * kJacobiBatch) {
-        double gp[kJacobiBatch], gq[kJacobiBatch], vp[kJacobiBatch], vq[kJacobiBatch];
 #pragma unroll
-        for (int u = 0; u < kJacobiBatch; ++u) {
-          const int idx = base + u * NT;
-          const int m = idx / l, row = idx - m * l;
-          const bool ok = idx < np * l && qq[m < np ? m : 0] >= 0;
-          gp[u] = ok ? G[row * l + pp[m]] : 0.0;
-          gq[u] = ok ? G[row * l + qq[m]] : 0.0;
-          vp[u] = ok ? V[row * l + pp[m]] : 0.0;
-          vq[u] = ok ? V[row * l + qq[m]] : 0.0;
-        }
-#pragma unroll
-        for (int u = 0; u < kJacobiBatch; ++u) {
-          const int idx = base + u * NT;
-          const int m = idx / l, row = idx - m * l;
-          if (idx >= np * l || qq[m] < 0) continue;
-          const double c = cs[m], s = sn[m];
-          G[row * l + pp[m]] = c * gp[u] - s * gq[u];
-          G[row * l + qq[m]] = s * gp[u] + c * gq[u];
-          V[row * l + pp[m]] = c * vp[u] - s * vq[u];
-          V[row * l + qq[m]] = s * vp[u] + c * vq[u];
-        }
+      for (int u = 0; u < kJacLdsV; ++u) {
+        if (vi[u] < 0) continue;
+        const int i = vi[u], a = va[u], p = pp[i], q = qq[i];
+        const double c = cs[i], s = sn[i], vp = V[a * n + p], vq = V[a * n + q];
+        V[a * n + p] = c * vp - s * vq;
+        V[a * n + q] = s * vp + c * vq;
       }
       __syncthreads();
     }
     if (!changed) break;
     __syncthreads();
   }
-  // sort descending (rank = number of larger eigenvalues, ties by index)
-  if (tid < l) lam[tid] = G[tid * l + tid];
+  for (int i = tid; i < n; i += 1024) lam[i] = i < l ? G[i * n + i] : -INFINITY;
   __syncthreads();
-  if (tid < l) {
-    int rk = 0;
-    for (int j = 0; j < l; ++j) rk += (lam[j] > lam[tid] || (lam[j] == lam[tid] && j < tid)) ? 1 : 0;
-    rank_of[tid] = rk;
-    lam_out[rk] = lam[tid];
+  jacobi_outputs<1024>(l, n, r, lam, rank_of, [&](int a, int i) { return V[a * n + i]; }, lam_out, Wu, Wv);
+}
+
+// Many workgroups, for n > 96: G and the eigenvectors in global memory, in
+// the order of the round-robin slots (the pairs of a round are the slots
+// (k, n - 1 - k), so the 2 x 2 blocks of a row of pairs are read as four
+// contiguous runs), ping-pong buffers: each round reads one copy and writes
+// the rotated matrix to the other at the slots its indices move to (slot 0
+// stays, slot s moves to s + 1 within 1 .. n - 1).  Every workgroup computes
+// all of a round's rotations from the same data (so they take the same
+// convergence decision without exchanging it); one grid barrier per round.
+struct JacobiGrid {
+  const double *Gin;
+  int l, r;
+  double *g[2], *v[2];      // [n][n] each; v row = slot of the eigenvector, column = coordinate
+  unsigned *ctr;            // barrier arrivals, zero at launch
+  unsigned *flag;           // the workspace's give-up word
+  int spin;                 // polls before a barrier wait gives up
+  int extra;                // arrivals awaited beyond the grid's (a host-forced give-up)
+  double *lam_out, *Wu, *Wv;
+};
+constexpr int kJacGridMaxWgs = 64;
+constexpr unsigned kGridAbort = 1u << 31;   // set in the counter by a give-up (arrivals stay far below)
+
+// Stores read by other workgroups after the barrier: device-coherent.
+__device__ __forceinline__ void store_coherent(double *p, double v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), (unsigned long long)__double_as_longlong(v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Barrier of the grid (at most kJacGridMaxWgs workgroups of 256 threads, all
+// resident at once).  Every wave's stores complete, one release arrival per
+// workgroup, a bounded poll, an acquire at agent scope.  A workgroup whose
+// poll runs out sets bit kGridAbort (which releases every other waiter at
+// once) and the flag word; false from then on, in every workgroup.
+__device__ bool grid_barrier(const JacobiGrid &a, unsigned target, int *s_ok) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(a.ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned v = __hip_atomic_load(a.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int it = 0; v < target && it < a.spin; ++it) {
+      __builtin_amdgcn_s_sleep(1);
+      v = __hip_atomic_load(a.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    bool ok = v >= target && v < kGridAbort;
+    if (v < target) {
+      __hip_atomic_fetch_or(a.ctr, kGridAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(a.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *s_ok = ok;
   }
   __syncthreads();
-  double lmax = 0.0;
-  for (int j = 0; j < l; ++j) lmax = lam[j] > lmax ? lam[j] : lmax;
-  const double smax = sqrt(lmax);
-  for (int idx = tid; idx < l * l; idx += NT) {
-    const int a = idx / l, i = idx - a * l, c = rank_of[i];
-    if (c >= r) continue;
-    const double sg = sqrt(lam[i] > 0.0 ? lam[i] : 0.0);
-    const double v = V[a * l + i];
-    Wu[(size_t)a * r + c] = v * sg;
-    Wv[(size_t)a * r + c] = sg > 1e-15 * smax && sg > 0.0 ? v / sg : 0.0;
+  return *s_ok != 0;
+}
+
+__global__ __launch_bounds__(256) void k_jacobi_grid(const JacobiGrid a) {
+  __shared__ double cs[kDecompMaxL / 2], sn[kDecompMaxL / 2];
+  __shared__ int s_changed, s_ok;
+  __shared__ double lam[kDecompMaxL];
+  __shared__ int rank_of[kDecompMaxL];
+  const int l = a.l, n = l + (l & 1), np = n / 2, nn = n * n;
+  const int tid = threadIdx.x, nb = gridDim.x;
+  const int gt = blockIdx.x * 256 + tid, gs = nb * 256;
+  auto next = [&](int s) { return s == 0 ? 0 : (s == n - 1 ? 1 : s + 1); };
+  for (int e = gt; e < nn; e += gs) {
+    const int x = e / n, y = e - x * n;
+    store_coherent(a.g[0] + e, x < l && y < l ? a.Gin[(size_t)x * l + y] : 0.0);
+    store_coherent(a.v[0] + e, x == y ? 1.0 : 0.0);
   }
+  // this thread's first block of G and first two entries of V (the default
+  // grid has no others): loaded each round together with the angles' inputs,
+  // so that a round costs one trip to memory
+  const int nblk = np * np, nv = np * l;
+  const bool hb = gt < nblk, hv0 = gt < nv, hv1 = gt + gs < nv;
+  const int bi = hb ? gt / np : 0, bj = gt - bi * np;
+  const int vi0 = hv0 ? gt / l : 0, vx0 = gt - vi0 * l;
+  const int vi1 = hv1 ? (gt + gs) / l : 0, vx1 = gt + gs - vi1 * l;
+  unsigned passed = 1;
+  bool ok = grid_barrier(a, passed * nb + a.extra, &s_ok);
+  int cur = 0, rounds = 0;
+  for (int sweep = 0; ok && sweep < 40; ++sweep) {
+    if (tid == 0) s_changed = 0;
+    __syncthreads();
+    for (int round = 0; ok && round < n - 1; ++round) {
+      const double *gc = a.g[cur], *vc = a.v[cur];
+      double *gn = a.g[cur ^ 1], *vn = a.v[cur ^ 1];
+      double a00 = 0.0, a01 = 0.0, a10 = 0.0, a11 = 0.0, vp0 = 0.0, vq0 = 0.0, vp1 = 0.0, vq1 = 0.0;
+      if (hb) {
+        a00 = gc[bi * n + bj];
+        a01 = gc[bi * n + n - 1 - bj];
+        a10 = gc[(n - 1 - bi) * n + bj];
+        a11 = gc[(n - 1 - bi) * n + n - 1 - bj];
+      }
+      if (hv0) {
+        vp0 = vc[vi0 * n + vx0];
+        vq0 = vc[(n - 1 - vi0) * n + vx0];
+      }
+      if (hv1) {
+        vp1 = vc[vi1 * n + vx1];
+        vq1 = vc[(n - 1 - vi1) * n + vx1];
+      }
+      if (tid < np) {
+        const int p = tid, q = n - 1 - tid;
+        double c, s;
+        bool big;
+        jacobi_angle(gc[p * n + p], gc[q * n + q], gc[p * n + q], c, s, big);
+        if (big) s_changed = 1;
+        cs[tid] = c;
+        sn[tid] = s;
+      }
+      __syncthreads();
+      auto put_block = [&](int i, int j, double b00, double b01, double b10, double b11) {
+        rot_block(b00, b01, b10, b11, cs[i], sn[i], cs[j], sn[j]);
+        const int npi = next(i), nqi = next(n - 1 - i), npj = next(j), nqj = next(n - 1 - j);
+        store_coherent(gn + npi * n + npj, b00);
+        store_coherent(gn + npi * n + nqj, b01);
+        store_coherent(gn + nqi * n + npj, b10);
+        store_coherent(gn + nqi * n + nqj, b11);
+      };
+      auto put_v = [&](int i, int x, double vp, double vq) {
+        const double c = cs[i], s = sn[i];
+        store_coherent(vn + next(i) * n + x, c * vp - s * vq);
+        store_coherent(vn + next(n - 1 - i) * n + x, s * vp + c * vq);
+      };
+      if (hb) put_block(bi, bj, a00, a01, a10, a11);
+      for (int b = gt + gs; b < nblk; b += gs) {   // grids smaller than the default
+        const int i = b / np, j = b - i * np;
+        put_block(i, j, gc[i * n + j], gc[i * n + n - 1 - j], gc[(n - 1 - i) * n + j],
+                  gc[(n - 1 - i) * n + n - 1 - j]);
+      }
+      if (hv0) put_v(vi0, vx0, vp0, vq0);
+      if (hv1) put_v(vi1, vx1, vp1, vq1);
+      for (int e = gt + 2 * gs; e < nv; e += gs) {
+        const int i = e / l, x = e - i * l;
+        put_v(i, x, vc[i * n + x], vc[(n - 1 - i) * n + x]);
+      }
+      ++passed;
+      ok = grid_barrier(a, passed * nb + a.extra, &s_ok);
+      cur ^= 1;
+      ++rounds;
+    }
+    if (!s_changed) break;
+  }
+  if (blockIdx.x != 0) return;
+  if (!ok) {   // a barrier gave up: no valid result
+    for (int idx = tid; idx < l * a.r; idx += 256) a.Wu[idx] = a.Wv[idx] = __builtin_nan("");
+    for (int i = tid; i < l; i += 256) a.lam_out[i] = __builtin_nan("");
+    return;
+  }
+  const double *gc = a.g[cur], *vc = a.v[cur];
+  // index l (the dummy, odd l) started at slot n - 1 and moved one slot per round
+  const int dummy = (l & 1) ? 1 + (n - 2 + rounds) % (n - 1) : -1;
+  for (int i = tid; i < n; i += 256) lam[i] = i == dummy ? -INFINITY : gc[i * n + i];
+  __syncthreads();
+  jacobi_outputs<256>(l, n, a.r, lam, rank_of, [&](int x, int i) { return vc[i * n + x]; }, a.lam_out, a.Wu,
+                      a.Wv);
+}
+
+// Q = I as [l = N][N]
+__global__ __launch_bounds__(256) void k_eye(double *Y, long N) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < N * N; i += (long)gridDim.x * 256)
+    Y[i] = i / N == i % N ? 1.0 : 0.0;
+}
+
+__global__ void k_zero_u32(unsigned *p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
 // ---------------------------------------------------------------- host side
 
 size_t decompose_ws_bytes(int64_t N, int64_t K, int64_t r, int64_t l, DecompPlan *pl) {
-  pl->lj = l <= 32 ? 32 : (l <= 64 ? 64 : (l <= 128 ? 128 : 256));
+  pl->lj = l <= 32 ? 32 : (l <= 64 ? 64 : (l <= 80 ? 80 : (l <= 128 ? 128 : 256)));
+  // R X: N tiles of 64 x K ranges (of >= 64 columns, multiples of 32), about
+  // 256 workgroups
+  {
+    const long nt = (N + 63) / 64;
+    long sk = (256 + nt - 1) / nt;
+    sk = sk < K / 64 ? sk : K / 64;
+    sk = sk < 32 ? sk : 32;
+    sk = sk > 1 ? sk : 1;
+    pl->kchunk = (int)(((K + sk - 1) / sk + 31) / 32 * 32);
+    pl->srm = (int)((K + pl->kchunk - 1) / pl->kchunk);
+  }
   // R^T Q: K tiles of 64 x N ranges (ranges of >= 256 rows), about 256 workgroups
   const long kt = (K + 63) / 64;
   long sr = (256 + kt - 1) / kt;
@@ -494,10 +796,24 @@ size_t decompose_ws_bytes(int64_t N, int64_t K, int64_t r, int64_t l, DecompPlan
   sr = sr < 64 ? sr : 64;
   pl->srt = (int)(sr > 1 ? sr : 1);
   pl->nchunk = (N + pl->srt - 1) / pl->srt;
+  // Gram sums: ranges of >= 32 rows, about 256 workgroups with the l tiles
   const long len = N > K ? N : K;
-  long sg = (len + 511) / 512;
+  long sg = (256 + (l + 63) / 64 - 1) / ((l + 63) / 64);
+  sg = sg < (len + 31) / 32 ? sg : (len + 31) / 32;
   sg = sg < 128 ? sg : 128;
   pl->sgram = (int)(sg > 1 ? sg : 1);
+  // the eigendecomposition: one workgroup with G and V in LDS where they fit
+  // (n <= 96), else the grid version (kJacGridMaxWgs workgroups at most)
+  const int n = (int)(l + (l & 1));
+  const int jk = debug_knob(AQ_DBG_JACOBI, 0);
+  const bool lds = jk == 1 ? two_fit(n) : (jk == 2 ? false : two_fit(n));
+  // one 2 x 2 block of G per thread (and at most two entries of V), at most
+  // kJacGridMaxWgs workgroups (n = 256)
+  const int np = n / 2, wdef = (np * np + 255) / 256;
+  const int wk = debug_knob(AQ_DBG_JACOBI_WGS, wdef);
+  pl->jac_wgs = lds ? 0 : (wk >= 1 && wk <= kJacGridMaxWgs ? wk : wdef);
+  pl->jac_spin = debug_knob(AQ_DBG_HANDOFF_SPIN, kHandoffSpin);
+  pl->jac_extra = debug_knob(AQ_DBG_HANDOFF_UNREACHABLE, 0) ? 1 : 0;
   // after the reserved region: its counter words belong to the recon calls
   // that share the workspace and must stay zero
   size_t off = kWsReserved;
@@ -511,11 +827,13 @@ size_t decompose_ws_bytes(int64_t N, int64_t K, int64_t r, int64_t l, DecompPlan
   pl->o_z1 = take((size_t)l * K);
   pl->o_z2 = take((size_t)l * K);
   pl->o_zp = take((size_t)pl->srt * l * K);
+  pl->o_yp = take(pl->srm > 1 ? (size_t)pl->srm * l * N : 1);
   pl->o_gp = take((size_t)pl->sgram * l * l);
   pl->o_g = take((size_t)l * l);
   pl->o_rinv = take((size_t)l * l);
   pl->o_scr = take((size_t)l * l);
-  pl->o_v = take((size_t)l * l);
+  pl->o_jac = take(4 * (size_t)n * n);   // the grid Jacobi's two copies of G and of V
+  pl->o_ctr = take(32);              // its barrier counter
   pl->o_lam = take((size_t)l);
   pl->o_wu = take((size_t)l * (r > 0 ? r : 1));
   pl->o_wv = take((size_t)l * (r > 0 ? r : 1));
@@ -531,7 +849,7 @@ static void run_decompose_t(const DecompArgs &d, const DecompPlan &pl, char *ws,
   double *Y1 = (double *)(ws + pl.o_y1), *Y2 = (double *)(ws + pl.o_y2);
   double *Z1 = (double *)(ws + pl.o_z1), *Z2 = (double *)(ws + pl.o_z2), *Zp = (double *)(ws + pl.o_zp);
   double *Gp = (double *)(ws + pl.o_gp), *G = (double *)(ws + pl.o_g), *Rinv = (double *)(ws + pl.o_rinv);
-  double *scr = (double *)(ws + pl.o_scr), *V = (double *)(ws + pl.o_v), *lam = (double *)(ws + pl.o_lam);
+  double *scr = (double *)(ws + pl.o_scr), *lam = (double *)(ws + pl.o_lam);
   double *Wu = (double *)(ws + pl.o_wu), *Wv = (double *)(ws + pl.o_wv);
 
   hipLaunchKernelGGL((k_lsq_scale<T>), dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, W, W0, N, K, s);
@@ -550,14 +868,23 @@ static void run_decompose_t(const DecompArgs &d, const DecompPlan &pl, char *ws,
     for (int pass = 0; pass < 2; ++pass) {
       double *src = pass == 0 ? a : b, *dst = pass == 0 ? b : a;
       gram(src, len);
-      hipLaunchKernelGGL(k_chol_inv, dim3(1), dim3(256), 0, st, (const double *)G, l, Rinv, scr);
+      if (l <= kTriLmax)
+        hipLaunchKernelGGL(k_chol_inv, dim3(1), dim3(kCholThreads), 0, st, (const double *)G, l, Rinv);
+      else
+        hipLaunchKernelGGL(k_chol_inv_global, dim3(1), dim3(256), 0, st, (const double *)G, l, Rinv, scr);
       hipLaunchKernelGGL((k_small_right<LJ>), dim3((unsigned)((len + 63) / 64)), dim3(256), 0, st,
                          (const double *)src, len, l, (const double *)Rinv, l, dst, 0);
     }
   };
   auto rmul = [&](const double *Xt, double *Yt) {
-    hipLaunchKernelGGL((k_rmul<LJ, T>), dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st, W, W0, (const double *)s,
-                       N, K, Xt, l, Yt);
+    double *Yp = pl.srm > 1 ? (double *)(ws + pl.o_yp) : Yt;
+    hipLaunchKernelGGL((k_rmul<LJ, T>), dim3((unsigned)((N + 63) / 64), pl.srm), dim3(256), 0, st, W, W0,
+                       (const double *)s, N, K, Xt, l, pl.kchunk, Yp);
+    if (pl.srm > 1) {
+      const long nn = (long)l * N;
+      hipLaunchKernelGGL(k_fold_parts, dim3((unsigned)((nn + 255) / 256 < 4096 ? (nn + 255) / 256 : 4096)),
+                         dim3(256), 0, st, (const double *)Yp, pl.srm, nn, Yt);
+    }
   };
   auto rtmul = [&](const double *Qt, double *Zt) {
     hipLaunchKernelGGL((k_rtmul<LJ, T>), dim3((unsigned)((K + 63) / 64), pl.srt), dim3(256), 0, st, W, W0,
@@ -567,17 +894,50 @@ static void run_decompose_t(const DecompArgs &d, const DecompPlan &pl, char *ws,
                        0, st, (const double *)Zp, pl.srt, nn, Zt);
   };
 
-  rmul(d.omega, Y1);                 // Y = R Omega^T
-  orth(Y1, Y2, N);                   // Q
-  for (int it = 0; it < d.q; ++it) {
-    rtmul(Y1, Z1);                   // R^T Q
-    orth(Z1, Z2, K);
-    rmul(Z1, Y1);                    // R Q~
-    orth(Y1, Y2, N);
+  if (l == N) {
+    // The probe is as wide as the column space: any orthonormal basis of R^N
+    // spans R's range exactly, so Q = I (B = R) and no subspace step can
+    // change the result.
+    hipLaunchKernelGGL(k_eye, dim3((unsigned)((N * N + 255) / 256 < 4096 ? (N * N + 255) / 256 : 4096)), dim3(256),
+                       0, st, Y1, N);
+  } else {
+    rmul(d.omega, Y1);               // Y = R Omega^T
+    orth(Y1, Y2, N);                 // Q
+    // where l = K the first Q already spans R's range (omega is K x K):
+    // the subspace steps would return the same space
+    const int q = l == K ? 0 : d.q;
+    for (int it = 0; it < q; ++it) {
+      rtmul(Y1, Z1);                 // R^T Q
+      orth(Z1, Z2, K);
+      rmul(Z1, Y1);                  // R Q~
+      orth(Y1, Y2, N);
+    }
   }
   rtmul(Y1, Z1);                     // B^T = R^T Q, i.e. B = Q^T R as [l][K]
   gram(Z1, K);                       // B B^T
-  hipLaunchKernelGGL(k_jacobi, dim3(1), dim3(1024), 0, st, (const double *)G, l, r, scr, V, lam, Wu, Wv);
+  if (pl.jac_wgs == 0) {
+    hipLaunchKernelGGL(k_jacobi_lds, dim3(1), dim3(1024), 0, st, (const double *)G, l, r, lam, Wu, Wv);
+  } else {
+    const size_t n2 = (size_t)(l + (l & 1)) * (l + (l & 1));
+    double *jac = (double *)(ws + pl.o_jac);
+    JacobiGrid ja{};
+    ja.Gin = G;
+    ja.l = l;
+    ja.r = r;
+    ja.g[0] = jac;
+    ja.g[1] = jac + n2;
+    ja.v[0] = jac + 2 * n2;
+    ja.v[1] = jac + 3 * n2;
+    ja.ctr = (unsigned *)(ws + pl.o_ctr);
+    ja.flag = (unsigned *)ws + kSyncFlag;
+    ja.spin = pl.jac_spin;
+    ja.extra = pl.jac_extra;
+    ja.lam_out = lam;
+    ja.Wu = Wu;
+    ja.Wv = Wv;
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, st, ja.ctr, 1);
+    hipLaunchKernelGGL(k_jacobi_grid, dim3((unsigned)pl.jac_wgs), dim3(256), 0, st, ja);
+  }
   // U [N][r] = Q (V_r S_r);  Vt [r][K] = (V_r S_r^-1)^T B
   hipLaunchKernelGGL((k_small_right<LJ>), dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st, (const double *)Y1, N, l,
                      (const double *)Wu, r, d.U, 1);
@@ -591,6 +951,7 @@ hipError_t launch_decompose(const DecompArgs &d, const DecompPlan &pl, void *ws,
   switch (pl.lj) {
     case 32: bf ? run_decompose_t<32, uint16_t>(d, pl, w, st) : run_decompose_t<32, float>(d, pl, w, st); break;
     case 64: bf ? run_decompose_t<64, uint16_t>(d, pl, w, st) : run_decompose_t<64, float>(d, pl, w, st); break;
+    case 80: bf ? run_decompose_t<80, uint16_t>(d, pl, w, st) : run_decompose_t<80, float>(d, pl, w, st); break;
     case 128: bf ? run_decompose_t<128, uint16_t>(d, pl, w, st) : run_decompose_t<128, float>(d, pl, w, st); break;
     default: bf ? run_decompose_t<256, uint16_t>(d, pl, w, st) : run_decompose_t<256, float>(d, pl, w, st); break;
   }

@@ -183,3 +183,53 @@ def test_decompose_refusals():
     with pytest.raises(B.AQError) as e:                # l < r
         B.decompose(W, W, 8, om[:4])
     assert e.value.status == B.AQ_ERR_SHAPE
+
+
+@pytest.mark.parametrize("N,K,r,oversample,jac,wgs", [
+    (300, 520, 8, 10, 2, 1),      # l = 18 on the many-workgroup solver: one workgroup
+    (300, 520, 8, 10, 2, 7),      # seven (rounds split unevenly)
+    (300, 520, 8, 11, 2, 64),     # l = 19 (odd: a dummy index), the most workgroups
+    (300, 520, 8, 11, 1, 0),      # l = 19 in LDS
+    (95, 300, 5, 10, 0, 0),       # l = N = 95: Q = I, the largest odd l in LDS
+    (95, 300, 5, 10, 2, 5),       # the same on the grid
+    (97, 400, 6, 10, 0, 0),       # l = N = 97: the grid by default (odd)
+    (97, 400, 6, 10, 0, 3),
+    (500, 128, 8, 10, 0, 0),      # l = K = 128: no subspace steps, the packed Cholesky at its limit
+    (600, 150, 8, 10, 0, 0),      # l = K = 150: the Cholesky in global memory
+    (400, 600, 40, 10, 0, 0),     # l = 50: the 64-wide contraction tiles
+])
+def test_decompose_eigensolvers(N, K, r, oversample, jac, wgs, force_plan):
+    """Both Jacobi eigensolvers (one workgroup with G and V in LDS; many
+    workgroups over global memory with a grid barrier per round) at odd and
+    even l, several grid sizes, and both Cholesky kernels."""
+    if jac:
+        force_plan("JACOBI", jac)
+    if wgs:
+        force_plan("JACOBI_WGS", wgs)
+    W, W0 = _weights(N, K, r, 7, "f32")
+    _check(N, K, r, 2, W, W0, "f32", f"{N}x{K} r={r} p={oversample} jacobi={jac} wgs={wgs}", oversample)
+
+
+def test_decompose_grid_give_up_reported(force_plan):
+    """A grid barrier of the many-workgroup eigensolver that gives up (forced
+    from the host: one more arrival awaited than will come, 64 polls): every
+    workgroup exits, U and Vt are NaN, and the workspace check reports it
+    (and clears it); the next call on that workspace is valid."""
+    N, K, r = 200, 264, 6
+    W, W0 = _weights(N, K, r, 8, "f32")
+    Wd, W0d = _dev(W, torch.float32), _dev(W0, torch.float32)
+    om = torch.zeros((N, K), dtype=torch.float64, device=dev())      # l = N: Q = I, omega unused
+    ws = B.Workspace()
+    force_plan("HANDOFF_SPIN", 64)
+    force_plan("HANDOFF_UNREACHABLE", 1)
+    s, U, Vt = B.decompose(Wd, W0d, r, om, q=1, workspace=ws)
+    assert torch.isnan(U).all() and torch.isnan(Vt).all()
+    with pytest.raises(B.AQError) as e:
+        ws.check()
+    assert e.value.status == B.AQ_ERR_HANDOFF, e.value
+    B.aq_debug_reset_plan()
+    s, U, Vt = B.decompose(Wd, W0d, r, om, q=1, workspace=ws)
+    ws.check()
+    so, Uo, Vto, _ = oracle.decompose_randomized(W, W0, r, np.zeros((N, K)), 1)
+    Po = Uo @ Vto
+    assert np.max(np.abs(U.cpu().numpy() @ Vt.cpu().numpy() - Po)) <= TOL_UV * np.max(np.abs(Po))
