@@ -834,8 +834,9 @@ def run_materialize_fp4(args, torch, B, I, nested=False):
     order = [(f, l) for f in I.FAMILIES for l in range(L)]
     n = len(order)
     mitems, fitems = (B.aq_mat_item * n)(), (B.aq_fp4_item * n)()
+    xitems = (B.aq_mat_fp4_item * n)()
     amax = torch.zeros(n, dtype=torch.int32, device=dev)
-    bmat = bpack = 0
+    bmat = bpack = bfused = 0
     seen = set()
     for i, (f, l) in enumerate(order):
         K, N = I.GEMMA_1B[f]
@@ -846,20 +847,32 @@ def run_materialize_fp4(args, torch, B, I, nested=False):
         gs = torch.empty((1,), dtype=torch.float32, device=dev)
         mitems[i] = B.aq_mat_item(K, B.make_proj(*bd), w.data_ptr(), K)
         fitems[i] = B.aq_fp4_item(N, K, K, w.data_ptr(), packed.data_ptr(), sc.data_ptr(), gs.data_ptr())
-        keep += [w, packed, sc, gs]
+        packed2 = torch.empty_like(packed)
+        sc2 = torch.empty_like(sc)
+        gs2 = torch.empty_like(gs)
+        xitems[i] = B.aq_mat_fp4_item(K, B.make_proj(*bd), packed2.data_ptr(), sc2.data_ptr(), gs2.data_ptr())
+        keep += [w, packed, sc, gs, packed2, sc2, gs2]
         if bd[0].data_ptr() not in seen:              # W0 read once per band
             seen.add(bd[0].data_ptr())
             bmat += N * K * 2
+            bfused += 2 * N * K * 2                   # ... in each of the two passes
         bmat += (N * K + N + N * 64 + 64 * K) * 2     # W_eff written; s, U, Vt read
         bpack += N * K * 2 + N * K // 2 + N * K // 16
+        bfused += 2 * (N + N * 64 + 64 * K) * 2 + N * K // 2 + N * K // 16
     keep += [mitems, fitems]
     matb = Call(lib.aq_materialize_batch, (B.AQ_BF16, n, mitems, amax.data_ptr(), stream), bmat,
                 2 * sum(I.GEMMA_1B[f][0] * I.GEMMA_1B[f][1] for f, _ in order) * 64, "mat.batch", "matb")
     packb = Call(lib.aq_quant_fp4_batch, (n, fitems, amax.data_ptr(), None, 0, stream), bpack, 0, "fp4.batch",
                  "fp4b")
+    fws_bytes = lib.aq_materialize_fp4_batch_workspace_bytes(n)
+    fws = torch.zeros(fws_bytes, dtype=torch.uint8, device=dev)
+    keep += [xitems, fws]
+    fusedb = Call(lib.aq_materialize_fp4_batch, (n, xitems, fws.data_ptr(), fws_bytes, stream), bfused, 0,
+                  "matfp4.batch", "mfb")
     ms_mb, _ = time_graph(torch, [matb], steps, warm)
     ms_pb, _ = time_graph(torch, [packb], steps, warm)
     ms_both, _ = time_graph(torch, [matb, packb], steps, warm)
+    ms_fused, _ = time_graph(torch, [fusedb], steps, warm)
     # Ceilings for this traffic mix, in the same graph setting: a device copy
     # (read + write) and a fill (write only) of 1 GiB.
     class _Op:
@@ -877,7 +890,11 @@ def run_materialize_fp4(args, torch, B, I, nested=False):
     batched = {"materialize": dict(leg(ms_mb, bmat), bytes=bmat,
                                    bytes_note="W0 once per band (13 x 7), W_eff written, s, U, V read"),
                "fp4_pack": dict(leg(ms_pb, bpack), bytes=bpack, bytes_note="W_eff read once, codes and scales written"),
-               "both": dict(leg(ms_both, bmat + bpack), bytes=bmat + bpack)}
+               "both": dict(leg(ms_both, bmat + bpack), bytes=bmat + bpack),
+               "fp4_without_w_eff": dict(leg(ms_fused, bfused), bytes=bfused,
+                                         bytes_note="aq_materialize_fp4_batch: W0 once per band, s, U, V read "
+                                                    "in each of its two passes; codes and scales written",
+                                         vs_both=_r(ms_fused / ms_both, 3))}
     return {"workload": "materialise + FP4 pack, 7 families x 26 layers (Gemma-3-1B shapes), 13 W0 bands, rank 64",
             "batched": batched, "calibration": calib,
             "note": "batched: one aq_materialize_batch call for all 182 projections, then one "

@@ -233,6 +233,30 @@ aq_status aq_quant_fp4_batch(int n, const aq_fp4_item *items, const uint32_t *am
                              void *stream);
 size_t aq_quant_fp4_batch_workspace_bytes(int n, int have_amax);
 
+/* The FP4 weights of many projections without their bf16 W_eff: the same
+ * bytes and global scales as aq_materialize_batch followed by
+ * aq_quant_fp4_batch with its maxima ("Execution paths", section
+ * "Precompute-outside": W_eff rebuilt at load and quantised there, where only
+ * the quantised weight is kept; "Internals and extension", section
+ * "Nvfp4Spec").  Two passes over the shared blocks and factors: the first
+ * forms every W_eff tile and keeps only each weight's largest magnitude, the
+ * second forms the same tiles again and encodes them; W_eff never reaches
+ * memory.  bf16, r <= 64, K % 16 == 0; items as aq_mat_item with the packed
+ * outputs of aq_fp4_item (dense [N, K/2] codes 8-byte aligned, [N, K/16]
+ * scales, one device float); consecutive items on the same W0 (the layers of
+ * a band) share its reads.  ws: aq_materialize_fp4_batch_workspace_bytes(n)
+ * bytes, 256-byte aligned (the maxima, after the reserved region, which is
+ * not touched).  Errors name the item.  Asynchronous on `stream`. */
+typedef struct aq_mat_fp4_item {
+  int64_t K;              /* in_dim */
+  aq_proj p;              /* N, r, W0, s, U, Vt */
+  uint8_t *packed;        /* [N, K/2] */
+  uint8_t *scales;        /* [N, K/16] */
+  float *global_scale;    /* one device float */
+} aq_mat_fp4_item;
+aq_status aq_materialize_fp4_batch(int n, const aq_mat_fp4_item *items, void *ws, size_t ws_bytes, void *stream);
+size_t aq_materialize_fp4_batch_workspace_bytes(int n);
+
 /* FP4 decode GEMV over a packed weight: y[m, n] = bf16(sum_k x[m, k] * Wq[n, k])
  * for m < M <= 16 tokens, where Wq[n, k] = E2M1(code) * RN_f32(g * E4M3(scale))
  * is the weight that aq_quant_fp4_block16's output stands for ("Execution

@@ -48,6 +48,11 @@ class aq_fp4_item(ctypes.Structure):
                 ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_scale", ctypes.c_void_p)]
 
 
+class aq_mat_fp4_item(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int64), ("p", aq_proj), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p)]
+
+
 class AQError(RuntimeError):
     def __init__(self, status, detail):
         self.status = status
@@ -108,6 +113,10 @@ def lib():
         L.aq_quant_fp4_batch.restype = ctypes.c_int
         L.aq_quant_fp4_batch_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
         L.aq_quant_fp4_batch_workspace_bytes.restype = sz
+        L.aq_materialize_fp4_batch.argtypes = [ctypes.c_int, ctypes.POINTER(aq_mat_fp4_item), vp, sz, vp]
+        L.aq_materialize_fp4_batch.restype = ctypes.c_int
+        L.aq_materialize_fp4_batch_workspace_bytes.argtypes = [ctypes.c_int]
+        L.aq_materialize_fp4_batch_workspace_bytes.restype = sz
         _lib = L
     return _lib
 
@@ -163,6 +172,14 @@ def aq_quant_fp4_batch(n, items, amax, ws, ws_bytes, stream):
 
 def aq_quant_fp4_batch_workspace_bytes(n, have_amax):
     return lib().aq_quant_fp4_batch_workspace_bytes(n, have_amax)
+
+
+def aq_materialize_fp4_batch(n, items, ws, ws_bytes, stream):
+    return lib().aq_materialize_fp4_batch(n, items, ws, ws_bytes, stream)
+
+
+def aq_materialize_fp4_batch_workspace_bytes(n):
+    return lib().aq_materialize_fp4_batch_workspace_bytes(n)
 
 
 def aq_workspace_bytes(op, dt, M, K, p, nproj):
@@ -499,6 +516,31 @@ def quant_fp4_batch(weights, amax=None, workspace=None):
     return out
 
 
+def materialize_fp4_batch(bundles, workspace=None):
+    """The FP4 weights of many bundles (W0, s, U, Vt; bf16, r <= 64, K % 16
+    == 0) without their bf16 W_eff: the bytes of materialize_batch followed by
+    quant_fp4_batch.  Returns a list of (packed, scales, global_scale)."""
+    n = len(bundles)
+    if n == 0:
+        return []
+    dev = bundles[0][0].device
+    items = (aq_mat_fp4_item * n)()
+    out = []
+    for i, bd in enumerate(bundles):
+        N, K = bd[0].shape
+        if K % 16:
+            raise ValueError(f"bundle {i}: K = {K} must be a multiple of 16")
+        packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+        g = torch.empty((1,), dtype=torch.float32, device=dev)
+        items[i] = aq_mat_fp4_item(K, make_proj(*bd), _ptr(packed), _ptr(scales), _ptr(g))
+        out.append((packed, scales, g))
+    need = lib().aq_materialize_fp4_batch_workspace_bytes(n)
+    ws, ws_bytes = (workspace or _WS).get(need, dev)
+    check(lib().aq_materialize_fp4_batch(n, items, ws, ws_bytes, _stream()))
+    return out
+
+
 def aq_fp4_linear(M, N, K, x, ldx, packed, scales, global_scale, y, ldy, ws, ws_bytes, stream):
     return lib().aq_fp4_linear(M, N, K, x, ldx, packed, scales, global_scale, y, ldy, ws, ws_bytes, stream)
 
@@ -653,8 +695,9 @@ def check_bundles(shared, layers, quant=None, require_gpu=True):
 
 
 def materialize_model(shared, layers, quant=None):
-    """The load-time path: ``check_bundles``, then every W_eff, then (with
-    ``quant="nvfp4"``) its FP4 pack.  Returns ``{layer: {family: W_eff}}`` or
+    """The load-time path: ``check_bundles``, then every W_eff, or (with
+    ``quant="nvfp4"``) every FP4 weight, without the bf16 W_eff where the
+    batched calls take the bundle.  Returns ``{layer: {family: W_eff}}`` or
     ``{layer: {family: (packed, scales, global_scale)}}``."""
     check_bundles(shared, layers, quant)
     # family by family, band by band: the layers of one band sit next to each
@@ -665,8 +708,7 @@ def materialize_model(shared, layers, quant=None):
     out = {l: {} for l in layers}
     if batch:
         bundles = [(shared[b][f],) + tuple(layers[l][f][1:]) for f, b, l in batch]
-        ws, amax = materialize_batch(bundles, want_amax=True)
-        packs = quant_fp4_batch(ws, amax) if quant == "nvfp4" else ws
+        packs = materialize_fp4_batch(bundles) if quant == "nvfp4" else materialize_batch(bundles)
         for (f, b, l), v in zip(batch, packs):
             out[l][f] = v
     for f, b, l in order:                  # fp32 weights and ranks above 64

@@ -431,6 +431,42 @@ aq_status aq_materialize_batch(aq_dtype dt, int n, const aq_mat_item *items, uin
   return AQ_OK;
 }
 
+size_t aq_materialize_fp4_batch_workspace_bytes(int n) {
+  if (n < 1 || n > kMaxBatchItems) return 0;
+  return aq::kWsReserved + ((size_t)n * 4 + 255) / 256 * 256;
+}
+
+aq_status aq_materialize_fp4_batch(int n, const aq_mat_fp4_item *items, void *ws, size_t ws_bytes, void *stream) {
+  if (n < 0 || n > kMaxBatchItems) return fail(AQ_ERR_INVALID_ARG, "n = %d outside [0, %d]", n, kMaxBatchItems);
+  if (n == 0) return AQ_OK;
+  if (!items) return fail(AQ_ERR_INVALID_ARG, "items is NULL");
+  std::vector<aq::MatItem> v((size_t)n);
+  for (int i = 0; i < n; ++i) {
+    const aq_mat_fp4_item &it = items[i];
+    // the materialisation's checks on the bundle (no W_eff: W0 stands in for
+    // it) and the pack's on the outputs
+    aq_status cs = check_materialize(AQ_BF16, it.K, &it.p, it.p.W0 ? it.p.W0 : (const void *)&it, it.K);
+    if (cs == AQ_OK && it.p.r > aq::kMatBatchMaxRank)
+      cs = fail(AQ_ERR_UNSUPPORTED, "rank %lld above %d", (long long)it.p.r, aq::kMatBatchMaxRank);
+    if (cs == AQ_OK) cs = check_fp4_pack(it.p.N, it.K, it.p.W0, it.K, it.packed, it.scales, it.global_scale);
+    if (cs != AQ_OK) return item_fail(cs, i);
+    aq::MatItem &m = v[(size_t)i];
+    m = aq::MatItem{it.p.N, it.K, it.p.r, it.K, it.p.W0, it.p.s, it.p.U, it.p.Vt, nullptr};
+    m.packed = it.packed;
+    m.scales = it.scales;
+    m.gscale = it.global_scale;
+  }
+  const size_t need = aq_materialize_fp4_batch_workspace_bytes(n);
+  if (!ws) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (ws_bytes < need) return fail(AQ_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
+  if (!aligned(ws, 256)) return fail(AQ_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  unsigned *amax = (unsigned *)((char *)ws + aq::kWsReserved);
+  hipError_t e = aq::launch_materialize_batch(n, v.data(), amax, (hipStream_t)stream, 1);
+  if (e == hipSuccess) e = aq::launch_materialize_batch(n, v.data(), amax, (hipStream_t)stream, 2);
+  if (e != hipSuccess) return fail(AQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return AQ_OK;
+}
+
 size_t aq_quant_fp4_batch_workspace_bytes(int n, int have_amax) {
   if (n < 1 || n > kMaxBatchItems) return 0;
   return aq::fp4_batch_ws_bytes(n, have_amax != 0);

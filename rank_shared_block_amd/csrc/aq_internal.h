@@ -151,11 +151,16 @@ constexpr int kMatRunMax = 2, kMatBatchRuns = 24, kMatBatchOuts = 48, kMatBatchM
 struct MatItem {
   int64_t N, K, r, ldw;
   const void *W0, *s, *U, *Vt;
-  void *w;
+  void *w;                     // W_eff (mode 0)
+  uint8_t *packed = nullptr, *scales = nullptr;   // the FP4 weight (mode 2)
+  float *gscale = nullptr;
 };
-// amax: NULL, or n device words that receive each W_eff's largest magnitude as
-// bf16 bits (zeroed here first).
-hipError_t launch_materialize_batch(int n, const MatItem *items, unsigned *amax, hipStream_t st);
+// mode 0: W_eff stored; amax NULL, or n device words that receive each W_eff's
+// largest magnitude as bf16 bits (zeroed here first).  mode 1: only those
+// maxima (amax required, zeroed here first), nothing stored.  mode 2: W_eff
+// encoded as block-16 FP4 (K % 16 == 0) with the global scale derived from
+// amax (read, not zeroed: the maxima of a mode-1 launch).
+hipError_t launch_materialize_batch(int n, const MatItem *items, unsigned *amax, hipStream_t st, int mode = 0);
 
 // ---- FP4 pack -------------------------------------------------------------------
 constexpr int kFp4AmaxBlocks = 1024;

@@ -27,6 +27,7 @@
 
 #include "aq_internal.h"
 #include "device_common.h"
+#include "fp4_block.h"
 
 namespace aq {
 
@@ -232,7 +233,9 @@ __global__ __launch_bounds__(256) void k_materialize_f32(const MatArgs a) {
 // the FP4 pack skip its own pass over W_eff.
 struct MatBOut {
   const uint16_t *s, *U, *Vt;
-  uint16_t *w;
+  uint16_t *w;               // W_eff (kMatStore), or the FP4 codes [N, K/2] (kMatPack)
+  uint8_t *scales;           // kMatPack: the block scales [N, K/16]
+  float *gscale;             // kMatPack: the global scale
   int r, ldw;
 };
 struct MatBRun {
@@ -247,7 +250,13 @@ struct MatBatchArgs {
 };
 static_assert(sizeof(MatBatchArgs) <= 3584, "kernel arguments stay well inside 4 KiB");
 
-template <int RJ>
+// What a launch does with each W_eff tile: store it (bf16; with amax set, the
+// maxima too), only fold its largest magnitude into amax, or encode it as
+// block-16 FP4 with the global scale that amax gives (the tile is the same
+// one, value for value, that kMatStore writes).
+enum { kMatStore = 0, kMatMax = 1, kMatPack = 2 };
+
+template <int RJ, int MODE>
 __global__ __launch_bounds__(256, 3) void k_materialize_batch(const MatBatchArgs a) {
   constexpr int CB = 64, RB = 128;
   constexpr int RP = 16 * RJ + 8, WP = CB + 8;
@@ -295,9 +304,23 @@ __global__ __launch_bounds__(256, 3) void k_materialize_batch(const MatBatchArgs
     }
   }
 
-  unsigned amx[kMatRunMax];
+  // Each output's largest |W_eff| before rounding: rounding to bf16 is
+  // monotone and symmetric, so one rounding of that maximum is the largest
+  // rounded magnitude (one max per element instead of a max over bits).
+  float amx[kMatRunMax];
 #pragma unroll
-  for (int o = 0; o < kMatRunMax; ++o) amx[o] = 0u;
+  for (int o = 0; o < kMatRunMax; ++o) amx[o] = 0.f;
+  float gq[kMatRunMax];                     // kMatPack: each output's global scale
+#pragma unroll
+  for (int o = 0; o < kMatRunMax; ++o) gq[o] = 1.f;
+  if constexpr (MODE == kMatPack) {
+#pragma unroll
+    for (int o = 0; o < kMatRunMax; ++o) {
+      if (o >= nout) break;
+      gq[o] = fp4_global_scale(a.amax[a.amax0 + R.out0 + o]);
+      if (u == 0 && tid == 0) *a.out[R.out0 + o].gscale = gq[o];
+    }
+  }
   for (int n0 = g0; n0 < gend; n0 += RB) {
     const int nrow = min(RB, gend - n0);
     // This lane's output row: its s and U row (the B operand) per output.
@@ -366,34 +389,64 @@ __global__ __launch_bounds__(256, 3) void k_materialize_batch(const MatBatchArgs
       }
       __syncthreads();                      // every lane is done reading wt
       const float sv = bf2f(s_raw[o]);
-      unsigned m = amx[o];
+      float m = amx[o];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const uint2 w = w0[t][g];
-          const uint32_t e0 = f2bf(fmaf(sv, bf2f((uint16_t)w.x), acc[t][4 * g + 0]));
-          const uint32_t e1 = f2bf(fmaf(sv, bf2f((uint16_t)(w.x >> 16)), acc[t][4 * g + 1]));
-          const uint32_t e2 = f2bf(fmaf(sv, bf2f((uint16_t)w.y), acc[t][4 * g + 2]));
-          const uint32_t e3 = f2bf(fmaf(sv, bf2f((uint16_t)(w.y >> 16)), acc[t][4 * g + 3]));
-          m = max(max(m, max(e0 & 0x7FFFu, e1 & 0x7FFFu)), max(e2 & 0x7FFFu, e3 & 0x7FFFu));
-          *reinterpret_cast<uint2 *>(&wt[rl * WP + 32 * t + 8 * g + 4 * hi]) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+          const float v0 = fmaf(sv, bf2f((uint16_t)w.x), acc[t][4 * g + 0]);
+          const float v1 = fmaf(sv, bf2f((uint16_t)(w.x >> 16)), acc[t][4 * g + 1]);
+          const float v2 = fmaf(sv, bf2f((uint16_t)w.y), acc[t][4 * g + 2]);
+          const float v3 = fmaf(sv, bf2f((uint16_t)(w.y >> 16)), acc[t][4 * g + 3]);
+          m = fmaxf(fmaxf(fmaxf(m, fabsf(v0)), fmaxf(fabsf(v1), fabsf(v2))), fabsf(v3));
+          if constexpr (MODE != kMatMax) {
+            // one rounding to bf16 each (round to nearest even; the hardware
+            // conversion, two values per instruction)
+            const f32x2 lo2 = {v0, v1}, hi2 = {v2, v3};
+            *reinterpret_cast<uint2 *>(&wt[rl * WP + 32 * t + 8 * g + 4 * hi]) =
+                make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo2, bf16x2)),
+                           __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2)));
+          }
         }
       amx[o] = m;                           // rows and columns past the tile hold exact zeros
-      __syncthreads();                      // W_eff tile complete
+      if constexpr (MODE == kMatStore) {
+        __syncthreads();                    // W_eff tile complete
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int c = tid + 256 * q, row = c >> 3, col = (c & 7) * 8;
-        if (row < nrow && col < ncol)
-          *reinterpret_cast<uint4 *>(O.w + (size_t)(n0 + row) * O.ldw + cb0 + col) =
-              *reinterpret_cast<const uint4 *>(&wt[row * WP + col]);
+        for (int q = 0; q < NQ; ++q) {
+          const int c = tid + 256 * q, row = c >> 3, col = (c & 7) * 8;
+          if (row < nrow && col < ncol)
+            *reinterpret_cast<uint4 *>(O.w + (size_t)(n0 + row) * O.ldw + cb0 + col) =
+                *reinterpret_cast<const uint4 *>(&wt[row * WP + col]);
+        }
+      } else if constexpr (MODE == kMatPack) {
+        __syncthreads();                    // W_eff tile complete
+        // 128 rows x four 16-column blocks: two blocks per thread, each read
+        // from the tile as 32 bytes, encoded, one 8-byte code store and one
+        // scale byte (K is a multiple of 16, so every block is whole)
+        const int kb = K >> 4;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int bi = 2 * tid + h2, row = bi >> 2, col = (bi & 3) * 16;
+          if (row < nrow && col < ncol) {
+            const uint4 v0 = *reinterpret_cast<const uint4 *>(&wt[row * WP + col]);
+            const uint4 v1 = *reinterpret_cast<const uint4 *>(&wt[row * WP + col + 8]);
+            const uint32_t qv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t lo, hb, sf;
+            pack_block16(qv, gq[o], lo, hb, sf);
+            const size_t n = (size_t)(n0 + row);
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint8_t *>(O.w) + n * (size_t)(K >> 1) + (cb0 + col) / 2) =
+                make_uint2(lo, hb);
+            O.scales[n * kb + (cb0 + col) / 16] = (uint8_t)sf;
+          }
+        }
       }
     }
   }
-  if (a.amax) {
+  if (MODE != kMatPack && a.amax) {
 #pragma unroll
     for (int o = 0; o < kMatRunMax; ++o) {
-      unsigned m = amx[o];
+      unsigned m = f2bf(amx[o]) & 0x7FFFu;   // the rounded maximum's magnitude bits
 #pragma unroll
       for (int sh = 32; sh > 0; sh >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, sh));
       if (lane == 0) red[wave][o] = m;
@@ -413,12 +466,12 @@ __global__ __launch_bounds__(256) void k_fill_u32(unsigned *p, int n, unsigned v
 
 int matb_rank_steps(int64_t r) { return r <= 16 ? 1 : (r <= 32 ? 2 : 4); }
 
-hipError_t launch_materialize_batch(int n, const MatItem *it, unsigned *amax, hipStream_t st) {
+hipError_t launch_materialize_batch(int n, const MatItem *it, unsigned *amax, hipStream_t st, int mode) {
   // Row steps per work unit: 128-row steps with the next W0 tile in flight;
   // longer units keep the pipeline full, shorter ones fill the CUs' last round.
   int steps = debug_knob(AQ_DBG_MAT_STEPS, 3);
   if (steps < 1 || steps > 8) steps = 3;
-  if (amax) {
+  if (amax && mode != kMatPack) {
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, amax, n, 0u);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -458,7 +511,9 @@ hipError_t launch_materialize_batch(int n, const MatItem *it, unsigned *amax, hi
         O.s = (const uint16_t *)g.s;
         O.U = (const uint16_t *)g.U;
         O.Vt = (const uint16_t *)g.Vt;
-        O.w = (uint16_t *)g.w;
+        O.w = (uint16_t *)(mode == kMatPack ? (void *)g.packed : g.w);
+        O.scales = (uint8_t *)g.scales;
+        O.gscale = g.gscale;
         O.r = (int)g.r;
         O.ldw = (int)g.ldw;
         if (!(g.r % 8 == 0 && ((uintptr_t)g.U & 15) == 0)) a.ufast_all = 0;
@@ -469,12 +524,19 @@ hipError_t launch_materialize_batch(int n, const MatItem *it, unsigned *amax, hi
     }
     a.nunits = units;
     const dim3 grid((unsigned)(8 * ((units + 7) / 8)));
-    if (rj == 1)
-      hipLaunchKernelGGL((k_materialize_batch<1>), grid, dim3(256), 0, st, a);
-    else if (rj == 2)
-      hipLaunchKernelGGL((k_materialize_batch<2>), grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_materialize_batch<4>), grid, dim3(256), 0, st, a);
+#define AQ_MATB(M)                                                          \
+  if (mode == M) {                                                          \
+    if (rj == 1)                                                            \
+      hipLaunchKernelGGL((k_materialize_batch<1, M>), grid, dim3(256), 0, st, a); \
+    else if (rj == 2)                                                       \
+      hipLaunchKernelGGL((k_materialize_batch<2, M>), grid, dim3(256), 0, st, a); \
+    else                                                                    \
+      hipLaunchKernelGGL((k_materialize_batch<4, M>), grid, dim3(256), 0, st, a); \
+  }
+    AQ_MATB(kMatStore)
+    AQ_MATB(kMatMax)
+    AQ_MATB(kMatPack)
+#undef AQ_MATB
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     i += nout;

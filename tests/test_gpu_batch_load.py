@@ -1,5 +1,5 @@
 """GPU parity of the load-time batch calls (aq_materialize_batch,
-aq_quant_fp4_batch): every W_eff against the oracle's (one rounding; bit-exact
+aq_quant_fp4_batch, aq_materialize_fp4_batch): every W_eff against the oracle's (one rounding; bit-exact
 where the rank term is absent), the same bits as the one-projection call, the
 largest magnitudes they report, and the FP4 bytes against the oracle's pack.
 
@@ -168,6 +168,42 @@ def test_load_time_chain_gemma_band():
         assert torch.equal(p, p1) and torch.equal(s, s1) and torch.equal(g, g1), f"item {i}: pack bytes"
     for i in (0, 9, 13):                       # q of layer 0, gate and down of layer 1, against the oracle
         assert_parity(down(outs[i]), oracle.materialize(*bundle_np(bds[i])), "bf16", f"item {i}")
+    for i, ((p, s, g), (p1, s1, g1)) in enumerate(zip(B.materialize_fp4_batch(dbs), packs)):
+        assert torch.equal(p, p1) and torch.equal(s, s1) and torch.equal(g, g1), f"item {i}: FP4 without W_eff"
+
+
+def test_materialize_fp4_batch_same_bytes():
+    """aq_materialize_fp4_batch (W_eff formed twice, never stored): the same
+    codes, scales and global scales as the batched materialisation followed by
+    the batched pack with its maxima, on bundles with K % 16 == 0 -- runs of
+    two layers on one W0, ragged N, rank 0, a passthrough bundle, a one-row
+    weight, more items than one launch holds."""
+    bds = []
+    bds += _band(80, 300, 272, [64, 64], 80)
+    bds += _band(81, 130, 1056, [16, 5, 33], 81)
+    bds += _band(82, 77, 64, [0], 82)
+    bds += _band(83, 96, 144, [8, 8], 83, "passthrough")
+    bds += _band(84, 1, 16, [40], 84)
+    for j in range(28):
+        bds += _band(90 + j, 16 + 8 * j, 64 + 16 * (j % 5), [4 * (j % 17), 2 * (j % 9)], 90 + j)
+    dbs = _upload(bds)
+    assert len(dbs) > 48
+    outs, amax = B.materialize_batch(dbs, want_amax=True)
+    ref = B.quant_fp4_batch(outs, amax)
+    got = B.materialize_fp4_batch(dbs)
+    for i, ((p, sc, g), (p1, s1, g1)) in enumerate(zip(got, ref)):
+        assert torch.equal(g, g1), f"item {i}: global scale"
+        assert torch.equal(sc, s1), f"item {i}: scales"
+        assert torch.equal(p, p1), f"item {i}: codes"
+    # and the oracle's pack of the oracle's W_eff where W_eff is exact (rank 0
+    # and passthrough: one rounding of s W0)
+    for i in (5, 6, 7):
+        bd = bds[i]
+        if bd["U"].shape[1] == 0 or not np.any(bd["U"]):
+            ep, es, eg = oracle.fp4_pack(oracle.rne_bf16(oracle.materialize(*bundle_np(bd))))
+            p, sc, g = got[i]
+            assert float(g.cpu()[0]) == eg and np.array_equal(sc.cpu().numpy(), es) and \
+                np.array_equal(p.cpu().numpy(), ep), f"item {i}: oracle"
 
 
 def test_materialize_model_uses_the_batch_and_falls_back():

@@ -180,6 +180,25 @@ def test_batch_argument_errors_name_the_item():
     assert B.aq_quant_fp4_batch(2, fp4_items(), None, None, 0, None) == B.AQ_ERR_WORKSPACE
     assert B.aq_quant_fp4_batch(2, fp4_items(packed=FAKE + 4), FAKE, None, 0, None) == B.AQ_ERR_ALIGNMENT
 
+    def mf_items(**bad):
+        items = (B.aq_mat_fp4_item * 3)()
+        for i in range(3):
+            items[i] = B.aq_mat_fp4_item(128, _proj(), FAKE, FAKE, FAKE)
+        for k, v in bad.items():
+            setattr(items[2], k, v)
+        return items
+    need = B.aq_materialize_fp4_batch_workspace_bytes(3)
+    assert need == 65536 + 256 and B.aq_materialize_fp4_batch_workspace_bytes(0) == 0
+    assert B.aq_materialize_fp4_batch(3, mf_items(K=136), FAKE, need, None) == B.AQ_ERR_ALIGNMENT
+    assert B.last_error().startswith("item 2: ") and "multiple of 16" in B.last_error()
+    assert B.aq_materialize_fp4_batch(3, mf_items(p=_proj(r=65)), FAKE, need, None) == B.AQ_ERR_UNSUPPORTED
+    assert B.last_error().startswith("item 2: ")
+    assert B.aq_materialize_fp4_batch(3, mf_items(packed=None), FAKE, need, None) == B.AQ_ERR_INVALID_ARG
+    assert B.aq_materialize_fp4_batch(3, mf_items(packed=FAKE + 4), FAKE, need, None) == B.AQ_ERR_ALIGNMENT
+    assert B.aq_materialize_fp4_batch(3, mf_items(), FAKE, need - 1, None) == B.AQ_ERR_WORKSPACE
+    assert B.aq_materialize_fp4_batch(3, mf_items(), None, 0, None) == B.AQ_ERR_WORKSPACE
+    assert B.aq_materialize_fp4_batch(0, None, None, 0, None) == B.AQ_OK
+
 
 def test_fp4_linear_argument_errors_and_workspace():
     def call(M=1, N=64, K=128, ldx=None, ldy=None, x=FAKE, ptr=FAKE):
