@@ -346,8 +346,9 @@ SOURCES = {"decode_gateup": "rank_shared_block_amd/csrc/recon_decode.hip",
                                     "rank_shared_block_amd/csrc/handoff.h"),
            "fp4_gemv_gateup": "rank_shared_block_amd/csrc/fp4_gemv.hip",
            "fp4_gemv_dot_large": "rank_shared_block_amd/csrc/fp4_gemv.hip",
-           "materialize_batch": "rank_shared_block_amd/csrc/materialize.hip",
-           "fp4_pack_batch": "rank_shared_block_amd/csrc/fp4_pack.hip"}
+           "materialize_batch": ("rank_shared_block_amd/csrc/materialize.hip",
+                                 "rank_shared_block_amd/csrc/fp4_block.h"),
+           "fp4_pack_batch": ("rank_shared_block_amd/csrc/fp4_pack.hip", "rank_shared_block_amd/csrc/fp4_block.h")}
 PMC_KERNELS = {"decode_gateup": (("k_decode_bf16",), "k_decode_bf16 (fused gate/up, Gemma-3-1B-shaped)"),
                "decode_gateup_large": (("k_decode_bf16",), "k_decode_bf16 (gate/up, large-decoder-shaped, M = 1)"),
                "prefill_gateup_large": (("k_gemm_bf16",), "k_gemm_bf16 (gate/up, large-decoder-shaped, M = 512)"),
