@@ -824,6 +824,8 @@ static const Cand kCands[] = {{128, 128, 64, 4, 4}, {256, 128, 32, 3, 4}, {256, 
 //   in three stages (QKV); otherwise 128 x 128 with 32-wide slices, two
 //   workgroups per CU, so that the rank-r pass tiles fit beside them in the
 //   same launch (fewer tiles: M = 1024 measured faster so);
+// * else, for K >= 8192 where 256 x 128 tiles K-split in S >= 2 ranges of
+//   >= 4096 fill at least 80% of the CUs in one round, those;
 // * else the cheapest of the four by the model; 128 x 128 splits long K
 //   (>= 4096) when its tiles cover at most half of the CUs (ranges >= 2048),
 //   else becomes 128 x 96 (four waves in a column) where those still fit in
@@ -860,7 +862,17 @@ TileCfg choose(const Recon &rq) {
       const double cost = (double)((t + e.slots - 1) / e.slots) * ((double)rq.K / 32.0 * step + e.epi_us);
       if (cost < best) best = cost, tc = e.tc;
     }
-    if (tc.BM == 128 && rq.K >= 4096 && 2 * t128 <= kNumCU) {
+    // Long K (>= 8192) with few 256 x 128 tiles: those tiles, K split so that
+    // the units fill at least 80% of the CUs in one round (ranges >= 4096):
+    // the large-decoder down at M = 512 (K = 21504, 84 tiles, S = 3) 146 us
+    // against 178 for one round of 240 unsplit 128 x 96 tiles (weights not in
+    // the Infinity Cache).
+    const int t256 = count_tiles(rq, 256, 128, false);
+    const int s256 = t256 > 0 ? kNumCU / t256 : 0, s256max = (int)(rq.K / 4096);
+    const int sl = s256 < s256max ? s256 : s256max;
+    if (rq.K >= 8192 && sl >= 2 && 10 * t256 * sl >= 8 * kNumCU) {
+      tc = {256, 128, 64, 3, sl, 4};
+    } else if (tc.BM == 128 && rq.K >= 4096 && 2 * t128 <= kNumCU) {
       const int S = kNumCU / t128, smax = (int)(rq.K / 2048);
       tc.S = S < smax ? S : smax;
     } else if (tc.BM == 128 && tc.BN == 128 && t128 < kNumCU && count_tiles(rq, 128, 96, false) <= kNumCU) {
