@@ -451,15 +451,28 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
   int Rs = 16, Ss = 1;
   double best_s = 1e30;
   const int smax = K / 256 > 1 ? (K / 256 < 16 ? K / 256 : 16) : 1;
-  for (int R = 8; R <= 16 * ngmax; ++R) {
-    const long t = tiles_of(R, true);
-    for (int sc = 1; sc <= smax; ++sc) {
-      const int kc = ((K + sc - 1) / sc + 127) / 128 * 128;
-      const int sr = (K + kc - 1) / kc;
-      if (sr != sc) continue;
-      const double c = rounds(t * sr) * (kUnit + (double)R * kc * 2.0 / kRate) + kComb;
-      if (c < best_s - 1e-9) { best_s = c; Rs = R; Ss = sr; }
+  auto search_split = [&](int smin) {
+    for (int R = 8; R <= 16 * ngmax; ++R) {
+      const long t = tiles_of(R, true);
+      for (int sc = smin; sc <= smax; ++sc) {
+        const int kc = ((K + sc - 1) / sc + 127) / 128 * 128;
+        const int sr = (K + kc - 1) / kc;
+        if (sr != sc) continue;
+        const double c = rounds(t * sr) * (kUnit + (double)R * kc * 2.0 / kRate) + kComb;
+        if (c < best_s - 1e-9) { best_s = c; Rs = R; Ss = sr; }
+      }
     }
+  };
+  search_split(1);
+  // One token, K unsplit over more than two rounds of units: the model's
+  // rounds are synchronous, but the units are not, and shorter ones (K in
+  // three or more ranges) let the CUs that stream faster take more of them --
+  // the large-decoder gate/up (2 x 21504 x 5376) 81 us against 91 with the
+  // model's 757 unsplit units of 57 rows (weights beyond the Infinity Cache).
+  // At 16 and 32 tokens the unsplit plans measured best.
+  if (pl->MT == 1 && Ss == 1 && tiles_of(Rs, true) > 2L * kNumCU && smax >= 3) {
+    best_s = 1e30;
+    search_split(3);
   }
   bool split = best_s < best_f;
 
