@@ -332,19 +332,17 @@ __global__ __launch_bounds__(256) void k_decode_combine(const CombArgs a) {
   const size_t pstride = (size_t)a.M * a.Wp;
   const float *row = a.part + (size_t)m * a.Wp;
 
-  // This thread's s and (for r <= 16) U row are requested together with the
+  // This thread's s and (for r <= 32) U row are requested together with the
   // partials, before the barrier, so that the kernel waits for memory once.
   const int n = (chunk - B.chunk0) * 256 + tid;
   const bool live = n < B.N;
   const int nc = live ? n : B.N - 1;
   const uint16_t s_raw = B.s[nc];
   const uint16_t *u = B.U + (size_t)nc * r;
-  const bool upre = B.ufast && r <= 16;
-  uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
-  if (upre && r > 0) {
-    u0 = ld16(u);
-    if (r > 8) u1 = ld16(u + 8);
-  }
+  const bool upre = B.ufast && r <= 32;
+  uint4 ur[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ur[q] = (upre && 8 * q < r) ? ld16(u + 8 * q) : make_uint4(0, 0, 0, 0);
   // The partials of this thread's column (z) and, for threads below r, of one
   // rank (t) are requested eight splits at a time, both before either is
   // added up (in split order): one memory round trip per eight splits, not one
@@ -379,15 +377,19 @@ __global__ __launch_bounds__(256) void k_decode_combine(const CombArgs a) {
   const float sn = bf2f(s_raw);
   float lr = 0.f;
   if (upre) {
-    const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    // r is a multiple of 8 here: whole float4s of T, terms in rank order.
+    const uint32_t w16[16] = {ur[0].x, ur[0].y, ur[0].z, ur[0].w, ur[1].x, ur[1].y, ur[1].z, ur[1].w,
+                              ur[2].x, ur[2].y, ur[2].z, ur[2].w, ur[3].x, ur[3].y, ur[3].z, ur[3].w};
     const float4 *t4 = reinterpret_cast<const float4 *>(T);
-    const float4 q0 = t4[0], q1 = t4[1], q2 = t4[2], q3 = t4[3];
-    const float tv[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
-                          q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float term = bf2f((uint16_t)(w8[j >> 1] >> ((j & 1) * 16))) * tv[j];
-      lr += j < r ? term : 0.f;
+    for (int q = 0; q < 8; ++q) {
+      if (4 * q < r) {
+        const float4 t = t4[q];
+        lr += bf2f((uint16_t)w16[2 * q]) * t.x;
+        lr += bf2f((uint16_t)(w16[2 * q] >> 16)) * t.y;
+        lr += bf2f((uint16_t)w16[2 * q + 1]) * t.z;
+        lr += bf2f((uint16_t)(w16[2 * q + 1] >> 16)) * t.w;
+      }
     }
   } else if (B.ufast) {
     for (int j0 = 0; j0 < r; j0 += 8) {
@@ -451,8 +453,16 @@ bool plan_decode(const Recon &rq, DecodePlan *pl) {
   int Rs = 16, Ss = 1;
   double best_s = 1e30;
   const int smax = K / 256 > 1 ? (K / 256 < 16 ? K / 256 : 16) : 1;
+  // A workgroup with four or more 16-row groups streams faster than one with
+  // fewer (more rows' loads in flight per wave), which the model, linear in
+  // rows, does not see.  Where there are at least 64 tiles of 64 rows, the
+  // split search takes only such tiles: on the large-decoder QKV, 27.3 us
+  // (67 rows, K in two) against 29.9 (three groups) at 32 tokens, and o 14.8
+  // against 16.1 at one.  Fewer tiles than that (the Gemma-3-1B QKV, o, down)
+  // would need very short K ranges to fill the CUs, which measured slower.
+  const int rlo = (ngmax >= 4 && tiles_of(64, true) >= 64) ? 49 : 8;
   auto search_split = [&](int smin) {
-    for (int R = 8; R <= 16 * ngmax; ++R) {
+    for (int R = rlo; R <= 16 * ngmax; ++R) {
       const long t = tiles_of(R, true);
       for (int sc = smin; sc <= smax; ++sc) {
         const int kc = ((K + sc - 1) / sc + 127) / 128 * 128;
