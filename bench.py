@@ -1139,13 +1139,17 @@ def run_decompose(args, torch, B, I, nested=False):
                        "q = 2, fp64)", "per_projection": res, "ms_per_layer": _r(total_ms, 3)}
     if not args.no_cpu_baseline:
         import oracle
-        K, N = I.GEMMA_1B["q"]
-        Wn = I.trained_weight("decompose", 0, "q", K, N, "bf16", waves=32).astype(np.float64)
-        W0n = I.bundle("decompose", 0, "q", K, N, 0, "bf16")["W0"].astype(np.float64)
-        omn = I.gaussian_probe("decompose", 7, B.probe_width(N, K, r), K)
-        t0 = time.perf_counter()
-        oracle.decompose_randomized(Wn, W0n, r, omn, q)
-        out["cpu_baseline_q_proj_ms"] = _r((time.perf_counter() - t0) * 1e3, 1)
+        for fam in ("q", "k"):         # the randomized branch, and the full SVD (min(N, K) = 256)
+            K, N = I.GEMMA_1B[fam]
+            Wn = I.trained_weight("decompose", 0, fam, K, N, "bf16", waves=32).astype(np.float64)
+            W0n = I.bundle("decompose", 0, fam, K, N, 0, "bf16")["W0"].astype(np.float64)
+            omn = I.gaussian_probe("decompose", 7, B.probe_width(N, K, r), K)
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                oracle.decompose_randomized(Wn, W0n, r, omn, q)
+                ts.append((time.perf_counter() - t0) * 1e3)
+            out[f"cpu_baseline_{fam}_proj_ms"] = _r(float(np.median(ts)), 1)
         out["cpu_baseline_blas"] = blas_info()
     return out
 
