@@ -167,6 +167,21 @@ def test_decode_high_rank_split(M, r):
     assert_parity(down(y), oracle.recon_linear(x, *bundle_np(bd)), "bf16", f"r={r} M={M}")
 
 
+@pytest.mark.parametrize("M,S", [(33, 1), (33, 3), (64, 2), (9, 1)])
+def test_decode_combine_token_groups(M, S, force_plan):
+    """Split mode on a wide gate/up pair (the combine launches more than 2048
+    workgroups of one token each), K in one or more ranges, token counts off
+    the 16-token groups of the streaming kernel (33, 9)."""
+    force_plan("DECODE_SPLIT", 1)
+    force_plan("DECODE_S", S)
+    K = 768
+    bds = [I.bundle("test", 10, f, K, 9000, 32, "bf16", variant="s0" if f == "up" else "normal")
+           for f in ("gate", "up")]
+    x = I.activations("test", 1200 + M + S, M, K, "bf16")
+    y = B.recon_gateup(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
+    assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in bds]), "bf16", f"M={M} S={S}")
+
+
 # The tiled kernel: every compiled tile shape (BM x BN output, BK-wide K slices
 # through NST LDS stages), forced K splits of the main pass and of the rank-r
 # pass, on ragged M, N and K (K = 1048 leaves a partial last K slice; N = 200,
