@@ -366,8 +366,9 @@ const char *aq_last_error(void);
  * makes the awaited count one more than will arrive, so that a test can make
  * the wait give up from the host while every kernel still exits normally.
  * AQ_DBG_JACOBI picks the eigensolver (1: one workgroup with both matrices in
- * LDS, taken only where l <= 96; 2: the many-workgroup one) and
- * AQ_DBG_JACOBI_WGS the latter's workgroups (1 to 64).
+ * LDS, taken only where l <= 96; 2: the scalar many-workgroup one; 3: the
+ * block one, the default above l = 96) and AQ_DBG_JACOBI_WGS the scalar
+ * many-workgroup one's workgroups (1 to 64).
  * aq_debug_force_plan returns AQ_ERR_INVALID_ARG for an unknown knob. */
 typedef enum aq_debug_knob {
   AQ_DBG_DECODE_SPLIT = 0, AQ_DBG_DECODE_NG, AQ_DBG_DECODE_ROWS, AQ_DBG_DECODE_S, AQ_DBG_DECODE_WAVES,

@@ -131,6 +131,8 @@ struct DecompPlan {
   int srt, sgram;              // N ranges of R^T Q; ranges of the Gram sums
   long nchunk;                 // rows per N range
   int jac_wgs;                 // workgroups of the grid Jacobi (0: the one-workgroup LDS kernel)
+  int jac_block;               // 1: the block Jacobi instead (jac_wgs workgroups, n padded to jac_n)
+  int jac_n;
   int jac_spin, jac_extra;     // its barrier's poll bound; arrivals awaited beyond the grid's
   size_t o_y1, o_y2, o_z1, o_z2, o_zp, o_yp, o_gp, o_g, o_rinv, o_scr, o_jac, o_ctr, o_lam, o_wu, o_wv;   // byte offsets
 };

@@ -638,26 +638,29 @@ __device__ __forceinline__ void store_coherent(double *p, double v) {
 // workgroup, a bounded poll, an acquire at agent scope.  A workgroup whose
 // poll runs out sets bit kGridAbort (which releases every other waiter at
 // once) and the flag word; false from then on, in every workgroup.
-__device__ bool grid_barrier(const JacobiGrid &a, unsigned target, int *s_ok) {
+__device__ bool grid_barrier(unsigned *ctr, unsigned *flag, int spin, unsigned target, int *s_ok) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(a.ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned v = __hip_atomic_load(a.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int it = 0; v < target && it < a.spin; ++it) {
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int it = 0; v < target && it < spin; ++it) {
       __builtin_amdgcn_s_sleep(1);
-      v = __hip_atomic_load(a.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     bool ok = v >= target && v < kGridAbort;
     if (v < target) {
-      __hip_atomic_fetch_or(a.ctr, kGridAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_or(a.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(ctr, kGridAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *s_ok = ok;
   }
   __syncthreads();
   return *s_ok != 0;
+}
+__device__ __forceinline__ bool grid_barrier(const JacobiGrid &a, unsigned target, int *s_ok) {
+  return grid_barrier(a.ctr, a.flag, a.spin, target, s_ok);
 }
 
 __global__ __launch_bounds__(256) void k_jacobi_grid(const JacobiGrid a) {
@@ -763,6 +766,213 @@ __global__ __launch_bounds__(256) void k_jacobi_grid(const JacobiGrid a) {
                       a.Wv);
 }
 
+// Block Jacobi, for 96 < l <= 256 (the default there): the index range, padded
+// to n = 64 ceil(l / 64) with zero rows and columns (which no rotation ever
+// touches: their off-diagonal entries stay exactly zero), is cut into blocks
+// of 32; a round pairs the blocks round-robin (block 0 fixed, the others
+// moving one place per round) into nsets = n / 64 sets of 64 indices.  Phase
+// A: workgroup k runs one cyclic Jacobi sweep (the rotations of jacobi_angle,
+// round-robin pairs, 63 rounds) on the 64 x 64 submatrix G[I_k, I_k] in LDS
+// and accumulates its rotations into J_k (J <- J R, the update of V).
+// Phase B: G[I_k, I_m] <- J_k^T G[I_k, I_m] J_m for every pair of sets and
+// V[:, I_k] <- V[:, I_k] J_k, one 64 x 64 block per workgroup.  A sweep is the
+// nb - 1 rounds in which every pair of blocks meets once; sweeps repeat until
+// no rotation of a sweep met an off-diagonal entry above the bound (the
+// scalar one, and an absolute floor below), at most 40.  Two grid barriers
+// per round (instead of one per scalar round).
+struct JacobiBlock {
+  const double *Gin;
+  int l, r, n;              // n: the padded size (a multiple of 64, at most 256)
+  double *G, *V, *J;        // G, V: [n][n] (V[a][i]: coordinate a of eigenvector i); J: [nsets][64][64]
+  unsigned *ctr;            // ctr[0]: barrier arrivals; ctr[1 + s % 3]: a rotation of sweep s was big
+  unsigned *flag;
+  int spin, extra;
+  double *lam_out, *Wu, *Wv;
+};
+
+// LDS layouts: the phase-A submatrix with rows of 65 doubles (rows of a
+// rotation pair fall in different banks) and J transposed (the columns p, q
+// that a rotation updates are contiguous rows).  1024 threads: one 2 x 2 block
+// of the submatrix and two entries of J per thread per scalar round, a 2 x 2
+// output tile per thread in the block products.
+constexpr int kJbA = 65;
+__global__ __launch_bounds__(1024) void k_jacobi_block(const JacobiBlock a) {
+  __shared__ __attribute__((aligned(16))) double A[64 * kJbA];
+  __shared__ __attribute__((aligned(16))) double B1[64 * 64];
+  __shared__ __attribute__((aligned(16))) double B2[64 * 64];
+  __shared__ double cs[32], sn[32];
+  __shared__ int pp[32], qq[32];
+  __shared__ int s_big, s_ok;
+  __shared__ double s_floor;
+  __shared__ double lam[kDecompMaxL];
+  __shared__ int rank_of[kDecompMaxL];
+  const int l = a.l, n = a.n, nb = n / 32, nsets = nb / 2;
+  const int tid = threadIdx.x, wg = blockIdx.x, nwg = gridDim.x;
+  const int gt = wg * 1024 + tid, gs = nwg * 1024;
+  for (int e = gt; e < n * n; e += gs) {
+    const int x = e / n, y = e - x * n;
+    store_coherent(a.G + e, x < l && y < l ? a.Gin[(size_t)x * l + y] : 0.0);
+    store_coherent(a.V + e, x == y ? 1.0 : 0.0);
+  }
+  // The block updates recompute every entry as a 64-term sum, which leaves an
+  // absolute error of order eps max|G| on each: an off-diagonal entry counts
+  // as big only above 2^-43 (~1.1e-13) of the largest diagonal entry as well,
+  // so that entries between two small eigenvalues, held at that noise level,
+  // do not keep the sweeps going to their bound.
+  if (tid < 64) {
+    double m = 0.0;
+    for (int i = tid; i < l; i += 64) m = fmax(m, fabs(a.Gin[(size_t)i * l + i]));
+    for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+    if (tid == 0) s_floor = 0x1p-43 * m;
+  }
+  unsigned passed = 1;
+  bool ok = grid_barrier(a.ctr, a.flag, a.spin, passed * nwg + a.extra, &s_ok);
+  const double floor_big = s_floor;
+  // this thread's 2 x 2 output tile of a 64 x 64 block product
+  const int ti = tid >> 5, tj = tid & 31;
+  for (int sweep = 0; ok && sweep < 40; ++sweep) {
+    if (wg == 0 && tid == 0)   // last read at the end of sweep - 2
+      __hip_atomic_store(a.ctr + 1 + (sweep + 1) % 3, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int round = 0; ok && round < nb - 1; ++round) {
+      auto bplayer = [&](int x) { return x == 0 ? 0 : ((x - 1 + round) % (nb - 1)) + 1; };
+      // global index of local index i (0..63) of set k
+      auto gidx = [&](int k, int i) { return i < 32 ? 32 * bplayer(k) + i : 32 * bplayer(nb - 1 - k) + i - 32; };
+      if (wg < nsets) {   // ---- phase A: one sweep on G[I_k, I_k]
+        const int k = wg;
+        for (int e = tid; e < 64 * 64; e += 1024) {
+          const int i = e >> 6, j = e & 63;
+          A[i * kJbA + j] = a.G[(size_t)gidx(k, i) * n + gidx(k, j)];
+          B1[e] = i == j ? 1.0 : 0.0;   // J^T
+        }
+        if (tid == 0) s_big = 0;
+        __syncthreads();
+        // this thread's 2 x 2 block (pair rows bi, pair columns bj) and its
+        // two entries of J (pair vi, row x)
+        const int bi = tid >> 5, bj = tid & 31, vi = tid >> 5, vx = (tid & 31) * 2;
+        for (int rr = 0; rr < 63; ++rr) {
+          if (tid < 32) {
+            auto player = [&](int x) { return x == 0 ? 0 : ((x - 1 + rr) % 63) + 1; };
+            int p = player(tid), q = player(63 - tid);
+            if (p > q) {
+              const int t = p;
+              p = q;
+              q = t;
+            }
+            double c, s;
+            bool big;
+            const double gpq = A[p * kJbA + q];
+            jacobi_angle(A[p * kJbA + p], A[q * kJbA + q], gpq, c, s, big);
+            if (big && fabs(gpq) > floor_big) s_big = 1;
+            cs[tid] = c;
+            sn[tid] = s;
+            pp[tid] = p;
+            qq[tid] = q;
+          }
+          __syncthreads();
+          {
+            const int pi = pp[bi], qi = qq[bi], pj = pp[bj], qj = qq[bj];
+            double a00 = A[pi * kJbA + pj], a01 = A[pi * kJbA + qj], a10 = A[qi * kJbA + pj],
+                   a11 = A[qi * kJbA + qj];
+            rot_block(a00, a01, a10, a11, cs[bi], sn[bi], cs[bj], sn[bj]);
+            A[pi * kJbA + pj] = a00;
+            A[pi * kJbA + qj] = a01;
+            A[qi * kJbA + pj] = a10;
+            A[qi * kJbA + qj] = a11;
+          }
+          {   // J <- J R: columns p, q of J, i.e. rows p, q of J^T
+            const int p = pp[vi], q = qq[vi];
+            const double c = cs[vi], s = sn[vi];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const double vp = B1[p * 64 + vx + u], vq = B1[q * 64 + vx + u];
+              B1[p * 64 + vx + u] = c * vp - s * vq;
+              B1[q * 64 + vx + u] = s * vp + c * vq;
+            }
+          }
+          __syncthreads();
+        }
+        for (int e = tid; e < 64 * 64; e += 1024) {   // J[x][i] = J^T[i][x]
+          const int i = e >> 6, x = e & 63;
+          store_coherent(a.J + (size_t)k * 4096 + x * 64 + i, B1[e]);
+        }
+        if (tid == 0 && s_big)
+          __hip_atomic_fetch_or(a.ctr + 1 + sweep % 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      ++passed;
+      ok = grid_barrier(a.ctr, a.flag, a.spin, passed * nwg + a.extra, &s_ok);
+      if (!ok) break;
+      // ---- phase B: one 64 x 64 block per workgroup (row stride 64 in LDS)
+      const bool gtask = wg < nsets * nsets, vtask = !gtask && wg < 2 * nsets * nsets;
+      if (gtask || vtask) {
+        const int t = gtask ? wg : wg - nsets * nsets, k = t / nsets, m = t - k * nsets;
+        // G task (k, m): A = G[I_k, I_m]; V task (k, c = m): A = V[rows 64 c .., I_k]
+        for (int e = tid; e < 64 * 64; e += 1024) {
+          const int i = e >> 6, j = e & 63;
+          A[e] = gtask ? a.G[(size_t)gidx(k, i) * n + gidx(m, j)] : a.V[(size_t)(64 * m + i) * n + gidx(k, j)];
+          B1[e] = a.J[(size_t)k * 4096 + e];
+          if (gtask) B2[e] = a.J[(size_t)m * 4096 + e];
+        }
+        __syncthreads();
+        double acc[2][2];
+        auto product = [&](const double *L, bool ltrans, const double *Rm) {
+          // acc = op(L) Rm over this thread's tile, op(L) = L^T where ltrans
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int v = 0; v < 2; ++v) acc[u][v] = 0.0;
+          for (int x = 0; x < 64; ++x) {
+            double lv[2], rv[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) lv[u] = ltrans ? L[x * 64 + 2 * ti + u] : L[(2 * ti + u) * 64 + x];
+#pragma unroll
+            for (int v = 0; v < 2; ++v) rv[v] = Rm[x * 64 + 2 * tj + v];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int v = 0; v < 2; ++v) acc[u][v] = __builtin_fma(lv[u], rv[v], acc[u][v]);
+          }
+        };
+        if (gtask) {
+          product(B1, true, A);               // T = J_k^T A
+          __syncthreads();
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int v = 0; v < 2; ++v) A[(2 * ti + u) * 64 + 2 * tj + v] = acc[u][v];
+          __syncthreads();
+          product(A, false, B2);              // T J_m
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int v = 0; v < 2; ++v)
+              store_coherent(a.G + (size_t)gidx(k, 2 * ti + u) * n + gidx(m, 2 * tj + v), acc[u][v]);
+        } else {
+          product(A, false, B1);              // V[rows, I_k] J_k
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int v = 0; v < 2; ++v)
+              store_coherent(a.V + (size_t)(64 * m + 2 * ti + u) * n + gidx(k, 2 * tj + v), acc[u][v]);
+        }
+      }
+      ++passed;
+      ok = grid_barrier(a.ctr, a.flag, a.spin, passed * nwg + a.extra, &s_ok);
+    }
+    if (!ok) break;
+    if (__hip_atomic_load(a.ctr + 1 + sweep % 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) break;
+  }
+  if (wg != 0) return;
+  if (!ok) {   // a barrier gave up: no valid result
+    for (int idx = tid; idx < l * a.r; idx += 1024) a.Wu[idx] = a.Wv[idx] = __builtin_nan("");
+    for (int i = tid; i < l; i += 1024) a.lam_out[i] = __builtin_nan("");
+    return;
+  }
+  for (int i = tid; i < n; i += 1024) lam[i] = i < l ? a.G[(size_t)i * n + i] : -INFINITY;
+  __syncthreads();
+  jacobi_outputs<1024>(l, n, a.r, lam, rank_of, [&](int x, int i) { return a.V[(size_t)x * n + i]; }, a.lam_out,
+                       a.Wu, a.Wv);
+}
+
 // Q = I as [l = N][N]
 __global__ __launch_bounds__(256) void k_eye(double *Y, long N) {
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < N * N; i += (long)gridDim.x * 256)
@@ -803,15 +1013,19 @@ size_t decompose_ws_bytes(int64_t N, int64_t K, int64_t r, int64_t l, DecompPlan
   sg = sg < 128 ? sg : 128;
   pl->sgram = (int)(sg > 1 ? sg : 1);
   // the eigendecomposition: one workgroup with G and V in LDS where they fit
-  // (n <= 96), else the grid version (kJacGridMaxWgs workgroups at most)
+  // (n <= 96), else the block Jacobi (2 nsets^2 workgroups); the scalar grid
+  // version (kJacGridMaxWgs workgroups at most) on request
   const int n = (int)(l + (l & 1));
   const int jk = debug_knob(AQ_DBG_JACOBI, 0);
-  const bool lds = jk == 1 ? two_fit(n) : (jk == 2 ? false : two_fit(n));
-  // one 2 x 2 block of G per thread (and at most two entries of V), at most
-  // kJacGridMaxWgs workgroups (n = 256)
+  const bool lds = jk == 1 ? two_fit(n) : (jk == 2 || jk == 3 ? false : two_fit(n));
+  pl->jac_block = !lds && jk != 2;
+  pl->jac_n = (int)((l + 63) / 64 * 64);
+  // grid version: one 2 x 2 block of G per thread (and at most two entries of
+  // V), at most kJacGridMaxWgs workgroups (n = 256)
   const int np = n / 2, wdef = (np * np + 255) / 256;
   const int wk = debug_knob(AQ_DBG_JACOBI_WGS, wdef);
-  pl->jac_wgs = lds ? 0 : (wk >= 1 && wk <= kJacGridMaxWgs ? wk : wdef);
+  const int nsets = pl->jac_n / 64;
+  pl->jac_wgs = lds ? 0 : (pl->jac_block ? 2 * nsets * nsets : (wk >= 1 && wk <= kJacGridMaxWgs ? wk : wdef));
   pl->jac_spin = debug_knob(AQ_DBG_HANDOFF_SPIN, kHandoffSpin);
   pl->jac_extra = debug_knob(AQ_DBG_HANDOFF_UNREACHABLE, 0) ? 1 : 0;
   // after the reserved region: its counter words belong to the recon calls
@@ -832,8 +1046,11 @@ size_t decompose_ws_bytes(int64_t N, int64_t K, int64_t r, int64_t l, DecompPlan
   pl->o_g = take((size_t)l * l);
   pl->o_rinv = take((size_t)l * l);
   pl->o_scr = take((size_t)l * l);
-  pl->o_jac = take(4 * (size_t)n * n);   // the grid Jacobi's two copies of G and of V
-  pl->o_ctr = take(32);              // its barrier counter
+  // the grid Jacobi's two copies of G and of V, or the block Jacobi's G, V and J
+  const size_t jn = (size_t)pl->jac_n;
+  const size_t jgrid = 4 * (size_t)n * n, jblock = 2 * jn * jn + (size_t)nsets * 4096;
+  pl->o_jac = take(jgrid > jblock ? jgrid : jblock);
+  pl->o_ctr = take(32);              // barrier counter (and the block version's sweep flags)
   pl->o_lam = take((size_t)l);
   pl->o_wu = take((size_t)l * (r > 0 ? r : 1));
   pl->o_wv = take((size_t)l * (r > 0 ? r : 1));
@@ -917,6 +1134,26 @@ static void run_decompose_t(const DecompArgs &d, const DecompPlan &pl, char *ws,
   gram(Z1, K);                       // B B^T
   if (pl.jac_wgs == 0) {
     hipLaunchKernelGGL(k_jacobi_lds, dim3(1), dim3(1024), 0, st, (const double *)G, l, r, lam, Wu, Wv);
+  } else if (pl.jac_block) {
+    const size_t jn = (size_t)pl.jac_n;
+    double *jac = (double *)(ws + pl.o_jac);
+    JacobiBlock jb{};
+    jb.Gin = G;
+    jb.l = l;
+    jb.r = r;
+    jb.n = pl.jac_n;
+    jb.G = jac;
+    jb.V = jac + jn * jn;
+    jb.J = jac + 2 * jn * jn;
+    jb.ctr = (unsigned *)(ws + pl.o_ctr);
+    jb.flag = (unsigned *)ws + kSyncFlag;
+    jb.spin = pl.jac_spin;
+    jb.extra = pl.jac_extra;
+    jb.lam_out = lam;
+    jb.Wu = Wu;
+    jb.Wv = Wv;
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, st, jb.ctr, 4);
+    hipLaunchKernelGGL(k_jacobi_block, dim3((unsigned)pl.jac_wgs), dim3(1024), 0, st, jb);
   } else {
     const size_t n2 = (size_t)(l + (l & 1)) * (l + (l & 1));
     double *jac = (double *)(ws + pl.o_jac);

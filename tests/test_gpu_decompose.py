@@ -192,16 +192,21 @@ def test_decompose_refusals():
     (300, 520, 8, 11, 1, 0),      # l = 19 in LDS
     (95, 300, 5, 10, 0, 0),       # l = N = 95: Q = I, the largest odd l in LDS
     (95, 300, 5, 10, 2, 5),       # the same on the grid
-    (97, 400, 6, 10, 0, 0),       # l = N = 97: the grid by default (odd)
-    (97, 400, 6, 10, 0, 3),
+    (97, 400, 6, 10, 0, 0),       # l = N = 97: the block solver by default (odd, padded to 128)
+    (97, 400, 6, 10, 2, 3),       # the scalar grid solver on three workgroups
     (500, 128, 8, 10, 0, 0),      # l = K = 128: no subspace steps, the packed Cholesky at its limit
-    (600, 150, 8, 10, 0, 0),      # l = K = 150: the Cholesky in global memory
+    (600, 150, 8, 10, 0, 0),      # l = K = 150: the Cholesky in global memory (block solver, 192)
+    (150, 500, 12, 10, 2, 0),     # l = N = 150 on the scalar grid solver
+    (256, 700, 16, 10, 0, 0),     # l = N = 256: the block solver at its largest (four sets of 64)
     (400, 600, 40, 10, 0, 0),     # l = 50: the 64-wide contraction tiles
+    (400, 600, 40, 10, 3, 0),     # l = 50 on the block solver (one set: n padded to 64)
+    (300, 520, 8, 11, 3, 0),      # l = 19 on the block solver
 ])
 def test_decompose_eigensolvers(N, K, r, oversample, jac, wgs, force_plan):
-    """Both Jacobi eigensolvers (one workgroup with G and V in LDS; many
-    workgroups over global memory with a grid barrier per round) at odd and
-    even l, several grid sizes, and both Cholesky kernels."""
+    """The three Jacobi eigensolvers (one workgroup with G and V in LDS; the
+    scalar one over many workgroups with a grid barrier per round; the block
+    one, 64 x 64 subproblems in LDS and block updates between grid barriers)
+    at odd and even l, several grid sizes, and both Cholesky kernels."""
     if jac:
         force_plan("JACOBI", jac)
     if wgs:
@@ -210,11 +215,15 @@ def test_decompose_eigensolvers(N, K, r, oversample, jac, wgs, force_plan):
     _check(N, K, r, 2, W, W0, "f32", f"{N}x{K} r={r} p={oversample} jacobi={jac} wgs={wgs}", oversample)
 
 
-def test_decompose_grid_give_up_reported(force_plan):
-    """A grid barrier of the many-workgroup eigensolver that gives up (forced
-    from the host: one more arrival awaited than will come, 64 polls): every
-    workgroup exits, U and Vt are NaN, and the workspace check reports it
-    (and clears it); the next call on that workspace is valid."""
+@pytest.mark.parametrize("jac", [0, 2])
+def test_decompose_grid_give_up_reported(jac, force_plan):
+    """A grid barrier of the many-workgroup eigensolvers (block: the default
+    at l = 200; scalar) that gives up (forced from the host: one more arrival
+    awaited than will come, 64 polls): every workgroup exits, U and Vt are
+    NaN, and the workspace check reports it (and clears it); the next call on
+    that workspace is valid."""
+    if jac:
+        force_plan("JACOBI", jac)
     N, K, r = 200, 264, 6
     W, W0 = _weights(N, K, r, 8, "f32")
     Wd, W0d = _dev(W, torch.float32), _dev(W0, torch.float32)
@@ -228,6 +237,8 @@ def test_decompose_grid_give_up_reported(force_plan):
         ws.check()
     assert e.value.status == B.AQ_ERR_HANDOFF, e.value
     B.aq_debug_reset_plan()
+    if jac:
+        force_plan("JACOBI", jac)
     s, U, Vt = B.decompose(Wd, W0d, r, om, q=1, workspace=ws)
     ws.check()
     so, Uo, Vto, _ = oracle.decompose_randomized(W, W0, r, np.zeros((N, K)), 1)
