@@ -121,10 +121,11 @@ def test_decompose_passthrough_and_rank_deficient():
     _check(N, K, 8, 1, Wd, W0, "f32", "rank 3")
 
 
-@pytest.mark.parametrize("fam,r", [("q", 16), ("gate", 64), ("down", 64)])
+@pytest.mark.parametrize("fam,r", [("q", 16), ("gate", 64), ("down", 64), ("k", 64)])
 def test_decompose_gemma_shapes(fam, r):
     """Gemma-3-1B-shaped projections (bf16): q 1152 -> 1024 at rank 16, gate
-    1152 -> 6912 and down 6912 -> 1152 at rank 64."""
+    1152 -> 6912 and down 6912 -> 1152 at rank 64, and k 1152 -> 256 at rank
+    64 (min(N, K) = 256: the full SVD, l = N, on the block eigensolver)."""
     K, N = I.GEMMA_1B[fam]
     W, W0 = _weights(N, K, r, 5, "bf16", family=fam)
     _check(N, K, r, 2, W, W0, "bf16", f"{fam} r={r}")
