@@ -202,6 +202,9 @@ def test_decompose_refusals():
     (400, 600, 40, 10, 0, 0),     # l = 50: the 64-wide contraction tiles
     (400, 600, 40, 10, 3, 0),     # l = 50 on the block solver (one set: n padded to 64)
     (300, 520, 8, 11, 3, 0),      # l = 19 on the block solver
+    (129, 400, 5, 10, 0, 0),      # l = N = 129: padded to 192 (63 zero rows), three sets
+    (193, 400, 7, 10, 0, 0),      # l = N = 193: padded to 256
+    (96, 300, 5, 10, 3, 0),       # l = N = 96 forced onto the block solver (padded to 128)
 ])
 def test_decompose_eigensolvers(N, K, r, oversample, jac, wgs, force_plan):
     """The three Jacobi eigensolvers (one workgroup with G and V in LDS; the
