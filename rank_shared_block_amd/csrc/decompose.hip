@@ -34,11 +34,14 @@
 //   dropped (zeroed) instead of divided by zero;
 // * k_chol_inv: Cholesky and the triangular inverse in one workgroup, both
 //   triangles packed in LDS (k_chol_inv_global above l = 128);
-// * k_jacobi_lds / k_jacobi_grid: the symmetric eigendecomposition of B B^T
-//   (l x l) by cyclic Jacobi, rotations of disjoint pairs in parallel
-//   (round-robin ordering), sorted descending; S = sqrt of the eigenvalues.
-//   One workgroup with G and V in LDS up to l = 96; above, many workgroups
-//   over global memory with one grid barrier per round.
+// * k_jacobi_lds / k_jacobi_block / k_jacobi_grid: the symmetric
+//   eigendecomposition of B B^T (l x l) by cyclic Jacobi, rotations of
+//   disjoint pairs in parallel (round-robin ordering), sorted descending;
+//   S = sqrt of the eigenvalues.  One workgroup with G and V in LDS up to
+//   l = 96; above, the block version (64 x 64 subproblems in LDS, block
+//   updates of G and V in global memory, two grid barriers per round of
+//   block pairs); the scalar version over many workgroups (one grid barrier
+//   per round of index pairs) on request.
 // Where l = N (the full SVD of a matrix with at most as many rows as
 // columns), Q = I and B = R; where l = K the subspace steps are skipped (the
 // first basis already spans R's range).
