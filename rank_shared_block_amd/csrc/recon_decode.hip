@@ -404,6 +404,103 @@ __global__ __launch_bounds__(256) void k_decode_combine(const CombArgs a) {
   a.y[(size_t)m * a.ldy + B.col + n] = f2bf(sn * z + lr);
 }
 
+// The combine for launches that would need more than 2048 one-token
+// workgroups (the large-decoder gate/up at 32 tokens: 168 chunks x 32 tokens,
+// each re-reading its 256 U rows from L2): workgroup (chunk, g) takes tokens
+// 4 g .. 4 g + 3, so each U row is read a quarter as often.  The partials go
+// through one buffer resource, the token and split in the uniform scalar
+// offset, so the loads of every token share one address register (with
+// 64-bit addresses per load the kernel ran at two waves per SIMD and lost).
+// Same sums in the same order as k_decode_combine.
+__global__ __launch_bounds__(256) void k_decode_combine4(const CombArgs a) {
+  constexpr int TG = 4;
+  __shared__ __attribute__((aligned(16))) float T[TG][AQ_MAX_RANK];
+  const int chunk = blockIdx.x, m0 = blockIdx.y * TG, tid = threadIdx.x;
+  int bi = 0;
+  if (a.nblk > 1 && chunk >= a.b[1].chunk0) bi = 1;
+  if (a.nblk > 2 && chunk >= a.b[2].chunk0) bi = 2;
+  const CombBlk B = bi == 0 ? a.b[0] : (bi == 1 ? a.b[1] : a.b[2]);
+  const int r = B.r, S = a.S, M = a.M, Wp = a.Wp;
+  const int n = (chunk - B.chunk0) * 256 + tid;
+  const bool live = n < B.N;
+  const int nc = live ? n : B.N - 1;
+  const uint16_t s_raw = B.s[nc];
+  const uint16_t *u = B.U + (size_t)nc * r;
+  const bool upre = B.ufast && r <= 32;
+  uint4 ur[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ur[q] = (upre && 8 * q < r) ? ld16(u + 8 * q) : make_uint4(0, 0, 0, 0);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.part, (uint32_t)((size_t)S * M * Wp * 4));
+  const int vz = (B.col + nc) * 4, vt = (B.tcol + (tid < r ? tid : 0)) * 4;
+  const bool has_t = tid < r;
+  float z[TG], tj[TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) z[t] = tj[t] = 0.f;
+  for (int q0 = 0; q0 < S; q0 += 4) {
+    float zv[TG][4], tv[TG][4];
+#pragma unroll
+    for (int t = 0; t < TG; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = m0 + t < M && q0 + e < S;
+        const int so = in ? ((q0 + e) * M + m0 + t) * Wp * 4 : 0;
+        zv[t][e] = in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, vz, so, 0)) : 0.f;
+        tv[t][e] = in && has_t ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, vt, so, 0)) : 0.f;
+      }
+#pragma unroll
+    for (int t = 0; t < TG; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (q0 + e < S) {
+          z[t] += zv[t][e];
+          tj[t] += tv[t][e];
+        }
+  }
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    if (has_t) T[t][tid] = tj[t];
+    for (int j = tid + 256; j < r && m0 + t < M; j += 256) {   // ranks past 256 threads (not reached for r <= 256)
+      float v = 0.f;
+      for (int q = 0; q < S; ++q) v += a.part[((size_t)q * M + m0 + t) * Wp + B.tcol + j];
+      T[t][j] = v;
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+  const float sn = bf2f(s_raw);
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    const int m = m0 + t;
+    if (m >= M) break;
+    float lr = 0.f;
+    if (upre) {
+      const uint32_t w16[16] = {ur[0].x, ur[0].y, ur[0].z, ur[0].w, ur[1].x, ur[1].y, ur[1].z, ur[1].w,
+                                ur[2].x, ur[2].y, ur[2].z, ur[2].w, ur[3].x, ur[3].y, ur[3].z, ur[3].w};
+      const float4 *t4 = reinterpret_cast<const float4 *>(T[t]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (4 * q < r) {
+          const float4 v = t4[q];
+          lr += bf2f((uint16_t)w16[2 * q]) * v.x;
+          lr += bf2f((uint16_t)(w16[2 * q] >> 16)) * v.y;
+          lr += bf2f((uint16_t)w16[2 * q + 1]) * v.z;
+          lr += bf2f((uint16_t)(w16[2 * q + 1] >> 16)) * v.w;
+        }
+      }
+    } else if (B.ufast) {
+      for (int j0 = 0; j0 < r; j0 += 8) {
+        const uint4 uv = ld16(u + j0);
+        const uint32_t w4[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) lr += bf2f((uint16_t)(w4[q >> 1] >> ((q & 1) * 16))) * T[t][j0 + q];
+      }
+    } else {
+      for (int j = 0; j < r; ++j) lr += bf2f(u[j]) * T[t][j];
+    }
+    a.y[(size_t)m * a.ldy + B.col + n] = f2bf(sn * z[t] + lr);
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 // Largest row-group count per workgroup: the fragments of two steps
@@ -647,7 +744,10 @@ hipError_t launch_decode(const Recon &rq, const DecodePlan &pl, void *ws, hipStr
     d.ufast = (P.r % 8 == 0) && (((uintptr_t)P.U & 15) == 0);
     chunks += (int)((P.N + 255) / 256);
   }
-  hipLaunchKernelGGL(k_decode_combine, dim3(chunks, c.M), dim3(256), 0, st, c);
+  if ((long)chunks * c.M > 2048 && (size_t)pl.S * c.M * c.Wp * 4 < (size_t(1) << 31))
+    hipLaunchKernelGGL(k_decode_combine4, dim3(chunks, (c.M + 3) / 4), dim3(256), 0, st, c);
+  else
+    hipLaunchKernelGGL(k_decode_combine, dim3(chunks, c.M), dim3(256), 0, st, c);
   return hipGetLastError();
 }
 
