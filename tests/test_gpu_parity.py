@@ -168,18 +168,21 @@ def test_decode_high_rank_split(M, r):
 
 
 @pytest.mark.parametrize("M,S", [(33, 1), (33, 3), (64, 2), (9, 1)])
-def test_decode_combine_token_groups(M, S, force_plan):
+@pytest.mark.parametrize("ranks", [(32, 32), (48, 0), (36, 100)], ids=str)
+def test_decode_combine_token_groups(M, S, ranks, force_plan):
     """Split mode on a wide gate/up pair (the combine launches more than 2048
     workgroups of one token each), K in one or more ranges, token counts off
-    the 16-token groups of the streaming kernel (33, 9)."""
+    the 16-token groups of the streaming kernel (33, 9); U rows of up to 32
+    ranks requested before the barrier, longer 16-byte aligned rows (48), rows
+    that are not 16-byte aligned (36, 100), a block without rank."""
     force_plan("DECODE_SPLIT", 1)
     force_plan("DECODE_S", S)
     K = 768
-    bds = [I.bundle("test", 10, f, K, 9000, 32, "bf16", variant="s0" if f == "up" else "normal")
-           for f in ("gate", "up")]
+    bds = [I.bundle("test", 10, f, K, 9000, r, "bf16", variant="s0" if f == "up" else "normal")
+           for f, r in zip(("gate", "up"), ranks)]
     x = I.activations("test", 1200 + M + S, M, K, "bf16")
     y = B.recon_gateup(up(x, "bf16"), [bundle_up(b, "bf16") for b in bds])
-    assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in bds]), "bf16", f"M={M} S={S}")
+    assert_parity(down(y), oracle.recon_fused(x, [bundle_np(b) for b in bds]), "bf16", f"M={M} S={S} r={ranks}")
 
 
 # The tiled kernel: every compiled tile shape (BM x BN output, BK-wide K slices
