@@ -399,6 +399,7 @@ def run_pmc_probe(args, torch, B, I):
     then the dispatches named by --probe, eagerly:
     decode_gateup (Gemma-3-1B fused gate/up, 26 layers x M in {1, 4, 16}),
     decode_gateup_large (large-decoder gate/up at M = 1, 8 layers),
+    decode_gateup_large32 (the same at M = 32),
     prefill_gateup_large (large-decoder gate/up at M = 512, 8 layers)."""
     _calibration_copy(torch)
     probe = args.probe
@@ -419,7 +420,7 @@ def run_pmc_probe(args, torch, B, I):
         wl, shapes, L, G, r, Ms = "gemma_decode", I.GEMMA_1B, 26, None, 16, (1, 4, 16)
     else:
         wl, shapes, L, G, r = "large_decoder", I.LARGE_DECODER, 8, 4, 32
-        Ms = (1,) if probe == "decode_gateup_large" else (512,)
+        Ms = {"decode_gateup_large": (1,), "decode_gateup_large32": (32,)}.get(probe, (512,))
     layer_np = I.layer_bundles(wl, shapes, layers=L, r=r, dtype="bf16", num_bands=G, families=("gate", "up"))
     layer_dev = upload_layers(torch, I, layer_np)
     dev = torch.device("cuda", 0)
@@ -1163,8 +1164,8 @@ def main():
                     choices=["headline", "gemma_decode", "gemma_prefill", "large_decoder", "materialize_fp4",
                              "fp4_decode", "fold", "rebuild", "decompose", "pmc_probe", "pmc_probe_fp4"])
     ap.add_argument("--probe", default="decode_gateup",
-                    choices=["decode_gateup", "decode_gateup_large", "prefill_gateup_large", "load_batch",
-                             "fp4_large"],
+                    choices=["decode_gateup", "decode_gateup_large", "decode_gateup_large32", "prefill_gateup_large",
+                             "load_batch", "fp4_large"],
                     help="with --workload pmc_probe: which dispatches the counter run covers")
     ap.add_argument("--summarize", action="store_true",
                     help="summarise rocprofv3 CSVs (--trace, --fetch/--write, --pmc) instead of running")
