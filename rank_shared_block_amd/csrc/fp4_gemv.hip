@@ -245,9 +245,6 @@ __global__ __launch_bounds__(512) void k_fp4_gemv_m4(const F4Args a) {
 
   const int unit = xcd_contiguous_tile(blockIdx.x, a.ntiles * a.S);
   if (unit < 0) return;
-  const float g = *a.g;
-  if (tid < 256) scale_lut[tid] = g * e4m3_value(tid & 0x7Fu);
-  __syncthreads();
   const int tile = unit / a.S, p = unit - tile * a.S;
   const int K = a.K, row0 = tile * a.rows;
   const int Rv = min(a.rows, a.N - row0);
@@ -304,6 +301,14 @@ __global__ __launch_bounds__(512) void k_fp4_gemv_m4(const F4Args a) {
   uint4 ca[NG], cb[NG], xa[KS], xb[KS];
   uint2 sa[NG], sb[NG];
   if (nmine > 0) fetch(wave, ca, sa, xa);
+  // The step-scale table is built while the first step's loads are in
+  // flight (the global scale is a scalar load; the barrier waits for the
+  // table's LDS writes only).
+  {
+    const float g = *a.g;
+    if (tid < 256) scale_lut[tid] = g * e4m3_value(tid & 0x7Fu);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
   int i = 0;
   for (; i + 2 < nmine; i += 2) {
     fetch(wave + (i + 1) * WAVES, cb, sb, xb);
@@ -371,15 +376,6 @@ __global__ __launch_bounds__(256) void k_fp4_gemv_dot(const F4Args a) {
   const int kbeg = p * a.kchunk, kend = min(K, kbeg + a.kchunk), kn = kend - kbeg;
   const float g = *a.g;
 
-  // x[m][kbeg, kend) into LDS (zeros for tokens past M), 16 bytes per thread
-  for (int i = tid; i < MT * (kn / 8); i += 256) {
-    const int m = i / (kn / 8), k8 = (i - m * (kn / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (m < a.M) v = ld16(a.x + (size_t)m * a.ldx + kbeg + k8);
-    *reinterpret_cast<uint4 *>(&xs[m * a.kchunk + k8]) = v;
-  }
-  __syncthreads();
-
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.packed + (size_t)row0 * (K / 2), (uint32_t)Rv * (K / 2));
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + (size_t)row0 * (K / 16), (uint32_t)Rv * (K / 16));
   float acc[NG][MT];
@@ -440,6 +436,15 @@ __global__ __launch_bounds__(256) void k_fp4_gemv_dot(const F4Args a) {
   uint32_t sa[NG], sb[NG];
   int k0 = kbeg;
   fetch(k0, ca, sa);
+  // x[m][kbeg, kend) into LDS (zeros for tokens past M), 16 bytes per thread,
+  // while the first step's codes are in flight
+  for (int i = tid; i < MT * (kn / 8); i += 256) {
+    const int m = i / (kn / 8), k8 = (i - m * (kn / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (m < a.M) v = ld16(a.x + (size_t)m * a.ldx + kbeg + k8);
+    *reinterpret_cast<uint4 *>(&xs[m * a.kchunk + k8]) = v;
+  }
+  __syncthreads();
   for (; k0 + KSTEP < kend; k0 += 2 * KSTEP) {
     fetch(k0 + KSTEP, cb, sb);
     compute(k0, ca, sa);
